@@ -1,0 +1,230 @@
+"""MI355X (gfx950) delta-rule sequence mixer: Python binding of libdeltanet.so.
+
+Argument marshalling only.  Every step of the delta rule runs in the HIP kernels
+behind the C ABI declared in ``include/deltanet.h``; torch provides device memory
+and the stream.  There is no CPU path: without the built library, or without a GPU,
+the calls raise.
+
+The rule (frankenstein "DeltaNet Attention" page, module docstring; gate order of
+the nnterp "linear_attention" page): per (sequence, value head), with the state S
+mapping keys to values and a = exp(g_t),
+
+    S_t = a S_{t-1} - beta_t (a S_{t-1} k_t - v_t) k_t^T,    o_t = scale * S_t q_t.
+
+States are fp32 ``[N, Hv, Dk, Dv]`` holding S^T (key-major).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib_path", "load_library",
+           "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
+           "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdeltanet.so")
+
+DN_OK, DN_ERR_INVALID_ARG, DN_ERR_UNSUPPORTED, DN_ERR_HIP, DN_ERR_WORKSPACE = 0, 1, 2, 3, 4
+DN_F32, DN_BF16 = 0, 1
+EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step",
+            "dn_status_str", "dn_version")
+
+
+class DeltaNetError(RuntimeError):
+    pass
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("Hqk", ctypes.c_int32), ("Hv", ctypes.c_int32), ("Dk", ctypes.c_int32),
+                ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdeltanet.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m delta_rule_recurrent_chunked_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        sp = ctypes.POINTER(_Shape)
+        lib.dn_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.dn_chunk_fwd.restype = ctypes.c_int
+        lib.dn_chunk_fwd_workspace_bytes.argtypes = [sp]
+        lib.dn_chunk_fwd_workspace_bytes.restype = sz
+        lib.dn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.dn_decode_step.restype = ctypes.c_int
+        lib.dn_status_str.argtypes = [ctypes.c_int]
+        lib.dn_status_str.restype = ctypes.c_char_p
+        lib.dn_version.argtypes = []
+        lib.dn_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def _raise(code: int, what: str):
+    msg = f"{what}: {load_library().dn_status_str(code).decode()}"
+    if code in (DN_ERR_INVALID_ARG, DN_ERR_WORKSPACE):
+        raise ValueError(msg)
+    if code == DN_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise DeltaNetError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DN_F32
+    if t.dtype == torch.bfloat16:
+        return DN_BF16
+    raise NotImplementedError(f"q/k/v dtype {t.dtype} is not supported (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: torch.dtype,
+                    num_seqs: Optional[int] = None, chunk_size: int = 64) -> int:
+    """Device workspace (bytes) ``dn_chunk_fwd`` needs for these sizes."""
+    s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
+               DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0)
+    return int(load_library().dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+              g: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+              scale: float = 1.0, chunk_size: int = 64, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = True
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Delta rule over whole sequences (prefill), chunkwise-parallel form.
+
+    q, k ``[B, T, Hqk, Dk]``, v ``[B, T, Hv, Dv]`` (float32 or bfloat16, one dtype);
+    beta, g ``[B, T, Hv]`` float32 (g None: plain rule); initial_state
+    ``[N, Hv, Dk, Dv]`` float32 or None (zero state); cu_seqlens int32 ``[N + 1]``
+    packs N sequences along T (B == 1).  Returns ``(o [B, T, Hv, Dv], final_state or
+    None)``.  ``final_state`` may be passed (and may be ``initial_state``, to update
+    it in place); ``out`` and ``workspace`` may be passed to avoid allocation.
+    ``check_cu_seqlens`` copies cu_seqlens to the host (a synchronising copy) and
+    checks ``cu[0] == 0``, non-decreasing, ``cu[N] == T``: the kernels trust it.
+    """
+    lib = load_library()
+    _dev(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, Hqk, Dk]")
+    B, T, Hqk, Dk = q.shape
+    _dev(k, "k", q.dtype, q.shape)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, T, Hv, Dv]")
+    _dev(v, "v", q.dtype)
+    Hv, Dv = v.shape[2], v.shape[3]
+    if tuple(v.shape[:2]) != (B, T):
+        raise ValueError("v must be [B, T, Hv, Dv] with the batch and length of q")
+    _dev(beta, "beta", torch.float32, (B, T, Hv))
+    if g is not None:
+        _dev(g, "g", torch.float32, (B, T, Hv))
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+        N = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("a packed batch (cu_seqlens) must have B == 1")
+        if check_cu_seqlens:
+            c = cu_seqlens.cpu()
+            if int(c[0]) != 0 or int(c[-1]) != T or bool((c[1:] < c[:-1]).any()):
+                raise ValueError("cu_seqlens must start at 0, not decrease and end at T")
+    else:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32, (N, Hv, Dk, Dv))
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=dev)
+    else:
+        _dev(out, "out", q.dtype, (B, T, Hv, Dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, Dk, Dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _dev(final_state, "final_state", torch.float32, (N, Hv, Dk, Dv))
+    shape = _Shape(B, T, N, Hqk, Hv, Dk, Dv, _dtype_code(q), chunk_size, float(scale))
+    need = int(lib.dn_chunk_fwd_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+    else:
+        _dev(workspace, "workspace", torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    with torch.cuda.device(dev):
+        rc = lib.dn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                              _ptr(g), _ptr(initial_state), _ptr(final_state),
+                              _ptr(cu_seqlens), _ptr(out), _ptr(workspace), ws_bytes,
+                              _stream(dev))
+    if rc != DN_OK:
+        _raise(rc, "dn_chunk_fwd")
+    return out, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                g: Optional[torch.Tensor], state: torch.Tensor, scale: float = 1.0,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence against the cached ``state`` (updated in place).
+
+    q, k ``[N, Hqk, Dk]``, v ``[N, Hv, Dv]``; beta, g ``[N, Hv]`` float32 (g may be
+    None); state ``[N, Hv, Dk, Dv]`` float32.  Returns o ``[N, Hv, Dv]``.
+    """
+    lib = load_library()
+    _dev(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [N, Hqk, Dk]")
+    N, Hqk, Dk = q.shape
+    _dev(k, "k", q.dtype, q.shape)
+    _dev(v, "v", q.dtype)
+    if v.dim() != 3 or v.shape[0] != N:
+        raise ValueError("v must be [N, Hv, Dv]")
+    Hv, Dv = v.shape[1], v.shape[2]
+    _dev(beta, "beta", torch.float32, (N, Hv))
+    if g is not None:
+        _dev(g, "g", torch.float32, (N, Hv))
+    _dev(state, "state", torch.float32, (N, Hv, Dk, Dv))
+    if out is None:
+        out = torch.empty((N, Hv, Dv), dtype=q.dtype, device=q.device)
+    else:
+        _dev(out, "out", q.dtype, (N, Hv, Dv))
+    shape = _Shape(N, 1, N, Hqk, Hv, Dk, Dv, _dtype_code(q), 0, float(scale))
+    with torch.cuda.device(q.device):
+        rc = lib.dn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                _ptr(g), _ptr(state), _ptr(out), _stream(q.device))
+    if rc != DN_OK:
+        _raise(rc, "dn_decode_step")
+    return out

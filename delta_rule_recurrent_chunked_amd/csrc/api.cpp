@@ -1,0 +1,117 @@
+// api.cpp -- the exported C ABI (include/deltanet.h): host-side argument checks,
+// then the launch of the right kernels on the caller's stream.  No allocation, no
+// global state.
+#include "../../include/deltanet.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Checks shared by both entry points.  Returns DN_OK or the error to report.
+dn_status check_common(const dn_shape* s) {
+    if (!s) return DN_ERR_INVALID_ARG;
+    if (s->B < 0 || s->T < 0 || s->num_seqs < 0 || s->Hqk <= 0 || s->Hv <= 0 || s->Dk <= 0 ||
+        s->Dv <= 0)
+        return DN_ERR_INVALID_ARG;
+    if (s->Hv % s->Hqk != 0) return DN_ERR_INVALID_ARG;
+    if (s->dtype != DN_F32 && s->dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
+    if (!dim_ok(s->Dk) || !dim_ok(s->Dv)) return DN_ERR_UNSUPPORTED;
+    return DN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dn_version(void) { return 10000; }
+
+const char* dn_status_str(dn_status st) {
+    switch (st) {
+        case DN_OK: return "ok";
+        case DN_ERR_INVALID_ARG: return "invalid argument";
+        case DN_ERR_UNSUPPORTED: return "unsupported size or dtype";
+        case DN_ERR_HIP: return "HIP runtime error";
+        case DN_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+// Sizes of a prefill call.  `packed` tells whether cu_seqlens is given.
+static dn_status prefill_shape(const dn_shape* s, bool packed, dn::PrefillArgs& a) {
+    dn_status st = check_common(s);
+    if (st != DN_OK) return st;
+    const int C = s->chunk_size == 0 ? 64 : s->chunk_size;
+    if (C != 16 && C != 32 && C != 64) return DN_ERR_UNSUPPORTED;
+    if (packed) {
+        if (s->B != 1 || s->num_seqs < 1) return DN_ERR_INVALID_ARG;
+    } else if (s->num_seqs != s->B) {
+        return DN_ERR_INVALID_ARG;
+    }
+    a = dn::PrefillArgs{};
+    a.B = s->B; a.T = s->T; a.N = s->num_seqs; a.Hqk = s->Hqk; a.Hv = s->Hv;
+    a.Dk = s->Dk; a.Dv = s->Dv; a.C = C; a.bf16 = s->dtype == DN_BF16; a.scale = s->scale;
+    return DN_OK;
+}
+
+size_t dn_chunk_fwd_workspace_bytes(const dn_shape* s) {
+    // The bound covers both a batch of rows and a packed batch of num_seqs sequences.
+    dn::PrefillArgs a;
+    const bool packed = s && s->B == 1 && s->num_seqs != 1;
+    if (prefill_shape(s, packed, a) != DN_OK) return 0;
+    return dn::prefill_fast_supported(a) ? dn::prefill_fast_workspace_bytes(a) : 0;
+}
+
+dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, float* hT,
+                       const int32_t* cu, void* o, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    dn::PrefillArgs a;
+    dn_status st = prefill_shape(s, cu != nullptr, a);
+    if (st != DN_OK) return st;
+    const long tokens = (long)s->B * s->T;
+    if (tokens > 0 && (!q || !k || !v || !beta || !o)) return DN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, h0, hT, o, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
+    const void* scalars[] = {beta, g, cu};
+    for (const void* p : scalars)
+        if (p && !aligned4(p)) return DN_ERR_INVALID_ARG;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.h0 = h0; a.hT = hT; a.cu = cu; a.o = o;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+    hipError_t e;
+    if (dn::prefill_fast_supported(a)) {
+        const size_t need = dn::prefill_fast_workspace_bytes(a);
+        if (need > ws_bytes || (need > 0 && !ws)) return DN_ERR_WORKSPACE;
+        e = dn::launch_prefill_fast(a, stream);
+    } else {
+        e = dn::launch_prefill_generic(a, stream);
+    }
+    return e == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, float* state, void* o,
+                         hipStream_t stream) {
+    dn_status st = check_common(s);
+    if (st != DN_OK) return st;
+    if (s->T != 1 || s->num_seqs != s->B) return DN_ERR_INVALID_ARG;
+    if (s->B > 0 && (!q || !k || !v || !beta || !state || !o)) return DN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, state, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
+    const void* scalars[] = {beta, g};
+    for (const void* p : scalars)
+        if (p && !aligned4(p)) return DN_ERR_INVALID_ARG;
+    dn::DecodeArgs a{};
+    a.N = s->B; a.Hqk = s->Hqk; a.Hv = s->Hv; a.Dk = s->Dk; a.Dv = s->Dv;
+    a.bf16 = s->dtype == DN_BF16; a.scale = s->scale;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.state = state; a.o = o;
+    return dn::launch_decode(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+}  // extern "C"

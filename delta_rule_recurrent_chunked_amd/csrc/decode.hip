@@ -1,0 +1,159 @@
+// decode.hip -- one token of the gated delta rule against a cached fp32 state,
+// updated in place (the nnterp "linear_attention" page: the token-by-token rule on
+// a decode step, with the cached state as state_input, overwritten afterwards).
+//
+// Per (sequence n, value head h), with the state stored key-major, M = S^T [Dk][Dv]:
+//   a      = exp(g)                         (nnterp "decays": log of the fraction kept)
+//   r_k    = M^T k,  r_q = M^T q            (column reductions over the key dim)
+//   delta  = beta (v - a r_k)               (= -beta (S' k - v), S' = a S; "The Delta
+//                                            Rule" section of the mutichung DeltaNet page)
+//   o      = scale (a r_q + (k.q) delta)    (= scale S_t q with S_t = S' + delta k^T)
+//   M     <- a M + k delta^T
+// The state is read once and written once: this kernel is bound by HBM bandwidth.
+//
+// Work decomposition: one workgroup per (n, h, slice of CW value columns).  A thread
+// owns a float4 of CW/4 consecutive columns in RPT rows, so a wave reads whole
+// CW*4-byte row segments and every state byte moves through one 128-bit load and one
+// 128-bit store.  Column sums over the key dim reduce across lanes (xor shuffles),
+// then across the waves of the workgroup through LDS.
+#include "internal.h"
+
+namespace dn {
+namespace {
+
+template <int DK, int CW>
+struct DecodeShape {
+    static constexpr int TPR = CW / 4;                              // threads per state row
+    static constexpr int NT = (TPR * DK < 256) ? TPR * DK : 256;    // threads per workgroup
+    static constexpr int RPP = NT / TPR;                            // rows per pass
+    static constexpr int RPT = DK / RPP;                            // rows per thread
+    static constexpr int NW = NT / 64;                              // waves
+    static_assert(CW % 4 == 0 && TPR <= 64 && NT % 64 == 0 && DK % RPP == 0, "decode tiling");
+};
+
+template <typename T, int DK, int DV, int CW>
+__global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(DecodeArgs a) {
+    using S = DecodeShape<DK, CW>;
+    constexpr int TPR = S::TPR, RPP = S::RPP, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
+    __shared__ float red[NW][2 * CW + 1];
+    __shared__ float dsh[CW];
+
+    const int tid = threadIdx.x;
+    const int ct = tid % TPR;                 // float4 column group
+    const int rg = tid / TPR;                 // row group
+    const int slice = blockIdx.x % SLICES;
+    const int nh = blockIdx.x / SLICES;       // n * Hv + h
+    const int h = nh % a.Hv;
+    const int n = nh / a.Hv;
+    const int hq = h / (a.Hv / a.Hqk);
+
+    const T* qp = static_cast<const T*>(a.q) + ((long)n * a.Hqk + hq) * DK;
+    const T* kp = static_cast<const T*>(a.k) + ((long)n * a.Hqk + hq) * DK;
+    float* Mp = a.state + (long)nh * DK * DV + slice * CW + ct * 4;
+
+    float4 m[RPT];
+#pragma unroll
+    for (int p = 0; p < RPT; ++p)
+        m[p] = *reinterpret_cast<const float4*>(Mp + (long)(p * RPP + rg) * DV);
+    float kr[RPT], qr[RPT];
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        kr[p] = ld_f32(kp, p * RPP + rg);
+        qr[p] = ld_f32(qp, p * RPP + rg);
+    }
+    const float alpha = a.g ? expf(a.g[nh]) : 1.0f;
+    const float beta = a.beta[nh];
+
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        pk[0] += m[p].x * kr[p]; pk[1] += m[p].y * kr[p]; pk[2] += m[p].z * kr[p]; pk[3] += m[p].w * kr[p];
+        pq[0] += m[p].x * qr[p]; pq[1] += m[p].y * qr[p]; pq[2] += m[p].z * qr[p]; pq[3] += m[p].w * qr[p];
+        if (ct == 0) kq += kr[p] * qr[p];
+    }
+    // reduce over the row groups of this wave (lanes that share ct)
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pk[c] += __shfl_xor(pk[c], off);
+            pq[c] += __shfl_xor(pq[c], off);
+        }
+        kq += __shfl_xor(kq, off);
+    }
+    const int lane = tid % 64, wave = tid / 64;
+    if (lane < TPR) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            red[wave][ct * 4 + c] = pk[c];
+            red[wave][CW + ct * 4 + c] = pq[c];
+        }
+        if (lane == 0) red[wave][2 * CW] = kq;
+    }
+    __syncthreads();
+    if (tid < CW) {
+        float rk = 0.f, rq = 0.f, kqs = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            rk += red[w][tid];
+            rq += red[w][CW + tid];
+            kqs += red[w][2 * CW];
+        }
+        const long vo = (long)nh * DV + slice * CW + tid;
+        const float d = beta * (ld_f32(static_cast<const T*>(a.v), vo) - alpha * rk);
+        dsh[tid] = d;
+        st_out(static_cast<T*>(a.o), vo, a.scale * (alpha * rq + kqs * d));
+    }
+    __syncthreads();
+    const float d0 = dsh[ct * 4 + 0], d1 = dsh[ct * 4 + 1], d2 = dsh[ct * 4 + 2], d3 = dsh[ct * 4 + 3];
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        float4 r;
+        r.x = alpha * m[p].x + kr[p] * d0;
+        r.y = alpha * m[p].y + kr[p] * d1;
+        r.z = alpha * m[p].z + kr[p] * d2;
+        r.w = alpha * m[p].w + kr[p] * d3;
+        *reinterpret_cast<float4*>(Mp + (long)(p * RPP + rg) * DV) = r;
+    }
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_dims(const DecodeArgs& a, hipStream_t s) {
+    constexpr int CW = DV < 32 ? DV : 32;
+    using S = DecodeShape<DK, CW>;
+    const long blocks = (long)a.N * a.Hv * (DV / CW);
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW>), dim3((unsigned)blocks), dim3(S::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t launch_dv(const DecodeArgs& a, hipStream_t s) {
+    switch (a.Dv) {
+        case 16: return launch_dims<T, DK, 16>(a, s);
+        case 32: return launch_dims<T, DK, 32>(a, s);
+        case 64: return launch_dims<T, DK, 64>(a, s);
+        case 128: return launch_dims<T, DK, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_dk(const DecodeArgs& a, hipStream_t s) {
+    switch (a.Dk) {
+        case 16: return launch_dv<T, 16>(a, s);
+        case 32: return launch_dv<T, 32>(a, s);
+        case 64: return launch_dv<T, 64>(a, s);
+        case 128: return launch_dv<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    if (a.N == 0) return hipSuccess;
+    return a.bf16 ? launch_dk<__bf16>(a, s) : launch_dk<float>(a, s);
+}
+
+}  // namespace dn

@@ -1,0 +1,70 @@
+// internal.h -- declarations shared by the HIP sources of libdeltanet (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dn {
+
+// Everything one prefill launch needs, already validated on the host.
+struct PrefillArgs {
+    int B, T, N, Hqk, Hv, Dk, Dv, C;
+    int bf16;                       // 1: q/k/v/o are bfloat16, 0: float
+    float scale;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* beta;
+    const float* g;                 // may be null (no decay)
+    const float* h0;                // may be null (zero initial state)
+    float* hT;                      // may be null (no final state); may alias h0
+    const int32_t* cu;              // may be null (each batch row is a sequence)
+    void* o;
+    void* ws;                       // workspace (fast path)
+    size_t ws_bytes;
+};
+
+struct DecodeArgs {
+    int N, Hqk, Hv, Dk, Dv;
+    int bf16;
+    float scale;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* beta;
+    const float* g;
+    float* state;
+    void* o;
+};
+
+// Launchers (host functions); each returns hipGetLastError() after its launches.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
+bool prefill_fast_supported(const PrefillArgs& a);
+size_t prefill_fast_workspace_bytes(const PrefillArgs& a);
+hipError_t launch_prefill_fast(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace dn
+
+// ------------------------------------------------------------------ device helpers
+namespace dn {
+
+__device__ __forceinline__ float ld_f32(const float* p, long i) { return p[i]; }
+__device__ __forceinline__ float ld_f32(const __bf16* p, long i) { return (float)p[i]; }
+
+__device__ __forceinline__ void st_out(float* p, long i, float x) { p[i] = x; }
+__device__ __forceinline__ void st_out(__bf16* p, long i, float x) { p[i] = (__bf16)x; }
+
+// Token range [bos, eos) of sequence n.
+__device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, long& bos, long& eos) {
+    if (cu) {
+        bos = cu[n];
+        eos = cu[n + 1];
+    } else {
+        bos = (long)n * T;
+        eos = bos + T;
+    }
+}
+
+}  // namespace dn

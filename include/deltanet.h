@@ -1,0 +1,154 @@
+/*
+ * deltanet.h -- C ABI of the MI355X (gfx950) delta-rule sequence mixer.
+ *
+ * The operation (all pages cited are the three web pages this library restates):
+ *
+ *   Per (sequence, value head) the state S is a d_v x d_k matrix mapping keys to
+ *   values.  Each token t updates it by the delta rule of the frankenstein
+ *   "DeltaNet Attention" page (module docstring) -- equivalently the error-
+ *   correcting form of the mutichung garden "DeltaNet" page, section "The Delta
+ *   Rule" -- after first decaying it by the gate of the nnterp "linear_attention"
+ *   page (LinearAttention class text; "decays" is the log of the fraction kept):
+ *
+ *       S'_t = exp(g_t) S_{t-1}
+ *       S_t  = S'_t - beta_t (S'_t k_t - v_t) k_t^T
+ *       o_t  = scale * S_t q_t                      (read after the write)
+ *
+ *   With g absent the decay factor is 1 (the plain delta rule).  beta may lie in
+ *   (0, 1), or in (0, 2) for the negative-eigenvalue variant (nnterp "betas"); any
+ *   real beta is computed as given.  q and k are expected to be L2-normalised by the
+ *   caller (the frankenstein forward and the DeltaNet block flowchart normalise
+ *   them before the rule); the library does not normalise.
+ *
+ *   A prompt runs the chunked (chunkwise-parallel) form of the rule over the whole
+ *   sequence; a decode step runs the rule for one token against the cached state,
+ *   which it overwrites in place (nnterp "state_input": None on a fresh prompt, the
+ *   cache's own buffer on a decode step).
+ *
+ * State layout.  Every state tensor is fp32, [.., Dk, Dv] row-major: element
+ * (i, j) is S[j][i], i.e. the library stores M = S^T, "one key_dim by value_dim
+ * matrix per head" as the nnterp page puts it.
+ *
+ * Head sharing.  Hv value heads read Hqk <= Hv query/key heads, Hv % Hqk == 0;
+ * value head h reads query/key head h / (Hv / Hqk) (the nnterp queries accessor
+ * repeats the query/key heads to the value heads; each query/key head serves that
+ * many consecutive value heads).
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller, contiguous
+ *     row-major; q, k, v, o, states and workspace 16-byte aligned, beta, g and
+ *     cu_seqlens 4-byte aligned.  The library allocates nothing and keeps no
+ *     state between calls; calls on different streams may run concurrently when
+ *     their output buffers do not overlap.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream) and
+ *     is asynchronous: the call returns before the kernels finish.
+ *   - Argument errors are detected on the host and returned synchronously before
+ *     anything is launched; nothing is written then.  Data-dependent
+ *     preconditions (g <= 0, q/k normalisation, cu_seqlens monotone with
+ *     cu_seqlens[0] == 0 and cu_seqlens[N] == T) are not checked on the device.
+ */
+#ifndef DELTANET_H
+#define DELTANET_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DN_OK = 0,
+    DN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad or inconsistent sizes     */
+    DN_ERR_UNSUPPORTED = 2,  /* a size or dtype outside what the kernels are built for */
+    DN_ERR_HIP = 3,          /* the HIP runtime reported an error at launch            */
+    DN_ERR_WORKSPACE = 4     /* workspace missing or smaller than required             */
+} dn_status;
+
+typedef enum {
+    DN_F32 = 0,              /* q, k, v and o are float                                */
+    DN_BF16 = 1              /* q, k, v and o are bfloat16 (round to nearest even)     */
+} dn_dtype;
+
+/* Sizes of one call.  Supported: Dk, Dv in {16, 32, 64, 128}; chunk_size in
+ * {16, 32, 64} (0 selects 64).  beta, g and all states are fp32 regardless of dtype. */
+typedef struct {
+    int32_t B;           /* batch rows; 1 when cu_seqlens is given                       */
+    int32_t T;           /* tokens per row; total packed tokens when cu_seqlens is given */
+    int32_t num_seqs;    /* N: B, or len(cu_seqlens) - 1                                  */
+    int32_t Hqk;         /* query/key heads                                               */
+    int32_t Hv;          /* value heads (multiple of Hqk)                                 */
+    int32_t Dk;          /* key dim                                                       */
+    int32_t Dv;          /* value dim                                                     */
+    int32_t dtype;       /* dn_dtype of q, k, v, o                                        */
+    int32_t chunk_size;  /* tokens per chunk of the chunked form                          */
+    float scale;         /* multiplies every read; 1.0 reproduces o_t = S_t q_t           */
+} dn_shape;
+
+/*
+ * dn_chunk_fwd -- the delta rule over whole sequences (prefill), in the
+ * chunkwise-parallel form: inside each chunk the updates are solved together as a
+ * unit-lower-triangular system, and the state is carried from chunk to chunk.
+ * The result equals the token-by-token recurrence above up to rounding.
+ *
+ *   q, k           [B, T, Hqk, Dk]  dtype
+ *   v              [B, T, Hv, Dv]   dtype
+ *   beta           [B, T, Hv]       fp32 write strengths
+ *   g              [B, T, Hv]       fp32 log decays, or NULL for the plain rule
+ *   initial_state  [N, Hv, Dk, Dv]  fp32 state each sequence starts from, or NULL
+ *                                   for the zero state (a fresh prompt)
+ *   final_state    [N, Hv, Dk, Dv]  fp32 state after each sequence's last token,
+ *                                   or NULL to skip it; may alias initial_state
+ *   cu_seqlens     [N + 1] int32 device offsets of N sequences packed along T (B must
+ *                                   be 1), or NULL: each batch row is one sequence.
+ *                                   A sequence of length 0 returns its initial state.
+ *   o              [B, T, Hv, Dv]   dtype, written for every token
+ *   workspace      device scratch of at least dn_chunk_fwd_workspace_bytes(shape)
+ *                                   bytes (may be NULL when that is 0); contents on
+ *                                   entry are ignored, on exit undefined
+ *
+ * Errors: DN_ERR_INVALID_ARG (null required pointer, non-positive sizes, Hv % Hqk,
+ * B != 1 or num_seqs < 1 with cu_seqlens, num_seqs != B without, misaligned
+ * pointer), DN_ERR_UNSUPPORTED (Dk, Dv, chunk_size or dtype not supported),
+ * DN_ERR_WORKSPACE, DN_ERR_HIP.  T == 0 is valid: final_state = initial_state.
+ */
+dn_status dn_chunk_fwd(const dn_shape* shape,
+                       const void* q, const void* k, const void* v,
+                       const float* beta, const float* g,
+                       const float* initial_state, float* final_state,
+                       const int32_t* cu_seqlens, void* o,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none). */
+size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
+
+/*
+ * dn_decode_step -- one token of the delta rule for each of N sequences against a
+ * cached state, updated in place (the nnterp page's token-by-token rule on a decode
+ * step, where the sequence axis is 1 and state_input is the cached state).
+ *
+ *   shape->B = N sequences, shape->T must be 1, num_seqs = N, cu_seqlens unused;
+ *   q, k   [N, Hqk, Dk] dtype;  v [N, Hv, Dv] dtype;  beta, g [N, Hv] fp32 (g may be NULL)
+ *   state  [N, Hv, Dk, Dv] fp32, read and overwritten with the new state
+ *   o      [N, Hv, Dv] dtype
+ *
+ * Errors: as dn_chunk_fwd (chunk_size is ignored).
+ */
+dn_status dn_decode_step(const dn_shape* shape,
+                         const void* q, const void* k, const void* v,
+                         const float* beta, const float* g,
+                         float* state, void* o, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* dn_status_str(dn_status status);
+
+/* ABI version (major * 10000 + minor * 100 + patch). */
+int32_t dn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTANET_H */

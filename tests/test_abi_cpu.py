@@ -1,0 +1,95 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delta_rule_recurrent_chunked_amd as dn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltanet.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dn.load_library()
+    declared = _declared()
+    assert set(declared) == set(dn.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.dn_version() >= 10000
+
+
+def test_status_strings():
+    lib = dn.load_library()
+    for code in range(5):
+        assert lib.dn_status_str(code)
+    assert b"invalid" in lib.dn_status_str(dn.DN_ERR_INVALID_ARG)
+
+
+def _shape(**kw):
+    d = dict(B=1, T=64, num_seqs=1, Hqk=2, Hv=2, Dk=16, Dv=16, dtype=dn.DN_BF16, chunk_size=64,
+             scale=1.0)
+    d.update(kw)
+    return dn._Shape(**d)
+
+
+def _chunk(shape, ptr=16, **over):
+    lib = dn.load_library()
+    p = ctypes.c_void_p(ptr)
+    args = dict(q=p, k=p, v=p, beta=p, g=None, h0=None, hT=None, cu=None, o=p, ws=None, wsb=0)
+    args.update(over)
+    return lib.dn_chunk_fwd(ctypes.byref(shape), args["q"], args["k"], args["v"], args["beta"],
+                            args["g"], args["h0"], args["hT"], args["cu"], args["o"], args["ws"],
+                            args["wsb"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(Hqk=3, Hv=4), dn.DN_ERR_INVALID_ARG),        # Hv not a multiple of Hqk
+    (dict(Hqk=0), dn.DN_ERR_INVALID_ARG),
+    (dict(T=-1), dn.DN_ERR_INVALID_ARG),
+    (dict(B=2, num_seqs=1), dn.DN_ERR_INVALID_ARG),     # num_seqs != B without cu_seqlens
+    (dict(Dk=48), dn.DN_ERR_UNSUPPORTED),
+    (dict(Dv=256), dn.DN_ERR_UNSUPPORTED),
+    (dict(chunk_size=128), dn.DN_ERR_UNSUPPORTED),
+    (dict(dtype=7), dn.DN_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_rejects_bad_shapes(bad, code):
+    assert _chunk(_shape(**bad)) == code
+
+
+def test_chunk_fwd_rejects_null_and_misaligned():
+    assert _chunk(_shape(), q=None) == dn.DN_ERR_INVALID_ARG
+    assert _chunk(_shape(), ptr=18) == dn.DN_ERR_INVALID_ARG
+    # packed batch needs B == 1
+    assert _chunk(_shape(B=2, num_seqs=3), cu=ctypes.c_void_p(16)) == dn.DN_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_shapes():
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    s = _shape(B=4, T=2, num_seqs=4)
+    assert lib.dn_decode_step(ctypes.byref(s), p, p, p, p, None, p, p, None) == dn.DN_ERR_INVALID_ARG
+    s = _shape(B=4, T=1, num_seqs=4, Dk=24)
+    assert lib.dn_decode_step(ctypes.byref(s), p, p, p, p, None, p, p, None) == dn.DN_ERR_UNSUPPORTED
+    s = _shape(B=4, T=1, num_seqs=4)
+    assert lib.dn_decode_step(ctypes.byref(s), p, None, p, p, None, p, p, None) == dn.DN_ERR_INVALID_ARG
+
+
+def test_workspace_query_is_host_only():
+    import torch
+    assert dn.workspace_bytes(1, 64, 2, 2, 16, 16, torch.float32) == 0
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        dn.chunk_fwd(q, q, q, torch.zeros(1, 4, 1))
