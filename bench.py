@@ -1,0 +1,228 @@
+"""Benchmark of the delta-rule mixer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--decode-reps R]
+
+One step is one prefill call (dn_chunk_fwd) over the DeltaNet layer-prefill workload
+(B=4, H=16, T=2048, d_k=d_v=128, bf16 q/k/v, fp32 beta, no decay, zero initial state,
+final state returned): 8192 tokens.  K steps are timed back to back between two
+device synchronisations, cycling through several copies of the inputs so the working
+set (> 256 MB) does not stay in the Infinity Cache between steps.  The decode step
+(256 sequences x 32 heads, state updated in place) is timed the same way and reported
+in the same line.  The fp64 oracle is timed on the host cores on a bounded sample of
+the prefill workload.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, TFLOP/s
+PREFILL = dict(B=4, T=2048, H=16, D=128, C=64)
+DECODE = dict(N=256, H=32, D=128)
+
+
+def prefill_bytes(B, T, Hqk, Hv, D, gated, N, init):
+    """Algorithmic HBM bytes of one prefill call: q, k, v read and o written once
+    (bf16), beta (and g) read once (fp32), final state written (and initial read)."""
+    tok = B * T
+    b = tok * (2 * Hqk * D * 2 + Hv * D * 2 + Hv * D * 2) + tok * Hv * 4 * (2 if gated else 1)
+    b += N * Hv * D * D * 4 * (2 if init else 1)
+    return b
+
+
+def prefill_flops(B, T, Hqk, Hv, D, C):
+    """Algorithmic matrix flops of the chunked form per call (dense tiles, triangles
+    not exploited): per chunk and value head, [K;Q] M (2*2C*D*D), T R (2*C*C*D),
+    P Delta (2*C*C*D), K^T Delta (2*C*D*D) and the Gram matrices K K^T, Q K^T
+    (2*2*C*C*D, shared by the value heads of one key head)."""
+    chunks = B * ((T + C - 1) // C)
+    per_v = 2 * 2 * C * D * D + 2 * 2 * C * C * D + 2 * C * D * D
+    per_qk = 2 * 2 * C * C * D
+    return chunks * (Hv * per_v + Hqk * per_qk)
+
+
+def decode_bytes(N, Hqk, Hv, D):
+    return N * Hv * D * D * 4 * 2 + N * (2 * Hqk * D * 2 + 2 * Hv * D * 2 + 2 * Hv * 4)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("prefill_fast.hip", "decode.hip"):
+        with open(os.path.join(ROOT, "delta_rule_recurrent_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per call measured with rocprofv3 counters (profiles/traffic.json),
+    used only while the kernel sources are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if t.get("source_digest") != source_digest():
+        return None, None
+    return t.get("prefill_bytes_per_call"), t.get("decode_bytes_per_call")
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The fp64 oracle on the host cores, on the same prefill workload, repeated until
+    about budget_s seconds of wall time have passed (at least one full call)."""
+    import oracle
+    f = x.f64()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrent(f["q"], f["k"], f["v"], f["beta"], f["g"], f["init"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    toks = reps * x.B * x.T
+    return {"value": toks / el, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"full prefill workload (B{x.B} H{x.Hv} T{x.T} d{x.Dk}) x {reps} call(s), "
+                      f"{el:.1f} s, fp64 token-by-token recurrence, OpenMP over (sequence, head)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-reps", type=int, default=50)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the mixer "
+              "runs no collectives; run --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import delta_rule_recurrent_chunked_amd as dn
+    from synth import make_case, make_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------------------------ prefill
+    x = make_config(2)
+    B, T, Hqk, Hv, D = x.B, x.T, x.Hqk, x.Hv, x.Dk
+    base = dict(q=to_dev(x.q), k=to_dev(x.k), v=to_dev(x.v), beta=to_dev(x.beta))
+    wsb = dn.workspace_bytes(B, T, Hqk, Hv, D, D, torch.bfloat16)
+    sets = []
+    for i in range(args.copies):
+        s = {k: (t if i == 0 else t.clone()) for k, t in base.items()}
+        s["o"] = torch.empty((B, T, Hv, D), dtype=torch.bfloat16, device=dev)
+        s["fs"] = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+        s["ws"] = torch.empty(max(1, wsb), dtype=torch.uint8, device=dev)
+        sets.append(s)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        dn.chunk_fwd(s["q"], s["k"], s["v"], s["beta"], None, None, out=s["o"], final_state=s["fs"],
+                     workspace=s["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = wall * 1e3 / args.steps
+    tokens = B * T
+    call_us = float(np.mean(ev_ms)) * 1e3
+    alg_b = prefill_bytes(B, T, Hqk, Hv, D, gated=False, N=B, init=False)
+    alg_f = prefill_flops(B, T, Hqk, Hv, D, PREFILL["C"])
+    traffic_p, traffic_d = load_traffic()
+    achieved = alg_b / (call_us * 1e-6) / 1e9
+
+    # ------------------------------------------------------------------- decode
+    y = make_case(B=DECODE["N"], T=1, Hqk=DECODE["H"], Dk=DECODE["D"], dtype="bf16", g_scale=0.1,
+                  init_std=0.02, seed=0, decode=True)
+    dq, dk, dv = to_dev(y.q)[:, 0], to_dev(y.k)[:, 0], to_dev(y.v)[:, 0]
+    db, dg = to_dev(y.beta)[:, 0], to_dev(y.g)[:, 0]
+    dstate = [to_dev(y.init) for _ in range(2)]
+    dout = torch.empty((y.B, y.Hv, y.Dv), dtype=torch.bfloat16, device=dev)
+    for i in range(3):
+        dn.decode_step(dq, dk, dv, db, dg, dstate[i % 2], out=dout)
+    torch.cuda.synchronize()
+    devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.decode_reps)]
+    for i in range(args.decode_reps):
+        devs[i][0].record(stream)
+        dn.decode_step(dq, dk, dv, db, dg, dstate[i % 2], out=dout)
+        devs[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = float(np.mean([a.elapsed_time(b) for a, b in devs])) * 1e3
+    state_b = y.B * y.Hv * y.Dk * y.Dv * 4 * 2
+    dec_b = decode_bytes(y.B, y.Hqk, y.Hv, y.Dk)
+    dec_gbs = state_b / (dec_us * 1e-6) / 1e9
+
+    line = {
+        "metric": "prefill tokens/sec + MFMA util; decode-step state GB/s vs HBM peak",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta sigmoid(N(0,1)))",
+        "config": {"workload": "DeltaNet layer prefill B4 H16 T2048 d_k=d_v=128 bf16, no decay, "
+                               "zero initial state, chunk 64", "global_batch": B, "seq_len": T,
+                   "heads": Hv, "head_dim": D, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_p,
+                     "kernel": "dn_chunk_fwd (prep_kernel + state_kernel)",
+                     "call_us": call_us, "algorithmic_bytes": alg_b},
+        "mfma": {"algorithmic_flops": alg_f, "tflops": alg_f / (call_us * 1e-6) / 1e12,
+                 "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+        "decode": {"workload": "gated decode step, 256 sequences x 32 heads, d=128, bf16, fp32 state "
+                               "in place", "us_per_step": dec_us, "state_GBps": dec_gbs,
+                   "roofline": {"bound": "hbm", "achieved": dec_b / (dec_us * 1e-6) / 1e9,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_b / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                "traffic": traffic_d, "kernel": "decode_kernel",
+                                "algorithmic_bytes": dec_b}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
