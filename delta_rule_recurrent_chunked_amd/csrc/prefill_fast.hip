@@ -7,37 +7,39 @@
 // "linear_attention" page.  Inside a chunk of n <= 64 tokens, with the state slice
 // M (key-major, S^T) at the chunk start and gamma_r = sum_{i<=r} g_i:
 //
-//   A_ri = beta_r exp(gamma_r - gamma_i) k_r.k_i (i < r),  T = (I + A)^{-1}
-//   R    = diag(beta) (V - diag(exp(gamma)) K M)
+//   A_ri  = beta_r exp(gamma_r - gamma_i) k_r.k_i (i < r),   T = (I + A)^{-1}
+//   R     = diag(beta) (V - diag(exp(gamma)) K M)
 //   Delta = T R                                   (row r: beta_r x prediction error)
-//   O    = scale (diag(exp(gamma)) Q M + P Delta),  P_ri = exp(gamma_r - gamma_i) q_r.k_i (i <= r)
-//   M   <- exp(gamma_last) M + K^T diag(exp(gamma_last - gamma)) Delta
+//   O     = scale (diag(exp(gamma)) Q M + P Delta),  P_ri = exp(gamma_r - gamma_i) q_r.k_i (i <= r)
+//   M    <- exp(gamma_last) M + K^T diag(exp(gamma_last - gamma)) Delta
 //
 // Three kernels on the caller's stream:
-//   chunk_offsets_kernel  (packed batches only) chunk index of each sequence's first
-//                         chunk, into the workspace.
-//   prep_kernel           one workgroup per (chunk, query/key head), all chunks in
-//                         parallel: K K^T on the matrix cores, the decay/beta mask, and
-//                         T = (I + A)^{-1} by 16x16 diagonal-block substitution plus
-//                         block back-substitution in fp32; T goes to the workspace in
-//                         bf16.  The Gram matrix is shared by the value heads that read
-//                         the same key head.
-//   state_kernel          one workgroup per (sequence, value head, 32-column slice of
-//                         the state).  The value columns of the state are independent,
-//                         so slices never exchange data; each carries its 128 x 32 fp32
-//                         state slice in MFMA accumulators across the sequential chunk
-//                         loop, with a bf16 copy in LDS as the next chunk's operand.
-//                         The next chunk's K, Q, V and T are fetched into registers
-//                         while the current chunk computes.
+//   chunk_offsets_kernel  (packed batches only) index of each sequence's first chunk.
+//   prep_kernel           one wave per (chunk, value head), all chunks in parallel:
+//                         K K^T on the matrix cores, the decay/beta mask, and
+//                         T = (I + A)^{-1}: the four 16x16 diagonal blocks by fp32
+//                         forward substitution (one lane per column), then the blocks
+//                         below the diagonal in two levels of 2x2 block inversion,
+//                         T21 = -T22 A21 T11, one MFMA per 16x16 tile.  T goes to the
+//                         workspace in bf16.
+//   state_kernel          one workgroup of 8 waves per (sequence, value head, 32-column
+//                         slice of the state); the value columns of the state are
+//                         independent, so slices never exchange data.
+//                           waves 0-3 ("chain"): X = K M, R, Delta = T R and the state
+//                             update, holding the 128 x 32 fp32 slice in accumulators;
+//                           waves 4-7 ("output"): Q M, the P tiles and O = Y + P Delta,
+//                             and they stage the next chunk (fetched into registers one
+//                             chunk ahead) into the other half of a double-buffered LDS.
+//                         Three workgroup barriers per chunk.
 //
-// MFMA lane layouts used here (gfx950, wave64):
+// MFMA lane layouts (gfx950, wave64):
 //   32x32x16 bf16: lane l supplies A[l%32][8(l/32) + e] and B[8(l/32) + e][l%32],
 //                  e < 8; accumulator element e is D[8(e/4) + 4(l/32) + e%4][l%32].
 //   16x16x32 bf16: lane l supplies A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16];
 //                  accumulator element e is D[4(l/16) + e][l%16].
 // Every operand is read from LDS as 8 consecutive bf16 along the contraction index, so
-// operands are stored contraction-contiguous (the state copy and the R/Delta tiles
-// are stored value-column-major for that reason).
+// each operand is stored contraction-contiguous; the matrices produced here (state copy,
+// R, Delta, T's transposed copy) are written in the layout their consumer reads.
 #include "internal.h"
 
 namespace dn {
@@ -47,9 +49,10 @@ constexpr int FC = 64;             // chunk
 constexpr int FD = 128;            // Dk = Dv
 constexpr int DVS = 32;            // state columns per state-pass workgroup
 constexpr int NSL = FD / DVS;      // slices per (sequence, value head)
-constexpr int KPITCH = FD + 8;     // bf16 row pitches (16-byte multiples, skewed banks)
-constexpr int CPITCH = FC + 8;
+constexpr int KPITCH = FD + 8;     // bf16 row pitches: 16-byte multiples that put the
+constexpr int CPITCH = FC + 8;     //   16 rows of one MFMA operand read on distinct banks
 constexpr int VPITCH = DVS + 8;
+constexpr int SNT = 512;           // state-pass threads (8 waves)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -67,6 +70,12 @@ __device__ __forceinline__ void st4(__bf16* p, float a, float b, float c, float 
     bf16x4 v;
     v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
     *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ bf16x8 zero8() {
+    bf16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+    return z;
 }
 
 // Chunks each workspace T slot can hold: enough for a batch of rows and for a packed
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(OFF_NT) void chunk_offsets_kernel(const int32_t* cu
     for (int n = lo; n < hi; ++n) s += (cu[n + 1] - cu[n] + FC - 1) / FC;
     part[tid] = s;
     __syncthreads();
-    if (tid == 0) {  // exclusive scan of the 1024 partial sums
+    if (tid == 0) {  // exclusive scan of the per-thread sums
         int acc = 0;
         for (int t = 0; t < OFF_NT; ++t) {
             const int x = part[t];
@@ -131,141 +140,184 @@ __device__ __forceinline__ void locate_chunk(const PrefillArgs& a, const int32_t
 
 // --------------------------------------------------------------------------- prep
 struct PrepSmem {
-    __bf16 K[FC][KPITCH];
-    float A[FC][FC + 1];
-    float Tm[FC][FC + 1];
-    float X[3][16][17];
+    union {
+        __bf16 K[FC][KPITCH];              // the chunk's keys (until the Gram is formed)
+        struct {
+            __bf16 Ab[FC][CPITCH];         // A, bf16 (blocks below the diagonal)
+            float Ad[4][16][17];           // A's diagonal 16x16 blocks, fp32
+        } a;
+    } u;
+    __bf16 Tb[FC][CPITCH];                 // T row-major
+    __bf16 TbT[FC][CPITCH];                // T transposed (column-major)
+    __bf16 XT[32][40];                     // level products' intermediate, transposed
     float gam[FC];
     float beta[FC];
 };
 
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, const int32_t* off, __bf16* Tws, long nct) {
+// One wave = one (chunk slot, value head).
+__global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* off, __bf16* Tws, long nct) {
     __shared__ PrepSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hq = blockIdx.x % a.Hqk;
-    const long gc = blockIdx.x / a.Hqk;
+    const int l = threadIdx.x;
+    const int l32 = l & 31, hi32 = l >> 5, l16 = l & 15, q16 = l >> 4;
+    const int h = blockIdx.x % a.Hv;
+    const long gc = blockIdx.x / a.Hv;
     int n, len;
     long t0;
     locate_chunk(a, off, nct, gc, n, t0, len);
     if (len <= 0) return;
-    const int R = a.Hv / a.Hqk;
+    const int hq = h / (a.Hv / a.Hqk);
     const __bf16* kp = static_cast<const __bf16*>(a.k);
 
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int v = tid + 256 * p, row = v >> 4, cg = v & 15;
+    for (int p = 0; p < 16; ++p) {
+        const int v = l + 64 * p, row = v >> 4, cg = v & 15;
         uint4 val = make_uint4(0, 0, 0, 0);
         if (row < len) val = *reinterpret_cast<const uint4*>(kp + ((t0 + row) * a.Hqk + hq) * FD + cg * 8);
-        *reinterpret_cast<uint4*>(&sm.K[row][cg * 8]) = val;
+        *reinterpret_cast<uint4*>(&sm.u.K[row][cg * 8]) = val;
+    }
+    {
+        const bool in = l < len;
+        const long idx = (t0 + l) * a.Hv + h;
+        float gv = (in && a.g) ? a.g[idx] : 0.f;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(gv, o);
+            if (l >= o) gv += y;
+        }
+        sm.gam[l] = gv;
+        sm.beta[l] = in ? a.beta[idx] : 0.f;
+    }
+    // T is zero above its block diagonal: those blocks of Tb, and the mirrored blocks
+    // (below the block diagonal) of the transposed copy TbT
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = l + 64 * p, r = v >> 3, cg = v & 7;  // 8 bf16 per store
+        if (cg * 8 >= ((r >> 4) + 1) * 16) *reinterpret_cast<bf16x8*>(&sm.Tb[r][cg * 8]) = zero8();
+        if (cg * 8 + 8 <= (r >> 4) * 16) *reinterpret_cast<bf16x8*>(&sm.TbT[r][cg * 8]) = zero8();
     }
     __syncthreads();
 
-    // K K^T, lower tiles (0,0), (1,0), (1,1) on waves 0..2
-    const int ta = wave == 0 ? 0 : 1, tb = wave == 2 ? 1 : 0;
-    f32x16 G = {};
-    if (wave < 3) {
-        const int ra = 32 * ta + (lane & 31), rb = 32 * tb + (lane & 31), ko = (lane >> 5) * 8;
+    // Gram K K^T: lower tiles (0,0), (1,0), (1,1) of 32x32
+    f32x16 G00 = {}, G10 = {}, G11 = {};
 #pragma unroll
-        for (int kk = 0; kk < FD / 16; ++kk)
-            G = mma32(ld8(&sm.K[ra][kk * 16 + ko]), ld8(&sm.K[rb][kk * 16 + ko]), G);
+    for (int kk = 0; kk < FD / 16; ++kk) {
+        const bf16x8 f0 = ld8(&sm.u.K[l32][kk * 16 + 8 * hi32]);
+        const bf16x8 f1 = ld8(&sm.u.K[32 + l32][kk * 16 + 8 * hi32]);
+        G00 = mma32(f0, f0, G00);
+        G10 = mma32(f1, f0, G10);
+        G11 = mma32(f1, f1, G11);
     }
-
-    for (int u = 0; u < R; ++u) {
-        const int h = hq * R + u;
-        if (tid < FC) {
-            const bool in = tid < len;
-            const long idx = (t0 + tid) * a.Hv + h;
-            float gv = (in && a.g) ? a.g[idx] : 0.f;
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(gv, o);
-                if (lane >= o) gv += y;
-            }
-            sm.gam[tid] = gv;
-            sm.beta[tid] = in ? a.beta[idx] : 0.f;
-        }
-        __syncthreads();
-        // A = strictly-lower beta/decay-weighted Gram; zero the tile above the diagonal
+    __syncthreads();  // K is overwritten below
+    // A_ri = beta_r exp(gamma_r - gamma_i) G_ri for i < r < len
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        const int ta = t == 0 ? 0 : 1, tb = t == 2 ? 1 : 0;
+        const f32x16& G = t == 0 ? G00 : (t == 1 ? G10 : G11);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), c = lane & 31;
-            if (wave < 3) {
-                const int r = 32 * ta + m, i = 32 * tb + c;
-                sm.A[r][i] = (i < r && r < len) ? sm.beta[r] * expf(sm.gam[r] - sm.gam[i]) * G[e] : 0.f;
-            } else {
-                sm.A[m][32 + c] = 0.f;
+            const int r = 32 * ta + 8 * (e >> 2) + 4 * hi32 + (e & 3), i = 32 * tb + l32;
+            const float av = (i < r && r < len) ? sm.beta[r] * expf(sm.gam[r] - sm.gam[i]) * G[e] : 0.f;
+            if ((r >> 4) == (i >> 4)) sm.u.a.Ad[r >> 4][r & 15][i & 15] = av;
+            sm.u.a.Ab[r][i] = (__bf16)av;
+        }
+    }
+    __syncthreads();
+
+    // diagonal blocks: lane = 16 * block + column; forward substitution down the column
+    {
+        const int b = q16, c = l16;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) {
+                if (m & 1) s1 += sm.u.a.Ad[b][r][m] * x[m];
+                else s0 += sm.u.a.Ad[b][r][m] * x[m];
             }
+            x[r] = (r == c) ? 1.f : (r < c ? 0.f : -(s0 + s1));
         }
-        // T's blocks above the block diagonal are zero
-        for (int e = tid; e < FC * FC; e += 256) {
-            const int r = e >> 6, i = e & 63;
-            if ((i >> 4) > (r >> 4)) sm.Tm[r][i] = 0.f;
+        bf16x8 lo8, hi8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo8[e] = (__bf16)x[e];
+            hi8[e] = (__bf16)x[8 + e];
         }
-        __syncthreads();
-        // diagonal 16x16 blocks of (I + A)^{-1}: forward substitution, one lane per column
-        if (wave == 0) {
-            const int base = 16 * (lane >> 4), c = lane & 15;
-            float x[16];
+        *reinterpret_cast<bf16x8*>(&sm.TbT[16 * b + c][16 * b]) = lo8;
+        *reinterpret_cast<bf16x8*>(&sm.TbT[16 * b + c][16 * b + 8]) = hi8;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = 0.f;
+        for (int r = 0; r < 16; ++r) sm.Tb[16 * b + r][16 * b + c] = (__bf16)x[r];
+    }
+    __syncthreads();
+
+    // level 1: within each 32x32 diagonal block, T21 = -T22 A21 T11 (16x16 blocks, k = 16
+    // padded to the instruction's 32 with zero lanes)
 #pragma unroll
-                for (int m = 0; m < r; ++m) s += sm.A[base + r][base + m] * x[m];
-                x[r] = (r == c) ? 1.f : (r < c ? 0.f : -s);
-            }
+    for (int base = 0; base < FC; base += 32) {
+        const bool live = q16 < 2;
+        bf16x8 af = live ? ld8(&sm.u.a.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
+        bf16x8 bf = live ? ld8(&sm.TbT[base + l16][base + 8 * q16]) : zero8();
+        f32x4 X = mma16(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        st4(&sm.XT[(base >> 1) + l16][4 * q16], X[0], X[1], X[2], X[3]);
+    }
+    __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Tm[base + r][base + c] = x[r];
-        }
-        __syncthreads();
-        // blocks below the diagonal, one block diagonal at a time:
-        // T_ij = -T_ii sum_{j <= m < i} A_im T_mj
-        for (int d = 1; d < 4; ++d) {
-            const int nb = 4 - d;
-            for (int e = tid; e < nb * 256; e += 256) {
-                const int j = e >> 8, i = j + d, r = (e >> 4) & 15, c = e & 15;
-                float s = 0.f;
-                for (int m = j; m < i; ++m)
+    for (int base = 0; base < FC; base += 32) {
+        const bool live = q16 < 2;
+        bf16x8 af = live ? ld8(&sm.Tb[base + 16 + l16][base + 16 + 8 * q16]) : zero8();
+        bf16x8 bf = live ? ld8(&sm.XT[(base >> 1) + l16][8 * q16]) : zero8();
+        f32x4 Y = mma16(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        const int r = base + 16 + 4 * q16, i = base + l16;
+        st4(&sm.TbT[i][r], -Y[0], -Y[1], -Y[2], -Y[3]);
 #pragma unroll
-                    for (int x = 0; x < 16; ++x) s += sm.A[16 * i + r][16 * m + x] * sm.Tm[16 * m + x][16 * j + c];
-                sm.X[j][r][c] = s;
-            }
-            __syncthreads();
-            for (int e = tid; e < nb * 256; e += 256) {
-                const int j = e >> 8, i = j + d, r = (e >> 4) & 15, c = e & 15;
-                float s = 0.f;
+        for (int e = 0; e < 4; ++e) sm.Tb[r + e][i] = (__bf16)(-Y[e]);
+    }
+    __syncthreads();
+    // level 2: T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32], 16x16 tiles
 #pragma unroll
-                for (int x = 0; x < 16; ++x) s += sm.Tm[16 * i + r][16 * i + x] * sm.X[j][x][c];
-                sm.Tm[16 * i + r][16 * j + c] = -s;
-            }
-            __syncthreads();
-        }
-        __bf16* tout = Tws + ((size_t)gc * a.Hv + h) * (FC * FC);
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tr = tt >> 1, tc = tt & 1;
+        f32x4 X = mma16(ld8(&sm.u.a.Ab[32 + 16 * tr + l16][8 * q16]), ld8(&sm.TbT[16 * tc + l16][8 * q16]),
+                        f32x4{0.f, 0.f, 0.f, 0.f});
+        st4(&sm.XT[16 * tc + l16][16 * tr + 4 * q16], X[0], X[1], X[2], X[3]);
+    }
+    __syncthreads();
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int v = tid + 256 * p, row = v >> 3, cg = v & 7;
-            bf16x8 val;
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tr = tt >> 1, tc = tt & 1;
+        f32x4 Y = mma16(ld8(&sm.Tb[32 + 16 * tr + l16][32 + 8 * q16]), ld8(&sm.XT[16 * tc + l16][8 * q16]),
+                        f32x4{0.f, 0.f, 0.f, 0.f});
+        const int r = 32 + 16 * tr + 4 * q16, i = 16 * tc + l16;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) val[e] = (__bf16)sm.Tm[row][cg * 8 + e];
-            *reinterpret_cast<bf16x8*>(tout + row * FC + cg * 8) = val;
-        }
-        __syncthreads();
+        for (int e = 0; e < 4; ++e) sm.Tb[r + e][i] = (__bf16)(-Y[e]);
+    }
+    __syncthreads();
+    __bf16* tout = Tws + ((size_t)gc * a.Hv + h) * (FC * FC);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = l + 64 * p, row = v >> 3, cg = v & 7;
+        *reinterpret_cast<bf16x8*>(tout + row * FC + cg * 8) = ld8(&sm.Tb[row][cg * 8]);
     }
 }
 
 // --------------------------------------------------------------------- state pass
-struct StateSmem {
+struct ChunkBuf {
     __bf16 K[FC][KPITCH];      // chunk keys, token-major
     __bf16 Q[FC][KPITCH];      // chunk queries, token-major
     __bf16 T[FC][CPITCH];      // (I + A)^{-1}
-    __bf16 P[FC][CPITCH];      // masked, decayed Q K^T
     __bf16 V[FC][VPITCH];      // value slice
-    __bf16 MbT[DVS][KPITCH];   // bf16 copy of the state slice, value-column-major
-    __bf16 RT[DVS][CPITCH];    // R, value-column-major
-    __bf16 DT[DVS][CPITCH];    // Delta, value-column-major
-    __bf16 DtT[DVS][CPITCH];   // Delta scaled by exp(gamma_last - gamma_r)
     float gam[FC];
     float beta[FC];
     float eg[FC];              // exp(gamma_r)
     float tail[FC];            // exp(gamma_last - gamma_r)
+};
+
+struct StateSmem {
+    ChunkBuf buf[2];           // chunk c in buf[c & 1]; the output waves stage chunk c + 1
+    __bf16 P[FC][CPITCH];      // masked, decayed Q K^T (row r = query token)
+    __bf16 MbT[DVS][KPITCH];   // bf16 copy of the state slice, value-column-major
+    __bf16 RT[DVS][CPITCH];    // R, value-column-major
+    __bf16 DT[DVS][CPITCH];    // Delta, value-column-major
+    __bf16 DtT[DVS][CPITCH];   // Delta scaled by exp(gamma_last - gamma_r)
 };
 
 struct Prefetch {
@@ -273,14 +325,15 @@ struct Prefetch {
     float beta, g;
 };
 
+// Output-wave thread pt (0..255) fetches its share of one chunk into registers.
 __device__ __forceinline__ void fetch_chunk(const PrefillArgs& a, const __bf16* Tchunk, long t0, int len,
-                                            int hq, int h, int j0, int tid, Prefetch& f) {
+                                            int hq, int h, int j0, int pt, Prefetch& f) {
     const __bf16* kp = static_cast<const __bf16*>(a.k);
     const __bf16* qp = static_cast<const __bf16*>(a.q);
     const __bf16* vp = static_cast<const __bf16*>(a.v);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int v = tid + 256 * p, row = v >> 4, cg = v & 15;
+        const int v = pt + 256 * p, row = v >> 4, cg = v & 15;
         f.k[p] = f.q[p] = make_uint4(0, 0, 0, 0);
         if (row < len) {
             const long off = ((t0 + row) * a.Hqk + hq) * FD + cg * 8;
@@ -289,29 +342,56 @@ __device__ __forceinline__ void fetch_chunk(const PrefillArgs& a, const __bf16* 
         }
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int v = tid + 256 * p;
-        f.t[p] = *reinterpret_cast<const uint4*>(Tchunk + v * 8);
-    }
+    for (int p = 0; p < 2; ++p) f.t[p] = *reinterpret_cast<const uint4*>(Tchunk + (pt + 256 * p) * 8);
     {
-        const int row = tid >> 2, cg = tid & 3;
+        const int row = pt >> 2, cg = pt & 3;
         f.v = make_uint4(0, 0, 0, 0);
         if (row < len) f.v = *reinterpret_cast<const uint4*>(vp + ((t0 + row) * a.Hv + h) * FD + j0 + cg * 8);
     }
     f.beta = 0.f;
     f.g = 0.f;
-    if (tid < FC && tid < len) {
-        const long idx = (t0 + tid) * a.Hv + h;
+    if (pt < FC && pt < len) {
+        const long idx = (t0 + pt) * a.Hv + h;
         f.beta = a.beta[idx];
         if (a.g) f.g = a.g[idx];
     }
 }
 
-__global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
+__device__ __forceinline__ void stage_chunk(ChunkBuf& cb, const Prefetch& f, int pt) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int v = pt + 256 * p, row = v >> 4, cg = v & 15;
+        *reinterpret_cast<uint4*>(&cb.K[row][cg * 8]) = f.k[p];
+        *reinterpret_cast<uint4*>(&cb.Q[row][cg * 8]) = f.q[p];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int v = pt + 256 * p, row = v >> 3, cg = v & 7;
+        *reinterpret_cast<uint4*>(&cb.T[row][cg * 8]) = f.t[p];
+    }
+    *reinterpret_cast<uint4*>(&cb.V[pt >> 2][(pt & 3) * 8]) = f.v;
+    if (pt < FC) {  // one wave: inclusive scan of the log decays over the chunk
+        float gv = f.g;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(gv, o);
+            if (pt >= o) gv += y;
+        }
+        const float glast = __shfl(gv, 63);
+        cb.gam[pt] = gv;
+        cb.beta[pt] = f.beta;
+        cb.eg[pt] = expf(gv);
+        cb.tail[pt] = expf(glast - gv);
+    }
+}
+
+__global__ __launch_bounds__(SNT) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
                                                     long nct) {
     __shared__ StateSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hi32 = lane >> 5;
+    const int l16 = lane & 15, q16 = lane >> 4;
+    const bool chain_wave = wave < 4;
+    const int w4 = wave & 3;          // index within the chain or the output group
+    const int pt = tid - 256;         // output-wave thread index
 
     // Workgroup -> (chain = sequence * Hv + head, slice).  When the chain count is a
     // multiple of 8, the slices of one chain land on one XCD (workgroups are dealt to
@@ -349,164 +429,216 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, const int32_t
     seq_range(a.cu, n, a.T, bos, eos);
     const int nchunks = (int)((eos - bos + FC - 1) / FC);
     const long gc0 = a.cu ? (long)off[n] : (long)n * nct;
+    const __bf16* Tseq = Tws + ((size_t)gc0 * a.Hv + h) * (FC * FC);
+    const size_t Tstride = (size_t)a.Hv * FC * FC;
 
-    // state slice rows 32*wave .. +31 (key index), columns j0 + l32 (value index)
-    f32x16 M;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int i = 32 * wave + 8 * (e >> 2) + 4 * hi32 + (e & 3);
-        M[e] = a.h0 ? a.h0[((long)nh * FD + i) * FD + j0 + l32] : 0.f;
-    }
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-        st4(&sm.MbT[l32][32 * wave + 8 * g4 + 4 * hi32], M[4 * g4], M[4 * g4 + 1], M[4 * g4 + 2], M[4 * g4 + 3]);
-
+    // Chain waves: state rows 32*w4 + 16*rt + 4*q16 + e, columns 16*ct + l16, as four
+    // 16x16 accumulator tiles M[rt][ct].
+    f32x4 M[2][2];
     Prefetch f;
-    if (nchunks > 0)
-        fetch_chunk(a, Tws + ((size_t)gc0 * a.Hv + h) * (FC * FC), bos, (int)min((long)FC, eos - bos),
-                    hq, h, j0, tid, f);
+    if (chain_wave) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int i = 32 * w4 + 16 * rt + 4 * q16, j = 16 * ct + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    M[rt][ct][e] = a.h0 ? a.h0[((long)nh * FD + i + e) * FD + j0 + j] : 0.f;
+                st4(&sm.MbT[j][i], M[rt][ct][0], M[rt][ct][1], M[rt][ct][2], M[rt][ct][3]);
+            }
+    } else {
+        // P above the diagonal stays zero for the whole sequence
+        for (int e = pt; e < FC * FC; e += 256) {
+            const int r = e >> 6, i = e & 63;
+            if (i > r) sm.P[r][i] = (__bf16)0.f;
+        }
+        if (nchunks > 0) {
+            fetch_chunk(a, Tseq, bos, (int)min((long)FC, eos - bos), hq, h, j0, pt, f);
+            stage_chunk(sm.buf[0], f, pt);
+        }
+        if (nchunks > 1) {
+            const long t1 = bos + FC;
+            fetch_chunk(a, Tseq + Tstride, t1, (int)min((long)FC, eos - t1), hq, h, j0, pt, f);
+        }
+    }
+    __syncthreads();
 
     for (int c = 0; c < nchunks; ++c) {
         const long t0 = bos + (long)c * FC;
         const int len = (int)min((long)FC, eos - t0);
-        // ---- stage the fetched chunk in LDS
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int v = tid + 256 * p, row = v >> 4, cg = v & 15;
-            *reinterpret_cast<uint4*>(&sm.K[row][cg * 8]) = f.k[p];
-            *reinterpret_cast<uint4*>(&sm.Q[row][cg * 8]) = f.q[p];
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int v = tid + 256 * p, row = v >> 3, cg = v & 7;
-            *reinterpret_cast<uint4*>(&sm.T[row][cg * 8]) = f.t[p];
-        }
-        *reinterpret_cast<uint4*>(&sm.V[tid >> 2][(tid & 3) * 8]) = f.v;
-        if (tid < FC) {
-            float gv = f.g;
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(gv, o);
-                if (lane >= o) gv += y;
-            }
-            const float glast = __shfl(gv, 63);
-            sm.gam[tid] = gv;
-            sm.beta[tid] = f.beta;
-            sm.eg[tid] = expf(gv);
-            sm.tail[tid] = expf(glast - gv);
-        }
-        __syncthreads();
-        if (c + 1 < nchunks) {
-            const long t1 = t0 + FC;
-            fetch_chunk(a, Tws + ((size_t)(gc0 + c + 1) * a.Hv + h) * (FC * FC), t1,
-                        (int)min((long)FC, eos - t1), hq, h, j0, tid, f);
-        }
+        ChunkBuf& cb = sm.buf[c & 1];
+        bf16x8 kcol[2][2];            // chain waves: K^T operand of the state update
+        f32x4 Y[2];                   // output waves: exp(gamma) Q M for rows 16*w4 + ...
 
-        // ---- phase A: X = [K; Q] M (waves 0,1: K rows, waves 2,3: Q rows) and P^T tiles
-        const int xr = 32 * (wave & 1) + l32;
-        const __bf16* xsrc = wave < 2 ? &sm.K[xr][0] : &sm.Q[xr][0];
-        f32x16 X = {};
+        // ================= phase A =================
+        {
+            // X = (K or Q) M for rows 16*w4 .. +15, both 16-column tiles
+            const __bf16* src = chain_wave ? &cb.K[16 * w4 + l16][0] : &cb.Q[16 * w4 + l16][0];
+            bf16x8 af[4], bf0[4], bf1[4];
 #pragma unroll
-        for (int kk = 0; kk < FD / 16; ++kk)
-            X = mma32(ld8(xsrc + kk * 16 + 8 * hi32), ld8(&sm.MbT[l32][kk * 16 + 8 * hi32]), X);
-        if (wave < 2) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int r = 32 * wave + 8 * g4 + 4 * hi32;
-                float rv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rv[e] = sm.beta[r + e] * ((float)sm.V[r + e][l32] - sm.eg[r + e] * X[4 * g4 + e]);
-                st4(&sm.RT[l32][r], rv[0], rv[1], rv[2], rv[3]);
+            for (int kk = 0; kk < 4; ++kk) {
+                af[kk] = ld8(src + 32 * kk + 8 * q16);
+                bf0[kk] = ld8(&sm.MbT[l16][32 * kk + 8 * q16]);
+                bf1[kk] = ld8(&sm.MbT[16 + l16][32 * kk + 8 * q16]);
             }
-        } else {
+            f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = 32 * (wave - 2) + 8 * (e >> 2) + 4 * hi32 + (e & 3);
-                X[e] *= sm.eg[r];
+            for (int kk = 0; kk < 4; ++kk) {
+                X0 = mma16(af[kk], bf0[kk], X0);
+                X1 = mma16(af[kk], bf1[kk], X1);
+            }
+            const int r = 16 * w4 + 4 * q16;
+            if (chain_wave) {
+                // K^T operand for phase C: A[i][k] = K[k][i], i = 32*w4 + 16*rt + l16
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            kcol[rt][kk][e] = cb.K[32 * kk + 8 * q16 + e][32 * w4 + 16 * rt + l16];
+                // R = beta (V - exp(gamma) X), stored value-column-major
+                float rv0[4], rv1[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bt = cb.beta[r + e], eg = cb.eg[r + e];
+                    rv0[e] = bt * ((float)cb.V[r + e][l16] - eg * X0[e]);
+                    rv1[e] = bt * ((float)cb.V[r + e][16 + l16] - eg * X1[e]);
+                }
+                st4(&sm.RT[l16][r], rv0[0], rv0[1], rv0[2], rv0[3]);
+                st4(&sm.RT[16 + l16][r], rv1[0], rv1[1], rv1[2], rv1[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float eg = cb.eg[r + e];
+                    Y[0][e] = eg * X0[e];
+                    Y[1][e] = eg * X1[e];
+                }
             }
         }
-        // P^T tile (ti, tr): rows = key token i, columns = query token r; tile (1,0) is zero
-        {
-            const int ti = wave == 2 ? 1 : 0, tr = wave == 0 ? 0 : 1;
-            f32x16 Pt = {};
-            if (wave < 3) {
+        if (!chain_wave) {
+            // P tiles (16x16, key token i below query token r); output wave w4 does
+            // tiles (ti, tr): w4=0: (0,0) (0,3) (1,3); 1: (0,1) (1,1) (2,3);
+            // 2: (0,2) (1,2) (2,2); 3: (3,3)
+            const int ntile = w4 == 3 ? 1 : 3;
 #pragma unroll
-                for (int kk = 0; kk < FD / 16; ++kk)
-                    Pt = mma32(ld8(&sm.K[32 * ti + l32][kk * 16 + 8 * hi32]),
-                               ld8(&sm.Q[32 * tr + l32][kk * 16 + 8 * hi32]), Pt);
-            }
-            const int r = (wave < 3 ? 32 * tr : 0) + l32;
+            for (int t = 0; t < 3; ++t) {
+                if (t >= ntile) break;
+                int ti, tr;
+                if (w4 == 0) { ti = t == 0 ? 0 : t - 1; tr = t == 0 ? 0 : 3; }
+                else if (w4 == 1) { ti = t == 2 ? 2 : t; tr = t == 2 ? 3 : 1; }
+                else if (w4 == 2) { ti = t; tr = 2; }
+                else { ti = 3; tr = 3; }
+                bf16x8 ka[4], qb[4];
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int i = (wave < 3 ? 32 * ti : 32) + 8 * g4 + 4 * hi32;
+                for (int kk = 0; kk < 4; ++kk) {
+                    ka[kk] = ld8(&cb.K[16 * ti + l16][32 * kk + 8 * q16]);
+                    qb[kk] = ld8(&cb.Q[16 * tr + l16][32 * kk + 8 * q16]);
+                }
+                f32x4 Pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) Pt = mma16(ka[kk], qb[kk], Pt);
+                // element e: key token i = 16 ti + 4 q16 + e, query token r = 16 tr + l16
+                const int i = 16 * ti + 4 * q16, r = 16 * tr + l16;
+                const float gr = cb.gam[r];
                 float pv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pv[e] = (wave < 3 && i + e <= r) ? expf(sm.gam[r] - sm.gam[i + e]) * Pt[4 * g4 + e] : 0.f;
+                for (int e = 0; e < 4; ++e) pv[e] = (i + e <= r) ? expf(gr - cb.gam[i + e]) * Pt[e] : 0.f;
                 st4(&sm.P[r][i], pv[0], pv[1], pv[2], pv[3]);
             }
         }
         __syncthreads();
 
-        // ---- phase B: Delta = T R, rows 16*wave .. +15, two 16-column tiles
-        {
-            const int l16 = lane & 15, q16 = lane >> 4;
-            f32x4 D0 = {}, D1 = {};
+        // ================= phase B =================
+        if (chain_wave) {
+            // Delta = T R for rows 16*w4 .. +15 (T is lower triangular: k < 16 (w4 + 1))
+            const int nk = w4 < 2 ? 1 : 2;
+            f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < FC / 32; ++kk) {
-                const bf16x8 ta = ld8(&sm.T[16 * wave + l16][kk * 32 + 8 * q16]);
-                D0 = mma16(ta, ld8(&sm.RT[l16][kk * 32 + 8 * q16]), D0);
-                D1 = mma16(ta, ld8(&sm.RT[16 + l16][kk * 32 + 8 * q16]), D1);
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk >= nk) break;
+                const bf16x8 ta = ld8(&cb.T[16 * w4 + l16][32 * kk + 8 * q16]);
+                const bf16x8 r0 = ld8(&sm.RT[l16][32 * kk + 8 * q16]);
+                const bf16x8 r1 = ld8(&sm.RT[16 + l16][32 * kk + 8 * q16]);
+                D0 = mma16(ta, r0, D0);
+                D1 = mma16(ta, r1, D1);
             }
-            const int r = 16 * wave + 4 * q16;
+            const int r = 16 * w4 + 4 * q16;
             st4(&sm.DT[l16][r], D0[0], D0[1], D0[2], D0[3]);
             st4(&sm.DT[16 + l16][r], D1[0], D1[1], D1[2], D1[3]);
-            st4(&sm.DtT[l16][r], sm.tail[r] * D0[0], sm.tail[r + 1] * D0[1], sm.tail[r + 2] * D0[2],
-                sm.tail[r + 3] * D0[3]);
-            st4(&sm.DtT[16 + l16][r], sm.tail[r] * D1[0], sm.tail[r + 1] * D1[1], sm.tail[r + 2] * D1[2],
-                sm.tail[r + 3] * D1[3]);
+            const float t0v = cb.tail[r], t1v = cb.tail[r + 1], t2v = cb.tail[r + 2], t3v = cb.tail[r + 3];
+            st4(&sm.DtT[l16][r], t0v * D0[0], t1v * D0[1], t2v * D0[2], t3v * D0[3]);
+            st4(&sm.DtT[16 + l16][r], t0v * D1[0], t1v * D1[1], t2v * D1[2], t3v * D1[3]);
+        } else if (c + 1 < nchunks) {
+            // stage chunk c + 1 into the other buffer, then fetch chunk c + 2
+            stage_chunk(sm.buf[(c + 1) & 1], f, pt);
+            if (c + 2 < nchunks) {
+                const long t2 = t0 + 2 * FC;
+                fetch_chunk(a, Tseq + (size_t)(c + 2) * Tstride, t2, (int)min((long)FC, eos - t2), hq, h, j0,
+                            pt, f);
+            }
         }
         __syncthreads();
 
-        // ---- phase C: carry M <- exp(gamma_last) M + K^T Delta~, and O = X + P Delta
-        {
-            const float Gl = sm.eg[FC - 1];  // rows past the chunk end add g = 0
+        // ================= phase C =================
+        if (chain_wave) {
+            // M <- exp(gamma_last) M + K^T Delta~   (rows past the chunk end add g = 0)
+            const float Gl = cb.eg[FC - 1];
+            bf16x8 db[2][2];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) M[e] *= Gl;
-            const int i = 32 * wave + l32;
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int kk = 0; kk < FC / 16; ++kk) {
-                bf16x8 ka;
+                for (int kk = 0; kk < 2; ++kk) db[ct][kk] = ld8(&sm.DtT[16 * ct + l16][32 * kk + 8 * q16]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ka[e] = sm.K[kk * 16 + 8 * hi32 + e][i];
-                M = mma32(ka, ld8(&sm.DtT[l32][kk * 16 + 8 * hi32]), M);
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    M[rt][ct] *= Gl;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) M[rt][ct] = mma16(kcol[rt][kk], db[ct][kk], M[rt][ct]);
+                }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    st4(&sm.MbT[16 * ct + l16][32 * w4 + 16 * rt + 4 * q16], M[rt][ct][0], M[rt][ct][1],
+                        M[rt][ct][2], M[rt][ct][3]);
+        } else {
+            // O = Y + P Delta for query rows 16*w4 .. +15 (P is lower triangular)
+            const int nk = w4 < 2 ? 1 : 2;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk >= nk) break;
+                const bf16x8 pa = ld8(&sm.P[16 * w4 + l16][32 * kk + 8 * q16]);
+                const bf16x8 d0 = ld8(&sm.DT[l16][32 * kk + 8 * q16]);
+                const bf16x8 d1 = ld8(&sm.DT[16 + l16][32 * kk + 8 * q16]);
+                Y[0] = mma16(pa, d0, Y[0]);
+                Y[1] = mma16(pa, d1, Y[1]);
             }
+            __bf16* op = static_cast<__bf16*>(a.o);
+            const int r = 16 * w4 + 4 * q16;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4)
-                st4(&sm.MbT[l32][32 * wave + 8 * g4 + 4 * hi32], M[4 * g4], M[4 * g4 + 1], M[4 * g4 + 2],
-                    M[4 * g4 + 3]);
-            if (wave >= 2) {
-                const int pr = 32 * (wave - 2) + l32;
-#pragma unroll
-                for (int kk = 0; kk < FC / 16; ++kk)
-                    X = mma32(ld8(&sm.P[pr][kk * 16 + 8 * hi32]), ld8(&sm.DT[l32][kk * 16 + 8 * hi32]), X);
-                __bf16* op = static_cast<__bf16*>(a.o);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int r = 32 * (wave - 2) + 8 * (e >> 2) + 4 * hi32 + (e & 3);
-                    if (r < len) op[((t0 + r) * a.Hv + h) * FD + j0 + l32] = (__bf16)(a.scale * X[e]);
+            for (int e = 0; e < 4; ++e) {
+                if (r + e < len) {
+                    __bf16* row = op + ((t0 + r + e) * a.Hv + h) * FD + j0;
+                    row[l16] = (__bf16)(a.scale * Y[0][e]);
+                    row[16 + l16] = (__bf16)(a.scale * Y[1][e]);
                 }
             }
         }
         __syncthreads();
     }
 
-    if (a.hT) {
+    if (chain_wave && a.hT) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = 32 * wave + 8 * (e >> 2) + 4 * hi32 + (e & 3);
-            a.hT[((long)nh * FD + i) * FD + j0 + l32] = M[e];
-        }
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int i = 32 * w4 + 16 * rt + 4 * q16, j = 16 * ct + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a.hT[((long)nh * FD + i + e) * FD + j0 + j] = M[rt][ct][e];
+            }
     }
 }
 
@@ -527,14 +659,14 @@ hipError_t launch_prefill_fast(const PrefillArgs& a, hipStream_t s) {
     const long nct = a.cu ? 0 : ((long)a.T + FC - 1) / FC;
     const long slots = a.cu ? slot_bound(a) : (long)a.B * nct;
     if (a.cu) hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(OFF_NT), 0, s, a.cu, a.N, off);
-    const long prep_blocks = slots * a.Hqk;
+    const long prep_blocks = slots * a.Hv;
     if (prep_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (prep_blocks > 0)
-        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, s, a, off, Tws, nct);
+        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(64), 0, s, a, off, Tws, nct);
     const long state_blocks = (long)a.N * a.Hv * NSL;
     if (state_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (state_blocks > 0)
-        hipLaunchKernelGGL(state_kernel, dim3((unsigned)state_blocks), dim3(256), 0, s, a, off, Tws, nct);
+        hipLaunchKernelGGL(state_kernel, dim3((unsigned)state_blocks), dim3(SNT), 0, s, a, off, Tws, nct);
     return hipGetLastError();
 }
 
