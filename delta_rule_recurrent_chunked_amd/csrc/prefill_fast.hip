@@ -71,6 +71,20 @@ __device__ __forceinline__ void st4(__bf16* p, float a, float b, float c, float 
     v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
     *reinterpret_cast<bf16x4*>(p) = v;
 }
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives
+// element i%4 of the 8-byte rows addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+// With lane s of the group addressing row base + s/4, column 4*(s%4) of a row-major tile,
+// lane i gets column i of rows base .. base+3: four consecutive rows of one column.
+__device__ __forceinline__ bf16x4 trld(const __bf16* p) {
+    typedef __bf16 v4bf16 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+    typedef __attribute__((address_space(3))) v4bf16 lds_v4bf16;
+    const v4bf16 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_v4bf16*)((__attribute__((address_space(3))) __bf16*)(p)));
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 __device__ __forceinline__ bf16x8 zero8() {
     bf16x8 z;
 #pragma unroll
@@ -139,22 +153,23 @@ __device__ __forceinline__ void locate_chunk(const PrefillArgs& a, const int32_t
 }
 
 // --------------------------------------------------------------------------- prep
-struct PrepSmem {
-    union {
-        __bf16 K[FC][KPITCH];              // the chunk's keys (until the Gram is formed)
-        struct {
-            __bf16 Ab[FC][CPITCH];         // A, bf16 (blocks below the diagonal)
-            float Ad[4][16][17];           // A's diagonal 16x16 blocks, fp32
-        } a;
-    } u;
-    __bf16 Tb[FC][CPITCH];                 // T row-major
-    __bf16 TbT[FC][CPITCH];                // T transposed (column-major)
-    __bf16 XT[32][40];                     // level products' intermediate, transposed
+// Per (chunk slot, value head) the workspace holds T^T and P, both 64 x 64 bf16:
+//   Tt[c][r] = T[r][c]   (T = (I + A)^{-1}, stored transposed)
+//   P[r][i]  = exp(gamma_r - gamma_i) q_r.k_i for i <= r < len, else 0 (rows past len: 0)
+constexpr int TP_ELEMS = 2 * FC * FC;
+
+struct alignas(16) PrepSmem {
+    __bf16 Ab[FC][CPITCH];     // A in bf16 (only the blocks below the diagonal are read)
+    float Ad[4][260];          // A's diagonal 16x16 blocks, fp32, row pitch 16, block pitch 260
+    __bf16 Tt[FC][CPITCH];     // T^T
+    __bf16 XT[32][40];         // level products' intermediate, transposed
     float gam[FC];
     float beta[FC];
 };
 
-// One wave = one (chunk slot, value head).
+// One wave = one (chunk slot, value head).  The Gram operands come straight from global
+// memory in MFMA layout (each key/query element is loaded once), so the only LDS traffic
+// is the small triangular solve.
 __global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* off, __bf16* Tws, long nct) {
     __shared__ PrepSmem sm;
     const int l = threadIdx.x;
@@ -167,13 +182,19 @@ __global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* 
     if (len <= 0) return;
     const int hq = h / (a.Hv / a.Hqk);
     const __bf16* kp = static_cast<const __bf16*>(a.k);
+    const __bf16* qp = static_cast<const __bf16*>(a.q);
 
+    // operand fragments: rows 32*rb + l32, columns 16*kk + 8*hi32 .. +7
+    bf16x8 kf[2][8], qf[2][8];
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        const int v = l + 64 * p, row = v >> 4, cg = v & 15;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (row < len) val = *reinterpret_cast<const uint4*>(kp + ((t0 + row) * a.Hqk + hq) * FD + cg * 8);
-        *reinterpret_cast<uint4*>(&sm.u.K[row][cg * 8]) = val;
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = 32 * rb + l32;
+        const long base = ((t0 + row) * a.Hqk + hq) * FD + 8 * hi32;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            kf[rb][kk] = row < len ? ld8(kp + base + 16 * kk) : zero8();
+            qf[rb][kk] = row < len ? ld8(qp + base + 16 * kk) : zero8();
+        }
     }
     {
         const bool in = l < len;
@@ -186,38 +207,70 @@ __global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* 
         sm.gam[l] = gv;
         sm.beta[l] = in ? a.beta[idx] : 0.f;
     }
-    // T is zero above its block diagonal: those blocks of Tb, and the mirrored blocks
-    // (below the block diagonal) of the transposed copy TbT
+    // T^T is zero where T is (above T's block diagonal): Tt blocks below the diagonal
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-        const int v = l + 64 * p, r = v >> 3, cg = v & 7;  // 8 bf16 per store
-        if (cg * 8 >= ((r >> 4) + 1) * 16) *reinterpret_cast<bf16x8*>(&sm.Tb[r][cg * 8]) = zero8();
-        if (cg * 8 + 8 <= (r >> 4) * 16) *reinterpret_cast<bf16x8*>(&sm.TbT[r][cg * 8]) = zero8();
+        const int v = l + 64 * p, r = v >> 3, cg = v & 7;
+        if (cg * 8 + 8 <= (r >> 4) * 16) *reinterpret_cast<bf16x8*>(&sm.Tt[r][cg * 8]) = zero8();
+    }
+
+    // K K^T tiles (0,0), (1,0), (1,1) and K Q^T tiles (key block, query block)
+    // (0,0), (0,1), (1,1): element e of tile (x, y) is row 32x + 8(e/4) + 4 hi32 + e%4,
+    // column 32y + l32
+    f32x16 G00 = {}, G10 = {}, G11 = {}, P00 = {}, P01 = {}, P11 = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        G00 = mma32(kf[0][kk], kf[0][kk], G00);
+        G10 = mma32(kf[1][kk], kf[0][kk], G10);
+        G11 = mma32(kf[1][kk], kf[1][kk], G11);
+        P00 = mma32(kf[0][kk], qf[0][kk], P00);
+        P01 = mma32(kf[0][kk], qf[1][kk], P01);
+        P11 = mma32(kf[1][kk], qf[1][kk], P11);
     }
     __syncthreads();
 
-    // Gram K K^T: lower tiles (0,0), (1,0), (1,1) of 32x32
-    f32x16 G00 = {}, G10 = {}, G11 = {};
-#pragma unroll
-    for (int kk = 0; kk < FD / 16; ++kk) {
-        const bf16x8 f0 = ld8(&sm.u.K[l32][kk * 16 + 8 * hi32]);
-        const bf16x8 f1 = ld8(&sm.u.K[32 + l32][kk * 16 + 8 * hi32]);
-        G00 = mma32(f0, f0, G00);
-        G10 = mma32(f1, f0, G10);
-        G11 = mma32(f1, f1, G11);
-    }
-    __syncthreads();  // K is overwritten below
-    // A_ri = beta_r exp(gamma_r - gamma_i) G_ri for i < r < len
+    // A_ri = beta_r exp(gamma_r - gamma_i) (k_r . k_i) for i < r < len
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
         const int ta = t == 0 ? 0 : 1, tb = t == 2 ? 1 : 0;
-        const f32x16& G = t == 0 ? G00 : (t == 1 ? G10 : G11);
+        const f32x16 G = t == 0 ? G00 : (t == 1 ? G10 : G11);
+        const int i = 32 * tb + l32;
+        const float gi = sm.gam[i];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = 32 * ta + 8 * (e >> 2) + 4 * hi32 + (e & 3), i = 32 * tb + l32;
-            const float av = (i < r && r < len) ? sm.beta[r] * expf(sm.gam[r] - sm.gam[i]) * G[e] : 0.f;
-            if ((r >> 4) == (i >> 4)) sm.u.a.Ad[r >> 4][r & 15][i & 15] = av;
-            sm.u.a.Ab[r][i] = (__bf16)av;
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int r0 = 32 * ta + 8 * g4 + 4 * hi32;
+            const float4 gr = *reinterpret_cast<const float4*>(&sm.gam[r0]);
+            const float4 br = *reinterpret_cast<const float4*>(&sm.beta[r0]);
+            const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + e;
+                const float av = (i < r && r < len) ? brv[e] * __expf(grv[e] - gi) * G[4 * g4 + e] : 0.f;
+                if ((r >> 4) == (i >> 4)) sm.Ad[r >> 4][(r & 15) * 16 + (i & 15)] = av;
+                sm.Ab[r][i] = (__bf16)av;
+            }
+        }
+    }
+    // P_ri = exp(gamma_r - gamma_i) (q_r . k_i) for i <= r < len, written row-major
+    {
+        __bf16* pout = Tws + ((size_t)gc * a.Hv + h) * TP_ELEMS + FC * FC;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int xa = t == 2 ? 1 : 0, yb = t == 0 ? 0 : 1;  // key block, query block
+            const f32x16 Pt = t == 0 ? P00 : (t == 1 ? P01 : P11);
+            const int r = 32 * yb + l32;
+            const float gr = sm.gam[r];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int i0 = 32 * xa + 8 * g4 + 4 * hi32;
+                const float4 gi = *reinterpret_cast<const float4*>(&sm.gam[i0]);
+                const float giv[4] = {gi.x, gi.y, gi.z, gi.w};
+                bf16x4 pv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pv[e] = (__bf16)((i0 + e <= r && r < len) ? __expf(gr - giv[e]) * Pt[4 * g4 + e] : 0.f);
+                *reinterpret_cast<bf16x4*>(pout + r * FC + i0) = pv;
+            }
         }
     }
     __syncthreads();
@@ -225,14 +278,23 @@ __global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* 
     // diagonal blocks: lane = 16 * block + column; forward substitution down the column
     {
         const int b = q16, c = l16;
+        const float* Ab_ = &sm.Ad[b][0];
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int m = 0; m < r; ++m) {
-                if (m & 1) s1 += sm.u.a.Ad[b][r][m] * x[m];
-                else s0 += sm.u.a.Ad[b][r][m] * x[m];
+            for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
+                const float4 av = *reinterpret_cast<const float4*>(Ab_ + r * 16 + 4 * m4);
+                const float avv[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int m = 4 * m4 + u;
+                    if (m < r) {
+                        if (u & 1) s1 += avv[u] * x[m];
+                        else s0 += avv[u] * x[m];
+                    }
+                }
             }
             x[r] = (r == c) ? 1.f : (r < c ? 0.f : -(s0 + s1));
         }
@@ -242,68 +304,67 @@ __global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* 
             lo8[e] = (__bf16)x[e];
             hi8[e] = (__bf16)x[8 + e];
         }
-        *reinterpret_cast<bf16x8*>(&sm.TbT[16 * b + c][16 * b]) = lo8;
-        *reinterpret_cast<bf16x8*>(&sm.TbT[16 * b + c][16 * b + 8]) = hi8;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Tb[16 * b + r][16 * b + c] = (__bf16)x[r];
+        *reinterpret_cast<bf16x8*>(&sm.Tt[16 * b + c][16 * b]) = lo8;
+        *reinterpret_cast<bf16x8*>(&sm.Tt[16 * b + c][16 * b + 8]) = hi8;
     }
     __syncthreads();
 
-    // level 1: within each 32x32 diagonal block, T21 = -T22 A21 T11 (16x16 blocks, k = 16
+    // level 1: within each 32x32 diagonal block, T21 = -T22 A21 T11 (16x16 blocks; k = 16
     // padded to the instruction's 32 with zero lanes)
+    const bool live = q16 < 2;
 #pragma unroll
     for (int base = 0; base < FC; base += 32) {
-        const bool live = q16 < 2;
-        bf16x8 af = live ? ld8(&sm.u.a.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
-        bf16x8 bf = live ? ld8(&sm.TbT[base + l16][base + 8 * q16]) : zero8();
-        f32x4 X = mma16(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        const bf16x8 af = live ? ld8(&sm.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
+        const bf16x8 bf = live ? ld8(&sm.Tt[base + l16][base + 8 * q16]) : zero8();
+        const f32x4 X = mma16(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
         st4(&sm.XT[(base >> 1) + l16][4 * q16], X[0], X[1], X[2], X[3]);
     }
     __syncthreads();
 #pragma unroll
     for (int base = 0; base < FC; base += 32) {
-        const bool live = q16 < 2;
-        bf16x8 af = live ? ld8(&sm.Tb[base + 16 + l16][base + 16 + 8 * q16]) : zero8();
-        bf16x8 bf = live ? ld8(&sm.XT[(base >> 1) + l16][8 * q16]) : zero8();
-        f32x4 Y = mma16(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-        const int r = base + 16 + 4 * q16, i = base + l16;
-        st4(&sm.TbT[i][r], -Y[0], -Y[1], -Y[2], -Y[3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Tb[r + e][i] = (__bf16)(-Y[e]);
+        // A operand T22[m][k] = Tt[base+16+k][base+16+m]: transposed read, k = 8 q16 + e
+        const int s = l16;   // groups 2,3 only pad k: keep their (unused) reads inside the tile
+        const __bf16* src = &sm.Tt[base + 16 + 8 * (q16 & 1) + (s >> 2)][base + 16 + 4 * (s & 3)];
+        bf16x8 af = cat(trld(src), trld(src + 4 * CPITCH));
+        if (!live) af = zero8();
+        const bf16x8 bf = live ? ld8(&sm.XT[(base >> 1) + l16][8 * q16]) : zero8();
+        const f32x4 Y = mma16(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        st4(&sm.Tt[base + l16][base + 16 + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
     }
     __syncthreads();
     // level 2: T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32], 16x16 tiles
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const int tr = tt >> 1, tc = tt & 1;
-        f32x4 X = mma16(ld8(&sm.u.a.Ab[32 + 16 * tr + l16][8 * q16]), ld8(&sm.TbT[16 * tc + l16][8 * q16]),
-                        f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 X = mma16(ld8(&sm.Ab[32 + 16 * tr + l16][8 * q16]), ld8(&sm.Tt[16 * tc + l16][8 * q16]),
+                              f32x4{0.f, 0.f, 0.f, 0.f});
         st4(&sm.XT[16 * tc + l16][16 * tr + 4 * q16], X[0], X[1], X[2], X[3]);
     }
     __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const int tr = tt >> 1, tc = tt & 1;
-        f32x4 Y = mma16(ld8(&sm.Tb[32 + 16 * tr + l16][32 + 8 * q16]), ld8(&sm.XT[16 * tc + l16][8 * q16]),
-                        f32x4{0.f, 0.f, 0.f, 0.f});
-        const int r = 32 + 16 * tr + 4 * q16, i = 16 * tc + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Tb[r + e][i] = (__bf16)(-Y[e]);
+        const int s = l16;
+        const __bf16* src = &sm.Tt[32 + 8 * q16 + (s >> 2)][32 + 16 * tr + 4 * (s & 3)];
+        const bf16x8 af = cat(trld(src), trld(src + 4 * CPITCH));
+        const f32x4 Y = mma16(af, ld8(&sm.XT[16 * tc + l16][8 * q16]), f32x4{0.f, 0.f, 0.f, 0.f});
+        st4(&sm.Tt[16 * tc + l16][32 + 16 * tr + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
     }
     __syncthreads();
-    __bf16* tout = Tws + ((size_t)gc * a.Hv + h) * (FC * FC);
+    __bf16* tout = Tws + ((size_t)gc * a.Hv + h) * TP_ELEMS;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int v = l + 64 * p, row = v >> 3, cg = v & 7;
-        *reinterpret_cast<bf16x8*>(tout + row * FC + cg * 8) = ld8(&sm.Tb[row][cg * 8]);
+        *reinterpret_cast<bf16x8*>(tout + row * FC + cg * 8) = ld8(&sm.Tt[row][cg * 8]);
     }
 }
 
 // --------------------------------------------------------------------- state pass
-struct ChunkBuf {
+struct alignas(16) ChunkBuf {
     __bf16 K[FC][KPITCH];      // chunk keys, token-major
     __bf16 Q[FC][KPITCH];      // chunk queries, token-major
-    __bf16 T[FC][CPITCH];      // (I + A)^{-1}
+    __bf16 Tt[FC][CPITCH];     // T^T
+    __bf16 P[FC][CPITCH];      // masked, decayed Q K^T, row r = query token
     __bf16 V[FC][VPITCH];      // value slice
     float gam[FC];
     float beta[FC];
@@ -311,9 +372,8 @@ struct ChunkBuf {
     float tail[FC];            // exp(gamma_last - gamma_r)
 };
 
-struct StateSmem {
-    ChunkBuf buf[2];           // chunk c in buf[c & 1]; the output waves stage chunk c + 1
-    __bf16 P[FC][CPITCH];      // masked, decayed Q K^T (row r = query token)
+struct alignas(16) StateSmem {
+    ChunkBuf buf[2];           // chunk c in buf[c & 1]; loader waves stage chunk c + 1
     __bf16 MbT[DVS][KPITCH];   // bf16 copy of the state slice, value-column-major
     __bf16 RT[DVS][CPITCH];    // R, value-column-major
     __bf16 DT[DVS][CPITCH];    // Delta, value-column-major
@@ -321,19 +381,19 @@ struct StateSmem {
 };
 
 struct Prefetch {
-    uint4 k[4], q[4], t[2], v;
+    uint4 k[4], q[4], t[2], p[2], v;
     float beta, g;
 };
 
-// Output-wave thread pt (0..255) fetches its share of one chunk into registers.
-__device__ __forceinline__ void fetch_chunk(const PrefillArgs& a, const __bf16* Tchunk, long t0, int len,
-                                            int hq, int h, int j0, int pt, Prefetch& f) {
+// Loader thread lt (0..255) fetches its share of one chunk into registers.
+__device__ __forceinline__ void fetch_chunk(const PrefillArgs& a, const __bf16* TP, long t0, int len, int hq,
+                                            int h, int j0, int lt, Prefetch& f) {
     const __bf16* kp = static_cast<const __bf16*>(a.k);
     const __bf16* qp = static_cast<const __bf16*>(a.q);
     const __bf16* vp = static_cast<const __bf16*>(a.v);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int v = pt + 256 * p, row = v >> 4, cg = v & 15;
+        const int v = lt + 256 * p, row = v >> 4, cg = v & 15;
         f.k[p] = f.q[p] = make_uint4(0, 0, 0, 0);
         if (row < len) {
             const long off = ((t0 + row) * a.Hqk + hq) * FD + cg * 8;
@@ -342,60 +402,68 @@ __device__ __forceinline__ void fetch_chunk(const PrefillArgs& a, const __bf16* 
         }
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) f.t[p] = *reinterpret_cast<const uint4*>(Tchunk + (pt + 256 * p) * 8);
+    for (int p = 0; p < 2; ++p) {
+        f.t[p] = *reinterpret_cast<const uint4*>(TP + (lt + 256 * p) * 8);
+        f.p[p] = *reinterpret_cast<const uint4*>(TP + FC * FC + (lt + 256 * p) * 8);
+    }
     {
-        const int row = pt >> 2, cg = pt & 3;
+        const int row = lt >> 2, cg = lt & 3;
         f.v = make_uint4(0, 0, 0, 0);
         if (row < len) f.v = *reinterpret_cast<const uint4*>(vp + ((t0 + row) * a.Hv + h) * FD + j0 + cg * 8);
     }
     f.beta = 0.f;
     f.g = 0.f;
-    if (pt < FC && pt < len) {
-        const long idx = (t0 + pt) * a.Hv + h;
+    if (lt < FC && lt < len) {
+        const long idx = (t0 + lt) * a.Hv + h;
         f.beta = a.beta[idx];
         if (a.g) f.g = a.g[idx];
     }
 }
 
-__device__ __forceinline__ void stage_chunk(ChunkBuf& cb, const Prefetch& f, int pt) {
+__device__ __forceinline__ void stage_chunk(ChunkBuf& cb, const Prefetch& f, int lt) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int v = pt + 256 * p, row = v >> 4, cg = v & 15;
+        const int v = lt + 256 * p, row = v >> 4, cg = v & 15;
         *reinterpret_cast<uint4*>(&cb.K[row][cg * 8]) = f.k[p];
         *reinterpret_cast<uint4*>(&cb.Q[row][cg * 8]) = f.q[p];
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const int v = pt + 256 * p, row = v >> 3, cg = v & 7;
-        *reinterpret_cast<uint4*>(&cb.T[row][cg * 8]) = f.t[p];
+        const int v = lt + 256 * p, row = v >> 3, cg = v & 7;
+        *reinterpret_cast<uint4*>(&cb.Tt[row][cg * 8]) = f.t[p];
+        *reinterpret_cast<uint4*>(&cb.P[row][cg * 8]) = f.p[p];
     }
-    *reinterpret_cast<uint4*>(&cb.V[pt >> 2][(pt & 3) * 8]) = f.v;
-    if (pt < FC) {  // one wave: inclusive scan of the log decays over the chunk
+    *reinterpret_cast<uint4*>(&cb.V[lt >> 2][(lt & 3) * 8]) = f.v;
+    if (lt < FC) {  // one wave: inclusive scan of the log decays over the chunk
         float gv = f.g;
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(gv, o);
-            if (pt >= o) gv += y;
+            if (lt >= o) gv += y;
         }
         const float glast = __shfl(gv, 63);
-        cb.gam[pt] = gv;
-        cb.beta[pt] = f.beta;
-        cb.eg[pt] = expf(gv);
-        cb.tail[pt] = expf(glast - gv);
+        cb.gam[lt] = gv;
+        cb.beta[lt] = f.beta;
+        cb.eg[lt] = __expf(gv);
+        cb.tail[lt] = __expf(glast - gv);
     }
 }
 
-__global__ __launch_bounds__(SNT) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
+// Wave roles (8 waves): 0,1 compute X = K M and R; 0..3 compute Delta and carry the state
+// (rows 32*w .. of the slice); 4,5 compute O^T = (Q M)^T + Delta^T P^T and store it;
+// 2,3,6,7 fetch and stage the next chunk.  Waves that fetch never store to global
+// memory inside the loop, so their waits on loads never wait on stores.
+__global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
                                                     long nct) {
     __shared__ StateSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, q16 = lane >> 4;
-    const bool chain_wave = wave < 4;
-    const int w4 = wave & 3;          // index within the chain or the output group
-    const int pt = tid - 256;         // output-wave thread index
+    const int l16 = lane & 15, q16 = lane >> 4, l32 = lane & 31, hi32 = lane >> 5;
+    const bool carry = wave < 4;                              // holds state rows 32*wave ..
+    const bool loader = wave == 2 || wave == 3 || wave >= 6;
+    const int lt = ((wave & 1) + (wave >= 6 ? 2 : 0)) * 64 + lane;   // loader thread index
 
     // Workgroup -> (chain = sequence * Hv + head, slice).  When the chain count is a
     // multiple of 8, the slices of one chain land on one XCD (workgroups are dealt to
-    // the 8 XCDs round-robin), so they share K, Q and T through that XCD's L2.
+    // the 8 XCDs round-robin), so they share K, Q, T and P through that XCD's L2.
     const int chains = a.N * a.Hv;
     const int b = blockIdx.x;
     int chain, slice;
@@ -429,37 +497,30 @@ __global__ __launch_bounds__(SNT) void state_kernel(PrefillArgs a, const int32_t
     seq_range(a.cu, n, a.T, bos, eos);
     const int nchunks = (int)((eos - bos + FC - 1) / FC);
     const long gc0 = a.cu ? (long)off[n] : (long)n * nct;
-    const __bf16* Tseq = Tws + ((size_t)gc0 * a.Hv + h) * (FC * FC);
-    const size_t Tstride = (size_t)a.Hv * FC * FC;
+    const __bf16* TPseq = Tws + ((size_t)gc0 * a.Hv + h) * TP_ELEMS;
+    const size_t TPstride = (size_t)a.Hv * TP_ELEMS;
 
-    // Chain waves: state rows 32*w4 + 16*rt + 4*q16 + e, columns 16*ct + l16, as four
-    // 16x16 accumulator tiles M[rt][ct].
-    f32x4 M[2][2];
+    // carry waves: state rows 32*wave + 8(e/4) + 4 hi32 + e%4, column l32 (one 32x32 tile)
+    f32x16 M = {};
     Prefetch f;
-    if (chain_wave) {
+    if (carry) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int i = 32 * w4 + 16 * rt + 4 * q16, j = 16 * ct + l16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    M[rt][ct][e] = a.h0 ? a.h0[((long)nh * FD + i + e) * FD + j0 + j] : 0.f;
-                st4(&sm.MbT[j][i], M[rt][ct][0], M[rt][ct][1], M[rt][ct][2], M[rt][ct][3]);
-            }
-    } else {
-        // P above the diagonal stays zero for the whole sequence
-        for (int e = pt; e < FC * FC; e += 256) {
-            const int r = e >> 6, i = e & 63;
-            if (i > r) sm.P[r][i] = (__bf16)0.f;
+        for (int e = 0; e < 16; ++e) {
+            const int i = 32 * wave + 8 * (e >> 2) + 4 * hi32 + (e & 3);
+            M[e] = a.h0 ? a.h0[((long)nh * FD + i) * FD + j0 + l32] : 0.f;
         }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+            st4(&sm.MbT[l32][32 * wave + 8 * g4 + 4 * hi32], M[4 * g4], M[4 * g4 + 1], M[4 * g4 + 2], M[4 * g4 + 3]);
+    }
+    if (loader) {
         if (nchunks > 0) {
-            fetch_chunk(a, Tseq, bos, (int)min((long)FC, eos - bos), hq, h, j0, pt, f);
-            stage_chunk(sm.buf[0], f, pt);
+            fetch_chunk(a, TPseq, bos, (int)min((long)FC, eos - bos), hq, h, j0, lt, f);
+            stage_chunk(sm.buf[0], f, lt);
         }
         if (nchunks > 1) {
             const long t1 = bos + FC;
-            fetch_chunk(a, Tseq + Tstride, t1, (int)min((long)FC, eos - t1), hq, h, j0, pt, f);
+            fetch_chunk(a, TPseq + TPstride, t1, (int)min((long)FC, eos - t1), hq, h, j0, lt, f);
         }
     }
     __syncthreads();
@@ -468,177 +529,121 @@ __global__ __launch_bounds__(SNT) void state_kernel(PrefillArgs a, const int32_t
         const long t0 = bos + (long)c * FC;
         const int len = (int)min((long)FC, eos - t0);
         ChunkBuf& cb = sm.buf[c & 1];
-        bf16x8 kcol[2][2];            // chain waves: K^T operand of the state update
-        f32x4 Y[2];                   // output waves: exp(gamma) Q M for rows 16*w4 + ...
+        bf16x8 kfr[4];    // carry waves: K^T operand of the state update, k-steps of 16 tokens
+        f32x16 Yt;        // output waves: (exp(gamma) Q M)^T, tokens 32*(wave-4) + l32
 
         // ================= phase A =================
-        {
-            // X = (K or Q) M for rows 16*w4 .. +15, both 16-column tiles
-            const __bf16* src = chain_wave ? &cb.K[16 * w4 + l16][0] : &cb.Q[16 * w4 + l16][0];
-            bf16x8 af[4], bf0[4], bf1[4];
+        if (wave < 2 || wave == 4 || wave == 5) {
+            const int t = wave & 1;
+            f32x16 X = {};
+            if (wave < 2) {
+                // X = K M for tokens 32t + ..: element e is token 32t + 8(e/4) + 4 hi32 + e%4, column l32
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                af[kk] = ld8(src + 32 * kk + 8 * q16);
-                bf0[kk] = ld8(&sm.MbT[l16][32 * kk + 8 * q16]);
-                bf1[kk] = ld8(&sm.MbT[16 + l16][32 * kk + 8 * q16]);
-            }
-            f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = {0.f, 0.f, 0.f, 0.f};
+                for (int kk = 0; kk < FD / 16; ++kk)
+                    X = mma32(ld8(&cb.K[32 * t + l32][16 * kk + 8 * hi32]), ld8(&sm.MbT[l32][16 * kk + 8 * hi32]), X);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                X0 = mma16(af[kk], bf0[kk], X0);
-                X1 = mma16(af[kk], bf1[kk], X1);
-            }
-            const int r = 16 * w4 + 4 * q16;
-            if (chain_wave) {
-                // K^T operand for phase C: A[i][k] = K[k][i], i = 32*w4 + 16*rt + l16
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            kcol[rt][kk][e] = cb.K[32 * kk + 8 * q16 + e][32 * w4 + 16 * rt + l16];
-                // R = beta (V - exp(gamma) X), stored value-column-major
-                float rv0[4], rv1[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float bt = cb.beta[r + e], eg = cb.eg[r + e];
-                    rv0[e] = bt * ((float)cb.V[r + e][l16] - eg * X0[e]);
-                    rv1[e] = bt * ((float)cb.V[r + e][16 + l16] - eg * X1[e]);
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int r = 32 * t + 8 * g4 + 4 * hi32;
+                    const float4 bt = *reinterpret_cast<const float4*>(&cb.beta[r]);
+                    const float4 eg = *reinterpret_cast<const float4*>(&cb.eg[r]);
+                    const bf16x4 vv = {cb.V[r][l32], cb.V[r + 1][l32], cb.V[r + 2][l32], cb.V[r + 3][l32]};
+                    st4(&sm.RT[l32][r], bt.x * ((float)vv[0] - eg.x * X[4 * g4]),
+                        bt.y * ((float)vv[1] - eg.y * X[4 * g4 + 1]), bt.z * ((float)vv[2] - eg.z * X[4 * g4 + 2]),
+                        bt.w * ((float)vv[3] - eg.w * X[4 * g4 + 3]));
                 }
-                st4(&sm.RT[l16][r], rv0[0], rv0[1], rv0[2], rv0[3]);
-                st4(&sm.RT[16 + l16][r], rv1[0], rv1[1], rv1[2], rv1[3]);
             } else {
+                // (Q M)^T: element e is state column 8(e/4) + 4 hi32 + e%4, token 32t + l32
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float eg = cb.eg[r + e];
-                    Y[0][e] = eg * X0[e];
-                    Y[1][e] = eg * X1[e];
-                }
+                for (int kk = 0; kk < FD / 16; ++kk)
+                    X = mma32(ld8(&sm.MbT[l32][16 * kk + 8 * hi32]), ld8(&cb.Q[32 * t + l32][16 * kk + 8 * hi32]), X);
+                const float eg = cb.eg[32 * t + l32];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Yt[e] = eg * X[e];
             }
         }
-        if (!chain_wave) {
-            // P tiles (16x16, key token i below query token r); output wave w4 does
-            // tiles (ti, tr): w4=0: (0,0) (0,3) (1,3); 1: (0,1) (1,1) (2,3);
-            // 2: (0,2) (1,2) (2,2); 3: (3,3)
-            const int ntile = w4 == 3 ? 1 : 3;
+        if (loader && c + 1 < nchunks) {
+            stage_chunk(sm.buf[(c + 1) & 1], f, lt);
+            if (c + 2 < nchunks) {
+                const long t2 = t0 + 2 * FC;
+                fetch_chunk(a, TPseq + (size_t)(c + 2) * TPstride, t2, (int)min((long)FC, eos - t2), hq, h, j0,
+                            lt, f);
+            }
+        }
+        if (carry) {
+            // K^T operand: A[i][k] = K[k][i] for i = 32 wave + l32, k = 16 kk + 8 hi32 + e,
+            // by transposed LDS reads (each 16-lane group: 16 key columns x 4 tokens)
+            const int grp = lane >> 4, s = l16;
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                if (t >= ntile) break;
-                int ti, tr;
-                if (w4 == 0) { ti = t == 0 ? 0 : t - 1; tr = t == 0 ? 0 : 3; }
-                else if (w4 == 1) { ti = t == 2 ? 2 : t; tr = t == 2 ? 3 : 1; }
-                else if (w4 == 2) { ti = t; tr = 2; }
-                else { ti = 3; tr = 3; }
-                bf16x8 ka[4], qb[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    ka[kk] = ld8(&cb.K[16 * ti + l16][32 * kk + 8 * q16]);
-                    qb[kk] = ld8(&cb.Q[16 * tr + l16][32 * kk + 8 * q16]);
-                }
-                f32x4 Pt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) Pt = mma16(ka[kk], qb[kk], Pt);
-                // element e: key token i = 16 ti + 4 q16 + e, query token r = 16 tr + l16
-                const int i = 16 * ti + 4 * q16, r = 16 * tr + l16;
-                const float gr = cb.gam[r];
-                float pv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pv[e] = (i + e <= r) ? expf(gr - cb.gam[i + e]) * Pt[e] : 0.f;
-                st4(&sm.P[r][i], pv[0], pv[1], pv[2], pv[3]);
+            for (int kk = 0; kk < 4; ++kk) {
+                const __bf16* src = &cb.K[16 * kk + 8 * (grp >> 1) + (s >> 2)][32 * wave + 16 * (grp & 1) + 4 * (s & 3)];
+                kfr[kk] = cat(trld(src), trld(src + 4 * KPITCH));
             }
         }
         __syncthreads();
 
         // ================= phase B =================
-        if (chain_wave) {
-            // Delta = T R for rows 16*w4 .. +15 (T is lower triangular: k < 16 (w4 + 1))
-            const int nk = w4 < 2 ? 1 : 2;
+        if (carry) {
+            // Delta = T R for tokens 16 wave .. +15 (T lower triangular: k < 16 (wave + 1))
+            const int nk = wave < 2 ? 1 : 2;
             f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+            const int s = l16;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 if (kk >= nk) break;
-                const bf16x8 ta = ld8(&cb.T[16 * w4 + l16][32 * kk + 8 * q16]);
-                const bf16x8 r0 = ld8(&sm.RT[l16][32 * kk + 8 * q16]);
-                const bf16x8 r1 = ld8(&sm.RT[16 + l16][32 * kk + 8 * q16]);
-                D0 = mma16(ta, r0, D0);
-                D1 = mma16(ta, r1, D1);
+                // A[m][k] = T[16 wave + m][k] = Tt[k][16 wave + m], k = 32 kk + 8 q16 + e
+                const __bf16* src = &cb.Tt[32 * kk + 8 * q16 + (s >> 2)][16 * wave + 4 * (s & 3)];
+                const bf16x8 ta = cat(trld(src), trld(src + 4 * CPITCH));
+                D0 = mma16(ta, ld8(&sm.RT[l16][32 * kk + 8 * q16]), D0);
+                D1 = mma16(ta, ld8(&sm.RT[16 + l16][32 * kk + 8 * q16]), D1);
             }
-            const int r = 16 * w4 + 4 * q16;
+            const int r = 16 * wave + 4 * q16;
             st4(&sm.DT[l16][r], D0[0], D0[1], D0[2], D0[3]);
             st4(&sm.DT[16 + l16][r], D1[0], D1[1], D1[2], D1[3]);
-            const float t0v = cb.tail[r], t1v = cb.tail[r + 1], t2v = cb.tail[r + 2], t3v = cb.tail[r + 3];
-            st4(&sm.DtT[l16][r], t0v * D0[0], t1v * D0[1], t2v * D0[2], t3v * D0[3]);
-            st4(&sm.DtT[16 + l16][r], t0v * D1[0], t1v * D1[1], t2v * D1[2], t3v * D1[3]);
-        } else if (c + 1 < nchunks) {
-            // stage chunk c + 1 into the other buffer, then fetch chunk c + 2
-            stage_chunk(sm.buf[(c + 1) & 1], f, pt);
-            if (c + 2 < nchunks) {
-                const long t2 = t0 + 2 * FC;
-                fetch_chunk(a, Tseq + (size_t)(c + 2) * Tstride, t2, (int)min((long)FC, eos - t2), hq, h, j0,
-                            pt, f);
-            }
+            const float4 tl = *reinterpret_cast<const float4*>(&cb.tail[r]);
+            st4(&sm.DtT[l16][r], tl.x * D0[0], tl.y * D0[1], tl.z * D0[2], tl.w * D0[3]);
+            st4(&sm.DtT[16 + l16][r], tl.x * D1[0], tl.y * D1[1], tl.z * D1[2], tl.w * D1[3]);
         }
         __syncthreads();
 
         // ================= phase C =================
-        if (chain_wave) {
+        if (carry) {
             // M <- exp(gamma_last) M + K^T Delta~   (rows past the chunk end add g = 0)
             const float Gl = cb.eg[FC - 1];
-            bf16x8 db[2][2];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int e = 0; e < 16; ++e) M[e] *= Gl;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) db[ct][kk] = ld8(&sm.DtT[16 * ct + l16][32 * kk + 8 * q16]);
+            for (int kk = 0; kk < 4; ++kk) M = mma32(kfr[kk], ld8(&sm.DtT[l32][16 * kk + 8 * hi32]), M);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int g4 = 0; g4 < 4; ++g4)
+                st4(&sm.MbT[l32][32 * wave + 8 * g4 + 4 * hi32], M[4 * g4], M[4 * g4 + 1], M[4 * g4 + 2],
+                    M[4 * g4 + 3]);
+        } else if (wave == 4 || wave == 5) {
+            // O^T = Y^T + Delta^T P^T for tokens 32t + l32 (P lower triangular)
+            const int t = wave & 1;
+            const int nk = t == 0 ? 2 : 4;
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    M[rt][ct] *= Gl;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) M[rt][ct] = mma16(kcol[rt][kk], db[ct][kk], M[rt][ct]);
-                }
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-                    st4(&sm.MbT[16 * ct + l16][32 * w4 + 16 * rt + 4 * q16], M[rt][ct][0], M[rt][ct][1],
-                        M[rt][ct][2], M[rt][ct][3]);
-        } else {
-            // O = Y + P Delta for query rows 16*w4 .. +15 (P is lower triangular)
-            const int nk = w4 < 2 ? 1 : 2;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
+            for (int kk = 0; kk < 4; ++kk) {
                 if (kk >= nk) break;
-                const bf16x8 pa = ld8(&sm.P[16 * w4 + l16][32 * kk + 8 * q16]);
-                const bf16x8 d0 = ld8(&sm.DT[l16][32 * kk + 8 * q16]);
-                const bf16x8 d1 = ld8(&sm.DT[16 + l16][32 * kk + 8 * q16]);
-                Y[0] = mma16(pa, d0, Y[0]);
-                Y[1] = mma16(pa, d1, Y[1]);
+                Yt = mma32(ld8(&sm.DT[l32][16 * kk + 8 * hi32]), ld8(&cb.P[32 * t + l32][16 * kk + 8 * hi32]), Yt);
             }
-            __bf16* op = static_cast<__bf16*>(a.o);
-            const int r = 16 * w4 + 4 * q16;
+            const int r = 32 * t + l32;
+            if (r < len) {
+                __bf16* row = static_cast<__bf16*>(a.o) + ((t0 + r) * a.Hv + h) * FD + j0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (r + e < len) {
-                    __bf16* row = op + ((t0 + r + e) * a.Hv + h) * FD + j0;
-                    row[l16] = (__bf16)(a.scale * Y[0][e]);
-                    row[16 + l16] = (__bf16)(a.scale * Y[1][e]);
-                }
+                for (int g4 = 0; g4 < 4; ++g4)
+                    st4(row + 8 * g4 + 4 * hi32, a.scale * Yt[4 * g4], a.scale * Yt[4 * g4 + 1],
+                        a.scale * Yt[4 * g4 + 2], a.scale * Yt[4 * g4 + 3]);
             }
         }
         __syncthreads();
     }
 
-    if (chain_wave && a.hT) {
+    if (carry && a.hT) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int i = 32 * w4 + 16 * rt + 4 * q16, j = 16 * ct + l16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a.hT[((long)nh * FD + i + e) * FD + j0 + j] = M[rt][ct][e];
-            }
+        for (int e = 0; e < 16; ++e) {
+            const int i = 32 * wave + 8 * (e >> 2) + 4 * hi32 + (e & 3);
+            a.hT[((long)nh * FD + i) * FD + j0 + l32] = M[e];
+        }
     }
 }
 
@@ -649,7 +654,7 @@ bool prefill_fast_supported(const PrefillArgs& a) {
 }
 
 size_t prefill_fast_workspace_bytes(const PrefillArgs& a) {
-    return offsets_bytes(a) + (size_t)slot_bound(a) * a.Hv * FC * FC * sizeof(__bf16);
+    return offsets_bytes(a) + (size_t)slot_bound(a) * a.Hv * 2 * FC * FC * sizeof(__bf16);
 }
 
 hipError_t launch_prefill_fast(const PrefillArgs& a, hipStream_t s) {
