@@ -373,11 +373,11 @@ struct alignas(16) ChunkBuf {
 };
 
 struct alignas(16) StateSmem {
-    ChunkBuf buf[2];           // chunk c in buf[c & 1]; loader waves stage chunk c + 1
-    __bf16 MbT[DVS][KPITCH];   // bf16 copy of the state slice, value-column-major
+    ChunkBuf buf[2];           // chunk c in buf[c & 1]; the loader waves stage chunk c + 1
+    __bf16 MbT[DVS][KPITCH];   // bf16 state at the chunk start, value-column-major
     __bf16 RT[DVS][CPITCH];    // R, value-column-major
-    __bf16 DT[DVS][CPITCH];    // Delta, value-column-major
-    __bf16 DtT[DVS][CPITCH];   // Delta scaled by exp(gamma_last - gamma_r)
+    __bf16 DtT[DVS][CPITCH];   // Delta scaled by exp(gamma_last - gamma_r), value-column-major
+    __bf16 DT[DVS][CPITCH];    // Delta, value-column-major (read by the output waves)
 };
 
 struct Prefetch {
@@ -448,18 +448,31 @@ __device__ __forceinline__ void stage_chunk(ChunkBuf& cb, const Prefetch& f, int
     }
 }
 
-// Wave roles (8 waves): 0,1 compute X = K M and R; 0..3 compute Delta and carry the state
-// (rows 32*w .. of the slice); 4,5 compute O^T = (Q M)^T + Delta^T P^T and store it;
-// 2,3,6,7 fetch and stage the next chunk.  Waves that fetch never store to global
-// memory inside the loop, so their waits on loads never wait on stores.
+// Orders this wave's LDS writes before its later LDS reads of the same data (LDS executes
+// one wave's instructions in order; this only stops the compiler from reordering them).
+__device__ __forceinline__ void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
+
+// Wave roles (8 waves, two workgroup barriers per chunk):
+//   0,1  chain waves: each carries 16 columns of the state slice (128 x 16 fp32, eight
+//        16x16 accumulator tiles) and runs the whole recurrence for them: X = K M, R,
+//        Delta = T R and M <- exp(gamma_last) M + K^T Delta~.  Their operands that come
+//        from their own results pass through LDS within the wave only (no barrier).
+//   2,3  output waves: tokens 32*(w-2) ..: O^T = (exp(gamma) Q M)^T + Delta^T P^T.
+//   4..7 loader waves: fetch the chunk after next into registers and stage the next chunk
+//        into the other LDS buffer.  They never store to global memory in the loop, so
+//        their waits on loads never wait on stores.
+// Per chunk: phase 1 = chain (X, R, Delta) + loaders; phase 2 = chain (state update) +
+// output waves (Q M, O).
 __global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
-                                                    long nct) {
+                                                       long nct) {
     __shared__ StateSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q16 = lane >> 4, l32 = lane & 31, hi32 = lane >> 5;
-    const bool carry = wave < 4;                              // holds state rows 32*wave ..
-    const bool loader = wave == 2 || wave == 3 || wave >= 6;
-    const int lt = ((wave & 1) + (wave >= 6 ? 2 : 0)) * 64 + lane;   // loader thread index
+    const bool chainw = wave < 2;
+    const bool outw = wave == 2 || wave == 3;
+    const bool loader = wave >= 4;
+    const int lt = tid - 256;                               // loader thread index
+    const int jc = 16 * wave;                               // chain wave: first column
 
     // Workgroup -> (chain = sequence * Hv + head, slice).  When the chain count is a
     // multiple of 8, the slices of one chain land on one XCD (workgroups are dealt to
@@ -500,18 +513,17 @@ __global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int3
     const __bf16* TPseq = Tws + ((size_t)gc0 * a.Hv + h) * TP_ELEMS;
     const size_t TPstride = (size_t)a.Hv * TP_ELEMS;
 
-    // carry waves: state rows 32*wave + 8(e/4) + 4 hi32 + e%4, column l32 (one 32x32 tile)
-    f32x16 M = {};
+    // chain waves: tile mt holds keys 16 mt + 4 q16 + e, column jc + l16 of the slice
+    f32x4 M[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     Prefetch f;
-    if (carry) {
+    if (chainw && a.h0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = 32 * wave + 8 * (e >> 2) + 4 * hi32 + (e & 3);
-            M[e] = a.h0 ? a.h0[((long)nh * FD + i) * FD + j0 + l32] : 0.f;
-        }
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-            st4(&sm.MbT[l32][32 * wave + 8 * g4 + 4 * hi32], M[4 * g4], M[4 * g4 + 1], M[4 * g4 + 2], M[4 * g4 + 3]);
+            for (int e = 0; e < 4; ++e)
+                M[mt][e] = a.h0[((long)nh * FD + 16 * mt + 4 * q16 + e) * FD + j0 + jc + l16];
     }
     if (loader) {
         if (nchunks > 0) {
@@ -529,39 +541,62 @@ __global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int3
         const long t0 = bos + (long)c * FC;
         const int len = (int)min((long)FC, eos - t0);
         ChunkBuf& cb = sm.buf[c & 1];
-        bf16x8 kfr[4];    // carry waves: K^T operand of the state update, k-steps of 16 tokens
-        f32x16 Yt;        // output waves: (exp(gamma) Q M)^T, tokens 32*(wave-4) + l32
 
-        // ================= phase A =================
-        if (wave < 2 || wave == 4 || wave == 5) {
-            const int t = wave & 1;
-            f32x16 X = {};
-            if (wave < 2) {
-                // X = K M for tokens 32t + ..: element e is token 32t + 8(e/4) + 4 hi32 + e%4, column l32
+        // ================= phase 1 =================
+        if (chainw) {
+            // this chunk's starting state, bf16, for X = K M here and (Q M)^T in phase 2
 #pragma unroll
-                for (int kk = 0; kk < FD / 16; ++kk)
-                    X = mma32(ld8(&cb.K[32 * t + l32][16 * kk + 8 * hi32]), ld8(&sm.MbT[l32][16 * kk + 8 * hi32]), X);
+            for (int mt = 0; mt < 8; ++mt)
+                st4(&sm.MbT[jc + l16][16 * mt + 4 * q16], M[mt][0], M[mt][1], M[mt][2], M[mt][3]);
+            wave_lds_order();
+            bf16x8 mb[4];
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int r = 32 * t + 8 * g4 + 4 * hi32;
-                    const float4 bt = *reinterpret_cast<const float4*>(&cb.beta[r]);
-                    const float4 eg = *reinterpret_cast<const float4*>(&cb.eg[r]);
-                    const bf16x4 vv = {cb.V[r][l32], cb.V[r + 1][l32], cb.V[r + 2][l32], cb.V[r + 3][l32]};
-                    st4(&sm.RT[l32][r], bt.x * ((float)vv[0] - eg.x * X[4 * g4]),
-                        bt.y * ((float)vv[1] - eg.y * X[4 * g4 + 1]), bt.z * ((float)vv[2] - eg.z * X[4 * g4 + 2]),
-                        bt.w * ((float)vv[3] - eg.w * X[4 * g4 + 3]));
-                }
-            } else {
-                // (Q M)^T: element e is state column 8(e/4) + 4 hi32 + e%4, token 32t + l32
+            for (int kk = 0; kk < 4; ++kk) mb[kk] = ld8(&sm.MbT[jc + l16][32 * kk + 8 * q16]);
+            // X = K M: token tile t, element e = token 16 t + 4 q16 + e, column jc + l16
+            f32x4 X[4];
 #pragma unroll
-                for (int kk = 0; kk < FD / 16; ++kk)
-                    X = mma32(ld8(&sm.MbT[l32][16 * kk + 8 * hi32]), ld8(&cb.Q[32 * t + l32][16 * kk + 8 * hi32]), X);
-                const float eg = cb.eg[32 * t + l32];
+            for (int t = 0; t < 4; ++t) {
+                bf16x8 ka[4];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Yt[e] = eg * X[e];
+                for (int kk = 0; kk < 4; ++kk) ka[kk] = ld8(&cb.K[16 * t + l16][32 * kk + 8 * q16]);
+                X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) X[t] = mma16(ka[kk], mb[kk], X[t]);
             }
-        }
-        if (loader && c + 1 < nchunks) {
+            // R = beta (V - exp(gamma) X), value-column-major
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * t + 4 * q16;
+                const float4 bt = *reinterpret_cast<const float4*>(&cb.beta[r]);
+                const float4 eg = *reinterpret_cast<const float4*>(&cb.eg[r]);
+                const int col = jc + l16;
+                st4(&sm.RT[col][r], bt.x * ((float)cb.V[r][col] - eg.x * X[t][0]),
+                    bt.y * ((float)cb.V[r + 1][col] - eg.y * X[t][1]),
+                    bt.z * ((float)cb.V[r + 2][col] - eg.z * X[t][2]),
+                    bt.w * ((float)cb.V[r + 3][col] - eg.w * X[t][3]));
+            }
+            wave_lds_order();
+            bf16x8 rb[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) rb[kk] = ld8(&sm.RT[jc + l16][32 * kk + 8 * q16]);
+            // Delta = T R: token tile a (T lower triangular: k < 16 (a + 1)); A operand
+            // T[16a + m][k] = Tt[k][16a + m] by transposed reads
+            const int s = l16;
+#pragma unroll
+            for (int at = 0; at < 4; ++at) {
+                f32x4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (kk == 1 && at < 2) break;
+                    const __bf16* src = &cb.Tt[32 * kk + 8 * q16 + (s >> 2)][16 * at + 4 * (s & 3)];
+                    D = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb[kk], D);
+                }
+                const int r = 16 * at + 4 * q16;
+                const float4 tl = *reinterpret_cast<const float4*>(&cb.tail[r]);
+                st4(&sm.DT[jc + l16][r], D[0], D[1], D[2], D[3]);
+                st4(&sm.DtT[jc + l16][r], tl.x * D[0], tl.y * D[1], tl.z * D[2], tl.w * D[3]);
+            }
+        } else if (loader && c + 1 < nchunks) {
             stage_chunk(sm.buf[(c + 1) & 1], f, lt);
             if (c + 2 < nchunks) {
                 const long t2 = t0 + 2 * FC;
@@ -569,81 +604,64 @@ __global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int3
                             lt, f);
             }
         }
-        if (carry) {
-            // K^T operand: A[i][k] = K[k][i] for i = 32 wave + l32, k = 16 kk + 8 hi32 + e,
-            // by transposed LDS reads (each 16-lane group: 16 key columns x 4 tokens)
-            const int grp = lane >> 4, s = l16;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const __bf16* src = &cb.K[16 * kk + 8 * (grp >> 1) + (s >> 2)][32 * wave + 16 * (grp & 1) + 4 * (s & 3)];
-                kfr[kk] = cat(trld(src), trld(src + 4 * KPITCH));
-            }
-        }
         __syncthreads();
 
-        // ================= phase B =================
-        if (carry) {
-            // Delta = T R for tokens 16 wave .. +15 (T lower triangular: k < 16 (wave + 1))
-            const int nk = wave < 2 ? 1 : 2;
-            f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+        // ================= phase 2 =================
+        if (chainw) {
+            // M <- exp(gamma_last) M + K^T Delta~  (rows past the chunk end add g = 0)
+            bf16x8 db[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) db[kk] = ld8(&sm.DtT[jc + l16][32 * kk + 8 * q16]);
+            const float Gl = cb.eg[FC - 1];
             const int s = l16;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk >= nk) break;
-                // A[m][k] = T[16 wave + m][k] = Tt[k][16 wave + m], k = 32 kk + 8 q16 + e
-                const __bf16* src = &cb.Tt[32 * kk + 8 * q16 + (s >> 2)][16 * wave + 4 * (s & 3)];
-                const bf16x8 ta = cat(trld(src), trld(src + 4 * CPITCH));
-                D0 = mma16(ta, ld8(&sm.RT[l16][32 * kk + 8 * q16]), D0);
-                D1 = mma16(ta, ld8(&sm.RT[16 + l16][32 * kk + 8 * q16]), D1);
+            for (int mt = 0; mt < 8; ++mt) {
+                // A operand K^T[16 mt + m][k] = K[k][16 mt + m], k = 32 kk + 8 q16 + e
+                bf16x8 kt[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const __bf16* src = &cb.K[32 * kk + 8 * q16 + (s >> 2)][16 * mt + 4 * (s & 3)];
+                    kt[kk] = cat(trld(src), trld(src + 4 * KPITCH));
+                }
+                if (a.g) M[mt] *= Gl;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) M[mt] = mma16(kt[kk], db[kk], M[mt]);
             }
-            const int r = 16 * wave + 4 * q16;
-            st4(&sm.DT[l16][r], D0[0], D0[1], D0[2], D0[3]);
-            st4(&sm.DT[16 + l16][r], D1[0], D1[1], D1[2], D1[3]);
-            const float4 tl = *reinterpret_cast<const float4*>(&cb.tail[r]);
-            st4(&sm.DtT[l16][r], tl.x * D0[0], tl.y * D0[1], tl.z * D0[2], tl.w * D0[3]);
-            st4(&sm.DtT[16 + l16][r], tl.x * D1[0], tl.y * D1[1], tl.z * D1[2], tl.w * D1[3]);
-        }
-        __syncthreads();
-
-        // ================= phase C =================
-        if (carry) {
-            // M <- exp(gamma_last) M + K^T Delta~   (rows past the chunk end add g = 0)
-            const float Gl = cb.eg[FC - 1];
+        } else if (outw) {
+            // (Q M)^T and O^T = (exp(gamma) Q M)^T + Delta^T P^T for tokens 32u + l32;
+            // element e: state column 8(e/4) + 4 hi32 + e%4
+            const int u = wave - 2;
+            f32x16 Y = {};
 #pragma unroll
-            for (int e = 0; e < 16; ++e) M[e] *= Gl;
+            for (int kk = 0; kk < FD / 16; ++kk)
+                Y = mma32(ld8(&sm.MbT[l32][16 * kk + 8 * hi32]), ld8(&cb.Q[32 * u + l32][16 * kk + 8 * hi32]), Y);
+            const float eg = cb.eg[32 * u + l32];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) M = mma32(kfr[kk], ld8(&sm.DtT[l32][16 * kk + 8 * hi32]), M);
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4)
-                st4(&sm.MbT[l32][32 * wave + 8 * g4 + 4 * hi32], M[4 * g4], M[4 * g4 + 1], M[4 * g4 + 2],
-                    M[4 * g4 + 3]);
-        } else if (wave == 4 || wave == 5) {
-            // O^T = Y^T + Delta^T P^T for tokens 32t + l32 (P lower triangular)
-            const int t = wave & 1;
-            const int nk = t == 0 ? 2 : 4;
+            for (int e = 0; e < 16; ++e) Y[e] *= eg;
+            const int nk = u == 0 ? 2 : 4;   // P is lower triangular
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 if (kk >= nk) break;
-                Yt = mma32(ld8(&sm.DT[l32][16 * kk + 8 * hi32]), ld8(&cb.P[32 * t + l32][16 * kk + 8 * hi32]), Yt);
+                Y = mma32(ld8(&sm.DT[l32][16 * kk + 8 * hi32]), ld8(&cb.P[32 * u + l32][16 * kk + 8 * hi32]), Y);
             }
-            const int r = 32 * t + l32;
+            const int r = 32 * u + l32;
             if (r < len) {
                 __bf16* row = static_cast<__bf16*>(a.o) + ((t0 + r) * a.Hv + h) * FD + j0;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
-                    st4(row + 8 * g4 + 4 * hi32, a.scale * Yt[4 * g4], a.scale * Yt[4 * g4 + 1],
-                        a.scale * Yt[4 * g4 + 2], a.scale * Yt[4 * g4 + 3]);
+                    st4(row + 8 * g4 + 4 * hi32, a.scale * Y[4 * g4], a.scale * Y[4 * g4 + 1],
+                        a.scale * Y[4 * g4 + 2], a.scale * Y[4 * g4 + 3]);
             }
         }
         __syncthreads();
     }
 
-    if (carry && a.hT) {
+    if (chainw && a.hT) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = 32 * wave + 8 * (e >> 2) + 4 * hi32 + (e & 3);
-            a.hT[((long)nh * FD + i) * FD + j0 + l32] = M[e];
-        }
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.hT[((long)nh * FD + 16 * mt + 4 * q16 + e) * FD + j0 + jc + l16] = M[mt][e];
     }
 }
 
