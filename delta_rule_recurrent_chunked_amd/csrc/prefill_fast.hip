@@ -40,6 +40,8 @@
 // Every operand is read from LDS as 8 consecutive bf16 along the contraction index, so
 // each operand is stored contraction-contiguous; the matrices produced here (state copy,
 // R, Delta, T's transposed copy) are written in the layout their consumer reads.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace dn {
@@ -52,7 +54,6 @@ constexpr int NSL = FD / DVS;      // slices per (sequence, value head)
 constexpr int KPITCH = FD + 8;     // bf16 row pitches: 16-byte multiples that put the
 constexpr int CPITCH = FC + 8;     //   16 rows of one MFMA operand read on distinct banks
 constexpr int VPITCH = DVS + 8;
-constexpr int SNT = 512;           // state-pass threads (8 waves)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -360,24 +361,25 @@ __global__ __launch_bounds__(64) void prep_kernel(PrefillArgs a, const int32_t* 
 }
 
 // --------------------------------------------------------------------- state pass
+constexpr int CW = 16;              // state columns per chain wave
+constexpr int NCW = DVS / CW;       // chain waves per workgroup
+constexpr int NLW = 4;              // loader waves per workgroup
+constexpr int SNT = 64 * (NCW + NLW);
+
 struct alignas(16) ChunkBuf {
     __bf16 K[FC][KPITCH];      // chunk keys, token-major
     __bf16 Q[FC][KPITCH];      // chunk queries, token-major
     __bf16 Tt[FC][CPITCH];     // T^T
     __bf16 P[FC][CPITCH];      // masked, decayed Q K^T, row r = query token
-    __bf16 V[FC][VPITCH];      // value slice
-    float gam[FC];
+    __bf16 V[FC][VPITCH];      // value slice, token-major
     float beta[FC];
     float eg[FC];              // exp(gamma_r)
     float tail[FC];            // exp(gamma_last - gamma_r)
 };
 
 struct alignas(16) StateSmem {
-    ChunkBuf buf[2];           // chunk c in buf[c & 1]; the loader waves stage chunk c + 1
-    __bf16 MbT[DVS][KPITCH];   // bf16 state at the chunk start, value-column-major
-    __bf16 RT[DVS][CPITCH];    // R, value-column-major
-    __bf16 DtT[DVS][CPITCH];   // Delta scaled by exp(gamma_last - gamma_r), value-column-major
-    __bf16 DT[DVS][CPITCH];    // Delta, value-column-major (read by the output waves)
+    ChunkBuf buf[2];              // chunk c in buf[c & 1]; the loader waves stage chunk c + 1
+    __bf16 OT[NCW][CW][CPITCH];   // per chain wave: its output tile, column-major
 };
 
 struct Prefetch {
@@ -441,7 +443,6 @@ __device__ __forceinline__ void stage_chunk(ChunkBuf& cb, const Prefetch& f, int
             if (lt >= o) gv += y;
         }
         const float glast = __shfl(gv, 63);
-        cb.gam[lt] = gv;
         cb.beta[lt] = f.beta;
         cb.eg[lt] = __expf(gv);
         cb.tail[lt] = __expf(glast - gv);
@@ -452,27 +453,45 @@ __device__ __forceinline__ void stage_chunk(ChunkBuf& cb, const Prefetch& f, int
 // one wave's instructions in order; this only stops the compiler from reordering them).
 __device__ __forceinline__ void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
 
-// Wave roles (8 waves, two workgroup barriers per chunk):
-//   0,1  chain waves: each carries 16 columns of the state slice (128 x 16 fp32, eight
-//        16x16 accumulator tiles) and runs the whole recurrence for them: X = K M, R,
-//        Delta = T R and M <- exp(gamma_last) M + K^T Delta~.  Their operands that come
-//        from their own results pass through LDS within the wave only (no barrier).
-//   2,3  output waves: tokens 32*(w-2) ..: O^T = (exp(gamma) Q M)^T + Delta^T P^T.
-//   4..7 loader waves: fetch the chunk after next into registers and stage the next chunk
-//        into the other LDS buffer.  They never store to global memory in the loop, so
-//        their waits on loads never wait on stores.
-// Per chunk: phase 1 = chain (X, R, Delta) + loaders; phase 2 = chain (state update) +
-// output waves (Q M, O).
-__global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// Two 16x16 accumulator tiles a (rows 0..15) and b (rows 16..31) of one 32-row block, as
+// the B operand of a 16x16x32 MFMA contracting over those 32 rows.  Lane group g = l/16
+// holds rows 4g..4g+3 of each tile and needs rows 8g..8g+7 of the block: a swap of lane
+// halves between a and b, then of odd and even 16-lane rows, routes each 4-row piece to
+// its lane (v_permlane32_swap / v_permlane16_swap), with no trip through LDS.
+__device__ __forceinline__ bf16x8 acc_to_b(f32x4 a, f32x4 b) {
+    const uint32_t a0 = pack_bf16x2(a[0], a[1]), a1 = pack_bf16x2(a[2], a[3]);
+    const uint32_t b0 = pack_bf16x2(b[0], b[1]), b1 = pack_bf16x2(b[2], b[3]);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    const auto u0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+    const auto u1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {u0[0], u1[0], u0[1], u1[1]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// One workgroup = (sequence, value head, 32-column slice); six waves, one barrier per chunk.
+//   waves 0,1  chain waves: each owns 16 state columns (128 x 16 fp32 in eight 16x16
+//              accumulator tiles) and, per chunk, runs X = K M, R, Delta = T R, the state
+//              update, Y = Q M and O = exp(gamma) Y + P Delta for its columns.  Results
+//              feed the next product as B operands through register lane swaps.
+//   waves 2-5  loader waves: stage the next chunk from registers into the other LDS
+//              buffer and fetch the chunk three ahead (two chunks in flight).
+template <bool GATED>
+__global__ __launch_bounds__(SNT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(PrefillArgs a, const int32_t* off, const __bf16* Tws,
                                                        long nct) {
     __shared__ StateSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, q16 = lane >> 4, l32 = lane & 31, hi32 = lane >> 5;
-    const bool chainw = wave < 2;
-    const bool outw = wave == 2 || wave == 3;
-    const bool loader = wave >= 4;
-    const int lt = tid - 256;                               // loader thread index
-    const int jc = 16 * wave;                               // chain wave: first column
+    const int l16 = lane & 15, q16 = lane >> 4;
+    const bool chainw = wave < NCW;
+    const int lt = tid - 64 * NCW;                          // loader thread index
+    const int jc = CW * wave;                               // chain wave: first column
 
     // Workgroup -> (chain = sequence * Hv + head, slice).  When the chain count is a
     // multiple of 8, the slices of one chain land on one XCD (workgroups are dealt to
@@ -512,156 +531,156 @@ __global__ __launch_bounds__(SNT, 1) void state_kernel(PrefillArgs a, const int3
     const long gc0 = a.cu ? (long)off[n] : (long)n * nct;
     const __bf16* TPseq = Tws + ((size_t)gc0 * a.Hv + h) * TP_ELEMS;
     const size_t TPstride = (size_t)a.Hv * TP_ELEMS;
+    __bf16* const obase = static_cast<__bf16*>(a.o) + (long)h * FD + j0 + jc;
 
-    // chain waves: tile mt holds keys 16 mt + 4 q16 + e, column jc + l16 of the slice
-    f32x4 M[8];
+    // Every wave passes one barrier per chunk: the chain waves after consuming chunk c
+    // from buf[c & 1], the loader waves after staging chunk c + 1 into buf[(c + 1) & 1].
+    // The two roles run separate loops so their registers never overlap.
+    if (chainw) {
+        // tile mt holds keys 16 mt + 4 q16 + e, column jc + l16 of the slice
+        f32x4 M[8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Prefetch f;
-    if (chainw && a.h0) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                M[mt][e] = a.h0[((long)nh * FD + 16 * mt + 4 * q16 + e) * FD + j0 + jc + l16];
-    }
-    if (loader) {
-        if (nchunks > 0) {
-            fetch_chunk(a, TPseq, bos, (int)min((long)FC, eos - bos), hq, h, j0, lt, f);
-            stage_chunk(sm.buf[0], f, lt);
-        }
-        if (nchunks > 1) {
-            const long t1 = bos + FC;
-            fetch_chunk(a, TPseq + TPstride, t1, (int)min((long)FC, eos - t1), hq, h, j0, lt, f);
-        }
-    }
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const long t0 = bos + (long)c * FC;
-        const int len = (int)min((long)FC, eos - t0);
-        ChunkBuf& cb = sm.buf[c & 1];
-
-        // ================= phase 1 =================
-        if (chainw) {
-            // this chunk's starting state, bf16, for X = K M here and (Q M)^T in phase 2
+        for (int mt = 0; mt < 8; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.h0) {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
-                st4(&sm.MbT[jc + l16][16 * mt + 4 * q16], M[mt][0], M[mt][1], M[mt][2], M[mt][3]);
-            wave_lds_order();
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    M[mt][e] = a.h0[((long)nh * FD + 16 * mt + 4 * q16 + e) * FD + j0 + jc + l16];
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            const ChunkBuf& cb = sm.buf[c & 1];
+            const long t0 = bos + (long)c * FC;
+            const int len = (int)min((long)FC, eos - t0);
+            // the state at the chunk start as B operands: k = key 32 s + 8 q16 + e
             bf16x8 mb[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) mb[kk] = ld8(&sm.MbT[jc + l16][32 * kk + 8 * q16]);
-            // X = K M: token tile t, element e = token 16 t + 4 q16 + e, column jc + l16
+            for (int s = 0; s < 4; ++s) mb[s] = acc_to_b(M[2 * s], M[2 * s + 1]);
+            // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
             f32x4 X[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                bf16x8 ka[4];
+            for (int t = 0; t < 4; ++t) X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) ka[kk] = ld8(&cb.K[16 * t + l16][32 * kk + 8 * q16]);
-                X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) X[t] = mma16(ka[kk], mb[kk], X[t]);
-            }
-            // R = beta (V - exp(gamma) X), value-column-major
+                for (int t = 0; t < 4; ++t) X[t] = mma16(ld8(&cb.K[16 * t + l16][32 * s + 8 * q16]), mb[s], X[t]);
+            // R = beta (V - exp(gamma) X); V read transposed: lane gets 4 tokens of its column
+            f32x4 R[4], egv[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int r = 16 * t + 4 * q16;
-                const float4 bt = *reinterpret_cast<const float4*>(&cb.beta[r]);
-                const float4 eg = *reinterpret_cast<const float4*>(&cb.eg[r]);
-                const int col = jc + l16;
-                st4(&sm.RT[col][r], bt.x * ((float)cb.V[r][col] - eg.x * X[t][0]),
-                    bt.y * ((float)cb.V[r + 1][col] - eg.y * X[t][1]),
-                    bt.z * ((float)cb.V[r + 2][col] - eg.z * X[t][2]),
-                    bt.w * ((float)cb.V[r + 3][col] - eg.w * X[t][3]));
+                const int r0 = 16 * t + 4 * q16;
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&cb.beta[r0]);
+                const bf16x4 vv = trld(&cb.V[r0 + (l16 >> 2)][jc + 4 * (l16 & 3)]);
+                if (GATED) egv[t] = *reinterpret_cast<const f32x4*>(&cb.eg[r0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    R[t][e] = bt[e] * ((float)vv[e] - (GATED ? egv[t][e] * X[t][e] : X[t][e]));
             }
-            wave_lds_order();
-            bf16x8 rb[2];
+            const bf16x8 rb[2] = {acc_to_b(R[0], R[1]), acc_to_b(R[2], R[3])};
+            // Delta = T R (T lower triangular: token tile t needs k < 16 (t + 1)); A operand
+            // T[16 t + m][k] = Tt[k][16 t + m] by transposed reads
+            f32x4 D[4];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) rb[kk] = ld8(&sm.RT[jc + l16][32 * kk + 8 * q16]);
-            // Delta = T R: token tile a (T lower triangular: k < 16 (a + 1)); A operand
-            // T[16a + m][k] = Tt[k][16a + m] by transposed reads
-            const int s = l16;
+            for (int t = 0; t < 4; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int at = 0; at < 4; ++at) {
-                f32x4 D = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk == 1 && at < 2) break;
-                    const __bf16* src = &cb.Tt[32 * kk + 8 * q16 + (s >> 2)][16 * at + 4 * (s & 3)];
-                    D = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb[kk], D);
+                for (int t = 2 * u; t < 4; ++t) {
+                    const __bf16* src = &cb.Tt[32 * u + 8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
+                    D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb[u], D[t]);
                 }
-                const int r = 16 * at + 4 * q16;
-                const float4 tl = *reinterpret_cast<const float4*>(&cb.tail[r]);
-                st4(&sm.DT[jc + l16][r], D[0], D[1], D[2], D[3]);
-                st4(&sm.DtT[jc + l16][r], tl.x * D[0], tl.y * D[1], tl.z * D[2], tl.w * D[3]);
+            const bf16x8 dd[2] = {acc_to_b(D[0], D[1]), acc_to_b(D[2], D[3])};
+            bf16x8 db[2] = {dd[0], dd[1]};
+            if (GATED) {  // Delta~ = diag(exp(gamma_last - gamma)) Delta for the state update
+                f32x4 Dt[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const f32x4 tl = *reinterpret_cast<const f32x4*>(&cb.tail[16 * t + 4 * q16]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Dt[t][e] = tl[e] * D[t][e];
+                }
+                db[0] = acc_to_b(Dt[0], Dt[1]);
+                db[1] = acc_to_b(Dt[2], Dt[3]);
             }
-        } else if (loader && c + 1 < nchunks) {
-            stage_chunk(sm.buf[(c + 1) & 1], f, lt);
-            if (c + 2 < nchunks) {
-                const long t2 = t0 + 2 * FC;
-                fetch_chunk(a, TPseq + (size_t)(c + 2) * TPstride, t2, (int)min((long)FC, eos - t2), hq, h, j0,
-                            lt, f);
-            }
-        }
-        __syncthreads();
-
-        // ================= phase 2 =================
-        if (chainw) {
+            // Y = Q M (uses the chunk-start state)
+            f32x4 Y[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Y[t] = mma16(ld8(&cb.Q[16 * t + l16][32 * s + 8 * q16]), mb[s], Y[t]);
             // M <- exp(gamma_last) M + K^T Delta~  (rows past the chunk end add g = 0)
-            bf16x8 db[2];
+            const float Gl = GATED ? cb.eg[FC - 1] : 1.f;
+            if (GATED) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) db[kk] = ld8(&sm.DtT[jc + l16][32 * kk + 8 * q16]);
-            const float Gl = cb.eg[FC - 1];
-            const int s = l16;
+                for (int mt = 0; mt < 8; ++mt) M[mt] *= Gl;
+            }
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                // A operand K^T[16 mt + m][k] = K[k][16 mt + m], k = 32 kk + 8 q16 + e
-                bf16x8 kt[2];
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const __bf16* src = &cb.K[32 * kk + 8 * q16 + (s >> 2)][16 * mt + 4 * (s & 3)];
-                    kt[kk] = cat(trld(src), trld(src + 4 * KPITCH));
+                for (int mt = 0; mt < 8; ++mt) {
+                    // A operand K^T[16 mt + m][k] = K[k][16 mt + m], k = 32 u + 8 q16 + e
+                    const __bf16* src = &cb.K[32 * u + 8 * q16 + (l16 >> 2)][16 * mt + 4 * (l16 & 3)];
+                    M[mt] = mma16(cat(trld(src), trld(src + 4 * KPITCH)), db[u], M[mt]);
                 }
-                if (a.g) M[mt] *= Gl;
+            // O = scale (exp(gamma) Y + P Delta), P lower triangular; staged column-major
+            if (GATED) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) M[mt] = mma16(kt[kk], db[kk], M[mt]);
+                for (int t = 0; t < 4; ++t) Y[t] *= egv[t];
             }
-        } else if (outw) {
-            // (Q M)^T and O^T = (exp(gamma) Q M)^T + Delta^T P^T for tokens 32u + l32;
-            // element e: state column 8(e/4) + 4 hi32 + e%4
-            const int u = wave - 2;
-            f32x16 Y = {};
 #pragma unroll
-            for (int kk = 0; kk < FD / 16; ++kk)
-                Y = mma32(ld8(&sm.MbT[l32][16 * kk + 8 * hi32]), ld8(&cb.Q[32 * u + l32][16 * kk + 8 * hi32]), Y);
-            const float eg = cb.eg[32 * u + l32];
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) Y[e] *= eg;
-            const int nk = u == 0 ? 2 : 4;   // P is lower triangular
+                for (int t = 2 * u; t < 4; ++t) Y[t] = mma16(ld8(&cb.P[16 * t + l16][32 * u + 8 * q16]), dd[u], Y[t]);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk >= nk) break;
-                Y = mma32(ld8(&sm.DT[l32][16 * kk + 8 * hi32]), ld8(&cb.P[32 * u + l32][16 * kk + 8 * hi32]), Y);
+            for (int t = 0; t < 4; ++t)
+                st4(&sm.OT[wave][l16][16 * t + 4 * q16], a.scale * Y[t][0], a.scale * Y[t][1], a.scale * Y[t][2],
+                    a.scale * Y[t][3]);
+            wave_lds_order();
+            // rows back by transposed reads: lane gets token 16 k + l16, columns 4 q16 .. +3
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bf16x4 ov = trld(&sm.OT[wave][4 * q16 + (l16 >> 2)][16 * k + 4 * (l16 & 3)]);
+                const int r = 16 * k + l16;
+                if (r < len) *reinterpret_cast<bf16x4*>(obase + (t0 + r) * a.Hv * FD + 4 * q16) = ov;
             }
-            const int r = 32 * u + l32;
-            if (r < len) {
-                __bf16* row = static_cast<__bf16*>(a.o) + ((t0 + r) * a.Hv + h) * FD + j0;
+            __syncthreads();
+        }
+        if (a.hT) {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
-                    st4(row + 8 * g4 + 4 * hi32, a.scale * Y[4 * g4], a.scale * Y[4 * g4 + 1],
-                        a.scale * Y[4 * g4 + 2], a.scale * Y[4 * g4 + 3]);
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    a.hT[((long)nh * FD + 16 * mt + 4 * q16 + e) * FD + j0 + jc + l16] = M[mt][e];
+        }
+    } else {
+        Prefetch f0, f1;   // even chunks in f0, odd chunks in f1
+        auto fetch = [&](int c, Prefetch& f) {
+            const long tc = bos + (long)c * FC;
+            fetch_chunk(a, TPseq + (size_t)c * TPstride, tc, (int)min((long)FC, eos - tc), hq, h, j0, lt, f);
+        };
+        if (nchunks > 0) fetch(0, f0);
+        if (nchunks > 1) fetch(1, f1);
+        if (nchunks > 0) stage_chunk(sm.buf[0], f0, lt);
+        if (nchunks > 2) fetch(2, f0);
+        __syncthreads();
+        // phase c: stage chunk c + 1 (held in f[(c + 1) & 1]) and refill that set with c + 3
+        for (int c = 0; c < nchunks; c += 2) {
+            if (c + 1 < nchunks) {
+                stage_chunk(sm.buf[1], f1, lt);
+                if (c + 3 < nchunks) fetch(c + 3, f1);
+            }
+            __syncthreads();
+            if (c + 1 < nchunks) {
+                if (c + 2 < nchunks) {
+                    stage_chunk(sm.buf[0], f0, lt);
+                    if (c + 4 < nchunks) fetch(c + 4, f0);
+                }
+                __syncthreads();
             }
         }
-        __syncthreads();
-    }
-
-    if (chainw && a.hT) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.hT[((long)nh * FD + 16 * mt + 4 * q16 + e) * FD + j0 + jc + l16] = M[mt][e];
     }
 }
 
@@ -688,8 +707,12 @@ hipError_t launch_prefill_fast(const PrefillArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(64), 0, s, a, off, Tws, nct);
     const long state_blocks = (long)a.N * a.Hv * NSL;
     if (state_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (state_blocks > 0)
-        hipLaunchKernelGGL(state_kernel, dim3((unsigned)state_blocks), dim3(SNT), 0, s, a, off, Tws, nct);
+    if (state_blocks > 0) {
+        if (a.g)
+            hipLaunchKernelGGL(state_kernel<true>, dim3((unsigned)state_blocks), dim3(SNT), 0, s, a, off, Tws, nct);
+        else
+            hipLaunchKernelGGL(state_kernel<false>, dim3((unsigned)state_blocks), dim3(SNT), 0, s, a, off, Tws, nct);
+    }
     return hipGetLastError();
 }
 
