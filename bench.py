@@ -57,7 +57,7 @@ def decode_bytes(N, Hqk, Hv, D):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("prefill_fast.hip", "decode.hip"):
+    for f in ("prefill_fused.hip", "mfma_ops.h", "decode.hip"):
         with open(os.path.join(ROOT, "delta_rule_recurrent_chunked_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

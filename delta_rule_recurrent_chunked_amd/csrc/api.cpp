@@ -62,7 +62,8 @@ size_t dn_chunk_fwd_workspace_bytes(const dn_shape* s) {
     dn::PrefillArgs a;
     const bool packed = s && s->B == 1 && s->num_seqs != 1;
     if (prefill_shape(s, packed, a) != DN_OK) return 0;
-    return dn::prefill_fast_supported(a) ? dn::prefill_fast_workspace_bytes(a) : 0;
+    (void)a;
+    return 0;  // every current prefill path keeps its intermediates on chip
 }
 
 dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const void* v,
@@ -84,10 +85,8 @@ dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const vo
     a.ws = ws;
     a.ws_bytes = ws_bytes;
     hipError_t e;
-    if (dn::prefill_fast_supported(a)) {
-        const size_t need = dn::prefill_fast_workspace_bytes(a);
-        if (need > ws_bytes || (need > 0 && !ws)) return DN_ERR_WORKSPACE;
-        e = dn::launch_prefill_fast(a, stream);
+    if (dn::prefill_fused_supported(a)) {
+        e = dn::launch_prefill_fused(a, stream);
     } else {
         e = dn::launch_prefill_generic(a, stream);
     }

@@ -21,7 +21,7 @@ struct PrefillArgs {
     float* hT;                      // may be null (no final state); may alias h0
     const int32_t* cu;              // may be null (each batch row is a sequence)
     void* o;
-    void* ws;                       // workspace (fast path)
+    void* ws;                       // caller's workspace (no current path needs one)
     size_t ws_bytes;
 };
 
@@ -41,9 +41,8 @@ struct DecodeArgs {
 // Launchers (host functions); each returns hipGetLastError() after its launches.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
-bool prefill_fast_supported(const PrefillArgs& a);
-size_t prefill_fast_workspace_bytes(const PrefillArgs& a);
-hipError_t launch_prefill_fast(const PrefillArgs& a, hipStream_t s);
+bool prefill_fused_supported(const PrefillArgs& a);
+hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace dn
 

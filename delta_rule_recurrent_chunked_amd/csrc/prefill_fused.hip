@@ -1,0 +1,706 @@
+// prefill_fused.hip -- one-kernel chunked prefill of the gated delta rule on the gfx950
+// matrix cores (bf16 operands, fp32 accumulation), for bf16 inputs with Dk = Dv = 128 and
+// 64-token chunks.
+//
+// The algebra is the chunked form of the update on the frankenstein "DeltaNet
+// Attention" page (module docstring), with the gate order of the nnterp
+// "linear_attention" page.  Inside a chunk of n <= 64 tokens, with the state slice M
+// (key-major, S^T) at the chunk start and gamma_r = sum_{i<=r} g_i:
+//
+//   A_ri  = beta_r exp(gamma_r - gamma_i) k_r.k_i (i < r),   T = (I + A)^{-1}
+//   R     = diag(beta) (V - diag(exp(gamma)) K M)
+//   Delta = T R                                   (row r: beta_r x prediction error)
+//   O     = scale (diag(exp(gamma)) Q M + P Delta),  P_ri = exp(gamma_r - gamma_i) q_r.k_i (i <= r)
+//   M    <- exp(gamma_last) M + K^T diag(exp(gamma_last - gamma)) Delta
+//
+// One workgroup of eight waves per (sequence, value head, 32-column slice of the state).
+// The value columns of the state are independent, so slices never exchange data; the
+// chunk-local matrices (A, T, P) are recomputed by each slice's workgroup, which keeps
+// every intermediate on chip: HBM sees q, k, v, beta, g once and o once.
+//
+// Each chunk takes one "phase" of two halves separated by workgroup barriers.  In phase j:
+//
+//   wave      SIMD  first half (.1)                    second half (.2)
+//   0, 1      0, 1  chain, chunk j: X = K M, R         Delta = T R, state update
+//   2, 3      2, 3  output: O of chunk j - 1           Y = Q M of chunk j
+//   4, 5      0, 1  loaders: K, Q, scalars of j + 1    V of j + 1; fetch chunk j + 3
+//   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, half
+//   7         3     P of chunk j                       A of chunk j + 1, other half
+//
+// Chain wave w owns state columns 16w .. 16w+15 of the slice as eight 16x16 fp32
+// accumulator tiles; products that consume its results take them as B operands through
+// register lane swaps (acc_to_b).  The output waves get the chain's bf16 state and Delta
+// fragments through LDS.  LDS holds K and Q double-buffered, one V, T and A, two P.
+#include <type_traits>
+
+#include "internal.h"
+#include "mfma_ops.h"
+
+namespace dn {
+namespace {
+
+constexpr int FC = 64;             // chunk
+constexpr int FD = 128;            // Dk = Dv
+constexpr int DVS = 32;            // state columns per workgroup
+constexpr int NSL = FD / DVS;      // slices per (sequence, value head)
+constexpr int CW = 16;             // state columns per chain wave
+constexpr int NCW = DVS / CW;      // chain waves
+constexpr int KPITCH = FD + 8;     // bf16 row pitches: 16-byte multiples that put the
+constexpr int CPITCH = FC + 8;     //   16 rows of one MFMA operand read on distinct banks
+constexpr int VPITCH = DVS + 8;
+constexpr int NT = 512;            // threads (8 waves)
+constexpr int NLD = 128;           // loader threads (waves 4, 5)
+
+// Per-token scalars of a chunk.  With e(I) = 16 I + 15 the last token of 16-token block I,
+// exp(gamma_r - gamma_i) for i in block I < block of r factors as
+// F1[I][r] * F2[i] = exp(gamma_r - gamma_e(I)) * exp(gamma_e(I) - gamma_i), both <= 1 when
+// g <= 0, so the masks of the blocks below the diagonal need no exponentials.
+enum Sc { SC_BETA = 0, SC_GAM = 1, SC_EG = 2, SC_TAIL = 3, SC_F2 = 4, SC_F1 = 5, SC_N = 8 };
+
+struct alignas(16) FusedSmem {
+    __bf16 K[2][FC][KPITCH];       // chunk keys, token-major (chunk j in K[j & 1])
+    __bf16 Q[2][FC][KPITCH];       // chunk queries, token-major
+    __bf16 V[FC][VPITCH];          // value slice of the next chunk the chain reads
+    __bf16 Tt[FC][CPITCH];         // T^T of the chunk being processed
+    __bf16 P[2][FC][CPITCH];       // P, row r = query token (chunk j in P[j & 1])
+    __bf16 Ab[FC][CPITCH];         // A in bf16 (blocks below the 16x16 block diagonal)
+    float Ad[8][32];               // A's diagonal 8x8 blocks, fp32, strictly lower part
+                                   //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m
+    bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
+    bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
+    __bf16 OT[NCW][CW][CPITCH];    // output waves: O tile, column-major, for row stores
+    float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
+};
+
+struct LoadSet {
+    uint4 k[8], q[8], v[2];
+    float beta, g;
+};
+
+struct Geo {  // where this workgroup works
+    long bos, eos;
+    int n, h, hq, j0, nh, nchunks;
+};
+
+__device__ __forceinline__ int chunk_len(const Geo& w, int j) {
+    return (int)min((long)FC, w.eos - (w.bos + (long)j * FC));
+}
+
+// ------------------------------------------------------------------------ loaders
+// Raw buffer loads: the descriptor of each stream covers exactly the sequence's own
+// tokens, so loads past the sequence end (the ragged last chunk and the chunks the loop
+// fetches beyond the last) return zeros by the hardware range check: every load is
+// unconditional, and each lane keeps one 32-bit offset per 16-byte piece.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Streams {
+    __amdgpu_buffer_rsrc_t k, q, v, beta, g;
+    uint32_t kq_chunk, v_chunk, s_chunk;   // bytes per chunk of 64 tokens
+    uint32_t off_kq[8], off_v[2], off_s;   // this lane's piece offsets within a chunk
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w, int lt, Streams& st) {
+    const long L = w.eos - w.bos;           // tokens of this sequence
+    const uint32_t kq_tok = (uint32_t)a.Hqk * FD * 2, v_tok = (uint32_t)a.Hv * FD * 2, s_tok = (uint32_t)a.Hv * 4;
+    const uint32_t kq_end = L > 0 ? (uint32_t)((L - 1) * kq_tok + FD * 2) : 0;
+    const uint32_t v_end = L > 0 ? (uint32_t)((L - 1) * v_tok + DVS * 2) : 0;
+    const uint32_t s_end = L > 0 ? (uint32_t)((L - 1) * s_tok + 4) : 0;
+    const long kq0 = (w.bos * a.Hqk + w.hq) * FD, v0 = (w.bos * a.Hv + w.h) * FD + w.j0, s0 = w.bos * a.Hv + w.h;
+    st.k = rsrc(static_cast<const __bf16*>(a.k) + kq0, kq_end);
+    st.q = rsrc(static_cast<const __bf16*>(a.q) + kq0, kq_end);
+    st.v = rsrc(static_cast<const __bf16*>(a.v) + v0, v_end);
+    st.beta = rsrc(a.beta + s0, s_end);
+    st.g = rsrc(a.g ? a.g + s0 : a.beta + s0, a.g ? s_end : 0);
+    st.kq_chunk = FC * kq_tok;
+    st.v_chunk = FC * v_tok;
+    st.s_chunk = FC * s_tok;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = lt + NLD * p;
+        st.off_kq[p] = (uint32_t)(v >> 4) * kq_tok + (v & 15) * 16;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int v = lt + NLD * p;
+        st.off_v[p] = (uint32_t)(v >> 2) * v_tok + (v & 3) * 16;
+    }
+    st.off_s = (uint32_t)(lt & 63) * s_tok;  // both loader waves fetch the chunk's scalars
+}
+
+__device__ __forceinline__ uint4 u4(u32x4 x) { return make_uint4(x[0], x[1], x[2], x[3]); }
+
+__device__ __forceinline__ void fetch(const Streams& st, int j, LoadSet& f) {
+    // the chunk offset goes into the per-lane offset, which the range check covers
+    const uint32_t ckq = (uint32_t)j * st.kq_chunk, cv = (uint32_t)j * st.v_chunk, cs = (uint32_t)j * st.s_chunk;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        f.k[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.k, st.off_kq[p] + ckq, 0, 0));
+        f.q[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.q, st.off_kq[p] + ckq, 0, 0));
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) f.v[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.v, st.off_v[p] + cv, 0, 0));
+    f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.beta, st.off_s + cs, 0, 0));
+    f.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.g, st.off_s + cs, 0, 0));
+}
+
+// K, Q and the per-token scalars of chunk j (rows past the sequence end hold zeros)
+__device__ __forceinline__ void put_kq(FusedSmem& sm, int j, int lt, const LoadSet& f) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = lt + NLD * p, row = v >> 4, cg = v & 15;
+        *reinterpret_cast<uint4*>(&sm.K[j & 1][row][cg * 8]) = f.k[p];
+        *reinterpret_cast<uint4*>(&sm.Q[j & 1][row][cg * 8]) = f.q[p];
+    }
+    if (lt < FC) {  // one wave: inclusive scan of the log decays over the chunk
+        float gv = f.g;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(gv, o);
+            if (lt >= o) gv += y;
+        }
+        const float glast = __shfl(gv, 63);
+        float* s = &sm.sc[j % 3][0][0];
+        s[SC_BETA * FC + lt] = f.beta;
+        s[SC_GAM * FC + lt] = gv;
+        s[SC_EG * FC + lt] = __expf(gv);
+        s[SC_TAIL * FC + lt] = __expf(glast - gv);
+        const float ge[3] = {__shfl(gv, 15), __shfl(gv, 31), __shfl(gv, 47)};
+        s[SC_F2 * FC + lt] = __expf(__shfl(gv, (lt | 15)) - gv);
+#pragma unroll
+        for (int I = 0; I < 3; ++I) s[(SC_F1 + I) * FC + lt] = __expf(fminf(gv - ge[I], 0.f));
+    }
+}
+
+__device__ __forceinline__ void put_v(FusedSmem& sm, int lt, const LoadSet& f) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int v = lt + NLD * p;
+        *reinterpret_cast<uint4*>(&sm.V[v >> 2][(v & 3) * 8]) = f.v[p];
+    }
+}
+
+// ------------------------------------------------------------------ Gram products
+// Key fragments of one chunk as 16x16x32 operands: kf[X][s] = rows 16 X + l16, keys
+// 32 s + 8 q16 .. +7.  The same fragment serves as A operand (rows of the tile) and as
+// B operand (columns of the tile) of a product contracting over keys.
+__device__ __forceinline__ void load_rows(const __bf16 (*src)[KPITCH], int l16, int q16, bf16x8 (&f)[4][4]) {
+#pragma unroll
+    for (int X = 0; X < 4; ++X)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[X][s] = ld8(&src[16 * X + l16][32 * s + 8 * q16]);
+}
+
+// A and P come from 16x16 tiles (I, R), I <= R, of K K^T and K Q^T: tile (I, R) holds
+// k_i . k_r (or k_i . q_r) with i = 16 I + 4 q16 + e, r = 16 R + l16, so each lane owns
+// four consecutive columns i of one row r: 8-byte stores.  Rows past the sequence end
+// need no mask: their keys, queries and beta are zero.
+__device__ __forceinline__ void decay4(const float* s, int R, int I, int r, int i0, f32x4& d) {
+    // exp(gamma_r - gamma_i), i = i0 .. i0 + 3 <= r (diagonal tile: direct; below: factors)
+    if (I == R) {
+        const float gr = s[SC_GAM * FC + r];
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&s[SC_GAM * FC + i0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = __expf(fminf(gr - gi[e], 0.f));
+    } else {
+        const float f1 = s[(SC_F1 + I) * FC + r];
+        const f32x4 f2 = *reinterpret_cast<const f32x4*>(&s[SC_F2 * FC + i0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = f1 * f2[e];
+    }
+}
+
+// A of chunk j, the tiles of one half: half 0 = row blocks 0, 3 (tiles (0,0), (0..3,3)),
+// half 1 = row blocks 1, 2 (tiles (0..1,1), (0..2,2)); five tiles each.  Below the block
+// diagonal A goes to Ab in bf16, the diagonal blocks to Ad in fp32 (packed).
+template <bool GATED, int HALF>
+__device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
+    constexpr int R0 = HALF == 0 ? 0 : 1, R1 = HALF == 0 ? 3 : 2;
+    bf16x8 kf[4][4];
+    load_rows(sm.K[j & 1], l16, q16, kf);
+    f32x4 G[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) G[u][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int R = u == 0 ? R0 : R1;
+#pragma unroll
+            for (int I = 0; I <= R; ++I) G[u][I] = mma16(kf[I][ks], kf[R][ks], G[u][I]);
+        }
+    const float* s = &sm.sc[j % 3][0][0];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int R = u == 0 ? R0 : R1;
+        const int r = 16 * R + l16;
+        const float br = s[SC_BETA * FC + r];
+#pragma unroll
+        for (int I = 0; I <= R; ++I) {
+            const int i0 = 16 * I + 4 * q16;
+            f32x4 d = {1.f, 1.f, 1.f, 1.f};
+            if (GATED) decay4(s, R, I, r, i0, d);
+            f32x4 av;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = br * d[e] * G[u][I][e];
+            if (I < R) {
+                st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
+            } else {
+                // diagonal tile: the lower-left 8x8 in bf16, the two diagonal 8x8 blocks'
+                // strictly lower parts in fp32
+                if (l16 >= 8 && q16 < 2) st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
+                const int rr = l16 & 7;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ii = 4 * q16 + e;
+                    if ((ii >> 3) == (l16 >> 3) && (ii & 7) < rr)
+                        sm.Ad[2 * R + (l16 >> 3)][rr * (rr - 1) / 2 + (ii & 7)] = av[e];
+                }
+            }
+        }
+    }
+}
+
+// P of chunk j (its blocks above the diagonal that the output waves read are zero, written
+// once before the first chunk).
+template <bool GATED>
+__device__ __forceinline__ void make_p(FusedSmem& sm, int j, int l16, int q16) {
+    bf16x8 kf[4][4], qf[4][4];
+    load_rows(sm.K[j & 1], l16, q16, kf);
+    load_rows(sm.Q[j & 1], l16, q16, qf);
+    f32x4 G[10];
+#pragma unroll
+    for (int t = 0; t < 10; ++t) G[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        int t = 0;
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int I = 0; I <= R; ++I, ++t) G[t] = mma16(kf[I][ks], qf[R][ks], G[t]);
+    }
+    const float* s = &sm.sc[j % 3][0][0];
+    int t = 0;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const int r = 16 * R + l16;
+#pragma unroll
+        for (int I = 0; I <= R; ++I, ++t) {
+            const int i0 = 16 * I + 4 * q16;
+            f32x4 d = {1.f, 1.f, 1.f, 1.f};
+            if (GATED) decay4(s, R, I, r, i0, d);
+            f32x4 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] = (I < R || i0 + e <= r) ? d[e] * G[t][e] : 0.f;
+            st4(&sm.P[j & 1][r][i0], pv[0], pv[1], pv[2], pv[3]);
+        }
+    }
+}
+
+// Wave 6, first half: T = (I + A)^{-1} into Tt (T^T).  The eight 8x8 diagonal blocks by
+// fp32 forward substitution, then the blocks below the diagonal by three levels of 2x2
+// block inversion, T21 = -T22 (A21 T11), with the inner product handed to the outer one
+// as a B operand in registers.  The zero blocks of Tt are written once, before the first
+// chunk.
+__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16) {
+    const int lane = 16 * q16 + l16;
+    {
+        // lane = 8 * block + column c: solve (I + A_bb) x = e_c in the column order: once
+        // x[m] is final, subtract its share from every later row.  The block's strictly
+        // lower entries (28, packed) are read into registers first.
+        const int b = lane >> 3, c = lane & 7;
+        f32x4 ap[7];
+#pragma unroll
+        for (int g = 0; g < 7; ++g) ap[g] = *reinterpret_cast<const f32x4*>(&sm.Ad[b][4 * g]);
+        float x[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[r] = r == c ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 7; ++m)
+#pragma unroll
+            for (int r = m + 1; r < 8; ++r) {
+                const int idx = r * (r - 1) / 2 + m;
+                x[r] -= ap[idx >> 2][idx & 3] * x[m];
+            }
+        bf16x8 col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[e] = (__bf16)x[e];
+        *reinterpret_cast<bf16x8*>(&sm.Tt[8 * b + c][8 * b]) = col;
+    }
+    wave_lds_order();
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // level 0, the four 16x16 diagonal blocks: with L = A's lower-left 8x8 and
+    // D = diag(T00, T11) (the 8x8 inverses), T's lower-left 8x8 = -(D (L D)) there.  k = 16
+    // is padded to the instruction's 32 with zero lanes (q16 >= 2); operand parts outside
+    // the 8x8 blocks they stand for are zeroed.
+    {
+        const bool klo = q16 == 0, kin = q16 < 2;
+        f32x4 X[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int o = 16 * b;
+            // A operand L[m][k]: rows m >= 8, keys k < 8 of the diagonal block
+            const bf16x8 af = (klo && l16 >= 8) ? ld8(&sm.Ab[o + l16][o]) : zero8();
+            // B operand D[k][n] = Tt[o + n][o + k], only inside n's own 8x8 block
+            const bf16x8 bf = (kin && q16 == (l16 >> 3)) ? ld8(&sm.Tt[o + l16][o + 8 * q16]) : zero8();
+            X[b] = mma16(af, bf, z4);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int o = 16 * b;
+            // A operand D[m][k] = Tt[o + k][o + m] (transposed read), inside m's 8x8 block
+            const __bf16* src = &sm.Tt[o + 8 * (q16 & 1) + (l16 >> 2)][o + 4 * (l16 & 3)];
+            bf16x8 af = cat(trld(src), trld(src + 4 * CPITCH));
+            if (!(kin && q16 == (l16 >> 3))) af = zero8();
+            const f32x4 Y = mma16(af, acc_to_b(X[b], z4), z4);
+            // rows 8..15 (q16 >= 2), columns 0..7 (l16 < 8): T[o+4q16+e][o+l16]
+            if (q16 >= 2 && l16 < 8) st4(&sm.Tt[o + l16][o + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
+        }
+    }
+    wave_lds_order();
+    // level 1, both 32x32 diagonal blocks (base 0, 32); k = 16 is padded to the
+    // instruction's 32 with zero lanes (q16 >= 2)
+    {
+        const bool live = q16 < 2;
+        f32x4 X[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int base = 32 * h;
+            // X = A21 T11: A rows base+16+m; B[k][n] = T11[k][n] = Tt[base+n][base+k]
+            const bf16x8 af = live ? ld8(&sm.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
+            const bf16x8 bf = live ? ld8(&sm.Tt[base + l16][base + 8 * q16]) : zero8();
+            X[h] = mma16(af, bf, z4);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int base = 32 * h;
+            // T21 = -T22 X: A operand T22[m][k] = Tt[base+16+k][base+16+m] (transposed read;
+            // k >= 16 meets the zero half of the B operand)
+            const __bf16* src = &sm.Tt[base + 16 + 8 * (q16 & 1) + (l16 >> 2)][base + 16 + 4 * (l16 & 3)];
+            const f32x4 Y = mma16(cat(trld(src), trld(src + 4 * CPITCH)), acc_to_b(X[h], z4), z4);
+            st4(&sm.Tt[base + l16][base + 16 + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
+        }
+    }
+    wave_lds_order();
+    // level 2: T[32:64, 0:32] = -T[32:64, 32:64] (A[32:64, 0:32] T[0:32, 0:32]); 16x16 tiles
+    // (tr, tc), k = 32 in one instruction
+    {
+        f32x4 X[2][2];
+#pragma unroll
+        for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc)
+                X[tr][tc] = mma16(ld8(&sm.Ab[32 + 16 * tr + l16][8 * q16]), ld8(&sm.Tt[16 * tc + l16][8 * q16]), z4);
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) {
+            const bf16x8 xb = acc_to_b(X[0][tc], X[1][tc]);
+#pragma unroll
+            for (int tr = 0; tr < 2; ++tr) {
+                // A operand T[32+16tr+m][32+k] = Tt[32+k][32+16tr+m], k = 8 q16 + e
+                const __bf16* src = &sm.Tt[32 + 8 * q16 + (l16 >> 2)][32 + 16 * tr + 4 * (l16 & 3)];
+                const f32x4 Y = mma16(cat(trld(src), trld(src + 4 * CPITCH)), xb, z4);
+                st4(&sm.Tt[16 * tc + l16][32 + 16 * tr + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
+            }
+        }
+    }
+}
+
+// -------------------------------------------------------------------------- kernel
+template <bool GATED>
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void fused_kernel(PrefillArgs a) {
+    __shared__ FusedSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q16 = lane >> 4;
+
+    // Workgroup -> (chain = sequence * Hv + head, slice).  When the chain count is a
+    // multiple of 8, the slices of one chain land on one XCD (workgroups are dealt to
+    // the 8 XCDs round-robin), so they share the chain's K and Q through that XCD's L2.
+    const int chains = a.N * a.Hv;
+    const int b = blockIdx.x;
+    int chain, slice;
+    if ((chains & 7) == 0) {
+        const int y = b >> 3;
+        slice = y % NSL;
+        chain = (b & 7) + 8 * (y / NSL);
+    } else {
+        slice = b % NSL;
+        chain = b / NSL;
+    }
+    Geo w;
+    w.n = chain / a.Hv;
+    w.h = chain % a.Hv;
+    if (a.cu && a.N <= 64) {
+        // longest sequences first: rank -> sequence (ties by index)
+        const int rank = w.n;
+        for (int m = 0; m < a.N; ++m) {
+            const int lm = a.cu[m + 1] - a.cu[m];
+            int r = 0;
+            for (int x = 0; x < a.N; ++x) {
+                const int lx = a.cu[x + 1] - a.cu[x];
+                r += (lx > lm) || (lx == lm && x < m);
+            }
+            if (r == rank) w.n = m;
+        }
+    }
+    w.nh = w.n * a.Hv + w.h;
+    w.hq = w.h / (a.Hv / a.Hqk);
+    w.j0 = slice * DVS;
+    seq_range(a.cu, w.n, a.T, w.bos, w.eos);
+    w.nchunks = (int)((w.eos - w.bos + FC - 1) / FC);
+    const int nc = w.nchunks;
+    const int nph = (nc + 2) & ~1;   // phases 0 .. nph - 1 (>= nc + 1, even)
+
+    // Every wave runs phases j = -1 .. nph - 1, two barriers each.
+    if (wave < NCW) {
+        // ------------------------------------------------------------ chain waves
+        const int jc = CW * wave;
+        f32x4 M[8];  // tile mt: keys 16 mt + 4 q16 + e, column jc + l16 of the slice
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.h0) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    M[mt][e] = a.h0[((long)w.nh * FD + 16 * mt + 4 * q16 + e) * FD + w.j0 + jc + l16];
+        }
+        bf16x8 mb[4];  // the state at the chunk start as B operands: k = key 32 s + 8 q16 + e
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            mb[s] = acc_to_b(M[2 * s], M[2 * s + 1]);
+            sm.mb[0][wave][s][lane] = mb[s];
+        }
+        __syncthreads();
+        __syncthreads();
+        for (int j = 0; j < nph; ++j) {
+            const bool live = j < nc;
+            const float* s = &sm.sc[j % 3][0][0];
+            bf16x8 rb[2];
+            if (live) {
+                // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
+                f32x4 X[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        X[t] = mma16(ld8(&sm.K[j & 1][16 * t + l16][32 * ks + 8 * q16]), mb[ks], X[t]);
+                // R = beta (V - exp(gamma) X); V read transposed: lane gets 4 tokens of its column
+                f32x4 R[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int r0 = 16 * t + 4 * q16;
+                    const f32x4 bt = *reinterpret_cast<const f32x4*>(&s[SC_BETA * FC + r0]);
+                    const bf16x4 vv = trld(&sm.V[r0 + (l16 >> 2)][jc + 4 * (l16 & 3)]);
+                    f32x4 eg = {1.f, 1.f, 1.f, 1.f};
+                    if (GATED) eg = *reinterpret_cast<const f32x4*>(&s[SC_EG * FC + r0]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) R[t][e] = bt[e] * ((float)vv[e] - eg[e] * X[t][e]);
+                }
+                rb[0] = acc_to_b(R[0], R[1]);
+                rb[1] = acc_to_b(R[2], R[3]);
+            }
+            __syncthreads();
+            if (live) {
+                // Delta = T R (T lower triangular: token tile t needs k < 16 (t + 1)); A
+                // operand T[16 t + m][k] = Tt[k][16 t + m] by transposed reads
+                f32x4 D[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int t = 2 * u; t < 4; ++t) {
+                        const __bf16* src = &sm.Tt[32 * u + 8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
+                        D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb[u], D[t]);
+                    }
+                bf16x8 db[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    db[u] = acc_to_b(D[2 * u], D[2 * u + 1]);
+                    sm.dd[wave][u][lane] = db[u];
+                }
+                if (GATED) {  // Delta~ = diag(exp(gamma_last - gamma)) Delta for the state update
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const f32x4 tl = *reinterpret_cast<const f32x4*>(&s[SC_TAIL * FC + 16 * t + 4 * q16]);
+                        D[t] *= tl;
+                    }
+                    db[0] = acc_to_b(D[0], D[1]);
+                    db[1] = acc_to_b(D[2], D[3]);
+                    const float Gl = s[SC_EG * FC + FC - 1];
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) M[mt] *= Gl;
+                }
+                // M <- exp(gamma_last) M + K^T Delta~  (rows past the chunk end add g = 0)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) {
+                        // A operand K^T[16 mt + m][k] = K[k][16 mt + m], k = 32 u + 8 q16 + e
+                        const __bf16* src = &sm.K[j & 1][32 * u + 8 * q16 + (l16 >> 2)][16 * mt + 4 * (l16 & 3)];
+                        M[mt] = mma16(cat(trld(src), trld(src + 4 * KPITCH)), db[u], M[mt]);
+                    }
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    mb[s4] = acc_to_b(M[2 * s4], M[2 * s4 + 1]);
+                    sm.mb[(j + 1) & 1][wave][s4][lane] = mb[s4];
+                }
+            }
+            __syncthreads();
+        }
+        if (a.hT) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    a.hT[((long)w.nh * FD + 16 * mt + 4 * q16 + e) * FD + w.j0 + jc + l16] = M[mt][e];
+        }
+    } else if (wave < 2 * NCW) {
+        // ----------------------------------------------------------- output waves
+        const int cw = wave - NCW, jc = CW * cw;
+        __bf16* const obase = static_cast<__bf16*>(a.o) + (long)w.h * FD + w.j0 + jc;
+        f32x4 Y[4];  // Y = Q M of the previous chunk: token 16 t + 4 q16 + e, column jc + l16
+        __syncthreads();
+        __syncthreads();
+        for (int j = 0; j < nph; ++j) {
+            if (j >= 1 && j <= nc) {
+                // O of chunk j - 1 = scale (exp(gamma) Y + P Delta), P lower triangular
+                const int jp = j - 1;
+                const float* s = &sm.sc[jp % 3][0][0];
+                if (GATED) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) Y[t] *= *reinterpret_cast<const f32x4*>(&s[SC_EG * FC + 16 * t + 4 * q16]);
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const bf16x8 d = sm.dd[cw][u][lane];
+#pragma unroll
+                    for (int t = 2 * u; t < 4; ++t) Y[t] = mma16(ld8(&sm.P[jp & 1][16 * t + l16][32 * u + 8 * q16]), d, Y[t]);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    st4(&sm.OT[cw][l16][16 * t + 4 * q16], a.scale * Y[t][0], a.scale * Y[t][1], a.scale * Y[t][2],
+                        a.scale * Y[t][3]);
+                wave_lds_order();
+                // rows back by transposed reads: lane gets token 16 k + l16, columns 4 q16 .. +3
+                const long t0 = w.bos + (long)jp * FC;
+                const int len = chunk_len(w, jp);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const bf16x4 ov = trld(&sm.OT[cw][4 * q16 + (l16 >> 2)][16 * k + 4 * (l16 & 3)]);
+                    const int r = 16 * k + l16;
+                    if (r < len) *reinterpret_cast<bf16x4*>(obase + (t0 + r) * a.Hv * FD + 4 * q16) = ov;
+                }
+            }
+            __syncthreads();
+            if (j < nc) {
+                // Y = Q M with the chain's bf16 state at the start of chunk j
+                bf16x8 m4[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) m4[ks] = sm.mb[j & 1][cw][ks][lane];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        Y[t] = mma16(ld8(&sm.Q[j & 1][16 * t + l16][32 * ks + 8 * q16]), m4[ks], Y[t]);
+            }
+            __syncthreads();
+        }
+    } else if (wave < 2 * NCW + 2) {
+        // ---------------------------------------------------------------- loaders
+        const int lt = tid - 64 * 2 * NCW;
+        Streams st;
+        make_streams(a, w, lt, st);
+        LoadSet f0, f1;   // even chunks in f0, odd chunks in f1
+        fetch(st, 0, f0);
+        fetch(st, 1, f1);
+        // phase -1: chunk 0
+        put_kq(sm, 0, lt, f0);
+        __syncthreads();
+        put_v(sm, lt, f0);
+        fetch(st, 2, f0);
+        __syncthreads();
+        // phase j: chunk j + 1 (in f[(j + 1) & 1]); then refill that set with chunk j + 3
+        for (int j = 0; j < nph; j += 2) {
+            put_kq(sm, j + 1, lt, f1);
+            __syncthreads();
+            put_v(sm, lt, f1);
+            fetch(st, j + 3, f1);
+            __syncthreads();
+            put_kq(sm, j + 2, lt, f0);
+            __syncthreads();
+            put_v(sm, lt, f0);
+            fetch(st, j + 4, f0);
+            __syncthreads();
+        }
+    } else if (wave == 2 * NCW + 2) {
+        // ------------------------------------------ wave 6: T of j, half of A of j + 1
+        // zero blocks, written once: Tt below its block diagonal, P above its diagonal in
+        // the tiles the output waves read (rows 0-15 x keys 16-31, rows 32-47 x keys 48-63)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int v = lane + 64 * p, r = v >> 3, cg = v & 7;
+            const bool below = cg * 8 + 8 <= (r >> 4) * 16;                  // left of the 16x16 diagonal
+            const bool inner = (r & 8) && cg * 8 == (r >> 4) * 16;           // upper-right 8x8 of T inside it
+            if (below || inner) *reinterpret_cast<bf16x8*>(&sm.Tt[r][cg * 8]) = zero8();
+        }
+#pragma unroll
+        for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int v = lane + 64 * p, r = v >> 2, half = (v >> 1) & 1, cg = v & 1;
+                const int row = r < 16 ? r : r + 16;      // rows 0-15 and 32-47
+                const int col = (row < 16 ? 16 : 48) + 8 * cg;
+                if (half == 0) *reinterpret_cast<bf16x8*>(&sm.P[bf][row][col]) = zero8();
+            }
+        // phase -1, second half: half of A of chunk 0
+        __syncthreads();
+        make_a<GATED, 0>(sm, 0, l16, q16);
+        __syncthreads();
+        for (int j = 0; j < nph; ++j) {
+            if (j < nc) make_t(sm, l16, q16);
+            __syncthreads();
+            if (j + 1 < nc) make_a<GATED, 0>(sm, j + 1, l16, q16);
+            __syncthreads();
+        }
+    } else {
+        // ------------------------------------------ wave 7: P of j, half of A of j + 1
+        __syncthreads();
+        make_a<GATED, 1>(sm, 0, l16, q16);
+        __syncthreads();
+        for (int j = 0; j < nph; ++j) {
+            if (j < nc) make_p<GATED>(sm, j, l16, q16);
+            __syncthreads();
+            if (j + 1 < nc) make_a<GATED, 1>(sm, j + 1, l16, q16);
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace
+
+bool prefill_fused_supported(const PrefillArgs& a) {
+    return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC;
+}
+
+hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s) {
+    const long blocks = (long)a.N * a.Hv * NSL;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (blocks > 0) {
+        if (a.g)
+            hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, s, a);
+        else
+            hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dn

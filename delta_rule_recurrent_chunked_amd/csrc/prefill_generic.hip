@@ -1,6 +1,6 @@
 // prefill_generic.hip -- chunked form of the gated delta rule in fp32 on the vector
 // ALUs, for every supported size (Dk, Dv <= 128, chunk <= 64) and for fp32 inputs.
-// The bf16 Dk = Dv = 128 prompts take the matrix-core path (prefill_fast.hip).
+// The bf16 Dk = Dv = 128 prompts take the matrix-core path (prefill_fused.hip).
 //
 // The chunked form follows from the update of the frankenstein "DeltaNet
 // Attention" page (module docstring) with the gate order of the nnterp

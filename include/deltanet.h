@@ -121,7 +121,8 @@ dn_status dn_chunk_fwd(const dn_shape* shape,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
-/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none). */
+/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none; every
+ * current path keeps its intermediates on chip and returns 0). */
 size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
 
 /*
