@@ -21,11 +21,13 @@
 // Each chunk takes one "phase" of two halves separated by workgroup barriers.  In phase j:
 //
 //   wave      SIMD  first half (.1)                    second half (.2)
-//   0, 1      0, 1  chain, chunk j: X = K M, R         Delta = T R, state update
-//   2, 3      2, 3  output: O of chunk j - 1           Y = Q M of chunk j
+//   0, 1      0, 1  chain, chunk j: X = K M, R         Delta, state update
+//   3, 7      3     output: O of chunk j - 1           Y = Q M and half of P, chunk j
 //   4, 5      0, 1  loaders: K, Q, scalars of j + 1    V of j + 1; fetch chunk j + 3
 //   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, half
-//   7         3     P of chunk j                       A of chunk j + 1, other half
+//   2         2     -                                  A of chunk j + 1, other half
+//
+// The UT inverse, the longest serial step, has SIMD 2 to itself in the first half.
 //
 // Chain wave w owns state columns 16w .. 16w+15 of the slice as eight 16x16 fp32
 // accumulator tiles; products that consume its results take them as B operands through
@@ -64,7 +66,7 @@ struct alignas(16) FusedSmem {
     __bf16 Tt[FC][CPITCH];         // T^T of the chunk being processed
     __bf16 P[2][FC][CPITCH];       // P, row r = query token (chunk j in P[j & 1])
     __bf16 Ab[FC][CPITCH];         // A in bf16 (blocks below the 16x16 block diagonal)
-    float Ad[8][32];               // A's diagonal 8x8 blocks, fp32, strictly lower part
+    float Ad[4][128];              // A's diagonal 16x16 blocks, fp32, strictly lower part
                                    //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m
     bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
@@ -147,6 +149,15 @@ __device__ __forceinline__ void fetch(const Streams& st, int j, LoadSet& f) {
     f.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.g, st.off_s + cs, 0, 0));
 }
 
+// DPP move of a float with bound_ctrl (lanes without a source read 0)
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xf, true));
+}
+__device__ __forceinline__ float lane_f32(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 // K, Q and the per-token scalars of chunk j (rows past the sequence end hold zeros)
 __device__ __forceinline__ void put_kq(FusedSmem& sm, int j, int lt, const LoadSet& f) {
 #pragma unroll
@@ -155,20 +166,22 @@ __device__ __forceinline__ void put_kq(FusedSmem& sm, int j, int lt, const LoadS
         *reinterpret_cast<uint4*>(&sm.K[j & 1][row][cg * 8]) = f.k[p];
         *reinterpret_cast<uint4*>(&sm.Q[j & 1][row][cg * 8]) = f.q[p];
     }
-    if (lt < FC) {  // one wave: inclusive scan of the log decays over the chunk
+    if (lt < FC) {  // one wave: inclusive scan of the log decays over the chunk (DPP)
         float gv = f.g;
-        for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(gv, o);
-            if (lt >= o) gv += y;
-        }
-        const float glast = __shfl(gv, 63);
+        gv += dpp_f32<0x111, 0xf>(gv);   // row_shr:1, 2, 4, 8 within rows of 16 lanes
+        gv += dpp_f32<0x112, 0xf>(gv);
+        gv += dpp_f32<0x114, 0xf>(gv);
+        gv += dpp_f32<0x118, 0xf>(gv);
+        gv += dpp_f32<0x142, 0xa>(gv);   // row_bcast:15 into rows 1, 3
+        gv += dpp_f32<0x143, 0xc>(gv);   // row_bcast:31 into rows 2, 3
+        const float ge[4] = {lane_f32(gv, 15), lane_f32(gv, 31), lane_f32(gv, 47), lane_f32(gv, 63)};
         float* s = &sm.sc[j % 3][0][0];
         s[SC_BETA * FC + lt] = f.beta;
         s[SC_GAM * FC + lt] = gv;
         s[SC_EG * FC + lt] = __expf(gv);
-        s[SC_TAIL * FC + lt] = __expf(glast - gv);
-        const float ge[3] = {__shfl(gv, 15), __shfl(gv, 31), __shfl(gv, 47)};
-        s[SC_F2 * FC + lt] = __expf(__shfl(gv, (lt | 15)) - gv);
+        s[SC_TAIL * FC + lt] = __expf(ge[3] - gv);
+        const int blk = lt >> 4;
+        s[SC_F2 * FC + lt] = __expf((blk == 0 ? ge[0] : blk == 1 ? ge[1] : blk == 2 ? ge[2] : ge[3]) - gv);
 #pragma unroll
         for (int I = 0; I < 3; ++I) s[(SC_F1 + I) * FC + lt] = __expf(fminf(gv - ge[I], 0.f));
     }
@@ -250,162 +263,110 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
             if (I < R) {
                 st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
             } else {
-                // diagonal tile: the lower-left 8x8 in bf16, the two diagonal 8x8 blocks'
-                // strictly lower parts in fp32
-                if (l16 >= 8 && q16 < 2) st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
-                const int rr = l16 & 7;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ii = 4 * q16 + e;
-                    if ((ii >> 3) == (l16 >> 3) && (ii & 7) < rr)
-                        sm.Ad[2 * R + (l16 >> 3)][rr * (rr - 1) / 2 + (ii & 7)] = av[e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q16 + e < l16) sm.Ad[R][l16 * (l16 - 1) / 2 + 4 * q16 + e] = av[e];
             }
         }
     }
 }
 
-// P of chunk j (its blocks above the diagonal that the output waves read are zero, written
-// once before the first chunk).
-template <bool GATED>
-__device__ __forceinline__ void make_p(FusedSmem& sm, int j, int l16, int q16) {
-    bf16x8 kf[4][4], qf[4][4];
+// P of chunk j, the tiles of one half (row blocks as for A), from the query fragments the
+// output wave already holds for Q M.  P's blocks above the diagonal that the output waves
+// read are zero, written once before the first chunk.
+template <bool GATED, int HALF>
+__device__ __forceinline__ void make_p(FusedSmem& sm, int j, const bf16x8 (&qf)[4][4], int l16, int q16) {
+    constexpr int R0 = HALF == 0 ? 0 : 1, R1 = HALF == 0 ? 3 : 2;
+    bf16x8 kf[4][4];
     load_rows(sm.K[j & 1], l16, q16, kf);
-    load_rows(sm.Q[j & 1], l16, q16, qf);
-    f32x4 G[10];
+    f32x4 G[2][4];
 #pragma unroll
-    for (int t = 0; t < 10; ++t) G[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        int t = 0;
+        for (int I = 0; I < 4; ++I) G[u][I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int I = 0; I <= R; ++I, ++t) G[t] = mma16(kf[I][ks], qf[R][ks], G[t]);
-    }
+        for (int u = 0; u < 2; ++u) {
+            const int R = u == 0 ? R0 : R1;
+#pragma unroll
+            for (int I = 0; I <= R; ++I) G[u][I] = mma16(kf[I][ks], qf[R][ks], G[u][I]);
+        }
     const float* s = &sm.sc[j % 3][0][0];
-    int t = 0;
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
+    for (int u = 0; u < 2; ++u) {
+        const int R = u == 0 ? R0 : R1;
         const int r = 16 * R + l16;
 #pragma unroll
-        for (int I = 0; I <= R; ++I, ++t) {
+        for (int I = 0; I <= R; ++I) {
             const int i0 = 16 * I + 4 * q16;
             f32x4 d = {1.f, 1.f, 1.f, 1.f};
             if (GATED) decay4(s, R, I, r, i0, d);
             f32x4 pv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = (I < R || i0 + e <= r) ? d[e] * G[t][e] : 0.f;
+            for (int e = 0; e < 4; ++e) pv[e] = (I < R || i0 + e <= r) ? d[e] * G[u][I][e] : 0.f;
             st4(&sm.P[j & 1][r][i0], pv[0], pv[1], pv[2], pv[3]);
         }
     }
 }
 
-// Wave 6, first half: T = (I + A)^{-1} into Tt (T^T).  The eight 8x8 diagonal blocks by
-// fp32 forward substitution, then the blocks below the diagonal by three levels of 2x2
-// block inversion, T21 = -T22 (A21 T11), with the inner product handed to the outer one
-// as a B operand in registers.  The zero blocks of Tt are written once, before the first
-// chunk.
+// Wave 6, first half: the two 32x32 diagonal blocks of T = (I + A)^{-1} into Tt (T^T).
+// The four 16x16 diagonal blocks by fp32 forward substitution, then the blocks below them
+// by one level of 2x2 block inversion, T21 = -T22 (A21 T11), the inner product handed to
+// the outer one as a B operand in registers.  The rest of T is never formed: the chain
+// waves finish Delta by block substitution over the two 32-token halves.  The zero blocks
+// of Tt are written once, before the first chunk.
 __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16) {
-    const int lane = 16 * q16 + l16;
     {
-        // lane = 8 * block + column c: solve (I + A_bb) x = e_c in the column order: once
+        // lane = 16 * block + column c: solve (I + A_bb) x = e_c in the column order: once
         // x[m] is final, subtract its share from every later row.  The block's strictly
-        // lower entries (28, packed) are read into registers first.
-        const int b = lane >> 3, c = lane & 7;
-        f32x4 ap[7];
+        // lower entries (120, packed) are read into registers first.
+        const int b = q16, c = l16;
+        const float* Ab_ = &sm.Ad[b][0];
+        f32x4 ap[30];
 #pragma unroll
-        for (int g = 0; g < 7; ++g) ap[g] = *reinterpret_cast<const f32x4*>(&sm.Ad[b][4 * g]);
-        float x[8];
+        for (int g = 0; g < 30; ++g) ap[g] = *reinterpret_cast<const f32x4*>(Ab_ + 4 * g);
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) x[r] = r == c ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < 7; ++m)
+        for (int m = 0; m < 15; ++m)
 #pragma unroll
-            for (int r = m + 1; r < 8; ++r) {
+            for (int r = m + 1; r < 16; ++r) {
                 const int idx = r * (r - 1) / 2 + m;
                 x[r] -= ap[idx >> 2][idx & 3] * x[m];
             }
-        bf16x8 col;
+        bf16x8 lo8, hi8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) col[e] = (__bf16)x[e];
-        *reinterpret_cast<bf16x8*>(&sm.Tt[8 * b + c][8 * b]) = col;
+        for (int e = 0; e < 8; ++e) {
+            lo8[e] = (__bf16)x[e];
+            hi8[e] = (__bf16)x[8 + e];
+        }
+        *reinterpret_cast<bf16x8*>(&sm.Tt[16 * b + c][16 * b]) = lo8;
+        *reinterpret_cast<bf16x8*>(&sm.Tt[16 * b + c][16 * b + 8]) = hi8;
     }
     wave_lds_order();
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    // level 0, the four 16x16 diagonal blocks: with L = A's lower-left 8x8 and
-    // D = diag(T00, T11) (the 8x8 inverses), T's lower-left 8x8 = -(D (L D)) there.  k = 16
-    // is padded to the instruction's 32 with zero lanes (q16 >= 2); operand parts outside
-    // the 8x8 blocks they stand for are zeroed.
-    {
-        const bool klo = q16 == 0, kin = q16 < 2;
-        f32x4 X[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int o = 16 * b;
-            // A operand L[m][k]: rows m >= 8, keys k < 8 of the diagonal block
-            const bf16x8 af = (klo && l16 >= 8) ? ld8(&sm.Ab[o + l16][o]) : zero8();
-            // B operand D[k][n] = Tt[o + n][o + k], only inside n's own 8x8 block
-            const bf16x8 bf = (kin && q16 == (l16 >> 3)) ? ld8(&sm.Tt[o + l16][o + 8 * q16]) : zero8();
-            X[b] = mma16(af, bf, z4);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int o = 16 * b;
-            // A operand D[m][k] = Tt[o + k][o + m] (transposed read), inside m's 8x8 block
-            const __bf16* src = &sm.Tt[o + 8 * (q16 & 1) + (l16 >> 2)][o + 4 * (l16 & 3)];
-            bf16x8 af = cat(trld(src), trld(src + 4 * CPITCH));
-            if (!(kin && q16 == (l16 >> 3))) af = zero8();
-            const f32x4 Y = mma16(af, acc_to_b(X[b], z4), z4);
-            // rows 8..15 (q16 >= 2), columns 0..7 (l16 < 8): T[o+4q16+e][o+l16]
-            if (q16 >= 2 && l16 < 8) st4(&sm.Tt[o + l16][o + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
-        }
-    }
-    wave_lds_order();
     // level 1, both 32x32 diagonal blocks (base 0, 32); k = 16 is padded to the
     // instruction's 32 with zero lanes (q16 >= 2)
-    {
-        const bool live = q16 < 2;
-        f32x4 X[2];
+    const bool live = q16 < 2;
+    f32x4 X[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int base = 32 * h;
-            // X = A21 T11: A rows base+16+m; B[k][n] = T11[k][n] = Tt[base+n][base+k]
-            const bf16x8 af = live ? ld8(&sm.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
-            const bf16x8 bf = live ? ld8(&sm.Tt[base + l16][base + 8 * q16]) : zero8();
-            X[h] = mma16(af, bf, z4);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int base = 32 * h;
-            // T21 = -T22 X: A operand T22[m][k] = Tt[base+16+k][base+16+m] (transposed read;
-            // k >= 16 meets the zero half of the B operand)
-            const __bf16* src = &sm.Tt[base + 16 + 8 * (q16 & 1) + (l16 >> 2)][base + 16 + 4 * (l16 & 3)];
-            const f32x4 Y = mma16(cat(trld(src), trld(src + 4 * CPITCH)), acc_to_b(X[h], z4), z4);
-            st4(&sm.Tt[base + l16][base + 16 + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
-        }
+    for (int h = 0; h < 2; ++h) {
+        const int base = 32 * h;
+        // X = A21 T11: A rows base+16+m; B[k][n] = T11[k][n] = Tt[base+n][base+k]
+        const bf16x8 af = live ? ld8(&sm.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
+        const bf16x8 bf = live ? ld8(&sm.Tt[base + l16][base + 8 * q16]) : zero8();
+        X[h] = mma16(af, bf, z4);
     }
-    wave_lds_order();
-    // level 2: T[32:64, 0:32] = -T[32:64, 32:64] (A[32:64, 0:32] T[0:32, 0:32]); 16x16 tiles
-    // (tr, tc), k = 32 in one instruction
-    {
-        f32x4 X[2][2];
 #pragma unroll
-        for (int tr = 0; tr < 2; ++tr)
-#pragma unroll
-            for (int tc = 0; tc < 2; ++tc)
-                X[tr][tc] = mma16(ld8(&sm.Ab[32 + 16 * tr + l16][8 * q16]), ld8(&sm.Tt[16 * tc + l16][8 * q16]), z4);
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc) {
-            const bf16x8 xb = acc_to_b(X[0][tc], X[1][tc]);
-#pragma unroll
-            for (int tr = 0; tr < 2; ++tr) {
-                // A operand T[32+16tr+m][32+k] = Tt[32+k][32+16tr+m], k = 8 q16 + e
-                const __bf16* src = &sm.Tt[32 + 8 * q16 + (l16 >> 2)][32 + 16 * tr + 4 * (l16 & 3)];
-                const f32x4 Y = mma16(cat(trld(src), trld(src + 4 * CPITCH)), xb, z4);
-                st4(&sm.Tt[16 * tc + l16][32 + 16 * tr + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
-            }
-        }
+    for (int h = 0; h < 2; ++h) {
+        const int base = 32 * h;
+        // T21 = -T22 X: A operand T22[m][k] = Tt[base+16+k][base+16+m] (transposed read;
+        // k >= 16 meets the zero half of the B operand)
+        const __bf16* src = &sm.Tt[base + 16 + 8 * (q16 & 1) + (l16 >> 2)][base + 16 + 4 * (l16 & 3)];
+        const f32x4 Y = mma16(cat(trld(src), trld(src + 4 * CPITCH)), acc_to_b(X[h], z4), z4);
+        st4(&sm.Tt[base + l16][base + 16 + 4 * q16], -Y[0], -Y[1], -Y[2], -Y[3]);
     }
 }
 
@@ -479,8 +440,12 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         for (int j = 0; j < nph; ++j) {
             const bool live = j < nc;
             const float* s = &sm.sc[j % 3][0][0];
-            bf16x8 rb[2];
+            bf16x8 rb0;   // R rows 0..31 as B operand (k = token)
+            f32x4 R[4];   // R, token tile t: tokens 16 t + 4 q16 + e, column jc + l16
+            bf16x8 abl[2];  // A rows 32..63, tokens 0..31 (read here: the A waves rewrite Ab in .2)
             if (live) {
+#pragma unroll
+                for (int t = 2; t < 4; ++t) abl[t - 2] = ld8(&sm.Ab[16 * t + l16][8 * q16]);
                 // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
                 f32x4 X[4];
 #pragma unroll
@@ -491,7 +456,6 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                     for (int t = 0; t < 4; ++t)
                         X[t] = mma16(ld8(&sm.K[j & 1][16 * t + l16][32 * ks + 8 * q16]), mb[ks], X[t]);
                 // R = beta (V - exp(gamma) X); V read transposed: lane gets 4 tokens of its column
-                f32x4 R[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int r0 = 16 * t + 4 * q16;
@@ -502,23 +466,28 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                     for (int e = 0; e < 4; ++e) R[t][e] = bt[e] * ((float)vv[e] - eg[e] * X[t][e]);
                 }
-                rb[0] = acc_to_b(R[0], R[1]);
-                rb[1] = acc_to_b(R[2], R[3]);
+                rb0 = acc_to_b(R[0], R[1]);
             }
             __syncthreads();
             if (live) {
-                // Delta = T R (T lower triangular: token tile t needs k < 16 (t + 1)); A
-                // operand T[16 t + m][k] = Tt[k][16 t + m] by transposed reads
+                // Delta = T R by block substitution over the two 32-token halves:
+                //   Delta_top = T_TL R_top;  Delta_bot = T_BR (R_bot - A_BL Delta_top).
+                // T operands T[16 t + m][k] = Tt[k][16 t + m] by transposed reads.
                 f32x4 D[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 2; ++t) {
+                    const __bf16* src = &sm.Tt[8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
+                    D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+                const bf16x8 dtop = acc_to_b(-D[0], -D[1]);
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                for (int t = 2; t < 4; ++t) R[t] = mma16(abl[t - 2], dtop, R[t]);
+                const bf16x8 zb = acc_to_b(R[2], R[3]);
 #pragma unroll
-                    for (int t = 2 * u; t < 4; ++t) {
-                        const __bf16* src = &sm.Tt[32 * u + 8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
-                        D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb[u], D[t]);
-                    }
+                for (int t = 2; t < 4; ++t) {
+                    const __bf16* src = &sm.Tt[32 + 8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
+                    D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), zb, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
                 bf16x8 db[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
@@ -561,9 +530,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 for (int e = 0; e < 4; ++e)
                     a.hT[((long)w.nh * FD + 16 * mt + 4 * q16 + e) * FD + w.j0 + jc + l16] = M[mt][e];
         }
-    } else if (wave < 2 * NCW) {
+    } else if (wave == 3 || wave == 7) {
         // ----------------------------------------------------------- output waves
-        const int cw = wave - NCW, jc = CW * cw;
+        const int cw = wave == 3 ? 0 : 1, jc = CW * cw;
         __bf16* const obase = static_cast<__bf16*>(a.o) + (long)w.h * FD + w.j0 + jc;
         f32x4 Y[4];  // Y = Q M of the previous chunk: token 16 t + 4 q16 + e, column jc + l16
         __syncthreads();
@@ -600,8 +569,10 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             }
             __syncthreads();
             if (j < nc) {
-                // Y = Q M with the chain's bf16 state at the start of chunk j
-                bf16x8 m4[4];
+                // Y = Q M with the chain's bf16 state at the start of chunk j, then half of
+                // P of chunk j from the same query fragments
+                bf16x8 qf[4][4], m4[4];
+                load_rows(sm.Q[j & 1], l16, q16, qf);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) m4[ks] = sm.mb[j & 1][cw][ks][lane];
 #pragma unroll
@@ -609,14 +580,15 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        Y[t] = mma16(ld8(&sm.Q[j & 1][16 * t + l16][32 * ks + 8 * q16]), m4[ks], Y[t]);
+                    for (int t = 0; t < 4; ++t) Y[t] = mma16(qf[t][ks], m4[ks], Y[t]);
+                if (cw == 0) make_p<GATED, 0>(sm, j, qf, l16, q16);
+                else make_p<GATED, 1>(sm, j, qf, l16, q16);
             }
             __syncthreads();
         }
-    } else if (wave < 2 * NCW + 2) {
+    } else if (wave == 4 || wave == 5) {
         // ---------------------------------------------------------------- loaders
-        const int lt = tid - 64 * 2 * NCW;
+        const int lt = tid - 256;
         Streams st;
         make_streams(a, w, lt, st);
         LoadSet f0, f1;   // even chunks in f0, odd chunks in f1
@@ -641,16 +613,14 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             fetch(st, j + 4, f0);
             __syncthreads();
         }
-    } else if (wave == 2 * NCW + 2) {
+    } else if (wave == 6) {
         // ------------------------------------------ wave 6: T of j, half of A of j + 1
         // zero blocks, written once: Tt below its block diagonal, P above its diagonal in
         // the tiles the output waves read (rows 0-15 x keys 16-31, rows 32-47 x keys 48-63)
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int v = lane + 64 * p, r = v >> 3, cg = v & 7;
-            const bool below = cg * 8 + 8 <= (r >> 4) * 16;                  // left of the 16x16 diagonal
-            const bool inner = (r & 8) && cg * 8 == (r >> 4) * 16;           // upper-right 8x8 of T inside it
-            if (below || inner) *reinterpret_cast<bf16x8*>(&sm.Tt[r][cg * 8]) = zero8();
+            if (cg * 8 + 8 <= (r >> 4) * 16) *reinterpret_cast<bf16x8*>(&sm.Tt[r][cg * 8]) = zero8();
         }
 #pragma unroll
         for (int bf = 0; bf < 2; ++bf)
@@ -672,12 +642,11 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             __syncthreads();
         }
     } else {
-        // ------------------------------------------ wave 7: P of j, half of A of j + 1
+        // -------------------------------------------- wave 2: other half of A of j + 1
         __syncthreads();
         make_a<GATED, 1>(sm, 0, l16, q16);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            if (j < nc) make_p<GATED>(sm, j, l16, q16);
             __syncthreads();
             if (j + 1 < nc) make_a<GATED, 1>(sm, j + 1, l16, q16);
             __syncthreads();
