@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=50)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy five times (calibrates rocprofv3's "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the mixer "
@@ -117,6 +120,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = 512 << 20
+        src = torch.zeros(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+        return
 
     def to_dev(a):
         if a is None:
@@ -206,7 +218,7 @@ def main():
                    "heads": Hv, "head_dim": D, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_p,
-                     "kernel": "dn_chunk_fwd (prep_kernel + state_kernel)",
+                     "kernel": "fused_kernel<false> (the only kernel of a dn_chunk_fwd call)",
                      "call_us": call_us, "algorithmic_bytes": alg_b},
         "mfma": {"algorithmic_flops": alg_f, "tflops": alg_f / (call_us * 1e-6) / 1e12,
                  "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
