@@ -22,7 +22,7 @@
 //
 //   wave      SIMD  first half (.1)                    second half (.2)
 //   0, 1      0, 1  chain, chunk j: X = K M, R         Delta, state update
-//   3, 7      3     output: O of chunk j - 1           Y = Q M and half of P, chunk j
+//   3, 7      3     output: O of chunk j - 1, Y = Q M  half of P of chunk j
 //   4, 5      0, 1  loaders: K, Q, scalars of j + 1    V of j + 1; fetch chunk j + 3
 //   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, half
 //   2         2     -                                  A of chunk j + 1, other half
@@ -47,9 +47,15 @@ constexpr int DVS = 32;            // state columns per workgroup
 constexpr int NSL = FD / DVS;      // slices per (sequence, value head)
 constexpr int CW = 16;             // state columns per chain wave
 constexpr int NCW = DVS / CW;      // chain waves
-constexpr int KPITCH = FD + 8;     // bf16 row pitches: 16-byte multiples that put the
-constexpr int CPITCH = FC + 8;     //   16 rows of one MFMA operand read on distinct banks
-constexpr int VPITCH = DVS + 8;
+// bf16 row pitches.  gfx950's LDS serves a 16-byte-per-lane read 32 lanes at a time
+// across 128 four-byte banks (measured: this model predicts which pitches run
+// conflict-free).  An operand read takes 16 rows x 2 chunks per 32 lanes, so the 16 row
+// offsets (pitch in dwords x row, mod 128) must be distinct multiples of 8: 72 dwords for
+// the 128-wide K and Q rows, 40 for the 64-wide T, P and A rows.  V (read only transposed,
+// 16 rows x 8 dwords) takes 24.
+constexpr int KPITCH = FD + 16;
+constexpr int CPITCH = FC + 16;
+constexpr int VPITCH = DVS + 16;
 constexpr int NT = 512;            // threads (8 waves)
 constexpr int NLD = 128;           // loader threads (waves 4, 5)
 
@@ -66,8 +72,9 @@ struct alignas(16) FusedSmem {
     __bf16 Tt[FC][CPITCH];         // T^T of the chunk being processed
     __bf16 P[2][FC][CPITCH];       // P, row r = query token (chunk j in P[j & 1])
     __bf16 Ab[FC][CPITCH];         // A in bf16 (blocks below the 16x16 block diagonal)
-    float Ad[4][128];              // A's diagonal 16x16 blocks, fp32, strictly lower part
-                                   //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m
+    float Ad[4][132];              // A's diagonal 16x16 blocks, fp32, strictly lower part
+                                   //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m;
+                                   //   block pitch 132: the four blocks' reads on distinct banks
     bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
     __bf16 OT[NCW][CW][CPITCH];    // output waves: O tile, column-major, for row stores
@@ -534,7 +541,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         // ----------------------------------------------------------- output waves
         const int cw = wave == 3 ? 0 : 1, jc = CW * cw;
         __bf16* const obase = static_cast<__bf16*>(a.o) + (long)w.h * FD + w.j0 + jc;
-        f32x4 Y[4];  // Y = Q M of the previous chunk: token 16 t + 4 q16 + e, column jc + l16
+        f32x4 Y[4];          // Y = Q M: token 16 t + 4 q16 + e, column jc + l16
+        bf16x8 qf[4][4];     // query fragments of the current chunk (for Y here, P in .2)
         __syncthreads();
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
@@ -567,11 +575,10 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                     if (r < len) *reinterpret_cast<bf16x4*>(obase + (t0 + r) * a.Hv * FD + 4 * q16) = ov;
                 }
             }
-            __syncthreads();
             if (j < nc) {
-                // Y = Q M with the chain's bf16 state at the start of chunk j, then half of
-                // P of chunk j from the same query fragments
-                bf16x8 qf[4][4], m4[4];
+                // Y = Q M with the chain's bf16 state at the start of chunk j (written at the
+                // end of the previous phase)
+                bf16x8 m4[4];
                 load_rows(sm.Q[j & 1], l16, q16, qf);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) m4[ks] = sm.mb[j & 1][cw][ks][lane];
@@ -581,6 +588,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                     for (int t = 0; t < 4; ++t) Y[t] = mma16(qf[t][ks], m4[ks], Y[t]);
+            }
+            __syncthreads();
+            if (j < nc) {  // half of P of chunk j from the same query fragments
                 if (cw == 0) make_p<GATED, 0>(sm, j, qf, l16, q16);
                 else make_p<GATED, 1>(sm, j, qf, l16, q16);
             }
