@@ -23,7 +23,7 @@
 //   wave      SIMD  first half (.1)                    second half (.2)
 //   0, 1      0, 1  chain, chunk j: X = K M, R         Delta, state update
 //   3, 7      3     output: O of chunk j - 1, Y = Q M  half of P of chunk j
-//   4, 5      0, 1  loaders: K, Q, scalars of j + 1    V of j + 1; fetch chunk j + 3
+//   4, 5      0, 1  loaders: K, Q, scalars of j + 1    V of j + 1; fetch j + 3; store O of j - 1
 //   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, half
 //   2         2     -                                  A of chunk j + 1, other half
 //
@@ -77,7 +77,8 @@ struct alignas(16) FusedSmem {
                                    //   block pitch 132: the four blocks' reads on distinct banks
     bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
-    __bf16 OT[NCW][CW][CPITCH];    // output waves: O tile, column-major, for row stores
+    __bf16 OT[DVS][CPITCH];        // O of the previous chunk, column-major (output waves write,
+                                   //   loader waves store it to HBM in the second half)
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
 };
 
@@ -91,9 +92,6 @@ struct Geo {  // where this workgroup works
     int n, h, hq, j0, nh, nchunks;
 };
 
-__device__ __forceinline__ int chunk_len(const Geo& w, int j) {
-    return (int)min((long)FC, w.eos - (w.bos + (long)j * FC));
-}
 
 // ------------------------------------------------------------------------ loaders
 // Raw buffer loads: the descriptor of each stream covers exactly the sequence's own
@@ -103,7 +101,7 @@ __device__ __forceinline__ int chunk_len(const Geo& w, int j) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct Streams {
-    __amdgpu_buffer_rsrc_t k, q, v, beta, g;
+    __amdgpu_buffer_rsrc_t k, q, v, beta, g, o;
     uint32_t kq_chunk, v_chunk, s_chunk;   // bytes per chunk of 64 tokens
     uint32_t off_kq[8], off_v[2], off_s;   // this lane's piece offsets within a chunk
 };
@@ -124,6 +122,7 @@ __device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w,
     st.v = rsrc(static_cast<const __bf16*>(a.v) + v0, v_end);
     st.beta = rsrc(a.beta + s0, s_end);
     st.g = rsrc(a.g ? a.g + s0 : a.beta + s0, a.g ? s_end : 0);
+    st.o = rsrc(static_cast<__bf16*>(a.o) + v0, v_end);   // o has v's layout
     st.kq_chunk = FC * kq_tok;
     st.v_chunk = FC * v_tok;
     st.s_chunk = FC * s_tok;
@@ -194,6 +193,20 @@ __device__ __forceinline__ void put_kq(FusedSmem& sm, int j, int lt, const LoadS
     }
 }
 
+// O of chunk j from the column-major tile to HBM: loader lane lt takes token
+// 16 (g & 3) + i and columns 16 (g >> 2) .. +15 (g = lt / 16, i = lt % 16), gathered by four
+// transposed reads.  Buffer stores: tokens past the sequence end, and chunks outside it
+// (j < 0 or j >= nchunks), fall outside the descriptor and are dropped by the hardware.
+__device__ __forceinline__ void store_o(const FusedSmem& sm, const Streams& st, int j, int lt) {
+    const int g = lt >> 4, i = lt & 15, tok = 16 * (g & 3) + i, c0 = 16 * (g >> 2);
+    bf16x4 p[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = trld(&sm.OT[c0 + 4 * k + (i >> 2)][16 * (g & 3) + 4 * (i & 3)]);
+    const uint32_t off = j < 0 ? 0xfffffff0u : (uint32_t)(j * FC + tok) * (st.v_chunk / FC) + c0 * 2;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat(p[0], p[1])), st.o, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat(p[2], p[3])), st.o, off + 16, 0, 0);
+}
+
 __device__ __forceinline__ void put_v(FusedSmem& sm, int lt, const LoadSet& f) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -232,12 +245,14 @@ __device__ __forceinline__ void decay4(const float* s, int R, int I, int r, int 
     }
 }
 
-// A of chunk j, the tiles of one half: half 0 = row blocks 0, 3 (tiles (0,0), (0..3,3)),
-// half 1 = row blocks 1, 2 (tiles (0..1,1), (0..2,2)); five tiles each.  Below the block
-// diagonal A goes to Ab in bf16, the diagonal blocks to Ad in fp32 (packed).
+// A of chunk j, the tiles of one part (part 0 goes to the wave that also runs the UT
+// inverse).  Without decay: part 0 = row blocks 0, 1 (three tiles), part 1 = row blocks 2, 3
+// (seven tiles); with decay, whose masks cost more per tile: row blocks 0, 3 and 1, 2 (five
+// tiles each).  Below the block diagonal A goes to Ab in bf16, the diagonal blocks to Ad in
+// fp32 (packed).
 template <bool GATED, int HALF>
 __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
-    constexpr int R0 = HALF == 0 ? 0 : 1, R1 = HALF == 0 ? 3 : 2;
+    constexpr int R0 = HALF == 0 ? 0 : (GATED ? 1 : 2), R1 = HALF == 0 ? (GATED ? 3 : 1) : (GATED ? 2 : 3);
     bf16x8 kf[4][4];
     load_rows(sm.K[j & 1], l16, q16, kf);
     f32x4 G[2][4];
@@ -540,7 +555,6 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     } else if (wave == 3 || wave == 7) {
         // ----------------------------------------------------------- output waves
         const int cw = wave == 3 ? 0 : 1, jc = CW * cw;
-        __bf16* const obase = static_cast<__bf16*>(a.o) + (long)w.h * FD + w.j0 + jc;
         f32x4 Y[4];          // Y = Q M: token 16 t + 4 q16 + e, column jc + l16
         bf16x8 qf[4][4];     // query fragments of the current chunk (for Y here, P in .2)
         __syncthreads();
@@ -562,18 +576,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    st4(&sm.OT[cw][l16][16 * t + 4 * q16], a.scale * Y[t][0], a.scale * Y[t][1], a.scale * Y[t][2],
+                    st4(&sm.OT[jc + l16][16 * t + 4 * q16], a.scale * Y[t][0], a.scale * Y[t][1], a.scale * Y[t][2],
                         a.scale * Y[t][3]);
-                wave_lds_order();
-                // rows back by transposed reads: lane gets token 16 k + l16, columns 4 q16 .. +3
-                const long t0 = w.bos + (long)jp * FC;
-                const int len = chunk_len(w, jp);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const bf16x4 ov = trld(&sm.OT[cw][4 * q16 + (l16 >> 2)][16 * k + 4 * (l16 & 3)]);
-                    const int r = 16 * k + l16;
-                    if (r < len) *reinterpret_cast<bf16x4*>(obase + (t0 + r) * a.Hv * FD + 4 * q16) = ov;
-                }
             }
             if (j < nc) {
                 // Y = Q M with the chain's bf16 state at the start of chunk j (written at the
@@ -616,11 +620,13 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             __syncthreads();
             put_v(sm, lt, f1);
             fetch(st, j + 3, f1);
+            store_o(sm, st, j - 1, lt);   // written by the output waves in this phase's first half
             __syncthreads();
             put_kq(sm, j + 2, lt, f0);
             __syncthreads();
             put_v(sm, lt, f0);
             fetch(st, j + 4, f0);
+            store_o(sm, st, j, lt);
             __syncthreads();
         }
     } else if (wave == 6) {
@@ -667,7 +673,10 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 }  // namespace
 
 bool prefill_fused_supported(const PrefillArgs& a) {
-    return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC;
+    // buffer offsets are 32-bit: a sequence (plus the two chunks fetched past its end) must
+    // span less than 2 GiB of q / k / v / o
+    const long span = ((long)a.T + 2 * FC) * (a.Hqk > a.Hv ? a.Hqk : a.Hv) * FD * 2;
+    return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC && span < (1L << 31);
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s) {
