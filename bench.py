@@ -1,12 +1,14 @@
 """Benchmark of the delta-rule mixer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--decode-reps R]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--decode-reps R] [--eager]
 
 One step is one prefill call (dn_chunk_fwd) over the DeltaNet layer-prefill workload
 (B=4, H=16, T=2048, d_k=d_v=128, bf16 q/k/v, fp32 beta, no decay, zero initial state,
-final state returned): 8192 tokens.  K steps are timed back to back between two
-device synchronisations, cycling through several copies of the inputs so the working
-set (> 256 MB) does not stay in the Infinity Cache between steps.  The decode step
+final state returned): 8192 tokens.  K steps run back to back between two device
+synchronisations, cycling through several copies of the inputs so the working set
+(> 256 MB) does not stay in the Infinity Cache between steps.  The K steps are captured
+once in a HIP graph and the replay is timed (--eager times the Python launch loop); each
+call's kernel time is also taken with HIP events on the launching stream.  The decode step
 (256 sequences x 32 heads, state updated in place) is timed the same way and reported
 in the same line.  The fp64 oracle is timed on the host cores on a bounded sample of
 the prefill workload.
@@ -103,6 +105,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=50)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager launch loop instead of a HIP-graph replay of it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy five times (calibrates rocprofv3's "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -159,6 +163,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    # per-call kernel time: HIP events around each eager call on the launching stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -168,8 +173,29 @@ def main():
         step(i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
     ev_ms = [a.elapsed_time(b) for a, b in evs]
+    if args.eager:
+        wall = wall_eager
+    else:
+        # the K steps captured once in a HIP graph and replayed: the launch loop of a
+        # serving engine, without Python's per-call overhead between kernels
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     tokens = B * T
     call_us = float(np.mean(ev_ms)) * 1e3
@@ -220,6 +246,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_p,
                      "kernel": "fused_kernel<false> (the only kernel of a dn_chunk_fwd call)",
                      "call_us": call_us, "algorithmic_bytes": alg_b},
+        "timing": {"loop": "eager" if args.eager else "hip_graph_replay",
+                   "ms_per_step_eager": wall_eager * 1e3 / args.steps},
         "mfma": {"algorithmic_flops": alg_f, "tflops": alg_f / (call_us * 1e-6) / 1e12,
                  "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
         "decode": {"workload": "gated decode step, 256 sequences x 32 heads, d=128, bf16, fp32 state "

@@ -198,3 +198,49 @@ def test_outputs_fully_written_and_deterministic():
         assert not torch.isnan(o).any() and not torch.isnan(s).any()
         outs.append((o, s))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_graph_replay_matches_eager():
+    """A HIP graph capturing prefill and decode calls replays to the eager results, every
+    replay, with eager work and synchronisations between replays (the library allocates
+    nothing and records no memset inside a call)."""
+    _say("graph replay")
+    x = make_config(2)
+    d = to_inputs(x)
+    B, T, H, D = x.B, x.T, x.Hv, x.Dk
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    y = make_config(4)
+    e = to_inputs(y)
+    st = e["init"].clone()
+    od = torch.empty((y.B, y.Hv, y.Dv), dtype=torch.bfloat16, device="cuda")
+    dargs = (e["q"][:, 0].contiguous(), e["k"][:, 0].contiguous(), e["v"][:, 0].contiguous(),
+             e["beta"][:, 0].contiguous(), e["g"][:, 0].contiguous())
+
+    def calls():
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, None, out=o, final_state=fs)
+        dn.decode_step(*dargs, st, out=od)
+
+    st.copy_(e["init"])
+    calls()
+    torch.cuda.synchronize()
+    ref = (o.clone(), fs.clone(), od.clone(), st.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.copy_(e["init"])
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        o.zero_(), fs.zero_(), od.zero_()
+        st.copy_(e["init"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((o, fs, od, st), ref, ("o", "final_state", "decode o", "state")):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager call"
+        _ = (o.float().sum() + 1).item()   # eager work between replays
