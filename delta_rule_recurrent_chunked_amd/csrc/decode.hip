@@ -11,11 +11,11 @@
 //   M     <- a M + k delta^T
 // The state is read once and written once: this kernel is bound by HBM bandwidth.
 //
-// Work decomposition: one workgroup per (n, h, slice of CW value columns).  A thread
-// owns a float4 of CW/4 consecutive columns in RPT rows, so a wave reads whole
-// CW*4-byte row segments and every state byte moves through one 128-bit load and one
-// 128-bit store.  Column sums over the key dim reduce across lanes (xor shuffles),
-// then across the waves of the workgroup through LDS.
+// Work decomposition: one workgroup per (n, h, slice of CW value columns; CW = Dv).  A
+// thread owns a float4 of columns in RPT rows, so a wave reads whole CW*4-byte row
+// segments and every state byte moves through one 128-bit load and one 128-bit store,
+// both nontemporal (the state streams through once).  Column sums over the key dim
+// reduce across lanes (xor shuffles), then across the waves of the workgroup through LDS.
 #include "internal.h"
 
 namespace dn {
@@ -51,10 +51,13 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     const T* kp = static_cast<const T*>(a.k) + ((long)n * a.Hqk + hq) * DK;
     float* Mp = a.state + (long)nh * DK * DV + slice * CW + ct * 4;
 
-    float4 m[RPT];
+    // the state streams through once: nontemporal loads and stores keep it from
+    // displacing q, k, v in the caches
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    f32x4v m[RPT];
 #pragma unroll
     for (int p = 0; p < RPT; ++p)
-        m[p] = *reinterpret_cast<const float4*>(Mp + (long)(p * RPP + rg) * DV);
+        m[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(Mp + (long)(p * RPP + rg) * DV));
     float kr[RPT], qr[RPT];
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
@@ -67,8 +70,11 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
-        pk[0] += m[p].x * kr[p]; pk[1] += m[p].y * kr[p]; pk[2] += m[p].z * kr[p]; pk[3] += m[p].w * kr[p];
-        pq[0] += m[p].x * qr[p]; pq[1] += m[p].y * qr[p]; pq[2] += m[p].z * qr[p]; pq[3] += m[p].w * qr[p];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pk[c] += m[p][c] * kr[p];
+            pq[c] += m[p][c] * qr[p];
+        }
         if (ct == 0) kq += kr[p] * qr[p];
     }
     // reduce over the row groups of this wave (lanes that share ct)
@@ -108,18 +114,18 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     const float d0 = dsh[ct * 4 + 0], d1 = dsh[ct * 4 + 1], d2 = dsh[ct * 4 + 2], d3 = dsh[ct * 4 + 3];
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
-        float4 r;
-        r.x = alpha * m[p].x + kr[p] * d0;
-        r.y = alpha * m[p].y + kr[p] * d1;
-        r.z = alpha * m[p].z + kr[p] * d2;
-        r.w = alpha * m[p].w + kr[p] * d3;
-        *reinterpret_cast<float4*>(Mp + (long)(p * RPP + rg) * DV) = r;
+        f32x4v r;
+        r[0] = alpha * m[p][0] + kr[p] * d0;
+        r[1] = alpha * m[p][1] + kr[p] * d1;
+        r[2] = alpha * m[p][2] + kr[p] * d2;
+        r[3] = alpha * m[p][3] + kr[p] * d3;
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4v*>(Mp + (long)(p * RPP + rg) * DV));
     }
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_dims(const DecodeArgs& a, hipStream_t s) {
-    constexpr int CW = DV < 32 ? DV : 32;
+    constexpr int CW = DV;   // one workgroup per (sequence, head): 16 float4 of state per thread at d = 128
     using S = DecodeShape<DK, CW>;
     const long blocks = (long)a.N * a.Hv * (DV / CW);
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
