@@ -54,6 +54,10 @@ __device__ __forceinline__ bf16x8 zero8() {
 // one wave's instructions in order; this only stops the compiler from reordering them).
 __device__ __forceinline__ void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
 
+// Scheduling fence: the compiler moves no instruction across it (used to issue a step's
+// LDS reads together, so that one round trip covers them all).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -22,17 +22,20 @@
 //
 //   wave      SIMD  first half (.1)                    second half (.2)
 //   0, 1      0, 1  chain, chunk j: X = K M, R         Delta, state update
-//   3, 7      3     output: O of chunk j - 1, Y = Q M  half of P of chunk j
-//   4, 5      0, 1  loaders: K, Q, scalars of j + 1    V of j + 1; fetch j + 3; store O of j - 1
-//   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, half
-//   2         2     -                                  A of chunk j + 1, other half
+//   3, 7      3     output: O of chunk j - 1, Y = Q M  P of chunk j
+//                   (each wave: two 16-token row blocks, all 32 columns)
+//   4, 5      0, 1  loaders: K, scalars of j + 1       Q, V of j + 1; fetch j + 3; store O of j - 1
+//   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, diagonal tiles
+//   2         2     -                                  A of chunk j + 1, tiles below them
 //
-// The UT inverse, the longest serial step, has SIMD 2 to itself in the first half.
+// The UT inverse, the longest serial step, has SIMD 2 to itself in the first half; the
+// wave that runs it builds A's diagonal tiles itself and keeps them in registers.
 //
 // Chain wave w owns state columns 16w .. 16w+15 of the slice as eight 16x16 fp32
 // accumulator tiles; products that consume its results take them as B operands through
 // register lane swaps (acc_to_b).  The output waves get the chain's bf16 state and Delta
-// fragments through LDS.  LDS holds K and Q double-buffered, one V, T and A, two P.
+// fragments through LDS and use them as the A operands of the transposed products; P stays
+// in their registers.  LDS holds K and Q double-buffered, one V, T, A and O tile.
 #include <type_traits>
 
 #include "internal.h"
@@ -56,6 +59,7 @@ constexpr int NCW = DVS / CW;      // chain waves
 constexpr int KPITCH = FD + 16;
 constexpr int CPITCH = FC + 16;
 constexpr int VPITCH = DVS + 16;
+constexpr int OPITCH = DVS + 8;
 constexpr int NT = 512;            // threads (8 waves)
 constexpr int NLD = 128;           // loader threads (waves 4, 5)
 
@@ -70,15 +74,14 @@ struct alignas(16) FusedSmem {
     __bf16 Q[2][FC][KPITCH];       // chunk queries, token-major
     __bf16 V[FC][VPITCH];          // value slice of the next chunk the chain reads
     __bf16 Tt[FC][CPITCH];         // T^T of the chunk being processed
-    __bf16 P[2][FC][CPITCH];       // P, row r = query token (chunk j in P[j & 1])
     __bf16 Ab[FC][CPITCH];         // A in bf16 (blocks below the 16x16 block diagonal)
     float Ad[4][132];              // A's diagonal 16x16 blocks, fp32, strictly lower part
                                    //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m;
                                    //   block pitch 132: the four blocks' reads on distinct banks
     bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
-    __bf16 OT[DVS][CPITCH];        // O of the previous chunk, column-major (output waves write,
-                                   //   loader waves store it to HBM in the second half)
+    __bf16 O[FC][OPITCH];          // O of the previous chunk, token-major (the output waves write
+                                   //   it, the loader waves store it to HBM in the second half)
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
 };
 
@@ -164,13 +167,12 @@ __device__ __forceinline__ float lane_f32(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-// K, Q and the per-token scalars of chunk j (rows past the sequence end hold zeros)
-__device__ __forceinline__ void put_kq(FusedSmem& sm, int j, int lt, const LoadSet& f) {
+// K and the per-token scalars of chunk j (rows past the sequence end hold zeros)
+__device__ __forceinline__ void put_k(FusedSmem& sm, int j, int lt, const LoadSet& f) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int v = lt + NLD * p, row = v >> 4, cg = v & 15;
         *reinterpret_cast<uint4*>(&sm.K[j & 1][row][cg * 8]) = f.k[p];
-        *reinterpret_cast<uint4*>(&sm.Q[j & 1][row][cg * 8]) = f.q[p];
     }
     if (lt < FC) {  // one wave: inclusive scan of the log decays over the chunk (DPP)
         float gv = f.g;
@@ -193,18 +195,28 @@ __device__ __forceinline__ void put_kq(FusedSmem& sm, int j, int lt, const LoadS
     }
 }
 
-// O of chunk j from the column-major tile to HBM: loader lane lt takes token
-// 16 (g & 3) + i and columns 16 (g >> 2) .. +15 (g = lt / 16, i = lt % 16), gathered by four
-// transposed reads.  Buffer stores: tokens past the sequence end, and chunks outside it
-// (j < 0 or j >= nchunks), fall outside the descriptor and are dropped by the hardware.
+// O of chunk j from the token-major tile to HBM: loader lane lt stores the 16-byte pieces
+// lt and lt + 128 (token piece / 4, columns 8 (piece % 4) ..).  Buffer stores: tokens past
+// the sequence end, and chunks outside it (j < 0 or j >= nchunks), fall outside the
+// descriptor and are dropped by the hardware.
 __device__ __forceinline__ void store_o(const FusedSmem& sm, const Streams& st, int j, int lt) {
-    const int g = lt >> 4, i = lt & 15, tok = 16 * (g & 3) + i, c0 = 16 * (g >> 2);
-    bf16x4 p[4];
+    const uint32_t tok_bytes = st.v_chunk / FC;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) p[k] = trld(&sm.OT[c0 + 4 * k + (i >> 2)][16 * (g & 3) + 4 * (i & 3)]);
-    const uint32_t off = j < 0 ? 0xfffffff0u : (uint32_t)(j * FC + tok) * (st.v_chunk / FC) + c0 * 2;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat(p[0], p[1])), st.o, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat(p[2], p[3])), st.o, off + 16, 0, 0);
+    for (int pp = 0; pp < 2; ++pp) {
+        const int piece = lt + NLD * pp, tok = piece >> 2, cg = piece & 3;
+        const bf16x8 v = ld8(&sm.O[tok][8 * cg]);
+        const uint32_t off = j < 0 ? 0xfffffff0u : (uint32_t)(j * FC + tok) * tok_bytes + 16 * cg;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), st.o, off, 0, 0);
+    }
+}
+
+// Q of chunk j
+__device__ __forceinline__ void put_q(FusedSmem& sm, int j, int lt, const LoadSet& f) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = lt + NLD * p, row = v >> 4, cg = v & 15;
+        *reinterpret_cast<uint4*>(&sm.Q[j & 1][row][cg * 8]) = f.q[p];
+    }
 }
 
 __device__ __forceinline__ void put_v(FusedSmem& sm, int lt, const LoadSet& f) {
@@ -230,75 +242,104 @@ __device__ __forceinline__ void load_rows(const __bf16 (*src)[KPITCH], int l16, 
 // k_i . k_r (or k_i . q_r) with i = 16 I + 4 q16 + e, r = 16 R + l16, so each lane owns
 // four consecutive columns i of one row r: 8-byte stores.  Rows past the sequence end
 // need no mask: their keys, queries and beta are zero.
-__device__ __forceinline__ void decay4(const float* s, int R, int I, int r, int i0, f32x4& d) {
-    // exp(gamma_r - gamma_i), i = i0 .. i0 + 3 <= r (diagonal tile: direct; below: factors)
-    if (I == R) {
-        const float gr = s[SC_GAM * FC + r];
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(&s[SC_GAM * FC + i0]);
+struct DecayIn {  // what exp(gamma_r - gamma_i), i = i0 .. i0 + 3 <= r, is made from
+    float a;       // diagonal tile: gamma_r; below it: F1[I][r]
+    f32x4 b;       // diagonal tile: gamma_i; below it: F2[i]
+};
+__device__ __forceinline__ DecayIn decay_load(const float* s, int R, int I, int r, int i0) {
+    DecayIn x;
+    x.a = I == R ? s[SC_GAM * FC + r] : s[(SC_F1 + I) * FC + r];
+    x.b = *reinterpret_cast<const f32x4*>(&s[(I == R ? SC_GAM : SC_F2) * FC + i0]);
+    return x;
+}
+__device__ __forceinline__ f32x4 decay_eval(const DecayIn& x, bool diag) {
+    f32x4 d;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = __expf(fminf(gr - gi[e], 0.f));
-    } else {
-        const float f1 = s[(SC_F1 + I) * FC + r];
-        const f32x4 f2 = *reinterpret_cast<const f32x4*>(&s[SC_F2 * FC + i0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = f1 * f2[e];
-    }
+    for (int e = 0; e < 4; ++e) d[e] = diag ? __expf(fminf(x.a - x.b[e], 0.f)) : x.a * x.b[e];
+    return d;
 }
 
-// A of chunk j, the tiles of one part (part 0 goes to the wave that also runs the UT
-// inverse).  Without decay: part 0 = row blocks 0, 1 (three tiles), part 1 = row blocks 2, 3
-// (seven tiles); with decay, whose masks cost more per tile: row blocks 0, 3 and 1, 2 (five
-// tiles each).  Below the block diagonal A goes to Ab in bf16, the diagonal blocks to Ad in
-// fp32 (packed).
-template <bool GATED, int HALF>
+// A of chunk j, one part of its tiles (I, R).  Part 0, the four diagonal tiles, goes to
+// Ad in fp32 (strictly lower part, packed); part 1, the six tiles below them, to Ab in bf16.
+constexpr int a_tiles(int part) { return part == 0 ? 4 : 6; }
+constexpr int a_tile_i(int part, int n) { return part == 0 ? n : (n == 2 || n == 4) ? 1 : n == 5 ? 2 : 0; }
+constexpr int a_tile_r(int part, int n) { return part == 0 ? n : n == 0 ? 1 : n <= 2 ? 2 : 3; }
+
+template <bool GATED, int PART>
 __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
-    constexpr int R0 = HALF == 0 ? 0 : (GATED ? 1 : 2), R1 = HALF == 0 ? (GATED ? 3 : 1) : (GATED ? 2 : 3);
+    constexpr int NTL = a_tiles(PART);
+    // every LDS read before the first store (a read after a store waits a round trip)
+    const float* s = &sm.sc[j % 3][0][0];
+    float br[NTL];
+    DecayIn din[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+        const int I = a_tile_i(PART, n), R = a_tile_r(PART, n), r = 16 * R + l16;
+        br[n] = s[SC_BETA * FC + r];
+        if (GATED) din[n] = decay_load(s, R, I, r, 16 * I + 4 * q16);
+    }
     bf16x8 kf[4][4];
     load_rows(sm.K[j & 1], l16, q16, kf);
-    f32x4 G[2][4];
+    sched_fence();  // all fragments in one round trip (the compiler would stage them)
+    f32x4 G[NTL];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int I = 0; I < 4; ++I) G[u][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NTL; ++n) G[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int R = u == 0 ? R0 : R1;
+        for (int n = 0; n < NTL; ++n)
+            G[n] = mma16(kf[a_tile_i(PART, n)][ks], kf[a_tile_r(PART, n)][ks], G[n]);
 #pragma unroll
-            for (int I = 0; I <= R; ++I) G[u][I] = mma16(kf[I][ks], kf[R][ks], G[u][I]);
-        }
-    const float* s = &sm.sc[j % 3][0][0];
+    for (int n = 0; n < NTL; ++n) {
+        const int I = a_tile_i(PART, n), R = a_tile_r(PART, n);
+        const int r = 16 * R + l16, i0 = 16 * I + 4 * q16;
+        f32x4 d = {1.f, 1.f, 1.f, 1.f};
+        if (GATED) d = decay_eval(din[n], I == R);
+        f32x4 av;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int R = u == 0 ? R0 : R1;
-        const int r = 16 * R + l16;
-        const float br = s[SC_BETA * FC + r];
+        for (int e = 0; e < 4; ++e) av[e] = br[n] * d[e] * G[n][e];
+        if (PART == 1) {
+            st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
+        } else {
+            // entries on or above the diagonal go to the spare slot 120 of the block
 #pragma unroll
-        for (int I = 0; I <= R; ++I) {
-            const int i0 = 16 * I + 4 * q16;
-            f32x4 d = {1.f, 1.f, 1.f, 1.f};
-            if (GATED) decay4(s, R, I, r, i0, d);
-            f32x4 av;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) av[e] = br * d[e] * G[u][I][e];
-            if (I < R) {
-                st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * q16 + e < l16) sm.Ad[R][l16 * (l16 - 1) / 2 + 4 * q16 + e] = av[e];
+            for (int e = 0; e < 4; ++e) {
+                const int m = 4 * q16 + e;
+                sm.Ad[R][m < l16 ? l16 * (l16 - 1) / 2 + m : 120] = av[e];
             }
         }
     }
 }
 
-// P of chunk j, the tiles of one half (row blocks as for A), from the query fragments the
-// output wave already holds for Q M.  P's blocks above the diagonal that the output waves
-// read are zero, written once before the first chunk.
+// Diagonal block q16 of A (packed, as part 0 of make_a wrote it) into registers, by the
+// wave that wrote it: the UT inverse of the next half starts without an LDS round trip.
+__device__ __forceinline__ void load_ad(const FusedSmem& sm, int q16, f32x4 (&ap)[30]) {
+    wave_lds_order();
+#pragma unroll
+    for (int g = 0; g < 30; ++g) ap[g] = *reinterpret_cast<const f32x4*>(&sm.Ad[q16][4 * g]);
+}
+
+// P of chunk j for the query rows of one output wave's two row blocks R (half 0: 0 and 3,
+// half 1: 1 and 2, five tiles each), from the query fragments qf[u] of row block R_u that
+// the wave holds.  The tiles come out as P^T (rows i = key token, columns r = query token):
+// pt[u][s] is P^T for keys 32 s .. 32 s + 31 and the queries of R_u as a B operand
+// (k = key token), the form the output product O^T = Delta^T P^T takes.  P never goes
+// through LDS.
+constexpr int p_block(int half, int u) { return half == 0 ? (u == 0 ? 0 : 3) : (u == 0 ? 1 : 2); }
+
 template <bool GATED, int HALF>
-__device__ __forceinline__ void make_p(FusedSmem& sm, int j, const bf16x8 (&qf)[4][4], int l16, int q16) {
-    constexpr int R0 = HALF == 0 ? 0 : 1, R1 = HALF == 0 ? 3 : 2;
+__device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 (&qf)[2][4], int l16, int q16,
+                                       bf16x8 (&pt)[2][2]) {
+    const float* s = &sm.sc[j % 3][0][0];
+    DecayIn din[2][4];
+    if (GATED) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int R = p_block(HALF, u), r = 16 * R + l16;
+#pragma unroll
+            for (int I = 0; I <= R; ++I) din[u][I] = decay_load(s, R, I, r, 16 * I + 4 * q16);
+        }
+    }
     bf16x8 kf[4][4];
     load_rows(sm.K[j & 1], l16, q16, kf);
     f32x4 G[2][4];
@@ -310,25 +351,26 @@ __device__ __forceinline__ void make_p(FusedSmem& sm, int j, const bf16x8 (&qf)[
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int R = u == 0 ? R0 : R1;
+            const int R = p_block(HALF, u);
 #pragma unroll
-            for (int I = 0; I <= R; ++I) G[u][I] = mma16(kf[I][ks], qf[R][ks], G[u][I]);
+            for (int I = 0; I <= R; ++I) G[u][I] = mma16(kf[I][ks], qf[u][ks], G[u][I]);
         }
-    const float* s = &sm.sc[j % 3][0][0];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int R = u == 0 ? R0 : R1;
+        const int R = p_block(HALF, u);
         const int r = 16 * R + l16;
 #pragma unroll
         for (int I = 0; I <= R; ++I) {
+            // tile (I, R): lane holds P[r][i] for i = 16 I + 4 q16 + e; zero above the diagonal
             const int i0 = 16 * I + 4 * q16;
             f32x4 d = {1.f, 1.f, 1.f, 1.f};
-            if (GATED) decay4(s, R, I, r, i0, d);
-            f32x4 pv;
+            if (GATED) d = decay_eval(din[u][I], I == R);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = (I < R || i0 + e <= r) ? d[e] * G[u][I][e] : 0.f;
-            st4(&sm.P[j & 1][r][i0], pv[0], pv[1], pv[2], pv[3]);
+            for (int e = 0; e < 4; ++e) G[u][I][e] = (I < R || i0 + e <= r) ? d[e] * G[u][I][e] : 0.f;
         }
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+            if (2 * sb <= R) pt[u][sb] = acc_to_b(G[u][2 * sb], G[u][2 * sb + 1]);  // tiles past R are zero
     }
 }
 
@@ -338,16 +380,12 @@ __device__ __forceinline__ void make_p(FusedSmem& sm, int j, const bf16x8 (&qf)[
 // the outer one as a B operand in registers.  The rest of T is never formed: the chain
 // waves finish Delta by block substitution over the two 32-token halves.  The zero blocks
 // of Tt are written once, before the first chunk.
-__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16) {
+__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f32x4 (&ap)[30]) {
     {
         // lane = 16 * block + column c: solve (I + A_bb) x = e_c in the column order: once
-        // x[m] is final, subtract its share from every later row.  The block's strictly
-        // lower entries (120, packed) are read into registers first.
+        // x[m] is final, subtract its share from every later row.  ap holds the block's
+        // strictly lower entries (120, packed).
         const int b = q16, c = l16;
-        const float* Ab_ = &sm.Ad[b][0];
-        f32x4 ap[30];
-#pragma unroll
-        for (int g = 0; g < 30; ++g) ap[g] = *reinterpret_cast<const f32x4*>(Ab_ + 4 * g);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
@@ -554,49 +592,76 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         }
     } else if (wave == 3 || wave == 7) {
         // ----------------------------------------------------------- output waves
-        const int cw = wave == 3 ? 0 : 1, jc = CW * cw;
-        f32x4 Y[4];          // Y = Q M: token 16 t + 4 q16 + e, column jc + l16
-        bf16x8 qf[4][4];     // query fragments of the current chunk (for Y here, P in .2)
+        // Output wave ow owns the query rows of row blocks R_0, R_1 (ow 0: blocks 0 and 3,
+        // ow 1: blocks 1 and 2) for all 32 columns, and computes in the transposed form,
+        // O^T = exp(gamma) Y^T + Delta^T P^T with Y^T = M^T Q^T: the chain's bf16 state and
+        // Delta fragments serve unchanged as the A operands M^T and Delta^T, the query rows as
+        // B operands, and P^T stays in registers from make_p.
+        const int ow = wave == 3 ? 0 : 1;
+        f32x4 yt[2][2];      // Y^T tile (u, c): columns 16 c + 4 q16 + e, query 16 R_u + l16
+        bf16x8 pt[2][2];     // P^T of the chunk as B operands (make_p)
+        bf16x8 qf[2][4];     // query rows of R_u: qf[u][ks] = keys 32 ks + 8 q16 ..
         __syncthreads();
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            if (j >= 1 && j <= nc) {
+            const bool o_live = j >= 1 && j <= nc, y_live = j < nc;
+            if (o_live) {
                 // O of chunk j - 1 = scale (exp(gamma) Y + P Delta), P lower triangular
                 const int jp = j - 1;
                 const float* s = &sm.sc[jp % 3][0][0];
+                bf16x8 dq[2][2];   // Delta^T: column tile c, key tokens 32 s ..
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb) dq[c][sb] = sm.dd[c][sb][lane];
+                float egr[2] = {1.f, 1.f};
                 if (GATED) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) Y[t] *= *reinterpret_cast<const f32x4*>(&s[SC_EG * FC + 16 * t + 4 * q16]);
+                    for (int u = 0; u < 2; ++u) egr[u] = s[SC_EG * FC + 16 * (ow == 0 ? 3 * u : 1 + u) + l16];
                 }
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const bf16x8 d = sm.dd[cw][u][lane];
+                    const int R = ow == 0 ? 3 * u : 1 + u;
 #pragma unroll
-                    for (int t = 2 * u; t < 4; ++t) Y[t] = mma16(ld8(&sm.P[jp & 1][16 * t + l16][32 * u + 8 * q16]), d, Y[t]);
+                    for (int c = 0; c < 2; ++c) {
+                        f32x4 o = yt[u][c] * egr[u];
+#pragma unroll
+                        for (int sb = 0; sb < 2; ++sb)
+                            if (2 * sb <= R) o = mma16(dq[c][sb], pt[u][sb], o);
+                        st4(&sm.O[16 * R + l16][16 * c + 4 * q16], a.scale * o[0], a.scale * o[1], a.scale * o[2],
+                            a.scale * o[3]);
+                    }
+                }
+            }
+            if (y_live) {
+                // Y^T = M^T Q^T with the chain's bf16 state at the start of chunk j (written at
+                // the end of the previous phase)
+                bf16x8 m4[2][4];
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) m4[c][ks] = sm.mb[j & 1][c][ks][lane];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int R = ow == 0 ? 3 * u : 1 + u;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) qf[u][ks] = ld8(&sm.Q[j & 1][16 * R + l16][32 * ks + 8 * q16]);
                 }
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    st4(&sm.OT[jc + l16][16 * t + 4 * q16], a.scale * Y[t][0], a.scale * Y[t][1], a.scale * Y[t][2],
-                        a.scale * Y[t][3]);
-            }
-            if (j < nc) {
-                // Y = Q M with the chain's bf16 state at the start of chunk j (written at the
-                // end of the previous phase)
-                bf16x8 m4[4];
-                load_rows(sm.Q[j & 1], l16, q16, qf);
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) m4[ks] = sm.mb[j & 1][cw][ks][lane];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) Y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int c = 0; c < 2; ++c) yt[u][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) Y[t] = mma16(qf[t][ks], m4[ks], Y[t]);
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) yt[u][c] = mma16(m4[c][ks], qf[u][ks], yt[u][c]);
             }
             __syncthreads();
-            if (j < nc) {  // half of P of chunk j from the same query fragments
-                if (cw == 0) make_p<GATED, 0>(sm, j, qf, l16, q16);
-                else make_p<GATED, 1>(sm, j, qf, l16, q16);
+            if (y_live) {  // P of chunk j for the same query rows
+                if (ow == 0) make_p<GATED, 0>(sm, j, qf, l16, q16, pt);
+                else make_p<GATED, 1>(sm, j, qf, l16, q16, pt);
             }
             __syncthreads();
         }
@@ -609,21 +674,25 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         fetch(st, 0, f0);
         fetch(st, 1, f1);
         // phase -1: chunk 0
-        put_kq(sm, 0, lt, f0);
+        put_k(sm, 0, lt, f0);
         __syncthreads();
+        put_q(sm, 0, lt, f0);
         put_v(sm, lt, f0);
         fetch(st, 2, f0);
         __syncthreads();
-        // phase j: chunk j + 1 (in f[(j + 1) & 1]); then refill that set with chunk j + 3
+        // phase j: chunk j + 1 (in f[(j + 1) & 1]): K and the scalars in the first half, Q
+        // and V in the second; then refill that set with chunk j + 3
         for (int j = 0; j < nph; j += 2) {
-            put_kq(sm, j + 1, lt, f1);
+            put_k(sm, j + 1, lt, f1);
             __syncthreads();
+            put_q(sm, j + 1, lt, f1);
             put_v(sm, lt, f1);
             fetch(st, j + 3, f1);
             store_o(sm, st, j - 1, lt);   // written by the output waves in this phase's first half
             __syncthreads();
-            put_kq(sm, j + 2, lt, f0);
+            put_k(sm, j + 2, lt, f0);
             __syncthreads();
+            put_q(sm, j + 2, lt, f0);
             put_v(sm, lt, f0);
             fetch(st, j + 4, f0);
             store_o(sm, st, j, lt);
@@ -631,30 +700,25 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         }
     } else if (wave == 6) {
         // ------------------------------------------ wave 6: T of j, half of A of j + 1
-        // zero blocks, written once: Tt below its block diagonal, P above its diagonal in
-        // the tiles the output waves read (rows 0-15 x keys 16-31, rows 32-47 x keys 48-63)
+        // zero blocks of Tt below its block diagonal, written once
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int v = lane + 64 * p, r = v >> 3, cg = v & 7;
             if (cg * 8 + 8 <= (r >> 4) * 16) *reinterpret_cast<bf16x8*>(&sm.Tt[r][cg * 8]) = zero8();
         }
-#pragma unroll
-        for (int bf = 0; bf < 2; ++bf)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int v = lane + 64 * p, r = v >> 2, half = (v >> 1) & 1, cg = v & 1;
-                const int row = r < 16 ? r : r + 16;      // rows 0-15 and 32-47
-                const int col = (row < 16 ? 16 : 48) + 8 * cg;
-                if (half == 0) *reinterpret_cast<bf16x8*>(&sm.P[bf][row][col]) = zero8();
-            }
-        // phase -1, second half: half of A of chunk 0
+        // phase -1, second half: A's diagonal tiles of chunk 0
+        f32x4 ap[30];
         __syncthreads();
         make_a<GATED, 0>(sm, 0, l16, q16);
+        load_ad(sm, q16, ap);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            if (j < nc) make_t(sm, l16, q16);
+            if (j < nc) make_t(sm, l16, q16, ap);
             __syncthreads();
-            if (j + 1 < nc) make_a<GATED, 0>(sm, j + 1, l16, q16);
+            if (j + 1 < nc) {
+                make_a<GATED, 0>(sm, j + 1, l16, q16);
+                load_ad(sm, q16, ap);
+            }
             __syncthreads();
         }
     } else {
