@@ -146,16 +146,18 @@ __device__ __forceinline__ uint4 u4(u32x4 x) { return make_uint4(x[0], x[1], x[2
 
 __device__ __forceinline__ void fetch(const Streams& st, int j, LoadSet& f) {
     // the chunk offset goes into the per-lane offset, which the range check covers
+    // issued in the order of use (loads complete in order): the scalars and K, which the
+    // first half takes, before Q and V
     const uint32_t ckq = (uint32_t)j * st.kq_chunk, cv = (uint32_t)j * st.v_chunk, cs = (uint32_t)j * st.s_chunk;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        f.k[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.k, st.off_kq[p] + ckq, 0, 0));
-        f.q[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.q, st.off_kq[p] + ckq, 0, 0));
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) f.v[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.v, st.off_v[p] + cv, 0, 0));
     f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.beta, st.off_s + cs, 0, 0));
     f.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.g, st.off_s + cs, 0, 0));
+#pragma unroll
+    for (int p = 0; p < 8; ++p) f.k[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.k, st.off_kq[p] + ckq, 0, 0));
+    sched_fence();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) f.q[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.q, st.off_kq[p] + ckq, 0, 0));
+#pragma unroll
+    for (int p = 0; p < 2; ++p) f.v[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.v, st.off_v[p] + cv, 0, 0));
 }
 
 // DPP move of a float with bound_ctrl (lanes without a source read 0)
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     seq_range(a.cu, w.n, a.T, w.bos, w.eos);
     w.nchunks = (int)((w.eos - w.bos + FC - 1) / FC);
     const int nc = w.nchunks;
-    const int nph = (nc + 2) & ~1;   // phases 0 .. nph - 1 (>= nc + 1, even)
+    const int nph = nc + 1;   // phases 0 .. nc (the last one writes O of the last chunk)
 
     // Every wave runs phases j = -1 .. nph - 1, two barriers each.
     if (wave < NCW) {
@@ -690,6 +692,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             fetch(st, j + 3, f1);
             store_o(sm, st, j - 1, lt);   // written by the output waves in this phase's first half
             __syncthreads();
+            if (j + 1 >= nph) break;
             put_k(sm, j + 2, lt, f0);
             __syncthreads();
             put_q(sm, j + 2, lt, f0);
