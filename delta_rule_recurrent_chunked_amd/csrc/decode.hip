@@ -12,10 +12,12 @@
 // The state is read once and written once: this kernel is bound by HBM bandwidth.
 //
 // Work decomposition: one workgroup per (n, h, slice of CW value columns; CW = Dv).  A
-// thread owns a float4 of columns in RPT rows, so a wave reads whole CW*4-byte row
-// segments and every state byte moves through one 128-bit load and one 128-bit store,
-// both nontemporal (the state streams through once).  Column sums over the key dim
-// reduce across lanes (xor shuffles), then across the waves of the workgroup through LDS.
+// thread owns a float4 of columns in RPT consecutive rows, so a wave reads whole
+// CW*4-byte row segments and every state byte moves through one 128-bit load and one
+// 128-bit store, both nontemporal (the state streams through once); the thread's RPT
+// elements of k and q arrive in 16-byte loads.  Everything a workgroup reads is requested
+// before its first wait.  Column sums over the key dim reduce across lanes (xor shuffles),
+// then across the waves of the workgroup through LDS.
 #include "internal.h"
 
 namespace dn {
@@ -31,10 +33,31 @@ struct DecodeShape {
     static_assert(CW % 4 == 0 && TPR <= 64 && NT % 64 == 0 && DK % RPP == 0, "decode tiling");
 };
 
-template <typename T, int DK, int DV, int CW>
+// N consecutive elements of k or q as floats, from a 16-byte-aligned address
+template <typename T, int N>
+__device__ __forceinline__ void ld_vec(const T* p, float (&out)[N]) {
+    constexpr int PER = 16 / (int)sizeof(T);
+    static_assert(N % PER == 0, "ld_vec: whole 16-byte pieces");
+#pragma unroll
+    for (int i = 0; i < N / PER; ++i) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p + i * PER);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(T) == 2) {   // bf16 pair: low half first
+                out[i * PER + 2 * j] = __uint_as_float(w[j] << 16);
+                out[i * PER + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            } else {
+                out[i * PER + j] = __uint_as_float(w[j]);
+            }
+        }
+    }
+}
+
+template <typename T, int DK, int DV, int CW, bool VEC>
 __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(DecodeArgs a) {
     using S = DecodeShape<DK, CW>;
-    constexpr int TPR = S::TPR, RPP = S::RPP, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
+    constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
     __shared__ float red[NW][2 * CW + 1];
     __shared__ float dsh[CW];
 
@@ -54,16 +77,24 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     // the state streams through once: nontemporal loads and stores keep it from
     // displacing q, k, v in the caches
     typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const int row0 = rg * RPT;                // this thread's rows: row0 .. row0 + RPT - 1
     f32x4v m[RPT];
 #pragma unroll
     for (int p = 0; p < RPT; ++p)
-        m[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(Mp + (long)(p * RPP + rg) * DV));
+        m[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(Mp + (long)(row0 + p) * DV));
     float kr[RPT], qr[RPT];
+    if constexpr (VEC) {
+        ld_vec(kp + row0, kr);
+        ld_vec(qp + row0, qr);
+    } else {
 #pragma unroll
-    for (int p = 0; p < RPT; ++p) {
-        kr[p] = ld_f32(kp, p * RPP + rg);
-        qr[p] = ld_f32(qp, p * RPP + rg);
+        for (int p = 0; p < RPT; ++p) {
+            kr[p] = ld_f32(kp, row0 + p);
+            qr[p] = ld_f32(qp, row0 + p);
+        }
     }
+    const long vo = (long)nh * DV + slice * CW + (tid < CW ? tid : 0);
+    const float vval = ld_f32(static_cast<const T*>(a.v), vo);
     const float alpha = a.g ? expf(a.g[nh]) : 1.0f;
     const float beta = a.beta[nh];
 
@@ -105,8 +136,7 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
             rq += red[w][CW + tid];
             kqs += red[w][2 * CW];
         }
-        const long vo = (long)nh * DV + slice * CW + tid;
-        const float d = beta * (ld_f32(static_cast<const T*>(a.v), vo) - alpha * rk);
+        const float d = beta * (vval - alpha * rk);
         dsh[tid] = d;
         st_out(static_cast<T*>(a.o), vo, a.scale * (alpha * rq + kqs * d));
     }
@@ -119,7 +149,7 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
         r[1] = alpha * m[p][1] + kr[p] * d1;
         r[2] = alpha * m[p][2] + kr[p] * d2;
         r[3] = alpha * m[p][3] + kr[p] * d3;
-        __builtin_nontemporal_store(r, reinterpret_cast<f32x4v*>(Mp + (long)(p * RPP + rg) * DV));
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4v*>(Mp + (long)(row0 + p) * DV));
     }
 }
 
@@ -129,7 +159,14 @@ hipError_t launch_dims(const DecodeArgs& a, hipStream_t s) {
     using S = DecodeShape<DK, CW>;
     const long blocks = (long)a.N * a.Hv * (DV / CW);
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW>), dim3((unsigned)blocks), dim3(S::NT), 0, s, a);
+    // 16-byte loads of k and q when a thread's rows fill whole pieces and the rows of every
+    // (sequence, head) start 16-byte aligned
+    constexpr bool kVecShape = (S::RPT * sizeof(T)) % 16 == 0 && (DK * sizeof(T)) % 16 == 0;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k)) & 15) == 0;
+    if (kVecShape && aligned)
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape>), dim3((unsigned)blocks), dim3(S::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false>), dim3((unsigned)blocks), dim3(S::NT), 0, s, a);
     return hipGetLastError();
 }
 
