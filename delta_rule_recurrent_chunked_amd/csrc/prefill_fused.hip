@@ -60,6 +60,10 @@ constexpr int KPITCH = FD + 16;
 constexpr int CPITCH = FC + 16;
 constexpr int VPITCH = DVS + 16;
 constexpr int OPITCH = DVS + 8;
+// A's diagonal blocks, 120 packed fp16 entries each (+ a spare slot), 68 dwords apart: the
+// four blocks' broadcast reads fall on distinct banks.
+constexpr int ADPITCH = 136;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int NT = 512;            // threads (8 waves)
 constexpr int NLD = 128;           // loader threads (waves 4, 5)
 
@@ -75,9 +79,8 @@ struct alignas(16) FusedSmem {
     __bf16 V[FC][VPITCH];          // value slice of the next chunk the chain reads
     __bf16 Tt[FC][CPITCH];         // T^T of the chunk being processed
     __bf16 Ab[FC][CPITCH];         // A in bf16 (blocks below the 16x16 block diagonal)
-    float Ad[4][132];              // A's diagonal 16x16 blocks, fp32, strictly lower part
-                                   //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m;
-                                   //   block pitch 132: the four blocks' reads on distinct banks
+    _Float16 Ad[4][ADPITCH];       // A's diagonal 16x16 blocks, fp16, strictly lower part
+                                   //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m
     bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
     __bf16 O[FC][OPITCH];          // O of the previous chunk, token-major (the output waves write
@@ -307,7 +310,7 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = 4 * q16 + e;
-                sm.Ad[R][m < l16 ? l16 * (l16 - 1) / 2 + m : 120] = av[e];
+                sm.Ad[R][m < l16 ? l16 * (l16 - 1) / 2 + m : 120] = (_Float16)av[e];
             }
         }
     }
@@ -315,10 +318,10 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
 
 // Diagonal block q16 of A (packed, as part 0 of make_a wrote it) into registers, by the
 // wave that wrote it: the UT inverse of the next half starts without an LDS round trip.
-__device__ __forceinline__ void load_ad(const FusedSmem& sm, int q16, f32x4 (&ap)[30]) {
+__device__ __forceinline__ void load_ad(const FusedSmem& sm, int q16, f16x8 (&ap)[15]) {
     wave_lds_order();
 #pragma unroll
-    for (int g = 0; g < 30; ++g) ap[g] = *reinterpret_cast<const f32x4*>(&sm.Ad[q16][4 * g]);
+    for (int g = 0; g < 15; ++g) ap[g] = *reinterpret_cast<const f16x8*>(&sm.Ad[q16][8 * g]);
 }
 
 // P of chunk j for the query rows of one output wave's two row blocks R (half 0: 0 and 3,
@@ -377,16 +380,18 @@ __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 
 }
 
 // Wave 6, first half: the two 32x32 diagonal blocks of T = (I + A)^{-1} into Tt (T^T).
-// The four 16x16 diagonal blocks by fp32 forward substitution, then the blocks below them
+// The four 16x16 diagonal blocks by forward substitution in fp32 arithmetic (from A's
+// entries stored in fp16), then the blocks below them
 // by one level of 2x2 block inversion, T21 = -T22 (A21 T11), the inner product handed to
 // the outer one as a B operand in registers.  The rest of T is never formed: the chain
 // waves finish Delta by block substitution over the two 32-token halves.  The zero blocks
 // of Tt are written once, before the first chunk.
-__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f32x4 (&ap)[30]) {
+__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f16x8 (&ap)[15]) {
     {
         // lane = 16 * block + column c: solve (I + A_bb) x = e_c in the column order: once
         // x[m] is final, subtract its share from every later row.  ap holds the block's
-        // strictly lower entries (120, packed).
+        // strictly lower entries (120, packed, fp16: mixed-precision FMAs take them as they
+        // are, and the arithmetic stays fp32).
         const int b = q16, c = l16;
         float x[16];
 #pragma unroll
@@ -396,7 +401,7 @@ __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f3
 #pragma unroll
             for (int r = m + 1; r < 16; ++r) {
                 const int idx = r * (r - 1) / 2 + m;
-                x[r] -= ap[idx >> 2][idx & 3] * x[m];
+                x[r] = __builtin_fmaf(-(float)ap[idx >> 3][idx & 7], x[m], x[r]);
             }
         bf16x8 lo8, hi8;
 #pragma unroll
@@ -710,7 +715,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             if (cg * 8 + 8 <= (r >> 4) * 16) *reinterpret_cast<bf16x8*>(&sm.Tt[r][cg * 8]) = zero8();
         }
         // phase -1, second half: A's diagonal tiles of chunk 0
-        f32x4 ap[30];
+        f16x8 ap[15];
         __syncthreads();
         make_a<GATED, 0>(sm, 0, l16, q16);
         load_ad(sm, q16, ap);
