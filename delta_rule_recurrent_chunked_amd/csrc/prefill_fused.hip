@@ -486,6 +486,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     if (wave < NCW) {
         // ------------------------------------------------------------ chain waves
         const int jc = CW * wave;
+        __builtin_amdgcn_s_setprio(2);  // the sequential chain goes first on its SIMD
         f32x4 M[8];  // tile mt: keys 16 mt + 4 q16 + e, column jc + l16 of the slice
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -716,6 +717,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         }
         // phase -1, second half: A's diagonal tiles of chunk 0
         f16x8 ap[15];
+        // first on SIMD 2: the UT inverse and A's diagonal tiles (with their readback) are
+        // the longer steps of both halves; the other A wave has slack
+        __builtin_amdgcn_s_setprio(2);
         __syncthreads();
         make_a<GATED, 0>(sm, 0, l16, q16);
         load_ad(sm, q16, ap);
