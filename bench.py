@@ -7,10 +7,10 @@ One step is one prefill call (dn_chunk_fwd) over the DeltaNet layer-prefill work
 final state returned): 8192 tokens.  K steps run back to back between two device
 synchronisations, cycling through several copies of the inputs so the working set
 (> 256 MB) does not stay in the Infinity Cache between steps.  The K steps are captured
-once in a HIP graph and the replay is timed (--eager times the Python launch loop); each
-call's kernel time is also taken with HIP events on the launching stream.  The decode step
-(256 sequences x 32 heads, state updated in place) is timed the same way and reported
-in the same line.  The fp64 oracle is timed on the host cores on a bounded sample of
+once in a HIP graph and the replay is timed (--eager times the Python launch loop); the
+average kernel time per call is also taken with HIP events on the launching stream around
+the eager loop.  The decode step (256 sequences x 32 heads, state updated in place) is
+timed with events around a loop of back-to-back steps and reported in the same line.  The fp64 oracle is timed on the host cores on a bounded sample of
 the prefill workload.
 
 Prints ONE JSON line.
@@ -163,18 +163,18 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    # per-call kernel time: HIP events around each eager call on the launching stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # average kernel time per call: HIP events on the launching stream around the eager
+    # loop (the launches queue back to back), divided by the call count
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
         step(i)
-        evs[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
-    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    call_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
     if args.eager:
         wall = wall_eager
     else:
@@ -198,7 +198,6 @@ def main():
         wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     tokens = B * T
-    call_us = float(np.mean(ev_ms)) * 1e3
     alg_b = prefill_bytes(B, T, Hqk, Hv, D, gated=False, N=B, init=False)
     alg_f = prefill_flops(B, T, Hqk, Hv, D, PREFILL["C"])
     traffic_p, traffic_d = load_traffic()
@@ -214,14 +213,12 @@ def main():
     for i in range(3):
         dn.decode_step(dq, dk, dv, db, dg, dstate[i % 2], out=dout)
     torch.cuda.synchronize()
-    devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.decode_reps)]
+    ev0.record(stream)
     for i in range(args.decode_reps):
-        devs[i][0].record(stream)
         dn.decode_step(dq, dk, dv, db, dg, dstate[i % 2], out=dout)
-        devs[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    dec_us = float(np.mean([a.elapsed_time(b) for a, b in devs])) * 1e3
+    dec_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
     state_b = y.B * y.Hv * y.Dk * y.Dv * 4 * 2
     dec_b = decode_bytes(y.B, y.Hqk, y.Hv, y.Dk)
     dec_gbs = state_b / (dec_us * 1e-6) / 1e9
