@@ -76,6 +76,13 @@ EDGE = {
     "d128_bf16_ragged_gqa": dict(B=2, T=333, Hqk=2, Hv=4, Dk=128, dtype="bf16", g_scale=0.1,
                                  init_std=0.02),
     "d128_fp32": dict(B=1, T=130, Hqk=2, Dk=128, dtype="f32", g_scale=0.1, init_std=0.02),
+    # more than 64 packed sequences (no longest-first ordering), lengths 0..191
+    "many_packed_seqs": dict(B=1, Hqk=2, Hv=2, Dk=128, dtype="bf16",
+                             seqlens=[(37 * i) % 192 for i in range(70)], g_scale=0.1,
+                             init_std=0.02, beta_scale=2.0),
+    # one long gated sequence: 16 chunks and a 40-token tail, from an initial state
+    "d128_bf16_long": dict(B=1, T=1000, Hqk=1, Hv=2, Dk=128, dtype="bf16", g_scale=0.05,
+                           init_std=0.02, beta_scale=2.0),
 }
 
 
