@@ -29,7 +29,8 @@
 //   2         2     -                                  A of chunk j + 1, tiles below them
 //
 // The UT inverse, the longest serial step, has SIMD 2 to itself in the first half; the
-// wave that runs it builds A's diagonal tiles itself and keeps them in registers.
+// wave that runs it builds A's diagonal tiles itself and keeps them in registers.  The
+// chain waves and that wave raise their wave priority: their instructions issue first.
 //
 // Chain wave w owns state columns 16w .. 16w+15 of the slice as eight 16x16 fp32
 // accumulator tiles; products that consume its results take them as B operands through
@@ -54,8 +55,9 @@ constexpr int NCW = DVS / CW;      // chain waves
 // across 128 four-byte banks (measured: this model predicts which pitches run
 // conflict-free).  An operand read takes 16 rows x 2 chunks per 32 lanes, so the 16 row
 // offsets (pitch in dwords x row, mod 128) must be distinct multiples of 8: 72 dwords for
-// the 128-wide K and Q rows, 40 for the 64-wide T, P and A rows.  V (read only transposed,
-// 16 rows x 8 dwords) takes 24.
+// the 128-wide K and Q rows, 40 for the 64-wide T and A rows.  V (read only transposed,
+// 16 rows x 8 dwords) takes 24; the O tile 20 (its 8-byte stores from 16 rows fall on
+// distinct bank pairs).
 constexpr int KPITCH = FD + 16;
 constexpr int CPITCH = FC + 16;
 constexpr int VPITCH = DVS + 16;
