@@ -223,6 +223,40 @@ def main():
     dec_b = decode_bytes(y.B, y.Hqk, y.Hv, y.Dk)
     dec_gbs = state_b / (dec_us * 1e-6) / 1e9
 
+    # ------------------------------------ the other two full-size prefill workloads
+    # (context beside the headline: each timed the same way, with HIP events around a loop
+    # of back-to-back calls on the launching stream)
+    other = {}
+    for cfg, what in ((3, "gated prefill, GQA 16 q/k heads -> 32 v heads, B2 T8192 d128 bf16, "
+                          "final state returned"),
+                      (5, "varlen gated prefill, 8 packed sequences, 32768 tokens, H32 d128 bf16, "
+                          "beta in (0,2), initial state per sequence")):
+        z = make_config(cfg)
+        zq, zk, zv, zb, zg, zi = (to_dev(a) for a in (z.q, z.k, z.v, z.beta, z.g, z.init))
+        zcu = None if z.cu_seqlens is None else to_dev(z.cu_seqlens.astype(np.int32))
+        zo = torch.empty((z.B, z.T, z.Hv, z.Dv), dtype=torch.bfloat16, device=dev)
+        zs = torch.empty((z.num_seqs, z.Hv, z.Dk, z.Dv), dtype=torch.float32, device=dev)
+        zw = torch.empty(max(1, dn.workspace_bytes(z.B, z.T, z.Hqk, z.Hv, z.Dk, z.Dv, torch.bfloat16)),
+                         dtype=torch.uint8, device=dev)
+
+        def zstep():
+            dn.chunk_fwd(zq, zk, zv, zb, zg, zi, cu_seqlens=zcu, out=zo, final_state=zs,
+                         workspace=zw, check_cu_seqlens=False)
+
+        for _ in range(2):
+            zstep()
+        reps = 10
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            zstep()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        z_us = ev0.elapsed_time(ev1) * 1e3 / reps
+        other[f"config{cfg}"] = {"workload": what, "us_per_call": z_us,
+                                 "tokens_per_s": z.B * z.T / (z_us * 1e-6)}
+        del zq, zk, zv, zb, zg, zi, zcu, zo, zs, zw
+
     line = {
         "metric": "prefill tokens/sec + MFMA util; decode-step state GB/s vs HBM peak",
         "value": tokens / (ms_step * 1e-3),
@@ -254,6 +288,7 @@ def main():
                                 "frac": dec_b / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                 "traffic": traffic_d, "kernel": "decode_kernel",
                                 "algorithmic_bytes": dec_b}},
+        "prefill_other_workloads": other,
         "cpu_baseline": None,
     }
     if not args.no_cpu:
