@@ -21,14 +21,16 @@
 // Each chunk takes one "phase" of two halves separated by workgroup barriers.  In phase j:
 //
 //   wave      SIMD  first half (.1)                    second half (.2)
-//   0, 1      0, 1  chain, chunk j: X = K M, R         Delta, state update
+//   0, 1      0, 2  chain, chunk j: X = K M, R         Delta, state update
 //   3, 7      3     output: O of chunk j - 1, Y = Q M  P of chunk j
 //                   (each wave: two 16-token row blocks, all 32 columns)
-//   4, 5      0, 1  loaders: K, scalars of j + 1       Q, V of j + 1; fetch j + 3; store O of j - 1
-//   6         2     T of chunk j (UT inverse of A)     A of chunk j + 1, diagonal tiles
-//   2         2     -                                  A of chunk j + 1, tiles below them
+//   4, 5      0, 2  loaders: K, scalars of j + 1       Q, V of j + 1; fetch j + 3; store O of j - 1
+//   6         1     T of chunk j (UT inverse of A)     A of chunk j + 1, diagonal tiles
+//   2         1     -                                  A of chunk j + 1, tiles below them
 //
-// The UT inverse, the longest serial step, has SIMD 2 to itself in the first half; the
+// Waves w and w + 4 share a SIMD (the hardware deals waves 0-3 to SIMDs 0, 2, 1, 3; read
+// from the HW_ID register).  The UT inverse, the longest serial step, has its SIMD to
+// itself in the first half; the
 // wave that runs it builds A's diagonal tiles itself and keeps them in registers.  The
 // chain waves and that wave raise their wave priority: their instructions issue first.
 //
@@ -719,7 +721,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         }
         // phase -1, second half: A's diagonal tiles of chunk 0
         f16x8 ap[15];
-        // first on SIMD 2: the UT inverse and A's diagonal tiles (with their readback) are
+        // first on its SIMD: the UT inverse and A's diagonal tiles (with their readback) are
         // the longer steps of both halves; the other A wave has slack
         __builtin_amdgcn_s_setprio(2);
         __syncthreads();
