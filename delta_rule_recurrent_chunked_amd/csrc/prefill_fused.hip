@@ -544,7 +544,16 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             if (live) {
                 // Delta = T R by block substitution over the two 32-token halves:
                 //   Delta_top = T_TL R_top;  Delta_bot = T_BR (R_bot - A_BL Delta_top).
-                // T operands T[16 t + m][k] = Tt[k][16 t + m] by transposed reads.
+                // T operands T[16 t + m][k] = Tt[k][16 t + m] by transposed reads.  With decay,
+                // the tail factors are read here, ahead of the Delta store (a read behind a
+                // store waits a round trip of its own).
+                f32x4 tl[4];
+                float Gl = 1.f;
+                if (GATED) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) tl[t] = *reinterpret_cast<const f32x4*>(&s[SC_TAIL * FC + 16 * t + 4 * q16]);
+                    Gl = s[SC_EG * FC + FC - 1];
+                }
                 f32x4 D[4];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -568,13 +577,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 }
                 if (GATED) {  // Delta~ = diag(exp(gamma_last - gamma)) Delta for the state update
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const f32x4 tl = *reinterpret_cast<const f32x4*>(&s[SC_TAIL * FC + 16 * t + 4 * q16]);
-                        D[t] *= tl;
-                    }
+                    for (int t = 0; t < 4; ++t) D[t] *= tl[t];
                     db[0] = acc_to_b(D[0], D[1]);
                     db[1] = acc_to_b(D[2], D[3]);
-                    const float Gl = s[SC_EG * FC + FC - 1];
 #pragma unroll
                     for (int mt = 0; mt < 8; ++mt) M[mt] *= Gl;
                 }
