@@ -90,6 +90,8 @@ struct alignas(16) FusedSmem {
     __bf16 O[FC][OPITCH];          // O of the previous chunk, token-major (the output waves write
                                    //   it, the loader waves store it to HBM in the second half)
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
+    int seq_len[64];               // packed batches of up to 64 sequences: their lengths,
+    int rank_seq[64];              //   and the sequence of each length rank
 };
 
 struct LoadSet {
@@ -466,17 +468,21 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     w.n = chain / a.Hv;
     w.h = chain % a.Hv;
     if (a.cu && a.N <= 64) {
-        // longest sequences first: rank -> sequence (ties by index)
-        const int rank = w.n;
-        for (int m = 0; m < a.N; ++m) {
-            const int lm = a.cu[m + 1] - a.cu[m];
+        // longest sequences first: rank -> sequence (ties by index).  Thread m ranks sequence
+        // m against the lengths staged in LDS; the ranks are a permutation of 0 .. N - 1.
+        if (tid < a.N) sm.seq_len[tid] = a.cu[tid + 1] - a.cu[tid];
+        __syncthreads();
+        if (tid < a.N) {
+            const int lm = sm.seq_len[tid];
             int r = 0;
             for (int x = 0; x < a.N; ++x) {
-                const int lx = a.cu[x + 1] - a.cu[x];
-                r += (lx > lm) || (lx == lm && x < m);
+                const int lx = sm.seq_len[x];
+                r += (lx > lm) || (lx == lm && x < tid);
             }
-            if (r == rank) w.n = m;
+            sm.rank_seq[r] = tid;
         }
+        __syncthreads();
+        w.n = sm.rank_seq[w.n];
     }
     w.nh = w.n * a.Hv + w.h;
     w.hq = w.h / (a.Hv / a.Hqk);

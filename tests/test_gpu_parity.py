@@ -80,6 +80,10 @@ EDGE = {
     "many_packed_seqs": dict(B=1, Hqk=2, Hv=2, Dk=128, dtype="bf16",
                              seqlens=[(37 * i) % 192 for i in range(70)], g_scale=0.1,
                              init_std=0.02, beta_scale=2.0),
+    # 64 packed sequences (the most that are ordered longest first), lengths 0..127
+    "packed_64_seqs": dict(B=1, Hqk=1, Hv=2, Dk=128, dtype="bf16",
+                           seqlens=[(53 * i + 11) % 128 for i in range(64)], g_scale=0.1,
+                           init_std=0.02),
     # one long gated sequence: 16 chunks and a 40-token tail, from an initial state
     "d128_bf16_long": dict(B=1, T=1000, Hqk=1, Hv=2, Dk=128, dtype="bf16", g_scale=0.05,
                            init_std=0.02, beta_scale=2.0),
