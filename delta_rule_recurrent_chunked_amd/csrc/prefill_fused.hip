@@ -90,8 +90,8 @@ struct alignas(16) FusedSmem {
     __bf16 O[FC][OPITCH];          // O of the previous chunk, token-major (the output waves write
                                    //   it, the loader waves store it to HBM in the second half)
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
-    int seq_len[64];               // packed batches of up to 64 sequences: their lengths,
-    int rank_seq[64];              //   and the sequence of each length rank
+    int seq_len[NT];               // packed batches of up to 512 sequences: their lengths,
+    int rank_seq[NT];              //   and the sequence of each length rank
 };
 
 struct LoadSet {
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     Geo w;
     w.n = chain / a.Hv;
     w.h = chain % a.Hv;
-    if (a.cu && a.N <= 64) {
+    if (a.cu && a.N <= NT) {
         // longest sequences first: rank -> sequence (ties by index).  Thread m ranks sequence
         // m against the lengths staged in LDS; the ranks are a permutation of 0 .. N - 1.
         if (tid < a.N) sm.seq_len[tid] = a.cu[tid + 1] - a.cu[tid];

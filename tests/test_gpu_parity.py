@@ -76,11 +76,15 @@ EDGE = {
     "d128_bf16_ragged_gqa": dict(B=2, T=333, Hqk=2, Hv=4, Dk=128, dtype="bf16", g_scale=0.1,
                                  init_std=0.02),
     "d128_fp32": dict(B=1, T=130, Hqk=2, Dk=128, dtype="f32", g_scale=0.1, init_std=0.02),
-    # more than 64 packed sequences (no longest-first ordering), lengths 0..191
+    # 70 packed sequences, lengths 0..191
     "many_packed_seqs": dict(B=1, Hqk=2, Hv=2, Dk=128, dtype="bf16",
                              seqlens=[(37 * i) % 192 for i in range(70)], g_scale=0.1,
                              init_std=0.02, beta_scale=2.0),
-    # 64 packed sequences (the most that are ordered longest first), lengths 0..127
+    # 300 short packed sequences (ordered longest first), lengths 0..40
+    "packed_300_seqs": dict(B=1, Hqk=1, Hv=2, Dk=128, dtype="bf16",
+                            seqlens=[(29 * i + 3) % 41 for i in range(300)], g_scale=0.1,
+                            init_std=0.02, beta_scale=2.0),
+    # 64 packed sequences, lengths 0..127
     "packed_64_seqs": dict(B=1, Hqk=1, Hv=2, Dk=128, dtype="bf16",
                            seqlens=[(53 * i + 11) % 128 for i in range(64)], g_scale=0.1,
                            init_std=0.02),
