@@ -22,9 +22,10 @@
 //
 //   wave      SIMD  first half (.1)                    second half (.2)
 //   0, 1      0, 2  chain, chunk j: X = K M, R         Delta, state update
-//   3, 7      3     output: O of chunk j - 1, Y = Q M  P of chunk j
+//   3, 7      3     output: O of chunk j - 1 (to HBM),  P of chunk j
+//                   Y = Q M
 //                   (each wave: two 16-token row blocks, all 32 columns)
-//   4, 5      0, 2  loaders: K, scalars of j + 1       Q, V of j + 1; fetch j + 3; store O of j - 1
+//   4, 5      0, 2  loaders: K, scalars of j + 1       Q, V of j + 1; fetch j + 3
 //   6         1     T of chunk j (UT inverse of A)     A of chunk j + 1, diagonal tiles
 //   2         1     -                                  A of chunk j + 1, tiles below them
 //
@@ -38,7 +39,8 @@
 // accumulator tiles; products that consume its results take them as B operands through
 // register lane swaps (acc_to_b).  The output waves get the chain's bf16 state and Delta
 // fragments through LDS and use them as the A operands of the transposed products; P stays
-// in their registers.  LDS holds K and Q double-buffered, one V, T, A and O tile.
+// in their registers, and store O to HBM from their registers.  LDS holds K and Q
+// double-buffered and one V, T and A tile.
 #include <type_traits>
 
 #include "internal.h"
@@ -58,12 +60,10 @@ constexpr int NCW = DVS / CW;      // chain waves
 // conflict-free).  An operand read takes 16 rows x 2 chunks per 32 lanes, so the 16 row
 // offsets (pitch in dwords x row, mod 128) must be distinct multiples of 8: 72 dwords for
 // the 128-wide K and Q rows, 40 for the 64-wide T and A rows.  V (read only transposed,
-// 16 rows x 8 dwords) takes 24; the O tile 20 (its 8-byte stores from 16 rows fall on
-// distinct bank pairs).
+// 16 rows x 8 dwords) takes 24.
 constexpr int KPITCH = FD + 16;
 constexpr int CPITCH = FC + 16;
 constexpr int VPITCH = DVS + 16;
-constexpr int OPITCH = DVS + 8;
 // A's diagonal blocks, 120 packed fp16 entries each (+ a spare slot), 68 dwords apart: the
 // four blocks' broadcast reads fall on distinct banks.
 constexpr int ADPITCH = 136;
@@ -87,8 +87,6 @@ struct alignas(16) FusedSmem {
                                    //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m
     bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
-    __bf16 O[FC][OPITCH];          // O of the previous chunk, token-major (the output waves write
-                                   //   it, the loader waves store it to HBM in the second half)
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
     int seq_len[NT];               // packed batches of up to 512 sequences: their lengths,
     int rank_seq[NT];              //   and the sequence of each length rank
@@ -113,7 +111,7 @@ struct Geo {  // where this workgroup works
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct Streams {
-    __amdgpu_buffer_rsrc_t k, q, v, beta, g, o;
+    __amdgpu_buffer_rsrc_t k, q, v, beta, g;
     uint32_t kq_chunk, v_chunk, s_chunk;   // bytes per chunk of 64 tokens
     uint32_t off_kq[8], off_v[2], off_s;   // this lane's piece offsets within a chunk
 };
@@ -134,7 +132,6 @@ __device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w,
     st.v = rsrc(static_cast<const __bf16*>(a.v) + v0, v_end);
     st.beta = rsrc(a.beta + s0, s_end);
     st.g = rsrc(a.g ? a.g + s0 : a.beta + s0, a.g ? s_end : 0);
-    st.o = rsrc(static_cast<__bf16*>(a.o) + v0, v_end);   // o has v's layout
     st.kq_chunk = FC * kq_tok;
     st.v_chunk = FC * v_tok;
     st.s_chunk = FC * s_tok;
@@ -203,21 +200,6 @@ __device__ __forceinline__ void put_k(FusedSmem& sm, int j, int lt, const LoadSe
         s[SC_F2 * FC + lt] = __expf((blk == 0 ? ge[0] : blk == 1 ? ge[1] : blk == 2 ? ge[2] : ge[3]) - gv);
 #pragma unroll
         for (int I = 0; I < 3; ++I) s[(SC_F1 + I) * FC + lt] = __expf(fminf(gv - ge[I], 0.f));
-    }
-}
-
-// O of chunk j from the token-major tile to HBM: loader lane lt stores the 16-byte pieces
-// lt and lt + 128 (token piece / 4, columns 8 (piece % 4) ..).  Buffer stores: tokens past
-// the sequence end, and chunks outside it (j < 0 or j >= nchunks), fall outside the
-// descriptor and are dropped by the hardware.
-__device__ __forceinline__ void store_o(const FusedSmem& sm, const Streams& st, int j, int lt) {
-    const uint32_t tok_bytes = st.v_chunk / FC;
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-        const int piece = lt + NLD * pp, tok = piece >> 2, cg = piece & 3;
-        const bf16x8 v = ld8(&sm.O[tok][8 * cg]);
-        const uint32_t off = j < 0 ? 0xfffffff0u : (uint32_t)(j * FC + tok) * tok_bytes + 16 * cg;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), st.o, off, 0, 0);
     }
 }
 
@@ -621,6 +603,15 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         // Delta fragments serve unchanged as the A operands M^T and Delta^T, the query rows as
         // B operands, and P^T stays in registers from make_p.
         const int ow = wave == 3 ? 0 : 1;
+        // O goes to HBM from registers: a lane stores four consecutive columns of one token
+        // (8 bytes), through a buffer descriptor that covers exactly this sequence's tokens
+        // of the slice, so rows past the sequence end are dropped by the range check.  The
+        // other slices of the row, on the same XCD, fill the rest of its cache lines.
+        const long L = w.eos - w.bos;
+        const uint32_t o_tok = (uint32_t)a.Hv * FD * 2;
+        const __amdgpu_buffer_rsrc_t o_rs =
+            rsrc(static_cast<__bf16*>(a.o) + (w.bos * a.Hv + w.h) * FD + w.j0,
+                 L > 0 ? (uint32_t)((L - 1) * o_tok + DVS * 2) : 0);
         f32x4 yt[2][2];      // Y^T tile (u, c): columns 16 c + 4 q16 + e, query 16 R_u + l16
         bf16x8 pt[2][2];     // P^T of the chunk as B operands (make_p)
         bf16x8 qf[2][4];     // query rows of R_u: qf[u][ks] = keys 32 ks + 8 q16 ..
@@ -651,8 +642,11 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                         for (int sb = 0; sb < 2; ++sb)
                             if (2 * sb <= R) o = mma16(dq[c][sb], pt[u][sb], o);
-                        st4(&sm.O[16 * R + l16][16 * c + 4 * q16], a.scale * o[0], a.scale * o[1], a.scale * o[2],
-                            a.scale * o[3]);
+                        const uint32_t off = (uint32_t)(jp * FC + 16 * R + l16) * o_tok + (16 * c + 4 * q16) * 2;
+                        const uint32_t lo = pack_bf16x2(a.scale * o[0], a.scale * o[1]);
+                        const uint32_t hi = pack_bf16x2(a.scale * o[2], a.scale * o[3]);
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, o_rs, off, 0, 0);
                     }
                 }
             }
@@ -711,7 +705,6 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             put_q(sm, j + 1, lt, f1);
             put_v(sm, lt, f1);
             fetch(st, j + 3, f1);
-            store_o(sm, st, j - 1, lt);   // written by the output waves in this phase's first half
             __syncthreads();
             if (j + 1 >= nph) break;
             put_k(sm, j + 2, lt, f0);
@@ -719,7 +712,6 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             put_q(sm, j + 2, lt, f0);
             put_v(sm, lt, f0);
             fetch(st, j + 4, f0);
-            store_o(sm, st, j, lt);
             __syncthreads();
         }
     } else if (wave == 6) {
