@@ -65,7 +65,8 @@ def _load(lib_path: Optional[str] = None):
         d = ctypes.POINTER(ctypes.c_double)
         i64 = ctypes.c_int64
         lib.dn_oracle_fwd.argtypes = [i64, ctypes.POINTER(i64), i64, i64, i64, i64,
-                                      d, d, d, d, d, d, ctypes.c_double, d, d, ctypes.c_int]
+                                      d, d, d, d, d, d, ctypes.c_double, ctypes.c_int,
+                                      ctypes.c_double, d, d, ctypes.c_int]
         lib.dn_oracle_fwd.restype = ctypes.c_int
         lib.dn_oracle_max_threads.argtypes = []
         lib.dn_oracle_max_threads.restype = ctypes.c_int
@@ -87,9 +88,13 @@ def _ptr(a: Optional[np.ndarray]):
 def recurrent(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
               g: Optional[np.ndarray] = None, init: Optional[np.ndarray] = None,
               cu_seqlens: Optional[np.ndarray] = None, scale: float = 1.0,
-              nthreads: int = 0, lib_path: Optional[str] = None
+              nthreads: int = 0, lib_path: Optional[str] = None,
+              qk_l2norm: bool = False, eps: float = 1e-6
               ) -> Tuple[np.ndarray, np.ndarray]:
     """Run the token-by-token delta rule in fp64.
+
+    With ``qk_l2norm`` every q_t and k_t is first replaced by
+    ``x / sqrt(sum(x**2) + eps)`` (normalisation inside the rule).
 
     q, k: ``[B, T, Hqk, Dk]``; v: ``[B, T, Hv, Dv]``; beta, g: ``[B, T, Hv]``;
     init: ``[N, Hv, Dk, Dv]`` (key-major state) or None.  With ``cu_seqlens``
@@ -127,7 +132,8 @@ def recurrent(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
     final = np.zeros((N, Hv, Dk, Dv), dtype=np.float64)
     rc = lib.dn_oracle_fwd(N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                            Hqk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
-                           _ptr(init), float(scale), _ptr(o), _ptr(final), int(nthreads))
+                           _ptr(init), float(scale), int(bool(qk_l2norm)), float(eps),
+                           _ptr(o), _ptr(final), int(nthreads))
     if rc != 0:
         raise ValueError(f"dn_oracle_fwd rejected its arguments (rc={rc})")
     return o, final

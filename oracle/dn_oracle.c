@@ -20,6 +20,13 @@
  *       S'_t = exp(g_t) S_{t-1},   S_t = S'_t - beta_t (S'_t k_t - v_t) k_t^T,
  *       o_t  = scale * S_t q_t      (read after the write; scale = 1 on the pages).
  *   A missing gate (g == NULL) is the plain rule (exp(0) = 1).
+ *   Optional in-rule normalisation (qk_l2norm != 0): the frankenstein class text
+ *   L2-normalises queries and keys before the rule, and the mutichung DeltaNet block
+ *   flowchart puts an "L2 Norm" on q and k right before the "Delta Rule" box; the
+ *   nnterp queries/keys accessors list the conv, the activation and the head repeat
+ *   but no normalisation, so the rule itself may be handed raw q and k.  Each q_t
+ *   and k_t (per query/key head) is then replaced by x / sqrt(sum_i x_i^2 + eps)
+ *   before it is used (eps keeps a zero vector at zero; the pages give no value).
  *   The nnterp page's state_input: None on a fresh prompt (zero state here), else
  *   the state the call starts from.  A decode step is the same loop run for one
  *   token from the cached state.
@@ -52,9 +59,12 @@ int dn_oracle_fwd(int64_t N, const int64_t *cu,
                   int64_t Hqk, int64_t Hv, int64_t Dk, int64_t Dv,
                   const double *q, const double *k, const double *v,
                   const double *beta, const double *g, const double *init,
-                  double scale, double *o, double *final_state, int nthreads)
+                  double scale, int qk_l2norm, double eps,
+                  double *o, double *final_state, int nthreads)
 {
     if (N < 0 || Hqk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hqk != 0)
+        return -1;
+    if (qk_l2norm && !(eps >= 0.0))
         return -1;
     if (!cu || (N > 0 && (!q || !k || !v || !beta || !o)))
         return -1;
@@ -77,9 +87,11 @@ int dn_oracle_fwd(int64_t N, const int64_t *cu,
         /* S[j * Dk + i]: value row j, key column i -- the pages' S, d_v x d_k. */
         double *S = (double *)malloc(sizeof(double) * (size_t)(Dv * Dk));
         double *pred = (double *)malloc(sizeof(double) * (size_t)Dv);
-        if (!S || !pred) {
+        double *kq_n = (double *)malloc(sizeof(double) * (size_t)(2 * Dk));
+        if (!S || !pred || !kq_n) {
             free(S);
             free(pred);
+            free(kq_n);
             err |= 1;
             continue;
         }
@@ -95,6 +107,21 @@ int dn_oracle_fwd(int64_t N, const int64_t *cu,
             const double *kt = k + (t * Hqk + hq) * Dk;
             const double *qt = q + (t * Hqk + hq) * Dk;
             const double *vt = v + (t * Hv + h) * Dv;
+            if (qk_l2norm) {
+                /* k_t / sqrt(|k_t|^2 + eps), q_t / sqrt(|q_t|^2 + eps) */
+                double sk = 0.0, sq = 0.0;
+                for (int64_t i = 0; i < Dk; ++i) {
+                    sk += kt[i] * kt[i];
+                    sq += qt[i] * qt[i];
+                }
+                const double ik = 1.0 / sqrt(sk + eps), iq = 1.0 / sqrt(sq + eps);
+                for (int64_t i = 0; i < Dk; ++i) {
+                    kq_n[i] = kt[i] * ik;
+                    kq_n[Dk + i] = qt[i] * iq;
+                }
+                kt = kq_n;
+                qt = kq_n + Dk;
+            }
             const double bt = beta[t * Hv + h];
             /* decay first: S <- exp(g_t) S */
             if (g) {
@@ -130,6 +157,7 @@ int dn_oracle_fwd(int64_t N, const int64_t *cu,
         }
         free(S);
         free(pred);
+        free(kq_n);
     }
     return err ? -2 : 0;
 }

@@ -11,7 +11,8 @@ preconditions the pages put on those inputs are applied here:
 
 * q and k are L2-normalised per (token, head) before the rule (frankenstein
   DeltaNetAttention docstring; the L2 Norm box of the DeltaNet block flowchart on
-  the mutichung garden page), in fp64 and before any cast;
+  the mutichung garden page), in fp64 and before any cast -- unless the case asks
+  for raw q and k (``qk_raw``), for calls that normalise inside the rule;
 * beta is a sigmoid output in (0, 1), or twice that, in (0, 2), for the
   negative-eigenvalue variant (nnterp ``betas``);
 * the log decay g is non-positive (nnterp ``decays``), drawn as
@@ -139,14 +140,15 @@ def make_case(*, B: int = 1, T: int = 64, Hqk: int = 2, Hv: Optional[int] = None
               beta_scale: float = 1.0, g_scale: Optional[float] = None,
               init_std: Optional[float] = None, seqlens: Optional[Sequence[int]] = None,
               num_seqs_cut: Optional[int] = None, chunk: int = 64, seed: int = 0,
-              name: str = "case", decode: bool = False) -> DeltaInputs:
+              name: str = "case", decode: bool = False, qk_raw: bool = False) -> DeltaInputs:
     """Draw one case.
 
     ``beta = beta_scale * sigmoid(z)``; ``g = -g_scale * softplus(z)`` or no decay when
     ``g_scale`` is None; ``init ~ N(0, init_std^2)`` per sequence or a zero (None) state.
     A packed batch is asked for either with explicit ``seqlens`` or with
     ``num_seqs_cut`` = N, which cuts T at N - 1 distinct points drawn uniformly
-    without replacement from {1, ..., T - 1}.
+    without replacement from {1, ..., T - 1}.  With ``qk_raw`` q and k are the raw
+    N(0, 1) draws (norm about sqrt(Dk)), not normalised.
     """
     Hv = Hqk if Hv is None else Hv
     Dv = Dk if Dv is None else Dv
@@ -159,8 +161,11 @@ def make_case(*, B: int = 1, T: int = 64, Hqk: int = 2, Hv: Optional[int] = None
         if seqlens is not None:
             T = int(sum(seqlens))
     shape_qk = (B, T, Hqk, Dk)
-    q = _l2_normalise(rng.standard_normal(shape_qk))
-    k = _l2_normalise(rng.standard_normal(shape_qk))
+    q = rng.standard_normal(shape_qk)
+    k = rng.standard_normal(shape_qk)
+    if not qk_raw:
+        q = _l2_normalise(q)
+        k = _l2_normalise(k)
     v = rng.standard_normal((B, T, Hv, Dv))
     beta = (beta_scale * _sigmoid(rng.standard_normal((B, T, Hv)))).astype(np.float32)
     g = None
@@ -181,7 +186,7 @@ def make_case(*, B: int = 1, T: int = 64, Hqk: int = 2, Hv: Optional[int] = None
         name=name, dtype=dtype, B=B, T=T, Hqk=Hqk, Hv=Hv, Dk=Dk, Dv=Dv,
         q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), beta=beta, g=g,
         init=init, cu_seqlens=None if cu is None else cu.astype(np.int32),
-        chunk=chunk, decode=decode)
+        chunk=chunk, decode=decode, meta={"qk_raw": qk_raw})
 
 
 CONFIG_NAMES = {

@@ -294,7 +294,79 @@ def pin_batch_rows(run):
             _close(fin[b, h], Sb.T, 1e-12, "batch row state")
 
 
+# ------------------------------------------------ normalisation inside the rule
+# [P1] class text: queries and keys are L2-normalised; [P2] block flowchart: "L2 Norm" on
+# q and k right before the "Delta Rule" box.  Reading: x / sqrt(sum x^2 + eps).
+
+def _raw_qk(rng, shape, lo=0.05, hi=20.0):
+    """Gaussian vectors with per-vector magnitudes spread over [lo, hi]."""
+    x = _unit(rng.standard_normal(shape))
+    return x * rng.uniform(lo, hi, shape[:-1] + (1,))
+
+
+def pin_l2norm_is_library_normalise(run):
+    """With eps = 0, normalising inside the rule equals handing the rule inputs that
+    numpy has normalised (numpy.linalg.norm), over GQA heads, packed sequences, gate,
+    initial state and beta in (0, 2)."""
+    rng = np.random.default_rng(31)
+    Hqk, Hv, Dk, Dv = 2, 4, 6, 3
+    lens = [9, 0, 5]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = _raw_qk(rng, (1, T, Hqk, Dk))
+    k = _raw_qk(rng, (1, T, Hqk, Dk))
+    v = rng.standard_normal((1, T, Hv, Dv))
+    beta = rng.uniform(0, 2, (1, T, Hv))
+    g = -0.2 * rng.uniform(0, 1, (1, T, Hv))
+    M0 = rng.standard_normal((len(lens), Hv, Dk, Dv))
+    o1, f1 = run(q, k, v, beta, g, M0, cu_seqlens=cu, qk_l2norm=True, eps=0.0)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o2, f2 = run(qn, kn, v, beta, g, M0, cu_seqlens=cu)
+    _close(o1, o2, 1e-13, "normalised in the rule vs by numpy: o")
+    _close(f1, f2, 1e-13, "normalised in the rule vs by numpy: state")
+
+
+def pin_l2norm_eps_one_token(run):
+    """One token from the zero state with k = c u, q = d w (u, w unit): the normalised
+    key is c u / sqrt(c^2 + eps), so S_1 = beta v k^T / sqrt(c^2 + eps) and
+    o_1 = beta (u.w) c d / (sqrt(c^2 + eps) sqrt(d^2 + eps)) v.  Small c and d make eps
+    visible (it sits under the square root)."""
+    rng = np.random.default_rng(32)
+    Dk, Dv, eps = 5, 3, 1e-6
+    u = _unit(rng.standard_normal(Dk))
+    w = _unit(rng.standard_normal(Dk))
+    c, d, b = 2e-3, 3e-3, 0.7
+    v = rng.standard_normal(Dv)
+    o, fin = run((d * w).reshape(1, 1, 1, Dk), (c * u).reshape(1, 1, 1, Dk),
+                 v.reshape(1, 1, 1, Dv), np.full((1, 1, 1), b), qk_l2norm=True, eps=eps)
+    nk, nq = np.sqrt(c * c + eps), np.sqrt(d * d + eps)
+    _close(fin.reshape(Dk, Dv), b * np.outer(c * u / nk, v), 1e-14, "one-token state")
+    _close(o.reshape(Dv), b * (u @ w) * c * d / (nk * nq) * v, 1e-14, "one-token read")
+
+
+def pin_l2norm_scale_free(run):
+    """Normalised inside the rule, q_t and k_t count only by direction (eps = 0): any
+    positive per-token rescaling leaves o and the state unchanged; a zero key (eps > 0)
+    leaves the state only decayed."""
+    rng = np.random.default_rng(33)
+    T, Dk, Dv = 8, 4, 5
+    q, k, v, beta, g, M0 = _rand_seq(rng, T, Dk, Dv, True, True)
+    cq = rng.uniform(0.1, 10, (T, 1))
+    ck = rng.uniform(0.1, 10, (T, 1))
+    norm = dict(qk_l2norm=True, eps=0.0)
+    o1, f1 = _one(lambda *a, **kw: run(*a, **kw, **norm), q, k, v, beta, g, M0)
+    o2, f2 = _one(lambda *a, **kw: run(*a, **kw, **norm), cq * q, ck * k, v, beta, g, M0)
+    _close(o2, o1, 1e-13, "rescaled q, k: o")
+    _close(f2, f1, 1e-13, "rescaled q, k: state")
+    z = np.zeros((1, Dk))
+    o3, f3 = _one(lambda *a, **kw: run(*a, **kw, qk_l2norm=True, eps=1e-6),
+                  q[:1], z, v[:1], beta[:1], g[:1], M0)
+    _close(f3, np.exp(g[0]) * M0, 1e-15, "zero key: state only decayed")
+
+
 ALL_PINS = [pin_hand_worked, pin_product_form, pin_retrieve_interpolate, pin_beta_zero,
             pin_exact_recall, pin_one_token, pin_gate_order, pin_contraction, pin_linearity,
             pin_sgd_step, pin_gate_zero_is_plain, pin_scale, pin_heads_and_packing,
-            pin_batch_rows]
+            pin_batch_rows, pin_l2norm_is_library_normalise, pin_l2norm_eps_one_token,
+            pin_l2norm_scale_free]

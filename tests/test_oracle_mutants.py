@@ -63,6 +63,11 @@ MUTANTS = {
     "outer_uses_query": _sub("-= bt * pred[j] * kt[i];", "-= bt * pred[j] * qt[i];"),
     "read_before_write": lambda s: _move(s, READ, PRED),
     "decay_after_write": lambda s: _move(s, DECAY, "            /* o_t = scale * S_t q_t */\n"),
+    "norm_eps_outside_sqrt": _sub("ik = 1.0 / sqrt(sk + eps)", "ik = 1.0 / (sqrt(sk) + eps)"),
+    "norm_by_squared_norm": _sub("ik = 1.0 / sqrt(sk + eps)", "ik = 1.0 / (sk + eps)"),
+    "norm_keys_only": _sub("iq = 1.0 / sqrt(sq + eps)", "iq = 1.0"),
+    "norm_key_by_query": _sub("ik = 1.0 / sqrt(sk + eps)", "ik = 1.0 / sqrt(sq + eps)"),
+    "norm_skipped": _sub("if (qk_l2norm) {", "if (0) {"),
     "skips_first_token": _sub("for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {",
                               "for (int64_t t = cu[n] + 1; t < cu[n + 1]; ++t) {"),
 }
