@@ -223,6 +223,51 @@ def main():
     dec_b = decode_bytes(y.B, y.Hqk, y.Hv, y.Dk)
     dec_gbs = state_b / (dec_us * 1e-6) / 1e9
 
+    # ------------- in-rule q/k normalisation: the same two workloads handed raw q and k
+    xr = make_case(B=B, T=T, Hqk=Hqk, Dk=D, dtype="bf16", seed=0, qk_raw=True)
+    rsets = []
+    for i in range(args.copies):
+        rsets.append(dict(q=to_dev(xr.q), k=to_dev(xr.k), v=sets[i]["v"], beta=sets[i]["beta"],
+                          o=sets[i]["o"], fs=sets[i]["fs"], ws=sets[i]["ws"]))
+
+    def rstep(i):
+        s = rsets[i % len(rsets)]
+        dn.chunk_fwd(s["q"], s["k"], s["v"], s["beta"], None, None, out=s["o"], final_state=s["fs"],
+                     workspace=s["ws"], qk_l2norm=True)
+
+    for i in range(args.warmup):
+        rstep(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        rstep(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    norm_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    del rsets
+    yr = make_case(B=DECODE["N"], T=1, Hqk=DECODE["H"], Dk=DECODE["D"], dtype="bf16", g_scale=0.1,
+                   init_std=0.02, seed=0, decode=True, qk_raw=True)
+    rq, rk = to_dev(yr.q)[:, 0], to_dev(yr.k)[:, 0]
+    for i in range(3):
+        dn.decode_step(rq, rk, dv, db, dg, dstate[i % 2], out=dout, qk_l2norm=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.decode_reps):
+        dn.decode_step(rq, rk, dv, db, dg, dstate[i % 2], out=dout, qk_l2norm=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_norm_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
+    in_rule_norm = {
+        "what": "q and k handed raw (N(0,1) draws) and L2-normalised inside the call "
+                "(DN_QK_L2NORM, eps 1e-6); same workloads, same timing as above",
+        "prefill": {"kernel": "fused_kernel<false, true>", "us_per_call": norm_us,
+                    "tokens_per_s": tokens / (norm_us * 1e-6),
+                    "hbm_frac": alg_b / (norm_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "vs_prenormalised_call": norm_us / call_us},
+        "decode": {"kernel": "decode_kernel (normalising)", "us_per_step": dec_norm_us,
+                   "hbm_frac": dec_b / (dec_norm_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+    }
+
     # ------------------------------------ the other two full-size prefill workloads
     # (context beside the headline: each timed the same way, with HIP events around a loop
     # of back-to-back calls on the launching stream)
@@ -275,7 +320,7 @@ def main():
                    "heads": Hv, "head_dim": D, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_p,
-                     "kernel": "fused_kernel<false> (the only kernel of a dn_chunk_fwd call)",
+                     "kernel": "fused_kernel<false, false> (the only kernel of a dn_chunk_fwd call)",
                      "call_us": call_us, "algorithmic_bytes": alg_b},
         "timing": {"loop": "eager" if args.eager else "hip_graph_replay",
                    "ms_per_step_eager": wall_eager * 1e3 / args.steps},
@@ -289,6 +334,7 @@ def main():
                                 "traffic": traffic_d, "kernel": "decode_kernel",
                                 "algorithmic_bytes": dec_b}},
         "prefill_other_workloads": other,
+        "in_rule_qk_l2norm": in_rule_norm,
         "cpu_baseline": None,
     }
     if not args.no_cpu:

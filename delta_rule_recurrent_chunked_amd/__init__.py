@@ -42,7 +42,15 @@ class _Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("Hqk", ctypes.c_int32), ("Hv", ctypes.c_int32), ("Dk", ctypes.c_int32),
                 ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("flags", ctypes.c_int32), ("l2norm_eps", ctypes.c_float)]
+
+
+DN_QK_L2NORM = 1
+
+
+def _norm_flags(qk_l2norm: bool, l2norm_eps: float):
+    return (DN_QK_L2NORM if qk_l2norm else 0), float(l2norm_eps)
 
 
 _lib = None
@@ -126,7 +134,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
               scale: float = 1.0, chunk_size: int = 64, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = True
+              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = True,
+              qk_l2norm: bool = False, l2norm_eps: float = 1e-6
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Delta rule over whole sequences (prefill), chunkwise-parallel form.
 
@@ -138,6 +147,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     it in place); ``out`` and ``workspace`` may be passed to avoid allocation.
     ``check_cu_seqlens`` copies cu_seqlens to the host (a synchronising copy) and
     checks ``cu[0] == 0``, non-decreasing, ``cu[N] == T``: the kernels trust it.
+    ``qk_l2norm`` normalises q and k inside the call, x / sqrt(|x|^2 + l2norm_eps).
     """
     lib = load_library()
     _dev(q, "q")
@@ -178,7 +188,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
         final_state = torch.empty((N, Hv, Dk, Dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _dev(final_state, "final_state", torch.float32, (N, Hv, Dk, Dv))
-    shape = _Shape(B, T, N, Hqk, Hv, Dk, Dv, _dtype_code(q), chunk_size, float(scale))
+    shape = _Shape(B, T, N, Hqk, Hv, Dk, Dv, _dtype_code(q), chunk_size, float(scale),
+                   *_norm_flags(qk_l2norm, l2norm_eps))
     need = int(lib.dn_chunk_fwd_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
@@ -197,11 +208,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                 g: Optional[torch.Tensor], state: torch.Tensor, scale: float = 1.0,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                l2norm_eps: float = 1e-6) -> torch.Tensor:
     """One token per sequence against the cached ``state`` (updated in place).
 
     q, k ``[N, Hqk, Dk]``, v ``[N, Hv, Dv]``; beta, g ``[N, Hv]`` float32 (g may be
     None); state ``[N, Hv, Dk, Dv]`` float32.  Returns o ``[N, Hv, Dv]``.
+    ``qk_l2norm`` normalises q and k inside the call, as in :func:`chunk_fwd`.
     """
     lib = load_library()
     _dev(q, "q")
@@ -221,7 +234,8 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
         out = torch.empty((N, Hv, Dv), dtype=q.dtype, device=q.device)
     else:
         _dev(out, "out", q.dtype, (N, Hv, Dv))
-    shape = _Shape(N, 1, N, Hqk, Hv, Dk, Dv, _dtype_code(q), 0, float(scale))
+    shape = _Shape(N, 1, N, Hqk, Hv, Dk, Dv, _dtype_code(q), 0, float(scale),
+                   *_norm_flags(qk_l2norm, l2norm_eps))
     with torch.cuda.device(q.device):
         rc = lib.dn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                 _ptr(g), _ptr(state), _ptr(out), _stream(q.device))

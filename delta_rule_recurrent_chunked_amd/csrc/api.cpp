@@ -20,6 +20,9 @@ dn_status check_common(const dn_shape* s) {
     if (s->Hv % s->Hqk != 0) return DN_ERR_INVALID_ARG;
     if (s->dtype != DN_F32 && s->dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
     if (!dim_ok(s->Dk) || !dim_ok(s->Dv)) return DN_ERR_UNSUPPORTED;
+    if (s->flags & ~DN_QK_L2NORM) return DN_ERR_INVALID_ARG;
+    if ((s->flags & DN_QK_L2NORM) && !(s->l2norm_eps >= 0.f && s->l2norm_eps <= 3.0e38f))
+        return DN_ERR_INVALID_ARG;
     return DN_OK;
 }
 
@@ -27,7 +30,7 @@ dn_status check_common(const dn_shape* s) {
 
 extern "C" {
 
-int32_t dn_version(void) { return 10000; }
+int32_t dn_version(void) { return 10100; }
 
 const char* dn_status_str(dn_status st) {
     switch (st) {
@@ -54,6 +57,8 @@ static dn_status prefill_shape(const dn_shape* s, bool packed, dn::PrefillArgs& 
     a = dn::PrefillArgs{};
     a.B = s->B; a.T = s->T; a.N = s->num_seqs; a.Hqk = s->Hqk; a.Hv = s->Hv;
     a.Dk = s->Dk; a.Dv = s->Dv; a.C = C; a.bf16 = s->dtype == DN_BF16; a.scale = s->scale;
+    a.qk_norm = (s->flags & DN_QK_L2NORM) != 0;
+    a.eps = s->l2norm_eps;
     return DN_OK;
 }
 
@@ -109,6 +114,8 @@ dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const 
     dn::DecodeArgs a{};
     a.N = s->B; a.Hqk = s->Hqk; a.Hv = s->Hv; a.Dk = s->Dk; a.Dv = s->Dv;
     a.bf16 = s->dtype == DN_BF16; a.scale = s->scale;
+    a.qk_norm = (s->flags & DN_QK_L2NORM) != 0;
+    a.eps = s->l2norm_eps;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.state = state; a.o = o;
     return dn::launch_decode(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }

@@ -9,6 +9,9 @@
 //                                            Rule" section of the mutichung DeltaNet page)
 //   o      = scale (a r_q + (k.q) delta)    (= scale S_t q with S_t = S' + delta k^T)
 //   M     <- a M + k delta^T
+// With the in-rule normalisation (q, k -> x / sqrt(|x|^2 + eps)) the norms come out of
+// the same reductions: r_k, r_q and k.q take the factors 1/|k|, 1/|q|, and the update
+// adds k (delta / |k|)^T.
 // The state is read once and written once: this kernel is bound by HBM bandwidth.
 //
 // Work decomposition: one workgroup per (n, h, slice of CW value columns; CW = Dv).  A
@@ -58,7 +61,7 @@ template <typename T, int DK, int DV, int CW, bool VEC>
 __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(DecodeArgs a) {
     using S = DecodeShape<DK, CW>;
     constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
-    __shared__ float red[NW][2 * CW + 1];
+    __shared__ float red[NW][2 * CW + 3];
     __shared__ float dsh[CW];
 
     const int tid = threadIdx.x;
@@ -98,7 +101,8 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     const float alpha = a.g ? expf(a.g[nh]) : 1.0f;
     const float beta = a.beta[nh];
 
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+    const bool nrm = a.qk_norm;
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
 #pragma unroll
@@ -106,7 +110,11 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
             pk[c] += m[p][c] * kr[p];
             pq[c] += m[p][c] * qr[p];
         }
-        if (ct == 0) kq += kr[p] * qr[p];
+        if (ct == 0) {
+            kq += kr[p] * qr[p];
+            kk += kr[p] * kr[p];
+            qq += qr[p] * qr[p];
+        }
     }
     // reduce over the row groups of this wave (lanes that share ct)
 #pragma unroll
@@ -117,6 +125,10 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
             pq[c] += __shfl_xor(pq[c], off);
         }
         kq += __shfl_xor(kq, off);
+        if (nrm) {
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
+        }
     }
     const int lane = tid % 64, wave = tid / 64;
     if (lane < TPR) {
@@ -125,19 +137,33 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
             red[wave][ct * 4 + c] = pk[c];
             red[wave][CW + ct * 4 + c] = pq[c];
         }
-        if (lane == 0) red[wave][2 * CW] = kq;
+        if (lane == 0) {
+            red[wave][2 * CW] = kq;
+            red[wave][2 * CW + 1] = kk;
+            red[wave][2 * CW + 2] = qq;
+        }
     }
     __syncthreads();
     if (tid < CW) {
-        float rk = 0.f, rq = 0.f, kqs = 0.f;
+        float rk = 0.f, rq = 0.f, kqs = 0.f, kks = 0.f, qqs = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             rk += red[w][tid];
             rq += red[w][CW + tid];
             kqs += red[w][2 * CW];
+            kks += red[w][2 * CW + 1];
+            qqs += red[w][2 * CW + 2];
+        }
+        float ik = 1.f;   // 1/|k| of the in-rule normalisation
+        if (nrm) {
+            ik = inv_norm(kks, a.eps);
+            const float iq = inv_norm(qqs, a.eps);
+            rk *= ik;
+            rq *= iq;
+            kqs *= ik * iq;
         }
         const float d = beta * (vval - alpha * rk);
-        dsh[tid] = d;
+        dsh[tid] = d * ik;
         st_out(static_cast<T*>(a.o), vo, a.scale * (alpha * rq + kqs * d));
     }
     __syncthreads();

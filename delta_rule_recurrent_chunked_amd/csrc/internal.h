@@ -12,6 +12,8 @@ struct PrefillArgs {
     int B, T, N, Hqk, Hv, Dk, Dv, C;
     int bf16;                       // 1: q/k/v/o are bfloat16, 0: float
     float scale;
+    int qk_norm;                    // 1: q, k -> x / sqrt(|x|^2 + eps) inside the rule
+    float eps;
     const void* q;
     const void* k;
     const void* v;
@@ -29,6 +31,8 @@ struct DecodeArgs {
     int N, Hqk, Hv, Dk, Dv;
     int bf16;
     float scale;
+    int qk_norm;                    // as in PrefillArgs
+    float eps;
     const void* q;
     const void* k;
     const void* v;
@@ -54,6 +58,13 @@ __device__ __forceinline__ float ld_f32(const __bf16* p, long i) { return (float
 
 __device__ __forceinline__ void st_out(float* p, long i, float x) { p[i] = x; }
 __device__ __forceinline__ void st_out(__bf16* p, long i, float x) { p[i] = (__bf16)x; }
+
+// 1 / sqrt(ss + eps) of the in-rule q/k normalisation (ss = sum of squares); a zero
+// vector with eps == 0 normalises to zero.
+__device__ __forceinline__ float inv_norm(float ss, float eps) {
+    const float x = ss + eps;
+    return x > 0.f ? rsqrtf(x) : 0.f;
+}
 
 // Token range [bos, eos) of sequence n.
 __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, long& bos, long& eos) {

@@ -13,6 +13,20 @@
 //   O     = scale (diag(exp(gamma)) Q M + P Delta),  P_ri = exp(gamma_r - gamma_i) q_r.k_i (i <= r)
 //   M    <- exp(gamma_last) M + K^T diag(exp(gamma_last - gamma)) Delta
 //
+// With the in-rule normalisation (q, k -> x / sqrt(|x|^2 + eps)) the kernel keeps the raw
+// q and k as matrix operands and folds the norms into per-token factors.  With
+// s_r = 1 / |k_r| and Delta'_r = s_r Delta_r, row r of (I + A) Delta = R times s_r gives
+//
+//   A'_ri = beta_r s_r^2 exp(gamma_r - gamma_i) k_r.k_i,     (I + A') Delta' = R'
+//   R'_r  = beta_r s_r v_r - beta_r s_r^2 exp(gamma_r) (K M)_r
+//   O_r   = scale / |q_r| (exp(gamma_r) (Q M)_r + (P Delta')_r)
+//   M    <- exp(gamma_last) M + K^T diag(exp(gamma_last - gamma)) Delta'
+//
+// with P and the state update in raw q and k: only the per-token scalars change.  The
+// squared norms come from the matrix cores: |k_r|^2 is the diagonal of the K K^T tiles the
+// UT-inverse wave builds for A's diagonal blocks, and |q_r|^2 the diagonal of Q Q^T tiles
+// the output waves add to their P products.
+//
 // One workgroup of eight waves per (sequence, value head, 32-column slice of the state).
 // The value columns of the state are independent, so slices never exchange data; the
 // chunk-local matrices (A, T, P) are recomputed by each slice's workgroup, which keeps
@@ -75,7 +89,10 @@ constexpr int NLD = 128;           // loader threads (waves 4, 5)
 // exp(gamma_r - gamma_i) for i in block I < block of r factors as
 // F1[I][r] * F2[i] = exp(gamma_r - gamma_e(I)) * exp(gamma_e(I) - gamma_i), both <= 1 when
 // g <= 0, so the masks of the blocks below the diagonal need no exponentials.
-enum Sc { SC_BETA = 0, SC_GAM = 1, SC_EG = 2, SC_TAIL = 3, SC_F2 = 4, SC_F1 = 5, SC_N = 8 };
+// With the in-rule normalisation (s_r = 1 / sqrt(|k_r|^2 + eps)): SC_B1 = beta_r s_r,
+// SC_B2 = beta_r s_r^2 exp(gamma_r), SC_S2 = s_r^2.
+enum Sc { SC_BETA = 0, SC_GAM = 1, SC_EG = 2, SC_TAIL = 3, SC_F2 = 4, SC_F1 = 5,
+          SC_B1 = 8, SC_B2 = 9, SC_S2 = 10, SC_N = 11 };
 
 struct alignas(16) FusedSmem {
     __bf16 K[2][FC][KPITCH];       // chunk keys, token-major (chunk j in K[j & 1])
@@ -252,14 +269,29 @@ __device__ __forceinline__ f32x4 decay_eval(const DecayIn& x, bool diag) {
     return d;
 }
 
+// Diagonal entry of row l16 of a 16x16 Gram tile (entry (4 q16 + e, l16) in lane
+// (l16, q16)), in every lane: lane l16 + 16 (l16 >> 2) holds it as entry l16 & 3.
+__device__ __forceinline__ float gram_diag(const f32x4& g, int l16) {
+    const int e = l16 & 3;
+    const float mine = e == 0 ? g[0] : e == 1 ? g[1] : e == 2 ? g[2] : g[3];
+    const int src = l16 + 16 * (l16 >> 2);
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, mine)));
+}
+
 // A of chunk j, one part of its tiles (I, R).  Part 0, the four diagonal tiles, goes to
 // Ad in fp32 (strictly lower part, packed); part 1, the six tiles below them, to Ab in bf16.
 constexpr int a_tiles(int part) { return part == 0 ? 4 : 6; }
 constexpr int a_tile_i(int part, int n) { return part == 0 ? n : (n == 2 || n == 4) ? 1 : n == 5 ? 2 : 0; }
 constexpr int a_tile_r(int part, int n) { return part == 0 ? n : n == 0 ? 1 : n <= 2 ? 2 : 3; }
 
-template <bool GATED, int PART>
-__device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
+//
+// With the in-rule normalisation, part 0 takes |k_r|^2 from the diagonal of its own Gram
+// tiles, scales A's rows by s_r^2 and publishes the chain's factors (SC_B1, SC_B2, SC_S2)
+// for row 16 q16 + l16.  Part 1 writes its tiles with beta alone; their consumers apply
+// s_r^2 to the rows of the products they form from them.
+template <bool GATED, bool NORM, int PART>
+__device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16, float eps) {
+    constexpr bool NRM = NORM && PART == 0;
     constexpr int NTL = a_tiles(PART);
     // every LDS read before the first store (a read after a store waits a round trip)
     const float* s = &sm.sc[j % 3][0][0];
@@ -271,6 +303,8 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
         br[n] = s[SC_BETA * FC + r];
         if (GATED) din[n] = decay_load(s, R, I, r, 16 * I + 4 * q16);
     }
+    float egq = 1.f;
+    if (NRM) egq = s[SC_EG * FC + 16 * q16 + l16];
     bf16x8 kf[4][4];
     load_rows(sm.K[j & 1], l16, q16, kf);
     sched_fence();  // all fragments in one round trip (the compiler would stage them)
@@ -282,6 +316,19 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16) {
 #pragma unroll
         for (int n = 0; n < NTL; ++n)
             G[n] = mma16(kf[a_tile_i(PART, n)][ks], kf[a_tile_r(PART, n)][ks], G[n]);
+    if (NRM) {
+        float rs[NTL];   // s_r of row 16 n + l16
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) rs[n] = inv_norm(gram_diag(G[n], l16), eps);
+        const float rq = q16 == 0 ? rs[0] : q16 == 1 ? rs[1] : q16 == 2 ? rs[2] : rs[3];
+        const float bq = q16 == 0 ? br[0] : q16 == 1 ? br[1] : q16 == 2 ? br[2] : br[3];
+        float* so = &sm.sc[j % 3][0][0];
+        so[SC_S2 * FC + 16 * q16 + l16] = rq * rq;
+        so[SC_B1 * FC + 16 * q16 + l16] = bq * rq;
+        so[SC_B2 * FC + 16 * q16 + l16] = bq * rq * rq * egq;
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) br[n] *= rs[n] * rs[n];
+    }
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
         const int I = a_tile_i(PART, n), R = a_tile_r(PART, n);
@@ -320,9 +367,12 @@ __device__ __forceinline__ void load_ad(const FusedSmem& sm, int q16, f16x8 (&ap
 // through LDS.
 constexpr int p_block(int half, int u) { return half == 0 ? (u == 0 ? 0 : 3) : (u == 0 ? 1 : 2); }
 
-template <bool GATED, int HALF>
+//
+// With the in-rule normalisation it also returns |q_r|^2 of its query rows (qn[u], row
+// 16 R_u + l16), the diagonal of Q Q^T tiles formed from the same fragments.
+template <bool GATED, bool NORM, int HALF>
 __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 (&qf)[2][4], int l16, int q16,
-                                       bf16x8 (&pt)[2][2]) {
+                                       bf16x8 (&pt)[2][2], float (&qn)[2]) {
     const float* s = &sm.sc[j % 3][0][0];
     DecayIn din[2][4];
     if (GATED) {
@@ -348,6 +398,15 @@ __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 
 #pragma unroll
             for (int I = 0; I <= R; ++I) G[u][I] = mma16(kf[I][ks], qf[u][ks], G[u][I]);
         }
+    if (NORM) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) gq = mma16(qf[u][ks], qf[u][ks], gq);
+            qn[u] = gram_diag(gq, l16);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int R = p_block(HALF, u);
@@ -374,7 +433,12 @@ __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 
 // the outer one as a B operand in registers.  The rest of T is never formed: the chain
 // waves finish Delta by block substitution over the two 32-token halves.  The zero blocks
 // of Tt are written once, before the first chunk.
-__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f16x8 (&ap)[15]) {
+//
+// With the in-rule normalisation the stored A21 rows lack s_r^2 (the tiles below the
+// block diagonal are written with beta alone): the product A21 T11 takes it per row, from
+// s2 = the chunk's SC_S2 scalars.
+template <bool NORM>
+__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f16x8 (&ap)[15], const float* s2) {
     {
         // lane = 16 * block + column c: solve (I + A_bb) x = e_c in the column order: once
         // x[m] is final, subtract its share from every later row.  ap holds the block's
@@ -413,6 +477,7 @@ __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f1
         const bf16x8 af = live ? ld8(&sm.Ab[base + 16 + l16][base + 8 * q16]) : zero8();
         const bf16x8 bf = live ? ld8(&sm.Tt[base + l16][base + 8 * q16]) : zero8();
         X[h] = mma16(af, bf, z4);
+        if (NORM) X[h] *= *reinterpret_cast<const f32x4*>(&s2[base + 16 + 4 * q16]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -426,7 +491,7 @@ __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f1
 }
 
 // -------------------------------------------------------------------------- kernel
-template <bool GATED>
+template <bool GATED, bool NORM>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void fused_kernel(PrefillArgs a) {
     __shared__ FusedSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -503,9 +568,14 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             bf16x8 rb0;   // R rows 0..31 as B operand (k = token)
             f32x4 R[4];   // R, token tile t: tokens 16 t + 4 q16 + e, column jc + l16
             bf16x8 abl[2];  // A rows 32..63, tokens 0..31 (read here: the A waves rewrite Ab in .2)
+            f32x4 s2bl[2];  // in-rule normalisation: s_r^2 of those rows (Ab holds them without)
             if (live) {
 #pragma unroll
                 for (int t = 2; t < 4; ++t) abl[t - 2] = ld8(&sm.Ab[16 * t + l16][8 * q16]);
+                if (NORM) {
+#pragma unroll
+                    for (int t = 2; t < 4; ++t) s2bl[t - 2] = *reinterpret_cast<const f32x4*>(&s[SC_S2 * FC + 16 * t + 4 * q16]);
+                }
                 // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
                 f32x4 X[4];
 #pragma unroll
@@ -519,12 +589,19 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int r0 = 16 * t + 4 * q16;
-                    const f32x4 bt = *reinterpret_cast<const f32x4*>(&s[SC_BETA * FC + r0]);
                     const bf16x4 vv = trld(&sm.V[r0 + (l16 >> 2)][jc + 4 * (l16 & 3)]);
-                    f32x4 eg = {1.f, 1.f, 1.f, 1.f};
-                    if (GATED) eg = *reinterpret_cast<const f32x4*>(&s[SC_EG * FC + r0]);
+                    if (NORM) {  // R' = beta s V - beta s^2 exp(gamma) X
+                        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&s[SC_B1 * FC + r0]);
+                        const f32x4 b2 = *reinterpret_cast<const f32x4*>(&s[SC_B2 * FC + r0]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) R[t][e] = bt[e] * ((float)vv[e] - eg[e] * X[t][e]);
+                        for (int e = 0; e < 4; ++e) R[t][e] = b1[e] * (float)vv[e] - b2[e] * X[t][e];
+                    } else {
+                        const f32x4 bt = *reinterpret_cast<const f32x4*>(&s[SC_BETA * FC + r0]);
+                        f32x4 eg = {1.f, 1.f, 1.f, 1.f};
+                        if (GATED) eg = *reinterpret_cast<const f32x4*>(&s[SC_EG * FC + r0]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) R[t][e] = bt[e] * ((float)vv[e] - eg[e] * X[t][e]);
+                    }
                 }
                 rb0 = acc_to_b(R[0], R[1]);
             }
@@ -550,7 +627,10 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 }
                 const bf16x8 dtop = acc_to_b(-D[0], -D[1]);
 #pragma unroll
-                for (int t = 2; t < 4; ++t) R[t] = mma16(abl[t - 2], dtop, R[t]);
+                for (int t = 2; t < 4; ++t) {
+                    if (NORM) R[t] += s2bl[t - 2] * mma16(abl[t - 2], dtop, f32x4{0.f, 0.f, 0.f, 0.f});
+                    else R[t] = mma16(abl[t - 2], dtop, R[t]);
+                }
                 const bf16x8 zb = acc_to_b(R[2], R[3]);
 #pragma unroll
                 for (int t = 2; t < 4; ++t) {
@@ -615,6 +695,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         f32x4 yt[2][2];      // Y^T tile (u, c): columns 16 c + 4 q16 + e, query 16 R_u + l16
         bf16x8 pt[2][2];     // P^T of the chunk as B operands (make_p)
         bf16x8 qf[2][4];     // query rows of R_u: qf[u][ks] = keys 32 ks + 8 q16 ..
+        float qn[2] = {0.f, 0.f};   // in-rule normalisation: |q_r|^2 of the rows of P^T
         __syncthreads();
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
@@ -628,10 +709,14 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int sb = 0; sb < 2; ++sb) dq[c][sb] = sm.dd[c][sb][lane];
-                float egr[2] = {1.f, 1.f};
+                float egr[2] = {1.f, 1.f}, osc[2] = {a.scale, a.scale};
                 if (GATED) {
 #pragma unroll
                     for (int u = 0; u < 2; ++u) egr[u] = s[SC_EG * FC + 16 * (ow == 0 ? 3 * u : 1 + u) + l16];
+                }
+                if (NORM) {  // scale / |q_r|
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) osc[u] *= inv_norm(qn[u], a.eps);
                 }
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
@@ -643,8 +728,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                         for (int sb = 0; sb < 2; ++sb)
                             if (2 * sb <= R) o = mma16(dq[c][sb], pt[u][sb], o);
                         const uint32_t off = (uint32_t)(jp * FC + 16 * R + l16) * o_tok + (16 * c + 4 * q16) * 2;
-                        const uint32_t lo = pack_bf16x2(a.scale * o[0], a.scale * o[1]);
-                        const uint32_t hi = pack_bf16x2(a.scale * o[2], a.scale * o[3]);
+                        const uint32_t lo = pack_bf16x2(osc[u] * o[0], osc[u] * o[1]);
+                        const uint32_t hi = pack_bf16x2(osc[u] * o[2], osc[u] * o[3]);
                         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                         __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, o_rs, off, 0, 0);
                     }
@@ -677,8 +762,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             }
             __syncthreads();
             if (y_live) {  // P of chunk j for the same query rows
-                if (ow == 0) make_p<GATED, 0>(sm, j, qf, l16, q16, pt);
-                else make_p<GATED, 1>(sm, j, qf, l16, q16, pt);
+                if (ow == 0) make_p<GATED, NORM, 0>(sm, j, qf, l16, q16, pt, qn);
+                else make_p<GATED, NORM, 1>(sm, j, qf, l16, q16, pt, qn);
             }
             __syncthreads();
         }
@@ -728,14 +813,14 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         // the longer steps of both halves; the other A wave has slack
         __builtin_amdgcn_s_setprio(2);
         __syncthreads();
-        make_a<GATED, 0>(sm, 0, l16, q16);
+        make_a<GATED, NORM, 0>(sm, 0, l16, q16, a.eps);
         load_ad(sm, q16, ap);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            if (j < nc) make_t(sm, l16, q16, ap);
+            if (j < nc) make_t<NORM>(sm, l16, q16, ap, &sm.sc[j % 3][SC_S2][0]);
             __syncthreads();
             if (j + 1 < nc) {
-                make_a<GATED, 0>(sm, j + 1, l16, q16);
+                make_a<GATED, NORM, 0>(sm, j + 1, l16, q16, a.eps);
                 load_ad(sm, q16, ap);
             }
             __syncthreads();
@@ -743,11 +828,11 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     } else {
         // -------------------------------------------- wave 2: other half of A of j + 1
         __syncthreads();
-        make_a<GATED, 1>(sm, 0, l16, q16);
+        make_a<GATED, NORM, 1>(sm, 0, l16, q16, a.eps);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
             __syncthreads();
-            if (j + 1 < nc) make_a<GATED, 1>(sm, j + 1, l16, q16);
+            if (j + 1 < nc) make_a<GATED, NORM, 1>(sm, j + 1, l16, q16, a.eps);
             __syncthreads();
         }
     }
@@ -766,10 +851,14 @@ hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s) {
     const long blocks = (long)a.N * a.Hv * NSL;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (blocks > 0) {
-        if (a.g)
-            hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, s, a);
-        else
-            hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, s, a);
+        const dim3 grid((unsigned)blocks), block(NT);
+        if (a.qk_norm) {
+            if (a.g) hipLaunchKernelGGL((fused_kernel<true, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((fused_kernel<false, true>), grid, block, 0, s, a);
+        } else {
+            if (a.g) hipLaunchKernelGGL((fused_kernel<true, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((fused_kernel<false, false>), grid, block, 0, s, a);
+        }
     }
     return hipGetLastError();
 }

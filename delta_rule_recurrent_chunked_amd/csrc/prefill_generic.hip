@@ -19,6 +19,8 @@
 // arithmetic.  The decay factors are formed as exp(gamma_r - gamma_i) for i <= r only
 // (never as a ratio of two exponentials), so strong decay cannot produce 0/0.
 //
+// With the in-rule normalisation the chunk's K and Q rows are normalised in LDS first.
+//
 // One workgroup per (sequence, value head, slice of GS value columns); the value
 // columns of the state are independent, so slices need no exchange.  K, Q, the V
 // slice, the state slice, A and P live in LDS for the whole chunk.
@@ -103,6 +105,27 @@ __global__ __launch_bounds__(NT) void prefill_generic_kernel(PrefillArgs a) {
             for (int r = 0; r < C; ++r) {
                 s += sm.gam[r];
                 sm.gam[r] = s;
+            }
+        }
+        if (a.qk_norm) {  // q, k -> x / sqrt(|x|^2 + eps) in place, four threads per row
+            const int r = tid >> 2, part = tid & 3;
+            float sk = 0.f, sq = 0.f;
+            if (r < C) {
+                for (int x = part; x < Dk; x += 4) {
+                    sk += sm.K[r][x] * sm.K[r][x];
+                    sq += sm.Q[r][x] * sm.Q[r][x];
+                }
+            }
+            sk += __shfl_xor(sk, 1);
+            sk += __shfl_xor(sk, 2);
+            sq += __shfl_xor(sq, 1);
+            sq += __shfl_xor(sq, 2);
+            const float ik = inv_norm(sk, a.eps), iq = inv_norm(sq, a.eps);
+            if (r < C) {
+                for (int x = part; x < Dk; x += 4) {
+                    sm.K[r][x] *= ik;
+                    sm.Q[r][x] *= iq;
+                }
             }
         }
         __syncthreads();

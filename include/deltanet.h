@@ -16,9 +16,13 @@
  *
  *   With g absent the decay factor is 1 (the plain delta rule).  beta may lie in
  *   (0, 1), or in (0, 2) for the negative-eigenvalue variant (nnterp "betas"); any
- *   real beta is computed as given.  q and k are expected to be L2-normalised by the
- *   caller (the frankenstein forward and the DeltaNet block flowchart normalise
- *   them before the rule); the library does not normalise.
+ *   real beta is computed as given.  q and k are L2-normalised before the rule (the
+ *   frankenstein class text; the "L2 Norm" box right before the "Delta Rule" box of
+ *   the mutichung DeltaNet block flowchart): either by the caller (the default), or
+ *   inside the call when shape->flags has DN_QK_L2NORM, which replaces every q_t
+ *   and k_t by x / sqrt(sum_i x_i^2 + l2norm_eps) before it is used (the nnterp
+ *   queries/keys accessors list the conv, activation and head repeat but no
+ *   normalisation, so the values at the rule may be raw).
  *
  *   A prompt runs the chunked (chunkwise-parallel) form of the rule over the whole
  *   sequence; a decode step runs the rule for one token against the cached state,
@@ -71,8 +75,17 @@ typedef enum {
     DN_BF16 = 1              /* q, k, v and o are bfloat16 (round to nearest even)     */
 } dn_dtype;
 
+/* dn_shape.flags bits */
+#define DN_QK_L2NORM 1       /* L2-normalise q_t and k_t inside the call (see above)        */
+
 /* Sizes of one call.  Supported: Dk, Dv in {16, 32, 64, 128}; chunk_size in
- * {16, 32, 64} (0 selects 64).  beta, g and all states are fp32 regardless of dtype. */
+ * {16, 32, 64} (0 selects 64).  beta, g and all states are fp32 regardless of dtype.
+ * flags: 0 or DN_QK_L2NORM (other bits are an error); l2norm_eps >= 0 (finite) is read
+ * only with DN_QK_L2NORM.  With l2norm_eps == 0 a zero q or k vector normalises to
+ * zero.  The bf16 Dk = Dv = 128 path folds the normalisation into per-token factors
+ * and keeps A's 16x16 diagonal blocks in fp16: their entries are bounded by beta
+ * times the ratio of two key norms of one chunk, so key norms within a chunk may
+ * differ by up to about 10^4. */
 typedef struct {
     int32_t B;           /* batch rows; 1 when cu_seqlens is given                       */
     int32_t T;           /* tokens per row; total packed tokens when cu_seqlens is given */
@@ -84,6 +97,8 @@ typedef struct {
     int32_t dtype;       /* dn_dtype of q, k, v, o                                        */
     int32_t chunk_size;  /* tokens per chunk of the chunked form                          */
     float scale;         /* multiplies every read; 1.0 reproduces o_t = S_t q_t           */
+    int32_t flags;       /* 0, or DN_QK_L2NORM                                            */
+    float l2norm_eps;    /* eps of the in-call normalisation (1e-6 is customary)          */
 } dn_shape;
 
 /*
@@ -110,8 +125,8 @@ typedef struct {
  *
  * Errors: DN_ERR_INVALID_ARG (null required pointer, non-positive sizes, Hv % Hqk,
  * B != 1 or num_seqs < 1 with cu_seqlens, num_seqs != B without, misaligned
- * pointer), DN_ERR_UNSUPPORTED (Dk, Dv, chunk_size or dtype not supported),
- * DN_ERR_WORKSPACE, DN_ERR_HIP.  T == 0 is valid: final_state = initial_state.
+ * pointer, unknown flags, negative or non-finite l2norm_eps), DN_ERR_UNSUPPORTED
+ * (Dk, Dv, chunk_size or dtype not supported), DN_ERR_WORKSPACE, DN_ERR_HIP.  T == 0 is valid: final_state = initial_state.
  */
 dn_status dn_chunk_fwd(const dn_shape* shape,
                        const void* q, const void* k, const void* v,

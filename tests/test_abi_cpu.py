@@ -60,6 +60,10 @@ def _chunk(shape, ptr=16, **over):
     (dict(Dv=256), dn.DN_ERR_UNSUPPORTED),
     (dict(chunk_size=128), dn.DN_ERR_UNSUPPORTED),
     (dict(dtype=7), dn.DN_ERR_UNSUPPORTED),
+    (dict(flags=2), dn.DN_ERR_INVALID_ARG),             # unknown flag bit
+    (dict(flags=1, l2norm_eps=-1e-6), dn.DN_ERR_INVALID_ARG),
+    (dict(flags=1, l2norm_eps=float("inf")), dn.DN_ERR_INVALID_ARG),
+    (dict(flags=1, l2norm_eps=float("nan")), dn.DN_ERR_INVALID_ARG),
 ])
 def test_chunk_fwd_rejects_bad_shapes(bad, code):
     assert _chunk(_shape(**bad)) == code
@@ -81,6 +85,10 @@ def test_decode_rejects_bad_shapes():
     assert lib.dn_decode_step(ctypes.byref(s), p, p, p, p, None, p, p, None) == dn.DN_ERR_UNSUPPORTED
     s = _shape(B=4, T=1, num_seqs=4)
     assert lib.dn_decode_step(ctypes.byref(s), p, None, p, p, None, p, p, None) == dn.DN_ERR_INVALID_ARG
+    s = _shape(B=4, T=1, num_seqs=4, flags=4)
+    assert lib.dn_decode_step(ctypes.byref(s), p, p, p, p, None, p, p, None) == dn.DN_ERR_INVALID_ARG
+    s = _shape(B=4, T=1, num_seqs=4, flags=1, l2norm_eps=-1.0)
+    assert lib.dn_decode_step(ctypes.byref(s), p, p, p, p, None, p, p, None) == dn.DN_ERR_INVALID_ARG
 
 
 def test_workspace_query_is_host_only():
