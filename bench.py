@@ -65,17 +65,20 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic():
+def load_traffic(key=None):
     """HBM bytes per call measured with rocprofv3 counters (profiles/traffic.json),
-    used only while the kernel sources are the ones the counters were taken on."""
+    used only while the kernel sources are the ones the counters were taken on: the
+    (prefill, decode) pair, or the entry ``key``."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None, None
+        t = {}
     if t.get("source_digest") != source_digest():
-        return None, None
+        t = {}
+    if key is not None:
+        return t.get(key)
     return t.get("prefill_bytes_per_call"), t.get("decode_bytes_per_call")
 
 
@@ -201,6 +204,15 @@ def main():
     alg_b = prefill_bytes(B, T, Hqk, Hv, D, gated=False, N=B, init=False)
     alg_f = prefill_flops(B, T, Hqk, Hv, D, PREFILL["C"])
     traffic_p, traffic_d = load_traffic()
+    # matrix-core work and busy fraction per call from rocprofv3's SQ counters (profiles/),
+    # used only while the kernel sources are the ones they were taken on
+    mfma_counted = None
+    mc = load_traffic("prefill_mfma")
+    if mc:
+        mfma_counted = {"counted_flops_per_call": mc["counted_flops_per_call"],
+                        "counted_frac_of_bf16_peak": mc["counted_flops_per_call"] / (call_us * 1e-6)
+                        / 1e12 / BF16_PEAK_TFLOPS,
+                        "mfma_busy_util": mc["mfma_util"]}
     achieved = alg_b / (call_us * 1e-6) / 1e9
 
     # ------------------------------------------------------------------- decode
@@ -263,6 +275,7 @@ def main():
         "prefill": {"kernel": "fused_kernel<false, true>", "us_per_call": norm_us,
                     "tokens_per_s": tokens / (norm_us * 1e-6),
                     "hbm_frac": alg_b / (norm_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "traffic": load_traffic("prefill_qk_l2norm_bytes_per_call"),
                     "vs_prenormalised_call": norm_us / call_us},
         "decode": {"kernel": "decode_kernel (normalising)", "us_per_step": dec_norm_us,
                    "hbm_frac": dec_b / (dec_norm_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
@@ -325,7 +338,8 @@ def main():
         "timing": {"loop": "eager" if args.eager else "hip_graph_replay",
                    "ms_per_step_eager": wall_eager * 1e3 / args.steps},
         "mfma": {"algorithmic_flops": alg_f, "tflops": alg_f / (call_us * 1e-6) / 1e12,
-                 "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+                 "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                 "counters": mfma_counted},
         "decode": {"workload": "gated decode step, 256 sequences x 32 heads, d=128, bf16, fp32 state "
                                "in place", "us_per_step": dec_us, "state_GBps": dec_gbs,
                    "roofline": {"bound": "hbm", "achieved": dec_b / (dec_us * 1e-6) / 1e9,

@@ -71,3 +71,5 @@ def test_traffic_is_used_only_for_the_sources_it_was_measured_on(tmp_path, monke
     assert bench.load_traffic() == (None, None)
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
     assert bench.load_traffic() == (1, 2)
+    assert bench.load_traffic("prefill_bytes_per_call") == 1
+    assert bench.load_traffic("no_such_entry") is None
