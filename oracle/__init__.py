@@ -65,7 +65,7 @@ def _load(lib_path: Optional[str] = None):
         d = ctypes.POINTER(ctypes.c_double)
         i64 = ctypes.c_int64
         lib.dn_oracle_fwd.argtypes = [i64, ctypes.POINTER(i64), i64, i64, i64, i64,
-                                      d, d, d, d, d, d, ctypes.c_double, ctypes.c_int,
+                                      d, d, d, d, d, i64, d, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_double, d, d, ctypes.c_int]
         lib.dn_oracle_fwd.restype = ctypes.c_int
         lib.dn_oracle_max_threads.argtypes = []
@@ -96,7 +96,8 @@ def recurrent(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
     With ``qk_l2norm`` every q_t and k_t is first replaced by
     ``x / sqrt(sum(x**2) + eps)`` (normalisation inside the rule).
 
-    q, k: ``[B, T, Hqk, Dk]``; v: ``[B, T, Hv, Dv]``; beta, g: ``[B, T, Hv]``;
+    q, k: ``[B, T, Hqk, Dk]``; v: ``[B, T, Hv, Dv]``; beta: ``[B, T, Hv]``; g: ``[B, T, Hv]``
+    (one log decay per head) or ``[B, T, Hv, Dk]`` (per key channel);
     init: ``[N, Hv, Dk, Dv]`` (key-major state) or None.  With ``cu_seqlens``
     (``[N + 1]``) the B*T tokens are N packed sequences, else each of the B rows is one
     sequence.  Returns ``(o [B, T, Hv, Dv], final [N, Hv, Dk, Dv])`` in fp64.
@@ -113,10 +114,13 @@ def recurrent(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
     Hv, Dv = v.shape[2], v.shape[3]
     if beta.shape != (B, T, Hv):
         raise ValueError("beta must be [B, T, Hv]")
+    gdim = 1
     if g is not None:
         g = np.ascontiguousarray(g, dtype=np.float64)
-        if g.shape != (B, T, Hv):
-            raise ValueError("g must be [B, T, Hv]")
+        if g.shape == (B, T, Hv, Dk):
+            gdim = Dk
+        elif g.shape != (B, T, Hv):
+            raise ValueError("g must be [B, T, Hv] or [B, T, Hv, Dk]")
     if cu_seqlens is None:
         cu = np.arange(B + 1, dtype=np.int64) * T
     else:
@@ -132,7 +136,7 @@ def recurrent(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
     final = np.zeros((N, Hv, Dk, Dv), dtype=np.float64)
     rc = lib.dn_oracle_fwd(N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                            Hqk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
-                           _ptr(init), float(scale), int(bool(qk_l2norm)), float(eps),
+                           gdim, _ptr(init), float(scale), int(bool(qk_l2norm)), float(eps),
                            _ptr(o), _ptr(final), int(nthreads))
     if rc != 0:
         raise ValueError(f"dn_oracle_fwd rejected its arguments (rc={rc})")

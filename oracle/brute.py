@@ -6,7 +6,8 @@ are written from different statements of the same update than ``dn_oracle.c`` is
 so agreement between them pins the oracle.
 
 S is the pages' value-by-key state (``S k = v``), shape ``[Dv, Dk]``.  Every
-function takes q, k ``[T, Dk]``, v ``[T, Dv]``, beta ``[T]``, g ``[T]`` or None,
+function takes q, k ``[T, Dk]``, v ``[T, Dv]``, beta ``[T]``, g ``[T]`` (or ``[T, Dk]``, per
+key channel, for :func:`product_form`) or None,
 S0 ``[Dv, Dk]`` or None, and returns ``(o [T, Dv], S_T [Dv, Dk])``.
 """
 from __future__ import annotations
@@ -36,11 +37,22 @@ def product_form(q, k, v, beta, g=None, S0=None, scale: float = 1.0
     I = np.eye(Dk)
     o = np.zeros((T, v.shape[1]))
     for t in range(T):
-        a = 1.0 if g is None else np.exp(g[t])
         kt = k[t][:, None]
-        S = (a * S) @ (I - beta[t] * (kt @ kt.T)) + beta[t] * (v[t][:, None] @ kt.T)
+        S = _decayed(S, g, t) @ (I - beta[t] * (kt @ kt.T)) + beta[t] * (v[t][:, None] @ kt.T)
         o[t] = scale * (S @ q[t])
     return o, S
+
+
+def _decayed(S, g, t):
+    """The state after token t's gate: exp(g_t) S for one gate per head, or
+    S diag(exp(g_t)) for a gate per key channel (g[t] a vector of length Dk; the nnterp
+    page's ChannelGates, read as the key channels of S keeping exp(g_t[i]) each)."""
+    if g is None:
+        return S
+    a = np.exp(np.asarray(g[t], dtype=np.float64))
+    if a.ndim == 0:
+        return a * S
+    return S @ np.diag(a)
 
 
 def retrieve_interpolate_form(q, k, v, beta, g=None, S0=None, scale: float = 1.0

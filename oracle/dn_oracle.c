@@ -20,6 +20,10 @@
  *       S'_t = exp(g_t) S_{t-1},   S_t = S'_t - beta_t (S'_t k_t - v_t) k_t^T,
  *       o_t  = scale * S_t q_t      (read after the write; scale = 1 on the pages).
  *   A missing gate (g == NULL) is the plain rule (exp(0) = 1).
+ *   Channel gates (gdim == Dk): the nnterp page types a gate per key channel,
+ *   [batch, seq, heads, key_dim] ("ChannelGates", the KDA variant).  Read as the same
+ *   gate taken per key channel: S'_t = S_{t-1} diag(exp(g_t)), i.e. column i of S (the
+ *   state's weights on key channel i) keeps the fraction exp(g_t[i]).
  *   Optional in-rule normalisation (qk_l2norm != 0): the frankenstein class text
  *   L2-normalises queries and keys before the rule, and the mutichung DeltaNet block
  *   flowchart puts an "L2 Norm" on q and k right before the "Delta Rule" box; the
@@ -35,7 +39,7 @@
  *   q, k   [Ttot, Hqk, Dk]      token-major; a batch of B rows of T tokens is the
  *   v      [Ttot, Hv,  Dv]      same memory as Ttot = B*T packed tokens with
  *   beta   [Ttot, Hv]           cu = {0, T, 2T, ...}
- *   g      [Ttot, Hv] or NULL
+ *   g      [Ttot, Hv, gdim] or NULL; gdim = 1 (one gate per head) or Dk (per key channel)
  *   cu     [N + 1] token offsets of the N sequences (cu[0] = 0, non-decreasing)
  *   init   [N, Hv, Dk, Dv] or NULL.  Stored key-major: init[n,h,i,j] = S[j][i]
  *          (the nnterp page's "key_dim by value_dim matrix per head").
@@ -58,13 +62,15 @@
 int dn_oracle_fwd(int64_t N, const int64_t *cu,
                   int64_t Hqk, int64_t Hv, int64_t Dk, int64_t Dv,
                   const double *q, const double *k, const double *v,
-                  const double *beta, const double *g, const double *init,
+                  const double *beta, const double *g, int64_t gdim, const double *init,
                   double scale, int qk_l2norm, double eps,
                   double *o, double *final_state, int nthreads)
 {
     if (N < 0 || Hqk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hqk != 0)
         return -1;
     if (qk_l2norm && !(eps >= 0.0))
+        return -1;
+    if (g && gdim != 1 && gdim != Dk)
         return -1;
     if (!cu || (N > 0 && (!q || !k || !v || !beta || !o)))
         return -1;
@@ -124,10 +130,18 @@ int dn_oracle_fwd(int64_t N, const int64_t *cu,
             }
             const double bt = beta[t * Hv + h];
             /* decay first: S <- exp(g_t) S */
-            if (g) {
+            if (g && gdim == 1) {
                 const double a = exp(g[t * Hv + h]);
                 for (int64_t e = 0; e < Dv * Dk; ++e)
                     S[e] *= a;
+            }
+            /* channel gates: S <- S diag(exp(g_t)), key channel i keeps exp(g_t[i]) */
+            if (g && gdim != 1) {
+                for (int64_t i = 0; i < Dk; ++i) {
+                    const double a = exp(g[(t * Hv + h) * Dk + i]);
+                    for (int64_t j = 0; j < Dv; ++j)
+                        S[j * Dk + i] *= a;
+                }
             }
             /* prediction error S k_t - v_t */
             for (int64_t j = 0; j < Dv; ++j) {

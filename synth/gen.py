@@ -16,7 +16,7 @@ preconditions the pages put on those inputs are applied here:
 * beta is a sigmoid output in (0, 1), or twice that, in (0, 2), for the
   negative-eigenvalue variant (nnterp ``betas``);
 * the log decay g is non-positive (nnterp ``decays``), drawn as
-  ``-c * softplus(z)``.
+  ``-c * softplus(z)``, one per head or one per key channel (``ChannelGates``).
 
 Draw order per case, from one ``numpy.random.default_rng(seed)``: q, k, v, z_beta,
 z_g, initial state, then the cut points of a packed (varlen) batch.  Normal draws
@@ -68,7 +68,7 @@ class DeltaInputs:
     """One delta-rule call's inputs, as host arrays.
 
     Layout is token-major: q, k ``[B, T, Hqk, Dk]``, v ``[B, T, Hv, Dv]``, beta and g
-    ``[B, T, Hv]`` fp32.  A packed batch has ``B == 1``, ``T`` = total tokens and
+    ``[B, T, Hv]`` fp32 (g ``[B, T, Hv, Dk]`` for gates per key channel).  A packed batch has ``B == 1``, ``T`` = total tokens and
     ``cu_seqlens`` (int32, ``[N + 1]``).  ``init`` is ``[N, Hv, Dk, Dv]`` fp32, the
     state stored key-major (the transpose of the value-by-key map S), or None for a
     fresh prompt.  q/k/v are fp32 when ``dtype == "f32"`` and bf16 bit patterns
@@ -140,7 +140,8 @@ def make_case(*, B: int = 1, T: int = 64, Hqk: int = 2, Hv: Optional[int] = None
               beta_scale: float = 1.0, g_scale: Optional[float] = None,
               init_std: Optional[float] = None, seqlens: Optional[Sequence[int]] = None,
               num_seqs_cut: Optional[int] = None, chunk: int = 64, seed: int = 0,
-              name: str = "case", decode: bool = False, qk_raw: bool = False) -> DeltaInputs:
+              name: str = "case", decode: bool = False, qk_raw: bool = False,
+              g_per_key: bool = False) -> DeltaInputs:
     """Draw one case.
 
     ``beta = beta_scale * sigmoid(z)``; ``g = -g_scale * softplus(z)`` or no decay when
@@ -148,7 +149,8 @@ def make_case(*, B: int = 1, T: int = 64, Hqk: int = 2, Hv: Optional[int] = None
     A packed batch is asked for either with explicit ``seqlens`` or with
     ``num_seqs_cut`` = N, which cuts T at N - 1 distinct points drawn uniformly
     without replacement from {1, ..., T - 1}.  With ``qk_raw`` q and k are the raw
-    N(0, 1) draws (norm about sqrt(Dk)), not normalised.
+    N(0, 1) draws (norm about sqrt(Dk)), not normalised.  With ``g_per_key`` the log decay
+    is drawn per key channel, ``[B, T, Hv, Dk]`` (the nnterp page's ChannelGates).
     """
     Hv = Hqk if Hv is None else Hv
     Dv = Dk if Dv is None else Dv
@@ -170,7 +172,8 @@ def make_case(*, B: int = 1, T: int = 64, Hqk: int = 2, Hv: Optional[int] = None
     beta = (beta_scale * _sigmoid(rng.standard_normal((B, T, Hv)))).astype(np.float32)
     g = None
     if g_scale is not None:
-        g = (-g_scale * _softplus(rng.standard_normal((B, T, Hv)))).astype(np.float32)
+        gshape = (B, T, Hv, Dk) if g_per_key else (B, T, Hv)
+        g = (-g_scale * _softplus(rng.standard_normal(gshape))).astype(np.float32)
     cu = None
     if seqlens is not None:
         cu = np.concatenate([[0], np.cumsum(np.asarray(seqlens, dtype=np.int64))])

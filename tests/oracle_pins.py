@@ -365,8 +365,84 @@ def pin_l2norm_scale_free(run):
     _close(f3, np.exp(g[0]) * M0, 1e-15, "zero key: state only decayed")
 
 
+# ------------------------------------------------------- gates per key channel
+# [P3] ChannelGates [batch, seq, heads, key_dim] (the KDA variant).  Reading: key channel i
+# of the state keeps exp(g_t[i]): S'_t = S_{t-1} diag(exp(g_t)).
+
+def pin_channel_gates_product_form(run):
+    """Channel gates against the explicit-matrix product form with diag(exp(g_t)), d_k != d_v,
+    beta in (0, 2), an initial state."""
+    rng = np.random.default_rng(41)
+    T, Dk, Dv = 9, 5, 3
+    q, k, v, beta, _, M0 = _rand_seq(rng, T, Dk, Dv, False, True, beta_hi=2.0)
+    g = -0.5 * rng.uniform(0, 1, (T, Dk))
+    o, fin = run(q.reshape(1, T, 1, Dk), k.reshape(1, T, 1, Dk), v.reshape(1, T, 1, Dv),
+                 beta.reshape(1, T, 1), g.reshape(1, T, 1, Dk), M0.reshape(1, 1, Dk, Dv))
+    ob, Sb = brute.product_form(q, k, v, beta, g, M0.T)
+    _close(o.reshape(T, Dv), ob, 1e-13, "channel gates: o")
+    _close(fin.reshape(Dk, Dv), Sb.T, 1e-13, "channel gates: state")
+
+
+def pin_channel_gates_uniform_are_the_head_gate(run):
+    """The same gate on every key channel is the one-gate-per-head rule."""
+    rng = np.random.default_rng(42)
+    T, Dk, Dv = 12, 4, 6
+    q, k, v, beta, g, M0 = _rand_seq(rng, T, Dk, Dv, True, True)
+    gc = np.repeat(g[:, None], Dk, axis=1)
+    shp = lambda x, *d: x.reshape(1, T, 1, *d)
+    o1, f1 = run(shp(q, Dk), shp(k, Dk), shp(v, Dv), beta.reshape(1, T, 1), gc.reshape(1, T, 1, Dk),
+                 M0.reshape(1, 1, Dk, Dv))
+    o2, f2 = _one(run, q, k, v, beta, g, M0)
+    _close(o1.reshape(T, Dv), o2, 1e-14, "uniform channel gates: o")
+    _close(f1.reshape(Dk, Dv), f2, 1e-14, "uniform channel gates: state")
+
+
+def pin_channel_gates_decay_only(run):
+    """beta = 0: key channel i of the state is scaled by exp(sum_s g_s[i]) and nothing else
+    happens (closed form, d_k != d_v); the read is S_t q_t."""
+    rng = np.random.default_rng(43)
+    T, Dk, Dv = 7, 3, 5
+    q, k, v, _, _, M0 = _rand_seq(rng, T, Dk, Dv, False, True)
+    g = -rng.uniform(0, 0.7, (T, Dk))
+    o, fin = run(q.reshape(1, T, 1, Dk), k.reshape(1, T, 1, Dk), v.reshape(1, T, 1, Dv),
+                 np.zeros((1, T, 1)), g.reshape(1, T, 1, Dk), M0.reshape(1, 1, Dk, Dv))
+    cum = np.cumsum(g, axis=0)
+    want_o = np.stack([(np.exp(cum[t])[:, None] * M0).T @ q[t] for t in range(T)])
+    _close(fin.reshape(Dk, Dv), np.exp(cum[-1])[:, None] * M0, 1e-15, "decay-only state")
+    _close(o.reshape(T, Dv), want_o, 1e-15, "decay-only read")
+
+
+def pin_channel_gates_heads_and_packing(run):
+    """Channel gates [1, T, Hv, Dk] over GQA heads and packed sequences: each (sequence,
+    value head) unit equals the product form with its own gate rows."""
+    rng = np.random.default_rng(44)
+    Hqk, Hv, Dk, Dv = 1, 3, 4, 2
+    lens = [6, 0, 9]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = _unit(rng.standard_normal((1, T, Hqk, Dk)))
+    k = _unit(rng.standard_normal((1, T, Hqk, Dk)))
+    v = rng.standard_normal((1, T, Hv, Dv))
+    beta = rng.uniform(0, 2, (1, T, Hv))
+    g = -0.4 * rng.uniform(0, 1, (1, T, Hv, Dk))
+    M0 = rng.standard_normal((len(lens), Hv, Dk, Dv))
+    o, fin = run(q, k, v, beta, g, M0, cu_seqlens=cu)
+    for n in range(len(lens)):
+        s_, e_ = cu[n], cu[n + 1]
+        for h in range(Hv):
+            if e_ == s_:
+                _close(fin[n, h], M0[n, h], 0, "empty sequence keeps its state")
+                continue
+            ob, Sb = brute.product_form(q[0, s_:e_, 0], k[0, s_:e_, 0], v[0, s_:e_, h],
+                                        beta[0, s_:e_, h], g[0, s_:e_, h], M0[n, h].T)
+            _close(o[0, s_:e_, h], ob, 1e-12, f"channel gates seq {n} head {h}: o")
+            _close(fin[n, h], Sb.T, 1e-12, f"channel gates seq {n} head {h}: state")
+
+
 ALL_PINS = [pin_hand_worked, pin_product_form, pin_retrieve_interpolate, pin_beta_zero,
             pin_exact_recall, pin_one_token, pin_gate_order, pin_contraction, pin_linearity,
             pin_sgd_step, pin_gate_zero_is_plain, pin_scale, pin_heads_and_packing,
             pin_batch_rows, pin_l2norm_is_library_normalise, pin_l2norm_eps_one_token,
-            pin_l2norm_scale_free]
+            pin_l2norm_scale_free, pin_channel_gates_product_form,
+            pin_channel_gates_uniform_are_the_head_gate, pin_channel_gates_decay_only,
+            pin_channel_gates_heads_and_packing]

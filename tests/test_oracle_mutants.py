@@ -22,10 +22,18 @@ READ = """            /* o_t = scale * S_t q_t */
             }
 """
 DECAY = """            /* decay first: S <- exp(g_t) S */
-            if (g) {
+            if (g && gdim == 1) {
                 const double a = exp(g[t * Hv + h]);
                 for (int64_t e = 0; e < Dv * Dk; ++e)
                     S[e] *= a;
+            }
+            /* channel gates: S <- S diag(exp(g_t)), key channel i keeps exp(g_t[i]) */
+            if (g && gdim != 1) {
+                for (int64_t i = 0; i < Dk; ++i) {
+                    const double a = exp(g[(t * Hv + h) * Dk + i]);
+                    for (int64_t j = 0; j < Dv; ++j)
+                        S[j * Dk + i] *= a;
+                }
             }
 """
 PRED = "            /* prediction error S k_t - v_t */\n"
@@ -68,6 +76,14 @@ MUTANTS = {
     "norm_keys_only": _sub("iq = 1.0 / sqrt(sq + eps)", "iq = 1.0"),
     "norm_key_by_query": _sub("ik = 1.0 / sqrt(sk + eps)", "ik = 1.0 / sqrt(sq + eps)"),
     "norm_skipped": _sub("if (qk_l2norm) {", "if (0) {"),
+    "channel_gate_reversed": _sub("const double a = exp(g[(t * Hv + h) * Dk + i]);",
+                                  "const double a = exp(g[(t * Hv + h) * Dk + (Dk - 1 - i)]);"),
+    "channel_gate_first_channel": _sub("const double a = exp(g[(t * Hv + h) * Dk + i]);",
+                                       "const double a = exp(g[(t * Hv + h) * Dk]);"),
+    "channel_gate_of_qk_head": _sub("const double a = exp(g[(t * Hv + h) * Dk + i]);",
+                                    "const double a = exp(g[(t * Hv + hq) * Dk + i]);"),
+    "channel_gate_sign": _sub("const double a = exp(g[(t * Hv + h) * Dk + i]);",
+                              "const double a = exp(-g[(t * Hv + h) * Dk + i]);"),
     "skips_first_token": _sub("for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {",
                               "for (int64_t t = cu[n] + 1; t < cu[n + 1]; ++t) {"),
 }
