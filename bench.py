@@ -281,6 +281,46 @@ def main():
                    "hbm_frac": dec_b / (dec_norm_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
     }
 
+    # ------------- gates per key channel (ChannelGates): decode and layer prefill
+    yc = make_case(B=DECODE["N"], T=1, Hqk=DECODE["H"], Dk=DECODE["D"], dtype="bf16", g_scale=0.1,
+                   init_std=0.02, seed=0, decode=True, g_per_key=True)
+    cg = to_dev(yc.g)[:, 0].contiguous()
+    for i in range(3):
+        dn.decode_step(dq, dk, dv, db, cg, dstate[i % 2], out=dout)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.decode_reps):
+        dn.decode_step(dq, dk, dv, db, cg, dstate[i % 2], out=dout)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_chg_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
+    dec_chg_b = dec_b + y.B * y.Hv * y.Dk * 4
+    xc = make_case(B=B, T=T, Hqk=Hqk, Dk=D, dtype="bf16", seed=0, g_scale=0.1, g_per_key=True)
+    cq, ck, cv, cb, cgp = (to_dev(a) for a in (xc.q, xc.k, xc.v, xc.beta, xc.g))
+    co = torch.empty((B, T, Hv, D), dtype=torch.bfloat16, device=dev)
+    cs = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    dn.chunk_fwd(cq, ck, cv, cb, cgp, None, out=co, final_state=cs)
+    torch.cuda.synchronize()
+    creps = 3
+    ev0.record(stream)
+    for _ in range(creps):
+        dn.chunk_fwd(cq, ck, cv, cb, cgp, None, out=co, final_state=cs)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    pre_chg_us = ev0.elapsed_time(ev1) * 1e3 / creps
+    pre_chg_b = alg_b + B * T * Hv * D * 4
+    channel_gates = {
+        "what": "log decay per key channel (DN_GATE_PER_KEY, g = -0.1 softplus(N(0,1)) per channel)",
+        "decode": {"workload": "256 sequences x 32 heads d128 bf16, state in place",
+                   "kernel": "decode_kernel (channel gates)", "us_per_step": dec_chg_us,
+                   "hbm_frac": dec_chg_b / (dec_chg_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        "prefill": {"workload": "B4 H16 T2048 d128 bf16, final state returned",
+                    "kernel": "prefill_channel_gate_kernel (vector ALU, 32-token chunks)",
+                    "us_per_call": pre_chg_us, "tokens_per_s": tokens / (pre_chg_us * 1e-6),
+                    "hbm_frac": pre_chg_b / (pre_chg_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+    }
+    del cq, ck, cv, cb, cgp, co, cs
+
     # ------------------------------------ the other two full-size prefill workloads
     # (context beside the headline: each timed the same way, with HIP events around a loop
     # of back-to-back calls on the launching stream)
@@ -349,6 +389,7 @@ def main():
                                 "algorithmic_bytes": dec_b}},
         "prefill_other_workloads": other,
         "in_rule_qk_l2norm": in_rule_norm,
+        "channel_gates": channel_gates,
         "cpu_baseline": None,
     }
     if not args.no_cpu:

@@ -47,10 +47,12 @@ class _Shape(ctypes.Structure):
 
 
 DN_QK_L2NORM = 1
+DN_GATE_PER_KEY = 2
 
 
-def _norm_flags(qk_l2norm: bool, l2norm_eps: float):
-    return (DN_QK_L2NORM if qk_l2norm else 0), float(l2norm_eps)
+def _flags(qk_l2norm: bool, l2norm_eps: float, gate_per_key: bool):
+    f = (DN_QK_L2NORM if qk_l2norm else 0) | (DN_GATE_PER_KEY if gate_per_key else 0)
+    return f, float(l2norm_eps)
 
 
 _lib = None
@@ -140,7 +142,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     """Delta rule over whole sequences (prefill), chunkwise-parallel form.
 
     q, k ``[B, T, Hqk, Dk]``, v ``[B, T, Hv, Dv]`` (float32 or bfloat16, one dtype);
-    beta, g ``[B, T, Hv]`` float32 (g None: plain rule); initial_state
+    beta, g ``[B, T, Hv]`` float32 (g None: plain rule; g ``[B, T, Hv, Dk]``: one log decay
+    per key channel); initial_state
     ``[N, Hv, Dk, Dv]`` float32 or None (zero state); cu_seqlens int32 ``[N + 1]``
     packs N sequences along T (B == 1).  Returns ``(o [B, T, Hv, Dv], final_state or
     None)``.  ``final_state`` may be passed (and may be ``initial_state``, to update
@@ -162,8 +165,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     if tuple(v.shape[:2]) != (B, T):
         raise ValueError("v must be [B, T, Hv, Dv] with the batch and length of q")
     _dev(beta, "beta", torch.float32, (B, T, Hv))
+    per_key = g is not None and g.dim() == 4
     if g is not None:
-        _dev(g, "g", torch.float32, (B, T, Hv))
+        _dev(g, "g", torch.float32, (B, T, Hv, Dk) if per_key else (B, T, Hv))
     if cu_seqlens is not None:
         _dev(cu_seqlens, "cu_seqlens", torch.int32)
         if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
@@ -189,7 +193,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     elif final_state is not None:
         _dev(final_state, "final_state", torch.float32, (N, Hv, Dk, Dv))
     shape = _Shape(B, T, N, Hqk, Hv, Dk, Dv, _dtype_code(q), chunk_size, float(scale),
-                   *_norm_flags(qk_l2norm, l2norm_eps))
+                   *_flags(qk_l2norm, l2norm_eps, per_key))
     need = int(lib.dn_chunk_fwd_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
@@ -213,7 +217,8 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
     """One token per sequence against the cached ``state`` (updated in place).
 
     q, k ``[N, Hqk, Dk]``, v ``[N, Hv, Dv]``; beta, g ``[N, Hv]`` float32 (g may be
-    None); state ``[N, Hv, Dk, Dv]`` float32.  Returns o ``[N, Hv, Dv]``.
+    None, or ``[N, Hv, Dk]``: one log decay per key channel); state ``[N, Hv, Dk, Dv]``
+    float32.  Returns o ``[N, Hv, Dv]``.
     ``qk_l2norm`` normalises q and k inside the call, as in :func:`chunk_fwd`.
     """
     lib = load_library()
@@ -227,15 +232,16 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
         raise ValueError("v must be [N, Hv, Dv]")
     Hv, Dv = v.shape[1], v.shape[2]
     _dev(beta, "beta", torch.float32, (N, Hv))
+    per_key = g is not None and g.dim() == 3
     if g is not None:
-        _dev(g, "g", torch.float32, (N, Hv))
+        _dev(g, "g", torch.float32, (N, Hv, Dk) if per_key else (N, Hv))
     _dev(state, "state", torch.float32, (N, Hv, Dk, Dv))
     if out is None:
         out = torch.empty((N, Hv, Dv), dtype=q.dtype, device=q.device)
     else:
         _dev(out, "out", q.dtype, (N, Hv, Dv))
     shape = _Shape(N, 1, N, Hqk, Hv, Dk, Dv, _dtype_code(q), 0, float(scale),
-                   *_norm_flags(qk_l2norm, l2norm_eps))
+                   *_flags(qk_l2norm, l2norm_eps, per_key))
     with torch.cuda.device(q.device):
         rc = lib.dn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                 _ptr(g), _ptr(state), _ptr(out), _stream(q.device))

@@ -20,7 +20,7 @@ dn_status check_common(const dn_shape* s) {
     if (s->Hv % s->Hqk != 0) return DN_ERR_INVALID_ARG;
     if (s->dtype != DN_F32 && s->dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
     if (!dim_ok(s->Dk) || !dim_ok(s->Dv)) return DN_ERR_UNSUPPORTED;
-    if (s->flags & ~DN_QK_L2NORM) return DN_ERR_INVALID_ARG;
+    if (s->flags & ~(DN_QK_L2NORM | DN_GATE_PER_KEY)) return DN_ERR_INVALID_ARG;
     if ((s->flags & DN_QK_L2NORM) && !(s->l2norm_eps >= 0.f && s->l2norm_eps <= 3.0e38f))
         return DN_ERR_INVALID_ARG;
     return DN_OK;
@@ -59,6 +59,7 @@ static dn_status prefill_shape(const dn_shape* s, bool packed, dn::PrefillArgs& 
     a.Dk = s->Dk; a.Dv = s->Dv; a.C = C; a.bf16 = s->dtype == DN_BF16; a.scale = s->scale;
     a.qk_norm = (s->flags & DN_QK_L2NORM) != 0;
     a.eps = s->l2norm_eps;
+    a.g_per_key = (s->flags & DN_GATE_PER_KEY) != 0;
     return DN_OK;
 }
 
@@ -80,6 +81,7 @@ dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const vo
     if (st != DN_OK) return st;
     const long tokens = (long)s->B * s->T;
     if (tokens > 0 && (!q || !k || !v || !beta || !o)) return DN_ERR_INVALID_ARG;
+    if (a.g_per_key && !g) return DN_ERR_INVALID_ARG;
     const void* ptrs[] = {q, k, v, h0, hT, o, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
@@ -116,6 +118,8 @@ dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const 
     a.bf16 = s->dtype == DN_BF16; a.scale = s->scale;
     a.qk_norm = (s->flags & DN_QK_L2NORM) != 0;
     a.eps = s->l2norm_eps;
+    a.g_per_key = (s->flags & DN_GATE_PER_KEY) != 0;
+    if (a.g_per_key && !g) return DN_ERR_INVALID_ARG;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.state = state; a.o = o;
     return dn::launch_decode(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }

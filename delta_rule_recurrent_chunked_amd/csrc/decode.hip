@@ -9,6 +9,8 @@
 //                                            Rule" section of the mutichung DeltaNet page)
 //   o      = scale (a r_q + (k.q) delta)    (= scale S_t q with S_t = S' + delta k^T)
 //   M     <- a M + k delta^T
+// With gates per key channel (CHG; the nnterp page's ChannelGates) row i of M decays by
+// a_i = exp(g[i]): the reductions take a_i k_i and a_i q_i, and M <- diag(a) M + k delta^T.
 // With the in-rule normalisation (q, k -> x / sqrt(|x|^2 + eps)) the norms come out of
 // the same reductions: r_k, r_q and k.q take the factors 1/|k|, 1/|q|, and the update
 // adds k (delta / |k|)^T.
@@ -57,7 +59,7 @@ __device__ __forceinline__ void ld_vec(const T* p, float (&out)[N]) {
     }
 }
 
-template <typename T, int DK, int DV, int CW, bool VEC>
+template <typename T, int DK, int DV, int CW, bool VEC, bool CHG>
 __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(DecodeArgs a) {
     using S = DecodeShape<DK, CW>;
     constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
@@ -98,17 +100,23 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     }
     const long vo = (long)nh * DV + slice * CW + (tid < CW ? tid : 0);
     const float vval = ld_f32(static_cast<const T*>(a.v), vo);
-    const float alpha = a.g ? expf(a.g[nh]) : 1.0f;
+    const float alpha = (a.g && !CHG) ? expf(a.g[nh]) : 1.0f;
     const float beta = a.beta[nh];
+    float ar[RPT];   // channel gates: decay of each of this thread's rows
+    if (CHG) {
+#pragma unroll
+        for (int p = 0; p < RPT; ++p) ar[p] = expf(a.g[(long)nh * DK + row0 + p]);
+    }
 
     const bool nrm = a.qk_norm;
     float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
+        const float kd = CHG ? ar[p] * kr[p] : kr[p], qd = CHG ? ar[p] * qr[p] : qr[p];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            pk[c] += m[p][c] * kr[p];
-            pq[c] += m[p][c] * qr[p];
+            pk[c] += m[p][c] * kd;
+            pq[c] += m[p][c] * qd;
         }
         if (ct == 0) {
             kq += kr[p] * qr[p];
@@ -170,11 +178,12 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     const float d0 = dsh[ct * 4 + 0], d1 = dsh[ct * 4 + 1], d2 = dsh[ct * 4 + 2], d3 = dsh[ct * 4 + 3];
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
+        const float am = CHG ? ar[p] : alpha;
         f32x4v r;
-        r[0] = alpha * m[p][0] + kr[p] * d0;
-        r[1] = alpha * m[p][1] + kr[p] * d1;
-        r[2] = alpha * m[p][2] + kr[p] * d2;
-        r[3] = alpha * m[p][3] + kr[p] * d3;
+        r[0] = am * m[p][0] + kr[p] * d0;
+        r[1] = am * m[p][1] + kr[p] * d1;
+        r[2] = am * m[p][2] + kr[p] * d2;
+        r[3] = am * m[p][3] + kr[p] * d3;
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4v*>(Mp + (long)(row0 + p) * DV));
     }
 }
@@ -189,10 +198,14 @@ hipError_t launch_dims(const DecodeArgs& a, hipStream_t s) {
     // (sequence, head) start 16-byte aligned
     constexpr bool kVecShape = (S::RPT * sizeof(T)) % 16 == 0 && (DK * sizeof(T)) % 16 == 0;
     const bool aligned = ((reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k)) & 15) == 0;
-    if (kVecShape && aligned)
-        hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape>), dim3((unsigned)blocks), dim3(S::NT), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false>), dim3((unsigned)blocks), dim3(S::NT), 0, s, a);
+    const dim3 grid((unsigned)blocks), block(S::NT);
+    if (a.g_per_key) {
+        if (kVecShape && aligned) hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false, true>), grid, block, 0, s, a);
+    } else {
+        if (kVecShape && aligned) hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

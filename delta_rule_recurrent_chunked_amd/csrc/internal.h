@@ -14,6 +14,7 @@ struct PrefillArgs {
     float scale;
     int qk_norm;                    // 1: q, k -> x / sqrt(|x|^2 + eps) inside the rule
     float eps;
+    int g_per_key;                  // 1: g is [.., Hv, Dk], one log decay per key channel
     const void* q;
     const void* k;
     const void* v;
@@ -33,6 +34,7 @@ struct DecodeArgs {
     float scale;
     int qk_norm;                    // as in PrefillArgs
     float eps;
+    int g_per_key;
     const void* q;
     const void* k;
     const void* v;

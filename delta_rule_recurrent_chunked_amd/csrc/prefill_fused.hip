@@ -844,7 +844,7 @@ bool prefill_fused_supported(const PrefillArgs& a) {
     // buffer offsets are 32-bit: a sequence (plus the two chunks fetched past its end) must
     // span less than 2 GiB of q / k / v / o
     const long span = ((long)a.T + 2 * FC) * (a.Hqk > a.Hv ? a.Hqk : a.Hv) * FD * 2;
-    return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC && span < (1L << 31);
+    return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC && !a.g_per_key && span < (1L << 31);
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s) {

@@ -14,7 +14,10 @@
  *       S_t  = S'_t - beta_t (S'_t k_t - v_t) k_t^T
  *       o_t  = scale * S_t q_t                      (read after the write)
  *
- *   With g absent the decay factor is 1 (the plain delta rule).  beta may lie in
+ *   With g absent the decay factor is 1 (the plain delta rule).  With DN_GATE_PER_KEY
+ *   the gate is taken per key channel (the nnterp page's ChannelGates, [batch, seq,
+ *   heads, key_dim], the KDA variant): S'_t = S_{t-1} diag(exp(g_t)), key channel i of
+ *   the state keeping exp(g_t[i]).  beta may lie in
  *   (0, 1), or in (0, 2) for the negative-eigenvalue variant (nnterp "betas"); any
  *   real beta is computed as given.  q and k are L2-normalised before the rule (the
  *   frankenstein class text; the "L2 Norm" box right before the "Delta Rule" box of
@@ -77,10 +80,12 @@ typedef enum {
 
 /* dn_shape.flags bits */
 #define DN_QK_L2NORM 1       /* L2-normalise q_t and k_t inside the call (see above)        */
+#define DN_GATE_PER_KEY 2    /* g holds one log decay per key channel: [.., Hv, Dk]          */
 
 /* Sizes of one call.  Supported: Dk, Dv in {16, 32, 64, 128}; chunk_size in
  * {16, 32, 64} (0 selects 64).  beta, g and all states are fp32 regardless of dtype.
- * flags: 0 or DN_QK_L2NORM (other bits are an error); l2norm_eps >= 0 (finite) is read
+ * flags: any of DN_QK_L2NORM, DN_GATE_PER_KEY (other bits are an error; DN_GATE_PER_KEY
+ * needs g); l2norm_eps >= 0 (finite) is read
  * only with DN_QK_L2NORM.  With l2norm_eps == 0 a zero q or k vector normalises to
  * zero.  The bf16 Dk = Dv = 128 path folds the normalisation into per-token factors
  * and keeps A's 16x16 diagonal blocks in fp16: their entries are bounded by beta
@@ -97,7 +102,7 @@ typedef struct {
     int32_t dtype;       /* dn_dtype of q, k, v, o                                        */
     int32_t chunk_size;  /* tokens per chunk of the chunked form                          */
     float scale;         /* multiplies every read; 1.0 reproduces o_t = S_t q_t           */
-    int32_t flags;       /* 0, or DN_QK_L2NORM                                            */
+    int32_t flags;       /* 0, or DN_QK_L2NORM | DN_GATE_PER_KEY                          */
     float l2norm_eps;    /* eps of the in-call normalisation (1e-6 is customary)          */
 } dn_shape;
 
@@ -110,7 +115,9 @@ typedef struct {
  *   q, k           [B, T, Hqk, Dk]  dtype
  *   v              [B, T, Hv, Dv]   dtype
  *   beta           [B, T, Hv]       fp32 write strengths
- *   g              [B, T, Hv]       fp32 log decays, or NULL for the plain rule
+ *   g              [B, T, Hv]       fp32 log decays, or NULL for the plain rule;
+ *                  [B, T, Hv, Dk]   with DN_GATE_PER_KEY (never NULL then).  Channel
+ *                                   gates run on the vector-ALU path in 32-token chunks.
  *   initial_state  [N, Hv, Dk, Dv]  fp32 state each sequence starts from, or NULL
  *                                   for the zero state (a fresh prompt)
  *   final_state    [N, Hv, Dk, Dv]  fp32 state after each sequence's last token,
@@ -146,7 +153,8 @@ size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
  * step, where the sequence axis is 1 and state_input is the cached state).
  *
  *   shape->B = N sequences, shape->T must be 1, num_seqs = N, cu_seqlens unused;
- *   q, k   [N, Hqk, Dk] dtype;  v [N, Hv, Dv] dtype;  beta, g [N, Hv] fp32 (g may be NULL)
+ *   q, k   [N, Hqk, Dk] dtype;  v [N, Hv, Dv] dtype;  beta, g [N, Hv] fp32 (g may be NULL;
+ *          [N, Hv, Dk] with DN_GATE_PER_KEY)
  *   state  [N, Hv, Dk, Dv] fp32, read and overwritten with the new state
  *   o      [N, Hv, Dv] dtype
  *

@@ -60,7 +60,8 @@ def _chunk(shape, ptr=16, **over):
     (dict(Dv=256), dn.DN_ERR_UNSUPPORTED),
     (dict(chunk_size=128), dn.DN_ERR_UNSUPPORTED),
     (dict(dtype=7), dn.DN_ERR_UNSUPPORTED),
-    (dict(flags=2), dn.DN_ERR_INVALID_ARG),             # unknown flag bit
+    (dict(flags=4), dn.DN_ERR_INVALID_ARG),             # unknown flag bit
+    (dict(flags=2), dn.DN_ERR_INVALID_ARG),             # gates per key channel without g
     (dict(flags=1, l2norm_eps=-1e-6), dn.DN_ERR_INVALID_ARG),
     (dict(flags=1, l2norm_eps=float("inf")), dn.DN_ERR_INVALID_ARG),
     (dict(flags=1, l2norm_eps=float("nan")), dn.DN_ERR_INVALID_ARG),
