@@ -313,7 +313,9 @@ def main():
         "what": "log decay per key channel (DN_GATE_PER_KEY, g = -0.1 softplus(N(0,1)) per channel)",
         "decode": {"workload": "256 sequences x 32 heads d128 bf16, state in place",
                    "kernel": "decode_kernel (channel gates)", "us_per_step": dec_chg_us,
-                   "hbm_frac": dec_chg_b / (dec_chg_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+                   "hbm_frac": dec_chg_b / (dec_chg_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                   "algorithmic_bytes": dec_chg_b,
+                   "traffic": load_traffic("decode_channel_gates_bytes_per_call")},
         "prefill": {"workload": "B4 H16 T2048 d128 bf16, final state returned",
                     "kernel": "prefill_channel_gate_kernel (vector ALU, 32-token chunks)",
                     "us_per_call": pre_chg_us, "tokens_per_s": tokens / (pre_chg_us * 1e-6),

@@ -135,3 +135,32 @@ def test_channel_gates_prefill_equals_decode_steps():
     o_ref, s_ref = _oracle(x)
     _check(x, od, host(state), o_ref, s_ref)
     _check(x, host(o), host(s), o_ref, s_ref)
+
+
+def test_decode_channel_gates_full_size():
+    """The decode workload (256 sequences x 32 heads, d128 bf16, state ~ N(0, 0.02^2) in
+    place) with a log decay per key channel."""
+    _say("channel gates decode 256 x 32 heads")
+    x = make_case(B=256, T=1, Hqk=32, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02, seed=0,
+                  decode=True, name="decode_full_chg", g_per_key=True)
+    d = to_inputs(x)
+    state = d["init"].clone()
+    o = dn.decode_step(d["q"][:, 0], d["k"][:, 0], d["v"][:, 0], d["beta"][:, 0],
+                       d["g"][:, 0].contiguous(), state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o)[:, None], host(state), o_ref, s_ref)
+
+
+def test_prefill_channel_gates_packed_workload_sample():
+    """Packed sequences with initial states and beta in (0, 2), as the 32K-token packed
+    workload has them, at 4 sequences of 1,900 tokens in all (the vector-ALU path)."""
+    _say("channel gates packed sample")
+    x = make_case(B=1, Hqk=4, Hv=4, Dk=128, dtype="bf16", seqlens=[700, 1, 0, 1199],
+                  g_scale=0.05, init_std=0.02, beta_scale=2.0, seed=27, name="packed_chg",
+                  g_per_key=True)
+    d = to_inputs(x)
+    o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], cu_seqlens=d["cu"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o), host(s), o_ref, s_ref)

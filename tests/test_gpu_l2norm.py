@@ -136,3 +136,56 @@ def test_l2norm_prefill_equals_decode_steps():
     o_ref, s_ref = _oracle(x)
     _check(x, od, host(state), o_ref, s_ref)
     _check(x, host(o), host(s), o_ref, s_ref)
+
+
+def test_prefill_l2norm_gated_gqa_workload():
+    """The gated GQA workload (B2, 16 q/k heads -> 32 v heads, T8192, d128 bf16) handed raw
+    q and k: the gated matrix-core path with the normalisation folded in."""
+    _say("l2norm prefill gated GQA B2 T8192")
+    x = make_case(B=2, T=8192, Hqk=16, Hv=32, Dk=128, dtype="bf16", g_scale=0.1, seed=0,
+                  name="gated_gqa_raw_qk", qk_raw=True)
+    d = to_inputs(x)
+    o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], None, qk_l2norm=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o), host(s), o_ref, s_ref)
+
+
+def test_l2norm_graph_replay_matches_eager():
+    """A HIP graph of a normalising prefill and decode replays to the eager results."""
+    _say("l2norm graph replay")
+    x = make_case(B=2, T=300, Hqk=2, Hv=4, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
+                  seed=16, name="graph", qk_raw=True)
+    d = to_inputs(x)
+    o = torch.empty((x.B, x.T, x.Hv, x.Dv), dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty((x.B, x.Hv, x.Dk, x.Dv), dtype=torch.float32, device="cuda")
+    st = d["init"].clone()
+    od = torch.empty((x.B, x.Hv, x.Dv), dtype=torch.bfloat16, device="cuda")
+    dargs = tuple(t[:, 0].contiguous() for t in (d["q"], d["k"], d["v"], d["beta"], d["g"]))
+
+    def calls():
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], out=o, final_state=fs,
+                     qk_l2norm=True)
+        dn.decode_step(*dargs, st, out=od, qk_l2norm=True)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = (o.clone(), fs.clone(), od.clone(), st.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.copy_(d["init"])
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        o.zero_(), fs.zero_(), od.zero_()
+        st.copy_(d["init"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((o, fs, od, st), ref, ("o", "final_state", "decode o", "state")):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager call"
