@@ -323,6 +323,55 @@ def main():
     }
     del cq, ck, cv, cb, cgp, co, cs
 
+    # ---------------- readout epilogue: over the prefill's output, and fused into decode
+    from synth import make_epilogue_inputs
+    ep_in = make_epilogue_inputs((B, T, Hv, D), "bf16", seed=1)
+    ew = to_dev(ep_in["weight"])
+    esets = []
+    for i in range(args.copies):
+        esets.append((sets[i]["o"], to_dev(ep_in["gate"]) if i == 0 else esets[0][1].clone(),
+                      torch.empty_like(sets[i]["o"])))
+    for i in range(args.warmup):
+        eo, eg, ey = esets[i % len(esets)]
+        dn.norm_gate(eo, "rms", 1e-6, ew, None, eg, out=ey)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        eo, eg, ey = esets[i % len(esets)]
+        dn.norm_gate(eo, "rms", 1e-6, ew, None, eg, out=ey)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ng_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    ng_b = B * T * Hv * D * 2 * 3 + D * 4
+    del esets
+    dep_in = make_epilogue_inputs((y.B, y.Hv, y.Dv), "bf16", seed=2)
+    dw, dgt = to_dev(dep_in["weight"]), to_dev(dep_in["gate"])
+    for i in range(3):
+        dn.decode_step(dq, dk, dv, db, dg, dstate[i % 2], out=dout, norm="rms", norm_weight=dw,
+                       out_gate=dgt)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.decode_reps):
+        dn.decode_step(dq, dk, dv, db, dg, dstate[i % 2], out=dout, norm="rms", norm_weight=dw,
+                       out_gate=dgt)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_ep_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
+    dec_ep_b = dec_b + y.B * y.Hv * y.Dv * 2 + y.Dv * 4
+    epilogue = {
+        "what": "per-head RMSNorm over d_v with weight, then * silu(gate) (gate shaped like o, bf16)",
+        "prefill_output": {"workload": "the B4 H16 T2048 d128 bf16 prefill output",
+                           "kernel": "norm_gate_kernel", "us_per_call": ng_us,
+                           "roofline": {"bound": "hbm", "achieved": ng_b / (ng_us * 1e-6) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": ng_b / (ng_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                        "algorithmic_bytes": ng_b}},
+        "decode_fused": {"workload": "gated decode step 256 x 32 heads d128 bf16",
+                         "kernel": "decode_kernel (fused epilogue)", "us_per_step": dec_ep_us,
+                         "hbm_frac": dec_ep_b / (dec_ep_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "vs_plain_step": dec_ep_us / dec_us},
+    }
+
     # ------------------------------------ the other two full-size prefill workloads
     # (context beside the headline: each timed the same way, with HIP events around a loop
     # of back-to-back calls on the launching stream)
@@ -392,6 +441,7 @@ def main():
         "prefill_other_workloads": other,
         "in_rule_qk_l2norm": in_rule_norm,
         "channel_gates": channel_gates,
+        "readout_epilogue": epilogue,
         "cpu_baseline": None,
     }
     if not args.no_cpu:

@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib_path", "load_library",
+__all__ = ["chunk_fwd", "decode_step", "norm_gate", "workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
 
@@ -30,7 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libdeltanet.so")
 
 DN_OK, DN_ERR_INVALID_ARG, DN_ERR_UNSUPPORTED, DN_ERR_HIP, DN_ERR_WORKSPACE = 0, 1, 2, 3, 4
 DN_F32, DN_BF16 = 0, 1
-EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step",
+EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
+            "dn_norm_gate",
             "dn_status_str", "dn_version")
 
 
@@ -45,6 +46,14 @@ class _Shape(ctypes.Structure):
                 ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("flags", ctypes.c_int32), ("l2norm_eps", ctypes.c_float)]
 
+
+class _Epilogue(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("eps", ctypes.c_float), ("weight", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("gate", ctypes.c_void_p)]
+
+
+DN_NORM_RMS, DN_NORM_LAYER = 0, 1
+_NORM_KINDS = {"rms": DN_NORM_RMS, "layer": DN_NORM_LAYER}
 
 DN_QK_L2NORM = 1
 DN_GATE_PER_KEY = 2
@@ -77,6 +86,11 @@ def load_library():
         lib.dn_chunk_fwd_workspace_bytes.argtypes = [sp]
         lib.dn_chunk_fwd_workspace_bytes.restype = sz
         lib.dn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+        ep = ctypes.POINTER(_Epilogue)
+        lib.dn_decode_step_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, ep, vp, vp]
+        lib.dn_decode_step_ex.restype = ctypes.c_int
+        lib.dn_norm_gate.argtypes = [sp, ep, vp, vp, vp]
+        lib.dn_norm_gate.restype = ctypes.c_int
         lib.dn_decode_step.restype = ctypes.c_int
         lib.dn_status_str.argtypes = [ctypes.c_int]
         lib.dn_status_str.restype = ctypes.c_char_p
@@ -213,13 +227,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                 g: Optional[torch.Tensor], state: torch.Tensor, scale: float = 1.0,
                 out: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
-                l2norm_eps: float = 1e-6) -> torch.Tensor:
+                l2norm_eps: float = 1e-6, norm: Optional[str] = None, norm_eps: float = 1e-6,
+                norm_weight: Optional[torch.Tensor] = None,
+                norm_bias: Optional[torch.Tensor] = None,
+                out_gate: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One token per sequence against the cached ``state`` (updated in place).
 
     q, k ``[N, Hqk, Dk]``, v ``[N, Hv, Dv]``; beta, g ``[N, Hv]`` float32 (g may be
     None, or ``[N, Hv, Dk]``: one log decay per key channel); state ``[N, Hv, Dk, Dv]``
     float32.  Returns o ``[N, Hv, Dv]``.
     ``qk_l2norm`` normalises q and k inside the call, as in :func:`chunk_fwd`.
+    ``norm`` ("rms" or "layer") fuses the readout epilogue of :func:`norm_gate` (with
+    ``norm_eps``, ``norm_weight``, ``norm_bias`` and the output gate ``out_gate``, shaped
+    like o): ``out`` then holds the epilogue's result.
     """
     lib = load_library()
     _dev(q, "q")
@@ -242,9 +262,52 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
         _dev(out, "out", q.dtype, (N, Hv, Dv))
     shape = _Shape(N, 1, N, Hqk, Hv, Dk, Dv, _dtype_code(q), 0, float(scale),
                    *_flags(qk_l2norm, l2norm_eps, per_key))
+    ep = None
+    if norm is not None:
+        ep = _epilogue(norm, norm_eps, norm_weight, norm_bias, out_gate, Dv, q.dtype, (N, Hv, Dv))
     with torch.cuda.device(q.device):
-        rc = lib.dn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                _ptr(g), _ptr(state), _ptr(out), _stream(q.device))
+        rc = lib.dn_decode_step_ex(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                   _ptr(g), _ptr(state), None if ep is None else ctypes.byref(ep),
+                                   _ptr(out), _stream(q.device))
     if rc != DN_OK:
-        _raise(rc, "dn_decode_step")
+        _raise(rc, "dn_decode_step_ex")
+    return out
+
+
+def _epilogue(kind, eps, weight, bias, gate, Dv, dtype, shape) -> _Epilogue:
+    if kind not in _NORM_KINDS:
+        raise ValueError(f"norm must be one of {sorted(_NORM_KINDS)}")
+    if weight is not None:
+        _dev(weight, "norm_weight", torch.float32, (Dv,))
+    if bias is not None:
+        _dev(bias, "norm_bias", torch.float32, (Dv,))
+    if gate is not None:
+        _dev(gate, "out_gate", dtype, shape)
+    return _Epilogue(_NORM_KINDS[kind], float(eps), _ptr(weight), _ptr(bias), _ptr(gate))
+
+
+def norm_gate(o: torch.Tensor, norm: str = "rms", eps: float = 1e-6,
+              weight: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+              gate: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None
+              ) -> torch.Tensor:
+    """Readout epilogue over a prefill's output o ``[B, T, Hv, Dv]``: per (token, head)
+    an RMS ("rms") or layer ("layer") normalisation over Dv with ``weight`` (and
+    ``bias``, layer only) of length Dv, then ``* silu(gate)`` when ``gate`` (shaped like
+    o) is given.  ``out`` may be ``o`` (in place)."""
+    lib = load_library()
+    _dev(o, "o")
+    if o.dim() != 4:
+        raise ValueError("o must be [B, T, Hv, Dv]")
+    B, T, Hv, Dv = o.shape
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _dev(out, "out", o.dtype, tuple(o.shape))
+    ep = _epilogue(norm, eps, weight, bias, gate, Dv, o.dtype, tuple(o.shape))
+    shape = _Shape(B, T, B, Hv, Hv, Dv, Dv, _dtype_code(o), 0, 1.0, 0, 0.0)
+    with torch.cuda.device(o.device):
+        rc = lib.dn_norm_gate(ctypes.byref(shape), ctypes.byref(ep), _ptr(o), _ptr(out),
+                              _stream(o.device))
+    if rc != DN_OK:
+        _raise(rc, "dn_norm_gate")
     return out

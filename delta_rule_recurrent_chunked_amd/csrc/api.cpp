@@ -26,11 +26,29 @@ dn_status check_common(const dn_shape* s) {
     return DN_OK;
 }
 
+// The epilogue's fields; fills `e` (kind -1 when ep is null and `optional`).
+dn_status check_epilogue(const dn_epilogue* ep, bool optional, dn::EpilogueArgs& e) {
+    e = dn::EpilogueArgs{-1, 0.f, nullptr, nullptr, nullptr};
+    if (!ep) return optional ? DN_OK : DN_ERR_INVALID_ARG;
+    if (ep->kind != DN_NORM_RMS && ep->kind != DN_NORM_LAYER) return DN_ERR_INVALID_ARG;
+    if (!(ep->eps >= 0.f && ep->eps <= 3.0e38f)) return DN_ERR_INVALID_ARG;
+    if (ep->kind == DN_NORM_RMS && ep->bias) return DN_ERR_INVALID_ARG;
+    if ((ep->weight && !aligned4(ep->weight)) || (ep->bias && !aligned4(ep->bias)) ||
+        (ep->gate && !aligned16(ep->gate)))
+        return DN_ERR_INVALID_ARG;
+    e.kind = ep->kind;
+    e.eps = ep->eps;
+    e.w = ep->weight;
+    e.b = ep->bias;
+    e.gate = ep->gate;
+    return DN_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t dn_version(void) { return 10100; }
+int32_t dn_version(void) { return 10200; }
 
 const char* dn_status_str(dn_status st) {
     switch (st) {
@@ -103,7 +121,16 @@ dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const vo
 dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float* state, void* o,
                          hipStream_t stream) {
+    return dn_decode_step_ex(s, q, k, v, beta, g, state, nullptr, o, stream);
+}
+
+dn_status dn_decode_step_ex(const dn_shape* s, const void* q, const void* k, const void* v,
+                            const float* beta, const float* g, float* state,
+                            const dn_epilogue* ep, void* o, hipStream_t stream) {
     dn_status st = check_common(s);
+    if (st != DN_OK) return st;
+    dn::EpilogueArgs e;
+    st = check_epilogue(ep, true, e);
     if (st != DN_OK) return st;
     if (s->T != 1 || s->num_seqs != s->B) return DN_ERR_INVALID_ARG;
     if (s->B > 0 && (!q || !k || !v || !beta || !state || !o)) return DN_ERR_INVALID_ARG;
@@ -121,7 +148,28 @@ dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const 
     a.g_per_key = (s->flags & DN_GATE_PER_KEY) != 0;
     if (a.g_per_key && !g) return DN_ERR_INVALID_ARG;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.state = state; a.o = o;
+    a.ep = e;
     return dn::launch_decode(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+dn_status dn_norm_gate(const dn_shape* s, const dn_epilogue* ep, const void* o, void* y,
+                       hipStream_t stream) {
+    dn_status st = check_common(s);
+    if (st != DN_OK) return st;
+    dn::EpilogueArgs e;
+    st = check_epilogue(ep, false, e);
+    if (st != DN_OK) return st;
+    const long rows = (long)s->B * s->T * s->Hv;
+    if (rows > 0 && (!o || !y)) return DN_ERR_INVALID_ARG;
+    if ((o && !aligned16(o)) || (y && !aligned16(y))) return DN_ERR_INVALID_ARG;
+    dn::NormGateArgs a{};
+    a.rows = rows;
+    a.Dv = s->Dv;
+    a.bf16 = s->dtype == DN_BF16;
+    a.ep = e;
+    a.o = o;
+    a.y = y;
+    return dn::launch_norm_gate(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@
 // With the in-rule normalisation (q, k -> x / sqrt(|x|^2 + eps)) the norms come out of
 // the same reductions: r_k, r_q and k.q take the factors 1/|k|, 1/|q|, and the update
 // adds k (delta / |k|)^T.
+// The readout epilogue (normalisation over the head's d_v entries, silu output gate) can
+// run fused: the workgroup holds the head's whole readout.
 // The state is read once and written once: this kernel is bound by HBM bandwidth.
 //
 // Work decomposition: one workgroup per (n, h, slice of CW value columns; CW = Dv).  A
@@ -72,6 +74,7 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
     __shared__ float red[NW][2 * CW + 3];
     __shared__ float dsh[CW];
+    __shared__ __align__(16) float osh[CW];   // the readout, for a fused epilogue
 
     const int tid = threadIdx.x;
     const int ct = tid % TPR;                 // float4 column group
@@ -181,9 +184,12 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
         }
         const float d = beta * (vval - alpha * rk);
         dsh[tid] = d * ik;
-        st_out(static_cast<T*>(a.o), vo, a.scale * (alpha * rq + kqs * d));
+        const float ov = a.scale * (alpha * rq + kqs * d);
+        if (a.ep.kind >= 0) osh[tid] = ov;
+        else st_out(static_cast<T*>(a.o), vo, ov);
     }
     __syncthreads();
+
     const float d0 = dsh[ct * 4 + 0], d1 = dsh[ct * 4 + 1], d2 = dsh[ct * 4 + 2], d3 = dsh[ct * 4 + 3];
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
@@ -194,6 +200,29 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
         r[2] = am * m[p][2] + kr[p] * d2;
         r[3] = am * m[p][3] + kr[p] * d3;
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4v*>(Mp + (long)(row0 + p) * DV));
+    }
+    if (a.ep.kind >= 0 && tid < CW) {
+        // readout epilogue over the head's d_v = CW entries (one slice per head), after the
+        // state stores: the mean (layer norm) and the mean square around it, from the
+        // readout in LDS; the weight, bias and gate of this column are requested first
+        const int j = slice * CW + tid;
+        const float wj = a.ep.w ? a.ep.w[j] : 1.f;
+        const float bj = a.ep.b ? a.ep.b[j] : 0.f;
+        const float zj = a.ep.gate ? ld_f32(static_cast<const T*>(a.ep.gate), vo) : 0.f;
+        const float4* o4 = reinterpret_cast<const float4*>(osh);
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < CW / 4; ++i) sm += o4[i].x + o4[i].y + o4[i].z + o4[i].w;
+        const float c = a.ep.kind == 1 ? sm * (1.f / CW) : 0.f;
+        float sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < CW / 4; ++i) {
+            const float4 t = o4[i];
+            sq += (t.x - c) * (t.x - c) + (t.y - c) * (t.y - c) + (t.z - c) * (t.z - c) + (t.w - c) * (t.w - c);
+        }
+        float y = (osh[tid] - c) * rsqrtf(sq * (1.f / CW) + a.ep.eps) * wj + bj;
+        if (a.ep.gate) y *= silu(zj);
+        st_out(static_cast<T*>(a.o), vo, y);
     }
 }
 

@@ -28,6 +28,15 @@ struct PrefillArgs {
     size_t ws_bytes;
 };
 
+// Readout epilogue, validated on the host (kind < 0: none).
+struct EpilogueArgs {
+    int kind;                       // -1 none, 0 RMS, 1 layer norm
+    float eps;
+    const float* w;                 // may be null (ones)
+    const float* b;                 // may be null (zeros)
+    const void* gate;               // may be null (no output gate)
+};
+
 struct DecodeArgs {
     int N, Hqk, Hv, Dk, Dv;
     int bf16;
@@ -35,6 +44,7 @@ struct DecodeArgs {
     int qk_norm;                    // as in PrefillArgs
     float eps;
     int g_per_key;
+    EpilogueArgs ep;
     const void* q;
     const void* k;
     const void* v;
@@ -44,7 +54,17 @@ struct DecodeArgs {
     void* o;
 };
 
+struct NormGateArgs {
+    long rows;                      // tokens x value heads
+    int Dv;
+    int bf16;
+    EpilogueArgs ep;
+    const void* o;
+    void* y;                        // may alias o
+};
+
 // Launchers (host functions); each returns hipGetLastError() after its launches.
+hipError_t launch_norm_gate(const NormGateArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
 bool prefill_fused_supported(const PrefillArgs& a);
@@ -67,6 +87,9 @@ __device__ __forceinline__ float inv_norm(float ss, float eps) {
     const float x = ss + eps;
     return x > 0.f ? rsqrtf(x) : 0.f;
 }
+
+// silu(z) = z / (1 + exp(-z)), the output gate's activation (hardware reciprocal)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 // Token range [bos, eos) of sequence n.
 __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, long& bos, long& eos) {

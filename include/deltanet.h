@@ -165,6 +165,55 @@ dn_status dn_decode_step(const dn_shape* shape,
                          const float* beta, const float* g,
                          float* state, void* o, hipStream_t stream);
 
+/*
+ * Readout epilogue: the step after the rule, per (token, value head) over the d_v
+ * entries of the readout o -- a normalisation (the frankenstein page's layer norm of the
+ * recurrent readout; the mutichung block flowchart's RMSNorm after the Delta Rule box),
+ * then the silu-gated output gate (frankenstein g_proj):
+ *
+ *   DN_NORM_RMS:    y = o / sqrt(mean(o^2) + eps) * w
+ *   DN_NORM_LAYER:  y = (o - mean(o)) / sqrt(mean((o - mean(o))^2) + eps) * w + b
+ *   with a gate z:  y <- y * z / (1 + exp(-z))
+ *
+ * w and b (length d_v, fp32) are shared by the heads; NULL weight = ones, NULL bias =
+ * zeros (a bias is an error with DN_NORM_RMS).  The gate has the readout's shape and
+ * dtype, or is NULL (no output gate).  Arithmetic is fp32.
+ */
+typedef enum { DN_NORM_RMS = 0, DN_NORM_LAYER = 1 } dn_norm_kind;
+
+typedef struct {
+    int32_t kind;          /* dn_norm_kind                                               */
+    float eps;             /* >= 0 and finite; inside the square root                    */
+    const float* weight;   /* [Dv] fp32 device, 4-byte aligned, or NULL (ones)           */
+    const float* bias;     /* [Dv] fp32 device, 4-byte aligned, or NULL (zeros)          */
+    const void* gate;      /* readout-shaped, dtype, 16-byte aligned, or NULL (no gate)  */
+} dn_epilogue;
+
+/*
+ * dn_norm_gate -- the epilogue over a prefill's output: o and y are [B, T, Hv, Dv] in
+ * shape->dtype (B * T tokens; Hqk, Dk and chunk_size are checked as for dn_chunk_fwd
+ * but not used), the gate likewise.  y may alias o.  Bound by HBM bandwidth: it reads o
+ * (and the gate) once and writes y once.
+ *
+ * Errors: as dn_chunk_fwd, and DN_ERR_INVALID_ARG for a NULL or bad epilogue (unknown
+ * kind, negative or non-finite eps, a bias with DN_NORM_RMS, misaligned pointer).
+ */
+dn_status dn_norm_gate(const dn_shape* shape, const dn_epilogue* epilogue,
+                       const void* o, void* y, hipStream_t stream);
+
+/*
+ * dn_decode_step_ex -- dn_decode_step with the epilogue fused: o receives y (the raw
+ * readout is not written).  epilogue == NULL is dn_decode_step.  The decode workgroup
+ * holds a head's whole readout, so the epilogue adds no HBM traffic beyond the gate.
+ *
+ * Errors: as dn_decode_step and dn_norm_gate.
+ */
+dn_status dn_decode_step_ex(const dn_shape* shape,
+                            const void* q, const void* k, const void* v,
+                            const float* beta, const float* g,
+                            float* state, const dn_epilogue* epilogue, void* o,
+                            hipStream_t stream);
+
 /* Static description of a status code. */
 const char* dn_status_str(dn_status status);
 

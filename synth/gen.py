@@ -31,7 +31,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "DeltaInputs", "make_case", "make_config", "CONFIG_NAMES",
+    "DeltaInputs", "make_case", "make_config", "CONFIG_NAMES", "make_epilogue_inputs",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_f64",
 ]
 
@@ -220,3 +220,18 @@ def make_config(i: int, seed: int = 0) -> DeltaInputs:
                          g_scale=0.05, init_std=0.02, num_seqs_cut=8, seed=seed,
                          name=CONFIG_NAMES[5])
     raise ValueError(f"no config {i}")
+
+
+def make_epilogue_inputs(shape, dtype: str = "bf16", seed: int = 0, offset: float = 0.5) -> dict:
+    """Seeded inputs of the readout epilogue: a readout ``o`` of ``shape`` (``[..., Dv]``,
+    N(offset, 1)), an output gate ``gate`` of the same shape (N(0, 1)), both cast like
+    q/k/v (fp32 values or bf16 bit patterns), and fp32 ``weight`` (U(0.5, 1.5)) and
+    ``bias`` (N(0, 0.1^2)) of length Dv.  Draw order: o, gate, weight, bias."""
+    rng = np.random.default_rng(seed)
+    Dv = shape[-1]
+    o = offset + rng.standard_normal(shape)
+    gate = rng.standard_normal(shape)
+    weight = rng.uniform(0.5, 1.5, Dv).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(Dv)).astype(np.float32)
+    return dict(o=_cast(o, dtype), gate=_cast(gate, dtype), weight=weight, bias=bias)
+

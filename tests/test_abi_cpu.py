@@ -102,3 +102,41 @@ def test_python_wrapper_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 1, 16)
     with pytest.raises(ValueError):
         dn.chunk_fwd(q, q, q, torch.zeros(1, 4, 1))
+
+
+def _ep(**kw):
+    d = dict(kind=dn.DN_NORM_RMS, eps=1e-6, weight=None, bias=None, gate=None)
+    d.update(kw)
+    return dn._Epilogue(**d)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(kind=2),                                   # unknown norm
+    dict(eps=-1.0),
+    dict(eps=float("nan")),
+    dict(bias=16),                                  # a bias with the RMS norm
+    dict(kind=dn.DN_NORM_LAYER, gate=24),           # misaligned gate
+    dict(kind=dn.DN_NORM_LAYER, weight=18),         # misaligned weight
+])
+def test_epilogue_rejects_bad_specs(bad):
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    ep = _ep(**bad)
+    s = _shape(B=4, T=1, num_seqs=4)
+    assert lib.dn_decode_step_ex(ctypes.byref(s), p, p, p, p, None, p, ctypes.byref(ep), p,
+                                 None) == dn.DN_ERR_INVALID_ARG
+    s = _shape(B=2, T=8, num_seqs=2)
+    assert lib.dn_norm_gate(ctypes.byref(s), ctypes.byref(ep), p, p, None) == dn.DN_ERR_INVALID_ARG
+
+
+def test_norm_gate_needs_an_epilogue_and_buffers():
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    s = _shape(B=2, T=8, num_seqs=2)
+    assert lib.dn_norm_gate(ctypes.byref(s), None, p, p, None) == dn.DN_ERR_INVALID_ARG
+    ep = _ep(kind=dn.DN_NORM_LAYER)
+    assert lib.dn_norm_gate(ctypes.byref(s), ctypes.byref(ep), None, p, None) == dn.DN_ERR_INVALID_ARG
+    assert lib.dn_norm_gate(ctypes.byref(s), ctypes.byref(ep), ctypes.c_void_p(20), p, None) == dn.DN_ERR_INVALID_ARG
+    s = _shape(B=2, T=8, num_seqs=2, Dv=48)
+    assert lib.dn_norm_gate(ctypes.byref(s), ctypes.byref(ep), p, p, None) == dn.DN_ERR_UNSUPPORTED
+
