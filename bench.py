@@ -372,6 +372,23 @@ def main():
                          "vs_plain_step": dec_ep_us / dec_us},
     }
 
+    # ------------- the token-by-token route on the layer-prefill workload (for context)
+    s0 = sets[0]
+    dn.recurrent_fwd(s0["q"], s0["k"], s0["v"], s0["beta"], None, None, out=s0["o"],
+                     final_state=s0["fs"])
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(3):
+        dn.recurrent_fwd(s0["q"], s0["k"], s0["v"], s0["beta"], None, None, out=s0["o"],
+                         final_state=s0["fs"])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    rec_us = ev0.elapsed_time(ev1) * 1e3 / 3
+    recurrent = {"workload": "B4 H16 T2048 d128 bf16, no decay, final state, no trace",
+                 "kernel": "recurrent_kernel (token by token, state in registers)",
+                 "us_per_call": rec_us, "tokens_per_s": tokens / (rec_us * 1e-6),
+                 "vs_chunked_call": rec_us / call_us}
+
     # ------------------------------------ the other two full-size prefill workloads
     # (context beside the headline: each timed the same way, with HIP events around a loop
     # of back-to-back calls on the launching stream)
@@ -442,6 +459,7 @@ def main():
         "in_rule_qk_l2norm": in_rule_norm,
         "channel_gates": channel_gates,
         "readout_epilogue": epilogue,
+        "recurrent_route": recurrent,
         "cpu_baseline": None,
     }
     if not args.no_cpu:

@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "norm_gate", "workspace_bytes", "lib_path", "load_library",
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "norm_gate", "workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
 
@@ -31,7 +31,7 @@ _LIB_PATH = os.path.join(_HERE, "libdeltanet.so")
 DN_OK, DN_ERR_INVALID_ARG, DN_ERR_UNSUPPORTED, DN_ERR_HIP, DN_ERR_WORKSPACE = 0, 1, 2, 3, 4
 DN_F32, DN_BF16 = 0, 1
 EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
-            "dn_norm_gate",
+            "dn_norm_gate", "dn_recurrent_fwd",
             "dn_status_str", "dn_version")
 
 
@@ -90,6 +90,8 @@ def load_library():
         lib.dn_decode_step_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, ep, vp, vp]
         lib.dn_decode_step_ex.restype = ctypes.c_int
         lib.dn_norm_gate.argtypes = [sp, ep, vp, vp, vp]
+        lib.dn_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.dn_recurrent_fwd.restype = ctypes.c_int
         lib.dn_norm_gate.restype = ctypes.c_int
         lib.dn_decode_step.restype = ctypes.c_int
         lib.dn_status_str.argtypes = [ctypes.c_int]
@@ -145,28 +147,10 @@ def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: 
     return int(load_library().dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
 
 
-def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
-              g: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
-              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
-              scale: float = 1.0, chunk_size: int = 64, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = True,
-              qk_l2norm: bool = False, l2norm_eps: float = 1e-6
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Delta rule over whole sequences (prefill), chunkwise-parallel form.
-
-    q, k ``[B, T, Hqk, Dk]``, v ``[B, T, Hv, Dv]`` (float32 or bfloat16, one dtype);
-    beta, g ``[B, T, Hv]`` float32 (g None: plain rule; g ``[B, T, Hv, Dk]``: one log decay
-    per key channel); initial_state
-    ``[N, Hv, Dk, Dv]`` float32 or None (zero state); cu_seqlens int32 ``[N + 1]``
-    packs N sequences along T (B == 1).  Returns ``(o [B, T, Hv, Dv], final_state or
-    None)``.  ``final_state`` may be passed (and may be ``initial_state``, to update
-    it in place); ``out`` and ``workspace`` may be passed to avoid allocation.
-    ``check_cu_seqlens`` copies cu_seqlens to the host (a synchronising copy) and
-    checks ``cu[0] == 0``, non-decreasing, ``cu[N] == T``: the kernels trust it.
-    ``qk_l2norm`` normalises q and k inside the call, x / sqrt(|x|^2 + l2norm_eps).
-    """
-    lib = load_library()
+def _prompt_args(q, k, v, beta, g, initial_state, output_final_state, cu_seqlens, scale,
+                 chunk_size, out, final_state, check_cu_seqlens, qk_l2norm, l2norm_eps):
+    """Checks and allocations shared by the whole-sequence calls; returns
+    (shape, out, final_state, N)."""
     _dev(q, "q")
     if q.dim() != 4:
         raise ValueError("q must be [B, T, Hqk, Dk]")
@@ -208,6 +192,35 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
         _dev(final_state, "final_state", torch.float32, (N, Hv, Dk, Dv))
     shape = _Shape(B, T, N, Hqk, Hv, Dk, Dv, _dtype_code(q), chunk_size, float(scale),
                    *_flags(qk_l2norm, l2norm_eps, per_key))
+    return shape, out, final_state, N
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+              g: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+              scale: float = 1.0, chunk_size: int = 64, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = True,
+              qk_l2norm: bool = False, l2norm_eps: float = 1e-6
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Delta rule over whole sequences (prefill), chunkwise-parallel form.
+
+    q, k ``[B, T, Hqk, Dk]``, v ``[B, T, Hv, Dv]`` (float32 or bfloat16, one dtype);
+    beta, g ``[B, T, Hv]`` float32 (g None: plain rule; g ``[B, T, Hv, Dk]``: one log decay
+    per key channel); initial_state
+    ``[N, Hv, Dk, Dv]`` float32 or None (zero state); cu_seqlens int32 ``[N + 1]``
+    packs N sequences along T (B == 1).  Returns ``(o [B, T, Hv, Dv], final_state or
+    None)``.  ``final_state`` may be passed (and may be ``initial_state``, to update
+    it in place); ``out`` and ``workspace`` may be passed to avoid allocation.
+    ``check_cu_seqlens`` copies cu_seqlens to the host (a synchronising copy) and
+    checks ``cu[0] == 0``, non-decreasing, ``cu[N] == T``: the kernels trust it.
+    ``qk_l2norm`` normalises q and k inside the call, x / sqrt(|x|^2 + l2norm_eps).
+    """
+    lib = load_library()
+    shape, out, final_state, _ = _prompt_args(q, k, v, beta, g, initial_state, output_final_state,
+                                              cu_seqlens, scale, chunk_size, out, final_state,
+                                              check_cu_seqlens, qk_l2norm, l2norm_eps)
+    dev = q.device
     need = int(lib.dn_chunk_fwd_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
@@ -222,6 +235,35 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     if rc != DN_OK:
         _raise(rc, "dn_chunk_fwd")
     return out, final_state
+
+
+def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                  g: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+                  scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, state_trace: bool = False,
+                  check_cu_seqlens: bool = True, qk_l2norm: bool = False,
+                  l2norm_eps: float = 1e-6):
+    """The rule token by token over whole sequences (the recurrent route), same arguments
+    as :func:`chunk_fwd`.  Returns ``(o, final_state, trace)`` where ``trace`` is the
+    state after every token, ``[B, T, Hv, Dk, Dv]`` float32, when ``state_trace`` (else
+    None)."""
+    lib = load_library()
+    shape, out, final_state, _ = _prompt_args(q, k, v, beta, g, initial_state, output_final_state,
+                                              cu_seqlens, scale, 64, out, final_state,
+                                              check_cu_seqlens, qk_l2norm, l2norm_eps)
+    B, T, Hv, Dv = out.shape
+    Dk = q.shape[3]
+    trace = None
+    if state_trace:
+        trace = torch.empty((B, T, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.dn_recurrent_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(g), _ptr(initial_state), _ptr(final_state),
+                                  _ptr(cu_seqlens), _ptr(out), _ptr(trace), _stream(q.device))
+    if rc != DN_OK:
+        _raise(rc, "dn_recurrent_fwd")
+    return out, final_state, trace
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,

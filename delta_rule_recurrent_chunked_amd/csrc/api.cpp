@@ -118,6 +118,26 @@ dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const vo
     return e == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
+dn_status dn_recurrent_fwd(const dn_shape* s, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const float* h0, float* hT,
+                           const int32_t* cu, void* o, float* trace, hipStream_t stream) {
+    dn::RecurrentArgs a;
+    dn_status st = prefill_shape(s, cu != nullptr, a);
+    if (st != DN_OK) return st;
+    const long tokens = (long)s->B * s->T;
+    if (tokens > 0 && (!q || !k || !v || !beta || !o)) return DN_ERR_INVALID_ARG;
+    if (a.g_per_key && !g) return DN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, h0, hT, o, trace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
+    const void* scalars[] = {beta, g, cu};
+    for (const void* p : scalars)
+        if (p && !aligned4(p)) return DN_ERR_INVALID_ARG;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.h0 = h0; a.hT = hT; a.cu = cu; a.o = o;
+    a.trace = trace;
+    return dn::launch_recurrent(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
 dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float* state, void* o,
                          hipStream_t stream) {

@@ -63,7 +63,14 @@ struct NormGateArgs {
     void* y;                        // may alias o
 };
 
+// The token-by-token route over whole sequences: the prefill's arguments plus an
+// optional per-token state trace [tokens, Hv, Dk, Dv].
+struct RecurrentArgs : PrefillArgs {
+    float* trace;                   // may be null
+};
+
 // Launchers (host functions); each returns hipGetLastError() after its launches.
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s);
 hipError_t launch_norm_gate(const NormGateArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);

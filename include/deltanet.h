@@ -166,6 +166,29 @@ dn_status dn_decode_step(const dn_shape* shape,
                          float* state, void* o, hipStream_t stream);
 
 /*
+ * dn_recurrent_fwd -- the rule token by token over whole sequences (the pages'
+ * recurrent route: the frankenstein forward's token loop; the nnterp page's recurrent
+ * delta-rule route, which exposes the state after every token).  Same arguments and
+ * results as dn_chunk_fwd (chunk_size is ignored, no workspace), plus
+ *
+ *   state_trace    [B, T, Hv, Dk, Dv] fp32 (B * T tokens), 16-byte aligned, or NULL:
+ *                  the state after each token (key-major like every state), written for
+ *                  every token of every sequence
+ *
+ * One workgroup per (sequence, value head) keeps the state in registers and steps through
+ * the tokens: it is for inspection and for checking the chunked path, not a fast prompt
+ * path (the trace alone is Dk * Dv * 4 bytes per token and head).
+ *
+ * Errors: as dn_chunk_fwd.
+ */
+dn_status dn_recurrent_fwd(const dn_shape* shape,
+                           const void* q, const void* k, const void* v,
+                           const float* beta, const float* g,
+                           const float* initial_state, float* final_state,
+                           const int32_t* cu_seqlens, void* o, float* state_trace,
+                           hipStream_t stream);
+
+/*
  * Readout epilogue: the step after the rule, per (token, value head) over the d_v
  * entries of the readout o -- a normalisation (the frankenstein page's layer norm of the
  * recurrent readout; the mutichung block flowchart's RMSNorm after the Delta Rule box),
