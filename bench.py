@@ -365,11 +365,13 @@ def main():
                            "roofline": {"bound": "hbm", "achieved": ng_b / (ng_us * 1e-6) / 1e9,
                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                         "frac": ng_b / (ng_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                        "algorithmic_bytes": ng_b}},
+                                        "algorithmic_bytes": ng_b,
+                                        "traffic": load_traffic("norm_gate_bytes_per_call")}},
         "decode_fused": {"workload": "gated decode step 256 x 32 heads d128 bf16",
                          "kernel": "decode_kernel (fused epilogue)", "us_per_step": dec_ep_us,
                          "hbm_frac": dec_ep_b / (dec_ep_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                         "vs_plain_step": dec_ep_us / dec_us},
+                         "vs_plain_step": dec_ep_us / dec_us,
+                         "traffic": load_traffic("decode_epilogue_bytes_per_call")},
     }
 
     # ------------- the token-by-token route on the layer-prefill workload (for context)

@@ -112,3 +112,53 @@ def test_decode_fused_epilogue_workload():
     o_ref, s_ref = run_oracle(x)
     want = ref_norm_gate(o_ref[:, 0], "rms", 1e-6, e["weight"], None, to_f64(e["gate"]))
     assert rel_l2(host(y), want) <= 1e-2 and rel_l2(host(state), s_ref) <= 1e-2
+
+
+def test_graph_replay_of_epilogue_and_recurrent_calls():
+    """A HIP graph holding dn_norm_gate, a decode step with the fused epilogue and the
+    token-by-token route (with its trace) replays to the eager results, every replay."""
+    _say("graph replay: epilogue, fused decode, recurrent route")
+    x = make_case(B=2, T=100, Hqk=2, Hv=4, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
+                  seed=33, name="graph")
+    e = make_epilogue_inputs((2, 100, 4, 128), "bf16", seed=34)
+    d = to_inputs(x)
+    w, gate = dev_tensor(e["weight"]), dev_tensor(e["gate"])
+    o = torch.empty((2, 100, 4, 128), dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty((2, 4, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(o)
+    st = d["init"].clone()
+    od = torch.empty((2, 4, 128), dtype=torch.bfloat16, device="cuda")
+    dargs = tuple(t[:, 0].contiguous() for t in (d["q"], d["k"], d["v"], d["beta"], d["g"]))
+    dgate = gate[:, 0].contiguous()
+    trace = {}
+
+    def calls():
+        _, _, tr = dn.recurrent_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], out=o,
+                                    final_state=fs, state_trace=True)
+        trace["t"] = tr
+        dn.norm_gate(o, "layer", 1e-5, w, None, gate, out=y)
+        dn.decode_step(*dargs, st, out=od, norm="rms", norm_weight=w, out_gate=dgate)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = (o.clone(), fs.clone(), y.clone(), od.clone(), st.clone(), trace["t"].clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.copy_(d["init"])
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    tr = trace["t"]
+    for rep in range(3):
+        o.zero_(), fs.zero_(), y.zero_(), od.zero_(), tr.zero_()
+        st.copy_(d["init"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((o, fs, y, od, st, tr), ref,
+                                   ("o", "final_state", "y", "decode y", "state", "trace")):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager call"
