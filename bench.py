@@ -391,6 +391,54 @@ def main():
                  "us_per_call": rec_us, "tokens_per_s": tokens / (rec_us * 1e-6),
                  "vs_chunked_call": rec_us / call_us}
 
+    # ------------ the short causal conv (+ silu) in front of the rule: prompt and decode
+    crng = np.random.default_rng(3)
+    Cc = 3 * Hv * D
+    cx = torch.from_numpy(crng.standard_normal((B, T, Cc)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    cw = torch.from_numpy((crng.standard_normal((Cc, 4)) / 2).astype(np.float32)).to(dev)
+    cb = torch.zeros(Cc, dtype=torch.float32, device=dev)
+    cy = torch.empty_like(cx)
+    cst = torch.empty((B, Cc, 3), dtype=torch.bfloat16, device=dev)
+    dn.causal_conv(cx, cw, cb, out=cy, final_state=cst)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(20):
+        dn.causal_conv(cx, cw, cb, out=cy, final_state=cst)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    conv_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    conv_b = 2 * B * T * Cc * 2 + Cc * 4 * 5 + B * Cc * 3 * 2
+    Cd = 3 * y.Hv * y.Dk
+    dx = torch.from_numpy(crng.standard_normal((y.B, Cd)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    dwt = torch.from_numpy((crng.standard_normal((Cd, 4)) / 2).astype(np.float32)).to(dev)
+    dcs = torch.from_numpy(crng.standard_normal((y.B, Cd, 3)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    dyo = torch.empty_like(dx)
+    for _ in range(3):
+        dn.causal_conv_step(dx, dwt, None, dcs, out=dyo)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.decode_reps):
+        dn.causal_conv_step(dx, dwt, None, dcs, out=dyo)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    cstep_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
+    cstep_b = 2 * y.B * Cd * 2 + 2 * y.B * Cd * 3 * 2 + Cd * 4 * 4
+    conv = {
+        "what": "causal depthwise conv, width 4, + silu, bf16, over the q, k and v channels",
+        "prompt": {"workload": f"B{B} T{T}, {Cc} channels (3 x {Hv} heads x {D})",
+                   "kernel": "conv_kernel", "us_per_call": conv_us,
+                   "roofline": {"bound": "hbm", "achieved": conv_b / (conv_us * 1e-6) / 1e9,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": conv_b / (conv_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                "algorithmic_bytes": conv_b,
+                                "traffic": load_traffic("conv_bytes_per_call")}},
+        "decode_step": {"workload": f"{y.B} sequences, {Cd} channels, conv state in place",
+                        "kernel": "conv_step_kernel", "us_per_step": cstep_us,
+                        "hbm_frac": cstep_b / (cstep_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "algorithmic_bytes": cstep_b},
+    }
+    del cx, cy, cst, dx, dcs, dyo
+
     # ------------------------------------ the other two full-size prefill workloads
     # (context beside the headline: each timed the same way, with HIP events around a loop
     # of back-to-back calls on the launching stream)
@@ -462,6 +510,7 @@ def main():
         "channel_gates": channel_gates,
         "readout_epilogue": epilogue,
         "recurrent_route": recurrent,
+        "causal_conv": conv,
         "cpu_baseline": None,
     }
     if not args.no_cpu:

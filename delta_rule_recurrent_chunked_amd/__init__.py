@@ -21,7 +21,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "norm_gate", "workspace_bytes", "lib_path", "load_library",
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "norm_gate", "causal_conv",
+           "causal_conv_step", "workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
 
@@ -31,7 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "libdeltanet.so")
 DN_OK, DN_ERR_INVALID_ARG, DN_ERR_UNSUPPORTED, DN_ERR_HIP, DN_ERR_WORKSPACE = 0, 1, 2, 3, 4
 DN_F32, DN_BF16 = 0, 1
 EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
-            "dn_norm_gate", "dn_recurrent_fwd",
+            "dn_norm_gate", "dn_recurrent_fwd", "dn_causal_conv", "dn_causal_conv_step",
             "dn_status_str", "dn_version")
 
 
@@ -45,6 +46,12 @@ class _Shape(ctypes.Structure):
                 ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("flags", ctypes.c_int32), ("l2norm_eps", ctypes.c_float)]
+
+
+class _ConvShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("C", ctypes.c_int32), ("width", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("activation", ctypes.c_int32)]
 
 
 class _Epilogue(ctypes.Structure):
@@ -91,6 +98,11 @@ def load_library():
         lib.dn_decode_step_ex.restype = ctypes.c_int
         lib.dn_norm_gate.argtypes = [sp, ep, vp, vp, vp]
         lib.dn_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        cs = ctypes.POINTER(_ConvShape)
+        lib.dn_causal_conv.argtypes = [cs, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.dn_causal_conv.restype = ctypes.c_int
+        lib.dn_causal_conv_step.argtypes = [cs, vp, vp, vp, vp, vp, vp]
+        lib.dn_causal_conv_step.restype = ctypes.c_int
         lib.dn_recurrent_fwd.restype = ctypes.c_int
         lib.dn_norm_gate.restype = ctypes.c_int
         lib.dn_decode_step.restype = ctypes.c_int
@@ -353,3 +365,89 @@ def norm_gate(o: torch.Tensor, norm: str = "rms", eps: float = 1e-6,
     if rc != DN_OK:
         _raise(rc, "dn_norm_gate")
     return out
+
+
+_ACTIVATIONS = {None: 0, "none": 0, "silu": 1}
+
+
+def causal_conv(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                cu_seqlens: Optional[torch.Tensor] = None, activation: Optional[str] = "silu",
+                out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Short causal depthwise convolution (+ silu) over whole sequences.
+
+    x ``[B, T, C]`` (float32 or bfloat16; C a multiple of 8); weight ``[C, W]`` float32
+    (W in 2..8, the last tap on the current token); bias ``[C]`` float32; initial_state
+    ``[N, C, W - 1]`` in x's dtype (the W - 1 inputs before each sequence, oldest first)
+    or None (zeros); cu_seqlens int32 ``[N + 1]`` packs N sequences (B == 1).  Returns
+    ``(y [B, T, C], final_state [N, C, W - 1] or None)``."""
+    lib = load_library()
+    _dev(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
+    B, T, C = x.shape
+    _dev(weight, "weight", torch.float32)
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [C, W]")
+    W = weight.shape[1]
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (C,))
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", x.dtype, (N, C, W - 1))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _dev(out, "out", x.dtype, (B, T, C))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, C, W - 1), dtype=x.dtype, device=x.device)
+    elif final_state is not None:
+        _dev(final_state, "final_state", x.dtype, (N, C, W - 1))
+    if activation not in _ACTIVATIONS:
+        raise ValueError("activation must be 'silu' or None")
+    shape = _ConvShape(B, T, N, C, W, _dtype_code(x), _ACTIVATIONS[activation])
+    with torch.cuda.device(x.device):
+        rc = lib.dn_causal_conv(ctypes.byref(shape), _ptr(x), _ptr(weight), _ptr(bias),
+                                _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(out),
+                                _stream(x.device))
+    if rc != DN_OK:
+        _raise(rc, "dn_causal_conv")
+    return out, final_state
+
+
+def causal_conv_step(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                     conv_state: torch.Tensor, activation: Optional[str] = "silu",
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence: x ``[N, C]``, conv_state ``[N, C, W - 1]`` (x's dtype)
+    updated in place.  Returns y ``[N, C]``."""
+    lib = load_library()
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, C]")
+    N, C = x.shape
+    _dev(weight, "weight", torch.float32)
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [C, W]")
+    W = weight.shape[1]
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (C,))
+    _dev(conv_state, "conv_state", x.dtype, (N, C, W - 1))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _dev(out, "out", x.dtype, (N, C))
+    if activation not in _ACTIVATIONS:
+        raise ValueError("activation must be 'silu' or None")
+    shape = _ConvShape(N, 1, N, C, W, _dtype_code(x), _ACTIVATIONS[activation])
+    with torch.cuda.device(x.device):
+        rc = lib.dn_causal_conv_step(ctypes.byref(shape), _ptr(x), _ptr(weight), _ptr(bias),
+                                     _ptr(conv_state), _ptr(out), _stream(x.device))
+    if rc != DN_OK:
+        _raise(rc, "dn_causal_conv_step")
+    return out
+

@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdeltanet.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = ["api.cpp", "decode.hip", "prefill_generic.hip", "prefill_fused.hip", "epilogue.hip",
-           "recurrent.hip"]
+           "recurrent.hip", "conv.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -138,6 +138,55 @@ dn_status dn_recurrent_fwd(const dn_shape* s, const void* q, const void* k, cons
     return dn::launch_recurrent(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
+static dn_status conv_shape(const dn_conv_shape* s, dn::ConvArgs& a) {
+    if (!s) return DN_ERR_INVALID_ARG;
+    if (s->B < 0 || s->T < 0 || s->num_seqs < 0 || s->C <= 0 || s->C % 8) return DN_ERR_INVALID_ARG;
+    if (s->dtype != DN_F32 && s->dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
+    if (s->width < 2 || s->width > 8) return DN_ERR_UNSUPPORTED;
+    if (s->activation != 0 && s->activation != 1) return DN_ERR_INVALID_ARG;
+    a = dn::ConvArgs{};
+    a.B = s->B; a.T = s->T; a.N = s->num_seqs; a.C = s->C; a.W = s->width;
+    a.bf16 = s->dtype == DN_BF16; a.silu = s->activation;
+    return DN_OK;
+}
+
+dn_status dn_causal_conv(const dn_conv_shape* s, const void* x, const float* w, const float* b,
+                         const void* s0, void* sT, const int32_t* cu, void* y, hipStream_t stream) {
+    dn::ConvArgs a;
+    dn_status st = conv_shape(s, a);
+    if (st != DN_OK) return st;
+    if (cu) {
+        if (s->B != 1 || s->num_seqs < 1) return DN_ERR_INVALID_ARG;
+    } else if (s->num_seqs != s->B) {
+        return DN_ERR_INVALID_ARG;
+    }
+    const long tokens = (long)s->B * s->T;
+    if (!w || (tokens > 0 && (!x || !y))) return DN_ERR_INVALID_ARG;
+    if ((x && !aligned16(x)) || (y && !aligned16(y)) || !aligned4(w) || (b && !aligned4(b)) ||
+        (cu && !aligned4(cu)))
+        return DN_ERR_INVALID_ARG;
+    const int es = s->dtype == DN_BF16 ? 2 : 4;
+    if ((s0 && ((uintptr_t)s0 % es)) || (sT && ((uintptr_t)sT % es))) return DN_ERR_INVALID_ARG;
+    if ((x && x == y) || (s0 && s0 == sT)) return DN_ERR_INVALID_ARG;
+    a.x = x; a.w = w; a.b = b; a.s0 = s0; a.sT = sT; a.cu = cu; a.y = y;
+    return dn::launch_causal_conv(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+dn_status dn_causal_conv_step(const dn_conv_shape* s, const void* x, const float* w, const float* b,
+                              void* state, void* y, hipStream_t stream) {
+    dn::ConvArgs a;
+    dn_status st = conv_shape(s, a);
+    if (st != DN_OK) return st;
+    if (s->T != 1 || s->num_seqs != s->B) return DN_ERR_INVALID_ARG;
+    if (!w || (s->B > 0 && (!x || !y || !state))) return DN_ERR_INVALID_ARG;
+    const int es = s->dtype == DN_BF16 ? 2 : 4;
+    if ((x && !aligned16(x)) || (y && !aligned16(y)) || !aligned4(w) || (b && !aligned4(b)) ||
+        (state && ((uintptr_t)state % es)))
+        return DN_ERR_INVALID_ARG;
+    a.x = x; a.w = w; a.b = b; a.s0 = state; a.sT = state; a.y = y;
+    return dn::launch_causal_conv_step(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
 dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float* state, void* o,
                          hipStream_t stream) {

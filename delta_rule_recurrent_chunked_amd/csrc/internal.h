@@ -69,7 +69,23 @@ struct RecurrentArgs : PrefillArgs {
     float* trace;                   // may be null
 };
 
+// Short causal depthwise convolution (+ silu), validated on the host.
+struct ConvArgs {
+    int B, T, N, C, W;
+    int bf16;
+    int silu;
+    const void* x;
+    const float* w;                 // [C, W]
+    const float* b;                 // may be null
+    const void* s0;                 // [N, C, W - 1], may be null (zeros)
+    void* sT;                       // [N, C, W - 1], may be null; in place for a step
+    const int32_t* cu;              // may be null
+    void* y;
+};
+
 // Launchers (host functions); each returns hipGetLastError() after its launches.
+hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t s);
+hipError_t launch_causal_conv_step(const ConvArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s);
 hipError_t launch_norm_gate(const NormGateArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

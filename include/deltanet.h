@@ -237,6 +237,52 @@ dn_status dn_decode_step_ex(const dn_shape* shape,
                             float* state, const dn_epilogue* epilogue, void* o,
                             hipStream_t stream);
 
+/*
+ * Short causal depthwise convolution in front of the rule (the mutichung DeltaNet block
+ * flowchart: a "Conv" box then a "SiLU" box on the q/k and on the v branch, the
+ * convolutions depthwise-separable, generalising the shift SSM).  Per channel c:
+ *
+ *   y_t[c] = act(b[c] + sum_{j<W} w[c][j] x_{t-W+1+j}[c]),   act = silu or identity
+ *
+ * Inputs before a sequence's first token come from its conv state, the W - 1 inputs
+ * before it, oldest first, [N, C, W - 1] in the dtype of x; a NULL initial state means
+ * zeros.  The final state is each sequence's last W - 1 inputs (state entries when the
+ * sequence is shorter).  Channels are the last axis of x: q, k and v of one layer can be
+ * one [.., Hqk*Dk + Hqk*Dk + Hv*Dv] tensor.  Bound by HBM bandwidth: x is read once and y
+ * written once.
+ */
+typedef struct {
+    int32_t B, T;          /* B rows of T tokens; B == 1 with cu_seqlens (T = total tokens)   */
+    int32_t num_seqs;      /* N: B, or len(cu_seqlens) - 1                                      */
+    int32_t C;             /* channels, a multiple of 8                                          */
+    int32_t width;         /* W, 2..8                                                            */
+    int32_t dtype;         /* dn_dtype of x, y and the conv states                               */
+    int32_t activation;    /* 0: none, 1: silu                                                   */
+} dn_conv_shape;
+
+/*
+ *   x              [B, T, C] dtype, 16-byte aligned
+ *   weight         [C, W] fp32 (4-byte aligned);  bias [C] fp32 or NULL
+ *   initial_state  [N, C, W - 1] dtype or NULL;   final_state [N, C, W - 1] dtype or NULL
+ *                  (may not alias initial_state: a sequence's last block may be read
+ *                  after another's state is written)
+ *   cu_seqlens     [N + 1] int32 device or NULL (each batch row is a sequence)
+ *   y              [B, T, C] dtype, 16-byte aligned; may not alias x
+ * Errors: DN_ERR_INVALID_ARG (null required pointer, sizes, C % 8, misalignment,
+ * aliasing), DN_ERR_UNSUPPORTED (W outside 2..8, dtype), DN_ERR_HIP.
+ */
+dn_status dn_causal_conv(const dn_conv_shape* shape, const void* x, const float* weight,
+                         const float* bias, const void* initial_state, void* final_state,
+                         const int32_t* cu_seqlens, void* y, hipStream_t stream);
+
+/*
+ * dn_causal_conv_step -- one token per sequence (decode): shape->B = N sequences, T == 1;
+ * x, y [N, C]; conv_state [N, C, W - 1] read and overwritten (shifted by one, x appended).
+ * Errors: as dn_causal_conv.
+ */
+dn_status dn_causal_conv_step(const dn_conv_shape* shape, const void* x, const float* weight,
+                              const float* bias, void* conv_state, void* y, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* dn_status_str(dn_status status);
 

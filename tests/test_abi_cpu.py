@@ -140,3 +140,35 @@ def test_norm_gate_needs_an_epilogue_and_buffers():
     s = _shape(B=2, T=8, num_seqs=2, Dv=48)
     assert lib.dn_norm_gate(ctypes.byref(s), ctypes.byref(ep), p, p, None) == dn.DN_ERR_UNSUPPORTED
 
+
+def _cshape(**kw):
+    d = dict(B=1, T=64, num_seqs=1, C=64, width=4, dtype=dn.DN_BF16, activation=1)
+    d.update(kw)
+    return dn._ConvShape(**d)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(C=60), dn.DN_ERR_INVALID_ARG),                # not a multiple of 8
+    (dict(width=1), dn.DN_ERR_UNSUPPORTED),
+    (dict(width=9), dn.DN_ERR_UNSUPPORTED),
+    (dict(activation=2), dn.DN_ERR_INVALID_ARG),
+    (dict(dtype=5), dn.DN_ERR_UNSUPPORTED),
+    (dict(B=2, num_seqs=3), dn.DN_ERR_INVALID_ARG),
+])
+def test_causal_conv_rejects_bad_shapes(bad, code):
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    s = _cshape(**bad)
+    assert lib.dn_causal_conv(ctypes.byref(s), p, p, None, None, None, None, ctypes.c_void_p(32), None) == code
+
+
+def test_causal_conv_rejects_aliasing_and_misalignment():
+    lib = dn.load_library()
+    p, q = ctypes.c_void_p(16), ctypes.c_void_p(32)
+    s = _cshape()
+    assert lib.dn_causal_conv(ctypes.byref(s), p, p, None, None, None, None, p, None) == dn.DN_ERR_INVALID_ARG
+    assert lib.dn_causal_conv(ctypes.byref(s), p, p, None, q, q, None, ctypes.c_void_p(48), None) == dn.DN_ERR_INVALID_ARG
+    assert lib.dn_causal_conv(ctypes.byref(s), ctypes.c_void_p(24), p, None, None, None, None, q, None) == dn.DN_ERR_INVALID_ARG
+    s = _cshape(B=4, T=2, num_seqs=4)
+    assert lib.dn_causal_conv_step(ctypes.byref(s), p, p, None, p, q, None) == dn.DN_ERR_INVALID_ARG
+
