@@ -1,0 +1,88 @@
+"""fp64 reverse pass of the gated delta rule, token by token -- TEST INFRASTRUCTURE ONLY
+(see ``oracle/__init__.py``): only the tests, the smoke check and the benchmark's CPU leg
+may import it, and the HIP library never calls it.
+
+The forward rule is the one ``dn_oracle.c`` runs (frankenstein "DeltaNet Attention" page,
+update equation; gate first per the nnterp "linear_attention" class text; read after the
+write), per (sequence, value head), with the state stored key-major, M = S^T [Dk, Dv]:
+
+    M'_t = a_t M_{t-1},  a_t = exp(g_t)
+    r_t  = M'_t^T k_t,   delta_t = beta_t (v_t - r_t)
+    M_t  = M'_t + k_t delta_t^T,      o_t = scale M_t^T q_t
+
+Given dL/do_t and dL/dM_T, the reverse pass walks the tokens backwards with the adjoint
+G = dL/dM_t (chain rule on each line above):
+
+    G    += scale q_t do_t^T,          dq_t = scale M_t do_t
+    dd    = G^T k_t                    (dL/d delta_t)
+    dv_t  = beta_t dd,                 dbeta_t = dd . (v_t - r_t)
+    dk_t  = G delta_t - beta_t M'_t dd
+    G'    = G - beta_t k_t dd^T        (dL/dM'_t)
+    dg_t  = <G', M'_t>,                G <- a_t G'   (dL/dM_{t-1})
+
+and dL/dM_0 is G after the first token.  Value head h reads query/key head h / (Hv/Hqk):
+dq and dk are summed over the value heads that share a query/key head.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["backward"]
+
+
+def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: float = 1.0):
+    """Gradients of the rule.  Shapes as ``oracle.recurrent`` (q, k ``[B, T, Hqk, Dk]``, v
+    ``[B, T, Hv, Dv]``, beta, g ``[B, T, Hv]`` or g None, init ``[N, Hv, Dk, Dv]`` or None),
+    do ``[B, T, Hv, Dv]``, dfinal ``[N, Hv, Dk, Dv]`` or None.  Returns a dict of fp64
+    arrays dq, dk, dv, dbeta, dg (None without g), dinit."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    beta, do = np.asarray(beta, dtype=np.float64), np.asarray(do, dtype=np.float64)
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    cu = np.arange(B + 1) * T if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    fl = lambda a, *tail: a.reshape((B * T,) + tail)
+    qf, kf, vf = fl(q, Hqk, Dk), fl(k, Hqk, Dk), fl(v, Hv, Dv)
+    bf, df = fl(beta, Hv), fl(do, Hv, Dv)
+    gf = None if g is None else fl(np.asarray(g, dtype=np.float64), Hv)
+    dq, dk = np.zeros_like(qf), np.zeros_like(kf)
+    dv, dbeta = np.zeros_like(vf), np.zeros_like(bf)
+    dg = None if g is None else np.zeros_like(gf)
+    dinit = np.zeros((N, Hv, Dk, Dv))
+    for n in range(N):
+        for h in range(Hv):
+            hq = h // grp
+            M = np.zeros((Dk, Dv)) if init is None else np.array(init[n, h], dtype=np.float64)
+            Ms, Mp = [], []                     # M_t and M'_t of each token (forward)
+            for t in range(cu[n], cu[n + 1]):
+                a = 1.0 if gf is None else np.exp(gf[t, h])
+                Mpt = a * M
+                r = Mpt.T @ kf[t, hq]
+                M = Mpt + np.outer(kf[t, hq], bf[t, h] * (vf[t, h] - r))
+                Mp.append(Mpt)
+                Ms.append(M)
+            G = np.zeros((Dk, Dv)) if dfinal is None else np.array(dfinal[n, h], dtype=np.float64)
+            for i, t in reversed(list(enumerate(range(cu[n], cu[n + 1])))):
+                kt, qt = kf[t, hq], qf[t, hq]
+                Mpt, Mt = Mp[i], Ms[i]
+                r = Mpt.T @ kt
+                delta = bf[t, h] * (vf[t, h] - r)
+                G = G + scale * np.outer(qt, df[t, h])
+                dq[t, hq] += scale * (Mt @ df[t, h])
+                dd = G.T @ kt
+                dv[t, h] = bf[t, h] * dd
+                dbeta[t, h] = dd @ (vf[t, h] - r)
+                dk[t, hq] += G @ delta - bf[t, h] * (Mpt @ dd)
+                Gp = G - bf[t, h] * np.outer(kt, dd)
+                a = 1.0 if gf is None else np.exp(gf[t, h])
+                if dg is not None:
+                    dg[t, h] = np.sum(Gp * Mpt)
+                G = a * Gp
+            dinit[n, h] = G
+    out = dict(dq=dq.reshape(q.shape), dk=dk.reshape(k.shape), dv=dv.reshape(v.shape),
+               dbeta=dbeta.reshape(beta.shape), dg=None if dg is None else dg.reshape(beta.shape),
+               dinit=dinit)
+    return out
