@@ -386,7 +386,25 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     rec_us = ev0.elapsed_time(ev1) * 1e3 / 3
+    # the reverse pass on a gated sample of the layer workload (one sequence of 2048 tokens,
+    # 16 heads), from the forward's state trace
+    xb = make_case(B=1, T=T, Hqk=Hqk, Dk=D, dtype="bf16", g_scale=0.1, seed=0)
+    bq, bk, bv, bb_, bg = (to_dev(a_) for a_ in (xb.q, xb.k, xb.v, xb.beta, xb.g))
+    _, _, btr = dn.recurrent_fwd(bq, bk, bv, bb_, bg, None, state_trace=True)
+    bdo = torch.randn((1, T, Hv, D), device=dev).to(torch.bfloat16)
+    dn.recurrent_bwd(bq, bk, bv, bb_, bg, None, btr, bdo)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(3):
+        dn.recurrent_bwd(bq, bk, bv, bb_, bg, None, btr, bdo)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    bwd_us = ev0.elapsed_time(ev1) * 1e3 / 3
+    del btr
     recurrent = {"workload": "B4 H16 T2048 d128 bf16, no decay, final state, no trace",
+                 "reverse_pass": {"workload": "B1 H16 T2048 d128 bf16 gated, from the state trace",
+                                  "kernel": "recurrent_bwd_kernel", "us_per_call": bwd_us,
+                                  "tokens_per_s": T / (bwd_us * 1e-6)},
                  "kernel": "recurrent_kernel (token by token, state in registers)",
                  "us_per_call": rec_us, "tokens_per_s": tokens / (rec_us * 1e-6),
                  "vs_chunked_call": rec_us / call_us}

@@ -187,6 +187,51 @@ dn_status dn_causal_conv_step(const dn_conv_shape* s, const void* x, const float
     return dn::launch_causal_conv_step(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
+size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* s) {
+    dn::PrefillArgs a;
+    const bool packed = s && s->B == 1 && s->num_seqs != 1;
+    if (prefill_shape(s, packed, a) != DN_OK || s->Hqk == s->Hv) return 0;
+    return (size_t)2 * s->B * s->T * s->Hv * s->Dk * sizeof(float);
+}
+
+dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const float* h0,
+                           const float* trace, const void* dout, const float* dfinal,
+                           const int32_t* cu, float* dq, float* dk, float* dv, float* dbeta,
+                           float* dg, float* dh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+    dn::RecurrentBwdArgs a{};
+    dn_status st = prefill_shape(s, cu != nullptr, a);
+    if (st != DN_OK) return st;
+    if (a.qk_norm || a.g_per_key) return DN_ERR_UNSUPPORTED;
+    const long tokens = (long)s->B * s->T;
+    if (tokens > 0 && (!q || !k || !v || !beta || !trace || !dout || !dq || !dk || !dv || !dbeta ||
+                       (g && !dg)))
+        return DN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, h0, trace, dout, dfinal, dh0, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
+    const void* scalars[] = {beta, g, cu, dq, dk, dv, dbeta, dg};
+    for (const void* p : scalars)
+        if (p && !aligned4(p)) return DN_ERR_INVALID_ARG;
+    const size_t need = dn_recurrent_bwd_workspace_bytes(s);
+    if (need && (!ws || ws_bytes < need)) return DN_ERR_WORKSPACE;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.h0 = h0; a.cu = cu;
+    a.trace = trace; a.dout = dout; a.dfinal = dfinal;
+    a.dv = dv; a.dbeta = dbeta; a.dg = g ? dg : nullptr; a.dh0 = dh0;
+    if (need) {   // per value head first, then the sum per query/key head
+        a.dq = static_cast<float*>(ws);
+        a.dk = static_cast<float*>(ws) + need / sizeof(float) / 2;
+        a.dq_out = dq;
+        a.dk_out = dk;
+    } else {
+        a.dq = dq;
+        a.dk = dk;
+        a.dq_out = nullptr;
+        a.dk_out = nullptr;
+    }
+    return dn::launch_recurrent_bwd(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
 dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float* state, void* o,
                          hipStream_t stream) {

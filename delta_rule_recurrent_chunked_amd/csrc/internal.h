@@ -83,7 +83,26 @@ struct ConvArgs {
     void* y;
 };
 
+// The reverse pass of the token-by-token route: the forward's arguments, its state
+// trace, dL/do and dL/dM_T in; gradients out (fp32).  dq, dk are first written per value
+// head ([tokens, Hv, Dk], caller's workspace) and then summed into dq_out, dk_out
+// ([tokens, Hqk, Dk]).
+struct RecurrentBwdArgs : PrefillArgs {
+    const float* trace;             // [tokens, Hv, Dk, Dv] from the forward
+    const void* dout;               // [tokens, Hv, Dv] dtype
+    const float* dfinal;            // [N, Hv, Dk, Dv] or null
+    float* dq;                      // [tokens, Hv, Dk] workspace
+    float* dk;                      // [tokens, Hv, Dk] workspace
+    float* dq_out;                  // [tokens, Hqk, Dk]
+    float* dk_out;                  // [tokens, Hqk, Dk]
+    float* dv;                      // [tokens, Hv, Dv]
+    float* dbeta;                   // [tokens, Hv]
+    float* dg;                      // [tokens, Hv] or null (no gate)
+    float* dh0;                     // [N, Hv, Dk, Dv] or null
+};
+
 // Launchers (host functions); each returns hipGetLastError() after its launches.
+hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s);
 hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_causal_conv_step(const ConvArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s);

@@ -189,6 +189,37 @@ dn_status dn_recurrent_fwd(const dn_shape* shape,
                            hipStream_t stream);
 
 /*
+ * dn_recurrent_bwd -- the reverse pass of the rule (gradients for training), token by
+ * token: given dL/do and dL/d final_state, the gradients of the loss for q, k, v, beta, g
+ * and the initial state.  It walks each sequence backwards from the state trace that
+ * dn_recurrent_fwd wrote for the same inputs.  One gate per head or none; the in-call
+ * normalisation and gates per key channel are DN_ERR_UNSUPPORTED here.
+ *
+ *   state_trace     [B, T, Hv, Dk, Dv] fp32 from dn_recurrent_fwd (required)
+ *   d_o             [B, T, Hv, Dv] dtype (required)
+ *   d_final_state   [N, Hv, Dk, Dv] fp32 or NULL (zero)
+ *   dq, dk          [B, T, Hqk, Dk] fp32 (summed over the value heads of each q/k head)
+ *   dv              [B, T, Hv, Dv] fp32;  dbeta [B, T, Hv] fp32
+ *   dg              [B, T, Hv] fp32, required when g is given, else ignored
+ *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
+ *   workspace       dn_recurrent_bwd_workspace_bytes(shape) bytes (0 when Hqk == Hv)
+ *
+ * Errors: as dn_recurrent_fwd, DN_ERR_UNSUPPORTED for the flags above, DN_ERR_WORKSPACE.
+ */
+dn_status dn_recurrent_bwd(const dn_shape* shape,
+                           const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const float* initial_state,
+                           const float* state_trace, const void* d_o,
+                           const float* d_final_state, const int32_t* cu_seqlens,
+                           float* dq, float* dk, float* dv, float* dbeta, float* dg,
+                           float* d_initial_state, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Bytes of workspace dn_recurrent_bwd needs: per-value-head dq, dk before the sum over a
+ * query/key head's value heads (0 when Hqk == Hv). */
+size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* shape);
+
+/*
  * Readout epilogue: the step after the rule, per (token, value head) over the d_v
  * entries of the readout o -- a normalisation (the frankenstein page's layer norm of the
  * recurrent readout; the mutichung block flowchart's RMSNorm after the Delta Rule box),
