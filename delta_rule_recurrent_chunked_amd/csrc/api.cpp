@@ -190,8 +190,8 @@ dn_status dn_causal_conv_step(const dn_conv_shape* s, const void* x, const float
 size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* s) {
     dn::PrefillArgs a;
     const bool packed = s && s->B == 1 && s->num_seqs != 1;
-    if (prefill_shape(s, packed, a) != DN_OK || s->Hqk == s->Hv) return 0;
-    return (size_t)2 * s->B * s->T * s->Hv * s->Dk * sizeof(float);
+    if (prefill_shape(s, packed, a) != DN_OK) return 0;
+    return (size_t)dn::recurrent_bwd_slices(s->Dv) * s->B * s->T * s->Hv * (2 * s->Dk + 2) * sizeof(float);
 }
 
 dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, const void* v,
@@ -217,18 +217,14 @@ dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, cons
     if (need && (!ws || ws_bytes < need)) return DN_ERR_WORKSPACE;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.h0 = h0; a.cu = cu;
     a.trace = trace; a.dout = dout; a.dfinal = dfinal;
-    a.dv = dv; a.dbeta = dbeta; a.dg = g ? dg : nullptr; a.dh0 = dh0;
-    if (need) {   // per value head first, then the sum per query/key head
-        a.dq = static_cast<float*>(ws);
-        a.dk = static_cast<float*>(ws) + need / sizeof(float) / 2;
-        a.dq_out = dq;
-        a.dk_out = dk;
-    } else {
-        a.dq = dq;
-        a.dk = dk;
-        a.dq_out = nullptr;
-        a.dk_out = nullptr;
-    }
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = g ? dg : nullptr; a.dh0 = dh0;
+    // the slices' shares: dq, dk [slices, tokens, Hv, Dk], then dbeta, dg [slices, tokens, Hv]
+    const size_t qk = (size_t)dn::recurrent_bwd_slices(s->Dv) * tokens * s->Hv * s->Dk;
+    const size_t sc = (size_t)dn::recurrent_bwd_slices(s->Dv) * tokens * s->Hv;
+    a.ws_dq = static_cast<float*>(ws);
+    a.ws_dk = a.ws_dq + qk;
+    a.ws_db = a.ws_dk + qk;
+    a.ws_dg = a.ws_db + sc;
     return dn::launch_recurrent_bwd(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 

@@ -84,22 +84,25 @@ struct ConvArgs {
 };
 
 // The reverse pass of the token-by-token route: the forward's arguments, its state
-// trace, dL/do and dL/dM_T in; gradients out (fp32).  dq, dk are first written per value
-// head ([tokens, Hv, Dk], caller's workspace) and then summed into dq_out, dk_out
-// ([tokens, Hqk, Dk]).
+// trace, dL/do and dL/dM_T in; gradients out (fp32).  Each workgroup takes a slice of the
+// value columns (recurrent_bwd_slices(Dv) of them) and writes its share of dq, dk, dbeta
+// and dg to the workspace; a second kernel adds the shares.
 struct RecurrentBwdArgs : PrefillArgs {
     const float* trace;             // [tokens, Hv, Dk, Dv] from the forward
     const void* dout;               // [tokens, Hv, Dv] dtype
     const float* dfinal;            // [N, Hv, Dk, Dv] or null
-    float* dq;                      // [tokens, Hv, Dk] workspace
-    float* dk;                      // [tokens, Hv, Dk] workspace
-    float* dq_out;                  // [tokens, Hqk, Dk]
-    float* dk_out;                  // [tokens, Hqk, Dk]
+    float* ws_dq;                   // [slices, tokens, Hv, Dk]
+    float* ws_dk;                   // [slices, tokens, Hv, Dk]
+    float* ws_db;                   // [slices, tokens, Hv]
+    float* ws_dg;                   // [slices, tokens, Hv]
+    float* dq;                      // [tokens, Hqk, Dk]
+    float* dk;                      // [tokens, Hqk, Dk]
     float* dv;                      // [tokens, Hv, Dv]
     float* dbeta;                   // [tokens, Hv]
     float* dg;                      // [tokens, Hv] or null (no gate)
     float* dh0;                     // [N, Hv, Dk, Dv] or null
 };
+int recurrent_bwd_slices(int Dv);
 
 // Launchers (host functions); each returns hipGetLastError() after its launches.
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s);

@@ -163,45 +163,77 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
 }
 
 // ------------------------------------------------------------------------ reverse pass
-// Walks each sequence backwards with the adjoint G = dL/dM_t in registers (the forward
-// layout: a thread owns a float4 of columns in RPT consecutive rows).  Per token, with M'
-// = a M_{t-1} rebuilt from the forward's state trace (or the initial state):
+// Walks each sequence backwards with the adjoint G = dL/dM_t in registers.  Per token, with
+// M' = a M_{t-1} rebuilt from the forward's state trace (or the initial state):
 //   r = M'^T k, delta = beta (v - r), M_t = M' + k delta^T
 //   G += scale q do^T,  dq = scale M_t do,  dd = G^T k,  dv = beta dd,
 //   dbeta = dd . (v - r),  dk = G delta - beta M' dd,  G' = G - beta k dd^T,
 //   dg = <G', M'>,  G <- a G'
-// Column sums (r, dd) reduce over row groups like the forward; row sums (dq, dk) over the
-// lanes that share rows; dbeta and dg through LDS atomics.  dq and dk come out per value
-// head; a second kernel sums the value heads that share a query/key head.
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_bwd_kernel(RecurrentBwdArgs a) {
-    using S = RecShape<DK, DV>;
-    constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW;
-    __shared__ float red[NW][DV];
-    __shared__ float vec_vr[DV], vec_d[DV], vec_do[DV], vec_dd[DV];
-    __shared__ float acc2[2];
+// The value columns are independent up to the row sums (dq, dk) and the scalars (dbeta,
+// dg), so a workgroup takes one slice of CW columns of one (sequence, value head) and writes
+// its share of those; a second kernel adds the slices (and the value heads that share a
+// query/key head) in a fixed order.  Column sums (r, dd) reduce over row groups like the
+// forward, row sums over the lanes that share rows.  Each token's inputs and trace state are
+// requested one token ahead, while the previous one is computed.
+template <typename T, int DK, int CW>
+struct BwdIn {
+    float m[RecShape<DK, CW>::RPT][4];   // M_{t-1} (this thread's block)
+    float k[RecShape<DK, CW>::RPT], q[RecShape<DK, CW>::RPT];
+    float v, dout, beta, g;
+};
+
+template <typename T, int DK, int DV, int CW>
+__device__ __forceinline__ void bwd_fetch(const RecurrentBwdArgs& a, long t, long bos, int nh, int h,
+                                          int hq, int row0, int ct, int tid, int j0, BwdIn<T, DK, CW>& f) {
+    constexpr int RPT = RecShape<DK, CW>::RPT;
     typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const float* prev = t > bos ? a.trace + ((t - 1) * a.Hv + h) * (long)DK * DV
+                                : (a.h0 ? a.h0 + (long)nh * DK * DV : nullptr);
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        f32x4v x = f32x4v{0.f, 0.f, 0.f, 0.f};
+        if (prev) x = *reinterpret_cast<const f32x4v*>(prev + (long)(row0 + p) * DV + j0 + ct * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.m[p][e] = x[e];
+    }
+    const long kq0 = (t * a.Hqk + hq) * DK + row0;
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        f.k[p] = ld_f32(static_cast<const T*>(a.k), kq0 + p);
+        f.q[p] = ld_f32(static_cast<const T*>(a.q), kq0 + p);
+    }
+    const long vo = (t * a.Hv + h) * DV + j0 + (tid < CW ? tid : 0);
+    f.v = ld_f32(static_cast<const T*>(a.v), vo);
+    f.dout = ld_f32(static_cast<const T*>(a.dout), vo);
+    f.beta = a.beta[t * a.Hv + h];
+    f.g = a.g ? a.g[t * a.Hv + h] : 0.f;
+}
+
+template <typename T, int DK, int DV, int CW>
+__global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(RecurrentBwdArgs a) {
+    using S = RecShape<DK, CW>;
+    constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, NSL = DV / CW;
+    __shared__ float red[NW][CW];
+    __shared__ float vec_vr[CW], vec_d[CW], vec_do[CW], vec_dd[CW];
+    __shared__ float acc2[2];
 
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int ct = tid % TPR, rg = tid / TPR;
-    const int nh = blockIdx.x;
+    const int slice = blockIdx.x % NSL;
+    const int nh = blockIdx.x / NSL;
     const int h = nh % a.Hv, n = nh / a.Hv;
     const int hq = h / (a.Hv / a.Hqk);
-    const int row0 = rg * RPT;
+    const int row0 = rg * RPT, j0 = slice * CW;
     long bos, eos;
     seq_range(a.cu, n, a.T, bos, eos);
-    const T* q = static_cast<const T*>(a.q);
-    const T* k = static_cast<const T*>(a.k);
-    const T* v = static_cast<const T*>(a.v);
-    const T* dout = static_cast<const T*>(a.dout);
+    const long tokens = (long)a.B * a.T;
 
-    f32x4v G[RPT];
+    float G[RPT][4];
 #pragma unroll
-    for (int p = 0; p < RPT; ++p) {
-        G[p] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        if (a.dfinal) G[p] = *reinterpret_cast<const f32x4v*>(a.dfinal + ((long)nh * DK + row0 + p) * DV + ct * 4);
-    }
-    // column sums over the key rows: lanes sharing ct, then the waves through LDS
+    for (int p = 0; p < RPT; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            G[p][e] = a.dfinal ? a.dfinal[((long)nh * DK + row0 + p) * DV + j0 + ct * 4 + e] : 0.f;
     auto colsum = [&](float (&c)[4]) {
 #pragma unroll
         for (int off = TPR; off < 64; off <<= 1)
@@ -212,48 +244,39 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_bwd_kernel(R
             for (int e = 0; e < 4; ++e) red[wave][ct * 4 + e] = c[e];
         }
     };
-    // row sums over the value columns: the TPR lanes that share rows
     auto rowsum = [&](float& x) {
 #pragma unroll
         for (int off = 1; off < TPR; off <<= 1) x += __shfl_xor(x, off);
     };
 
+    BwdIn<T, DK, CW> cur, nxt;
+    if (eos > bos) bwd_fetch<T, DK, DV, CW>(a, eos - 1, bos, nh, h, hq, row0, ct, tid, j0, cur);
     for (long t = eos - 1; t >= bos; --t) {
-        // M_{t-1}: the trace of the previous token, or the sequence's initial state
-        f32x4v Mp[RPT];
-        const float* prev = t > bos ? a.trace + ((t - 1) * a.Hv + h) * (long)DK * DV
-                                    : (a.h0 ? a.h0 + (long)nh * DK * DV : nullptr);
-        const float al = a.g ? expf(a.g[t * a.Hv + h]) : 1.f;
+        if (t - 1 >= bos) bwd_fetch<T, DK, DV, CW>(a, t - 1, bos, nh, h, hq, row0, ct, tid, j0, nxt);
+        const float al = a.g ? expf(cur.g) : 1.f;
+        const float beta = cur.beta;
+        float Mp[RPT][4];
 #pragma unroll
-        for (int p = 0; p < RPT; ++p) {
-            Mp[p] = f32x4v{0.f, 0.f, 0.f, 0.f};
-            if (prev) Mp[p] = al * *reinterpret_cast<const f32x4v*>(prev + (long)(row0 + p) * DV + ct * 4);
-        }
-        const long kq0 = (t * a.Hqk + hq) * DK + row0;
-        float kr[RPT], qr[RPT];
+        for (int p = 0; p < RPT; ++p)
 #pragma unroll
-        for (int p = 0; p < RPT; ++p) {
-            kr[p] = ld_f32(k, kq0 + p);
-            qr[p] = ld_f32(q, kq0 + p);
-        }
-        const float beta = a.beta[t * a.Hv + h];
+            for (int e = 0; e < 4; ++e) Mp[p][e] = al * cur.m[p][e];
         // r = M'^T k
         float c[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < RPT; ++p)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) c[e] += Mp[p][e] * kr[p];
+            for (int e = 0; e < 4; ++e) c[e] += Mp[p][e] * cur.k[p];
         colsum(c);
         if (tid < 2) acc2[tid] = 0.f;
         __syncthreads();
-        if (tid < DV) {
+        if (tid < CW) {
             float r = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) r += red[w][tid];
-            const float vr = ld_f32(v, (t * a.Hv + h) * DV + tid) - r;   // v - r
+            const float vr = cur.v - r;   // v - r
             vec_vr[tid] = vr;
             vec_d[tid] = beta * vr;
-            vec_do[tid] = a.scale * ld_f32(dout, (t * a.Hv + h) * DV + tid);
+            vec_do[tid] = a.scale * cur.dout;
         }
         __syncthreads();
         float dl[4], dov[4];
@@ -271,21 +294,21 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_bwd_kernel(R
             dqp[p] = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                G[p][e] += qr[p] * dov[e];
-                dqp[p] += (Mp[p][e] + kr[p] * dl[e]) * dov[e];
-                c[e] += G[p][e] * kr[p];
+                G[p][e] += cur.q[p] * dov[e];
+                dqp[p] += (Mp[p][e] + cur.k[p] * dl[e]) * dov[e];
+                c[e] += G[p][e] * cur.k[p];
             }
         }
 #pragma unroll
         for (int p = 0; p < RPT; ++p) rowsum(dqp[p]);
         colsum(c);
         __syncthreads();
-        if (tid < DV) {
+        if (tid < CW) {
             float dd = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) dd += red[w][tid];
-            a.dv[(t * a.Hv + h) * DV + tid] = beta * dd;
-            atomicAdd(&acc2[0], dd * vec_vr[tid]);   // dbeta = dd . (v - r)
+            a.dv[(t * a.Hv + h) * DV + j0 + tid] = beta * dd;
+            atomicAdd(&acc2[0], dd * vec_vr[tid]);   // this slice's share of dbeta
             vec_dd[tid] = dd;
         }
         __syncthreads();
@@ -300,16 +323,16 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_bwd_kernel(R
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 dkp[p] += G[p][e] * dl[e] - beta * Mp[p][e] * ddv[e];
-                G[p][e] -= beta * kr[p] * ddv[e];
+                G[p][e] -= beta * cur.k[p] * ddv[e];
                 dgp += G[p][e] * Mp[p][e];
                 G[p][e] *= al;
             }
         }
 #pragma unroll
         for (int p = 0; p < RPT; ++p) rowsum(dkp[p]);
-        if (ct == 0) {
-            float* dq = a.dq + (t * a.Hv + h) * (long)DK + row0;
-            float* dk = a.dk + (t * a.Hv + h) * (long)DK + row0;
+        if (ct == 0) {   // this slice's share of dq, dk for the rows of this thread
+            float* dq = a.ws_dq + ((slice * tokens + t) * a.Hv + h) * (long)DK + row0;
+            float* dk = a.ws_dk + ((slice * tokens + t) * a.Hv + h) * (long)DK + row0;
 #pragma unroll
             for (int p = 0; p < RPT; ++p) {
                 dq[p] = dqp[p];
@@ -321,32 +344,49 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_bwd_kernel(R
         if (lane == 0) atomicAdd(&acc2[1], dgp);
         __syncthreads();
         if (tid == 0) {
-            a.dbeta[t * a.Hv + h] = acc2[0];
-            if (a.dg) a.dg[t * a.Hv + h] = acc2[1];
+            a.ws_db[(slice * tokens + t) * a.Hv + h] = acc2[0];
+            a.ws_dg[(slice * tokens + t) * a.Hv + h] = acc2[1];
         }
         __syncthreads();   // acc2 and the reduction buffers are reused by the next token
+        cur = nxt;
     }
     if (a.dh0) {
 #pragma unroll
         for (int p = 0; p < RPT; ++p)
-            *reinterpret_cast<f32x4v*>(a.dh0 + ((long)nh * DK + row0 + p) * DV + ct * 4) = G[p];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.dh0[((long)nh * DK + row0 + p) * DV + j0 + ct * 4 + e] = G[p][e];
     }
 }
 
-// dq, dk per value head [tokens, Hv, D] -> per query/key head [tokens, Hqk, D]: the sum over
-// the Hv / Hqk value heads that read each query/key head
-__global__ __launch_bounds__(256) void group_sum_kernel(const float* src, float* dst, long tokens, int Hqk,
-                                                       int grp, int D) {
+// The slices' shares, in a fixed order: dq, dk per query/key head (over the slices and the
+// value heads that read the head), dbeta, dg per value head (over the slices).
+__global__ __launch_bounds__(256) void bwd_sum_kernel(RecurrentBwdArgs a, int nsl) {
+    const long tokens = (long)a.B * a.T;
+    const int grp = a.Hv / a.Hqk;
+    const long nqk = tokens * a.Hqk * a.Dk;
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    const long total = tokens * Hqk * D;
-    if (i >= total) return;
-    const int d = (int)(i % D);
-    const long th = i / D;          // t * Hqk + hq
-    const int hq = (int)(th % Hqk);
-    const long t = th / Hqk;
-    float s = 0.f;
-    for (int r = 0; r < grp; ++r) s += src[((t * Hqk + hq) * grp + r) * (long)D + d];
-    dst[i] = s;
+    if (i < nqk) {
+        const int d = (int)(i % a.Dk);
+        const long th = i / a.Dk;          // t * Hqk + hq
+        float sq = 0.f, sk = 0.f;
+        for (int sl = 0; sl < nsl; ++sl)
+            for (int r = 0; r < grp; ++r) {
+                const long o = ((sl * tokens * a.Hqk + th) * grp + r) * (long)a.Dk + d;
+                sq += a.ws_dq[o];
+                sk += a.ws_dk[o];
+            }
+        a.dq[i] = sq;
+        a.dk[i] = sk;
+    } else if (i < nqk + tokens * a.Hv) {
+        const long th = i - nqk;           // t * Hv + h
+        float sb = 0.f, sg = 0.f;
+        for (int sl = 0; sl < nsl; ++sl) {
+            sb += a.ws_db[sl * tokens * a.Hv + th];
+            sg += a.ws_dg[sl * tokens * a.Hv + th];
+        }
+        a.dbeta[th] = sb;
+        if (a.dg) a.dg[th] = sg;
+    }
 }
 
 template <typename T, int DK>
@@ -375,12 +415,12 @@ hipError_t launch_dk(const RecurrentArgs& a, hipStream_t s) {
 
 template <typename T, int DK>
 hipError_t launch_bwd_dv(const RecurrentBwdArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((long)a.N * a.Hv));
+    const long nh = (long)a.N * a.Hv;
     switch (a.Dv) {
-        case 16: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 16>), grid, dim3(RecShape<DK, 16>::NT), 0, s, a); break;
-        case 32: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 32>), grid, dim3(RecShape<DK, 32>::NT), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 64>), grid, dim3(RecShape<DK, 64>::NT), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 128>), grid, dim3(RecShape<DK, 128>::NT), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 16, 16>), dim3((unsigned)nh), dim3(RecShape<DK, 16>::NT), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 32, 32>), dim3((unsigned)nh), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 64, 32>), dim3((unsigned)(2 * nh)), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 128, 32>), dim3((unsigned)(4 * nh)), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -399,19 +439,19 @@ hipError_t launch_bwd_dk(const RecurrentBwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int recurrent_bwd_slices(int Dv) { return Dv > 32 ? Dv / 32 : 1; }
+
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
     if ((long)a.N * a.Hv == 0) return hipSuccess;
-    if ((long)a.N * a.Hv > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
     const hipError_t e = a.bf16 ? launch_bwd_dk<__bf16>(a, s) : launch_bwd_dk<float>(a, s);
     if (e != hipSuccess) return e;
     const long tokens = (long)a.B * a.T;
-    if (a.dq_out && tokens > 0) {   // sum the value heads of each query/key head
-        const int grp = a.Hv / a.Hqk;
-        const long total = tokens * a.Hqk * a.Dk;
+    const long total = tokens * a.Hqk * a.Dk + tokens * a.Hv;
+    if (total > 0) {
         const long blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.dq, a.dq_out, tokens, a.Hqk, grp, a.Dk);
-        hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.dk, a.dk_out, tokens, a.Hqk, grp, a.Dk);
+        hipLaunchKernelGGL(bwd_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, recurrent_bwd_slices(a.Dv));
     }
     return hipGetLastError();
 }

@@ -202,7 +202,7 @@ dn_status dn_recurrent_fwd(const dn_shape* shape,
  *   dv              [B, T, Hv, Dv] fp32;  dbeta [B, T, Hv] fp32
  *   dg              [B, T, Hv] fp32, required when g is given, else ignored
  *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
- *   workspace       dn_recurrent_bwd_workspace_bytes(shape) bytes (0 when Hqk == Hv)
+ *   workspace       dn_recurrent_bwd_workspace_bytes(shape) bytes
  *
  * Errors: as dn_recurrent_fwd, DN_ERR_UNSUPPORTED for the flags above, DN_ERR_WORKSPACE.
  */
@@ -215,8 +215,8 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
                            float* d_initial_state, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* Bytes of workspace dn_recurrent_bwd needs: per-value-head dq, dk before the sum over a
- * query/key head's value heads (0 when Hqk == Hv). */
+/* Bytes of workspace dn_recurrent_bwd needs: each 32-column slice's share of dq, dk,
+ * dbeta and dg before they are added in a fixed order. */
 size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* shape);
 
 /*
