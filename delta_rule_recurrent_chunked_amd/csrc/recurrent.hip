@@ -10,9 +10,11 @@
 //   delta = beta (v - r_k),  o = scale (r_q + (k.q) delta),  M <- M' + k delta^T
 // with the in-rule normalisation folded in as in decode.hip.
 //
-// One workgroup per (sequence, value head); a thread owns a float4 of columns in RPT
-// consecutive rows for the whole sequence.  Two workgroup barriers per token (the column
-// sums, then delta).  The trace, when asked for, streams out with nontemporal stores.
+// One workgroup per (sequence, value head, slice of CW = min(Dv, 32) value columns): the
+// columns are independent, and every slice forms k.q and the norms itself.  A thread owns a
+// float4 of columns in RPT consecutive rows for the whole sequence.  Two workgroup barriers
+// per token (the column sums, then delta).  The trace, when asked for, streams out with
+// nontemporal stores.
 #include "internal.h"
 
 namespace dn {
@@ -28,20 +30,21 @@ struct RecShape {
     static_assert(DV % 4 == 0 && TPR <= 64 && NT % 64 == 0 && DK % RPP == 0, "recurrent tiling");
 };
 
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(RecurrentArgs a) {
-    using S = RecShape<DK, DV>;
-    constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW;
-    __shared__ float red[NW][2 * DV + 3];
-    __shared__ float dsh[DV];
+template <typename T, int DK, int DV, int CW>
+__global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_kernel(RecurrentArgs a) {
+    using S = RecShape<DK, CW>;
+    constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, NSL = DV / CW;
+    __shared__ float red[NW][2 * CW + 3];
+    __shared__ float dsh[CW];
     typedef float f32x4v __attribute__((ext_vector_type(4)));
 
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int ct = tid % TPR, rg = tid / TPR;
-    const int nh = blockIdx.x;                // n * Hv + h
+    const int slice = blockIdx.x % NSL;
+    const int nh = blockIdx.x / NSL;          // n * Hv + h
     const int h = nh % a.Hv, n = nh / a.Hv;
     const int hq = h / (a.Hv / a.Hqk);
-    const int row0 = rg * RPT;
+    const int row0 = rg * RPT, jc = slice * CW + ct * 4;   // this thread's first column
     long bos, eos;
     seq_range(a.cu, n, a.T, bos, eos);
 
@@ -49,7 +52,7 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
         m[p] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        if (a.h0) m[p] = *reinterpret_cast<const f32x4v*>(a.h0 + ((long)nh * DK + row0 + p) * DV + ct * 4);
+        if (a.h0) m[p] = *reinterpret_cast<const f32x4v*>(a.h0 + ((long)nh * DK + row0 + p) * DV + jc);
     }
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);
@@ -75,7 +78,7 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
                 for (int p = 0; p < RPT; ++p) ar[p] = al;
             }
         }
-        const float vval = tid < DV ? ld_f32(v, (t * a.Hv + h) * DV + tid) : 0.f;
+        const float vval = tid < CW ? ld_f32(v, (t * a.Hv + h) * DV + slice * CW + tid) : 0.f;
         const float beta = a.beta[t * a.Hv + h];
 
         float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
@@ -108,24 +111,24 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 red[wave][ct * 4 + c] = pk[c];
-                red[wave][DV + ct * 4 + c] = pq[c];
+                red[wave][CW + ct * 4 + c] = pq[c];
             }
             if (lane == 0) {
-                red[wave][2 * DV] = kq;
-                red[wave][2 * DV + 1] = kk;
-                red[wave][2 * DV + 2] = qq;
+                red[wave][2 * CW] = kq;
+                red[wave][2 * CW + 1] = kk;
+                red[wave][2 * CW + 2] = qq;
             }
         }
         __syncthreads();
-        if (tid < DV) {
+        if (tid < CW) {
             float rk = 0.f, rq = 0.f, kqs = 0.f, kks = 0.f, qqs = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 rk += red[w][tid];
-                rq += red[w][DV + tid];
-                kqs += red[w][2 * DV];
-                kks += red[w][2 * DV + 1];
-                qqs += red[w][2 * DV + 2];
+                rq += red[w][CW + tid];
+                kqs += red[w][2 * CW];
+                kks += red[w][2 * CW + 1];
+                qqs += red[w][2 * CW + 2];
             }
             float ik = 1.f;
             if (a.qk_norm) {
@@ -137,7 +140,7 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
             }
             const float d = beta * (vval - rk);
             dsh[tid] = d * ik;
-            st_out(o, (t * a.Hv + h) * DV + tid, a.scale * (rq + kqs * d));
+            st_out(o, (t * a.Hv + h) * DV + slice * CW + tid, a.scale * (rq + kqs * d));
         }
         __syncthreads();
         const float d0 = dsh[ct * 4 + 0], d1 = dsh[ct * 4 + 1], d2 = dsh[ct * 4 + 2], d3 = dsh[ct * 4 + 3];
@@ -149,7 +152,7 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
             m[p][3] = ar[p] * m[p][3] + kr[p] * d3;
         }
         if (a.trace) {
-            float* tr = a.trace + ((t * a.Hv + h) * (long)DK + row0) * DV + ct * 4;
+            float* tr = a.trace + ((t * a.Hv + h) * (long)DK + row0) * DV + jc;
 #pragma unroll
             for (int p = 0; p < RPT; ++p)
                 __builtin_nontemporal_store(m[p], reinterpret_cast<f32x4v*>(tr + (long)p * DV));
@@ -158,7 +161,7 @@ __global__ __launch_bounds__((RecShape<DK, DV>::NT)) void recurrent_kernel(Recur
     if (a.hT) {
 #pragma unroll
         for (int p = 0; p < RPT; ++p)
-            *reinterpret_cast<f32x4v*>(a.hT + ((long)nh * DK + row0 + p) * DV + ct * 4) = m[p];
+            *reinterpret_cast<f32x4v*>(a.hT + ((long)nh * DK + row0 + p) * DV + jc) = m[p];
     }
 }
 
@@ -391,12 +394,12 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(RecurrentBwdArgs a, int ns
 
 template <typename T, int DK>
 hipError_t launch_dv(const RecurrentArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((long)a.N * a.Hv));
+    const long nh = (long)a.N * a.Hv;
     switch (a.Dv) {
-        case 16: hipLaunchKernelGGL((recurrent_kernel<T, DK, 16>), grid, dim3(RecShape<DK, 16>::NT), 0, s, a); break;
-        case 32: hipLaunchKernelGGL((recurrent_kernel<T, DK, 32>), grid, dim3(RecShape<DK, 32>::NT), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((recurrent_kernel<T, DK, 64>), grid, dim3(RecShape<DK, 64>::NT), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((recurrent_kernel<T, DK, 128>), grid, dim3(RecShape<DK, 128>::NT), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((recurrent_kernel<T, DK, 16, 16>), dim3((unsigned)nh), dim3(RecShape<DK, 16>::NT), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((recurrent_kernel<T, DK, 32, 32>), dim3((unsigned)nh), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((recurrent_kernel<T, DK, 64, 32>), dim3((unsigned)(2 * nh)), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((recurrent_kernel<T, DK, 128, 32>), dim3((unsigned)(4 * nh)), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -458,7 +461,7 @@ hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s) {
     if ((long)a.N * a.Hv == 0) return hipSuccess;
-    if ((long)a.N * a.Hv > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
     return a.bf16 ? launch_dk<__bf16>(a, s) : launch_dk<float>(a, s);
 }
 
