@@ -219,7 +219,10 @@ __global__ __launch_bounds__(NT) void prefill_generic_kernel(PrefillArgs a) {
 //   O     = scale ((Q o exp(G)) M0 + P Delta)
 //   M1[x] = exp(G[n-1][x]) M0[x] + sum_r k_r[x] exp(G[n-1][x] - G[r][x]) Delta_r
 //
-// with every pairwise factor formed as exp(G[r][x] - G[i][x]), i <= r, never as a ratio.
+// The pairwise factor exp(G[r][x] - G[i][x]), i <= r, is exp(G[r][x]) exp(-G[i][x]) from two
+// per-token tables when the chunk's decay stays above exp(-60) on every channel (then
+// exp(-G) <= exp(60) and every product <= 1); a chunk that decays harder forms each factor
+// as one exponential of a difference, never as a ratio.
 // The per-channel sums take a [chunk][Dk] tile of their own, so this path runs 32-token
 // chunks (the chunk size does not change the result in exact arithmetic).
 constexpr int HC = 32;                  // chunk of the channel-gate path
@@ -231,6 +234,8 @@ struct ChannelSmem {
     float Q[HC][KP];
     float G[HC][KP];     // per-channel inclusive sums of g over the chunk
     float E[HC][KP];     // exp(G)
+    float En[HC][KP];    // exp(-G), when the chunk's decay allows the factored form
+    int hard;            // some channel decays below exp(-60) over the chunk
     float V[HC][SP];
     float M[GK][SP];
     float A[HC][HCP];
@@ -286,6 +291,7 @@ __global__ __launch_bounds__(NT) void prefill_channel_gate_kernel(PrefillArgs a)
             sm.V[r][j] = (r < len && j < sw) ? ld_f32(v, ((c0 + r) * a.Hv + h) * Dv + j0 + j) : 0.f;
         }
         if (tid < C) sm.beta[tid] = tid < len ? a.beta[(c0 + tid) * a.Hv + h] : 0.f;
+        if (tid == 0) sm.hard = 0;
         __syncthreads();
         if (tid < Dk) {  // inclusive sums of the log decays, one key channel per thread
             float s = 0.f;
@@ -319,8 +325,11 @@ __global__ __launch_bounds__(NT) void prefill_channel_gate_kernel(PrefillArgs a)
         for (int e = tid; e < C * Dk; e += NT) {
             const int r = e / Dk, x = e % Dk;
             sm.E[r][x] = expf(sm.G[r][x]);
+            sm.En[r][x] = expf(-sm.G[r][x]);
         }
+        if (tid < Dk && sm.G[len - 1][tid] < -60.f) sm.hard = 1;
         __syncthreads();
+        const bool hard = sm.hard != 0;
 
         // Gram matrices with the per-channel decay inside the sum
         for (int e = tid; e < C * C; e += NT) {
@@ -328,10 +337,18 @@ __global__ __launch_bounds__(NT) void prefill_channel_gate_kernel(PrefillArgs a)
             float av = 0.f, pv = 0.f;
             if (r < len && i <= r) {
                 float kk = 0.f, qk = 0.f;
-                for (int x = 0; x < Dk; ++x) {
-                    const float d = expf(sm.G[r][x] - sm.G[i][x]);
-                    kk += sm.K[r][x] * sm.K[i][x] * d;
-                    qk += sm.Q[r][x] * sm.K[i][x] * d;
+                if (hard) {
+                    for (int x = 0; x < Dk; ++x) {
+                        const float d = expf(sm.G[r][x] - sm.G[i][x]);
+                        kk += sm.K[r][x] * sm.K[i][x] * d;
+                        qk += sm.Q[r][x] * sm.K[i][x] * d;
+                    }
+                } else {
+                    for (int x = 0; x < Dk; ++x) {
+                        const float ki = sm.K[i][x] * sm.En[i][x] * sm.E[r][x];
+                        kk += sm.K[r][x] * ki;
+                        qk += sm.Q[r][x] * ki;
+                    }
                 }
                 if (i < r) av = sm.beta[r] * kk;
                 pv = qk;

@@ -48,6 +48,8 @@ CASES = {
                                  beta_scale=2.0),
     "bf16_d128_long": dict(B=1, T=700, Hqk=1, Hv=2, Dk=128, dtype="bf16", g_scale=0.1,
                            init_std=0.02),
+    # decay strong enough that chunks fall below exp(-60): the per-pair exponential form
+    "f32_strong_decay": dict(B=1, T=80, Hqk=2, Dk=32, dtype="f32", g_scale=5.0, init_std=0.3),
 }
 
 
