@@ -231,6 +231,12 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     dec_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
+    ev0.record(stream)
+    for i in range(args.decode_reps):
+        dn.decode_step(dq, dk, dv, db, None, dstate[i % 2], out=dout)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_plain_us = ev0.elapsed_time(ev1) * 1e3 / args.decode_reps
     state_b = y.B * y.Hv * y.Dk * y.Dv * 4 * 2
     dec_b = decode_bytes(y.B, y.Hqk, y.Hv, y.Dk)
     dec_gbs = state_b / (dec_us * 1e-6) / 1e9
@@ -522,7 +528,8 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": dec_b / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                 "traffic": traffic_d, "kernel": "decode_kernel",
-                                "algorithmic_bytes": dec_b}},
+                                "algorithmic_bytes": dec_b},
+                   "ungated_us_per_step": dec_plain_us},
         "prefill_other_workloads": other,
         "in_rule_qk_l2norm": in_rule_norm,
         "channel_gates": channel_gates,

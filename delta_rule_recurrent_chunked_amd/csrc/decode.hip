@@ -2,22 +2,22 @@
 // updated in place (the nnterp "linear_attention" page: the token-by-token rule on
 // a decode step, with the cached state as state_input, overwritten afterwards).
 //
-// Per (sequence n, value head h), with the state stored key-major, M = S^T [Dk][Dv]:
-//   a      = exp(g)                         (nnterp "decays": log of the fraction kept)
-//   r_k    = M^T k,  r_q = M^T q            (column reductions over the key dim)
-//   delta  = beta (v - a r_k)               (= -beta (S' k - v), S' = a S; "The Delta
-//                                            Rule" section of the mutichung DeltaNet page)
-//   o      = scale (a r_q + (k.q) delta)    (= scale S_t q with S_t = S' + delta k^T)
-//   M     <- a M + k delta^T
-// Gated steps (CHG) take a decay per state row: row i of M decays by a_i = exp(g[i]) with
-// gates per key channel (the nnterp page's ChannelGates), and a_i = exp(g) for every row
-// with one gate per head (the same gate read with row stride 0).  The reductions take
-// a_i k_i and a_i q_i, and M <- diag(a) M + k delta^T.  One gate per head goes this way too
-// because it measured faster: with the per-row gate loads and exponentials ahead of the
-// state stream, the compiler paces the sixteen state loads of a thread (about seven in
-// flight per wave, each taken by the reduction as it lands) and spreads the sixteen stores
-// through the update, where the single-gate form issues every state load at once and
-// stores in a burst (168 us against 191 us for 256 x 32 heads at d = 128).
+// Per (sequence n, value head h), with the state stored key-major, M = S^T [Dk][Dv], and a
+// decay a_i for each state row i (nnterp "decays": the log of the fraction kept):
+//   M'     = diag(a) M
+//   r_k    = M'^T k,  r_q = M'^T q          (column reductions over the key dim)
+//   delta  = beta (v - r_k)                 (= -beta (S' k - v); "The Delta Rule" section
+//                                            of the mutichung DeltaNet page)
+//   o      = scale (r_q + (k.q) delta)      (= scale S_t q with S_t = S' + delta k^T)
+//   M     <- M' + k delta^T
+// a_i = exp(g[i]) with gates per key channel (the nnterp page's ChannelGates), a_i = exp(g)
+// for every row with one gate per head (the same gate read with row stride 0), a_i = 1
+// without a gate (a constant zero log decay read the same way).  The per-row form serves
+// every step because it measured faster: with the per-row gate loads and exponentials
+// ahead of the state stream, the compiler paces the sixteen state loads of a thread (about
+// seven in flight per wave, each taken by the reduction as it lands) and spreads the
+// sixteen stores through the update, where a single-factor form issued every state load at
+// once and stored in a burst (168 us against 191 us for 256 x 32 heads at d = 128).
 // With the in-rule normalisation (q, k -> x / sqrt(|x|^2 + eps)) the norms come out of
 // the same reductions: r_k, r_q and k.q take the factors 1/|k|, 1/|q|, and the update
 // adds k (delta / |k|)^T.
@@ -36,6 +36,10 @@
 
 namespace dn {
 namespace {
+
+// log decay 0 (a factor of 1): the gate an ungated step reads, so that it takes the
+// per-row path too
+__device__ const float zero_gate[1] = {0.f};
 
 template <int DK, int CW>
 struct DecodeShape {
@@ -68,7 +72,7 @@ __device__ __forceinline__ void ld_vec(const T* p, float (&out)[N]) {
     }
 }
 
-template <typename T, int DK, int DV, int CW, bool VEC, bool CHG>
+template <typename T, int DK, int DV, int CW, bool VEC>
 __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(DecodeArgs a) {
     using S = DecodeShape<DK, CW>;
     constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, SLICES = DV / CW;
@@ -110,21 +114,21 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     }
     const long vo = (long)nh * DV + slice * CW + (tid < CW ? tid : 0);
     const float vval = ld_f32(static_cast<const T*>(a.v), vo);
-    const float alpha = 1.0f;   // a gated step takes its decay per row (ar); ungated: none
     const float beta = a.beta[nh];
-    float ar[RPT];   // gated: decay of each of this thread's rows
-    if (CHG) {
-        const long gs = a.g_per_key ? DK : 1;   // gates of (n, h) start at nh * gs
-        const int gk = a.g_per_key ? 1 : 0;     // row stride: 0 for one gate per head
+    float ar[RPT];   // decay of each of this thread's rows
+    {
+        const float* gp = a.g ? a.g : zero_gate;
+        const long gs = a.g_per_key ? DK : (a.g ? 1 : 0);   // gates of (n, h) start at nh * gs
+        const int gk = a.g_per_key ? 1 : 0;                 // row stride: 0 for one gate per head
 #pragma unroll
-        for (int p = 0; p < RPT; ++p) ar[p] = expf(a.g[(long)nh * gs + (row0 + p) * gk]);
+        for (int p = 0; p < RPT; ++p) ar[p] = expf(gp[(long)nh * gs + (row0 + p) * gk]);
     }
 
     const bool nrm = a.qk_norm;
     float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
-        const float kd = CHG ? ar[p] * kr[p] : kr[p], qd = CHG ? ar[p] * qr[p] : qr[p];
+        const float kd = ar[p] * kr[p], qd = ar[p] * qr[p];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             pk[c] += m[p][c] * kd;
@@ -182,9 +186,9 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
             rq *= iq;
             kqs *= ik * iq;
         }
-        const float d = beta * (vval - alpha * rk);
+        const float d = beta * (vval - rk);
         dsh[tid] = d * ik;
-        const float ov = a.scale * (alpha * rq + kqs * d);
+        const float ov = a.scale * (rq + kqs * d);
         if (a.ep.kind >= 0) osh[tid] = ov;
         else st_out(static_cast<T*>(a.o), vo, ov);
     }
@@ -193,7 +197,7 @@ __global__ __launch_bounds__((DecodeShape<DK, CW>::NT)) void decode_kernel(Decod
     const float d0 = dsh[ct * 4 + 0], d1 = dsh[ct * 4 + 1], d2 = dsh[ct * 4 + 2], d3 = dsh[ct * 4 + 3];
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
-        const float am = CHG ? ar[p] : alpha;
+        const float am = ar[p];
         f32x4v r;
         r[0] = am * m[p][0] + kr[p] * d0;
         r[1] = am * m[p][1] + kr[p] * d1;
@@ -237,13 +241,8 @@ hipError_t launch_dims(const DecodeArgs& a, hipStream_t s) {
     constexpr bool kVecShape = (S::RPT * sizeof(T)) % 16 == 0 && (DK * sizeof(T)) % 16 == 0;
     const bool aligned = ((reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k)) & 15) == 0;
     const dim3 grid((unsigned)blocks), block(S::NT);
-    if (a.g) {
-        if (kVecShape && aligned) hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false, true>), grid, block, 0, s, a);
-    } else {
-        if (kVecShape && aligned) hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false, false>), grid, block, 0, s, a);
-    }
+    if (kVecShape && aligned) hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, kVecShape>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<T, DK, DV, CW, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

@@ -259,3 +259,18 @@ def test_graph_replay_matches_eager():
         for got, want, name in zip((o, fs, od, st), ref, ("o", "final_state", "decode o", "state")):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager call"
         _ = (o.float().sum() + 1).item()   # eager work between replays
+
+
+def test_decode_ungated_workload():
+    """The decode workload without a gate (the plain rule: 256 sequences x 32 heads, d128 bf16,
+    state in place)."""
+    _say("decode 256 x 32, no gate")
+    x = make_case(B=256, T=1, Hqk=32, Dk=128, dtype="bf16", init_std=0.02, seed=0, decode=True,
+                  name="decode_plain")
+    d = to_inputs(x)
+    state = d["init"].clone()
+    o = dn.decode_step(d["q"][:, 0], d["k"][:, 0], d["v"][:, 0], d["beta"][:, 0], None, state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(x)
+    _check(x, host(o)[:, None], host(state), o_ref=o_ref, s_ref=s_ref)
+
