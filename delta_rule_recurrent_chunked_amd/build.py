@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdeltanet.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-SOURCES = ["api.cpp", "decode.hip", "prefill_generic.hip", "prefill_fused.hip", "epilogue.hip",
+SOURCES = ["api.cpp", "decode.hip", "prefill_generic.hip", "prefill_fused.hip", "prefill_chg.hip",
+           "epilogue.hip",
            "recurrent.hip", "conv.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

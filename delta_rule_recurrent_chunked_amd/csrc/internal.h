@@ -113,6 +113,8 @@ hipError_t launch_norm_gate(const NormGateArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
 bool prefill_fused_supported(const PrefillArgs& a);
+bool prefill_chg_supported(const PrefillArgs& a);
+hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace dn

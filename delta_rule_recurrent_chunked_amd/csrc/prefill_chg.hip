@@ -1,0 +1,443 @@
+// prefill_chg.hip -- the chunked form with one log decay per key channel (the nnterp
+// "linear_attention" page's ChannelGates, the Kimi Delta Attention variant) on the
+// matrix cores, for bf16 q/k/v/o with Dk = 128, Dv a multiple of 32 and 64-token chunks.
+//
+// Key channel x of the state keeps exp(g_t[x]) at token t.  Inside one chunk, with
+// G_r[x] the sum of g over the chunk up to and including token r, the token-by-token
+// rule (decay, take up the pair, read) becomes, with M0 the chunk's start state:
+//
+//   A_ri = beta_r sum_x k_r[x] k_i[x] exp(G_r[x] - G_i[x])         (i < r)
+//   P_ri = sum_x q_r[x] k_i[x] exp(G_r[x] - G_i[x])                (i <= r)
+//   R    = diag(beta) (V - (K o e^G) M0)
+//   (I + A) Delta = R
+//   O    = scale ((Q o e^G) M0 + P Delta)
+//   M1   = diag(e^{G_last}) M0 + (K o e^{G_last - G})^T Delta
+//
+// A and P are plain products once the pairwise factor splits in two.  The chunk's tokens
+// form four blocks of 16; with Z_b the sum of g over the blocks before b, for r in block b
+// and i in block b' <= b,  exp(G_r - G_i) = exp(G_r - Z_b) exp(Z_b - G_i).  The first
+// factor is at most 1; so is the second when b' < b, and when b' = b it is at most
+// exp of block b's own decay.  The row operands k_r o exp(G_r - Z_b), q_r o exp(G_r - Z_b)
+// and the column operands k_i o exp(Z_b - G_i) (one set per row block) therefore stay in
+// range.  When some channel decays by more than e^60 within a block, that block's
+// diagonal tiles of A and P are formed from one exponential per pair and channel instead.
+// Every other operand (K o e^G, Q o e^G, K o e^{G_last - G}) has factors at most 1.
+//
+// One workgroup of four waves per (sequence, value head, 32 value columns).  Per chunk:
+//   1  every wave takes the g, k, q of one 16-token block (two channels per lane), sums g
+//      over the block and stages V and beta; the next chunk's loads are then issued
+//   2  operands into LDS (bf16); exact diagonal tiles for blocks that decay too fast
+//   3  A (waves 0, 1) and P (waves 2, 3) on the matrix cores, five 16x16 tiles each
+//   4  K o e^G and Q o e^G over the column operands; wave b inverts (I + A_bb)
+//   5  waves 0, 1 hold 16 state columns each in accumulators: X = (K o e^G) M0,
+//      R, Delta by block substitution; waves 2, 3 form (Q o e^G) M0;
+//      then waves 2, 3 add P Delta and store O, waves 0, 1 update the state.
+#include "internal.h"
+#include "mfma_ops.h"
+
+namespace dn {
+namespace {
+
+constexpr int CC = 64;          // tokens per chunk
+constexpr int NB = 4;           // 16-token blocks per chunk
+constexpr int HK = 128;         // key dim
+constexpr int SL = 32;          // value columns per workgroup
+constexpr int NTH = 256;
+constexpr int OP = 144;         // bf16 pitch of [token][key channel] tiles
+constexpr int AP = 80;          // bf16 pitch of A and P
+constexpr int TP = 24;          // bf16 pitch of the 16x16 inverses
+constexpr int VP = 40;          // bf16 pitch of the V slice
+constexpr int DP = 80;          // bf16 pitch of Delta^T
+constexpr float HARD = 60.f;    // in-block decay (nats) beyond which the diagonal tiles go exact
+constexpr float CLAMP = 80.f;   // cap of a diagonal column factor's exponent (hard blocks only)
+
+// Row offset, in the column-operand buffer, of the operand set of row block b (rows i < 16(b+1)).
+__device__ __forceinline__ int kc_off(int b) { return b == 0 ? 0 : b == 1 ? 16 : b == 2 ? 48 : 96; }
+
+struct ChgSmem {
+    __bf16 Kr[CC][OP];      // k_r o exp(G_r - Z_b(r))
+    __bf16 Qr[CC][OP];      // q_r o exp(G_r - Z_b(r))
+    __bf16 Kd[CC][OP];      // k_r o exp(G_last - G_r)
+    __bf16 Kc[160][OP];     // column operands of A and P; then K o e^G (0..63), Q o e^G (64..127)
+    __bf16 A[CC][AP];
+    __bf16 P[CC][AP];
+    float Ad[NB][16][17];   // A's diagonal tiles in fp32, for the inverses
+    __bf16 Tb[NB][16][TP];  // (I + A_bb)^-1
+    __bf16 V[CC][VP];
+    __bf16 Mt[SL][OP];      // the state slice, transposed (B operand of (Q o e^G) M0)
+    __bf16 Dt[SL][DP];      // Delta, transposed (B operand of P Delta)
+    float beta[CC];
+    float tot[NB][HK];      // per-block sums of g
+    float eg[HK];           // exp(G_last)
+    int hard[NB];
+};
+
+__device__ __forceinline__ float2 bf2_to_f2(uint32_t u) {
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+__device__ __forceinline__ void st2(__bf16* p, float a, float b) {
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// tile t of the ten lower 16x16 tiles of a 64x64 matrix -> (row block, column block);
+// even t: (0,0) (1,1) (2,1) (3,0) (3,2), odd t: (1,0) (2,0) (2,2) (3,1) (3,3)
+__device__ __forceinline__ void tile_of(int t, int& b, int& bp) {
+    b = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+    bp = t - (b * (b + 1)) / 2;
+}
+
+__global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
+    __shared__ __align__(16) ChgSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int Hv = a.Hv, Dv = a.Dv;
+    const int slices = Dv / SL;
+
+    // workgroup -> (sequence * Hv + head, slice); with a head count that is a multiple
+    // of 8 the slices of a head land on one XCD and share its k, q, g through that L2
+    const int heads = a.N * Hv;
+    int nh, slice;
+    if ((heads & 7) == 0) {
+        const int y = blockIdx.x >> 3;
+        slice = y % slices;
+        nh = (blockIdx.x & 7) + 8 * (y / slices);
+    } else {
+        slice = blockIdx.x % slices;
+        nh = blockIdx.x / slices;
+    }
+    const int h = nh % Hv, n = nh / Hv;
+    const int hq = h / (Hv / a.Hqk);
+    const int j0 = slice * SL;
+    const int u = w & 1;            // 16-column tile of the slice (waves 0, 1 and 2, 3)
+    const bool chain = w < 2;
+    const __bf16* qp = static_cast<const __bf16*>(a.q);
+    const __bf16* kp = static_cast<const __bf16*>(a.k);
+    const __bf16* vp = static_cast<const __bf16*>(a.v);
+    __bf16* op = static_cast<__bf16*>(a.o);
+
+    long bos, eos;
+    seq_range(a.cu, n, a.T, bos, eos);
+
+    // P's tiles above the diagonal that the output product reads stay zero
+    for (int e = tid; e < CC * AP; e += NTH) (&sm.P[0][0])[e] = (__bf16)0.f;
+
+    // state: chain wave u keeps rows 16t + 4 g4 + e, column 16u + l16 of the slice
+    f32x4 m[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = 16 * t + 4 * g4 + e;
+            m[t][e] = (chain && a.h0) ? a.h0[((long)nh * HK + x) * Dv + j0 + 16 * u + l16] : 0.f;
+        }
+        if (chain) st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], m[t][0], m[t][1], m[t][2], m[t][3]);
+    }
+
+    // raw inputs of one chunk: block w's tokens, key channels 2 lane and 2 lane + 1
+    float2 rg[16];
+    uint32_t rk[16], rq[16];
+    bf16x8 rv;
+    float rb;
+    auto fetch = [&](long c0) {
+        const long len = eos - c0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * w + i;
+            if (r < len) {
+                const long t = c0 + r;
+                rg[i] = *reinterpret_cast<const float2*>(a.g + (t * Hv + h) * HK + 2 * lane);
+                rk[i] = *reinterpret_cast<const uint32_t*>(kp + (t * a.Hqk + hq) * HK + 2 * lane);
+                rq[i] = *reinterpret_cast<const uint32_t*>(qp + (t * a.Hqk + hq) * HK + 2 * lane);
+            } else {
+                rg[i] = make_float2(0.f, 0.f);
+                rk[i] = 0u;
+                rq[i] = 0u;
+            }
+        }
+        const int vr = tid >> 2;
+        rv = vr < len ? *reinterpret_cast<const bf16x8*>(vp + ((c0 + vr) * Hv + h) * Dv + j0 + 8 * (tid & 3))
+                      : zero8();
+        rb = (tid < CC && tid < len) ? a.beta[(c0 + tid) * Hv + h] : 0.f;
+    };
+    fetch(bos);
+
+    for (long c0 = bos; c0 < eos; c0 += CC) {
+        const int len = (int)min((long)CC, eos - c0);
+
+        // ---- 1: block sums of g, k and q as floats (normalised if asked), V and beta
+        float2 L[16], kf[16], qf[16];
+        {
+            float2 s = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s.x += rg[i].x;
+                s.y += rg[i].y;
+                L[i] = s;
+                kf[i] = bf2_to_f2(rk[i]);
+                qf[i] = bf2_to_f2(rq[i]);
+            }
+            if (a.qk_norm) {
+                float nk[16], nq[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    nk[i] = kf[i].x * kf[i].x + kf[i].y * kf[i].y;
+                    nq[i] = qf[i].x * qf[i].x + qf[i].y * qf[i].y;
+                }
+#pragma unroll
+                for (int mm = 1; mm < 64; mm <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        nk[i] += __shfl_xor(nk[i], mm);
+                        nq[i] += __shfl_xor(nq[i], mm);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float ik = inv_norm(nk[i], a.eps), iq = inv_norm(nq[i], a.eps);
+                    kf[i].x *= ik;
+                    kf[i].y *= ik;
+                    qf[i].x *= iq;
+                    qf[i].y *= iq;
+                }
+            }
+            *reinterpret_cast<bf16x8*>(&sm.V[tid >> 2][8 * (tid & 3)]) = rv;
+            if (tid < CC) sm.beta[tid] = rb;
+            *reinterpret_cast<float2*>(&sm.tot[w][2 * lane]) = s;
+            const bool hb = __ballot(fminf(s.x, s.y) < -HARD) != 0;
+            if (lane == 0) sm.hard[w] = hb ? 1 : 0;
+        }
+        __syncthreads();
+
+        // ---- 2: operands
+        float2 Z[NB], Zw = make_float2(0.f, 0.f), Gl = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            Z[b] = Gl;
+            if (b == w) Zw = Gl;
+            const float2 tb = *reinterpret_cast<const float2*>(&sm.tot[b][2 * lane]);
+            Gl.x += tb.x;
+            Gl.y += tb.y;
+        }
+        uint32_t pke[16], pqe[16];  // K o e^G and Q o e^G, stored once the column operands are read
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * w + i;
+            const float ax = __expf(Zw.x + L[i].x), ay = __expf(Zw.y + L[i].y);
+            pke[i] = pack_bf16x2(kf[i].x * ax, kf[i].y * ay);
+            pqe[i] = pack_bf16x2(qf[i].x * ax, qf[i].y * ay);
+            const float ex = __expf(L[i].x), ey = __expf(L[i].y);
+            st2(&sm.Kr[r][2 * lane], kf[i].x * ex, kf[i].y * ey);
+            st2(&sm.Qr[r][2 * lane], qf[i].x * ex, qf[i].y * ey);
+            st2(&sm.Kd[r][2 * lane], kf[i].x * __expf(Gl.x - Zw.x - L[i].x),
+                kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b < w) continue;
+                float cx = Z[b].x - Zw.x - L[i].x, cy = Z[b].y - Zw.y - L[i].y;
+                if (b == w) {
+                    cx = fminf(cx, CLAMP);
+                    cy = fminf(cy, CLAMP);
+                }
+                st2(&sm.Kc[kc_off(b) + r][2 * lane], kf[i].x * __expf(cx), kf[i].y * __expf(cy));
+            }
+        }
+        if (w == 0) *reinterpret_cast<float2*>(&sm.eg[2 * lane]) = make_float2(__expf(Gl.x), __expf(Gl.y));
+        if (sm.hard[w]) {
+            // block w decays too fast for the factored diagonal tile: one exponential per
+            // (row, column, channel); the wave sums over its 128 channels.  Rare, so it
+            // runs over private copies rather than holding registers for the common path.
+            float2 hl[16], hk[16], hq[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                hl[i] = L[i];
+                hk[i] = kf[i];
+                hq[i] = qf[i];
+            }
+#pragma unroll 1
+            for (int r = 0; r < 16; ++r) {
+#pragma unroll 1
+                for (int i = 0; i < 16; ++i) {
+                    float pa = 0.f, pp = 0.f;
+                    if (i <= r) {
+                        const float dx = __expf(hl[r].x - hl[i].x), dy = __expf(hl[r].y - hl[i].y);
+                        pa = wave_sum(hk[r].x * hk[i].x * dx + hk[r].y * hk[i].y * dy);
+                        pp = wave_sum(hq[r].x * hk[i].x * dx + hq[r].y * hk[i].y * dy);
+                    }
+                    if (lane == 0) {
+                        const float av = i < r ? sm.beta[16 * w + r] * pa : 0.f;
+                        sm.A[16 * w + r][16 * w + i] = (__bf16)av;
+                        sm.Ad[w][r][i] = av;
+                        sm.P[16 * w + r][16 * w + i] = (__bf16)pp;
+                    }
+                }
+            }
+        }
+        fetch(c0 + CC);  // the next chunk's inputs land while this one is worked
+        __syncthreads();
+
+        // ---- 3: A (waves 0, 1) and P (waves 2, 3), five tiles per wave
+        {
+            const bool isP = w >= 2;
+#pragma unroll
+            for (int tt = 0; tt < 5; ++tt) {
+                int b, bp;
+                tile_of(2 * tt + u, b, bp);
+                if (b == bp && sm.hard[b]) continue;  // exact values are in place
+                const __bf16* rowp = isP ? &sm.Qr[16 * b + l16][8 * g4] : &sm.Kr[16 * b + l16][8 * g4];
+                const __bf16* colp = &sm.Kc[kc_off(b) + 16 * bp + l16][8 * g4];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma16(ld8(rowp + 32 * s), ld8(colp + 32 * s), acc);
+                const int i = 16 * bp + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * b + 4 * g4 + e;
+                    if (isP) {
+                        sm.P[r][i] = (__bf16)(i <= r ? acc[e] : 0.f);
+                    } else {
+                        const float av = i < r ? sm.beta[r] * acc[e] : 0.f;
+                        sm.A[r][i] = (__bf16)av;
+                        if (b == bp) sm.Ad[b][4 * g4 + e][l16] = av;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- 4: K o e^G and Q o e^G over the column operands; wave w inverts (I + A_ww)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            *reinterpret_cast<uint32_t*>(&sm.Kc[16 * w + i][2 * lane]) = pke[i];
+            *reinterpret_cast<uint32_t*>(&sm.Kc[CC + 16 * w + i][2 * lane]) = pqe[i];
+        }
+        if (lane < 16) {
+            // column `lane` of T: T[r][c] = delta_rc - sum_{i<r} A[r][i] T[i][c]
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = r == lane ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) s -= sm.Ad[w][r][i] * t[i];
+                t[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
+        }
+        __syncthreads();
+
+        // ---- 5a: chain waves: R and Delta; waves 2, 3: (Q o e^G) M0
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Y[NB] = {z4, z4, z4, z4};
+        bf16x8 d01 = zero8(), d23 = zero8();
+        if (chain) {
+            bf16x8 mb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mb[s] = acc_to_b(m[2 * s], m[2 * s + 1]);
+            f32x4 R[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 x = z4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) x = mma16(ld8(&sm.Kc[16 * b + l16][32 * s + 8 * g4]), mb[s], x);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * b + 4 * g4 + e;
+                    R[b][e] = sm.beta[r] * ((float)sm.V[r][16 * u + l16] - x[e]);
+                }
+            }
+            bf16x8 ta[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) ta[b] = g4 < 2 ? ld8(&sm.Tb[b][l16][8 * g4]) : zero8();
+            // Delta_b = T_bb (R_b - sum_{b'<b} A_bb' Delta_b')
+            const f32x4 D0 = mma16(ta[0], acc_to_b(R[0], z4), z4);
+            f32x4 c = mma16(ld8(&sm.A[16 + l16][8 * g4]), acc_to_b(D0, z4), z4);
+            const f32x4 D1 = mma16(ta[1], acc_to_b(R[1] - c, z4), z4);
+            d01 = acc_to_b(D0, D1);
+            c = mma16(ld8(&sm.A[32 + l16][8 * g4]), d01, z4);
+            const f32x4 D2 = mma16(ta[2], acc_to_b(R[2] - c, z4), z4);
+            c = mma16(ld8(&sm.A[48 + l16][8 * g4]), d01, z4);
+            c = mma16(ld8(&sm.A[48 + l16][32 + 8 * g4]), acc_to_b(D2, z4), c);
+            const f32x4 D3 = mma16(ta[3], acc_to_b(R[3] - c, z4), z4);
+            d23 = acc_to_b(D2, D3);
+            st4(&sm.Dt[16 * u + l16][4 * g4], D0[0], D0[1], D0[2], D0[3]);
+            st4(&sm.Dt[16 * u + l16][16 + 4 * g4], D1[0], D1[1], D1[2], D1[3]);
+            st4(&sm.Dt[16 * u + l16][32 + 4 * g4], D2[0], D2[1], D2[2], D2[3]);
+            st4(&sm.Dt[16 * u + l16][48 + 4 * g4], D3[0], D3[1], D3[2], D3[3]);
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 y = z4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    y = mma16(ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]),
+                              ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]), y);
+                Y[b] = y;
+            }
+        }
+        __syncthreads();
+
+        // ---- 5b: waves 2, 3: O = scale (Y + P Delta); chain waves: the state update
+        if (!chain) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 acc = Y[b];
+#pragma unroll
+                for (int s = 0; s <= b / 2; ++s)
+                    acc = mma16(ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]),
+                                ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]), acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * b + 4 * g4 + e;
+                    if (r < len) op[((c0 + r) * Hv + h) * Dv + j0 + 16 * u + l16] = (__bf16)(a.scale * acc[e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = m[t][e] * sm.eg[16 * t + 4 * g4 + e];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    // A operand (K o e^{G_last - G})^T: rows are key channels, read down columns
+                    const __bf16* base = &sm.Kd[32 * s + 8 * g4 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
+                    const bf16x8 ka = cat(trld(base), trld(base + 4 * OP));
+                    acc = mma16(ka, s ? d23 : d01, acc);
+                }
+                m[t] = acc;
+                st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (chain && a.hT) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.hT[((long)nh * HK + 16 * t + 4 * g4 + e) * Dv + j0 + 16 * u + l16] = m[t][e];
+    }
+}
+
+}  // namespace
+
+bool prefill_chg_supported(const PrefillArgs& a) {
+    const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.o;
+    return a.g_per_key && a.g && a.bf16 && a.Dk == HK && a.Dv >= SL && a.Dv % SL == 0 &&
+           a.C == CC && (al & 15) == 0 && ((uintptr_t)a.g & 7) == 0;
+}
+
+hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s) {
+    const long blocks = (long)a.N * a.Hv * (a.Dv / SL);
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (blocks > 0) hipLaunchKernelGGL(prefill_chg_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dn

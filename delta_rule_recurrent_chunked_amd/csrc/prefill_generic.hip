@@ -425,6 +425,7 @@ hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s) {
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (a.g_per_key) {
         if (!a.g) return hipErrorInvalidValue;
+        if (prefill_chg_supported(a)) return launch_prefill_chg(a, s);
         if (a.bf16)
             hipLaunchKernelGGL(prefill_channel_gate_kernel<__bf16>, dim3((unsigned)blocks), dim3(NT), 0, s, a);
         else

@@ -50,6 +50,19 @@ CASES = {
                            init_std=0.02),
     # decay strong enough that chunks fall below exp(-60): the per-pair exponential form
     "f32_strong_decay": dict(B=1, T=80, Hqk=2, Dk=32, dtype="f32", g_scale=5.0, init_std=0.3),
+    # the matrix-core kernel: 16-token blocks that decay by more than exp(-60) take exact
+    # diagonal tiles, the rest (and every block at the milder rate) the factored form
+    "bf16_d128_strong_decay": dict(B=1, T=300, Hqk=2, Dk=128, dtype="bf16", g_scale=3.0,
+                                   init_std=0.3),
+    "bf16_d128_every_block_exact": dict(B=1, T=100, Hqk=2, Dk=128, dtype="bf16", g_scale=5.0,
+                                        init_std=0.3),
+    "bf16_d128_mixed_decay": dict(B=2, T=200, Hqk=1, Hv=2, Dk=128, dtype="bf16", g_scale=0.9,
+                                  init_std=0.3, beta_scale=2.0),
+    "bf16_d128_dv64": dict(B=1, T=190, Hqk=2, Hv=2, Dk=128, Dv=64, dtype="bf16", g_scale=0.2,
+                           init_std=0.1),
+    # bf16 sizes the matrix-core kernel does not take run the vector-ALU kernel
+    "bf16_dk64_vector_path": dict(B=1, T=100, Hqk=2, Dk=64, Dv=64, dtype="bf16", g_scale=0.2,
+                                  init_std=0.1),
 }
 
 
@@ -67,6 +80,7 @@ def test_prefill_channel_gates(name):
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_channel_gates_chunk_sizes(chunk):
+    """The vector-ALU kernel at three chunk sizes (fp32, Dk = 64)."""
     _say(f"channel gates chunk {chunk}")
     x = make_case(B=1, T=100, Hqk=2, Dk=64, dtype="f32", g_scale=0.2, init_std=0.1, seed=22,
                   name=f"chunk{chunk}", g_per_key=True)
@@ -156,13 +170,27 @@ def test_decode_channel_gates_full_size():
 
 def test_prefill_channel_gates_packed_workload_sample():
     """Packed sequences with initial states and beta in (0, 2), as the 32K-token packed
-    workload has them, at 4 sequences of 1,900 tokens in all (the vector-ALU path)."""
+    workload has them, at 4 sequences of 1,900 tokens in all (the matrix-core kernel)."""
     _say("channel gates packed sample")
     x = make_case(B=1, Hqk=4, Hv=4, Dk=128, dtype="bf16", seqlens=[700, 1, 0, 1199],
                   g_scale=0.05, init_std=0.02, beta_scale=2.0, seed=27, name="packed_chg",
                   g_per_key=True)
     d = to_inputs(x)
     o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], cu_seqlens=d["cu"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o), host(s), o_ref, s_ref)
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_channel_gates_bf16_d128_chunk_choice(chunk):
+    """bf16 d128 at the default 64-token chunk takes the matrix-core kernel, at 32 the
+    vector-ALU one; both agree with the oracle."""
+    _say(f"channel gates bf16 d128 chunk {chunk}")
+    x = make_case(B=1, T=230, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.3, init_std=0.1,
+                  seed=28, name=f"bf16chunk{chunk}", g_per_key=True)
+    d = to_inputs(x)
+    o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], chunk_size=chunk)
     torch.cuda.synchronize()
     o_ref, s_ref = _oracle(x)
     _check(x, host(o), host(s), o_ref, s_ref)
