@@ -72,6 +72,11 @@ struct ChgSmem {
     int hard[NB];
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ float2 bf2_to_f2(uint32_t u) {
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
@@ -138,33 +143,34 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
         if (chain) st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], m[t][0], m[t][1], m[t][2], m[t][3]);
     }
 
-    // raw inputs of one chunk: block w's tokens, key channels 2 lane and 2 lane + 1
+    // raw inputs of one chunk: block w's tokens, key channels 2 lane and 2 lane + 1.  The
+    // buffer descriptors cover exactly this sequence's tokens, so loads past its end (the
+    // ragged last chunk, the chunk after the last) read zeros and every load is unconditional.
+    const long L = eos - bos;
+    const uint32_t g_tok = (uint32_t)Hv * HK * 4, kq_tok = (uint32_t)a.Hqk * HK * 2;
+    const uint32_t v_tok = (uint32_t)Hv * Dv * 2, b_tok = (uint32_t)Hv * 4;
+    const __amdgpu_buffer_rsrc_t gs = rsrc(a.g + (bos * Hv + h) * HK, L > 0 ? (L - 1) * g_tok + HK * 4 : 0);
+    const __amdgpu_buffer_rsrc_t ks = rsrc(kp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+    const __amdgpu_buffer_rsrc_t qs = rsrc(qp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+    const __amdgpu_buffer_rsrc_t vs = rsrc(vp + (bos * Hv + h) * Dv + j0, L > 0 ? (L - 1) * v_tok + SL * 2 : 0);
+    const __amdgpu_buffer_rsrc_t bs = rsrc(a.beta + bos * Hv + h, L > 0 ? (L - 1) * b_tok + 4 : 0);
     float2 rg[16];
     uint32_t rk[16], rq[16];
     bf16x8 rv;
     float rb;
-    auto fetch = [&](long c0) {
-        const long len = eos - c0;
+    auto fetch = [&](uint32_t c) {  // c: the chunk's first token, counted from the sequence start
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int r = 16 * w + i;
-            if (r < len) {
-                const long t = c0 + r;
-                rg[i] = *reinterpret_cast<const float2*>(a.g + (t * Hv + h) * HK + 2 * lane);
-                rk[i] = *reinterpret_cast<const uint32_t*>(kp + (t * a.Hqk + hq) * HK + 2 * lane);
-                rq[i] = *reinterpret_cast<const uint32_t*>(qp + (t * a.Hqk + hq) * HK + 2 * lane);
-            } else {
-                rg[i] = make_float2(0.f, 0.f);
-                rk[i] = 0u;
-                rq[i] = 0u;
-            }
+            const uint32_t r = c + 16 * w + i;
+            const u32x2 gv = __builtin_amdgcn_raw_buffer_load_b64(gs, r * g_tok + 8 * lane, 0, 0);
+            rg[i] = make_float2(__uint_as_float(gv[0]), __uint_as_float(gv[1]));
+            rk[i] = __builtin_amdgcn_raw_buffer_load_b32(ks, r * kq_tok + 4 * lane, 0, 0);
+            rq[i] = __builtin_amdgcn_raw_buffer_load_b32(qs, r * kq_tok + 4 * lane, 0, 0);
         }
-        const int vr = tid >> 2;
-        rv = vr < len ? *reinterpret_cast<const bf16x8*>(vp + ((c0 + vr) * Hv + h) * Dv + j0 + 8 * (tid & 3))
-                      : zero8();
-        rb = (tid < CC && tid < len) ? a.beta[(c0 + tid) * Hv + h] : 0.f;
+        rv = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vs, (c + (tid >> 2)) * v_tok + 16 * (tid & 3), 0, 0));
+        rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (c + (tid & 63)) * b_tok, 0, 0));
     };
-    fetch(bos);
+    fetch(0);
 
     for (long c0 = bos; c0 < eos; c0 += CC) {
         const int len = (int)min((long)CC, eos - c0);
@@ -224,30 +230,60 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
             Gl.y += tb.y;
         }
         uint32_t pke[16], pqe[16];  // K o e^G and Q o e^G, stored once the column operands are read
+        const bool hard = sm.hard[w] != 0;
+        if (!hard) {
+            // every factor from two exponentials per entry, e^{L} and e^{-L} (L the in-block
+            // sum, -L at most 60 here), and per-channel factors of at most 1
+            const float2 eZ = make_float2(__expf(Zw.x), __expf(Zw.y));
+            const float2 eD = make_float2(__expf(Gl.x - Zw.x), __expf(Gl.y - Zw.y));
+            float2 eF[NB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * w + i;
-            const float ax = __expf(Zw.x + L[i].x), ay = __expf(Zw.y + L[i].y);
-            pke[i] = pack_bf16x2(kf[i].x * ax, kf[i].y * ay);
-            pqe[i] = pack_bf16x2(qf[i].x * ax, qf[i].y * ay);
-            const float ex = __expf(L[i].x), ey = __expf(L[i].y);
-            st2(&sm.Kr[r][2 * lane], kf[i].x * ex, kf[i].y * ey);
-            st2(&sm.Qr[r][2 * lane], qf[i].x * ex, qf[i].y * ey);
-            st2(&sm.Kd[r][2 * lane], kf[i].x * __expf(Gl.x - Zw.x - L[i].x),
-                kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
+            for (int b = 0; b < NB; ++b) eF[b] = make_float2(__expf(Z[b].x - Zw.x), __expf(Z[b].y - Zw.y));
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (b < w) continue;
-                float cx = Z[b].x - Zw.x - L[i].x, cy = Z[b].y - Zw.y - L[i].y;
-                if (b == w) {
-                    cx = fminf(cx, CLAMP);
-                    cy = fminf(cy, CLAMP);
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * w + i;
+                const float e1x = __expf(L[i].x), e1y = __expf(L[i].y);
+                const float e2x = __expf(-L[i].x), e2y = __expf(-L[i].y);
+                const float kx = kf[i].x * e1x, ky = kf[i].y * e1y, qx = qf[i].x * e1x, qy = qf[i].y * e1y;
+                st2(&sm.Kr[r][2 * lane], kx, ky);
+                st2(&sm.Qr[r][2 * lane], qx, qy);
+                pke[i] = pack_bf16x2(kx * eZ.x, ky * eZ.y);
+                pqe[i] = pack_bf16x2(qx * eZ.x, qy * eZ.y);
+                const float cx = kf[i].x * e2x, cy = kf[i].y * e2y;
+                st2(&sm.Kd[r][2 * lane], cx * eD.x, cy * eD.y);
+                st2(&sm.Kc[kc_off(w) + r][2 * lane], cx, cy);
+#pragma unroll
+                for (int b = 1; b < NB; ++b)
+                    if (b > w) st2(&sm.Kc[kc_off(b) + r][2 * lane], cx * eF[b].x, cy * eF[b].y);
+            }
+        } else {
+            // one exponential per factor, each of a difference that is at most 0 (the
+            // diagonal column factor, replaced below, is capped)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * w + i;
+                const float ax = __expf(Zw.x + L[i].x), ay = __expf(Zw.y + L[i].y);
+                pke[i] = pack_bf16x2(kf[i].x * ax, kf[i].y * ay);
+                pqe[i] = pack_bf16x2(qf[i].x * ax, qf[i].y * ay);
+                const float ex = __expf(L[i].x), ey = __expf(L[i].y);
+                st2(&sm.Kr[r][2 * lane], kf[i].x * ex, kf[i].y * ey);
+                st2(&sm.Qr[r][2 * lane], qf[i].x * ex, qf[i].y * ey);
+                st2(&sm.Kd[r][2 * lane], kf[i].x * __expf(Gl.x - Zw.x - L[i].x),
+                    kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < w) continue;
+                    float cx = Z[b].x - Zw.x - L[i].x, cy = Z[b].y - Zw.y - L[i].y;
+                    if (b == w) {
+                        cx = fminf(cx, CLAMP);
+                        cy = fminf(cy, CLAMP);
+                    }
+                    st2(&sm.Kc[kc_off(b) + r][2 * lane], kf[i].x * __expf(cx), kf[i].y * __expf(cy));
                 }
-                st2(&sm.Kc[kc_off(b) + r][2 * lane], kf[i].x * __expf(cx), kf[i].y * __expf(cy));
             }
         }
         if (w == 0) *reinterpret_cast<float2*>(&sm.eg[2 * lane]) = make_float2(__expf(Gl.x), __expf(Gl.y));
-        if (sm.hard[w]) {
+        if (hard) {
             // block w decays too fast for the factored diagonal tile: one exponential per
             // (row, column, channel); the wave sums over its 128 channels.  Rare, so it
             // runs over private copies rather than holding registers for the common path.
@@ -277,7 +313,7 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
                 }
             }
         }
-        fetch(c0 + CC);  // the next chunk's inputs land while this one is worked
+        fetch((uint32_t)(c0 + CC - bos));  // the next chunk's inputs land while this one is worked
         __syncthreads();
 
         // ---- 3: A (waves 0, 1) and P (waves 2, 3), five tiles per wave
@@ -429,8 +465,12 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
 
 bool prefill_chg_supported(const PrefillArgs& a) {
     const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.o;
+    // buffer offsets are 32-bit: a sequence plus the chunk fetched past its end must span
+    // less than 2 GiB of every stream (g, fp32 per key channel, is the widest)
+    const int hmax = a.Hqk > a.Hv ? a.Hqk : a.Hv;
+    const long span = ((long)a.T + 2 * CC) * hmax * (HK * 4 > a.Dv * 2 ? HK * 4 : a.Dv * 2);
     return a.g_per_key && a.g && a.bf16 && a.Dk == HK && a.Dv >= SL && a.Dv % SL == 0 &&
-           a.C == CC && (al & 15) == 0 && ((uintptr_t)a.g & 7) == 0;
+           a.C == CC && (al & 15) == 0 && ((uintptr_t)a.g & 7) == 0 && span < (1L << 31);
 }
 
 hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s) {
