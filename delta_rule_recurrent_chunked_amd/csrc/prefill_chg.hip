@@ -26,9 +26,11 @@
 // One workgroup of four waves per (sequence, value head, 32 value columns).  Per chunk:
 //   1  every wave takes the g, k, q of one 16-token block (two channels per lane), sums g
 //      over the block and stages V and beta; the next chunk's loads are then issued
-//   2  operands into LDS (bf16); exact diagonal tiles for blocks that decay too fast
-//   3  A (waves 0, 1) and P (waves 2, 3) on the matrix cores, five 16x16 tiles each
-//   4  K o e^G and Q o e^G over the column operands; wave b inverts (I + A_bb)
+//   2  operands into LDS (bf16); wave b forms block b's diagonal tiles of A and P from
+//      the rows it wrote (exactly, per pair, for blocks that decay too fast) and inverts
+//      (I + A_bb)
+//   3  A (waves 0, 1) and P (waves 2, 3) below the diagonal on the matrix cores
+//   4  K o e^G and Q o e^G over the column operands
 //   5  waves 0, 1 hold 16 state columns each in accumulators: X = (K o e^G) M0,
 //      R, Delta by block substitution; waves 2, 3 form (Q o e^G) M0;
 //      then waves 2, 3 add P Delta and store O, waves 0, 1 update the state.
@@ -61,7 +63,7 @@ struct ChgSmem {
     __bf16 Kc[160][OP];     // column operands of A and P; then K o e^G (0..63), Q o e^G (64..127)
     __bf16 A[CC][AP];
     __bf16 P[CC][AP];
-    float Ad[NB][16][17];   // A's diagonal tiles in fp32, for the inverses
+    float Ad[NB][16][20];   // A's diagonal tiles in fp32, for the inverses (16-byte rows)
     __bf16 Tb[NB][16][TP];  // (I + A_bb)^-1
     __bf16 V[CC][VP];
     __bf16 Mt[SL][OP];      // the state slice, transposed (B operand of (Q o e^G) M0)
@@ -89,11 +91,11 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// tile t of the ten lower 16x16 tiles of a 64x64 matrix -> (row block, column block);
-// even t: (0,0) (1,1) (2,1) (3,0) (3,2), odd t: (1,0) (2,0) (2,2) (3,1) (3,3)
-__device__ __forceinline__ void tile_of(int t, int& b, int& bp) {
-    b = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-    bp = t - (b * (b + 1)) / 2;
+// tile t of the six 16x16 tiles below the diagonal of a 64x64 matrix -> (row block,
+// column block): (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+__device__ __forceinline__ void offdiag_tile(int t, int& b, int& bp) {
+    b = t < 1 ? 1 : t < 3 ? 2 : 3;
+    bp = t - (b * (b - 1)) / 2;
 }
 
 __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
@@ -283,7 +285,26 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
             }
         }
         if (w == 0) *reinterpret_cast<float2*>(&sm.eg[2 * lane]) = make_float2(__expf(Gl.x), __expf(Gl.y));
-        if (hard) {
+        if (!hard) {
+            // block w's diagonal tiles of A and P from the rows this wave has just written
+            wave_lds_order();
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 kc = ld8(&sm.Kc[kc_off(w) + 16 * w + l16][32 * s + 8 * g4]);
+                aa = mma16(ld8(&sm.Kr[16 * w + l16][32 * s + 8 * g4]), kc, aa);
+                pa = mma16(ld8(&sm.Qr[16 * w + l16][32 * s + 8 * g4]), kc, pa);
+            }
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * g4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                const float av = l16 < r ? bt[e] * aa[e] : 0.f;
+                sm.A[16 * w + r][16 * w + l16] = (__bf16)av;
+                sm.Ad[w][r][l16] = av;
+                sm.P[16 * w + r][16 * w + l16] = (__bf16)(l16 <= r ? pa[e] : 0.f);
+            }
+        } else {
             // block w decays too fast for the factored diagonal tile: one exponential per
             // (row, column, channel); the wave sums over its 128 channels.  Rare, so it
             // runs over private copies rather than holding registers for the common path.
@@ -313,56 +334,57 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
                 }
             }
         }
+        // (I + A_ww)^-1 by forward substitution, lane c < 16 solving column c in fp32
+        wave_lds_order();
+        if (lane < 16) {
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float sacc = r == lane ? 1.f : 0.f;
+#pragma unroll
+                for (int i4 = 0; i4 < r; i4 += 4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.Ad[w][r][i4]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (i4 + j < r) sacc -= av[j] * t[i4 + j];
+                }
+                t[r] = sacc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
+        }
         fetch((uint32_t)(c0 + CC - bos));  // the next chunk's inputs land while this one is worked
         __syncthreads();
 
-        // ---- 3: A (waves 0, 1) and P (waves 2, 3), five tiles per wave
+        // ---- 3: A (waves 0, 1) and P (waves 2, 3) below the diagonal, three tiles per wave
         {
             const bool isP = w >= 2;
 #pragma unroll
-            for (int tt = 0; tt < 5; ++tt) {
+            for (int tt = 0; tt < 3; ++tt) {
                 int b, bp;
-                tile_of(2 * tt + u, b, bp);
-                if (b == bp && sm.hard[b]) continue;  // exact values are in place
+                offdiag_tile(2 * tt + u, b, bp);
                 const __bf16* rowp = isP ? &sm.Qr[16 * b + l16][8 * g4] : &sm.Kr[16 * b + l16][8 * g4];
                 const __bf16* colp = &sm.Kc[kc_off(b) + 16 * bp + l16][8 * g4];
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) acc = mma16(ld8(rowp + 32 * s), ld8(colp + 32 * s), acc);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * b + 4 * g4]);
                 const int i = 16 * bp + l16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * b + 4 * g4 + e;
-                    if (isP) {
-                        sm.P[r][i] = (__bf16)(i <= r ? acc[e] : 0.f);
-                    } else {
-                        const float av = i < r ? sm.beta[r] * acc[e] : 0.f;
-                        sm.A[r][i] = (__bf16)av;
-                        if (b == bp) sm.Ad[b][4 * g4 + e][l16] = av;
-                    }
+                    if (isP) sm.P[r][i] = (__bf16)acc[e];
+                    else sm.A[r][i] = (__bf16)(bt[e] * acc[e]);
                 }
             }
         }
         __syncthreads();
 
-        // ---- 4: K o e^G and Q o e^G over the column operands; wave w inverts (I + A_ww)
+        // ---- 4: K o e^G and Q o e^G over the column operands
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             *reinterpret_cast<uint32_t*>(&sm.Kc[16 * w + i][2 * lane]) = pke[i];
             *reinterpret_cast<uint32_t*>(&sm.Kc[CC + 16 * w + i][2 * lane]) = pqe[i];
-        }
-        if (lane < 16) {
-            // column `lane` of T: T[r][c] = delta_rc - sum_{i<r} A[r][i] T[i][c]
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = r == lane ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 0; i < r; ++i) s -= sm.Ad[w][r][i] * t[i];
-                t[r] = s;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
         }
         __syncthreads();
 
