@@ -307,7 +307,7 @@ def main():
     cs = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
     dn.chunk_fwd(cq, ck, cv, cb, cgp, None, out=co, final_state=cs)
     torch.cuda.synchronize()
-    creps = 3
+    creps = 10
     ev0.record(stream)
     for _ in range(creps):
         dn.chunk_fwd(cq, ck, cv, cb, cgp, None, out=co, final_state=cs)

@@ -63,7 +63,7 @@ struct ChgSmem {
     __bf16 Kc[160][OP];     // column operands of A and P; then K o e^G (0..63), Q o e^G (64..127)
     __bf16 A[CC][AP];
     __bf16 P[CC][AP];
-    float Ad[NB][16][20];   // A's diagonal tiles in fp32, for the inverses (16-byte rows)
+    float Ad[NB][16][20];   // A's diagonal tiles in fp32, transposed ([column][row]), for the inverses
     __bf16 Tb[NB][16][TP];  // (I + A_bb)^-1
     __bf16 V[CC][VP];
     __bf16 Mt[SL][OP];      // the state slice, transposed (B operand of (Q o e^G) M0)
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
                 const int r = 4 * g4 + e;
                 const float av = l16 < r ? bt[e] * aa[e] : 0.f;
                 sm.A[16 * w + r][16 * w + l16] = (__bf16)av;
-                sm.Ad[w][r][l16] = av;
+                sm.Ad[w][l16][r] = av;
                 sm.P[16 * w + r][16 * w + l16] = (__bf16)(l16 <= r ? pa[e] : 0.f);
             }
         } else {
@@ -328,27 +328,28 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
                     if (lane == 0) {
                         const float av = i < r ? sm.beta[16 * w + r] * pa : 0.f;
                         sm.A[16 * w + r][16 * w + i] = (__bf16)av;
-                        sm.Ad[w][r][i] = av;
+                        sm.Ad[w][i][r] = av;
                         sm.P[16 * w + r][16 * w + i] = (__bf16)pp;
                     }
                 }
             }
         }
-        // (I + A_ww)^-1 by forward substitution, lane c < 16 solving column c in fp32
+        // (I + A_ww)^-1 by forward substitution, lane c < 16 solving column c in fp32; once
+        // row i is final it is taken out of every later row at once (independent updates)
         wave_lds_order();
         if (lane < 16) {
             float t[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float sacc = r == lane ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) t[r] = r == lane ? 1.f : 0.f;
 #pragma unroll
-                for (int i4 = 0; i4 < r; i4 += 4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.Ad[w][r][i4]);
+            for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                for (int r4 = (i + 1) & ~3; r4 < 16; r4 += 4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.Ad[w][i][r4]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (i4 + j < r) sacc -= av[j] * t[i4 + j];
+                        if (r4 + j > i) t[r4 + j] -= av[j] * t[i];
                 }
-                t[r] = sacc;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
