@@ -194,3 +194,17 @@ def test_channel_gates_bf16_d128_chunk_choice(chunk):
     torch.cuda.synchronize()
     o_ref, s_ref = _oracle(x)
     _check(x, host(o), host(s), o_ref, s_ref)
+
+
+def test_prefill_channel_gates_layer_workload():
+    """The layer-prefill workload (B4 H16 T2048 d128 bf16) with a log decay per key channel
+    and an initial state, in the launch configuration the benchmark times: every output and
+    final state against the oracle."""
+    _say("channel gates prefill B4 H16 T2048")
+    x = make_case(B=4, T=2048, Hqk=16, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
+                  seed=0, name="layer_chg", g_per_key=True)
+    d = to_inputs(x)
+    o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o), host(s), o_ref, s_ref)
