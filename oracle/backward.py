@@ -20,7 +20,9 @@ G = dL/dM_t (chain rule on each line above):
     G'    = G - beta_t k_t dd^T        (dL/dM'_t)
     dg_t  = <G', M'_t>,                G <- a_t G'   (dL/dM_{t-1})
 
-and dL/dM_0 is G after the first token.  Value head h reads query/key head h / (Hv/Hqk):
+and dL/dM_0 is G after the first token.  With a log decay per key channel (the nnterp
+page's ChannelGates), a_t is a vector over the rows of M: M'_t = diag(a_t) M_{t-1}, and
+the same chain rule gives dg_t[i] = sum_j G'[i, j] M'_t[i, j] and G <- diag(a_t) G'.  Value head h reads query/key head h / (Hv/Hqk):
 dq and dk are summed over the value heads that share a query/key head.
 """
 from __future__ import annotations
@@ -34,9 +36,10 @@ __all__ = ["backward"]
 
 def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: float = 1.0):
     """Gradients of the rule.  Shapes as ``oracle.recurrent`` (q, k ``[B, T, Hqk, Dk]``, v
-    ``[B, T, Hv, Dv]``, beta, g ``[B, T, Hv]`` or g None, init ``[N, Hv, Dk, Dv]`` or None),
-    do ``[B, T, Hv, Dv]``, dfinal ``[N, Hv, Dk, Dv]`` or None.  Returns a dict of fp64
-    arrays dq, dk, dv, dbeta, dg (None without g), dinit."""
+    ``[B, T, Hv, Dv]``, beta ``[B, T, Hv]``, g ``[B, T, Hv]``, ``[B, T, Hv, Dk]`` (a log
+    decay per key channel) or None, init ``[N, Hv, Dk, Dv]`` or None), do ``[B, T, Hv, Dv]``,
+    dfinal ``[N, Hv, Dk, Dv]`` or None.  Returns a dict of fp64 arrays dq, dk, dv, dbeta,
+    dg (g's shape; None without g), dinit."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     beta, do = np.asarray(beta, dtype=np.float64), np.asarray(do, dtype=np.float64)
     B, T, Hqk, Dk = q.shape
@@ -47,7 +50,11 @@ def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: fl
     fl = lambda a, *tail: a.reshape((B * T,) + tail)
     qf, kf, vf = fl(q, Hqk, Dk), fl(k, Hqk, Dk), fl(v, Hv, Dv)
     bf, df = fl(beta, Hv), fl(do, Hv, Dv)
-    gf = None if g is None else fl(np.asarray(g, dtype=np.float64), Hv)
+    per_key = g is not None and np.ndim(g) == 4
+    gshape = None if g is None else np.shape(g)
+    gf = None if g is None else (fl(np.asarray(g, dtype=np.float64), Hv, Dk) if per_key
+                                 else fl(np.asarray(g, dtype=np.float64), Hv))
+    rows = (lambda a: a[:, None]) if per_key else (lambda a: a)   # decay of each row of M
     dq, dk = np.zeros_like(qf), np.zeros_like(kf)
     dv, dbeta = np.zeros_like(vf), np.zeros_like(bf)
     dg = None if g is None else np.zeros_like(gf)
@@ -58,7 +65,7 @@ def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: fl
             M = np.zeros((Dk, Dv)) if init is None else np.array(init[n, h], dtype=np.float64)
             Ms, Mp = [], []                     # M_t and M'_t of each token (forward)
             for t in range(cu[n], cu[n + 1]):
-                a = 1.0 if gf is None else np.exp(gf[t, h])
+                a = 1.0 if gf is None else rows(np.exp(gf[t, h]))
                 Mpt = a * M
                 r = Mpt.T @ kf[t, hq]
                 M = Mpt + np.outer(kf[t, hq], bf[t, h] * (vf[t, h] - r))
@@ -77,12 +84,12 @@ def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: fl
                 dbeta[t, h] = dd @ (vf[t, h] - r)
                 dk[t, hq] += G @ delta - bf[t, h] * (Mpt @ dd)
                 Gp = G - bf[t, h] * np.outer(kt, dd)
-                a = 1.0 if gf is None else np.exp(gf[t, h])
+                a = 1.0 if gf is None else rows(np.exp(gf[t, h]))
                 if dg is not None:
-                    dg[t, h] = np.sum(Gp * Mpt)
+                    dg[t, h] = np.sum(Gp * Mpt, axis=1) if per_key else np.sum(Gp * Mpt)
                 G = a * Gp
             dinit[n, h] = G
     out = dict(dq=dq.reshape(q.shape), dk=dk.reshape(k.shape), dv=dv.reshape(v.shape),
-               dbeta=dbeta.reshape(beta.shape), dg=None if dg is None else dg.reshape(beta.shape),
+               dbeta=dbeta.reshape(beta.shape), dg=None if dg is None else dg.reshape(gshape),
                dinit=dinit)
     return out

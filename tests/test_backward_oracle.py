@@ -2,18 +2,19 @@
 the fp64 oracle's loss, and torch autograd through a plain PyTorch statement of the
 product form (CPU only)."""
 import numpy as np
+import pytest
 import torch
 
 import oracle
 from oracle.backward import backward
 
 
-def _case(rng, B=1, T=7, Hqk=1, Hv=2, Dk=3, Dv=4, N_lens=None):
+def _case(rng, B=1, T=7, Hqk=1, Hv=2, Dk=3, Dv=4, N_lens=None, per_key=False):
     q = rng.standard_normal((B, T, Hqk, Dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
     k = rng.standard_normal((B, T, Hqk, Dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
     v = rng.standard_normal((B, T, Hv, Dv))
     beta = rng.uniform(0.1, 1.9, (B, T, Hv))
-    g = -rng.uniform(0.0, 0.5, (B, T, Hv))
+    g = -rng.uniform(0.0, 0.5, (B, T, Hv, Dk) if per_key else (B, T, Hv))
     return q, k, v, beta, g
 
 
@@ -22,14 +23,15 @@ def _loss(fwd_out, do, dfin):
     return float(np.sum(o * do) + np.sum(fin * dfin))
 
 
-def test_finite_differences_packed_gqa():
+@pytest.mark.parametrize("per_key", [False, True])
+def test_finite_differences_packed_gqa(per_key):
     """Every input of a packed GQA case, central differences of L = <o, do> + <M_T, dM_T>
-    through the oracle of record (dn_oracle.c)."""
+    through the oracle of record (dn_oracle.c); one log decay per head, or per key channel."""
     rng = np.random.default_rng(1)
     lens = [4, 0, 5]
     T = sum(lens)
     cu = np.concatenate([[0], np.cumsum(lens)])
-    q, k, v, beta, g = _case(rng, T=T)
+    q, k, v, beta, g = _case(rng, T=T, per_key=per_key)
     init = rng.standard_normal((len(lens), 2, 3, 4))
     do = rng.standard_normal(v.shape)
     dfin = rng.standard_normal(init.shape)
@@ -79,3 +81,27 @@ def test_torch_autograd_of_the_product_form():
         np.testing.assert_allclose(grads["dbeta"], tb.grad.numpy(), rtol=1e-10, atol=1e-12)
         if gated:
             np.testing.assert_allclose(grads["dg"], tg.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_torch_autograd_of_the_product_form_channel_gates():
+    """Autograd through S_t = S_{t-1} diag(e^{g_t}) (I - beta k k^T) + beta v k^T, o_t = S_t
+    q_t, with a log decay per key channel (fp64 torch matrices)."""
+    rng = np.random.default_rng(3)
+    q, k, v, beta, g = _case(rng, B=2, T=6, Hqk=2, Hv=2, Dk=4, Dv=3, per_key=True)
+    do = rng.standard_normal(v.shape)
+    dfin = rng.standard_normal((2, 2, 4, 3))
+    tq, tk, tv, tb, tg = (torch.tensor(a, requires_grad=True) for a in (q, k, v, beta, g))
+    loss = 0.0
+    for b in range(2):
+        for h in range(2):
+            S = torch.zeros(3, 4, dtype=torch.float64)
+            for t in range(6):
+                kt = tk[b, t, h][:, None]
+                S = S @ torch.diag(torch.exp(tg[b, t, h]))
+                S = S @ (torch.eye(4, dtype=torch.float64) - tb[b, t, h] * (kt @ kt.T)) + tb[b, t, h] * (tv[b, t, h][:, None] @ kt.T)
+                loss = loss + (S @ tq[b, t, h]) @ torch.tensor(do[b, t, h])
+            loss = loss + torch.sum(S.T * torch.tensor(dfin[b, h]))
+    loss.backward()
+    grads = backward(q, k, v, beta, g, None, do, dfin)
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv), ("dbeta", tb), ("dg", tg)):
+        np.testing.assert_allclose(grads[name], t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
