@@ -291,15 +291,14 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
     """Reverse pass of the rule: gradients of a loss with dL/do = ``d_o`` and dL/d final
     state = ``d_final_state`` for q, k, v, beta, g and the initial state, from the state
     trace that :func:`recurrent_fwd` returned for the same inputs (``state_trace=True``).
-    One gate per head or none.  Returns a dict of float32 tensors dq, dk (``[B, T, Hqk,
-    Dk]``), dv, dbeta, dg (None without g) and d_initial_state."""
+    One gate per head (g ``[B, T, Hv]``), one per key channel (g ``[B, T, Hv, Dk]``) or
+    none.  Returns a dict of float32 tensors dq, dk (``[B, T, Hqk, Dk]``), dv, dbeta, dg
+    (g's shape; None without g) and d_initial_state."""
     lib = load_library()
     shape, _, _, N = _prompt_args(q, k, v, beta, g, initial_state, False, cu_seqlens, scale, 64,
                                   None, None, True, False, 1e-6)
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
-    if g is not None and g.dim() != 3:
-        raise NotImplementedError("the reverse pass takes one gate per head")
     _dev(state_trace, "state_trace", torch.float32, (B, T, Hv, Dk, Dv))
     _dev(d_o, "d_o", q.dtype, (B, T, Hv, Dv))
     if d_final_state is not None:
@@ -308,7 +307,7 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((B, T, Hqk, Dk), **f32), dk=torch.empty((B, T, Hqk, Dk), **f32),
                dv=torch.empty((B, T, Hv, Dv), **f32), dbeta=torch.empty((B, T, Hv), **f32),
-               dg=torch.empty((B, T, Hv), **f32) if g is not None else None,
+               dg=torch.empty(tuple(g.shape), **f32) if g is not None else None,
                d_initial_state=torch.empty((N, Hv, Dk, Dv), **f32))
     need = int(lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(shape)))
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None

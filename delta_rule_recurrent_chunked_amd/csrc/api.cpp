@@ -191,7 +191,10 @@ size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* s) {
     dn::PrefillArgs a;
     const bool packed = s && s->B == 1 && s->num_seqs != 1;
     if (prefill_shape(s, packed, a) != DN_OK) return 0;
-    return (size_t)dn::recurrent_bwd_slices(s->Dv) * s->B * s->T * s->Hv * (2 * s->Dk + 2) * sizeof(float);
+    // dq, dk shares [slices, tokens, Hv, Dk]; dbeta [slices, tokens, Hv]; dg [slices, tokens,
+    // Hv] or, with a decay per key channel, [slices, tokens, Hv, Dk]
+    const size_t per = (s->flags & DN_GATE_PER_KEY) ? 3 * (size_t)s->Dk + 1 : 2 * (size_t)s->Dk + 2;
+    return (size_t)dn::recurrent_bwd_slices(s->Dv) * s->B * s->T * s->Hv * per * sizeof(float);
 }
 
 dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, const void* v,
@@ -202,7 +205,8 @@ dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, cons
     dn::RecurrentBwdArgs a{};
     dn_status st = prefill_shape(s, cu != nullptr, a);
     if (st != DN_OK) return st;
-    if (a.qk_norm || a.g_per_key) return DN_ERR_UNSUPPORTED;
+    if (a.qk_norm) return DN_ERR_UNSUPPORTED;
+    if (a.g_per_key && !g) return DN_ERR_INVALID_ARG;
     const long tokens = (long)s->B * s->T;
     if (tokens > 0 && (!q || !k || !v || !beta || !trace || !dout || !dq || !dk || !dv || !dbeta ||
                        (g && !dg)))
@@ -218,7 +222,8 @@ dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, cons
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.h0 = h0; a.cu = cu;
     a.trace = trace; a.dout = dout; a.dfinal = dfinal;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = g ? dg : nullptr; a.dh0 = dh0;
-    // the slices' shares: dq, dk [slices, tokens, Hv, Dk], then dbeta, dg [slices, tokens, Hv]
+    // the slices' shares: dq, dk [slices, tokens, Hv, Dk], then dbeta [slices, tokens, Hv],
+    // then dg ([slices, tokens, Hv], or [slices, tokens, Hv, Dk] with a decay per key channel)
     const size_t qk = (size_t)dn::recurrent_bwd_slices(s->Dv) * tokens * s->Hv * s->Dk;
     const size_t sc = (size_t)dn::recurrent_bwd_slices(s->Dv) * tokens * s->Hv;
     a.ws_dq = static_cast<float*>(ws);

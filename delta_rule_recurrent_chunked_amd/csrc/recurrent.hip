@@ -182,7 +182,8 @@ template <typename T, int DK, int CW>
 struct BwdIn {
     float m[RecShape<DK, CW>::RPT][4];   // M_{t-1} (this thread's block)
     float k[RecShape<DK, CW>::RPT], q[RecShape<DK, CW>::RPT];
-    float v, dout, beta, g;
+    float g[RecShape<DK, CW>::RPT];      // log decay of each of the thread's rows
+    float v, dout, beta;
 };
 
 template <typename T, int DK, int DV, int CW>
@@ -209,7 +210,9 @@ __device__ __forceinline__ void bwd_fetch(const RecurrentBwdArgs& a, long t, lon
     f.v = ld_f32(static_cast<const T*>(a.v), vo);
     f.dout = ld_f32(static_cast<const T*>(a.dout), vo);
     f.beta = a.beta[t * a.Hv + h];
-    f.g = a.g ? a.g[t * a.Hv + h] : 0.f;
+#pragma unroll
+    for (int p = 0; p < RPT; ++p)
+        f.g[p] = !a.g ? 0.f : a.g_per_key ? a.g[(t * a.Hv + h) * (long)DK + row0 + p] : a.g[t * a.Hv + h];
 }
 
 template <typename T, int DK, int DV, int CW>
@@ -256,13 +259,15 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
     if (eos > bos) bwd_fetch<T, DK, DV, CW>(a, eos - 1, bos, nh, h, hq, row0, ct, tid, j0, cur);
     for (long t = eos - 1; t >= bos; --t) {
         if (t - 1 >= bos) bwd_fetch<T, DK, DV, CW>(a, t - 1, bos, nh, h, hq, row0, ct, tid, j0, nxt);
-        const float al = a.g ? expf(cur.g) : 1.f;
+        float al[RPT];
+#pragma unroll
+        for (int p = 0; p < RPT; ++p) al[p] = a.g ? expf(cur.g[p]) : 1.f;
         const float beta = cur.beta;
         float Mp[RPT][4];
 #pragma unroll
         for (int p = 0; p < RPT; ++p)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Mp[p][e] = al * cur.m[p][e];
+            for (int e = 0; e < 4; ++e) Mp[p][e] = al[p] * cur.m[p][e];
         // r = M'^T k
         float c[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -318,17 +323,19 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
         float ddv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ddv[e] = vec_dd[ct * 4 + e];
-        // dk = G delta - beta M' dd;  G' = G - beta k dd^T;  dg = <G', M'>;  G <- a G'
-        float dkp[RPT], dgp = 0.f;
+        // dk = G delta - beta M' dd;  G' = G - beta k dd^T;  dg = <G', M'> (per row of M' with
+        // a decay per key channel);  G <- diag(a) G'
+        float dkp[RPT], dgr[RPT];
 #pragma unroll
         for (int p = 0; p < RPT; ++p) {
             dkp[p] = 0.f;
+            dgr[p] = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 dkp[p] += G[p][e] * dl[e] - beta * Mp[p][e] * ddv[e];
                 G[p][e] -= beta * cur.k[p] * ddv[e];
-                dgp += G[p][e] * Mp[p][e];
-                G[p][e] *= al;
+                dgr[p] += G[p][e] * Mp[p][e];
+                G[p][e] *= al[p];
             }
         }
 #pragma unroll
@@ -342,13 +349,26 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
                 dk[p] = dkp[p];
             }
         }
+        if (a.g_per_key) {   // this slice's share of dg for the thread's rows
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) dgp += __shfl_xor(dgp, off);
-        if (lane == 0) atomicAdd(&acc2[1], dgp);
+            for (int p = 0; p < RPT; ++p) rowsum(dgr[p]);
+            if (ct == 0) {
+                float* dg = a.ws_dg + ((slice * tokens + t) * a.Hv + h) * (long)DK + row0;
+#pragma unroll
+                for (int p = 0; p < RPT; ++p) dg[p] = dgr[p];
+            }
+        } else {
+            float dgp = 0.f;
+#pragma unroll
+            for (int p = 0; p < RPT; ++p) dgp += dgr[p];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) dgp += __shfl_xor(dgp, off);
+            if (lane == 0) atomicAdd(&acc2[1], dgp);
+        }
         __syncthreads();
         if (tid == 0) {
             a.ws_db[(slice * tokens + t) * a.Hv + h] = acc2[0];
-            a.ws_dg[(slice * tokens + t) * a.Hv + h] = acc2[1];
+            if (!a.g_per_key) a.ws_dg[(slice * tokens + t) * a.Hv + h] = acc2[1];
         }
         __syncthreads();   // acc2 and the reduction buffers are reused by the next token
         cur = nxt;
@@ -362,7 +382,8 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
 }
 
 // The slices' shares, in a fixed order: dq, dk per query/key head (over the slices and the
-// value heads that read the head), dbeta, dg per value head (over the slices).
+// value heads that read the head), dbeta and dg per value head (over the slices); with a
+// decay per key channel, dg per value head and key channel (over the slices).
 __global__ __launch_bounds__(256) void bwd_sum_kernel(RecurrentBwdArgs a, int nsl) {
     const long tokens = (long)a.B * a.T;
     const int grp = a.Hv / a.Hqk;
@@ -388,7 +409,12 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(RecurrentBwdArgs a, int ns
             sg += a.ws_dg[sl * tokens * a.Hv + th];
         }
         a.dbeta[th] = sb;
-        if (a.dg) a.dg[th] = sg;
+        if (a.dg && !a.g_per_key) a.dg[th] = sg;
+    } else if (a.g_per_key && a.dg && i < nqk + tokens * a.Hv + tokens * a.Hv * a.Dk) {
+        const long th = i - nqk - tokens * a.Hv;   // (t * Hv + h) * Dk + x
+        float sg = 0.f;
+        for (int sl = 0; sl < nsl; ++sl) sg += a.ws_dg[sl * tokens * a.Hv * a.Dk + th];
+        a.dg[th] = sg;
     }
 }
 
@@ -450,7 +476,7 @@ hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
     const hipError_t e = a.bf16 ? launch_bwd_dk<__bf16>(a, s) : launch_bwd_dk<float>(a, s);
     if (e != hipSuccess) return e;
     const long tokens = (long)a.B * a.T;
-    const long total = tokens * a.Hqk * a.Dk + tokens * a.Hv;
+    const long total = tokens * a.Hqk * a.Dk + tokens * a.Hv + (a.g_per_key && a.dg ? tokens * a.Hv * a.Dk : 0);
     if (total > 0) {
         const long blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;

@@ -192,15 +192,17 @@ dn_status dn_recurrent_fwd(const dn_shape* shape,
  * dn_recurrent_bwd -- the reverse pass of the rule (gradients for training), token by
  * token: given dL/do and dL/d final_state, the gradients of the loss for q, k, v, beta, g
  * and the initial state.  It walks each sequence backwards from the state trace that
- * dn_recurrent_fwd wrote for the same inputs.  One gate per head or none; the in-call
- * normalisation and gates per key channel are DN_ERR_UNSUPPORTED here.
+ * dn_recurrent_fwd wrote for the same inputs.  One gate per head, one per key channel
+ * (DN_GATE_PER_KEY: M' = diag(exp(g_t)) M, so dg_t[i] sums row i of dL/dM' times M') or
+ * none; the in-call normalisation is DN_ERR_UNSUPPORTED here.
  *
  *   state_trace     [B, T, Hv, Dk, Dv] fp32 from dn_recurrent_fwd (required)
  *   d_o             [B, T, Hv, Dv] dtype (required)
  *   d_final_state   [N, Hv, Dk, Dv] fp32 or NULL (zero)
  *   dq, dk          [B, T, Hqk, Dk] fp32 (summed over the value heads of each q/k head)
  *   dv              [B, T, Hv, Dv] fp32;  dbeta [B, T, Hv] fp32
- *   dg              [B, T, Hv] fp32, required when g is given, else ignored
+ *   dg              g's shape ([B, T, Hv], or [B, T, Hv, Dk] per key channel) fp32,
+ *                   required when g is given, else ignored
  *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
  *   workspace       dn_recurrent_bwd_workspace_bytes(shape) bytes
  *
@@ -216,7 +218,8 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
                            hipStream_t stream);
 
 /* Bytes of workspace dn_recurrent_bwd needs: each 32-column slice's share of dq, dk,
- * dbeta and dg before they are added in a fixed order. */
+ * dbeta and dg before they are added in a fixed order (the shape's flags matter: dg per
+ * key channel takes Dk floats per token and head). */
 size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* shape);
 
 /*

@@ -172,3 +172,22 @@ def test_causal_conv_rejects_aliasing_and_misalignment():
     s = _cshape(B=4, T=2, num_seqs=4)
     assert lib.dn_causal_conv_step(ctypes.byref(s), p, p, None, p, q, None) == dn.DN_ERR_INVALID_ARG
 
+
+
+def test_reverse_pass_host_checks():
+    """dn_recurrent_bwd: the in-call normalisation is refused, a decay per key channel needs g,
+    and the workspace query counts Dk floats of dg per token and head with that flag."""
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    args = [p] * 6 + [p, p, None, None] + [p] * 6 + [p, 1 << 30, None]
+    s = _shape(B=1, T=8, num_seqs=1, flags=1)
+    assert lib.dn_recurrent_bwd(ctypes.byref(s), *args) == dn.DN_ERR_UNSUPPORTED
+    s = _shape(B=1, T=8, num_seqs=1, flags=2)
+    a2 = list(args)
+    a2[4] = None          # g
+    assert lib.dn_recurrent_bwd(ctypes.byref(s), *a2) == dn.DN_ERR_INVALID_ARG
+    plain = _shape(B=2, T=8, num_seqs=2, Dk=64, Dv=64)
+    chg = _shape(B=2, T=8, num_seqs=2, Dk=64, Dv=64, flags=2)
+    slices, per_tok = 2, 2 * 8 * plain.Hv
+    assert lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(plain)) == slices * per_tok * (2 * 64 + 2) * 4
+    assert lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(chg)) == slices * per_tok * (3 * 64 + 1) * 4

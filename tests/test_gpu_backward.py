@@ -31,6 +31,14 @@ CASES = {
                           init_std=0.2),
     "bf16_d128_gated": dict(B=1, T=100, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.1,
                             init_std=0.02),
+    # a log decay per key channel: dg per (token, head, key channel)
+    "f32_channel_gates_packed_gqa": dict(B=1, Hqk=1, Hv=2, Dk=16, Dv=32, dtype="f32",
+                                         seqlens=[5, 0, 9, 33], g_scale=0.2, init_std=0.5,
+                                         beta_scale=2.0, g_per_key=True),
+    "f32_channel_gates_d64": dict(B=1, T=70, Hqk=2, Hv=4, Dk=64, Dv=64, dtype="f32",
+                                  g_scale=0.1, init_std=0.2, g_per_key=True),
+    "bf16_d128_channel_gates": dict(B=1, T=100, Hqk=2, Hv=2, Dk=128, dtype="bf16",
+                                    g_scale=0.1, init_std=0.02, g_per_key=True),
 }
 
 
@@ -64,12 +72,3 @@ def test_reverse_pass(name):
         err = rel_l2(host(grads[got]), ref[want])
         _say(f"  {got}: rel_l2 {err:.2e}")
         assert err <= tol(x), got
-
-
-def test_reverse_pass_rejects_channel_gates_and_normalisation():
-    x = make_case(B=1, T=8, Hqk=1, Dk=16, dtype="f32", g_scale=0.1, seed=53, g_per_key=True)
-    d = to_inputs(x)
-    _, _, trace = dn.recurrent_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], None, state_trace=True)
-    with pytest.raises(NotImplementedError):
-        dn.recurrent_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], None, trace,
-                         torch.zeros_like(d["v"]))
