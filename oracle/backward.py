@@ -34,12 +34,37 @@ import numpy as np
 __all__ = ["backward"]
 
 
-def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: float = 1.0):
+def _unnormalise(x, dxh, eps):
+    """dL/dx from dL/dx_hat for x_hat = x / n, n = sqrt(|x|^2 + eps) over the last axis:
+    dx = (dx_hat - x (x . dx_hat) / n^2) / n, and 0 where n = 0 (the rule's zero vector)."""
+    n2 = np.sum(x * x, axis=-1, keepdims=True) + eps
+    n = np.sqrt(n2)
+    safe = np.where(n2 > 0, n2, 1.0)
+    out = (dxh - x * np.sum(x * dxh, axis=-1, keepdims=True) / safe) / np.sqrt(safe)
+    return np.where(n > 0, out, 0.0)
+
+
+def backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale: float = 1.0,
+             qk_l2norm: bool = False, eps: float = 1e-6):
     """Gradients of the rule.  Shapes as ``oracle.recurrent`` (q, k ``[B, T, Hqk, Dk]``, v
     ``[B, T, Hv, Dv]``, beta ``[B, T, Hv]``, g ``[B, T, Hv]``, ``[B, T, Hv, Dk]`` (a log
     decay per key channel) or None, init ``[N, Hv, Dk, Dv]`` or None), do ``[B, T, Hv, Dv]``,
     dfinal ``[N, Hv, Dk, Dv]`` or None.  Returns a dict of fp64 arrays dq, dk, dv, dbeta,
-    dg (g's shape; None without g), dinit."""
+    dg (g's shape; None without g), dinit.
+
+    With ``qk_l2norm`` the rule reads q / sqrt(|q|^2 + eps) and k / sqrt(|k|^2 + eps) (the
+    in-call normalisation of ``oracle.recurrent``): the pass runs on the normalised vectors
+    and dq, dk are taken back through the normalisation."""
+    if qk_l2norm:
+        q, k = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+        nq = np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+        nk = np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+        qh = np.where(nq > 0, q / np.where(nq > 0, nq, 1.0), 0.0)
+        kh = np.where(nk > 0, k / np.where(nk > 0, nk, 1.0), 0.0)
+        out = backward(qh, kh, v, beta, g, init, do, dfinal, cu_seqlens, scale)
+        out["dq"] = _unnormalise(q, out["dq"], eps)
+        out["dk"] = _unnormalise(k, out["dk"], eps)
+        return out
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     beta, do = np.asarray(beta, dtype=np.float64), np.asarray(do, dtype=np.float64)
     B, T, Hqk, Dk = q.shape

@@ -105,3 +105,53 @@ def test_torch_autograd_of_the_product_form_channel_gates():
     grads = backward(q, k, v, beta, g, None, do, dfin)
     for name, t in (("dq", tq), ("dk", tk), ("dv", tv), ("dbeta", tb), ("dg", tg)):
         np.testing.assert_allclose(grads[name], t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_finite_differences_in_call_normalisation():
+    """Raw q and k normalised inside the rule: central differences of the loss through the C
+    oracle with qk_l2norm, for q and k (the other inputs see the normalised vectors only)."""
+    rng = np.random.default_rng(4)
+    q, k, v, beta, g = _case(rng, T=6, Hqk=1, Hv=2, Dk=3, Dv=4)
+    q = q * rng.uniform(0.5, 3.0, q.shape[:-1] + (1,))
+    k = k * rng.uniform(0.5, 3.0, k.shape[:-1] + (1,))
+    init = rng.standard_normal((1, 2, 3, 4))
+    do = rng.standard_normal(v.shape)
+    dfin = rng.standard_normal(init.shape)
+    eps = 1e-3
+    grads = backward(q, k, v, beta, g, init, do, dfin, None, 0.9, qk_l2norm=True, eps=eps)
+    h = 1e-6
+    for name, x in (("q", q), ("k", k)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            qp, kp = (xp, k) if name == "q" else (q, xp)
+            qm, km = (xm, k) if name == "q" else (q, xm)
+            lp = _loss(oracle.recurrent(qp, kp, v, beta, g, init, None, 0.9, qk_l2norm=True, eps=eps), do, dfin)
+            lm = _loss(oracle.recurrent(qm, km, v, beta, g, init, None, 0.9, qk_l2norm=True, eps=eps), do, dfin)
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grads["d" + name], num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_torch_autograd_through_the_normalisation():
+    """Autograd of the product form with q, k replaced by x / sqrt(|x|^2 + eps) (fp64)."""
+    rng = np.random.default_rng(5)
+    q, k, v, beta, g = _case(rng, B=1, T=5, Hqk=1, Hv=1, Dk=4, Dv=3)
+    q, k = q * 2.5, k * 0.4
+    eps = 1e-2
+    do = rng.standard_normal(v.shape)
+    tq, tk = torch.tensor(q, requires_grad=True), torch.tensor(k, requires_grad=True)
+    nrm = lambda x: x / torch.sqrt(torch.sum(x * x, dim=-1, keepdim=True) + eps)
+    qh, kh = nrm(tq), nrm(tk)
+    S = torch.zeros(3, 4, dtype=torch.float64)
+    loss = 0.0
+    for t in range(5):
+        kt = kh[0, t, 0][:, None]
+        S = float(np.exp(g[0, t, 0])) * S
+        S = S @ (torch.eye(4, dtype=torch.float64) - beta[0, t, 0] * (kt @ kt.T)) + beta[0, t, 0] * (torch.tensor(v[0, t, 0])[:, None] @ kt.T)
+        loss = loss + (S @ qh[0, t, 0]) @ torch.tensor(do[0, t, 0])
+    loss.backward()
+    grads = backward(q, k, v, beta, g, None, do, qk_l2norm=True, eps=eps)
+    np.testing.assert_allclose(grads["dq"], tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(grads["dk"], tk.grad.numpy(), rtol=1e-10, atol=1e-12)
