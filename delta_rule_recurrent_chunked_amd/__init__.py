@@ -287,16 +287,18 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
                   g: Optional[torch.Tensor], initial_state: Optional[torch.Tensor],
                   state_trace: torch.Tensor, d_o: torch.Tensor,
                   d_final_state: Optional[torch.Tensor] = None,
-                  cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0) -> dict:
+                  cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+                  qk_l2norm: bool = False, l2norm_eps: float = 1e-6) -> dict:
     """Reverse pass of the rule: gradients of a loss with dL/do = ``d_o`` and dL/d final
     state = ``d_final_state`` for q, k, v, beta, g and the initial state, from the state
     trace that :func:`recurrent_fwd` returned for the same inputs (``state_trace=True``).
     One gate per head (g ``[B, T, Hv]``), one per key channel (g ``[B, T, Hv, Dk]``) or
-    none.  Returns a dict of float32 tensors dq, dk (``[B, T, Hqk, Dk]``), dv, dbeta, dg
-    (g's shape; None without g) and d_initial_state."""
+    none.  With ``qk_l2norm`` (as given to the forward call) dq and dk are the gradients for
+    the raw q and k.  Returns a dict of float32 tensors dq, dk (``[B, T, Hqk, Dk]``), dv,
+    dbeta, dg (g's shape; None without g) and d_initial_state."""
     lib = load_library()
     shape, _, _, N = _prompt_args(q, k, v, beta, g, initial_state, False, cu_seqlens, scale, 64,
-                                  None, None, True, False, 1e-6)
+                                  None, None, True, qk_l2norm, l2norm_eps)
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     _dev(state_trace, "state_trace", torch.float32, (B, T, Hv, Dk, Dv))

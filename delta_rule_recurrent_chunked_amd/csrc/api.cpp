@@ -205,7 +205,6 @@ dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, cons
     dn::RecurrentBwdArgs a{};
     dn_status st = prefill_shape(s, cu != nullptr, a);
     if (st != DN_OK) return st;
-    if (a.qk_norm) return DN_ERR_UNSUPPORTED;
     if (a.g_per_key && !g) return DN_ERR_INVALID_ARG;
     const long tokens = (long)s->B * s->T;
     if (tokens > 0 && (!q || !k || !v || !beta || !trace || !dout || !dq || !dk || !dv || !dbeta ||

@@ -222,6 +222,7 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
     __shared__ float red[NW][CW];
     __shared__ float vec_vr[CW], vec_d[CW], vec_do[CW], vec_dd[CW];
     __shared__ float acc2[2];
+    __shared__ float nrm[NW][2];   // per-wave |k|^2, |q|^2 partials (in-call normalisation)
 
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int ct = tid % TPR, rg = tid / TPR;
@@ -268,25 +269,63 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
         for (int p = 0; p < RPT; ++p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) Mp[p][e] = al[p] * cur.m[p][e];
-        // r = M'^T k
+        // r = M'^T k (k as loaded; with the in-call normalisation r is scaled once the
+        // norms are reduced)
         float c[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < RPT; ++p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) c[e] += Mp[p][e] * cur.k[p];
         colsum(c);
+        if (a.qk_norm) {
+            float kk = 0.f, qq = 0.f;
+            if (ct == 0) {
+#pragma unroll
+                for (int p = 0; p < RPT; ++p) {
+                    kk += cur.k[p] * cur.k[p];
+                    qq += cur.q[p] * cur.q[p];
+                }
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                kk += __shfl_xor(kk, off);
+                qq += __shfl_xor(qq, off);
+            }
+            if (lane == 0) {
+                nrm[wave][0] = kk;
+                nrm[wave][1] = qq;
+            }
+        }
         if (tid < 2) acc2[tid] = 0.f;
         __syncthreads();
+        float ik = 1.f, iq = 1.f;
+        if (a.qk_norm) {
+            float kk = 0.f, qq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                kk += nrm[w][0];
+                qq += nrm[w][1];
+            }
+            ik = inv_norm(kk, a.eps);
+            iq = inv_norm(qq, a.eps);
+        }
         if (tid < CW) {
             float r = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) r += red[w][tid];
-            const float vr = cur.v - r;   // v - r
+            const float vr = cur.v - ik * r;   // v - r
             vec_vr[tid] = vr;
             vec_d[tid] = beta * vr;
             vec_do[tid] = a.scale * cur.dout;
         }
         __syncthreads();
+        if (a.qk_norm) {   // from here on the rule's own (normalised) k and q
+#pragma unroll
+            for (int p = 0; p < RPT; ++p) {
+                cur.k[p] *= ik;
+                cur.q[p] *= iq;
+            }
+        }
         float dl[4], dov[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -418,6 +457,53 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(RecurrentBwdArgs a, int ns
     }
 }
 
+// dq, dk through the in-call normalisation, in place: with x_hat = x / n, n = sqrt(|x|^2 +
+// eps), dx = (dx_hat - x (x . dx_hat) / n^2) / n (zero where n = 0).  One wave per (token,
+// query/key head) row, two key channels per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(RecurrentBwdArgs a) {
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);   // t * Hqk + hq
+    const int lane = threadIdx.x & 63;
+    if (row >= (long)a.B * a.T * a.Hqk) return;
+    const T* q = static_cast<const T*>(a.q);
+    const T* k = static_cast<const T*>(a.k);
+    float xq[2], xk[2], gq[2], gk[2];
+    float nq = 0.f, nk = 0.f, sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int x = lane + 64 * c;
+        const long i = row * a.Dk + x;
+        const bool in = x < a.Dk;
+        xq[c] = in ? ld_f32(q, i) : 0.f;
+        xk[c] = in ? ld_f32(k, i) : 0.f;
+        gq[c] = in ? a.dq[i] : 0.f;
+        gk[c] = in ? a.dk[i] : 0.f;
+        nq += xq[c] * xq[c];
+        nk += xk[c] * xk[c];
+        sq += xq[c] * gq[c];
+        sk += xk[c] * gk[c];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        nq += __shfl_xor(nq, off);
+        nk += __shfl_xor(nk, off);
+        sq += __shfl_xor(sq, off);
+        sk += __shfl_xor(sk, off);
+    }
+    nq += a.eps;
+    nk += a.eps;
+    const float rq = nq > 0.f ? rsqrtf(nq) : 0.f, rk = nk > 0.f ? rsqrtf(nk) : 0.f;
+    const float cq = nq > 0.f ? sq / nq : 0.f, ck = nk > 0.f ? sk / nk : 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int x = lane + 64 * c;
+        if (x < a.Dk) {
+            a.dq[row * a.Dk + x] = (gq[c] - xq[c] * cq) * rq;
+            a.dk[row * a.Dk + x] = (gk[c] - xk[c] * ck) * rk;
+        }
+    }
+}
+
 template <typename T, int DK>
 hipError_t launch_dv(const RecurrentArgs& a, hipStream_t s) {
     const long nh = (long)a.N * a.Hv;
@@ -481,6 +567,13 @@ hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
         const long blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(bwd_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, recurrent_bwd_slices(a.Dv));
+    }
+    const long rows = tokens * a.Hqk;
+    if (a.qk_norm && rows > 0) {
+        const long blocks = (rows + 3) / 4;
+        if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        if (a.bf16) hipLaunchKernelGGL(norm_bwd_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(norm_bwd_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -192,9 +192,10 @@ dn_status dn_recurrent_fwd(const dn_shape* shape,
  * dn_recurrent_bwd -- the reverse pass of the rule (gradients for training), token by
  * token: given dL/do and dL/d final_state, the gradients of the loss for q, k, v, beta, g
  * and the initial state.  It walks each sequence backwards from the state trace that
- * dn_recurrent_fwd wrote for the same inputs.  One gate per head, one per key channel
- * (DN_GATE_PER_KEY: M' = diag(exp(g_t)) M, so dg_t[i] sums row i of dL/dM' times M') or
- * none; the in-call normalisation is DN_ERR_UNSUPPORTED here.
+ * dn_recurrent_fwd wrote for the same inputs (with the same flags).  One gate per head,
+ * one per key channel (DN_GATE_PER_KEY: M' = diag(exp(g_t)) M, so dg_t[i] sums row i of
+ * dL/dM' times M') or none.  With DN_QK_L2NORM, dq and dk are the gradients for the raw
+ * q and k, taken back through x / sqrt(|x|^2 + eps).
  *
  *   state_trace     [B, T, Hv, Dk, Dv] fp32 from dn_recurrent_fwd (required)
  *   d_o             [B, T, Hv, Dv] dtype (required)
@@ -206,7 +207,7 @@ dn_status dn_recurrent_fwd(const dn_shape* shape,
  *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
  *   workspace       dn_recurrent_bwd_workspace_bytes(shape) bytes
  *
- * Errors: as dn_recurrent_fwd, DN_ERR_UNSUPPORTED for the flags above, DN_ERR_WORKSPACE.
+ * Errors: as dn_recurrent_fwd, DN_ERR_WORKSPACE.
  */
 dn_status dn_recurrent_bwd(const dn_shape* shape,
                            const void* q, const void* k, const void* v,

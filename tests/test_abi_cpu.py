@@ -175,13 +175,11 @@ def test_causal_conv_rejects_aliasing_and_misalignment():
 
 
 def test_reverse_pass_host_checks():
-    """dn_recurrent_bwd: the in-call normalisation is refused, a decay per key channel needs g,
-    and the workspace query counts Dk floats of dg per token and head with that flag."""
+    """dn_recurrent_bwd: a decay per key channel needs g, and the workspace query counts Dk
+    floats of dg per token and head with that flag."""
     lib = dn.load_library()
     p = ctypes.c_void_p(16)
     args = [p] * 6 + [p, p, None, None] + [p] * 6 + [p, 1 << 30, None]
-    s = _shape(B=1, T=8, num_seqs=1, flags=1)
-    assert lib.dn_recurrent_bwd(ctypes.byref(s), *args) == dn.DN_ERR_UNSUPPORTED
     s = _shape(B=1, T=8, num_seqs=1, flags=2)
     a2 = list(args)
     a2[4] = None          # g

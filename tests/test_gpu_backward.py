@@ -39,6 +39,15 @@ CASES = {
                                   g_scale=0.1, init_std=0.2, g_per_key=True),
     "bf16_d128_channel_gates": dict(B=1, T=100, Hqk=2, Hv=2, Dk=128, dtype="bf16",
                                     g_scale=0.1, init_std=0.02, g_per_key=True),
+    # raw q and k (N(0,1) draws) normalised inside the rule: dq, dk for the raw inputs
+    "f32_in_call_norm_packed_gqa": dict(B=1, Hqk=1, Hv=2, Dk=16, Dv=32, dtype="f32",
+                                        seqlens=[5, 0, 9, 33], g_scale=0.2, init_std=0.5,
+                                        beta_scale=2.0, qk_raw=True),
+    "f32_in_call_norm_channel_gates_d64": dict(B=1, T=70, Hqk=2, Hv=4, Dk=64, Dv=64,
+                                               dtype="f32", g_scale=0.1, init_std=0.2,
+                                               g_per_key=True, qk_raw=True),
+    "bf16_d128_in_call_norm": dict(B=1, T=100, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.1,
+                                   init_std=0.02, qk_raw=True),
 }
 
 
@@ -58,14 +67,16 @@ def test_reverse_pass(name):
         do_dev, do_ref = dev_tensor(do), do.astype(np.float64)
     d = to_inputs(x)
     scale = 0.7
+    norm = bool(CASES[name].get("qk_raw"))
     _, _, trace = dn.recurrent_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"],
-                                   cu_seqlens=d["cu"], scale=scale, state_trace=True)
+                                   cu_seqlens=d["cu"], scale=scale, state_trace=True,
+                                   qk_l2norm=norm)
     grads = dn.recurrent_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], trace, do_dev,
-                             dev_tensor(dfin), cu_seqlens=d["cu"], scale=scale)
+                             dev_tensor(dfin), cu_seqlens=d["cu"], scale=scale, qk_l2norm=norm)
     torch.cuda.synchronize()
     f = x.f64()
     ref = ref_backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["init"], do_ref,
-                       dfin.astype(np.float64), x.cu_seqlens, scale)
+                       dfin.astype(np.float64), x.cu_seqlens, scale, qk_l2norm=norm)
     pairs = [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dbeta", "dbeta"),
              ("d_initial_state", "dinit")] + ([("dg", "dg")] if x.g is not None else [])
     for got, want in pairs:
