@@ -194,7 +194,7 @@ size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* s) {
     // dq, dk shares [slices, tokens, Hv, Dk]; dbeta [slices, tokens, Hv]; dg [slices, tokens,
     // Hv] or, with a decay per key channel, [slices, tokens, Hv, Dk]
     const size_t per = (s->flags & DN_GATE_PER_KEY) ? 3 * (size_t)s->Dk + 1 : 2 * (size_t)s->Dk + 2;
-    return (size_t)dn::recurrent_bwd_slices(s->Dv) * s->B * s->T * s->Hv * per * sizeof(float);
+    return (size_t)dn::recurrent_bwd_slices(s->Dk, s->Dv) * s->B * s->T * s->Hv * per * sizeof(float);
 }
 
 dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, const void* v,
@@ -223,8 +223,8 @@ dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, cons
     a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = g ? dg : nullptr; a.dh0 = dh0;
     // the slices' shares: dq, dk [slices, tokens, Hv, Dk], then dbeta [slices, tokens, Hv],
     // then dg ([slices, tokens, Hv], or [slices, tokens, Hv, Dk] with a decay per key channel)
-    const size_t qk = (size_t)dn::recurrent_bwd_slices(s->Dv) * tokens * s->Hv * s->Dk;
-    const size_t sc = (size_t)dn::recurrent_bwd_slices(s->Dv) * tokens * s->Hv;
+    const size_t qk = (size_t)dn::recurrent_bwd_slices(s->Dk, s->Dv) * tokens * s->Hv * s->Dk;
+    const size_t sc = (size_t)dn::recurrent_bwd_slices(s->Dk, s->Dv) * tokens * s->Hv;
     a.ws_dq = static_cast<float*>(ws);
     a.ws_dk = a.ws_dq + qk;
     a.ws_db = a.ws_dk + qk;

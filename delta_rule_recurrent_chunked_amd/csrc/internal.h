@@ -85,7 +85,7 @@ struct ConvArgs {
 
 // The reverse pass of the token-by-token route: the forward's arguments, its state
 // trace, dL/do and dL/dM_T in; gradients out (fp32).  Each workgroup takes a slice of the
-// value columns (recurrent_bwd_slices(Dv) of them) and writes its share of dq, dk, dbeta
+// value columns (recurrent_bwd_slices(Dk, Dv) of them) and writes its share of dq, dk, dbeta
 // and dg to the workspace; a second kernel adds the shares.
 struct RecurrentBwdArgs : PrefillArgs {
     const float* trace;             // [tokens, Hv, Dk, Dv] from the forward
@@ -102,7 +102,7 @@ struct RecurrentBwdArgs : PrefillArgs {
     float* dg;                      // [tokens, Hv] or null (no gate)
     float* dh0;                     // [N, Hv, Dk, Dv] or null
 };
-int recurrent_bwd_slices(int Dv);
+int recurrent_bwd_slices(int Dk, int Dv);
 
 // Launchers (host functions); each returns hipGetLastError() after its launches.
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s);

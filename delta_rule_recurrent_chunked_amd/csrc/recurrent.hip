@@ -30,6 +30,8 @@ struct RecShape {
     static_assert(DV % 4 == 0 && TPR <= 64 && NT % 64 == 0 && DK % RPP == 0, "recurrent tiling");
 };
 
+constexpr int bwd_cols(int Dk) { return Dk >= 32 ? 8 : 16; }
+
 template <typename T, int DK, int DV, int CW>
 __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_kernel(RecurrentArgs a) {
     using S = RecShape<DK, CW>;
@@ -530,12 +532,15 @@ hipError_t launch_dk(const RecurrentArgs& a, hipStream_t s) {
 
 template <typename T, int DK>
 hipError_t launch_bwd_dv(const RecurrentBwdArgs& a, hipStream_t s) {
+    // value columns per workgroup: 8 (more workgroups per head, the per-token latency is
+    // spread over more CUs) where a workgroup still holds a whole number of waves
+    constexpr int CW = bwd_cols(DK);
     const long nh = (long)a.N * a.Hv;
     switch (a.Dv) {
-        case 16: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 16, 16>), dim3((unsigned)nh), dim3(RecShape<DK, 16>::NT), 0, s, a); break;
-        case 32: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 32, 32>), dim3((unsigned)nh), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 64, 32>), dim3((unsigned)(2 * nh)), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 128, 32>), dim3((unsigned)(4 * nh)), dim3(RecShape<DK, 32>::NT), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 16, CW>), dim3((unsigned)(16 / CW * nh)), dim3(RecShape<DK, CW>::NT), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 32, CW>), dim3((unsigned)(32 / CW * nh)), dim3(RecShape<DK, CW>::NT), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 64, CW>), dim3((unsigned)(64 / CW * nh)), dim3(RecShape<DK, CW>::NT), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((recurrent_bwd_kernel<T, DK, 128, CW>), dim3((unsigned)(128 / CW * nh)), dim3(RecShape<DK, CW>::NT), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -554,11 +559,11 @@ hipError_t launch_bwd_dk(const RecurrentBwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int recurrent_bwd_slices(int Dv) { return Dv > 32 ? Dv / 32 : 1; }
+int recurrent_bwd_slices(int Dk, int Dv) { return Dv / bwd_cols(Dk); }
 
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
     if ((long)a.N * a.Hv == 0) return hipSuccess;
-    if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dk, a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
     const hipError_t e = a.bf16 ? launch_bwd_dk<__bf16>(a, s) : launch_bwd_dk<float>(a, s);
     if (e != hipSuccess) return e;
     const long tokens = (long)a.B * a.T;
@@ -566,7 +571,7 @@ hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
     if (total > 0) {
         const long blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, recurrent_bwd_slices(a.Dv));
+        hipLaunchKernelGGL(bwd_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, recurrent_bwd_slices(a.Dk, a.Dv));
     }
     const long rows = tokens * a.Hqk;
     if (a.qk_norm && rows > 0) {
@@ -580,7 +585,7 @@ hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s) {
     if ((long)a.N * a.Hv == 0) return hipSuccess;
-    if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dk, a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
     return a.bf16 ? launch_dk<__bf16>(a, s) : launch_dk<float>(a, s);
 }
 

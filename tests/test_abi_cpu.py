@@ -186,6 +186,6 @@ def test_reverse_pass_host_checks():
     assert lib.dn_recurrent_bwd(ctypes.byref(s), *a2) == dn.DN_ERR_INVALID_ARG
     plain = _shape(B=2, T=8, num_seqs=2, Dk=64, Dv=64)
     chg = _shape(B=2, T=8, num_seqs=2, Dk=64, Dv=64, flags=2)
-    slices, per_tok = 2, 2 * 8 * plain.Hv
+    slices, per_tok = 8, 2 * 8 * plain.Hv   # 8-column slices
     assert lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(plain)) == slices * per_tok * (2 * 64 + 2) * 4
     assert lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(chg)) == slices * per_tok * (3 * 64 + 1) * 4
