@@ -208,3 +208,52 @@ def test_prefill_channel_gates_layer_workload():
     torch.cuda.synchronize()
     o_ref, s_ref = _oracle(x)
     _check(x, host(o), host(s), o_ref, s_ref)
+
+
+def test_prefill_channel_gates_chunk_edges():
+    """Sequence lengths at and around the 64-token chunk and 16-token block edges, empty
+    sequences between them, four value heads per q/k head (matrix-core kernel)."""
+    _say("channel gates prefill: chunk edges")
+    x = make_case(B=1, Hqk=1, Hv=4, Dk=128, dtype="bf16", seqlens=[1, 63, 0, 64, 65, 16, 17, 128, 0],
+                  g_scale=0.3, init_std=0.1, beta_scale=2.0, seed=29, name="chg_edges",
+                  g_per_key=True)
+    d = to_inputs(x)
+    o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], cu_seqlens=d["cu"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o), host(s), o_ref, s_ref)
+
+
+def test_prefill_channel_gates_graph_replay():
+    """The matrix-core channel-gate prefill captured in a HIP graph replays to the eager
+    result, every replay, with eager work and synchronisations between the replays."""
+    _say("channel gates prefill: graph replay")
+    x = make_case(B=2, T=150, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.2, init_std=0.05,
+                  seed=30, name="chg_graph", g_per_key=True)
+    d = to_inputs(x)
+    o = torch.empty((2, 150, 2, 128), dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty((2, 2, 128, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], out=o, final_state=fs)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (o.clone(), fs.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        o.zero_(), fs.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(fs, ref[1]), f"replay {rep} differs"
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o), host(fs), o_ref, s_ref)
