@@ -157,10 +157,13 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
 
 
 def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: torch.dtype,
-                    num_seqs: Optional[int] = None, chunk_size: int = 64) -> int:
-    """Device workspace (bytes) ``dn_chunk_fwd`` needs for these sizes."""
+                    num_seqs: Optional[int] = None, chunk_size: int = 64,
+                    g_per_key: bool = False) -> int:
+    """Device workspace (bytes) ``dn_chunk_fwd`` needs for these sizes (only the matrix-core
+    path for a log decay per key channel uses one)."""
     s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
                DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0)
+    s.flags = DN_GATE_PER_KEY if g_per_key else 0
     return int(load_library().dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
 
 

@@ -86,8 +86,8 @@ size_t dn_chunk_fwd_workspace_bytes(const dn_shape* s) {
     dn::PrefillArgs a;
     const bool packed = s && s->B == 1 && s->num_seqs != 1;
     if (prefill_shape(s, packed, a) != DN_OK) return 0;
-    (void)a;
-    return 0;  // every current prefill path keeps its intermediates on chip
+    // only the matrix-core path for gates per key channel keeps per-chunk operands in HBM
+    return dn::prefill_chg_workspace_bytes(a);
 }
 
 dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const void* v,

@@ -75,6 +75,7 @@ struct ChgSmem {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -484,22 +485,570 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
     }
 }
 
+
+// ------------------------------------------------------------------ two-kernel form
+// With a workspace, the state-independent work of every chunk (steps 1 to 4 above) runs
+// once per (chunk, value head) in a kernel over all chunks at once, instead of once per
+// 32-column slice inside the sequential loop; the chain kernel then only loads each
+// chunk's operands and runs step 5.  Workspace record of one (chunk, value head), bytes:
+constexpr long OP_KE = 0;          // K o e^G            [64][128] bf16
+constexpr long OP_QE = 16384;      // Q o e^G            [64][128] bf16
+constexpr long OP_KD = 32768;      // K o e^{G_last - G} [64][128] bf16
+constexpr long OP_A = 49152;       // A                  [64][64] bf16
+constexpr long OP_P = 57344;       // P                  [64][64] bf16
+constexpr long OP_TB = 65536;      // (I + A_bb)^-1      [4][16][16] bf16
+constexpr long OP_EG = 67584;      // exp(G_last)        [128] fp32
+constexpr long OP_BETA = 68096;    // beta               [64] fp32
+constexpr long OP_BYTES = 68352;
+
+// Chunks are numbered sequence by sequence.  The sequence and chunk of chunk `gid`
+// (false past the last chunk), and the number of the first chunk of sequence n.
+__device__ bool chunk_of(const PrefillArgs& a, long gid, int& n, long& c) {
+    if (!a.cu) {
+        const long cps = ((long)a.T + CC - 1) / CC;
+        if (cps == 0) return false;
+        n = (int)(gid / cps);
+        c = gid % cps;
+        return n < a.N;
+    }
+    long acc = 0;
+    for (int m = 0; m < a.N; ++m) {
+        const long cnt = ((long)a.cu[m + 1] - a.cu[m] + CC - 1) / CC;
+        if (gid < acc + cnt) {
+            n = m;
+            c = gid - acc;
+            return true;
+        }
+        acc += cnt;
+    }
+    return false;
+}
+__device__ long first_chunk(const PrefillArgs& a, int n) {
+    if (!a.cu) return (long)n * (((long)a.T + CC - 1) / CC);
+    long acc = 0;
+    for (int m = 0; m < n; ++m) acc += ((long)a.cu[m + 1] - a.cu[m] + CC - 1) / CC;
+    return acc;
+}
+
+__global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a) {
+    __shared__ __align__(16) ChgSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int Hv = a.Hv;
+    const int u = w & 1;
+    const long gid = blockIdx.x / Hv;
+    const int h = blockIdx.x % Hv;
+    int n;
+    long cix;
+    if (!chunk_of(a, gid, n, cix)) return;   // past the last chunk (the grid is a bound)
+    const int hq = h / (Hv / a.Hqk);
+    const __bf16* qp = static_cast<const __bf16*>(a.q);
+    const __bf16* kp = static_cast<const __bf16*>(a.k);
+    long bos, eos;
+    seq_range(a.cu, n, a.T, bos, eos);
+    const long c0 = bos + cix * CC;
+    (void)u;
+    (void)l16;
+    (void)g4;
+
+    for (int e = tid; e < CC * AP; e += NTH) {
+        (&sm.P[0][0])[e] = (__bf16)0.f;
+        (&sm.A[0][0])[e] = (__bf16)0.f;
+    }
+
+    const long L = eos - bos;
+    const uint32_t g_tok = (uint32_t)Hv * HK * 4, kq_tok = (uint32_t)a.Hqk * HK * 2, b_tok = (uint32_t)Hv * 4;
+    const __amdgpu_buffer_rsrc_t gs = rsrc(a.g + (bos * Hv + h) * HK, L > 0 ? (L - 1) * g_tok + HK * 4 : 0);
+    const __amdgpu_buffer_rsrc_t ks = rsrc(kp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+    const __amdgpu_buffer_rsrc_t qs = rsrc(qp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+    const __amdgpu_buffer_rsrc_t bs = rsrc(a.beta + bos * Hv + h, L > 0 ? (L - 1) * b_tok + 4 : 0);
+    float2 rg[16];
+    uint32_t rk[16], rq[16];
+    float rb;
+    {
+        const uint32_t c = (uint32_t)(cix * CC);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t r = c + 16 * w + i;
+            const u32x2 gv = __builtin_amdgcn_raw_buffer_load_b64(gs, r * g_tok + 8 * lane, 0, 0);
+            rg[i] = make_float2(__uint_as_float(gv[0]), __uint_as_float(gv[1]));
+            rk[i] = __builtin_amdgcn_raw_buffer_load_b32(ks, r * kq_tok + 4 * lane, 0, 0);
+            rq[i] = __builtin_amdgcn_raw_buffer_load_b32(qs, r * kq_tok + 4 * lane, 0, 0);
+        }
+        rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (c + (tid & 63)) * b_tok, 0, 0));
+    }
+    {
+        // ---- 1: block sums of g, k and q as floats (normalised if asked), V and beta
+        float2 L[16], kf[16], qf[16];
+        {
+            float2 s = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s.x += rg[i].x;
+                s.y += rg[i].y;
+                L[i] = s;
+                kf[i] = bf2_to_f2(rk[i]);
+                qf[i] = bf2_to_f2(rq[i]);
+            }
+            if (a.qk_norm) {
+                float nk[16], nq[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    nk[i] = kf[i].x * kf[i].x + kf[i].y * kf[i].y;
+                    nq[i] = qf[i].x * qf[i].x + qf[i].y * qf[i].y;
+                }
+#pragma unroll
+                for (int mm = 1; mm < 64; mm <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        nk[i] += __shfl_xor(nk[i], mm);
+                        nq[i] += __shfl_xor(nq[i], mm);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float ik = inv_norm(nk[i], a.eps), iq = inv_norm(nq[i], a.eps);
+                    kf[i].x *= ik;
+                    kf[i].y *= ik;
+                    qf[i].x *= iq;
+                    qf[i].y *= iq;
+                }
+            }
+            if (tid < CC) sm.beta[tid] = rb;
+            *reinterpret_cast<float2*>(&sm.tot[w][2 * lane]) = s;
+            const bool hb = __ballot(fminf(s.x, s.y) < -HARD) != 0;
+            if (lane == 0) sm.hard[w] = hb ? 1 : 0;
+        }
+        __syncthreads();
+
+        // ---- 2: operands
+        float2 Z[NB], Zw = make_float2(0.f, 0.f), Gl = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            Z[b] = Gl;
+            if (b == w) Zw = Gl;
+            const float2 tb = *reinterpret_cast<const float2*>(&sm.tot[b][2 * lane]);
+            Gl.x += tb.x;
+            Gl.y += tb.y;
+        }
+        uint32_t pke[16], pqe[16];  // K o e^G and Q o e^G, stored once the column operands are read
+        const bool hard = sm.hard[w] != 0;
+        if (!hard) {
+            // every factor from two exponentials per entry, e^{L} and e^{-L} (L the in-block
+            // sum, -L at most 60 here), and per-channel factors of at most 1
+            const float2 eZ = make_float2(__expf(Zw.x), __expf(Zw.y));
+            const float2 eD = make_float2(__expf(Gl.x - Zw.x), __expf(Gl.y - Zw.y));
+            float2 eF[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) eF[b] = make_float2(__expf(Z[b].x - Zw.x), __expf(Z[b].y - Zw.y));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * w + i;
+                const float e1x = __expf(L[i].x), e1y = __expf(L[i].y);
+                const float e2x = __expf(-L[i].x), e2y = __expf(-L[i].y);
+                const float kx = kf[i].x * e1x, ky = kf[i].y * e1y, qx = qf[i].x * e1x, qy = qf[i].y * e1y;
+                st2(&sm.Kr[r][2 * lane], kx, ky);
+                st2(&sm.Qr[r][2 * lane], qx, qy);
+                pke[i] = pack_bf16x2(kx * eZ.x, ky * eZ.y);
+                pqe[i] = pack_bf16x2(qx * eZ.x, qy * eZ.y);
+                const float cx = kf[i].x * e2x, cy = kf[i].y * e2y;
+                st2(&sm.Kd[r][2 * lane], cx * eD.x, cy * eD.y);
+                st2(&sm.Kc[kc_off(w) + r][2 * lane], cx, cy);
+#pragma unroll
+                for (int b = 1; b < NB; ++b)
+                    if (b > w) st2(&sm.Kc[kc_off(b) + r][2 * lane], cx * eF[b].x, cy * eF[b].y);
+            }
+        } else {
+            // one exponential per factor, each of a difference that is at most 0 (the
+            // diagonal column factor, replaced below, is capped)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * w + i;
+                const float ax = __expf(Zw.x + L[i].x), ay = __expf(Zw.y + L[i].y);
+                pke[i] = pack_bf16x2(kf[i].x * ax, kf[i].y * ay);
+                pqe[i] = pack_bf16x2(qf[i].x * ax, qf[i].y * ay);
+                const float ex = __expf(L[i].x), ey = __expf(L[i].y);
+                st2(&sm.Kr[r][2 * lane], kf[i].x * ex, kf[i].y * ey);
+                st2(&sm.Qr[r][2 * lane], qf[i].x * ex, qf[i].y * ey);
+                st2(&sm.Kd[r][2 * lane], kf[i].x * __expf(Gl.x - Zw.x - L[i].x),
+                    kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < w) continue;
+                    float cx = Z[b].x - Zw.x - L[i].x, cy = Z[b].y - Zw.y - L[i].y;
+                    if (b == w) {
+                        cx = fminf(cx, CLAMP);
+                        cy = fminf(cy, CLAMP);
+                    }
+                    st2(&sm.Kc[kc_off(b) + r][2 * lane], kf[i].x * __expf(cx), kf[i].y * __expf(cy));
+                }
+            }
+        }
+        if (w == 0) *reinterpret_cast<float2*>(&sm.eg[2 * lane]) = make_float2(__expf(Gl.x), __expf(Gl.y));
+        if (!hard) {
+            // block w's diagonal tiles of A and P from the rows this wave has just written
+            wave_lds_order();
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 kc = ld8(&sm.Kc[kc_off(w) + 16 * w + l16][32 * s + 8 * g4]);
+                aa = mma16(ld8(&sm.Kr[16 * w + l16][32 * s + 8 * g4]), kc, aa);
+                pa = mma16(ld8(&sm.Qr[16 * w + l16][32 * s + 8 * g4]), kc, pa);
+            }
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * g4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                const float av = l16 < r ? bt[e] * aa[e] : 0.f;
+                sm.A[16 * w + r][16 * w + l16] = (__bf16)av;
+                sm.Ad[w][l16][r] = av;
+                sm.P[16 * w + r][16 * w + l16] = (__bf16)(l16 <= r ? pa[e] : 0.f);
+            }
+        } else {
+            // block w decays too fast for the factored diagonal tile: one exponential per
+            // (row, column, channel); the wave sums over its 128 channels.  Rare, so it
+            // runs over private copies rather than holding registers for the common path.
+            float2 hl[16], hk[16], hq[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                hl[i] = L[i];
+                hk[i] = kf[i];
+                hq[i] = qf[i];
+            }
+#pragma unroll 1
+            for (int r = 0; r < 16; ++r) {
+#pragma unroll 1
+                for (int i = 0; i < 16; ++i) {
+                    float pa = 0.f, pp = 0.f;
+                    if (i <= r) {
+                        const float dx = __expf(hl[r].x - hl[i].x), dy = __expf(hl[r].y - hl[i].y);
+                        pa = wave_sum(hk[r].x * hk[i].x * dx + hk[r].y * hk[i].y * dy);
+                        pp = wave_sum(hq[r].x * hk[i].x * dx + hq[r].y * hk[i].y * dy);
+                    }
+                    if (lane == 0) {
+                        const float av = i < r ? sm.beta[16 * w + r] * pa : 0.f;
+                        sm.A[16 * w + r][16 * w + i] = (__bf16)av;
+                        sm.Ad[w][i][r] = av;
+                        sm.P[16 * w + r][16 * w + i] = (__bf16)pp;
+                    }
+                }
+            }
+        }
+        // (I + A_ww)^-1 by forward substitution, lane c < 16 solving column c in fp32; once
+        // row i is final it is taken out of every later row at once (independent updates)
+        wave_lds_order();
+        if (lane < 16) {
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[r] = r == lane ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                for (int r4 = (i + 1) & ~3; r4 < 16; r4 += 4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.Ad[w][i][r4]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (r4 + j > i) t[r4 + j] -= av[j] * t[i];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
+        }
+        __syncthreads();
+
+        // ---- 3: A (waves 0, 1) and P (waves 2, 3) below the diagonal, three tiles per wave
+        {
+            const bool isP = w >= 2;
+#pragma unroll
+            for (int tt = 0; tt < 3; ++tt) {
+                int b, bp;
+                offdiag_tile(2 * tt + u, b, bp);
+                const __bf16* rowp = isP ? &sm.Qr[16 * b + l16][8 * g4] : &sm.Kr[16 * b + l16][8 * g4];
+                const __bf16* colp = &sm.Kc[kc_off(b) + 16 * bp + l16][8 * g4];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma16(ld8(rowp + 32 * s), ld8(colp + 32 * s), acc);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * b + 4 * g4]);
+                const int i = 16 * bp + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * b + 4 * g4 + e;
+                    if (isP) sm.P[r][i] = (__bf16)acc[e];
+                    else sm.A[r][i] = (__bf16)(bt[e] * acc[e]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- 4: K o e^G and Q o e^G over the column operands
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            *reinterpret_cast<uint32_t*>(&sm.Kc[16 * w + i][2 * lane]) = pke[i];
+            *reinterpret_cast<uint32_t*>(&sm.Kc[CC + 16 * w + i][2 * lane]) = pqe[i];
+        }
+        __syncthreads();
+
+
+        // ---- out: this chunk's operands to its workspace record
+        char* rec = static_cast<char*>(a.ws) + (gid * Hv + h) * OP_BYTES;
+        for (int e = tid; e < 1024; e += NTH) {
+            const int r = e >> 4, p = e & 15;
+            *reinterpret_cast<u32x4v*>(rec + OP_KE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[r][8 * p]);
+            *reinterpret_cast<u32x4v*>(rec + OP_QE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[CC + r][8 * p]);
+            *reinterpret_cast<u32x4v*>(rec + OP_KD + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kd[r][8 * p]);
+        }
+        for (int e = tid; e < 512; e += NTH) {
+            const int r = e >> 3, p = e & 7;
+            *reinterpret_cast<u32x4v*>(rec + OP_A + r * 128 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.A[r][8 * p]);
+            *reinterpret_cast<u32x4v*>(rec + OP_P + r * 128 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.P[r][8 * p]);
+        }
+        if (tid < 128) {
+            const int b = tid >> 5, r = (tid >> 1) & 15, p = tid & 1;
+            *reinterpret_cast<u32x4v*>(rec + OP_TB + (b * 16 + r) * 32 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Tb[b][r][8 * p]);
+        } else if (tid < 160) {
+            const int e = tid - 128;
+            *reinterpret_cast<u32x4v*>(rec + OP_EG + e * 16) = *reinterpret_cast<const u32x4v*>(&sm.eg[4 * e]);
+        } else if (tid < 176) {
+            const int e = tid - 160;
+            *reinterpret_cast<u32x4v*>(rec + OP_BETA + e * 16) = *reinterpret_cast<const u32x4v*>(&sm.beta[4 * e]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
+    __shared__ __align__(16) ChgSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int Hv = a.Hv, Dv = a.Dv;
+    const int slices = Dv / SL;
+    const int heads = a.N * Hv;
+    int nh, slice;
+    if ((heads & 7) == 0) {
+        const int y = blockIdx.x >> 3;
+        slice = y % slices;
+        nh = (blockIdx.x & 7) + 8 * (y / slices);
+    } else {
+        slice = blockIdx.x % slices;
+        nh = blockIdx.x / slices;
+    }
+    const int h = nh % Hv, n = nh / Hv;
+    const int j0 = slice * SL;
+    const int u = w & 1;
+    const bool chain = w < 2;
+    const __bf16* vp = static_cast<const __bf16*>(a.v);
+    __bf16* op = static_cast<__bf16*>(a.o);
+    long bos, eos;
+    seq_range(a.cu, n, a.T, bos, eos);
+    const long first = first_chunk(a, n);
+    const long nch = (eos - bos + CC - 1) / CC;
+
+    f32x4 m[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = 16 * t + 4 * g4 + e;
+            m[t][e] = (chain && a.h0) ? a.h0[((long)nh * HK + x) * Dv + j0 + 16 * u + l16] : 0.f;
+        }
+        if (chain) st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], m[t][0], m[t][1], m[t][2], m[t][3]);
+    }
+
+    // one chunk's record and V slice in registers: pieces tid + 256 i of K o e^G, Q o e^G,
+    // K o e^{G_last - G} (4 each), A and P (2 each), one of the inverses / e^{G_last} / beta
+    const long L = eos - bos;
+    const uint32_t v_tok = (uint32_t)Hv * Dv * 2;
+    const __amdgpu_buffer_rsrc_t vs = rsrc(vp + (bos * Hv + h) * Dv + j0, L > 0 ? (L - 1) * v_tok + SL * 2 : 0);
+    u32x4v rke[4], rqe[4], rkd[4], ra[2], rp[2], rx = u32x4v{0u, 0u, 0u, 0u};
+    bf16x8 rv;
+    auto fetch = [&](long c) {
+        const char* rec = static_cast<const char*>(a.ws) + ((first + c) * Hv + h) * OP_BYTES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + NTH * i, r = e >> 4, p = e & 15;
+            rke[i] = *reinterpret_cast<const u32x4v*>(rec + OP_KE + r * 256 + p * 16);
+            rqe[i] = *reinterpret_cast<const u32x4v*>(rec + OP_QE + r * 256 + p * 16);
+            rkd[i] = *reinterpret_cast<const u32x4v*>(rec + OP_KD + r * 256 + p * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + NTH * i, r = e >> 3, p = e & 7;
+            ra[i] = *reinterpret_cast<const u32x4v*>(rec + OP_A + r * 128 + p * 16);
+            rp[i] = *reinterpret_cast<const u32x4v*>(rec + OP_P + r * 128 + p * 16);
+        }
+        if (tid < 128) rx = *reinterpret_cast<const u32x4v*>(rec + OP_TB + tid * 16);
+        else if (tid < 176) rx = *reinterpret_cast<const u32x4v*>(rec + OP_EG + (tid - 128) * 16);
+        rv = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                 vs, (uint32_t)(c * CC + (tid >> 2)) * v_tok + 16 * (tid & 3), 0, 0));
+    };
+    if (nch > 0) fetch(0);
+
+    for (long cix = 0; cix < nch; ++cix) {
+        const long c0 = bos + cix * CC;
+        const int len = (int)min((long)CC, eos - c0);
+        // the chunk's record into LDS (the previous chunk's step 5 is done with it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + NTH * i, r = e >> 4, p = e & 15;
+            *reinterpret_cast<u32x4v*>(&sm.Kc[r][8 * p]) = rke[i];
+            *reinterpret_cast<u32x4v*>(&sm.Kc[CC + r][8 * p]) = rqe[i];
+            *reinterpret_cast<u32x4v*>(&sm.Kd[r][8 * p]) = rkd[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + NTH * i, r = e >> 3, p = e & 7;
+            *reinterpret_cast<u32x4v*>(&sm.A[r][8 * p]) = ra[i];
+            *reinterpret_cast<u32x4v*>(&sm.P[r][8 * p]) = rp[i];
+        }
+        if (tid < 128) {
+            const int b = tid >> 5, r = (tid >> 1) & 15, p = tid & 1;
+            *reinterpret_cast<u32x4v*>(&sm.Tb[b][r][8 * p]) = rx;
+        } else if (tid < 160) {
+            *reinterpret_cast<u32x4v*>(&sm.eg[4 * (tid - 128)]) = rx;
+        } else if (tid < 176) {
+            *reinterpret_cast<u32x4v*>(&sm.beta[4 * (tid - 160)]) = rx;
+        }
+        *reinterpret_cast<bf16x8*>(&sm.V[tid >> 2][8 * (tid & 3)]) = rv;
+        __syncthreads();
+        if (cix + 1 < nch) fetch(cix + 1);   // lands while this chunk is worked
+
+        // ---- 5a: chain waves: R and Delta; waves 2, 3: (Q o e^G) M0
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Y[NB] = {z4, z4, z4, z4};
+        bf16x8 d01 = zero8(), d23 = zero8();
+        if (chain) {
+            bf16x8 mb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mb[s] = acc_to_b(m[2 * s], m[2 * s + 1]);
+            f32x4 R[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 x = z4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) x = mma16(ld8(&sm.Kc[16 * b + l16][32 * s + 8 * g4]), mb[s], x);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * b + 4 * g4 + e;
+                    R[b][e] = sm.beta[r] * ((float)sm.V[r][16 * u + l16] - x[e]);
+                }
+            }
+            bf16x8 ta[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) ta[b] = g4 < 2 ? ld8(&sm.Tb[b][l16][8 * g4]) : zero8();
+            // Delta_b = T_bb (R_b - sum_{b'<b} A_bb' Delta_b')
+            const f32x4 D0 = mma16(ta[0], acc_to_b(R[0], z4), z4);
+            f32x4 c = mma16(ld8(&sm.A[16 + l16][8 * g4]), acc_to_b(D0, z4), z4);
+            const f32x4 D1 = mma16(ta[1], acc_to_b(R[1] - c, z4), z4);
+            d01 = acc_to_b(D0, D1);
+            c = mma16(ld8(&sm.A[32 + l16][8 * g4]), d01, z4);
+            const f32x4 D2 = mma16(ta[2], acc_to_b(R[2] - c, z4), z4);
+            c = mma16(ld8(&sm.A[48 + l16][8 * g4]), d01, z4);
+            c = mma16(ld8(&sm.A[48 + l16][32 + 8 * g4]), acc_to_b(D2, z4), c);
+            const f32x4 D3 = mma16(ta[3], acc_to_b(R[3] - c, z4), z4);
+            d23 = acc_to_b(D2, D3);
+            st4(&sm.Dt[16 * u + l16][4 * g4], D0[0], D0[1], D0[2], D0[3]);
+            st4(&sm.Dt[16 * u + l16][16 + 4 * g4], D1[0], D1[1], D1[2], D1[3]);
+            st4(&sm.Dt[16 * u + l16][32 + 4 * g4], D2[0], D2[1], D2[2], D2[3]);
+            st4(&sm.Dt[16 * u + l16][48 + 4 * g4], D3[0], D3[1], D3[2], D3[3]);
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 y = z4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    y = mma16(ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]),
+                              ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]), y);
+                Y[b] = y;
+            }
+        }
+        __syncthreads();
+
+        // ---- 5b: waves 2, 3: O = scale (Y + P Delta); chain waves: the state update
+        if (!chain) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 acc = Y[b];
+#pragma unroll
+                for (int s = 0; s <= b / 2; ++s)
+                    acc = mma16(ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]),
+                                ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]), acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * b + 4 * g4 + e;
+                    if (r < len) op[((c0 + r) * Hv + h) * Dv + j0 + 16 * u + l16] = (__bf16)(a.scale * acc[e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = m[t][e] * sm.eg[16 * t + 4 * g4 + e];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    // A operand (K o e^{G_last - G})^T: rows are key channels, read down columns
+                    const __bf16* base = &sm.Kd[32 * s + 8 * g4 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
+                    const bf16x8 ka = cat(trld(base), trld(base + 4 * OP));
+                    acc = mma16(ka, s ? d23 : d01, acc);
+                }
+                m[t] = acc;
+                st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (chain && a.hT) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.hT[((long)nh * HK + 16 * t + 4 * g4 + e) * Dv + j0 + 16 * u + l16] = m[t][e];
+    }
+}
+
 }  // namespace
 
-bool prefill_chg_supported(const PrefillArgs& a) {
-    const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.o;
+// chunks of all sequences together: a bound that holds for a batch of rows and for packed
+// sequences (each sequence adds at most one partial chunk)
+static long chg_chunk_bound(const PrefillArgs& a) {
+    const long rows = (long)a.B * (((long)a.T + CC - 1) / CC);
+    const long packed = ((long)a.B * a.T + (long)(CC - 1) * a.N) / CC + 1;
+    return rows > packed ? rows : packed;
+}
+
+static bool chg_shape_ok(const PrefillArgs& a) {
     // buffer offsets are 32-bit: a sequence plus the chunk fetched past its end must span
     // less than 2 GiB of every stream (g, fp32 per key channel, is the widest)
     const int hmax = a.Hqk > a.Hv ? a.Hqk : a.Hv;
     const long span = ((long)a.T + 2 * CC) * hmax * (HK * 4 > a.Dv * 2 ? HK * 4 : a.Dv * 2);
-    return a.g_per_key && a.g && a.bf16 && a.Dk == HK && a.Dv >= SL && a.Dv % SL == 0 &&
-           a.C == CC && (al & 15) == 0 && ((uintptr_t)a.g & 7) == 0 && span < (1L << 31);
+    return a.g_per_key && a.bf16 && a.Dk == HK && a.Dv >= SL && a.Dv % SL == 0 && a.C == CC &&
+           span < (1L << 31);
+}
+
+bool prefill_chg_supported(const PrefillArgs& a) {
+    const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.o;
+    return chg_shape_ok(a) && a.g && (al & 15) == 0 && ((uintptr_t)a.g & 7) == 0;
+}
+
+size_t prefill_chg_workspace_bytes(const PrefillArgs& a) {
+    if (!chg_shape_ok(a)) return 0;
+    return (size_t)chg_chunk_bound(a) * a.Hv * OP_BYTES;
 }
 
 hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s) {
     const long blocks = (long)a.N * a.Hv * (a.Dv / SL);
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (blocks > 0) hipLaunchKernelGGL(prefill_chg_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+    if (blocks == 0) return hipGetLastError();
+    const size_t need = prefill_chg_workspace_bytes(a);
+    if (need > 0 && a.ws && a.ws_bytes >= need && ((uintptr_t)a.ws & 15) == 0) {
+        // two kernels: every chunk's operands at once, then the chain over the chunks
+        const long prep = chg_chunk_bound(a) * a.Hv;
+        if (prep > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(chg_prep_kernel, dim3((unsigned)prep), dim3(NTH), 0, s, a);
+        hipLaunchKernelGGL(chg_chain_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(prefill_chg_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -257,3 +257,22 @@ def test_prefill_channel_gates_graph_replay():
         assert torch.equal(o, ref[0]) and torch.equal(fs, ref[1]), f"replay {rep} differs"
     o_ref, s_ref = _oracle(x)
     _check(x, host(o), host(fs), o_ref, s_ref)
+
+
+def test_prefill_channel_gates_without_workspace():
+    """With less workspace than the query returns, the matrix-core path runs as one kernel
+    (operands formed inside the chunk loop); both forms agree with the oracle."""
+    _say("channel gates prefill: one kernel vs two")
+    x = make_case(B=1, Hqk=2, Hv=4, Dk=128, dtype="bf16", seqlens=[130, 0, 64, 1, 200],
+                  g_scale=0.3, init_std=0.1, seed=31, name="chg_nows", g_per_key=True)
+    d = to_inputs(x)
+    need = dn.workspace_bytes(1, x.T, 2, 4, 128, 128, torch.bfloat16, num_seqs=5, g_per_key=True)
+    assert need > 0
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    o1, s1 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], cu_seqlens=d["cu"],
+                          workspace=small)
+    o2, s2 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], cu_seqlens=d["cu"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle(x)
+    _check(x, host(o1), host(s1), o_ref, s_ref)
+    _check(x, host(o2), host(s2), o_ref, s_ref)
