@@ -323,7 +323,7 @@ def main():
                    "algorithmic_bytes": dec_chg_b,
                    "traffic": load_traffic("decode_channel_gates_bytes_per_call")},
         "prefill": {"workload": "B4 H16 T2048 d128 bf16, final state returned",
-                    "kernel": "prefill_chg_kernel (matrix cores, 64-token chunks)",
+                    "kernel": "chg_prep_kernel + chg_chain_kernel (matrix cores, 64-token chunks)",
                     "us_per_call": pre_chg_us, "tokens_per_s": tokens / (pre_chg_us * 1e-6),
                     "hbm_frac": pre_chg_b / (pre_chg_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
     }

@@ -126,9 +126,10 @@ typedef struct {
  *                                   be 1), or NULL: each batch row is one sequence.
  *                                   A sequence of length 0 returns its initial state.
  *   o              [B, T, Hv, Dv]   dtype, written for every token
- *   workspace      device scratch of at least dn_chunk_fwd_workspace_bytes(shape)
- *                                   bytes (may be NULL when that is 0); contents on
- *                                   entry are ignored, on exit undefined
+ *   workspace      device scratch of dn_chunk_fwd_workspace_bytes(shape) bytes, or
+ *                                   NULL (with less, the per-key-channel path runs as
+ *                                   one slower kernel); contents on entry are ignored,
+ *                                   on exit undefined; calls that share one overlap-race
  *
  * Errors: DN_ERR_INVALID_ARG (null required pointer, non-positive sizes, Hv % Hqk,
  * B != 1 or num_seqs < 1 with cu_seqlens, num_seqs != B without, misaligned
@@ -143,8 +144,11 @@ dn_status dn_chunk_fwd(const dn_shape* shape,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
-/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none; every
- * current path keeps its intermediates on chip and returns 0). */
+/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none).  Only bf16
+ * prompts with DN_GATE_PER_KEY at Dk = 128, Dv a multiple of 32 and 64-token chunks use
+ * one: each (chunk, value head) keeps its state-independent operands there (68,352 B) for
+ * the sequential pass.  Given less, dn_chunk_fwd computes the same result in one kernel
+ * that forms those operands inside its chunk loop (slower). */
 size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
 
 /*
