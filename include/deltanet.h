@@ -129,7 +129,7 @@ typedef struct {
  *   workspace      device scratch of dn_chunk_fwd_workspace_bytes(shape) bytes, or
  *                                   NULL (with less, the per-key-channel path runs as
  *                                   one slower kernel); contents on entry are ignored,
- *                                   on exit undefined; calls that share one overlap-race
+ *                                   on exit undefined (two calls in flight on one workspace race)
  *
  * Errors: DN_ERR_INVALID_ARG (null required pointer, non-positive sizes, Hv % Hqk,
  * B != 1 or num_seqs < 1 with cu_seqlens, num_seqs != B without, misaligned
