@@ -530,42 +530,42 @@ __device__ long first_chunk(const PrefillArgs& a, int n) {
     return acc;
 }
 
-__global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a) {
+// One workgroup per CU walks the (chunk, value head) items, item = chunk * Hv + head; the
+// next item's inputs are requested as soon as the current one's are consumed.
+__global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitems) {
     __shared__ __align__(16) ChgSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int Hv = a.Hv;
     const int u = w & 1;
-    const long gid = blockIdx.x / Hv;
-    const int h = blockIdx.x % Hv;
-    int n;
-    long cix;
-    if (!chunk_of(a, gid, n, cix)) return;   // past the last chunk (the grid is a bound)
-    const int hq = h / (Hv / a.Hqk);
     const __bf16* qp = static_cast<const __bf16*>(a.q);
     const __bf16* kp = static_cast<const __bf16*>(a.k);
-    long bos, eos;
-    seq_range(a.cu, n, a.T, bos, eos);
-    const long c0 = bos + cix * CC;
-    (void)u;
-    (void)l16;
-    (void)g4;
 
+    // A's and P's tiles above the diagonal stay zero (only the tiles on and below it are written)
     for (int e = tid; e < CC * AP; e += NTH) {
         (&sm.P[0][0])[e] = (__bf16)0.f;
         (&sm.A[0][0])[e] = (__bf16)0.f;
     }
 
-    const long L = eos - bos;
-    const uint32_t g_tok = (uint32_t)Hv * HK * 4, kq_tok = (uint32_t)a.Hqk * HK * 2, b_tok = (uint32_t)Hv * 4;
-    const __amdgpu_buffer_rsrc_t gs = rsrc(a.g + (bos * Hv + h) * HK, L > 0 ? (L - 1) * g_tok + HK * 4 : 0);
-    const __amdgpu_buffer_rsrc_t ks = rsrc(kp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
-    const __amdgpu_buffer_rsrc_t qs = rsrc(qp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
-    const __amdgpu_buffer_rsrc_t bs = rsrc(a.beta + bos * Hv + h, L > 0 ? (L - 1) * b_tok + 4 : 0);
     float2 rg[16];
     uint32_t rk[16], rq[16];
     float rb;
-    {
+    // requests item `item`'s inputs: block w's tokens, key channels 2 lane and 2 lane + 1;
+    // false past the last chunk (items are in chunk order, so every later one is too)
+    auto fetch = [&](long item) -> bool {
+        int n;
+        long cix;
+        if (item >= nitems || !chunk_of(a, item / Hv, n, cix)) return false;
+        const int h = (int)(item % Hv);
+        const int hq = h / (Hv / a.Hqk);
+        long bos, eos;
+        seq_range(a.cu, n, a.T, bos, eos);
+        const long L = eos - bos;
+        const uint32_t g_tok = (uint32_t)Hv * HK * 4, kq_tok = (uint32_t)a.Hqk * HK * 2, b_tok = (uint32_t)Hv * 4;
+        const __amdgpu_buffer_rsrc_t gs = rsrc(a.g + (bos * Hv + h) * HK, L > 0 ? (L - 1) * g_tok + HK * 4 : 0);
+        const __amdgpu_buffer_rsrc_t ks = rsrc(kp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+        const __amdgpu_buffer_rsrc_t qs = rsrc(qp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+        const __amdgpu_buffer_rsrc_t bs = rsrc(a.beta + bos * Hv + h, L > 0 ? (L - 1) * b_tok + 4 : 0);
         const uint32_t c = (uint32_t)(cix * CC);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -576,8 +576,12 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a) {
             rq[i] = __builtin_amdgcn_raw_buffer_load_b32(qs, r * kq_tok + 4 * lane, 0, 0);
         }
         rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (c + (tid & 63)) * b_tok, 0, 0));
-    }
-    {
+        return true;
+    };
+
+    long item = blockIdx.x;
+    bool have = fetch(item);
+    while (have) {
         // ---- 1: block sums of g, k and q as floats (normalised if asked), V and beta
         float2 L[16], kf[16], qf[16];
         {
@@ -621,6 +625,8 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a) {
         }
         __syncthreads();
 
+        const long next = item + gridDim.x;
+        const bool have_next = fetch(next);   // lands while this item is worked
         // ---- 2: operands
         float2 Z[NB], Zw = make_float2(0.f, 0.f), Gl = make_float2(0.f, 0.f);
 #pragma unroll
@@ -788,9 +794,8 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a) {
         }
         __syncthreads();
 
-
-        // ---- out: this chunk's operands to its workspace record
-        char* rec = static_cast<char*>(a.ws) + (gid * Hv + h) * OP_BYTES;
+        // ---- out: this item's operands to its workspace record
+        char* rec = static_cast<char*>(a.ws) + item * OP_BYTES;
         for (int e = tid; e < 1024; e += NTH) {
             const int r = e >> 4, p = e & 15;
             *reinterpret_cast<u32x4v*>(rec + OP_KE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[r][8 * p]);
@@ -812,6 +817,9 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a) {
             const int e = tid - 160;
             *reinterpret_cast<u32x4v*>(rec + OP_BETA + e * 16) = *reinterpret_cast<const u32x4v*>(&sm.beta[4 * e]);
         }
+        __syncthreads();   // the next item rewrites LDS
+        item = next;
+        have = have_next;
     }
 }
 
@@ -1042,9 +1050,13 @@ hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s) {
     const size_t need = prefill_chg_workspace_bytes(a);
     if (need > 0 && a.ws && a.ws_bytes >= need && ((uintptr_t)a.ws & 15) == 0) {
         // two kernels: every chunk's operands at once, then the chain over the chunks
-        const long prep = chg_chunk_bound(a) * a.Hv;
-        if (prep > 0x7fffffffL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(chg_prep_kernel, dim3((unsigned)prep), dim3(NTH), 0, s, a);
+        const long items = chg_chunk_bound(a) * a.Hv;
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        const long prep = items < cus ? items : cus;   // one workgroup per CU (its LDS allows no more)
+        hipLaunchKernelGGL(chg_prep_kernel, dim3((unsigned)prep), dim3(NTH), 0, s, a, items);
         hipLaunchKernelGGL(chg_chain_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
     } else {
         hipLaunchKernelGGL(prefill_chg_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
