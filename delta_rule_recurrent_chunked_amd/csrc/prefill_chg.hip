@@ -23,7 +23,12 @@
 // diagonal tiles of A and P are formed from one exponential per pair and channel instead.
 // Every other operand (K o e^G, Q o e^G, K o e^{G_last - G}) has factors at most 1.
 //
-// One workgroup of four waves per (sequence, value head, 32 value columns).  Per chunk:
+// Two forms of the same arithmetic.  With the workspace dn_chunk_fwd_workspace_bytes
+// returns, chg_prep_kernel runs steps 1 to 4 below once per (chunk, value head) for all
+// chunks at once and chg_chain_kernel runs step 5 over each sequence's chunks (see the
+// two-kernel form further down).  Without it, prefill_chg_kernel does everything in its
+// chunk loop:  one workgroup of four waves per (sequence, value head, 32 value columns).
+// Per chunk:
 //   1  every wave takes the g, k, q of one 16-token block (two channels per lane), sums g
 //      over the block and stages V and beta; the next chunk's loads are then issued
 //   2  operands into LDS (bf16); wave b forms block b's diagonal tiles of A and P from
