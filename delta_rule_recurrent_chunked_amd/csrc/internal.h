@@ -24,7 +24,7 @@ struct PrefillArgs {
     float* hT;                      // may be null (no final state); may alias h0
     const int32_t* cu;              // may be null (each batch row is a sequence)
     void* o;
-    void* ws;                       // caller's workspace (no current path needs one)
+    void* ws;                       // caller's workspace (the two-kernel channel-gate path)
     size_t ws_bytes;
 };
 

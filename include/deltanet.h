@@ -117,7 +117,9 @@ typedef struct {
  *   beta           [B, T, Hv]       fp32 write strengths
  *   g              [B, T, Hv]       fp32 log decays, or NULL for the plain rule;
  *                  [B, T, Hv, Dk]   with DN_GATE_PER_KEY (never NULL then).  Channel
- *                                   gates run on the vector-ALU path in 32-token chunks.
+ *                                   gates run on the matrix cores for bf16 at Dk = 128,
+ *                                   Dv a multiple of 32 and 64-token chunks, else on the
+ *                                   vector ALUs in 32-token chunks.
  *   initial_state  [N, Hv, Dk, Dv]  fp32 state each sequence starts from, or NULL
  *                                   for the zero state (a fresh prompt)
  *   final_state    [N, Hv, Dk, Dv]  fp32 state after each sequence's last token,
@@ -222,7 +224,7 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
                            float* d_initial_state, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* Bytes of workspace dn_recurrent_bwd needs: each 32-column slice's share of dq, dk,
+/* Bytes of workspace dn_recurrent_bwd needs: each value-column slice's share of dq, dk,
  * dbeta and dg before they are added in a fixed order (the shape's flags matter: dg per
  * key channel takes Dk floats per token and head). */
 size_t dn_recurrent_bwd_workspace_bytes(const dn_shape* shape);
