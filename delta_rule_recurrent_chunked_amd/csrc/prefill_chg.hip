@@ -37,8 +37,9 @@
 //   3  A (waves 0, 1) and P (waves 2, 3) below the diagonal on the matrix cores
 //   4  K o e^G and Q o e^G over the column operands
 //   5  waves 0, 1 hold 16 state columns each in accumulators: X = (K o e^G) M0,
-//      R, Delta by block substitution; waves 2, 3 form (Q o e^G) M0;
-//      then waves 2, 3 add P Delta and store O, waves 0, 1 update the state.
+//      R, Delta by block substitution; waves 2, 3 form (Q o e^G) M0 transposed;
+//      then waves 2, 3 add Delta^T P^T and store O (8 bytes: four columns of one token
+//      per lane), waves 0, 1 update the state.
 #include "internal.h"
 #include "mfma_ops.h"
 
@@ -438,9 +439,9 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
             for (int b = 0; b < NB; ++b) {
                 f32x4 y = z4;
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    y = mma16(ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]),
-                              ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]), y);
+                for (int s = 0; s < 4; ++s)   // transposed: lane holds 4 columns of one token
+                    y = mma16(ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]),
+                              ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]), y);
                 Y[b] = y;
             }
         }
@@ -452,14 +453,13 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
             for (int b = 0; b < NB; ++b) {
                 f32x4 acc = Y[b];
 #pragma unroll
-                for (int s = 0; s <= b / 2; ++s)
-                    acc = mma16(ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]),
-                                ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]), acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * b + 4 * g4 + e;
-                    if (r < len) op[((c0 + r) * Hv + h) * Dv + j0 + 16 * u + l16] = (__bf16)(a.scale * acc[e]);
-                }
+                for (int s = 0; s <= b / 2; ++s)   // O^T = Delta^T P^T + Y^T
+                    acc = mma16(ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]),
+                                ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]), acc);
+                const int r = 16 * b + l16;   // token; columns 16 u + 4 g4 .. + 3
+                if (r < len)
+                    st4(op + ((c0 + r) * Hv + h) * Dv + j0 + 16 * u + 4 * g4, a.scale * acc[0],
+                        a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]);
             }
         } else {
 #pragma unroll
@@ -967,9 +967,9 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
             for (int b = 0; b < NB; ++b) {
                 f32x4 y = z4;
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    y = mma16(ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]),
-                              ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]), y);
+                for (int s = 0; s < 4; ++s)   // transposed: lane holds 4 columns of one token
+                    y = mma16(ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]),
+                              ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]), y);
                 Y[b] = y;
             }
         }
@@ -981,14 +981,13 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
             for (int b = 0; b < NB; ++b) {
                 f32x4 acc = Y[b];
 #pragma unroll
-                for (int s = 0; s <= b / 2; ++s)
-                    acc = mma16(ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]),
-                                ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]), acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * b + 4 * g4 + e;
-                    if (r < len) op[((c0 + r) * Hv + h) * Dv + j0 + 16 * u + l16] = (__bf16)(a.scale * acc[e]);
-                }
+                for (int s = 0; s <= b / 2; ++s)   // O^T = Delta^T P^T + Y^T
+                    acc = mma16(ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]),
+                                ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]), acc);
+                const int r = 16 * b + l16;   // token; columns 16 u + 4 g4 .. + 3
+                if (r < len)
+                    st4(op + ((c0 + r) * Hv + h) * Dv + j0 + 16 * u + 4 * g4, a.scale * acc[0],
+                        a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]);
             }
         } else {
 #pragma unroll
