@@ -1020,11 +1020,12 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
 
 }  // namespace
 
-// chunks of all sequences together: a bound that holds for a batch of rows and for packed
-// sequences (each sequence adds at most one partial chunk)
+// chunks of all sequences together: exact for a batch of rows, a bound for packed
+// sequences (only B = 1 packs; each sequence adds at most one partial chunk)
 static long chg_chunk_bound(const PrefillArgs& a) {
     const long rows = (long)a.B * (((long)a.T + CC - 1) / CC);
-    const long packed = ((long)a.B * a.T + (long)(CC - 1) * a.N) / CC + 1;
+    if (a.B != 1) return rows;
+    const long packed = ((long)a.T + (long)(CC - 1) * a.N) / CC + 1;
     return rows > packed ? rows : packed;
 }
 

@@ -189,3 +189,19 @@ def test_reverse_pass_host_checks():
     slices, per_tok = 8, 2 * 8 * plain.Hv   # 8-column slices
     assert lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(plain)) == slices * per_tok * (2 * 64 + 2) * 4
     assert lib.dn_recurrent_bwd_workspace_bytes(ctypes.byref(chg)) == slices * per_tok * (3 * 64 + 1) * 4
+
+
+def test_channel_gate_prompt_workspace_query():
+    """dn_chunk_fwd_workspace_bytes: 68,352 bytes per (chunk, value head) for a bf16 Dk = 128
+    prompt with a log decay per key channel, over a chunk bound that holds for rows and for
+    packed sequences; zero for every shape that runs without one."""
+    import torch
+    rec = 68352
+    # a batch of rows: exactly B * ceil(T / 64) chunks
+    assert dn.workspace_bytes(4, 2048, 16, 16, 128, 128, torch.bfloat16, g_per_key=True) == 4 * 32 * 16 * rec
+    # packed: 5 sequences in 300 tokens -> at most (300 + 63 * 5) // 64 + 1 = 10 chunks
+    assert dn.workspace_bytes(1, 300, 2, 4, 128, 128, torch.bfloat16, num_seqs=5, g_per_key=True) == 10 * 4 * rec
+    assert dn.workspace_bytes(4, 2048, 16, 16, 128, 128, torch.bfloat16) == 0
+    assert dn.workspace_bytes(4, 2048, 16, 16, 128, 128, torch.float32, g_per_key=True) == 0
+    assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, torch.bfloat16, g_per_key=True) == 0
+    assert dn.workspace_bytes(4, 2048, 16, 16, 128, 128, torch.bfloat16, chunk_size=32, g_per_key=True) == 0
