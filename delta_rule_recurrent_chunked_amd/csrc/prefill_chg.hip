@@ -828,8 +828,31 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
     }
 }
 
+// LDS of the chain kernel: the operands step 5a reads are double-buffered so that the
+// next chunk's arrive while this one is worked; those of step 5b are single.
+struct ChainSmem {
+    __bf16 Ke[2][CC][OP];      // K o e^G
+    __bf16 Qe[2][CC][OP];      // Q o e^G
+    __bf16 A[2][CC][AP];
+    __bf16 Tb[2][NB][16][TP];
+    __bf16 V[2][CC][VP];
+    float beta[2][CC];
+    __bf16 Kd[CC][OP];         // K o e^{G_last - G}
+    __bf16 P[CC][AP];
+    float eg[HK];
+    __bf16 Mt[SL][OP];
+    __bf16 Dt[SL][DP];
+};
+
+// Waves 0, 1 run the chain (16 state columns each in accumulators).  Waves 2, 3 load every
+// chunk's record and V slice one chunk ahead into registers and store them to LDS in
+// their slack, form (Q o e^G) M0 and store O.  Two barriers per chunk:
+//   X  chain: X, R, Delta from A/B buffer c % 2   |  2, 3: K o e^{G_last-G}, P, e^{G_last} of
+//      chunk c to LDS, request chunk c + 1, (Q o e^G) M0
+//   Y  chain: the state update                    |  2, 3: O; chunk c + 1's step-5a operands
+//                                                 |  to buffer (c + 1) % 2
 __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
-    __shared__ __align__(16) ChgSmem sm;
+    __shared__ __align__(16) ChainSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int Hv = a.Hv, Dv = a.Dv;
@@ -847,88 +870,27 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
     const int h = nh % Hv, n = nh / Hv;
     const int j0 = slice * SL;
     const int u = w & 1;
-    const bool chain = w < 2;
-    const __bf16* vp = static_cast<const __bf16*>(a.v);
-    __bf16* op = static_cast<__bf16*>(a.o);
     long bos, eos;
     seq_range(a.cu, n, a.T, bos, eos);
-    const long first = first_chunk(a, n);
     const long nch = (eos - bos + CC - 1) / CC;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    f32x4 m[8];
+    if (w < 2) {
+        // ------------------------------------------------------------ chain waves
+        f32x4 m[8];   // rows 16t + 4 g4 + e, column 16u + l16 of the slice
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int x = 16 * t + 4 * g4 + e;
-            m[t][e] = (chain && a.h0) ? a.h0[((long)nh * HK + x) * Dv + j0 + 16 * u + l16] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const int x = 16 * t + 4 * g4 + e;
+                m[t][e] = a.h0 ? a.h0[((long)nh * HK + x) * Dv + j0 + 16 * u + l16] : 0.f;
+            }
+            st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], m[t][0], m[t][1], m[t][2], m[t][3]);
         }
-        if (chain) st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], m[t][0], m[t][1], m[t][2], m[t][3]);
-    }
-
-    // one chunk's record and V slice in registers: pieces tid + 256 i of K o e^G, Q o e^G,
-    // K o e^{G_last - G} (4 each), A and P (2 each), one of the inverses / e^{G_last} / beta
-    const long L = eos - bos;
-    const uint32_t v_tok = (uint32_t)Hv * Dv * 2;
-    const __amdgpu_buffer_rsrc_t vs = rsrc(vp + (bos * Hv + h) * Dv + j0, L > 0 ? (L - 1) * v_tok + SL * 2 : 0);
-    u32x4v rke[4], rqe[4], rkd[4], ra[2], rp[2], rx = u32x4v{0u, 0u, 0u, 0u};
-    bf16x8 rv;
-    auto fetch = [&](long c) {
-        const char* rec = static_cast<const char*>(a.ws) + ((first + c) * Hv + h) * OP_BYTES;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + NTH * i, r = e >> 4, p = e & 15;
-            rke[i] = *reinterpret_cast<const u32x4v*>(rec + OP_KE + r * 256 + p * 16);
-            rqe[i] = *reinterpret_cast<const u32x4v*>(rec + OP_QE + r * 256 + p * 16);
-            rkd[i] = *reinterpret_cast<const u32x4v*>(rec + OP_KD + r * 256 + p * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + NTH * i, r = e >> 3, p = e & 7;
-            ra[i] = *reinterpret_cast<const u32x4v*>(rec + OP_A + r * 128 + p * 16);
-            rp[i] = *reinterpret_cast<const u32x4v*>(rec + OP_P + r * 128 + p * 16);
-        }
-        if (tid < 128) rx = *reinterpret_cast<const u32x4v*>(rec + OP_TB + tid * 16);
-        else if (tid < 176) rx = *reinterpret_cast<const u32x4v*>(rec + OP_EG + (tid - 128) * 16);
-        rv = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                 vs, (uint32_t)(c * CC + (tid >> 2)) * v_tok + 16 * (tid & 3), 0, 0));
-    };
-    if (nch > 0) fetch(0);
-
-    for (long cix = 0; cix < nch; ++cix) {
-        const long c0 = bos + cix * CC;
-        const int len = (int)min((long)CC, eos - c0);
-        // the chunk's record into LDS (the previous chunk's step 5 is done with it)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + NTH * i, r = e >> 4, p = e & 15;
-            *reinterpret_cast<u32x4v*>(&sm.Kc[r][8 * p]) = rke[i];
-            *reinterpret_cast<u32x4v*>(&sm.Kc[CC + r][8 * p]) = rqe[i];
-            *reinterpret_cast<u32x4v*>(&sm.Kd[r][8 * p]) = rkd[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + NTH * i, r = e >> 3, p = e & 7;
-            *reinterpret_cast<u32x4v*>(&sm.A[r][8 * p]) = ra[i];
-            *reinterpret_cast<u32x4v*>(&sm.P[r][8 * p]) = rp[i];
-        }
-        if (tid < 128) {
-            const int b = tid >> 5, r = (tid >> 1) & 15, p = tid & 1;
-            *reinterpret_cast<u32x4v*>(&sm.Tb[b][r][8 * p]) = rx;
-        } else if (tid < 160) {
-            *reinterpret_cast<u32x4v*>(&sm.eg[4 * (tid - 128)]) = rx;
-        } else if (tid < 176) {
-            *reinterpret_cast<u32x4v*>(&sm.beta[4 * (tid - 160)]) = rx;
-        }
-        *reinterpret_cast<bf16x8*>(&sm.V[tid >> 2][8 * (tid & 3)]) = rv;
-        __syncthreads();
-        if (cix + 1 < nch) fetch(cix + 1);   // lands while this chunk is worked
-
-        // ---- 5a: chain waves: R and Delta; waves 2, 3: (Q o e^G) M0
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 Y[NB] = {z4, z4, z4, z4};
-        bf16x8 d01 = zero8(), d23 = zero8();
-        if (chain) {
+        __syncthreads();   // buffer 0 holds chunk 0's step-5a operands
+        for (long cix = 0; cix < nch; ++cix) {
+            const int cb = (int)(cix & 1);
+            // X: R = beta (V - (K o e^G) M0), Delta by block substitution
             bf16x8 mb[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) mb[s] = acc_to_b(m[2 * s], m[2 * s + 1]);
@@ -937,59 +899,33 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
             for (int b = 0; b < NB; ++b) {
                 f32x4 x = z4;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) x = mma16(ld8(&sm.Kc[16 * b + l16][32 * s + 8 * g4]), mb[s], x);
+                for (int s = 0; s < 4; ++s) x = mma16(ld8(&sm.Ke[cb][16 * b + l16][32 * s + 8 * g4]), mb[s], x);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * b + 4 * g4 + e;
-                    R[b][e] = sm.beta[r] * ((float)sm.V[r][16 * u + l16] - x[e]);
+                    R[b][e] = sm.beta[cb][r] * ((float)sm.V[cb][r][16 * u + l16] - x[e]);
                 }
             }
             bf16x8 ta[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) ta[b] = g4 < 2 ? ld8(&sm.Tb[b][l16][8 * g4]) : zero8();
+            for (int b = 0; b < NB; ++b) ta[b] = g4 < 2 ? ld8(&sm.Tb[cb][b][l16][8 * g4]) : zero8();
             // Delta_b = T_bb (R_b - sum_{b'<b} A_bb' Delta_b')
             const f32x4 D0 = mma16(ta[0], acc_to_b(R[0], z4), z4);
-            f32x4 c = mma16(ld8(&sm.A[16 + l16][8 * g4]), acc_to_b(D0, z4), z4);
+            f32x4 c = mma16(ld8(&sm.A[cb][16 + l16][8 * g4]), acc_to_b(D0, z4), z4);
             const f32x4 D1 = mma16(ta[1], acc_to_b(R[1] - c, z4), z4);
-            d01 = acc_to_b(D0, D1);
-            c = mma16(ld8(&sm.A[32 + l16][8 * g4]), d01, z4);
+            const bf16x8 d01 = acc_to_b(D0, D1);
+            c = mma16(ld8(&sm.A[cb][32 + l16][8 * g4]), d01, z4);
             const f32x4 D2 = mma16(ta[2], acc_to_b(R[2] - c, z4), z4);
-            c = mma16(ld8(&sm.A[48 + l16][8 * g4]), d01, z4);
-            c = mma16(ld8(&sm.A[48 + l16][32 + 8 * g4]), acc_to_b(D2, z4), c);
+            c = mma16(ld8(&sm.A[cb][48 + l16][8 * g4]), d01, z4);
+            c = mma16(ld8(&sm.A[cb][48 + l16][32 + 8 * g4]), acc_to_b(D2, z4), c);
             const f32x4 D3 = mma16(ta[3], acc_to_b(R[3] - c, z4), z4);
-            d23 = acc_to_b(D2, D3);
+            const bf16x8 d23 = acc_to_b(D2, D3);
             st4(&sm.Dt[16 * u + l16][4 * g4], D0[0], D0[1], D0[2], D0[3]);
             st4(&sm.Dt[16 * u + l16][16 + 4 * g4], D1[0], D1[1], D1[2], D1[3]);
             st4(&sm.Dt[16 * u + l16][32 + 4 * g4], D2[0], D2[1], D2[2], D2[3]);
             st4(&sm.Dt[16 * u + l16][48 + 4 * g4], D3[0], D3[1], D3[2], D3[3]);
-        } else {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                f32x4 y = z4;
-#pragma unroll
-                for (int s = 0; s < 4; ++s)   // transposed: lane holds 4 columns of one token
-                    y = mma16(ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]),
-                              ld8(&sm.Kc[CC + 16 * b + l16][32 * s + 8 * g4]), y);
-                Y[b] = y;
-            }
-        }
-        __syncthreads();
-
-        // ---- 5b: waves 2, 3: O = scale (Y + P Delta); chain waves: the state update
-        if (!chain) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                f32x4 acc = Y[b];
-#pragma unroll
-                for (int s = 0; s <= b / 2; ++s)   // O^T = Delta^T P^T + Y^T
-                    acc = mma16(ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]),
-                                ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]), acc);
-                const int r = 16 * b + l16;   // token; columns 16 u + 4 g4 .. + 3
-                if (r < len)
-                    st4(op + ((c0 + r) * Hv + h) * Dv + j0 + 16 * u + 4 * g4, a.scale * acc[0],
-                        a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]);
-            }
-        } else {
+            __syncthreads();
+            // Y: M1 = diag(e^{G_last}) M0 + (K o e^{G_last - G})^T Delta
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 f32x4 acc;
@@ -1005,16 +941,127 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
                 m[t] = acc;
                 st4(&sm.Mt[16 * u + l16][16 * t + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
             }
+            __syncthreads();
         }
-        __syncthreads();
-    }
-
-    if (chain && a.hT) {
+        if (a.hT) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.hT[((long)nh * HK + 16 * t + 4 * g4 + e) * Dv + j0 + 16 * u + l16] = m[t][e];
+                for (int e = 0; e < 4; ++e)
+                    a.hT[((long)nh * HK + 16 * t + 4 * g4 + e) * Dv + j0 + 16 * u + l16] = m[t][e];
+        }
+    } else {
+        // ------------------------------------------------ loader and output waves
+        const int lt = tid - 128;   // 0 .. 127
+        const __bf16* vp = static_cast<const __bf16*>(a.v);
+        __bf16* op = static_cast<__bf16*>(a.o);
+        const long first = first_chunk(a, n);
+        const long L = eos - bos;
+        const uint32_t v_tok = (uint32_t)Hv * Dv * 2;
+        const __amdgpu_buffer_rsrc_t vs = rsrc(vp + (bos * Hv + h) * Dv + j0, L > 0 ? (L - 1) * v_tok + SL * 2 : 0);
+        // pieces (16 bytes) of one chunk: step 5a's K o e^G, Q o e^G (8 each), A (4), an inverse
+        // piece, V (2), beta (lt < 16); step 5b's K o e^{G_last - G} (8), P (4), e^{G_last} (lt < 32)
+        u32x4v rke[8], rqe[8], ra[4], rtb, rbe = u32x4v{0u, 0u, 0u, 0u};
+        u32x4v rkd[8], rp[4], reg = u32x4v{0u, 0u, 0u, 0u};
+        bf16x8 rv[2];
+        auto fetch = [&](long c) {
+            const char* rec = static_cast<const char*>(a.ws) + ((first + c) * Hv + h) * OP_BYTES;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = lt + 128 * i, r = e >> 4, p = e & 15;
+                rke[i] = *reinterpret_cast<const u32x4v*>(rec + OP_KE + r * 256 + p * 16);
+                rqe[i] = *reinterpret_cast<const u32x4v*>(rec + OP_QE + r * 256 + p * 16);
+                rkd[i] = *reinterpret_cast<const u32x4v*>(rec + OP_KD + r * 256 + p * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lt + 128 * i, r = e >> 3, p = e & 7;
+                ra[i] = *reinterpret_cast<const u32x4v*>(rec + OP_A + r * 128 + p * 16);
+                rp[i] = *reinterpret_cast<const u32x4v*>(rec + OP_P + r * 128 + p * 16);
+            }
+            rtb = *reinterpret_cast<const u32x4v*>(rec + OP_TB + lt * 16);
+            if (lt < 16) rbe = *reinterpret_cast<const u32x4v*>(rec + OP_BETA + lt * 16);
+            if (lt < 32) reg = *reinterpret_cast<const u32x4v*>(rec + OP_EG + lt * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int e = lt + 128 * i;   // row e >> 2, 16-byte piece e & 3 of the slice
+                rv[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            vs, (uint32_t)(c * CC + (e >> 2)) * v_tok + 16 * (e & 3), 0, 0));
+            }
+        };
+        auto store_a = [&](int cb) {   // step 5a's operands to buffer cb
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = lt + 128 * i, r = e >> 4, p = e & 15;
+                *reinterpret_cast<u32x4v*>(&sm.Ke[cb][r][8 * p]) = rke[i];
+                *reinterpret_cast<u32x4v*>(&sm.Qe[cb][r][8 * p]) = rqe[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lt + 128 * i, r = e >> 3, p = e & 7;
+                *reinterpret_cast<u32x4v*>(&sm.A[cb][r][8 * p]) = ra[i];
+            }
+            *reinterpret_cast<u32x4v*>(&sm.Tb[cb][lt >> 5][(lt >> 1) & 15][8 * (lt & 1)]) = rtb;
+            if (lt < 16) *reinterpret_cast<u32x4v*>(&sm.beta[cb][4 * lt]) = rbe;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int e = lt + 128 * i;
+                *reinterpret_cast<bf16x8*>(&sm.V[cb][e >> 2][8 * (e & 3)]) = rv[i];
+            }
+        };
+        auto store_b = [&]() {   // step 5b's operands
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = lt + 128 * i, r = e >> 4, p = e & 15;
+                *reinterpret_cast<u32x4v*>(&sm.Kd[r][8 * p]) = rkd[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lt + 128 * i, r = e >> 3, p = e & 7;
+                *reinterpret_cast<u32x4v*>(&sm.P[r][8 * p]) = rp[i];
+            }
+            if (lt < 32) *reinterpret_cast<u32x4v*>(&sm.eg[4 * lt]) = reg;
+        };
+        if (nch > 0) {
+            fetch(0);
+            store_a(0);
+        }
+        __syncthreads();   // buffer 0 holds chunk 0's step-5a operands
+        for (long cix = 0; cix < nch; ++cix) {
+            const int cb = (int)(cix & 1);
+            const long c0 = bos + cix * CC;
+            const int len = (int)min((long)CC, eos - c0);
+            // X: this chunk's step-5b operands, the next chunk's request, (Q o e^G) M0
+            store_b();
+            if (cix + 1 < nch) fetch(cix + 1);
+            f32x4 Y[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 y = z4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)   // transposed: lane holds 4 columns of one token
+                    y = mma16(ld8(&sm.Mt[16 * u + l16][32 * s + 8 * g4]),
+                              ld8(&sm.Qe[cb][16 * b + l16][32 * s + 8 * g4]), y);
+                Y[b] = y;
+            }
+            __syncthreads();
+            // Y: O^T = Delta^T P^T + Y^T, stored four columns per lane; the next chunk's
+            // step-5a operands to the other buffer
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4 acc = Y[b];
+#pragma unroll
+                for (int s = 0; s <= b / 2; ++s)
+                    acc = mma16(ld8(&sm.Dt[16 * u + l16][32 * s + 8 * g4]),
+                                ld8(&sm.P[16 * b + l16][32 * s + 8 * g4]), acc);
+                const int r = 16 * b + l16;
+                if (r < len)
+                    st4(op + ((c0 + r) * Hv + h) * Dv + j0 + 16 * u + 4 * g4, a.scale * acc[0],
+                        a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]);
+            }
+            if (cix + 1 < nch) store_a(cb ^ 1);
+            __syncthreads();
+        }
     }
 }
 
