@@ -506,8 +506,15 @@ constexpr long OP_EG = 67584;      // exp(G_last)        [128] fp32
 constexpr long OP_BETA = 68096;    // beta               [64] fp32
 constexpr long OP_BYTES = 68352;
 
-// Chunks are numbered sequence by sequence.  The sequence and chunk of chunk `gid`
-// (false past the last chunk), and the number of the first chunk of sequence n.
+// Record numbers.  A batch of rows numbers its chunks row by row.  Packed sequences give
+// chunk c of sequence n the number floor(cu[n] / 64) + n + c: distinct (the next
+// sequence's first number is past this one's last) and found without a scan; at most
+// T / 64 + N of them.  first_chunk(n) is sequence n's first number; chunk_of inverts the
+// numbering (false for a number no chunk takes).
+__device__ long first_chunk(const PrefillArgs& a, int n) {
+    if (!a.cu) return (long)n * (((long)a.T + CC - 1) / CC);
+    return (long)a.cu[n] / CC + n;
+}
 __device__ bool chunk_of(const PrefillArgs& a, long gid, int& n, long& c) {
     if (!a.cu) {
         const long cps = ((long)a.T + CC - 1) / CC;
@@ -516,23 +523,17 @@ __device__ bool chunk_of(const PrefillArgs& a, long gid, int& n, long& c) {
         c = gid % cps;
         return n < a.N;
     }
-    long acc = 0;
-    for (int m = 0; m < a.N; ++m) {
-        const long cnt = ((long)a.cu[m + 1] - a.cu[m] + CC - 1) / CC;
-        if (gid < acc + cnt) {
-            n = m;
-            c = gid - acc;
-            return true;
-        }
-        acc += cnt;
+    // the last sequence whose first number is at most gid (first numbers increase with n)
+    int lo = 0, hi = a.N - 1;
+    if (hi < 0 || first_chunk(a, 0) > gid) return false;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (first_chunk(a, mid) <= gid) lo = mid;
+        else hi = mid - 1;
     }
-    return false;
-}
-__device__ long first_chunk(const PrefillArgs& a, int n) {
-    if (!a.cu) return (long)n * (((long)a.T + CC - 1) / CC);
-    long acc = 0;
-    for (int m = 0; m < n; ++m) acc += ((long)a.cu[m + 1] - a.cu[m] + CC - 1) / CC;
-    return acc;
+    n = lo;
+    c = gid - first_chunk(a, lo);
+    return c < ((long)a.cu[lo + 1] - a.cu[lo] + CC - 1) / CC;
 }
 
 // One workgroup per CU walks the (chunk, value head) items, item = chunk * Hv + head; the
@@ -555,12 +556,19 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
     float2 rg[16];
     uint32_t rk[16], rq[16];
     float rb;
-    // requests item `item`'s inputs: block w's tokens, key channels 2 lane and 2 lane + 1;
-    // false past the last chunk (items are in chunk order, so every later one is too)
-    auto fetch = [&](long item) -> bool {
+    // the first item from `item` on (in steps of the grid) that a chunk takes; nitems if none
+    auto next_item = [&](long item) -> long {
         int n;
         long cix;
-        if (item >= nitems || !chunk_of(a, item / Hv, n, cix)) return false;
+        while (item < nitems && !chunk_of(a, item / Hv, n, cix)) item += gridDim.x;
+        return item;
+    };
+    // requests item `item`'s inputs (a chunk takes it): block w's tokens, key channels
+    // 2 lane and 2 lane + 1
+    auto fetch = [&](long item) {
+        int n;
+        long cix;
+        chunk_of(a, item / Hv, n, cix);
         const int h = (int)(item % Hv);
         const int hq = h / (Hv / a.Hqk);
         long bos, eos;
@@ -581,12 +589,11 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
             rq[i] = __builtin_amdgcn_raw_buffer_load_b32(qs, r * kq_tok + 4 * lane, 0, 0);
         }
         rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (c + (tid & 63)) * b_tok, 0, 0));
-        return true;
     };
 
-    long item = blockIdx.x;
-    bool have = fetch(item);
-    while (have) {
+    long item = next_item(blockIdx.x);
+    if (item < nitems) fetch(item);
+    while (item < nitems) {
         // ---- 1: block sums of g, k and q as floats (normalised if asked), V and beta
         float2 L[16], kf[16], qf[16];
         {
@@ -630,8 +637,8 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
         }
         __syncthreads();
 
-        const long next = item + gridDim.x;
-        const bool have_next = fetch(next);   // lands while this item is worked
+        const long next = next_item(item + gridDim.x);
+        if (next < nitems) fetch(next);   // lands while this item is worked
         // ---- 2: operands
         float2 Z[NB], Zw = make_float2(0.f, 0.f), Gl = make_float2(0.f, 0.f);
 #pragma unroll
@@ -824,7 +831,6 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
         }
         __syncthreads();   // the next item rewrites LDS
         item = next;
-        have = have_next;
     }
 }
 
@@ -1067,12 +1073,12 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
 
 }  // namespace
 
-// chunks of all sequences together: exact for a batch of rows, a bound for packed
-// sequences (only B = 1 packs; each sequence adds at most one partial chunk)
+// record numbers in use: exact for a batch of rows; for packed sequences (only B = 1
+// packs) the numbering above stays below T / 64 + N + 1
 static long chg_chunk_bound(const PrefillArgs& a) {
     const long rows = (long)a.B * (((long)a.T + CC - 1) / CC);
     if (a.B != 1) return rows;
-    const long packed = ((long)a.T + (long)(CC - 1) * a.N) / CC + 1;
+    const long packed = (long)a.T / CC + a.N + 1;
     return rows > packed ? rows : packed;
 }
 
