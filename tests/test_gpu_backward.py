@@ -83,3 +83,46 @@ def test_reverse_pass(name):
         err = rel_l2(host(grads[got]), ref[want])
         _say(f"  {got}: rel_l2 {err:.2e}")
         assert err <= tol(x), got
+
+
+def test_reverse_pass_graph_replay():
+    """dn_recurrent_bwd (reverse kernel, slice sums and, with the in-call normalisation, the
+    normalisation's reverse) captured in a HIP graph replays to the eager gradients, every
+    replay, with eager work and synchronisations between the replays."""
+    _say("reverse pass graph replay")
+    x = make_case(B=1, T=90, Hqk=2, Hv=2, Dk=64, Dv=64, dtype="f32", g_scale=0.1, init_std=0.2,
+                  seed=54, name="bwd_graph", g_per_key=True, qk_raw=True)
+    d = to_inputs(x)
+    rng = np.random.default_rng(55)
+    do = dev_tensor(rng.standard_normal((1, 90, 2, 64)).astype(np.float32))
+    _, _, trace = dn.recurrent_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"],
+                                   state_trace=True, qk_l2norm=True)
+    out = {}
+
+    def call():
+        out["g"] = dn.recurrent_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], trace,
+                                    do, qk_l2norm=True)
+
+    call()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out["g"].items() if v is not None}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    got = out["g"]
+    for rep in range(3):
+        for v in got.values():
+            if v is not None:
+                v.zero_()
+        torch.ones(1000, device="cuda").sum().item()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(got[k], v), f"replay {rep}: {k} differs from the eager call"

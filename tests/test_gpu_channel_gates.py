@@ -261,7 +261,8 @@ def test_prefill_channel_gates_graph_replay():
 
 def test_prefill_channel_gates_without_workspace():
     """With less workspace than the query returns, the matrix-core path runs as one kernel
-    (operands formed inside the chunk loop); both forms agree with the oracle."""
+    (operands formed inside the chunk loop); both forms agree with the oracle and with each
+    other bit for bit."""
     _say("channel gates prefill: one kernel vs two")
     x = make_case(B=1, Hqk=2, Hv=4, Dk=128, dtype="bf16", seqlens=[130, 0, 64, 1, 200],
                   g_scale=0.3, init_std=0.1, seed=31, name="chg_nows", g_per_key=True)
@@ -276,6 +277,8 @@ def test_prefill_channel_gates_without_workspace():
     o_ref, s_ref = _oracle(x)
     _check(x, host(o1), host(s1), o_ref, s_ref)
     _check(x, host(o2), host(s2), o_ref, s_ref)
+    # the same arithmetic in the same order: the two forms agree bit for bit
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
 def test_prefill_channel_gates_many_short_sequences():
