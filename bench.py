@@ -1,6 +1,7 @@
 """Benchmark of the delta-rule mixer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--decode-reps R] [--graph]
+    python bench.py --only prefill2|prefill3|prefill5 [--steps K] [--warmup W]
 
 One step is one prefill call (dn_chunk_fwd) over the DeltaNet layer-prefill workload
 (B=4, H=16, T=2048, d_k=d_v=128, bf16 q/k/v, fp32 beta, no decay, zero initial state,
@@ -10,9 +11,16 @@ synchronisations, cycling through several copies of the inputs so the working se
 launch loop gives the value (--graph times a HIP-graph replay of the same K steps instead;
 both are reported); the average kernel time per call is also taken with HIP events on the
 launching stream around the eager loop.  The warmup runs long enough (200 calls, about
-12 ms) for the GPU's clocks to settle before the timed region.  The decode step (256 sequences x 32 heads, state updated in place) is
-timed with events around a loop of back-to-back steps and reported in the same line.  The fp64 oracle is timed on the host cores on a bounded sample of
-the prefill workload.
+12 ms) for the GPU's clocks to settle before the timed region.
+
+The two other full-size prefill workloads (gated GQA B2 T8192 16 -> 32 heads; 8 packed gated
+sequences of 32,768 tokens in all) are timed the same way, with events around 10
+back-to-back calls, and each gets its own roofline block (algorithmic bytes and flops,
+rocprofv3 counters) under ``prefill_workloads``.  ``--only`` runs one of the three alone
+(for a rocprofv3 counter pass per workload).  The decode step (256 sequences x 32 heads,
+state updated in place) is timed with events around a loop of back-to-back steps and
+reported in the same line.  The fp64 oracle is timed on the host cores on a bounded
+sample of the prefill workload.
 
 Prints ONE JSON line.
 """
@@ -31,6 +39,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, TFLOP/s
 PREFILL = dict(B=4, T=2048, H=16, D=128, C=64)
+PREFILL_WHAT = {
+    2: "DeltaNet layer prefill B4 H16 T2048 d128 bf16, no decay, zero initial state, final state",
+    3: "gated prefill, GQA 16 q/k heads -> 32 v heads, B2 T8192 d128 bf16, g = -0.1 softplus(z), "
+       "final state",
+    5: "varlen gated prefill, 8 packed sequences, 32768 tokens, H32 d128 bf16, beta in (0,2), "
+       "g = -0.05 softplus(z), initial state per sequence",
+}
 DECODE = dict(N=256, H=32, D=128)
 
 
@@ -43,15 +58,27 @@ def prefill_bytes(B, T, Hqk, Hv, D, gated, N, init):
     return b
 
 
-def prefill_flops(B, T, Hqk, Hv, D, C):
-    """Algorithmic matrix flops of the chunked form per call (dense tiles, triangles
-    not exploited): per chunk and value head, [K;Q] M (2*2C*D*D), T R (2*C*C*D),
-    P Delta (2*C*C*D), K^T Delta (2*C*D*D) and the Gram matrices K K^T, Q K^T
-    (2*2*C*C*D, shared by the value heads of one key head)."""
-    chunks = B * ((T + C - 1) // C)
+def prefill_flops(tokens, Hqk, Hv, D, C):
+    """Algorithmic matrix flops of one prefill call, triangles exploited: per token and
+    value head 6 d_k d_v (K M and Q M against the state, K^T Delta into it) plus
+    C ((1 + 2/r) d_k + 2 d_v) (the masked Gram products K K^T and Q K^T at half a dense
+    tile each, shared by the r = Hv / Hqk value heads of a q/k head, and T R and P Delta
+    at half a tile each).  139,264 flop per token-head at r = 1, 131,072 at r = 2."""
+    r = Hv // Hqk
+    return int(tokens * Hv * (6 * D * D + C * ((1 + 2 / r) * D + 2 * D)))
+
+
+def prefill_flops_dense(tokens, Hqk, Hv, D, C):
+    """The same products with every tile dense (upper triangles and the padded diagonal
+    blocks counted): per chunk and value head [K;Q] M (2*2C*D*D), T R (2*C*C*D), P Delta
+    (2*C*C*D), K^T Delta (2*C*D*D); per chunk and q/k head K K^T, Q K^T (2*2*C*C*D).
+    Reported beside the algorithmic figure as what a dense-tile schedule issues; the
+    kernel's own count (its slice workgroups each form A, T and P) comes from the
+    rocprofv3 SQ counters."""
+    chunks = tokens / C
     per_v = 2 * 2 * C * D * D + 2 * 2 * C * C * D + 2 * C * D * D
     per_qk = 2 * 2 * C * C * D
-    return chunks * (Hv * per_v + Hqk * per_qk)
+    return int(chunks * (Hv * per_v + Hqk * per_qk))
 
 
 def decode_bytes(N, Hqk, Hv, D):
@@ -59,17 +86,21 @@ def decode_bytes(N, Hqk, Hv, D):
 
 
 def source_digest():
+    """Digest of every kernel source: counters in profiles/traffic.json are used only while
+    the sources are the ones they were taken on."""
     h = hashlib.sha256()
-    for f in ("prefill_fused.hip", "mfma_ops.h", "decode.hip"):
-        with open(os.path.join(ROOT, "delta_rule_recurrent_chunked_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "delta_rule_recurrent_chunked_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(key=None):
-    """HBM bytes per call measured with rocprofv3 counters (profiles/traffic.json),
-    used only while the kernel sources are the ones the counters were taken on: the
-    (prefill, decode) pair, or the entry ``key``."""
+def load_traffic(key):
+    """Entry ``key`` of profiles/traffic.json (HBM bytes and matrix-core work per call from
+    rocprofv3 counters), or None unless the kernel sources are the ones the counters were
+    taken on."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -77,10 +108,34 @@ def load_traffic(key=None):
     except (OSError, ValueError):
         t = {}
     if t.get("source_digest") != source_digest():
-        t = {}
-    if key is not None:
-        return t.get(key)
-    return t.get("prefill_bytes_per_call"), t.get("decode_bytes_per_call")
+        return None
+    return t.get(key)
+
+
+def prefill_roofline(key, kernel, call_us, alg_b, tokens, Hqk, Hv, D, C=64):
+    """Roofline block of one prefill workload: algorithmic HBM bytes and matrix flops of
+    one call over the call's kernel time (HIP events on the launching stream), against
+    MI355X's HBM and dense bf16 peaks; rocprofv3's counted bytes and matrix-core work
+    (profiles/traffic.json) while the kernel sources are the ones they were taken on."""
+    meas = load_traffic(key) or {}
+    achieved = alg_b / (call_us * 1e-6) / 1e9
+    alg_f = prefill_flops(tokens, Hqk, Hv, D, C)
+    counters = None
+    if meas.get("counted_flops_per_call"):
+        counters = {"counted_flops_per_call": meas["counted_flops_per_call"],
+                    "counted_frac_of_bf16_peak": meas["counted_flops_per_call"] / (call_us * 1e-6)
+                    / 1e12 / BF16_PEAK_TFLOPS,
+                    "mfma_busy_util": meas.get("mfma_busy_util")}
+    return {
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": meas.get("bytes_per_call"),
+                     "kernel": kernel, "call_us": call_us, "algorithmic_bytes": alg_b},
+        "mfma": {"algorithmic_flops": alg_f, "tflops": alg_f / (call_us * 1e-6) / 1e12,
+                 "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                 "dense_tile_flops": prefill_flops_dense(tokens, Hqk, Hv, D, C),
+                 "counters": counters},
+        "tokens_per_s": tokens / (call_us * 1e-6),
+    }
 
 
 def cpu_baseline(x, budget_s=12.0):
@@ -111,6 +166,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time a HIP-graph replay of the K steps instead of the eager launch loop")
+    ap.add_argument("--only", choices=["prefill2", "prefill3", "prefill5"], default=None,
+                    help="run only this prefill workload (a rocprofv3 counter pass per workload) "
+                         "and print its timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy five times (calibrates rocprofv3's "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -144,6 +202,50 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def time_prefill_workload(cfg, reps, warmup=3):
+        """One prefill workload: `reps` back-to-back calls between HIP events on the launching
+        stream (config 2 cycles over four copies of its inputs, so its 139 MB do not stay
+        in the 256 MB Infinity Cache; the others exceed it by themselves)."""
+        z = make_config(cfg)
+        zcu = None if z.cu_seqlens is None else to_dev(z.cu_seqlens.astype(np.int32))
+        ncopy = 4 if cfg == 2 else 1
+        zsets = []
+        for _ in range(ncopy):
+            zsets.append(dict(q=to_dev(z.q), k=to_dev(z.k), v=to_dev(z.v), b=to_dev(z.beta),
+                              g=to_dev(z.g), i=to_dev(z.init),
+                              o=torch.empty((z.B, z.T, z.Hv, z.Dv), dtype=torch.bfloat16, device=dev),
+                              s=torch.empty((z.num_seqs, z.Hv, z.Dk, z.Dv), dtype=torch.float32,
+                                            device=dev)))
+
+        def zstep(i):
+            w = zsets[i % ncopy]
+            dn.chunk_fwd(w["q"], w["k"], w["v"], w["b"], w["g"], w["i"], cu_seqlens=zcu, out=w["o"],
+                         final_state=w["s"])
+
+        for i in range(warmup):
+            zstep(i)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(reps):
+            zstep(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        z_us = e0.elapsed_time(e1) * 1e3 / reps
+        init = z.init is not None
+        zb = prefill_bytes(z.B, z.T, z.Hqk, z.Hv, z.Dk, gated=z.g is not None, N=z.num_seqs, init=init)
+        kern = "fused_kernel<%s, false>" % ("true" if z.g is not None else "false")
+        blk = prefill_roofline(f"prefill_config{cfg}", kern, z_us, zb, z.B * z.T, z.Hqk, z.Hv, z.Dk)
+        del zsets, zcu
+        return dict(workload=PREFILL_WHAT[cfg], **blk)
+
+    if args.only:
+        cfg = int(args.only[-1])
+        r = time_prefill_workload(cfg, args.steps, warmup=args.warmup)
+        print(json.dumps({"only": args.only, **r}), flush=True)
+        return
 
     # ------------------------------------------------------------------ prefill
     x = make_config(2)
@@ -203,18 +305,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
     tokens = B * T
     alg_b = prefill_bytes(B, T, Hqk, Hv, D, gated=False, N=B, init=False)
-    alg_f = prefill_flops(B, T, Hqk, Hv, D, PREFILL["C"])
-    traffic_p, traffic_d = load_traffic()
-    # matrix-core work and busy fraction per call from rocprofv3's SQ counters (profiles/),
-    # used only while the kernel sources are the ones they were taken on
-    mfma_counted = None
-    mc = load_traffic("prefill_mfma")
-    if mc:
-        mfma_counted = {"counted_flops_per_call": mc["counted_flops_per_call"],
-                        "counted_frac_of_bf16_peak": mc["counted_flops_per_call"] / (call_us * 1e-6)
-                        / 1e12 / BF16_PEAK_TFLOPS,
-                        "mfma_busy_util": mc["mfma_util"]}
-    achieved = alg_b / (call_us * 1e-6) / 1e9
+    traffic_d = load_traffic("decode_bytes_per_call")
+    head_block = prefill_roofline("prefill_config2", "fused_kernel<false, false>", call_us, alg_b,
+                                  tokens, Hqk, Hv, D)
 
     # ------------------------------------------------------------------- decode
     y = make_case(B=DECODE["N"], T=1, Hqk=DECODE["H"], Dk=DECODE["D"], dtype="bf16", g_scale=0.1,
@@ -465,38 +558,7 @@ def main():
     del cx, cy, cst, dx, dcs, dyo
 
     # ------------------------------------ the other two full-size prefill workloads
-    # (context beside the headline: each timed the same way, with HIP events around a loop
-    # of back-to-back calls on the launching stream)
-    other = {}
-    for cfg, what in ((3, "gated prefill, GQA 16 q/k heads -> 32 v heads, B2 T8192 d128 bf16, "
-                          "final state returned"),
-                      (5, "varlen gated prefill, 8 packed sequences, 32768 tokens, H32 d128 bf16, "
-                          "beta in (0,2), initial state per sequence")):
-        z = make_config(cfg)
-        zq, zk, zv, zb, zg, zi = (to_dev(a) for a in (z.q, z.k, z.v, z.beta, z.g, z.init))
-        zcu = None if z.cu_seqlens is None else to_dev(z.cu_seqlens.astype(np.int32))
-        zo = torch.empty((z.B, z.T, z.Hv, z.Dv), dtype=torch.bfloat16, device=dev)
-        zs = torch.empty((z.num_seqs, z.Hv, z.Dk, z.Dv), dtype=torch.float32, device=dev)
-        zw = torch.empty(max(1, dn.workspace_bytes(z.B, z.T, z.Hqk, z.Hv, z.Dk, z.Dv, torch.bfloat16)),
-                         dtype=torch.uint8, device=dev)
-
-        def zstep():
-            dn.chunk_fwd(zq, zk, zv, zb, zg, zi, cu_seqlens=zcu, out=zo, final_state=zs,
-                         workspace=zw, check_cu_seqlens=False)
-
-        for _ in range(2):
-            zstep()
-        reps = 10
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(reps):
-            zstep()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        z_us = ev0.elapsed_time(ev1) * 1e3 / reps
-        other[f"config{cfg}"] = {"workload": what, "us_per_call": z_us,
-                                 "tokens_per_s": z.B * z.T / (z_us * 1e-6)}
-        del zq, zk, zv, zb, zg, zi, zcu, zo, zs, zw
+    other = {cfg: time_prefill_workload(cfg, 10) for cfg in (3, 5)}
 
     line = {
         "metric": "prefill tokens/sec + MFMA util; decode-step state GB/s vs HBM peak",
@@ -514,16 +576,11 @@ def main():
         "config": {"workload": "DeltaNet layer prefill B4 H16 T2048 d_k=d_v=128 bf16, no decay, "
                                "zero initial state, chunk 64", "global_batch": B, "seq_len": T,
                    "heads": Hv, "head_dim": D, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_p,
-                     "kernel": "fused_kernel<false, false> (the only kernel of a dn_chunk_fwd call)",
-                     "call_us": call_us, "algorithmic_bytes": alg_b},
+        "roofline": head_block["roofline"],
         "timing": {"loop": "hip_graph_replay" if args.graph else "eager",
                    "ms_per_step_eager": wall_eager * 1e3 / args.steps,
                    "ms_per_step_graph": wall_graph * 1e3 / args.steps},
-        "mfma": {"algorithmic_flops": alg_f, "tflops": alg_f / (call_us * 1e-6) / 1e12,
-                 "frac_of_bf16_peak": alg_f / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
-                 "counters": mfma_counted},
+        "mfma": head_block["mfma"],
         "decode": {"workload": "gated decode step, 256 sequences x 32 heads, d=128, bf16, fp32 state "
                                "in place", "us_per_step": dec_us, "state_GBps": dec_gbs,
                    "roofline": {"bound": "hbm", "achieved": dec_b / (dec_us * 1e-6) / 1e9,
@@ -532,7 +589,9 @@ def main():
                                 "traffic": traffic_d, "kernel": "decode_kernel",
                                 "algorithmic_bytes": dec_b},
                    "ungated_us_per_step": dec_plain_us},
-        "prefill_other_workloads": other,
+        "prefill_workloads": {
+            "config2": dict(workload=PREFILL_WHAT[2], **head_block),
+            "config3": other[3], "config5": other[5]},
         "in_rule_qk_l2norm": in_rule_norm,
         "channel_gates": channel_gates,
         "readout_epilogue": epilogue,

@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv",
+__all__ = ["chunk_fwd", "chunk_fwd_path", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv",
            "causal_conv_step", "workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
@@ -33,7 +33,7 @@ DN_OK, DN_ERR_INVALID_ARG, DN_ERR_UNSUPPORTED, DN_ERR_HIP, DN_ERR_WORKSPACE = 0,
 DN_F32, DN_BF16 = 0, 1
 EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
             "dn_norm_gate", "dn_recurrent_fwd", "dn_causal_conv", "dn_causal_conv_step",
-            "dn_recurrent_bwd", "dn_recurrent_bwd_workspace_bytes",
+            "dn_recurrent_bwd", "dn_recurrent_bwd_workspace_bytes", "dn_chunk_fwd_path",
             "dn_status_str", "dn_version")
 
 
@@ -93,6 +93,8 @@ def load_library():
         lib.dn_chunk_fwd.restype = ctypes.c_int
         lib.dn_chunk_fwd_workspace_bytes.argtypes = [sp]
         lib.dn_chunk_fwd_workspace_bytes.restype = sz
+        lib.dn_chunk_fwd_path.argtypes = [sp, sz]
+        lib.dn_chunk_fwd_path.restype = ctypes.c_int32
         lib.dn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
         ep = ctypes.POINTER(_Epilogue)
         lib.dn_decode_step_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, ep, vp, vp]
@@ -167,6 +169,27 @@ def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: 
     return int(load_library().dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
 
 
+_PATHS = {-1: "invalid", 0: "fused", 1: "channel_gate_two_kernels", 2: "channel_gate_one_kernel",
+          3: "vector"}
+
+
+def chunk_fwd_path(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: torch.dtype,
+                   num_seqs: Optional[int] = None, chunk_size: int = 64, g_per_key: bool = False,
+                   qk_l2norm: bool = False, workspace_bytes: Optional[int] = None) -> str:
+    """Which kernels ``chunk_fwd`` runs for these sizes: "fused" (one matrix-core kernel),
+    "channel_gate_two_kernels" / "channel_gate_one_kernel" (per-key-channel gates on the
+    matrix cores, with / without enough workspace), "vector" (the vector-ALU chunked
+    kernel, about 100x slower), or "invalid".  ``workspace_bytes`` defaults to what
+    :func:`chunk_fwd` allocates itself."""
+    s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
+               DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0,
+               *_flags(qk_l2norm, 1e-6, g_per_key))
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = int(lib.dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
+    return _PATHS[int(lib.dn_chunk_fwd_path(ctypes.byref(s), int(workspace_bytes)))]
+
+
 def _prompt_args(q, k, v, beta, g, initial_state, output_final_state, cu_seqlens, scale,
                  chunk_size, out, final_state, check_cu_seqlens, qk_l2norm, l2norm_eps):
     """Checks and allocations shared by the whole-sequence calls; returns
@@ -220,7 +243,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
               scale: float = 1.0, chunk_size: int = 64, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = True,
+              workspace: Optional[torch.Tensor] = None, check_cu_seqlens: bool = False,
               qk_l2norm: bool = False, l2norm_eps: float = 1e-6
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Delta rule over whole sequences (prefill), chunkwise-parallel form.
@@ -232,8 +255,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     packs N sequences along T (B == 1).  Returns ``(o [B, T, Hv, Dv], final_state or
     None)``.  ``final_state`` may be passed (and may be ``initial_state``, to update
     it in place); ``out`` and ``workspace`` may be passed to avoid allocation.
-    ``check_cu_seqlens`` copies cu_seqlens to the host (a synchronising copy) and
-    checks ``cu[0] == 0``, non-decreasing, ``cu[N] == T``: the kernels trust it.
+    The kernels trust cu_seqlens (``cu[0] == 0``, non-decreasing, ``cu[N] == T``);
+    ``check_cu_seqlens=True`` checks it on a host copy first (a synchronising copy, which
+    also cannot be captured in a HIP graph), for debugging.
     ``qk_l2norm`` normalises q and k inside the call, x / sqrt(|x|^2 + l2norm_eps).
     """
     lib = load_library()
@@ -262,7 +286,7 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
                   output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
                   scale: float = 1.0, out: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None, state_trace: bool = False,
-                  check_cu_seqlens: bool = True, qk_l2norm: bool = False,
+                  check_cu_seqlens: bool = False, qk_l2norm: bool = False,
                   l2norm_eps: float = 1e-6):
     """The rule token by token over whole sequences (the recurrent route), same arguments
     as :func:`chunk_fwd`.  Returns ``(o, final_state, trace)`` where ``trace`` is the
@@ -291,7 +315,8 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
                   state_trace: torch.Tensor, d_o: torch.Tensor,
                   d_final_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
-                  qk_l2norm: bool = False, l2norm_eps: float = 1e-6) -> dict:
+                  qk_l2norm: bool = False, l2norm_eps: float = 1e-6,
+                  check_cu_seqlens: bool = False) -> dict:
     """Reverse pass of the rule: gradients of a loss with dL/do = ``d_o`` and dL/d final
     state = ``d_final_state`` for q, k, v, beta, g and the initial state, from the state
     trace that :func:`recurrent_fwd` returned for the same inputs (``state_trace=True``).
@@ -301,7 +326,7 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
     dbeta, dg (g's shape; None without g) and d_initial_state."""
     lib = load_library()
     shape, _, _, N = _prompt_args(q, k, v, beta, g, initial_state, False, cu_seqlens, scale, 64,
-                                  None, None, True, qk_l2norm, l2norm_eps)
+                                  None, None, check_cu_seqlens, qk_l2norm, l2norm_eps)
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     _dev(state_trace, "state_trace", torch.float32, (B, T, Hv, Dk, Dv))

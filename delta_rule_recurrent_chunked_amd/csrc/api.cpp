@@ -90,6 +90,18 @@ size_t dn_chunk_fwd_workspace_bytes(const dn_shape* s) {
     return dn::prefill_chg_workspace_bytes(a);
 }
 
+int32_t dn_chunk_fwd_path(const dn_shape* s, size_t ws_bytes) {
+    dn::PrefillArgs a;
+    const bool packed = s && s->B == 1 && s->num_seqs != 1;
+    if (prefill_shape(s, packed, a) != DN_OK) return DN_PATH_INVALID;
+    if (a.g_per_key) {
+        if (!dn::prefill_chg_shape_ok(a)) return DN_PATH_VECTOR;
+        const size_t need = dn::prefill_chg_workspace_bytes(a);
+        return ws_bytes >= need ? DN_PATH_CHANNEL_GATE_TWO_KERNELS : DN_PATH_CHANNEL_GATE_ONE_KERNEL;
+    }
+    return dn::prefill_fused_supported(a) ? DN_PATH_FUSED : DN_PATH_VECTOR;
+}
+
 dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const void* v,
                        const float* beta, const float* g, const float* h0, float* hT,
                        const int32_t* cu, void* o, void* ws, size_t ws_bytes,

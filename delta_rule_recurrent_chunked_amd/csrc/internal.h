@@ -114,6 +114,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
 bool prefill_fused_supported(const PrefillArgs& a);
 bool prefill_chg_supported(const PrefillArgs& a);
+bool prefill_chg_shape_ok(const PrefillArgs& a);
 size_t prefill_chg_workspace_bytes(const PrefillArgs& a);
 hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s);

@@ -1091,6 +1091,8 @@ static bool chg_shape_ok(const PrefillArgs& a) {
            span < (1L << 31);
 }
 
+bool prefill_chg_shape_ok(const PrefillArgs& a) { return chg_shape_ok(a); }
+
 bool prefill_chg_supported(const PrefillArgs& a) {
     const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.o;
     return chg_shape_ok(a) && a.g && (al & 15) == 0 && ((uintptr_t)a.g & 7) == 0;

@@ -223,7 +223,8 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
     constexpr int TPR = S::TPR, RPT = S::RPT, NW = S::NW, NSL = DV / CW;
     __shared__ float red[NW][CW];
     __shared__ float vec_vr[CW], vec_d[CW], vec_do[CW], vec_dd[CW];
-    __shared__ float acc2[2];
+    __shared__ float dbp[CW];      // this slice's dbeta terms, one per value column
+    __shared__ float dgw[NW];      // per-wave dg partials (one gate per head)
     __shared__ float nrm[NW][2];   // per-wave |k|^2, |q|^2 partials (in-call normalisation)
 
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -298,7 +299,6 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
                 nrm[wave][1] = qq;
             }
         }
-        if (tid < 2) acc2[tid] = 0.f;
         __syncthreads();
         float ik = 1.f, iq = 1.f;
         if (a.qk_norm) {
@@ -357,7 +357,7 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
 #pragma unroll
             for (int w = 0; w < NW; ++w) dd += red[w][tid];
             a.dv[(t * a.Hv + h) * DV + j0 + tid] = beta * dd;
-            atomicAdd(&acc2[0], dd * vec_vr[tid]);   // this slice's share of dbeta
+            dbp[tid] = dd * vec_vr[tid];   // summed below in column order
             vec_dd[tid] = dd;
         }
         __syncthreads();
@@ -404,14 +404,22 @@ __global__ __launch_bounds__((RecShape<DK, CW>::NT)) void recurrent_bwd_kernel(R
             for (int p = 0; p < RPT; ++p) dgp += dgr[p];
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) dgp += __shfl_xor(dgp, off);
-            if (lane == 0) atomicAdd(&acc2[1], dgp);
+            if (lane == 0) dgw[wave] = dgp;   // summed below in wave order
         }
         __syncthreads();
-        if (tid == 0) {
-            a.ws_db[(slice * tokens + t) * a.Hv + h] = acc2[0];
-            if (!a.g_per_key) a.ws_dg[(slice * tokens + t) * a.Hv + h] = acc2[1];
+        if (tid == 0) {   // fixed summation orders: the pass is bitwise reproducible
+            float db = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) db += dbp[c2];
+            a.ws_db[(slice * tokens + t) * a.Hv + h] = db;
+            if (!a.g_per_key) {
+                float dg = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) dg += dgw[w];
+                a.ws_dg[(slice * tokens + t) * a.Hv + h] = dg;
+            }
         }
-        __syncthreads();   // acc2 and the reduction buffers are reused by the next token
+        __syncthreads();   // dbp, dgw and the reduction buffers are reused by the next token
         cur = nxt;
     }
     if (a.dh0) {

@@ -33,8 +33,8 @@
  *   cache's own buffer on a decode step).
  *
  * State layout.  Every state tensor is fp32, [.., Dk, Dv] row-major: element
- * (i, j) is S[j][i], i.e. the library stores M = S^T, "one key_dim by value_dim
- * matrix per head" as the nnterp page puts it.
+ * (i, j) is S[j][i], i.e. the library stores M = S^T: a key-dimension by
+ * value-dimension matrix for every head, the orientation the nnterp page gives its state.
  *
  * Head sharing.  Hv value heads read Hqk <= Hv query/key heads, Hv % Hqk == 0;
  * value head h reads query/key head h / (Hv / Hqk) (the nnterp queries accessor
@@ -136,7 +136,10 @@ typedef struct {
  * Errors: DN_ERR_INVALID_ARG (null required pointer, non-positive sizes, Hv % Hqk,
  * B != 1 or num_seqs < 1 with cu_seqlens, num_seqs != B without, misaligned
  * pointer, unknown flags, negative or non-finite l2norm_eps), DN_ERR_UNSUPPORTED
- * (Dk, Dv, chunk_size or dtype not supported), DN_ERR_WORKSPACE, DN_ERR_HIP.  T == 0 is valid: final_state = initial_state.
+ * (Dk, Dv, chunk_size or dtype not supported), DN_ERR_HIP.  A missing or short
+ * workspace is not an error: the per-key-channel path then runs as one kernel
+ * (dn_chunk_fwd_path tells which kernels a call runs).  T == 0 is valid:
+ * final_state = initial_state.
  */
 dn_status dn_chunk_fwd(const dn_shape* shape,
                        const void* q, const void* k, const void* v,
@@ -153,10 +156,24 @@ dn_status dn_chunk_fwd(const dn_shape* shape,
  * that forms those operands inside its chunk loop (slower). */
 size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
 
+/* Which kernels dn_chunk_fwd runs for this shape and workspace size (no launch, no
+ * device access).  Only bf16 prompts with Dk = Dv = 128 and 64-token chunks run on the
+ * matrix cores (and, with DN_GATE_PER_KEY, Dk = 128, Dv a multiple of 32); every other
+ * supported shape runs the vector-ALU chunked kernel, which is about 100x slower on the
+ * same work.  Returns DN_PATH_INVALID for a shape dn_chunk_fwd would reject. */
+typedef enum {
+    DN_PATH_INVALID = -1,
+    DN_PATH_FUSED = 0,                         /* one matrix-core kernel                     */
+    DN_PATH_CHANNEL_GATE_TWO_KERNELS = 1,      /* per-key-channel gates, with the workspace  */
+    DN_PATH_CHANNEL_GATE_ONE_KERNEL = 2,       /* per-key-channel gates, workspace too small */
+    DN_PATH_VECTOR = 3                         /* vector-ALU chunked kernel                  */
+} dn_path;
+int32_t dn_chunk_fwd_path(const dn_shape* shape, size_t workspace_bytes);
+
 /*
  * dn_decode_step -- one token of the delta rule for each of N sequences against a
- * cached state, updated in place (the nnterp page's token-by-token rule on a decode
- * step, where the sequence axis is 1 and state_input is the cached state).
+ * cached state, updated in place (the nnterp page's token-by-token rule for a decode
+ * step: a single token per sequence, fed the cache as its state input).
  *
  *   shape->B = N sequences, shape->T must be 1, num_seqs = N, cu_seqlens unused;
  *   q, k   [N, Hqk, Dk] dtype;  v [N, Hv, Dv] dtype;  beta, g [N, Hv] fp32 (g may be NULL;

@@ -44,3 +44,36 @@ def rel_l2(a, b) -> float:
 def tol(x: DeltaInputs) -> float:
     """Relative-L2 bar on outputs and final states: 1e-4 for fp32 inputs, 1e-2 for bf16."""
     return 1e-4 if x.dtype == "f32" else 1e-2
+
+
+def per_unit_rel(o, o_ref, s, s_ref, x: DeltaInputs):
+    """Relative L2 of every (sequence, value head): the output over that sequence's tokens
+    and the final state.  Returns (worst output error, worst state error, where)."""
+    bounds = x.seq_bounds()
+    Hv, Dv = x.Hv, x.Dv
+    of = np.asarray(o, dtype=np.float64).reshape(-1, Hv, Dv)
+    rf = np.asarray(o_ref, dtype=np.float64).reshape(-1, Hv, Dv)
+    worst_o = worst_s = 0.0
+    where = None
+    for n in range(len(bounds) - 1):
+        a, b = int(bounds[n]), int(bounds[n + 1])
+        for h in range(Hv):
+            eo = rel_l2(of[a:b, h], rf[a:b, h]) if b > a else 0.0
+            es = rel_l2(s[n, h], s_ref[n, h])
+            if eo > worst_o or es > worst_s:
+                where = (n, h, b - a)
+            worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    return worst_o, worst_s, where
+
+
+def log_errors(case: str, **errors):
+    """Append one case's measured errors to gpurun_out/parity_errors.jsonl (kept with the
+    run's other outputs)."""
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = os.path.join(root, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "parity_errors.jsonl"), "a") as f:
+        f.write(json.dumps({"case": case, **{k: (float(v) if isinstance(v, (float, np.floating))
+                                                  else v) for k, v in errors.items()}}) + "\n")

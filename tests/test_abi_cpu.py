@@ -205,3 +205,27 @@ def test_channel_gate_prompt_workspace_query():
     assert dn.workspace_bytes(4, 2048, 16, 16, 128, 128, torch.float32, g_per_key=True) == 0
     assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, torch.bfloat16, g_per_key=True) == 0
     assert dn.workspace_bytes(4, 2048, 16, 16, 128, 128, torch.bfloat16, chunk_size=32, g_per_key=True) == 0
+
+
+def test_chunk_fwd_path_reports_the_kernels():
+    """The host-only query names the kernels a prompt call runs (the vector-ALU fallback
+    included), without touching a device."""
+    bf, f32 = torch_dtypes()
+    path = dn.chunk_fwd_path
+    assert path(4, 2048, 16, 16, 128, 128, bf) == "fused"
+    assert path(1, 32768, 32, 32, 128, 128, bf, num_seqs=8) == "fused"
+    assert path(4, 2048, 16, 16, 128, 128, bf, qk_l2norm=True) == "fused"
+    assert path(4, 2048, 16, 16, 64, 64, bf) == "vector"
+    assert path(4, 2048, 16, 16, 128, 128, f32) == "vector"
+    assert path(4, 2048, 16, 16, 128, 128, bf, chunk_size=32) == "vector"
+    assert path(4, 2048, 16, 16, 128, 128, bf, g_per_key=True) == "channel_gate_two_kernels"
+    assert path(4, 2048, 16, 16, 128, 128, bf, g_per_key=True, workspace_bytes=0) == \
+        "channel_gate_one_kernel"
+    assert path(4, 2048, 16, 16, 64, 64, bf, g_per_key=True) == "vector"
+    assert path(4, 2048, 3, 16, 128, 128, bf) == "invalid"
+    assert path(4, 2048, 16, 16, 48, 128, bf) == "invalid"
+
+
+def torch_dtypes():
+    import torch
+    return torch.bfloat16, torch.float32

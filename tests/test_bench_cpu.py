@@ -38,17 +38,25 @@ def test_prefill_bytes_counts_gates_initial_state_and_shared_qk():
 
 
 def test_prefill_flops_headline_workload():
+    # algorithmic count, triangles exploited: per token and value head 6 d_k d_v against the
+    # state plus C ((1 + 2/r) d_k + 2 d_v) for the masked Gram products (shared by the r
+    # value heads of a q/k head) and T R, P Delta; 139,264 flop at r = 1, 131,072 at r = 2
+    assert bench.prefill_flops(1, 1, 1, 128, 64) == 139_264
+    assert bench.prefill_flops(1, 1, 2, 128, 64) == 2 * 131_072
+    assert bench.prefill_flops(4 * 2048, 16, 16, 128, 64) == 18_253_611_008     # 18.25 GFLOP
+    assert bench.prefill_flops(2 * 8192, 16, 32, 128, 64) == 68_719_476_736     # 68.72 GFLOP
+    assert bench.prefill_flops(32768, 32, 32, 128, 64) == 146_028_888_064       # 146.03 GFLOP
+
+
+def test_prefill_dense_tile_flops():
     # per chunk and value head: [K;Q] M (2 x 2C x D x D), T R and P Delta (2 x C x C x D each),
     # K^T Delta (2 x C x D x D); per chunk and key head K K^T and Q K^T (2 x 2 x C x C x D)
     C, D, chunks, hv, hqk = 64, 128, 4 * 2048 // 64, 16, 16
     per_v = 2 * 2 * C * D * D + 2 * 2 * C * C * D + 2 * C * D * D
     per_qk = 2 * 2 * C * C * D
-    assert bench.prefill_flops(4, 2048, 16, 16, 128, 64) == chunks * (hv * per_v + hqk * per_qk)
-    assert bench.prefill_flops(4, 2048, 16, 16, 128, 64) == 21_474_836_480
-
-
-def test_prefill_flops_rounds_partial_chunks_up():
-    assert bench.prefill_flops(1, 65, 1, 1, 16, 64) == bench.prefill_flops(1, 128, 1, 1, 16, 64)
+    assert bench.prefill_flops_dense(4 * 2048, 16, 16, 128, 64) == chunks * (hv * per_v + hqk * per_qk)
+    assert bench.prefill_flops_dense(4 * 2048, 16, 16, 128, 64) == 21_474_836_480
+    assert bench.prefill_flops(4 * 2048, 16, 16, 128, 64) < bench.prefill_flops_dense(4 * 2048, 16, 16, 128, 64)
 
 
 def test_decode_bytes():
@@ -67,9 +75,16 @@ def test_traffic_is_used_only_for_the_sources_it_was_measured_on(tmp_path, monke
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "source_digest", lambda: digest)
     (prof / "traffic.json").write_text(json.dumps(
-        {"source_digest": "0" * 16, "prefill_bytes_per_call": 1, "decode_bytes_per_call": 2}))
-    assert bench.load_traffic() == (None, None)
+        {"source_digest": "0" * 16, "prefill_config2": {"bytes_per_call": 1},
+         "decode_bytes_per_call": 2}))
+    assert bench.load_traffic("prefill_config2") is None
+    assert bench.load_traffic("decode_bytes_per_call") is None
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
-    assert bench.load_traffic() == (1, 2)
-    assert bench.load_traffic("prefill_bytes_per_call") == 1
+    assert bench.load_traffic("prefill_config2") == {"bytes_per_call": 1}
+    assert bench.load_traffic("decode_bytes_per_call") == 2
     assert bench.load_traffic("no_such_entry") is None
+    # the roofline block takes the counted bytes only from a matching digest
+    blk = bench.prefill_roofline("prefill_config2", "k", 50.0, 138_936_320, 8192, 16, 16, 128)
+    assert blk["roofline"]["traffic"] == 1
+    assert abs(blk["roofline"]["frac"] - 138_936_320 / 50e-6 / 1e9 / 8000) < 1e-12
+    assert blk["mfma"]["algorithmic_flops"] == 18_253_611_008

@@ -126,3 +126,24 @@ def test_reverse_pass_graph_replay():
         torch.cuda.synchronize()
         for k, v in ref.items():
             assert torch.equal(got[k], v), f"replay {rep}: {k} differs from the eager call"
+
+
+def test_reverse_pass_bitwise_repeatable():
+    """Two reverse passes over the same inputs agree bit for bit: every slice share is summed
+    in a fixed order (no atomics), with one gate per head and per key channel."""
+    _say("reverse pass bitwise repeat")
+    for per_key in (False, True):
+        x = make_case(B=1, Hqk=1, Hv=2, Dk=128, dtype="bf16", seqlens=[70, 0, 129],
+                      g_scale=0.1, init_std=0.02, seed=56, name="bwd_repeat", g_per_key=per_key)
+        d = to_inputs(x)
+        rng = np.random.default_rng(57)
+        from synth import f32_to_bf16_bits
+        do = dev_tensor(f32_to_bf16_bits(rng.standard_normal((1, x.T, 2, 128)).astype(np.float32)))
+        _, _, trace = dn.recurrent_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"],
+                                       cu_seqlens=d["cu"], state_trace=True)
+        runs = [dn.recurrent_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], trace, do,
+                                 cu_seqlens=d["cu"]) for _ in range(2)]
+        torch.cuda.synchronize()
+        for k in runs[0]:
+            if runs[0][k] is not None:
+                assert torch.equal(runs[0][k], runs[1][k]), (per_key, k)

@@ -11,7 +11,7 @@ import torch
 
 import delta_rule_recurrent_chunked_amd as dn
 from synth import make_case, make_config
-from tests.gpu_util import host, rel_l2, run_oracle, to_inputs, tol
+from tests.gpu_util import host, log_errors, per_unit_rel, rel_l2, run_oracle, to_inputs, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -31,12 +31,19 @@ def _prefill(x, scale=1.0, chunk=None, **kw):
 
 
 def _check(x, o, s, scale=1.0, o_ref=None, s_ref=None):
+    """The bar on the whole tensors and on every (sequence, value head) separately, so that
+    one wrong short sequence or head cannot hide in the aggregate."""
     if o_ref is None:
         o_ref, s_ref = run_oracle(x, scale)
     eo, es = rel_l2(o, o_ref), rel_l2(s, s_ref)
-    _say(f"  {x.name}: rel_l2 o={eo:.2e} state={es:.2e} (bar {tol(x):.0e})")
+    uo, us, where = per_unit_rel(o, o_ref, s, s_ref, x)
+    _say(f"  {x.name}: rel_l2 o={eo:.2e} state={es:.2e}; worst (sequence, head) o={uo:.2e} "
+         f"state={us:.2e} at {where} (bar {tol(x):.0e})")
+    log_errors(x.name, o=eo, state=es, worst_unit_o=uo, worst_unit_state=us, bar=tol(x),
+               worst_unit=where)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
     assert eo <= tol(x) and es <= tol(x)
+    assert uo <= tol(x) and us <= tol(x)
     return eo, es
 
 

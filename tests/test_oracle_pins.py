@@ -54,3 +54,41 @@ def test_bad_arguments():
 
 def test_threads_reported():
     assert oracle.max_threads() >= 1
+
+
+@pytest.mark.parametrize("gate", [None, "head", "key"])
+def test_per_token_states_at_every_prefix(gate):
+    """brute.per_token_states (the checker of the GPU state trace) against the oracle at
+    every prefix: the T prefixes of one sequence packed as T sequences of lengths 1..T
+    into one oracle call, whose final states must be the trace's states, token by token.
+    Gates per head, per key channel, or none; d_k != d_v, beta in (0, 2), initial state."""
+    rng = np.random.default_rng(11)
+    T, Dk, Dv = 23, 5, 7
+    k = rng.standard_normal((T, Dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, Dv))
+    beta = 2.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    g = None
+    if gate == "head":
+        g = -0.3 * np.log1p(np.exp(rng.standard_normal(T)))
+    elif gate == "key":
+        g = -0.3 * np.log1p(np.exp(rng.standard_normal((T, Dk))))
+    S0 = rng.standard_normal((Dv, Dk)) * 0.5
+    trace = brute.per_token_states(k, v, beta, g, S0)
+    assert trace.shape == (T, Dv, Dk)
+    # packed prefixes: sequence t holds tokens 0..t
+    idx = np.concatenate([np.arange(t + 1) for t in range(T)])
+    cu = np.concatenate([[0], np.cumsum(np.arange(1, T + 1))])
+    pk = k[idx][None, :, None, :]
+    pv = v[idx][None, :, None, :]
+    pb = beta[idx][None, :, None]
+    pg = None
+    if g is not None:
+        pg = g[idx][None, :, None] if g.ndim == 1 else g[idx][None, :, None, :]
+    init = np.broadcast_to(S0.T, (T, 1, Dk, Dv)).copy()
+    _, fin = oracle.recurrent(pk, pk, pv, pb, pg, init, cu_seqlens=cu)
+    for t in range(T):
+        np.testing.assert_allclose(trace[t].T, fin[t, 0], rtol=0, atol=1e-12, err_msg=f"token {t}")
+    # and the last state is the product form's final state
+    _, S_T = brute.product_form(k, k, v, beta, g, S0)
+    np.testing.assert_allclose(trace[-1], S_T, rtol=0, atol=1e-13)
