@@ -34,7 +34,7 @@ DN_F32, DN_BF16 = 0, 1
 EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
             "dn_norm_gate", "dn_recurrent_fwd", "dn_causal_conv", "dn_causal_conv_step",
             "dn_recurrent_bwd", "dn_recurrent_bwd_workspace_bytes", "dn_chunk_fwd_path",
-            "dn_status_str", "dn_version")
+            "dn_chunk_fwd_noalloc", "dn_status_str", "dn_version")
 
 
 class DeltaNetError(RuntimeError):
@@ -94,6 +94,8 @@ def load_library():
         lib.dn_chunk_fwd_workspace_bytes.argtypes = [sp]
         lib.dn_chunk_fwd_workspace_bytes.restype = sz
         lib.dn_chunk_fwd_path.argtypes = [sp, sz]
+        lib.dn_chunk_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.dn_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.dn_chunk_fwd_path.restype = ctypes.c_int32
         lib.dn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
         ep = ctypes.POINTER(_Epilogue)

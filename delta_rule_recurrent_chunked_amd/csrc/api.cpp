@@ -102,6 +102,25 @@ int32_t dn_chunk_fwd_path(const dn_shape* s, size_t ws_bytes) {
     return dn::prefill_fused_supported(a) ? DN_PATH_FUSED : DN_PATH_VECTOR;
 }
 
+dn_status dn_chunk_fwd_noalloc(const dn_shape* s, const void* q, const void* k, const void* v,
+                               const float* beta, const float* g, const float* h0, float* hT,
+                               const int32_t* cu, void* o, hipStream_t stream) {
+    // Only the two-kernel channel-gate path needs scratch; it gets the static array (the
+    // checks that follow in dn_chunk_fwd see a workspace of exactly the array's size).
+    dn::PrefillArgs a;
+    dn_status st = prefill_shape(s, cu != nullptr, a);
+    if (st != DN_OK) return st;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const size_t need = dn::prefill_chg_workspace_bytes(a);
+    if (need > 0) {
+        if (need > dn::noalloc_scratch_bytes()) return DN_ERR_WORKSPACE;
+        if (dn::noalloc_scratch(&ws) != hipSuccess) return DN_ERR_HIP;
+        ws_bytes = dn::noalloc_scratch_bytes();
+    }
+    return dn_chunk_fwd(s, q, k, v, beta, g, h0, hT, cu, o, ws, ws_bytes, stream);
+}
+
 dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const void* v,
                        const float* beta, const float* g, const float* h0, float* hT,
                        const int32_t* cu, void* o, void* ws, size_t ws_bytes,

@@ -116,6 +116,10 @@ bool prefill_fused_supported(const PrefillArgs& a);
 bool prefill_chg_supported(const PrefillArgs& a);
 bool prefill_chg_shape_ok(const PrefillArgs& a);
 size_t prefill_chg_workspace_bytes(const PrefillArgs& a);
+// The allocation-free prompt call's static scratch: its size, and its device address on
+// the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s);
 

@@ -40,6 +40,9 @@
 //      R, Delta by block substitution; waves 2, 3 form (Q o e^G) M0 transposed;
 //      then waves 2, 3 add Delta^T P^T and store O (8 bytes: four columns of one token
 //      per lane), waves 0, 1 update the state.
+#include <mutex>
+
+#include "../../include/deltanet.h"
 #include "internal.h"
 #include "mfma_ops.h"
 
@@ -1124,4 +1127,40 @@ hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ allocation-free scratch
+// The per-(chunk, value head) records of the two-kernel form, for callers that cannot
+// allocate device memory: one static device array per GPU, held from the code object's
+// load on that GPU until the process ends.  In host code `scratch` names a host-side
+// stand-in, not the device array: its device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is ever handed to a kernel.
+constexpr size_t NOALLOC_BYTES = (size_t)64 << 20;
+static_assert(NOALLOC_BYTES == DN_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES];   // device address of `scratch` on each GPU, once known
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return NOALLOC_BYTES; }
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_dev[dev] = p;
+    }
+    *ptr = scratch_dev[dev];
+    return hipSuccess;
+}
+
 }  // namespace dn
+

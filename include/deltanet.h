@@ -156,6 +156,28 @@ dn_status dn_chunk_fwd(const dn_shape* shape,
  * that forms those operands inside its chunk loop (slower). */
 size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
 
+/*
+ * dn_chunk_fwd_noalloc -- dn_chunk_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as dn_chunk_fwd, without the workspace.  The only path that
+ * needs scratch (gates per key channel on the matrix cores: 68,352 B per chunk and value
+ * head) takes it from a static device array of DN_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing.  A call whose
+ * records exceed the array (for example more than 981 (chunk, value head) pairs) returns
+ * DN_ERR_WORKSPACE, before any launch.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or host threads) race and
+ * must be serialised by the caller.  Nothing in the array needs clearing between calls.
+ *
+ * Errors: as dn_chunk_fwd, DN_ERR_WORKSPACE as above, DN_ERR_HIP if the array's device
+ * address cannot be looked up.
+ */
+#define DN_NOALLOC_SCRATCH_BYTES (64u << 20)
+dn_status dn_chunk_fwd_noalloc(const dn_shape* shape,
+                               const void* q, const void* k, const void* v,
+                               const float* beta, const float* g,
+                               const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, void* o, hipStream_t stream);
+
 /* Which kernels dn_chunk_fwd runs for this shape and workspace size (no launch, no
  * device access).  Only bf16 prompts with Dk = Dv = 128 and 64-token chunks run on the
  * matrix cores (and, with DN_GATE_PER_KEY, Dk = 128, Dv a multiple of 32); every other

@@ -229,3 +229,18 @@ def test_chunk_fwd_path_reports_the_kernels():
 def torch_dtypes():
     import torch
     return torch.bfloat16, torch.float32
+
+
+def test_chunk_fwd_noalloc_rejects_oversized_scratch_on_the_host():
+    """The allocation-free prompt call refuses, before any HIP call, a channel-gate prompt
+    whose records exceed the static scratch (B4 H16 T2048: 2,048 records of 68,352 B
+    against 64 MiB), and checks shapes as dn_chunk_fwd does."""
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    big = _shape(B=4, T=2048, num_seqs=4, Hqk=16, Hv=16, Dk=128, Dv=128, flags=dn.DN_GATE_PER_KEY)
+    assert lib.dn_chunk_fwd_noalloc(ctypes.byref(big), p, p, p, p, p, None, None, None, p,
+                                    None) == dn.DN_ERR_WORKSPACE
+    assert lib.dn_chunk_fwd_noalloc(ctypes.byref(_shape(Dk=48)), p, p, p, p, None, None, None,
+                                    None, p, None) == dn.DN_ERR_UNSUPPORTED
+    assert lib.dn_chunk_fwd_noalloc(None, p, p, p, p, None, None, None, None, p,
+                                    None) == dn.DN_ERR_INVALID_ARG
