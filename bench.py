@@ -14,8 +14,9 @@ launching stream around the eager loop.  The warmup runs long enough (200 calls,
 12 ms) for the GPU's clocks to settle before the timed region.
 
 The two other full-size prefill workloads (gated GQA B2 T8192 16 -> 32 heads; 8 packed gated
-sequences of 32,768 tokens in all) are timed the same way, with events around 10
-back-to-back calls, and each gets its own roofline block (algorithmic bytes and flops,
+sequences of 32,768 tokens in all) are timed right after it, each warmed for about 20 ms
+of back-to-back calls and then timed with events around 10 calls, and each gets its own
+roofline block (algorithmic bytes and flops,
 rocprofv3 counters) under ``prefill_workloads``.  ``--only`` runs one of the three alone
 (for a rocprofv3 counter pass per workload).  The decode step (256 sequences x 32 heads,
 state updated in place) is timed with events around a loop of back-to-back steps and
@@ -309,6 +310,11 @@ def main():
     head_block = prefill_roofline("prefill_config2", "fused_kernel<false, false>", call_us, alg_b,
                                   tokens, Hqk, Hv, D)
 
+    # ------------------------------------ the other two full-size prefill workloads, right
+    # after the headline and warmed like it (about 20 ms of back-to-back calls each, so the
+    # clocks have settled before the timed calls)
+    other = {3: time_prefill_workload(3, 10, warmup=80), 5: time_prefill_workload(5, 10, warmup=40)}
+
     # ------------------------------------------------------------------- decode
     y = make_case(B=DECODE["N"], T=1, Hqk=DECODE["H"], Dk=DECODE["D"], dtype="bf16", g_scale=0.1,
                   init_std=0.02, seed=0, decode=True)
@@ -556,9 +562,6 @@ def main():
                         "algorithmic_bytes": cstep_b},
     }
     del cx, cy, cst, dx, dcs, dyo
-
-    # ------------------------------------ the other two full-size prefill workloads
-    other = {cfg: time_prefill_workload(cfg, 10) for cfg in (3, 5)}
 
     line = {
         "metric": "prefill tokens/sec + MFMA util; decode-step state GB/s vs HBM peak",

@@ -41,7 +41,8 @@
 //                   (each wave: two 16-token row blocks, all 32 columns)
 //   4, 5      0, 2  loaders: K, scalars of j + 1       Q, V of j + 1; fetch j + 3
 //   6         1     T of chunk j (UT inverse of A)     A of chunk j + 1, diagonal tiles
-//   2         1     -                                  A of chunk j + 1, tiles below them
+//   2         1     A of chunk j, rows 32..63 x        A of chunk j + 1, tiles (0,1), (2,3)
+//                   columns 0..31 (the chain's A_BL)   (the UT inverse's A21 blocks)
 //
 // Waves w and w + 4 share a SIMD (the hardware deals waves 0-3 to SIMDs 0, 2, 1, 3; read
 // from the HW_ID register).  The UT inverse, the longest serial step, has its SIMD to
@@ -279,16 +280,18 @@ __device__ __forceinline__ float gram_diag(const f32x4& g, int l16) {
 }
 
 // A of chunk j, one part of its tiles (I, R).  Part 0, the four diagonal tiles, goes to
-// Ad in fp32 (strictly lower part, packed); part 1, the six tiles below them, to Ab in bf16.
-constexpr int a_tiles(int part) { return part == 0 ? 4 : 6; }
-constexpr int a_tile_i(int part, int n) { return part == 0 ? n : (n == 2 || n == 4) ? 1 : n == 5 ? 2 : 0; }
-constexpr int a_tile_r(int part, int n) { return part == 0 ? n : n == 0 ? 1 : n <= 2 ? 2 : 3; }
+// Ad in fp16 (strictly lower part, packed); part 1, the tiles (0,1) and (2,3) right below
+// them (the UT inverse's A21 blocks), and part 2, the block rows 32..63 x columns 0..31
+// (the chain's A_BL), go to Ab in bf16.
+constexpr int a_tiles(int part) { return part == 0 ? 4 : part == 1 ? 2 : 4; }
+constexpr int a_tile_i(int part, int n) { return part == 0 ? n : part == 1 ? 2 * n : (n & 1); }
+constexpr int a_tile_r(int part, int n) { return part == 0 ? n : part == 1 ? 2 * n + 1 : 2 + (n >> 1); }
 
 //
 // With the in-rule normalisation, part 0 takes |k_r|^2 from the diagonal of its own Gram
 // tiles, scales A's rows by s_r^2 and publishes the chain's factors (SC_B1, SC_B2, SC_S2)
-// for row 16 q16 + l16.  Part 1 writes its tiles with beta alone; their consumers apply
-// s_r^2 to the rows of the products they form from them.
+// for row 16 q16 + l16.  Parts 1 and 2 write their tiles with beta alone; their consumers
+// apply s_r^2 to the rows of the products they form from them.
 template <bool GATED, bool NORM, int PART>
 __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16, float eps) {
     constexpr bool NRM = NORM && PART == 0;
@@ -338,7 +341,7 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16, f
         f32x4 av;
 #pragma unroll
         for (int e = 0; e < 4; ++e) av[e] = br[n] * d[e] * G[n][e];
-        if (PART == 1) {
+        if (PART >= 1) {
             st4(&sm.Ab[r][i0], av[0], av[1], av[2], av[3]);
         } else {
             // entries on or above the diagonal go to the spare slot 120 of the block
@@ -567,15 +570,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             const float* s = &sm.sc[j % 3][0][0];
             bf16x8 rb0;   // R rows 0..31 as B operand (k = token)
             f32x4 R[4];   // R, token tile t: tokens 16 t + 4 q16 + e, column jc + l16
-            bf16x8 abl[2];  // A rows 32..63, tokens 0..31 (read here: the A waves rewrite Ab in .2)
-            f32x4 s2bl[2];  // in-rule normalisation: s_r^2 of those rows (Ab holds them without)
             if (live) {
-#pragma unroll
-                for (int t = 2; t < 4; ++t) abl[t - 2] = ld8(&sm.Ab[16 * t + l16][8 * q16]);
-                if (NORM) {
-#pragma unroll
-                    for (int t = 2; t < 4; ++t) s2bl[t - 2] = *reinterpret_cast<const f32x4*>(&s[SC_S2 * FC + 16 * t + 4 * q16]);
-                }
                 // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
                 f32x4 X[4];
 #pragma unroll
@@ -612,6 +607,15 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                 // T operands T[16 t + m][k] = Tt[k][16 t + m] by transposed reads.  With decay,
                 // the tail factors are read here, ahead of the Delta store (a read behind a
                 // store waits a round trip of its own).
+                // A rows 32..63, tokens 0..31 (wave 2 wrote them in the first half)
+                bf16x8 abl[2];
+                f32x4 s2bl[2];  // in-rule normalisation: s_r^2 of those rows (Ab holds them without)
+#pragma unroll
+                for (int t = 2; t < 4; ++t) abl[t - 2] = ld8(&sm.Ab[16 * t + l16][8 * q16]);
+                if (NORM) {
+#pragma unroll
+                    for (int t = 2; t < 4; ++t) s2bl[t - 2] = *reinterpret_cast<const f32x4*>(&s[SC_S2 * FC + 16 * t + 4 * q16]);
+                }
                 f32x4 tl[4];
                 float Gl = 1.f;
                 if (GATED) {
@@ -826,11 +830,12 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             __syncthreads();
         }
     } else {
-        // -------------------------------------------- wave 2: other half of A of j + 1
+        // ------------------ wave 2: A_BL of j in the first half, A21 of j + 1 in the second
         __syncthreads();
         make_a<GATED, NORM, 1>(sm, 0, l16, q16, a.eps);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
+            if (j < nc) make_a<GATED, NORM, 2>(sm, j, l16, q16, a.eps);
             __syncthreads();
             if (j + 1 < nc) make_a<GATED, NORM, 1>(sm, j + 1, l16, q16, a.eps);
             __syncthreads();
