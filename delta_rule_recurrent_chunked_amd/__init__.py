@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_path", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv",
+__all__ = ["chunk_fwd", "chunk_fwd_path", "chunk_bwd", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv",
            "causal_conv_step", "workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
@@ -34,7 +34,8 @@ DN_F32, DN_BF16 = 0, 1
 EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
             "dn_norm_gate", "dn_recurrent_fwd", "dn_causal_conv", "dn_causal_conv_step",
             "dn_recurrent_bwd", "dn_recurrent_bwd_workspace_bytes", "dn_chunk_fwd_path",
-            "dn_chunk_fwd_noalloc", "dn_status_str", "dn_version")
+            "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_chunk_bwd_workspace_bytes",
+            "dn_status_str", "dn_version")
 
 
 class DeltaNetError(RuntimeError):
@@ -105,6 +106,10 @@ def load_library():
         lib.dn_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.dn_recurrent_bwd.argtypes = [sp] + [vp] * 17 + [sz, vp]
         lib.dn_recurrent_bwd.restype = ctypes.c_int
+        lib.dn_chunk_bwd.argtypes = [sp] + [vp] * 16 + [sz, vp]
+        lib.dn_chunk_bwd.restype = ctypes.c_int
+        lib.dn_chunk_bwd_workspace_bytes.argtypes = [sp]
+        lib.dn_chunk_bwd_workspace_bytes.restype = sz
         lib.dn_recurrent_bwd_workspace_bytes.argtypes = [sp]
         lib.dn_recurrent_bwd_workspace_bytes.restype = sz
         cs = ctypes.POINTER(_ConvShape)
@@ -352,6 +357,47 @@ def recurrent_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch
                                   _stream(dev))
     if rc != DN_OK:
         _raise(rc, "dn_recurrent_bwd")
+    return out
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+              g: Optional[torch.Tensor], initial_state: Optional[torch.Tensor], d_o: torch.Tensor,
+              d_final_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Reverse pass of the chunked form (no state trace): gradients of a loss with dL/do =
+    ``d_o`` and dL/d final state = ``d_final_state`` for q, k, v, beta, g and the initial
+    state.  bf16, Dk = Dv = 128, one gate per head or none.  Returns a dict of float32
+    tensors dq, dk (``[B, T, Hqk, Dk]``), dv, dbeta, dg (None without g) and
+    d_initial_state.  ``workspace`` (uint8, at least the size the library asks for) may be
+    passed to avoid its allocation."""
+    lib = load_library()
+    shape, _, _, N = _prompt_args(q, k, v, beta, g, initial_state, False, cu_seqlens, scale, 64,
+                                  None, None, False, False, 1e-6)
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    _dev(d_o, "d_o", q.dtype, (B, T, Hv, Dv))
+    if d_final_state is not None:
+        _dev(d_final_state, "d_final_state", torch.float32, (N, Hv, Dk, Dv))
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, Hqk, Dk), **f32), dk=torch.empty((B, T, Hqk, Dk), **f32),
+               dv=torch.empty((B, T, Hv, Dv), **f32), dbeta=torch.empty((B, T, Hv), **f32),
+               dg=torch.empty((B, T, Hv), **f32) if g is not None else None,
+               d_initial_state=torch.empty((N, Hv, Dk, Dv), **f32))
+    need = int(lib.dn_chunk_bwd_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev(workspace, "workspace", torch.uint8)
+    with torch.cuda.device(dev):
+        rc = lib.dn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                              _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(cu_seqlens),
+                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                              _ptr(out["dg"]), _ptr(out["d_initial_state"]), _ptr(workspace),
+                              workspace.numel(), _stream(dev))
+    if rc != DN_OK:
+        _raise(rc, "dn_chunk_bwd")
     return out
 
 

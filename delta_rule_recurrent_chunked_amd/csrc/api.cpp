@@ -263,6 +263,48 @@ dn_status dn_recurrent_bwd(const dn_shape* s, const void* q, const void* k, cons
     return dn::launch_recurrent_bwd(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
+// Chunk numbers the chunkwise reverse pass keeps per value head: every batch row's chunks,
+// or the packed bound; a query without cu_seqlens at B == 1 may be followed by either call.
+static long chunk_bwd_ncid(const dn_shape* s, bool packed) {
+    const long rows = (long)s->B * ((s->T + 63) / 64);
+    const long pk = (long)(s->T / 64) + s->num_seqs + 1;
+    return packed ? pk : (s->B == 1 ? (rows > pk ? rows : pk) : rows);
+}
+
+size_t dn_chunk_bwd_workspace_bytes(const dn_shape* s) {
+    dn::PrefillArgs a;
+    const bool packed = s && s->B == 1 && s->num_seqs != 1;
+    if (prefill_shape(s, packed, a) != DN_OK || !dn::chunk_bwd_supported(a)) return 0;
+    return dn::chunk_bwd_workspace_bytes(a, chunk_bwd_ncid(s, packed));
+}
+
+dn_status dn_chunk_bwd(const dn_shape* s, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, const void* dout,
+                       const float* dfinal, const int32_t* cu, float* dq, float* dk, float* dv,
+                       float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    dn::ChunkBwdArgs a{};
+    dn_status st = prefill_shape(s, cu != nullptr, a);
+    if (st != DN_OK) return st;
+    if (!dn::chunk_bwd_supported(a)) return DN_ERR_UNSUPPORTED;
+    const long tokens = (long)s->B * s->T;
+    if (tokens > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta || (g && !dg)))
+        return DN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, h0, dout, dfinal, dh0, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
+    const void* scalars[] = {beta, g, cu, dq, dk, dv, dbeta, dg};
+    for (const void* p : scalars)
+        if (p && !aligned4(p)) return DN_ERR_INVALID_ARG;
+    const size_t need = dn::chunk_bwd_workspace_bytes(a, chunk_bwd_ncid(s, cu != nullptr));
+    if (!ws || ws_bytes < need) return DN_ERR_WORKSPACE;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.h0 = h0; a.cu = cu; a.ws = ws;
+    a.ws_bytes = ws_bytes;
+    a.dout = dout; a.dfinal = dfinal;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = g ? dg : nullptr; a.dh0 = dh0;
+    return dn::launch_chunk_bwd(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
 dn_status dn_decode_step(const dn_shape* s, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float* state, void* o,
                          hipStream_t stream) {

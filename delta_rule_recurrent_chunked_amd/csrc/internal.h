@@ -104,6 +104,29 @@ struct RecurrentBwdArgs : PrefillArgs {
 };
 int recurrent_bwd_slices(int Dk, int Dv);
 
+// The chunkwise reverse pass: the forward's arguments, dL/do and dL/dM_T in; gradients out
+// (fp32).  The workspace holds the state at every chunk start and each 32-column slice's
+// share of dq, dk, dbeta and dgamma per (chunk, row).
+struct ChunkBwdArgs : PrefillArgs {
+    const void* dout;               // [tokens, Hv, Dv] bf16
+    const float* dfinal;            // [N, Hv, Dk, Dv] or null
+    long ncid;                      // chunk numbers (chunk_id_bound)
+    float* states;                  // [ncid, Hv, Dk, Dv]
+    float* ws_dq;                   // [4, ncid, Hv, 64, Dk]
+    float* ws_dk;                   // [4, ncid, Hv, 64, Dk]
+    float* ws_db;                   // [4, ncid, Hv, 64]
+    float* ws_dg;                   // [4, ncid, Hv, 64]
+    float* dq;                      // [tokens, Hqk, Dk]
+    float* dk;                      // [tokens, Hqk, Dk]
+    float* dv;                      // [tokens, Hv, Dv]
+    float* dbeta;                   // [tokens, Hv]
+    float* dg;                      // [tokens, Hv] or null (no gate)
+    float* dh0;                     // [N, Hv, Dk, Dv] or null
+};
+bool chunk_bwd_supported(const PrefillArgs& a);
+size_t chunk_bwd_workspace_bytes(const PrefillArgs& a, long ncid);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
+
 // Launchers (host functions); each returns hipGetLastError() after its launches.
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s);
 hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t s);
@@ -122,6 +145,8 @@ size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s);
+// the same kernel writing the state at every chunk start to a.ws instead of the outputs
+hipError_t launch_prefill_fused_states(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace dn
 
@@ -143,6 +168,17 @@ __device__ __forceinline__ float inv_norm(float ss, float eps) {
 
 // silu(z) = z / (1 + exp(-z)), the output gate's activation (hardware reciprocal)
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
+// Number of the first 64-token chunk of sequence n in per-chunk workspaces: n * ceil(T / 64)
+// for a batch of rows; floor(cu[n] / 64) + n for packed sequences, which gives every chunk
+// of every sequence a distinct number below T / 64 + N + 1 without a scan over the
+// sequences (chunk c of sequence n is chunk_id_base + c).
+__host__ __device__ __forceinline__ long chunk_id_base(const PrefillArgs& a, int n) {
+    return a.cu ? (long)(a.cu[n] / 64) + n : (long)n * ((a.T + 63) / 64);
+}
+__host__ __device__ __forceinline__ long chunk_id_bound(const PrefillArgs& a) {
+    return a.cu ? (long)(a.T / 64) + a.N + 1 : (long)a.N * ((a.T + 63) / 64);
+}
 
 // Token range [bos, eos) of sequence n.
 __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, long& bos, long& eos) {

@@ -494,7 +494,10 @@ __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f1
 }
 
 // -------------------------------------------------------------------------- kernel
-template <bool GATED, bool NORM>
+// STATES: the chain waves also write the state at every chunk start (fp32, key-major, at
+// a.ws + chunk_id_base(n) + chunk), the input of the chunkwise reverse pass, and the
+// output waves skip O (that launch needs only the states).
+template <bool GATED, bool NORM, bool STATES = false>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void fused_kernel(PrefillArgs a) {
     __shared__ FusedSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -565,11 +568,21 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         }
         __syncthreads();
         __syncthreads();
+        float* st_out = nullptr;   // STATES: this chain wave's columns of chunk 0's start state
+        if (STATES) st_out = static_cast<float*>(a.ws) + ((long)chunk_id_base(a, w.n) * a.Hv + w.h) * FD * FD +
+                             w.j0 + jc + l16;
         for (int j = 0; j < nph; ++j) {
             const bool live = j < nc;
             const float* s = &sm.sc[j % 3][0][0];
             bf16x8 rb0;   // R rows 0..31 as B operand (k = token)
             f32x4 R[4];   // R, token tile t: tokens 16 t + 4 q16 + e, column jc + l16
+            if (STATES && live) {
+                float* dst = st_out + (long)j * a.Hv * FD * FD;
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q16 + e) * FD] = M[mt][e];
+            }
             if (live) {
                 // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
                 f32x4 X[4];
@@ -703,7 +716,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         __syncthreads();
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            const bool o_live = j >= 1 && j <= nc, y_live = j < nc;
+            const bool o_live = !STATES && j >= 1 && j <= nc, y_live = !STATES && j < nc;
             if (o_live) {
                 // O of chunk j - 1 = scale (exp(gamma) Y + P Delta), P lower triangular
                 const int jp = j - 1;
@@ -850,6 +863,17 @@ bool prefill_fused_supported(const PrefillArgs& a) {
     // span less than 2 GiB of q / k / v / o
     const long span = ((long)a.T + 2 * FC) * (a.Hqk > a.Hv ? a.Hqk : a.Hv) * FD * 2;
     return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC && !a.g_per_key && span < (1L << 31);
+}
+
+hipError_t launch_prefill_fused_states(const PrefillArgs& a, hipStream_t s) {
+    const long blocks = (long)a.N * a.Hv * NSL;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (blocks > 0) {
+        const dim3 grid((unsigned)blocks), block(NT);
+        if (a.g) hipLaunchKernelGGL((fused_kernel<true, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((fused_kernel<false, false, true>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s) {

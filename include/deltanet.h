@@ -263,6 +263,44 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
                            float* d_initial_state, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * dn_chunk_bwd -- the reverse pass of the chunked form on the matrix cores (gradients for
+ * training; the learned gate and write strengths of the nnterp "linear_attention" page,
+ * LinearAttention class text): given dL/do and dL/d final_state, the gradients for q, k,
+ * v, beta, g and the initial state, without a per-token state trace.  It reruns the forward
+ * chunk chain to keep the state at every chunk start (Dk * Dv * 4 bytes per chunk and value
+ * head), then walks each sequence's chunks backwards, carrying dL/dM from chunk to chunk
+ * and recomputing each chunk's matrices (A, T, P, X, Delta) from its start state; value
+ * columns are split over 32-column slices whose shares of dq, dk, dbeta, dg are added in a
+ * fixed order (the result is bitwise reproducible).
+ *
+ * Supported: bf16 q/k/v/d_o, Dk = Dv = 128, 64-token chunks, one log decay per head or
+ * none, no flags; other shapes return DN_ERR_UNSUPPORTED (dn_recurrent_bwd computes them
+ * token by token from a state trace).  Arguments as dn_recurrent_bwd without the trace:
+ *
+ *   d_o             [B, T, Hv, Dv] bf16 (required)
+ *   d_final_state   [N, Hv, Dk, Dv] fp32 or NULL (zero)
+ *   dq, dk          [B, T, Hqk, Dk] fp32 (summed over the value heads of each q/k head)
+ *   dv              [B, T, Hv, Dv] fp32;  dbeta [B, T, Hv] fp32
+ *   dg              [B, T, Hv] fp32, required when g is given, else ignored
+ *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
+ *   workspace       dn_chunk_bwd_workspace_bytes(shape) bytes: the chunk-start states and
+ *                   the slices' shares ((Dk * Dv + 4 * 64 * (2 Dk + 2)) * 4 bytes per chunk
+ *                   and value head); contents on entry ignored, on exit undefined
+ *
+ * Errors: as dn_chunk_fwd, DN_ERR_UNSUPPORTED as above, DN_ERR_WORKSPACE.
+ */
+dn_status dn_chunk_bwd(const dn_shape* shape,
+                       const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* initial_state,
+                       const void* d_o, const float* d_final_state, const int32_t* cu_seqlens,
+                       float* dq, float* dk, float* dv, float* dbeta, float* dg,
+                       float* d_initial_state, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Bytes of workspace dn_chunk_bwd needs for this shape (0 when the shape is unsupported). */
+size_t dn_chunk_bwd_workspace_bytes(const dn_shape* shape);
+
 /* Bytes of workspace dn_recurrent_bwd needs: each value-column slice's share of dq, dk,
  * dbeta and dg before they are added in a fixed order (the shape's flags matter: dg per
  * key channel takes Dk floats per token and head). */

@@ -93,3 +93,93 @@ def chunked(q, k, v, beta, g=None, init=None, cu_seqlens=None, scale=1.0, C=64,
                 M = np.exp(gam[-1]) * M + K.T @ Q(tail[:, None] * Delta)
             final[n, h] = M
     return o.reshape(B, T, Hv, Dv), final
+
+
+def chunked_backward(q, k, v, beta, g, init, do, dfinal=None, cu_seqlens=None, scale=1.0, C=64):
+    """Reverse pass of the chunked form, chunk by chunk from the chunk-start states (the
+    algebra the HIP chunkwise reverse pass implements).  Per chunk, with dM' the gradient
+    of the state after it and dO of its outputs:
+
+      dDelta = scale P^T dO + diag(tail) K dM'        dR = T^T dDelta
+      dV = diag(beta) dR                               dX = -diag(beta exp(gamma)) dR
+      dM = exp(gamma_L) dM' + scale Q^T diag(exp(gamma)) dO + K^T dX
+      dA = -(dR Delta^T) strictly lower,   dP = scale (dO Delta^T) lower with the diagonal
+      dQ = scale diag(exp(gamma)) dO M^T + (dP o D) K
+      dK = dX M^T + diag(tail) Delta dM'^T + (W + W^T) K + (dP o D)^T Q,  W = dA o diag(beta) D
+      dbeta_r = (V - diag(exp(gamma)) X)_r . dR_r + sum_i dA_ri D_ri k_r.k_i
+      dgamma_r = scale exp(gamma_r) (Q M)_r . dO_r - beta_r exp(gamma_r) X_r . dR_r
+                 + rowsum_r(dA o A) - colsum_r(dA o A) + rowsum_r(dP o P) - colsum_r(dP o P) - c_r
+                 (+ exp(gamma_L) <M, dM'> + sum_r c_r on the chunk's last row),
+      c_r = tail_r (K dM')_r . Delta_r,   dg_i = sum_{r >= i in the chunk} dgamma_r.
+
+    Returns the dict of ``oracle.backward.backward``."""
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    qf, kf, vf = q.reshape(B * T, Hqk, Dk), k.reshape(B * T, Hqk, Dk), v.reshape(B * T, Hv, Dv)
+    bf = beta.reshape(B * T, Hv)
+    dof = do.reshape(B * T, Hv, Dv)
+    gf = None if g is None else g.reshape(B * T, Hv)
+    cu = (np.arange(B + 1) * T) if cu_seqlens is None else np.asarray(cu_seqlens)
+    N = len(cu) - 1
+    dq, dk = np.zeros_like(qf, dtype=np.float64), np.zeros_like(kf, dtype=np.float64)
+    dv, dbeta = np.zeros_like(vf, dtype=np.float64), np.zeros_like(bf, dtype=np.float64)
+    dg = None if g is None else np.zeros_like(gf, dtype=np.float64)
+    dinit = np.zeros((N, Hv, Dk, Dv))
+    for n in range(N):
+        for h in range(Hv):
+            hq = h // grp
+            starts = list(range(cu[n], cu[n + 1], C))
+            # forward sweep: the state at each chunk start
+            M = np.zeros((Dk, Dv)) if init is None else np.array(init[n, h], dtype=np.float64)
+            Ms = []
+            for s in starts:
+                e = min(s + C, cu[n + 1])
+                K, V, bt = kf[s:e, hq], vf[s:e, h], bf[s:e, h]
+                gam = np.zeros(e - s) if gf is None else np.cumsum(gf[s:e, h])
+                low = np.tril(np.ones((e - s, e - s), dtype=bool))
+                D = np.where(low, np.exp(np.where(low, gam[:, None] - gam[None, :], 0.0)), 0.0)
+                A = np.tril(bt[:, None] * D * (K @ K.T), -1)
+                Delta = np.linalg.solve(np.eye(e - s) + A, bt[:, None] * (V - np.exp(gam)[:, None] * (K @ M)))
+                Ms.append(M)
+                M = np.exp(gam[-1]) * M + K.T @ (np.exp(gam[-1] - gam)[:, None] * Delta)
+            dMp = np.zeros((Dk, Dv)) if dfinal is None else np.array(dfinal[n, h], dtype=np.float64)
+            for s, M in reversed(list(zip(starts, Ms))):
+                e = min(s + C, cu[n + 1])
+                L = e - s
+                K, Qc, V, bt, dO = kf[s:e, hq], qf[s:e, hq], vf[s:e, h], bf[s:e, h], dof[s:e, h]
+                gam = np.zeros(L) if gf is None else np.cumsum(gf[s:e, h])
+                eg, tail = np.exp(gam), np.exp(gam[-1] - gam)
+                low = np.tril(np.ones((L, L), dtype=bool))
+                D = np.where(low, np.exp(np.where(low, gam[:, None] - gam[None, :], 0.0)), 0.0)
+                Gk = D * (K @ K.T)
+                A = np.tril(bt[:, None] * Gk, -1)
+                Tm = np.linalg.inv(np.eye(L) + A)
+                P = D * (Qc @ K.T)
+                X = K @ M
+                Rt = V - eg[:, None] * X
+                Delta = Tm @ (bt[:, None] * Rt)
+                KdM = K @ dMp
+                dDelta = scale * P.T @ dO + tail[:, None] * KdM
+                dR = Tm.T @ dDelta
+                dv[s:e, h] = bt[:, None] * dR
+                dX = -(bt * eg)[:, None] * dR
+                dA = np.tril(-(dR @ Delta.T), -1)
+                dP = np.tril(scale * (dO @ Delta.T))
+                W = dA * bt[:, None] * D
+                Z = dP * D
+                dq[s:e, hq] += scale * eg[:, None] * (dO @ M.T) + Z @ K
+                dk[s:e, hq] += dX @ M.T + tail[:, None] * (Delta @ dMp.T) + (W + W.T) @ K + Z.T @ Qc
+                dbeta[s:e, h] = np.sum(Rt * dR, axis=1) + np.sum(dA * Gk, axis=1)
+                if dg is not None:
+                    c = tail * np.sum(KdM * Delta, axis=1)
+                    dA_A, dP_P = dA * A, dP * P
+                    dgam = (scale * eg * np.sum((Qc @ M) * dO, axis=1) - bt * eg * np.sum(X * dR, axis=1)
+                            + dA_A.sum(1) - dA_A.sum(0) + dP_P.sum(1) - dP_P.sum(0) - c)
+                    dgam[-1] += np.exp(gam[-1]) * np.sum(M * dMp) + c.sum()
+                    dg[s:e, h] = np.cumsum(dgam[::-1])[::-1]
+                dMp = np.exp(gam[-1]) * dMp + scale * Qc.T @ (eg[:, None] * dO) + K.T @ dX
+            dinit[n, h] = dMp
+    return dict(dq=dq.reshape(q.shape), dk=dk.reshape(k.shape), dv=dv.reshape(v.shape),
+                dbeta=dbeta.reshape(beta.shape), dg=None if dg is None else dg.reshape(g.shape),
+                dinit=dinit)

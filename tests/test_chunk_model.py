@@ -54,3 +54,23 @@ def test_bf16_operand_rounding_error_budget():
     o, s = chunked(f["q"], f["k"], f["v"], f["beta"], f["g"], f["init"], quant=_bf16)
     assert rel_l2(o, o_ref) < 5e-3
     assert rel_l2(s, s_ref) < 5e-3
+
+
+@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("gated", [False, True])
+def test_chunked_backward_matches_oracle(C, gated):
+    """The chunkwise reverse-pass algebra against the fp64 token-by-token reverse pass:
+    packed sequences (an empty one, ragged chunks), GQA, beta in (0, 2), initial state."""
+    from oracle.backward import backward
+    from tests.chunk_model import chunked_backward
+    x = make_case(B=1, Hqk=1, Hv=2, Dk=8, Dv=6, seqlens=[70, 0, 33, 5], g_scale=0.3 if gated else None,
+                  init_std=0.5, beta_scale=2.0, seed=21)
+    f = x.f64()
+    rng = np.random.default_rng(22)
+    do = rng.standard_normal((1, x.T, 2, 6))
+    dfin = rng.standard_normal((x.num_seqs, 2, 8, 6))
+    ref = backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["init"], do, dfin, x.cu_seqlens, 0.7)
+    got = chunked_backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["init"], do, dfin,
+                           x.cu_seqlens, 0.7, C=C)
+    for name in ("dq", "dk", "dv", "dbeta", "dinit") + (("dg",) if gated else ()):
+        np.testing.assert_allclose(got[name], ref[name], rtol=1e-9, atol=1e-9, err_msg=name)
