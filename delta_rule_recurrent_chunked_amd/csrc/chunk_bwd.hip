@@ -57,7 +57,7 @@ constexpr int P64 = BC + 16;
 constexpr int P32 = BS + 16;
 constexpr int ADP = 136;           // A's diagonal 16x16 blocks, 120 packed fp16 entries + spare
 constexpr int NDB = 8;             // dbeta partial slots per row
-constexpr int NDG = 24;            // dgamma partial slots per row
+constexpr int NDG = 48;            // dgamma partial slots per row
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct alignas(16) BwdSmem {
@@ -65,7 +65,7 @@ struct alignas(16) BwdSmem {
     __bf16 V[BC][P32], dO[BC][P32], R[BC][P32], Dl[BC][P32], dDl[BC][P32], dR[BC][P32];
     __bf16 M[BD][P32];             // the slice of the state at the chunk start
     __bf16 dM[BD][P32];            // the slice of dM' (the gradient of the state after the chunk)
-    __bf16 T[BC][P64];             // T = (I + A)^-1, lower triangular
+    __bf16 Tt[BC][P64];            // T^T, T = (I + A)^-1 lower triangular
     __bf16 P[BC][P64];             // P, then Z = dP o D
     __bf16 G[BC][P64];             // D o K K^T (strictly lower), then W = dA o diag(beta) D
     _Float16 Ad[4][ADP];           // A's diagonal blocks (strictly lower, packed by rows)
@@ -93,20 +93,24 @@ __device__ __forceinline__ void put_tile(__bf16* S, int pitch, int i, int j, con
 #pragma unroll
     for (int e = 0; e < 4; ++e) S[(16 * i + 4 * q16 + e) * pitch + 16 * j + l16] = (__bf16)c[e];
 }
-// sum over the 16 lanes of one q16 group (the tile's columns) of each of the lane's 4 rows
+// DPP lane moves within rows of 16 lanes (every lane has a source)
+template <int CTRL>
+__device__ __forceinline__ float dpp16(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 16 lanes of one q16 group (the tile's columns) of each of the lane's 4 rows:
+// lane ^ 1, lane ^ 2 (quad permutes), then the 8- and 16-lane mirrors, in every lane
 __device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], off);
+    for (int e = 0; e < 4; ++e) {
+        float x = v[e];
+        x += dpp16<0xB1>(x);
+        x += dpp16<0x4E>(x);
+        x += dpp16<0x141>(x);
+        x += dpp16<0x140>(x);
+        v[e] = x;
+    }
     return v;
-}
-// sum over the tile's 16 rows (4 entries x 4 q16 groups) of the lane's column
-__device__ __forceinline__ float col_sum16(const f32x4& v) {
-    float x = v[0] + v[1] + v[2] + v[3];
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -202,11 +206,12 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
     };
     put_dm();
 
-    // P and G (later Z and W) are written below their 16-block diagonal only; the products
-    // that read them by 32-row blocks also read the tiles above it, which stay zero
+    // P and G (later Z and W) are written below their 16-block diagonal only, T^T above
+    // it; the products that read them by 32-row blocks also read the other tiles, zero
     for (int i = tid; i < BC * P64; i += NTB) {
         (&sm.P[0][0])[i] = (__bf16)0.f;
         (&sm.G[0][0])[i] = (__bf16)0.f;
+        (&sm.Tt[0][0])[i] = (__bf16)0.f;   // T's blocks above the diagonal stay zero
     }
 
     BwdIn cur, nxt;
@@ -276,7 +281,9 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
 
         // ------------------------- B2: T (wave 0); X = K M, R (waves 1-4); Y = Q M (5-7)
         if (wave == 0) {
-            {   // the four 16x16 diagonal blocks by forward substitution (lane = block, column)
+            __bf16 (*Tt)[P64] = sm.Tt;
+            {   // the four 16x16 diagonal blocks by forward substitution (lane = block, column):
+                // column cc of T_bb is row cc of T^T_bb, written as two 16-byte pieces
                 const int b = q16, cc = l16;
                 f16x8 ap[15];
 #pragma unroll
@@ -291,30 +298,30 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
                         const int idx = r * (r - 1) / 2 + m;
                         x[r] = __builtin_fmaf(-(float)ap[idx >> 3][idx & 7], x[m], x[r]);
                     }
+                bf16x8 lo8, hi8;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sm.T[16 * b + r][16 * b + cc] = (__bf16)x[r];
-                // the rest of T's lower triangle starts at zero (blocks below the diagonal
-                // are written below); blocks above the diagonal are zero
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-#pragma unroll
-                    for (int bb = 0; bb < 4; ++bb)
-                        if (bb != b) sm.T[16 * b + r][16 * bb + cc] = (__bf16)0.f;
+                for (int e = 0; e < 8; ++e) {
+                    lo8[e] = (__bf16)x[e];
+                    hi8[e] = (__bf16)x[8 + e];
+                }
+                *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b]) = lo8;
+                *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b + 8]) = hi8;
             }
             wave_lds_order();
             const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
             const bool lo = q16 < 2;   // k = 16 padded to the instruction's 32
-            // level 1: T21 = -T22 (A21 T11) within each 32x32 diagonal block (base 0, 32)
+            // level 1: T21 = -T22 (A21 T11) within each 32x32 diagonal block (base 0, 32);
+            // T's block (b + 1, b) is T^T's block (b, b + 1)
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
                 const int base = 32 * hb;
                 const bf16x8 af = lo ? scale_r(frag_r(&sm.G[0][0], P64, base + 16, base, l16, q16),
                                                sm.beta[base + 16 + l16]) : zero8();
-                const bf16x8 bf = lo ? frag_c(&sm.T[0][0], P64, base, base, l16, q16) : zero8();
+                const bf16x8 bf = lo ? frag_r(&Tt[0][0], P64, base, base, l16, q16) : zero8();
                 const f32x4 X1 = mma16(af, bf, z4);
-                const bf16x8 tf = lo ? frag_r(&sm.T[0][0], P64, base + 16, base + 16, l16, q16) : zero8();
+                const bf16x8 tf = lo ? frag_c(&Tt[0][0], P64, base + 16, base + 16, l16, q16) : zero8();
                 const f32x4 Y1 = mma16(tf, acc_to_b(X1, z4), z4);
-                put_tile(&sm.T[0][0], P64, 2 * hb + 1, 2 * hb, -Y1, l16, q16);
+                st4(&Tt[base + l16][base + 16 + 4 * q16], -Y1[0], -Y1[1], -Y1[2], -Y1[3]);
             }
             wave_lds_order();
             // level 2: T_BL = -T_BR (A_BL T_TL), 32 x 32 blocks
@@ -324,14 +331,14 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
 #pragma unroll
                 for (int tj = 0; tj < 2; ++tj)
                     X2[ti][tj] = mma16(scale_r(frag_r(&sm.G[0][0], P64, 32 + 16 * ti, 0, l16, q16), sm.beta[32 + 16 * ti + l16]),
-                                       frag_c(&sm.T[0][0], P64, 16 * tj, 0, l16, q16), z4);
+                                       frag_r(&Tt[0][0], P64, 16 * tj, 0, l16, q16), z4);
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int tj = 0; tj < 2; ++tj) {
-                    const f32x4 Y2 = mma16(frag_r(&sm.T[0][0], P64, 32 + 16 * ti, 32, l16, q16),
+                    const f32x4 Y2 = mma16(frag_c(&Tt[0][0], P64, 32 + 16 * ti, 32, l16, q16),
                                            acc_to_b(X2[0][tj], X2[1][tj]), z4);
-                    put_tile(&sm.T[0][0], P64, 2 + ti, tj, -Y2, l16, q16);
+                    st4(&Tt[16 * tj + l16][32 + 16 * ti + 4 * q16], -Y2[0], -Y2[1], -Y2[2], -Y2[3]);
                 }
         } else {
             // X tiles (i, j) on waves 1-4 (two each), Y tiles on waves 5-7
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < BC; k0 += 32)
-                if (k0 <= 16 * ti) acc = mma16(frag_r(&sm.T[0][0], P64, 16 * ti, k0, l16, q16),
+                if (k0 <= 16 * ti) acc = mma16(frag_c(&sm.Tt[0][0], P64, 16 * ti, k0, l16, q16),
                                                frag_c(&sm.R[0][0], P32, 16 * tj, k0, l16, q16), acc);
             put_tile(&sm.Dl[0][0], P32, ti, tj, acc, l16, q16);
         }
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
                 cr = row_sum16(cr);
                 if (l16 == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sm.pg[16 * ti + 4 * q16 + e][20 + tj] = cr[e];
+                    for (int e = 0; e < 4; ++e) sm.pg[16 * ti + 4 * q16 + e][44 + tj] = cr[e];
                 }
             }
         }
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < BC; k0 += 32)
-                if (k0 + 32 > 16 * ti) acc = mma16(frag_c(&sm.T[0][0], P64, 16 * ti, k0, l16, q16),
+                if (k0 + 32 > 16 * ti) acc = mma16(frag_r(&sm.Tt[0][0], P64, 16 * ti, k0, l16, q16),
                                                    frag_c(&sm.dDl[0][0], P32, 16 * tj, k0, l16, q16), acc);
             put_tile(&sm.dR[0][0], P32, ti, tj, acc, l16, q16);
             const int col = 16 * tj + l16;
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
                 S[row * P64 + col] = (__bf16)(keep ? dv * f * dec : 0.f);   // W or Z
             }
             const f32x4 r16 = row_sum16(rs);
-            const float c16 = col_sum16(cs4);
+            const float c4 = cs4[0] + cs4[1] + cs4[2] + cs4[3];   // this lane's 4 rows of the column
             if (isa) {
                 const f32x4 b16 = row_sum16(bsum);
                 if (l16 == 0) {
@@ -489,9 +496,9 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
             if (GATED) {
                 if (l16 == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sm.pg[16 * ri + 4 * q16 + e][(isa ? 4 : 12) + ci] = r16[e];
+                    for (int e = 0; e < 4; ++e) sm.pg[16 * ri + 4 * q16 + e][(isa ? 4 : 24) + ci] = r16[e];
                 }
-                if (q16 == 0) sm.pg[col][(isa ? 8 : 16) + ri] = -c16;
+                sm.pg[col][(isa ? 8 : 28) + 4 * ri + q16] = -c4;
             }
         }
         if (GATED) {   // <M, dM'> over this wave's two dM' tiles
@@ -546,12 +553,9 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
                         ka = mma16(frag_c(&sm.P[0][0], P64, 16 * i, k0, l16, q16), frag_c(&sm.Q[0][0], P128, 16 * j, k0, l16, q16), ka);
                     }
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * i + 4 * q16 + e;
-                    wq[row * BD + 16 * j + l16] = qa[e];
-                    wk[row * BD + 16 * j + l16] = ka[e];
-                }
+                // in the accumulator layout: tile t's 64 lanes x 4 entries, 1 KiB per tile
+                *reinterpret_cast<f32x4*>(wq + 256 * t + 4 * lane) = qa;
+                *reinterpret_cast<f32x4*>(wk + 256 * t + 4 * lane) = ka;
             }
         }
         __syncthreads();   // the dM', M and Delta tiles are read above; dM' is replaced below
@@ -581,23 +585,26 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
             put_dm();
         }
         // this chunk's dbeta and dgamma shares (the partial slots were written before the
-        // last two barriers)
-        if (tid < BC) {
-            const long ws_row = ((long)(slice * a.ncid + cid0 + c) * a.Hv + h) * BC + tid;
+        // last two barriers), on wave 7: lane = row
+        if (wave == 7) {
+            const long ws_row = ((long)(slice * a.ncid + cid0 + c) * a.Hv + h) * BC + lane;
             float b = 0.f;
 #pragma unroll
-            for (int s = 0; s < 6; ++s) b += sm.pb[tid][s];
+            for (int s2 = 0; s2 < 6; ++s2) b += sm.pb[lane][s2];
             a.ws_db[ws_row] = b;
             if (GATED) {
                 float gsum = 0.f;
 #pragma unroll
-                for (int s = 0; s < 22; ++s) gsum += sm.pg[tid][s];
-                if (tid == BC - 1) {   // gamma_L: e^gamma_L <M, dM'> + sum_r c_r
-                    float m = 0.f, csum = 0.f;
+                for (int s2 = 0; s2 < 46; ++s2) gsum += sm.pg[lane][s2];
+                // gamma_L, on the last row: e^gamma_L <M, dM'> + sum_r c_r (slots 44, 45 hold -c_r)
+                float ct = -(sm.pg[lane][44] + sm.pg[lane][45]);
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) ct += __shfl_xor(ct, off);
+                if (lane == BC - 1) {
+                    float m = 0.f;
 #pragma unroll
                     for (int w = 0; w < 8; ++w) m += sm.mdm[w];
-                    for (int r = 0; r < BC; ++r) csum -= sm.pg[r][20] + sm.pg[r][21];
-                    gsum += sm.eg[BC - 1] * m + csum;
+                    gsum += sm.eg[BC - 1] * m + ct;
                 }
                 a.ws_dg[ws_row] = gsum;
             }
@@ -617,67 +624,73 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
     }
 }
 
-// The slices' shares added in a fixed order: one thread per (token, q/k head, key) for dq
-// and dk (summed over the slices and over the value heads of the q/k head), and per
-// (token, value head) for dbeta and dg (dg_t = sum over the rows r >= t of t's chunk of
-// dgamma_r).
-__device__ __forceinline__ void token_chunk(const ChunkBwdArgs& a, long t, long& cid, int& row) {
+// The slices' shares added in a fixed order, one workgroup per (chunk number, q/k head):
+// dq and dk summed over the slices and over the value heads of the q/k head (the shares sit
+// in the accumulator layout: tile t = 8 i + j of 16 x 16, lane l, entry e is row
+// 16 i + 4 (l >> 4) + e, key 16 j + (l & 15)); per value head of the group, dbeta summed over
+// the slices and dg_t = the sum of dgamma_r over the rows r >= t of the chunk (a suffix scan
+// on one wave, lane = row).
+__global__ __launch_bounds__(256) void bwd_chunk_sum_kernel(ChunkBwdArgs a) {
+    const int hq = (int)(blockIdx.x % a.Hqk);
+    const long cid = blockIdx.x / a.Hqk;
     int n;
-    if (a.cu) {   // the sequence holding token t: the last n with cu[n] <= t
+    if (a.cu) {   // the last sequence whose first chunk number is <= cid (strictly increasing)
         int lo = 0, hi = a.N - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (a.cu[mid] <= t) lo = mid; else hi = mid - 1;
+            if (chunk_id_base(a, mid) <= cid) lo = mid; else hi = mid - 1;
         }
         n = lo;
     } else {
-        n = (int)(t / a.T);
+        n = (int)(cid / ((a.T + BC - 1) / BC));
     }
     long bos, eos;
     seq_range(a.cu, n, a.T, bos, eos);
-    cid = chunk_id_base(a, n) + (t - bos) / BC;
-    row = (int)((t - bos) % BC);
-}
-
-__global__ __launch_bounds__(256) void bwd_chunk_sum_kernel(ChunkBwdArgs a) {
-    const long tokens = (long)a.B * a.T;
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    const long nqk = tokens * a.Hqk * BD;
+    const long c = cid - chunk_id_base(a, n);
+    if (c * BC >= eos - bos) return;   // a number no chunk uses
+    const int rows = (int)min((long)BC, eos - bos - c * BC);
+    const long tok0 = bos + c * BC;
     const int grp = a.Hv / a.Hqk;
-    const long slice_stride = (long)a.ncid * a.Hv * BC;
-    if (i < nqk) {
-        const int key = (int)(i % BD);
-        const long th = i / BD;
-        const int hq = (int)(th % a.Hqk);
-        const long t = th / a.Hqk;
-        long cid;
-        int row;
-        token_chunk(a, t, cid, row);
-        float sq = 0.f, sk = 0.f;
-        for (int s = 0; s < BNS; ++s)
+    const long sstride = a.ncid * a.Hv * BC;   // rows between slices
+    const int tid = threadIdx.x;
+    for (int p = tid; p < BC * BD / 4; p += 256) {
+        const int t = p >> 6, ln = p & 63;
+        const int i = t >> 3, j = t & 7, l16 = ln & 15, q16 = ln >> 4;
+        f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+        for (int sl = 0; sl < BNS; ++sl)
             for (int g = 0; g < grp; ++g) {
-                const long r = (s * slice_stride + (cid * a.Hv + hq * grp + g) * BC + row) * BD + key;
-                sq += a.ws_dq[r];
-                sk += a.ws_dk[r];
+                const long r = (sl * sstride + (cid * a.Hv + (long)hq * grp + g) * BC) * BD + 4 * p;
+                sq += *reinterpret_cast<const f32x4*>(a.ws_dq + r);
+                sk += *reinterpret_cast<const f32x4*>(a.ws_dk + r);
             }
-        a.dq[i] = sq;
-        a.dk[i] = sk;
-    } else if (i < nqk + tokens * a.Hv) {
-        const long j = i - nqk;
-        const int h = (int)(j % a.Hv);
-        const long t = j / a.Hv;
-        long cid;
-        int row;
-        token_chunk(a, t, cid, row);
-        float sb = 0.f, sg = 0.f;
-        for (int s = 0; s < BNS; ++s) {
-            const long r = s * slice_stride + (cid * a.Hv + h) * BC;
-            sb += a.ws_db[r + row];
-            if (a.dg)
-                for (int rr = row; rr < BC; ++rr) sg += a.ws_dg[r + rr];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * i + 4 * q16 + e;
+            if (row < rows) {
+                const long o = ((tok0 + row) * a.Hqk + hq) * BD + 16 * j + l16;
+                a.dq[o] = sq[e];
+                a.dk[o] = sk[e];
+            }
         }
-        a.dbeta[j] = sb;
-        if (a.dg) a.dg[j] = sg;
+    }
+    const int lane = tid & 63;
+    for (int g = tid >> 6; g < grp; g += 4) {
+        const int h = hq * grp + g;
+        float sb = 0.f, sg = 0.f;
+        for (int sl = 0; sl < BNS; ++sl) {
+            const long r = sl * sstride + (cid * a.Hv + h) * BC + lane;
+            sb += a.ws_db[r];
+            if (a.dg) sg += a.ws_dg[r];
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_down(sg, off);
+            if (lane + off < 64) sg += o;
+        }
+        if (lane < rows) {
+            a.dbeta[(tok0 + lane) * a.Hv + h] = sb;
+            if (a.dg) a.dg[(tok0 + lane) * a.Hv + h] = sg;
+        }
     }
 }
 
@@ -719,13 +732,9 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
         else hipLaunchKernelGGL(chunk_bwd_kernel<false>, dim3((unsigned)blocks), dim3(NTB), 0, s, a);
     }
     // 3. the slices' shares added
-    const long tokens = (long)a.B * a.T;
-    const long items = tokens * a.Hqk * BD + tokens * a.Hv;
-    if (items > 0) {
-        const long grid = (items + 255) / 256;
-        if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd_chunk_sum_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
-    }
+    const long sum_blocks = a.ncid * a.Hqk;
+    if (sum_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (sum_blocks > 0) hipLaunchKernelGGL(bwd_chunk_sum_kernel, dim3((unsigned)sum_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

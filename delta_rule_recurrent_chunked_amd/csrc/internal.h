@@ -112,8 +112,8 @@ struct ChunkBwdArgs : PrefillArgs {
     const float* dfinal;            // [N, Hv, Dk, Dv] or null
     long ncid;                      // chunk numbers (chunk_id_bound)
     float* states;                  // [ncid, Hv, Dk, Dv]
-    float* ws_dq;                   // [4, ncid, Hv, 64, Dk]
-    float* ws_dk;                   // [4, ncid, Hv, 64, Dk]
+    float* ws_dq;                   // [4, ncid, Hv, 64 x Dk in 16 x 16 accumulator tiles]
+    float* ws_dk;                   // [4, ncid, Hv, 64 x Dk in 16 x 16 accumulator tiles]
     float* ws_db;                   // [4, ncid, Hv, 64]
     float* ws_dg;                   // [4, ncid, Hv, 64]
     float* dq;                      // [tokens, Hqk, Dk]
