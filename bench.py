@@ -20,7 +20,9 @@ roofline block (algorithmic bytes and flops,
 rocprofv3 counters) under ``prefill_workloads``.  ``--only`` runs one of the three alone
 (for a rocprofv3 counter pass per workload).  The decode step (256 sequences x 32 heads,
 state updated in place) is timed with events around a loop of back-to-back steps and
-reported in the same line.  The fp64 oracle is timed on the host cores on a bounded
+reported in the same line, and so is the chunkwise reverse pass (dn_chunk_bwd) on the gated
+H16 T2048 shape at B1 and B4 (20 calls between events, own roofline block under
+``chunk_backward``).  The fp64 oracle is timed on the host cores on a bounded
 sample of the prefill workload.
 
 Prints ONE JSON line.
@@ -80,6 +82,28 @@ def prefill_flops_dense(tokens, Hqk, Hv, D, C):
     per_v = 2 * 2 * C * D * D + 2 * 2 * C * C * D + 2 * C * D * D
     per_qk = 2 * 2 * C * C * D
     return int(chunks * (Hv * per_v + Hqk * per_qk))
+
+
+def chunk_bwd_bytes(tokens, Hqk, Hv, D, gated, N, init, dfinal):
+    """Algorithmic HBM bytes of one chunkwise reverse pass: q, k, v, dL/do read once (bf16),
+    beta (and g) read once, dq, dk, dv, dbeta (and dg) written once (fp32), the initial
+    state read and its gradient written (when given), dL/d final state read (when given).
+    The chunk-start states it recomputes and its workspace traffic are not algorithmic."""
+    b = tokens * (2 * Hqk * D * 2 + 2 * Hv * D * 2) + tokens * Hv * 4 * (2 if gated else 1)
+    b += tokens * (2 * Hqk * D * 4 + Hv * D * 4) + tokens * Hv * 4 * (2 if gated else 1)
+    b += N * Hv * D * D * 4 * ((2 if init else 0) + (1 if dfinal else 0))
+    return b
+
+
+def chunk_bwd_flops(tokens, Hv, D, C):
+    """Algorithmic matrix flops of one chunkwise reverse pass, triangles exploited, per token
+    and value head (one q/k head per value head): recomputing the chunk-start states, K M
+    and K^T Delta (4 d^2) with K K^T and T R (2 C d, half tiles); the gradients, seven
+    products against the state or its gradient (K M, K dM', Q^T dO, K^T dX, dO M^T, dX M^T,
+    Delta dM'^T: 14 d^2) and eleven half-tile chunk products (K K^T, Q K^T, T R, P^T dO,
+    T^T dDelta, dR Delta^T, dO Delta^T, Z K, W K, W^T K, Z^T Q: 11 C d).
+    18 d^2 + 13 C d = 401,408 flop per token-head at d = 128, C = 64."""
+    return int(tokens * Hv * (18 * D * D + 13 * C * D))
 
 
 def decode_bytes(N, Hqk, Hv, D):
@@ -515,6 +539,43 @@ def main():
                  "us_per_call": rec_us, "tokens_per_s": tokens / (rec_us * 1e-6),
                  "vs_chunked_call": rec_us / call_us}
 
+    # ------------- the chunkwise reverse pass (dn_chunk_bwd), gated, H16 T2048, B1 and B4
+    chunk_backward = {"what": "dL/dq, dk, dv, dbeta, dg and the initial state's gradient from "
+                              "dL/do, through the chunked form (chunk-start states recomputed by "
+                              "the prompt kernel), fp32 gradients"}
+    for bb in (1, 4):
+        xg = make_case(B=bb, T=T, Hqk=Hqk, Dk=D, dtype="bf16", g_scale=0.1, seed=0)
+        gq, gk, gv, gb, gg = (to_dev(a_) for a_ in (xg.q, xg.k, xg.v, xg.beta, xg.g))
+        gdo = torch.randn((bb, T, Hv, D), device=dev).to(torch.bfloat16)
+        gws = torch.empty(dn.chunk_bwd_workspace_bytes(bb, T, Hqk, Hv, D, D, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            dn.chunk_bwd(gq, gk, gv, gb, gg, None, gdo, workspace=gws)
+        torch.cuda.synchronize()
+        greps = 20
+        ev0.record(stream)
+        for _ in range(greps):
+            dn.chunk_bwd(gq, gk, gv, gb, gg, None, gdo, workspace=gws)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        gb_us = ev0.elapsed_time(ev1) * 1e3 / greps
+        gbytes = chunk_bwd_bytes(bb * T, Hqk, Hv, D, gated=True, N=bb, init=False, dfinal=False)
+        gflops = chunk_bwd_flops(bb * T, Hv, D, 64)
+        chunk_backward[f"B{bb}"] = {
+            "workload": f"B{bb} H{Hv} T{T} d{D} bf16, g = -0.1 softplus(z), zero initial state",
+            "kernels": "fused_kernel<true, false, true> (chunk-start states) + "
+                       "chunk_bwd_kernel<true> + bwd_chunk_sum_kernel",
+            "us_per_call": gb_us, "tokens_per_s": bb * T / (gb_us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": gbytes / (gb_us * 1e-6) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbytes / (gb_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes": gbytes,
+                         "traffic": load_traffic(f"chunk_bwd_B{bb}_bytes_per_call")},
+            "mfma": {"algorithmic_flops": gflops, "tflops": gflops / (gb_us * 1e-6) / 1e12,
+                     "frac_of_bf16_peak": gflops / (gb_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+        }
+        del gq, gk, gv, gb, gg, gdo, gws
+
     # ------------ the short causal conv (+ silu) in front of the rule: prompt and decode
     crng = np.random.default_rng(3)
     Cc = 3 * Hv * D
@@ -599,6 +660,7 @@ def main():
         "channel_gates": channel_gates,
         "readout_epilogue": epilogue,
         "recurrent_route": recurrent,
+        "chunk_backward": chunk_backward,
         "causal_conv": conv,
         "cpu_baseline": None,
     }

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["chunk_fwd", "chunk_fwd_path", "chunk_bwd", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv",
-           "causal_conv_step", "workspace_bytes", "lib_path", "load_library",
+           "causal_conv_step", "workspace_bytes", "chunk_bwd_workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
 
@@ -174,6 +174,15 @@ def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: 
                DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0)
     s.flags = DN_GATE_PER_KEY if g_per_key else 0
     return int(load_library().dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
+
+
+def chunk_bwd_workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int,
+                              dtype: torch.dtype, num_seqs: Optional[int] = None) -> int:
+    """Device workspace (bytes) ``dn_chunk_bwd`` needs for these sizes (0 where the reverse
+    pass does not support them)."""
+    s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
+               DN_BF16 if dtype == torch.bfloat16 else DN_F32, 64, 1.0)
+    return int(load_library().dn_chunk_bwd_workspace_bytes(ctypes.byref(s)))
 
 
 _PATHS = {-1: "invalid", 0: "fused", 1: "channel_gate_two_kernels", 2: "channel_gate_one_kernel",

@@ -88,3 +88,19 @@ def test_traffic_is_used_only_for_the_sources_it_was_measured_on(tmp_path, monke
     assert blk["roofline"]["traffic"] == 1
     assert abs(blk["roofline"]["frac"] - 138_936_320 / 50e-6 / 1e9 / 8000) < 1e-12
     assert blk["mfma"]["algorithmic_flops"] == 18_253_611_008
+
+
+def test_chunk_bwd_bytes_and_flops():
+    """The reverse pass's algorithmic bytes and flops, written out per term for the gated
+    B1 H16 T2048 d128 shape: bf16 q, k, v, dL/do in; fp32 beta, g in; fp32 dq, dk, dv,
+    dbeta, dg out; 401,408 flop per token-head."""
+    tok, h, d = 2048, 16, 128
+    reads = tok * h * d * 2 * 4 + tok * h * 4 * 2
+    writes = tok * h * d * 4 * 3 + tok * h * 4 * 2
+    assert bench.chunk_bwd_bytes(tok, h, h, d, gated=True, N=1, init=False, dfinal=False) == reads + writes
+    assert bench.chunk_bwd_bytes(tok, h, h, d, gated=True, N=1, init=True, dfinal=True) == \
+        reads + writes + 3 * h * d * d * 4
+    assert bench.chunk_bwd_bytes(tok, h, h, d, gated=False, N=1, init=False, dfinal=False) == \
+        reads + writes - 2 * tok * h * 4
+    assert bench.chunk_bwd_flops(1, 1, 128, 64) == 401_408
+    assert bench.chunk_bwd_flops(tok, h, d, 64) == tok * h * 401_408
