@@ -28,19 +28,26 @@
 //   and on the chunk's last row + exp(gamma_L) <M, dM'> + sum_r c_r;
 //   dg_i = sum of dgamma_r over the rows r >= i of the chunk.
 //
-// Every product contracting over the value columns is linear in them, so the pass splits
-// the state's columns into 32-column slices like the forward: one workgroup of eight waves
-// per (sequence, value head, slice) walks the chunks backwards from the chunk-start states
-// the forward kernel saved, carries its columns of dM in MFMA accumulators, writes dV and
-// the initial state's gradient directly, and writes its share of dQ, dK, dbeta and dgamma
-// per (chunk, row) to the workspace; bwd_chunk_sum_kernel adds the shares over the slices
-// (and over the value heads of a q/k head) in a fixed order and sums dgamma into dg.
+// Only the carry dM runs across chunks, and it needs just T, P and the chunk's inputs; the
+// rest is independent per chunk once M and dM' are known.  Four launches:
+//   1. the prompt kernel writes the state at every chunk start (outputs skipped);
+//   2. chunk_tp_kernel, one workgroup per (chunk, value head): T^T and P to the workspace;
+//   3. chunk_carry_kernel, one workgroup per (sequence, value head, 32-column slice): the
+//      chunks backwards, dM' kept in MFMA accumulators and written out at every chunk (the
+//      last one is the initial state's gradient);
+//   4. chunk_grad_kernel, one workgroup per (chunk, q/k head): every gradient of the chunk,
+//      over the value heads of the q/k head and the four column slices, with dA, dP and the
+//      dq, dk terms accumulated in registers, so dq and dk are written once, in a fixed
+//      order, without atomics.  Three row dot products come out of accumulators already
+//      formed: (Q M)_r . dO_r = Q_r . (dO M^T)_r, X_r . dR_r = K_r . (dR M^T)_r and
+//      (K dM')_r . Delta_r = K_r . (Delta dM'^T)_r.
 //
-// Each chunk takes ten steps separated by workgroup barriers; a step's output tiles are
-// dealt to the waves.  Operands live in LDS as bf16, row-major: a "row" fragment (lane =
-// row of the stored matrix) is one 16-byte read, a "column" fragment (lane = column) two
-// transposed 8-byte reads (ds_read_b64_tr_b16).  The next chunk's inputs are fetched into
-// registers while the current one is worked.
+// Operands live in LDS as bf16: a "row" fragment (lane = row of the stored matrix) is one
+// 16-byte read, a "column" fragment (lane = column) two transposed 8-byte reads
+// (ds_read_b64_tr_b16).  Products whose consumer reads them by rows of their transpose are
+// stored transposed, four values of a lane in one 8-byte write.
+#include <mutex>
+
 #include "internal.h"
 #include "mfma_ops.h"
 
@@ -49,31 +56,13 @@ namespace {
 
 constexpr int BC = 64;             // chunk
 constexpr int BD = 128;            // Dk = Dv
-constexpr int BS = 32;             // state columns per workgroup
+constexpr int BS = 32;             // state columns per slice
 constexpr int BNS = BD / BS;       // slices
-constexpr int NTB = 512;           // threads (8 waves)
 constexpr int P128 = BD + 16;      // bf16 pitches (16-byte reads of 16 rows conflict-free)
 constexpr int P64 = BC + 16;
 constexpr int P32 = BS + 16;
 constexpr int ADP = 136;           // A's diagonal 16x16 blocks, 120 packed fp16 entries + spare
-constexpr int NDB = 8;             // dbeta partial slots per row
-constexpr int NDG = 48;            // dgamma partial slots per row
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-struct alignas(16) BwdSmem {
-    __bf16 K[BC][P128], Q[BC][P128];
-    __bf16 V[BC][P32], dO[BC][P32], R[BC][P32], Dl[BC][P32], dDl[BC][P32], dR[BC][P32];
-    __bf16 M[BD][P32];             // the slice of the state at the chunk start
-    __bf16 dM[BD][P32];            // the slice of dM' (the gradient of the state after the chunk)
-    __bf16 Tt[BC][P64];            // T^T, T = (I + A)^-1 lower triangular
-    __bf16 P[BC][P64];             // P, then Z = dP o D
-    __bf16 G[BC][P64];             // D o K K^T (strictly lower), then W = dA o diag(beta) D
-    _Float16 Ad[4][ADP];           // A's diagonal blocks (strictly lower, packed by rows)
-    float X[BC][BS];               // X = K M (fp32, for the dbeta and dgamma terms)
-    float beta[BC], gam[BC], eg[BC], tail[BC];
-    float pb[BC][NDB], pg[BC][NDG];   // per-row partial sums (fixed slots, summed in order)
-    float mdm[8];                  // <M, dM'> per wave
-};
 
 // --------------------------------------------------------------------- fragments
 __device__ __forceinline__ bf16x8 frag_r(const __bf16* S, int pitch, int r0, int k0, int l16, int q16) {
@@ -92,6 +81,10 @@ __device__ __forceinline__ bf16x8 scale_r(bf16x8 x, float f) {
 __device__ __forceinline__ void put_tile(__bf16* S, int pitch, int i, int j, const f32x4& c, int l16, int q16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) S[(16 * i + 4 * q16 + e) * pitch + 16 * j + l16] = (__bf16)c[e];
+}
+// the same tile transposed (S[16 j + l16][16 i + 4 q16 + e]): one 8-byte write per lane
+__device__ __forceinline__ void put_tile_t(__bf16* S, int pitch, int i, int j, const f32x4& c, int l16, int q16) {
+    st4(S + (16 * j + l16) * pitch + 16 * i + 4 * q16, c[0], c[1], c[2], c[3]);
 }
 // DPP lane moves within rows of 16 lanes (every lane has a source)
 template <int CTRL>
@@ -112,6 +105,46 @@ __device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
     }
     return v;
 }
+// x as a value the compiler cannot see through: addresses derived from it are computed where
+// they are used instead of being hoisted out of loops and held in registers
+__device__ __forceinline__ int fresh(int x) {
+    __asm__ volatile("" : "+v"(x));
+    return x;
+}
+// sum over the wave, the same value in every lane: the four 16-lane row sums, read out and
+// added in row order
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp16<0xB1>(x);
+    x += dpp16<0x4E>(x);
+    x += dpp16<0x141>(x);
+    x += dpp16<0x140>(x);
+    const int b = __builtin_bit_cast(int, x);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+// x moved by a DPP control; lanes with no source (or rows outside row_mask) get 0
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or0(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+// gamma: inclusive scan of g over a chunk on one wave (lane = row), by DPP: shifts right by
+// 1, 2, 4, 8 lanes within each 16-lane row, then lane 15 of each row added into the next row
+// and lane 31 into the upper two rows; gl = gamma of row 63
+__device__ __forceinline__ float gamma_scan(float g, float& gl) {
+    g += dpp_or0<0x111, 0xf>(g);   // row_shr:1
+    g += dpp_or0<0x112, 0xf>(g);   // row_shr:2
+    g += dpp_or0<0x114, 0xf>(g);   // row_shr:4
+    g += dpp_or0<0x118, 0xf>(g);   // row_shr:8
+    g += dpp_or0<0x142, 0xa>(g);   // row_bcast:15 into rows 1 and 3
+    g += dpp_or0<0x143, 0xc>(g);   // row_bcast:31 into rows 2 and 3
+    gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 63));
+    return g;
+}
+// lower tile u < 10 of a 64 x 64 matrix in 16 x 16 blocks: (ri, ci), ci <= ri
+__device__ __forceinline__ void lower_tile(int u, int& ri, int& ci) {
+    ri = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
+    ci = u - ri * (ri + 1) / 2;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -125,19 +158,202 @@ __device__ __forceinline__ float ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
-// One chunk's inputs in registers: thread t holds 16-byte pieces t and t + 512 of K and Q
-// (row = piece / 16), piece t & 255 of V (t < 256) or dO (t >= 256) (row = piece / 4),
-// pieces t and t + 512 of the state slice (128 rows x 8 float4), beta and g of token t (t < 64).
-struct BwdIn {
-    uint4 k[2], q[2], vo;
-    float4 m[2];
+// chunk number cid -> sequence n, chunk c of it, the sequence's first token and length;
+// false for a number no chunk uses
+__device__ __forceinline__ bool chunk_of_id(const ChunkBwdArgs& a, long cid, int& n, long& c, long& bos, long& L) {
+    if (a.cu) {   // the last sequence whose first chunk number is <= cid (strictly increasing)
+        int lo = 0, hi = a.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (chunk_id_base(a, mid) <= cid) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+    } else {
+        n = (int)(cid / ((a.T + BC - 1) / BC));
+    }
+    long eos;
+    seq_range(a.cu, n, a.T, bos, eos);
+    L = eos - bos;
+    c = cid - chunk_id_base(a, n);
+    return c * BC < L;
+}
+
+// ======================================================= 2. T^T and P per (chunk, head)
+constexpr int NTP = 256;
+
+struct alignas(16) PrepSmem {
+    __bf16 K[BC][P128], Q[BC][P128];
+    __bf16 Tt[BC][P64];            // T^T, T = (I + A)^-1 lower triangular
+    __bf16 P[BC][P64];             // P = lower(D o Q K^T)
+    __bf16 G[BC][P64];             // D o K K^T, strictly lower
+    _Float16 Ad[4][ADP];           // A's diagonal blocks (strictly lower, packed by rows)
+    float beta[BC], gam[BC];
+};
+
+__global__ __launch_bounds__(NTP, 2) void chunk_tp_kernel(ChunkBwdArgs a) {
+    __shared__ PrepSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q16 = lane >> 4;
+    const int h = (int)(blockIdx.x % a.Hv);
+    const long cid = blockIdx.x / a.Hv;
+    int n;
+    long c, bos, L;
+    if (!chunk_of_id(a, cid, n, c, bos, L)) return;
+    const int hq = h / (a.Hv / a.Hqk);
+    const long t0 = bos + c * BC;
+    const int rows = (int)min((long)BC, L - c * BC);
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+
+    for (int pc = tid; pc < BC * 16; pc += NTP) {   // K and Q, rows past the end zero
+        const int row = pc >> 4, cg = pc & 15;
+        uint4 kv = z4, qv = z4;
+        if (row < rows) {
+            const long off = ((t0 + row) * a.Hqk + hq) * BD + cg * 8;
+            kv = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.k) + off);
+            qv = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.q) + off);
+        }
+        *reinterpret_cast<uint4*>(&sm.K[row][cg * 8]) = kv;
+        *reinterpret_cast<uint4*>(&sm.Q[row][cg * 8]) = qv;
+    }
+    // the blocks above the diagonal of P and G, and below it of T^T, stay zero
+    for (int i = tid; i < BC * P64 / 8; i += NTP) {
+        reinterpret_cast<uint4*>(&sm.Tt[0][0])[i] = z4;
+        reinterpret_cast<uint4*>(&sm.P[0][0])[i] = z4;
+        reinterpret_cast<uint4*>(&sm.G[0][0])[i] = z4;
+    }
+    if (wave == 0) {
+        const bool ok = lane < rows;
+        const long s = (t0 + lane) * a.Hv + h;
+        float gl;
+        sm.gam[lane] = gamma_scan(ok && a.g ? a.g[s] : 0.f, gl);
+        sm.beta[lane] = ok ? a.beta[s] : 0.f;
+    }
+    __syncthreads();
+
+    // 20 lower tiles (incl. the diagonal): t < 10 of D o K K^T (strictly lower), t >= 10 of P
+    for (int t = wave; t < 20; t += NTP / 64) {
+        int ri, ci;
+        lower_tile(t % 10, ri, ci);
+        const __bf16* A = t < 10 ? &sm.K[0][0] : &sm.Q[0][0];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < BD; k0 += 32)
+            acc = mma16(frag_r(A, P128, 16 * ri, k0, l16, q16), frag_r(&sm.K[0][0], P128, 16 * ci, k0, l16, q16), acc);
+        const int col = 16 * ci + l16;
+        const float gc = sm.gam[col];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * ri + 4 * q16 + e;
+            const bool keep = t < 10 ? col < row : col <= row;
+            acc[e] = keep ? __expf(fminf(sm.gam[row] - gc, 0.f)) * acc[e] : 0.f;
+        }
+        put_tile(t < 10 ? &sm.G[0][0] : &sm.P[0][0], P64, ri, ci, acc, l16, q16);
+        if (t < 10 && ri == ci) {   // A's diagonal block ri in fp16, strictly lower, packed
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int lr = 4 * q16 + e, lc = l16;
+                if (lc < lr) sm.Ad[ri][lr * (lr - 1) / 2 + lc] = (_Float16)(sm.beta[16 * ri + lr] * acc[e]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1 on wave 0, stored transposed
+    if (wave == 0) {
+        __bf16 (*Tt)[P64] = sm.Tt;
+        {   // the four 16x16 diagonal blocks by forward substitution (lane = block, column):
+            // column cc of T_bb is row cc of T^T_bb, written as two 16-byte pieces
+            const int b = q16, cc = l16;
+            f16x8 ap[15];
+#pragma unroll
+            for (int g = 0; g < 15; ++g) ap[g] = *reinterpret_cast<const f16x8*>(&sm.Ad[b][8 * g]);
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = r == cc ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 15; ++m)
+#pragma unroll
+                for (int r = m + 1; r < 16; ++r) {
+                    const int idx = r * (r - 1) / 2 + m;
+                    x[r] = __builtin_fmaf(-(float)ap[idx >> 3][idx & 7], x[m], x[r]);
+                }
+            bf16x8 lo8, hi8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lo8[e] = (__bf16)x[e];
+                hi8[e] = (__bf16)x[8 + e];
+            }
+            *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b]) = lo8;
+            *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b + 8]) = hi8;
+        }
+        wave_lds_order();
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const bool lo = q16 < 2;   // k = 16 padded to the instruction's 32
+        // level 1: T21 = -T22 (A21 T11) within each 32x32 diagonal block (base 0, 32);
+        // T's block (b + 1, b) is T^T's block (b, b + 1)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const int base = 32 * hb;
+            const bf16x8 af = lo ? scale_r(frag_r(&sm.G[0][0], P64, base + 16, base, l16, q16),
+                                           sm.beta[base + 16 + l16]) : zero8();
+            const bf16x8 bf = lo ? frag_r(&Tt[0][0], P64, base, base, l16, q16) : zero8();
+            const f32x4 X1 = mma16(af, bf, z);
+            const bf16x8 tf = lo ? frag_c(&Tt[0][0], P64, base + 16, base + 16, l16, q16) : zero8();
+            const f32x4 Y1 = mma16(tf, acc_to_b(X1, z), z);
+            st4(&Tt[base + l16][base + 16 + 4 * q16], -Y1[0], -Y1[1], -Y1[2], -Y1[3]);
+        }
+        wave_lds_order();
+        // level 2: T_BL = -T_BR (A_BL T_TL), 32 x 32 blocks
+        f32x4 X2[2][2];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj)
+                X2[ti][tj] = mma16(scale_r(frag_r(&sm.G[0][0], P64, 32 + 16 * ti, 0, l16, q16), sm.beta[32 + 16 * ti + l16]),
+                                   frag_r(&Tt[0][0], P64, 16 * tj, 0, l16, q16), z);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj) {
+                const f32x4 Y2 = mma16(frag_c(&Tt[0][0], P64, 32 + 16 * ti, 32, l16, q16),
+                                       acc_to_b(X2[0][tj], X2[1][tj]), z);
+                st4(&Tt[16 * tj + l16][32 + 16 * ti + 4 * q16], -Y2[0], -Y2[1], -Y2[2], -Y2[3]);
+            }
+    }
+    __syncthreads();
+
+    __bf16* out = static_cast<__bf16*>(a.tp) + (cid * a.Hv + h) * (2L * BC * BC);
+    for (int pc = tid; pc < 2 * BC * 8; pc += NTP) {
+        const int m = pc >> 9, r = (pc >> 3) & 63, cg = pc & 7;
+        const __bf16* src = m ? &sm.P[r][cg * 8] : &sm.Tt[r][cg * 8];
+        *reinterpret_cast<uint4*>(out + m * BC * BC + r * BC + cg * 8) = *reinterpret_cast<const uint4*>(src);
+    }
+}
+
+// ============================================ 3. the carry dM per (sequence, head, slice)
+constexpr int NTB = 512;           // 8 waves
+
+struct alignas(16) CarrySmem {
+    __bf16 K[2][BC][P128], Q[2][BC][P128];    // two chunks: the current one and the next
+    __bf16 dO[2][BC][P32];
+    __bf16 Tt[2][BC][P64], P[2][BC][P64];
+    __bf16 dDt[BS][P64];           // dDelta^T
+    __bf16 dXt[BS][P64];           // dX^T
+    __bf16 dM[BD][P32];            // the slice of dM' (the gradient of the state after the chunk)
+    float tail[2][BC], sod[2][BC], bx[2][BC], egl[2][4];
+};
+
+// one chunk's inputs in registers: thread t holds 16-byte pieces t and t + 512 of K and Q
+// (row = piece / 16), piece t of dO's slice (t < 256, row = piece / 4), piece t of T^T and
+// of P (row = piece / 8), beta and g of token t (t < 64)
+struct CarryIn {
+    uint4 k[2], q[2], o, t, p;
     float beta, g;
 };
 
-template <bool GATED>
-__global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
-    __shared__ BwdSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
+    __shared__ CarrySmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q16 = lane >> 4;
     const int slice = blockIdx.x % BNS;
     const int nh = blockIdx.x / BNS;
@@ -159,34 +375,53 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
     const uint32_t s_end = L > 0 ? (uint32_t)((L - 1) * s_tok + 4) : 0;
     const auto k_rs = rsrc(static_cast<const __bf16*>(a.k) + kq0, kq_end);
     const auto q_rs = rsrc(static_cast<const __bf16*>(a.q) + kq0, kq_end);
-    const auto v_rs = rsrc(static_cast<const __bf16*>(a.v) + v0, v_end);
     const auto o_rs = rsrc(static_cast<const __bf16*>(a.dout) + v0, v_end);
     const auto b_rs = rsrc(a.beta + s0, s_end);
     const auto g_rs = rsrc(a.g ? a.g + s0 : a.beta + s0, a.g ? s_end : 0);
-    uint32_t kq_off[2], m_off[2];
+    uint32_t kq_off[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int pc = tid + NTB * u;
         kq_off[u] = (uint32_t)(pc >> 4) * kq_tok + (pc & 15) * 16;
-        m_off[u] = (uint32_t)((pc >> 3) * BD + (pc & 7) * 4);   // floats within the head's state
     }
-    const int vp = tid & 255;
-    const uint32_t vo_off = (uint32_t)(vp >> 2) * v_tok + (vp & 3) * 16;
-    const uint32_t sc_off = (uint32_t)(tid & 63) * s_tok;
+    const int op = tid & 255;
+    const uint32_t o_off = (uint32_t)(op >> 2) * v_tok + (op & 3) * 16;
+    const uint32_t sc_off = (uint32_t)lane * s_tok;
+    const uint4* tp_head = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.tp)) + tid;
 
-    auto fetch = [&](int c, BwdIn& f) {
+    auto fetch = [&](int c, CarryIn& f) {
         const uint32_t ck = (uint32_t)c * BC * kq_tok, cv = (uint32_t)c * BC * v_tok, cs = (uint32_t)c * BC * s_tok;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f.k[u] = ld128(k_rs, kq_off[u], ck);
             f.q[u] = ld128(q_rs, kq_off[u], ck);
         }
-        f.vo = ld128(tid < 256 ? v_rs : o_rs, vo_off, cv);
-        const float* st = a.states + ((cid0 + c) * a.Hv + h) * (long)BD * BD + j0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) f.m[u] = *reinterpret_cast<const float4*>(st + m_off[u]);
+        f.o = ld128(o_rs, o_off, cv);
+        const uint4* tp = tp_head + ((cid0 + c) * a.Hv + h) * (2L * BC * BC / 8);
+        f.t = tp[0];
+        f.p = tp[BC * BC / 8];
         f.beta = ld32(b_rs, sc_off, cs);
         f.g = ld32(g_rs, sc_off, cs);
+    };
+    auto put_in = [&](const CarryIn& f, int b) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pc = tid + NTB * u, row = pc >> 4, cg = pc & 15;
+            *reinterpret_cast<uint4*>(&sm.K[b][row][cg * 8]) = f.k[u];
+            *reinterpret_cast<uint4*>(&sm.Q[b][row][cg * 8]) = f.q[u];
+        }
+        if (tid < 256) *reinterpret_cast<uint4*>(&sm.dO[b][op >> 2][(op & 3) * 8]) = f.o;
+        *reinterpret_cast<uint4*>(&sm.Tt[b][tid >> 3][(tid & 7) * 8]) = f.t;
+        *reinterpret_cast<uint4*>(&sm.P[b][tid >> 3][(tid & 7) * 8]) = f.p;
+        if (wave == 0) {
+            float gl;
+            const float gv = gamma_scan(a.g ? f.g : 0.f, gl);
+            const float eg = __expf(gv);
+            sm.tail[b][lane] = __expf(gl - gv);
+            sm.sod[b][lane] = sc * eg;
+            sm.bx[b][lane] = -f.beta * eg;
+            if (lane == 0) sm.egl[b][0] = __expf(gl);
+        }
     };
 
     // dM' of this slice in MFMA accumulators: wave w holds tiles (key block 2 (w >> 1) + u,
@@ -204,413 +439,84 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) put_tile(&sm.dM[0][0], P32, 2 * (wave >> 1) + u, dmj, dm[u], l16, q16);
     };
+
+    CarryIn f;
     put_dm();
-
-    // P and G (later Z and W) are written below their 16-block diagonal only, T^T above
-    // it; the products that read them by 32-row blocks also read the other tiles, zero
-    for (int i = tid; i < BC * P64; i += NTB) {
-        (&sm.P[0][0])[i] = (__bf16)0.f;
-        (&sm.G[0][0])[i] = (__bf16)0.f;
-        (&sm.Tt[0][0])[i] = (__bf16)0.f;   // T's blocks above the diagonal stay zero
+    if (nc > 0) {
+        fetch(nc - 1, f);
+        put_in(f, (nc - 1) & 1);
+        if (nc > 1) fetch(nc - 2, f);
     }
-
-    BwdIn cur, nxt;
-    if (nc > 0) fetch(nc - 1, cur);
+    __syncthreads();
+    const int ti = wave >> 1, tj = wave & 1;   // this wave's 16 x 16 tile of a 64 x 32 product
     for (int c = nc - 1; c >= 0; --c) {
-        // -------------------------------------------------------- B0: inputs to LDS
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int pc = tid + NTB * u, row = pc >> 4, cg = pc & 15;
-            *reinterpret_cast<uint4*>(&sm.K[row][cg * 8]) = cur.k[u];
-            *reinterpret_cast<uint4*>(&sm.Q[row][cg * 8]) = cur.q[u];
-            const int mr = pc >> 3, mc = (pc & 7) * 4;
-            *reinterpret_cast<uint2*>(&sm.M[mr][mc]) =
-                make_uint2(pack_bf16x2(cur.m[u].x, cur.m[u].y), pack_bf16x2(cur.m[u].z, cur.m[u].w));
-        }
-        *reinterpret_cast<uint4*>(tid < 256 ? &sm.V[vp >> 2][(vp & 3) * 8] : &sm.dO[vp >> 2][(vp & 3) * 8]) = cur.vo;
-        for (int i = tid; i < BC * NDB; i += NTB) (&sm.pb[0][0])[i] = 0.f;
-        for (int i = tid; i < BC * NDG; i += NTB) (&sm.pg[0][0])[i] = 0.f;
-        if (wave == 0) {
-            // gamma: inclusive scan of g over the chunk (rows past the end carry g = 0)
-            float gv = GATED ? cur.g : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(gv, off);
-                if (lane >= off) gv += o;
-            }
-            const float gl = __shfl(gv, 63);
-            sm.beta[lane] = cur.beta;
-            sm.gam[lane] = gv;
-            sm.eg[lane] = __expf(gv);
-            sm.tail[lane] = __expf(gl - gv);
-        }
-        if (c > 0) fetch(c - 1, nxt);
-        __syncthreads();
-
-        // ------------------------------------------ B1: D o K K^T, P = D o Q K^T, Ad
-        // 20 lower tiles (incl. the diagonal): t < 10 of G, t >= 10 of P; tile (ri, ci)
-        // of rows 16 ri + 4 q16 + e, columns 16 ci + l16, ci <= ri
-        for (int t = wave; t < 20; t += 8) {
-            const int u = t % 10;
-            const int ri = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
-            const int ci = u - ri * (ri + 1) / 2;
-            const __bf16* A = t < 10 ? &sm.K[0][0] : &sm.Q[0][0];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BD; k0 += 32)
-                acc = mma16(frag_r(A, P128, 16 * ri, k0, l16, q16), frag_r(&sm.K[0][0], P128, 16 * ci, k0, l16, q16), acc);
-            const int col = 16 * ci + l16;
-            const float gc = sm.gam[col];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * ri + 4 * q16 + e;
-                const bool keep = t < 10 ? col < row : col <= row;
-                const float d = GATED ? __expf(fminf(sm.gam[row] - gc, 0.f)) : 1.f;
-                acc[e] = keep ? d * acc[e] : 0.f;
-            }
-            put_tile(t < 10 ? &sm.G[0][0] : &sm.P[0][0], P64, ri, ci, acc, l16, q16);
-            if (t < 10 && ri == ci) {   // A's diagonal block ri in fp16, strictly lower, packed
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int lr = 4 * q16 + e, lc = l16;
-                    if (lc < lr) sm.Ad[ri][lr * (lr - 1) / 2 + lc] = (_Float16)(sm.beta[16 * ri + lr] * acc[e]);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ------------------------- B2: T (wave 0); X = K M, R (waves 1-4); Y = Q M (5-7)
-        if (wave == 0) {
-            __bf16 (*Tt)[P64] = sm.Tt;
-            {   // the four 16x16 diagonal blocks by forward substitution (lane = block, column):
-                // column cc of T_bb is row cc of T^T_bb, written as two 16-byte pieces
-                const int b = q16, cc = l16;
-                f16x8 ap[15];
-#pragma unroll
-                for (int g = 0; g < 15; ++g) ap[g] = *reinterpret_cast<const f16x8*>(&sm.Ad[b][8 * g]);
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = r == cc ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < 15; ++m)
-#pragma unroll
-                    for (int r = m + 1; r < 16; ++r) {
-                        const int idx = r * (r - 1) / 2 + m;
-                        x[r] = __builtin_fmaf(-(float)ap[idx >> 3][idx & 7], x[m], x[r]);
-                    }
-                bf16x8 lo8, hi8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    lo8[e] = (__bf16)x[e];
-                    hi8[e] = (__bf16)x[8 + e];
-                }
-                *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b]) = lo8;
-                *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b + 8]) = hi8;
-            }
-            wave_lds_order();
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            const bool lo = q16 < 2;   // k = 16 padded to the instruction's 32
-            // level 1: T21 = -T22 (A21 T11) within each 32x32 diagonal block (base 0, 32);
-            // T's block (b + 1, b) is T^T's block (b, b + 1)
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const int base = 32 * hb;
-                const bf16x8 af = lo ? scale_r(frag_r(&sm.G[0][0], P64, base + 16, base, l16, q16),
-                                               sm.beta[base + 16 + l16]) : zero8();
-                const bf16x8 bf = lo ? frag_r(&Tt[0][0], P64, base, base, l16, q16) : zero8();
-                const f32x4 X1 = mma16(af, bf, z4);
-                const bf16x8 tf = lo ? frag_c(&Tt[0][0], P64, base + 16, base + 16, l16, q16) : zero8();
-                const f32x4 Y1 = mma16(tf, acc_to_b(X1, z4), z4);
-                st4(&Tt[base + l16][base + 16 + 4 * q16], -Y1[0], -Y1[1], -Y1[2], -Y1[3]);
-            }
-            wave_lds_order();
-            // level 2: T_BL = -T_BR (A_BL T_TL), 32 x 32 blocks
-            f32x4 X2[2][2];
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj)
-                    X2[ti][tj] = mma16(scale_r(frag_r(&sm.G[0][0], P64, 32 + 16 * ti, 0, l16, q16), sm.beta[32 + 16 * ti + l16]),
-                                       frag_r(&Tt[0][0], P64, 16 * tj, 0, l16, q16), z4);
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj) {
-                    const f32x4 Y2 = mma16(frag_c(&Tt[0][0], P64, 32 + 16 * ti, 32, l16, q16),
-                                           acc_to_b(X2[0][tj], X2[1][tj]), z4);
-                    st4(&Tt[16 * tj + l16][32 + 16 * ti + 4 * q16], -Y2[0], -Y2[1], -Y2[2], -Y2[3]);
-                }
-        } else {
-            // X tiles (i, j) on waves 1-4 (two each), Y tiles on waves 5-7
-            const bool isx = wave <= 4;
-            const int first = isx ? 2 * (wave - 1) : 3 * (wave - 5);
-            const int count = isx ? 2 : (wave == 7 ? 2 : 3);
-            for (int t = first; t < first + count && (isx || GATED); ++t) {
-                const int i = t >> 1, j = t & 1;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k0 = 0; k0 < BD; k0 += 32)
-                    acc = mma16(frag_r(isx ? &sm.K[0][0] : &sm.Q[0][0], P128, 16 * i, k0, l16, q16),
-                                frag_c(&sm.M[0][0], P32, 16 * j, k0, l16, q16), acc);
-                const int col = 16 * j + l16;
-                if (isx) {
-                    f32x4 r4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = 16 * i + 4 * q16 + e;
-                        sm.X[row][col] = acc[e];
-                        r4[e] = sm.beta[row] * ((float)sm.V[row][col] - sm.eg[row] * acc[e]);
-                    }
-                    put_tile(&sm.R[0][0], P32, i, j, r4, l16, q16);
-                } else {   // scale exp(gamma_r) (Q M)_r . dO_r, this tile's 16 columns
-                    f32x4 p;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = 16 * i + 4 * q16 + e;
-                        p[e] = acc[e] * (float)sm.dO[row][col];
-                    }
-                    p = row_sum16(p);
-                    if (l16 == 0) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int row = 16 * i + 4 * q16 + e;
-                            sm.pg[row][0 + j] = sc * sm.eg[row] * p[e];
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        // each wave owns one 64 x 32 tile (i, j) in the next steps
-        const int ti = wave >> 1, tj = wave & 1;
-        // ---------------------------------------------------------- B3: Delta = T R
-        {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 32)
-                if (k0 <= 16 * ti) acc = mma16(frag_c(&sm.Tt[0][0], P64, 16 * ti, k0, l16, q16),
-                                               frag_c(&sm.R[0][0], P32, 16 * tj, k0, l16, q16), acc);
-            put_tile(&sm.Dl[0][0], P32, ti, tj, acc, l16, q16);
-        }
-        __syncthreads();
-
-        // ------------------------------ B4: dDelta = scale P^T dO + diag(tail) K dM'; c_r
-        {
-            f32x4 pd = {0.f, 0.f, 0.f, 0.f}, kd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 32)
-                if (k0 + 32 > 16 * ti) pd = mma16(frag_c(&sm.P[0][0], P64, 16 * ti, k0, l16, q16),
-                                                  frag_c(&sm.dO[0][0], P32, 16 * tj, k0, l16, q16), pd);
-#pragma unroll
-            for (int k0 = 0; k0 < BD; k0 += 32)
-                kd = mma16(frag_r(&sm.K[0][0], P128, 16 * ti, k0, l16, q16), frag_c(&sm.dM[0][0], P32, 16 * tj, k0, l16, q16), kd);
-            f32x4 dd, cr;
-            const int col = 16 * tj + l16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * ti + 4 * q16 + e;
-                const float tk = sm.tail[row] * kd[e];
-                dd[e] = sc * pd[e] + tk;
-                cr[e] = -tk * (float)sm.Dl[row][col];   // -c_r (this tile's columns)
-            }
-            put_tile(&sm.dDl[0][0], P32, ti, tj, dd, l16, q16);
-            if (GATED) {
-                cr = row_sum16(cr);
-                if (l16 == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sm.pg[16 * ti + 4 * q16 + e][44 + tj] = cr[e];
-                }
-            }
-        }
-        __syncthreads();
-
-        // ------------------------------------------- B5: dR = T^T dDelta; dV; row terms
-        {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 32)
-                if (k0 + 32 > 16 * ti) acc = mma16(frag_r(&sm.Tt[0][0], P64, 16 * ti, k0, l16, q16),
-                                                   frag_c(&sm.dDl[0][0], P32, 16 * tj, k0, l16, q16), acc);
-            put_tile(&sm.dR[0][0], P32, ti, tj, acc, l16, q16);
-            const int col = 16 * tj + l16;
-            f32x4 rb, xg;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * ti + 4 * q16 + e;
-                const float x = sm.X[row][col];
-                rb[e] = ((float)sm.V[row][col] - sm.eg[row] * x) * acc[e];   // (V - e^gamma X) . dR
-                xg[e] = x * acc[e];                                            // X . dR
-                const long tok = (long)c * BC + row;
-                if (tok < L) a.dv[((bos + tok) * a.Hv + h) * BD + j0 + col] = sm.beta[row] * acc[e];
-            }
-            rb = row_sum16(rb);
-            xg = row_sum16(xg);
-            if (l16 == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * ti + 4 * q16 + e;
-                    sm.pb[row][tj] = rb[e];
-                    sm.pg[row][2 + tj] = -sm.beta[row] * sm.eg[row] * xg[e];
-                }
-            }
-        }
-        __syncthreads();
-
-        // ------------------------------------------ B6: dA -> W, dP -> Z; <M, dM'>
-        // 20 lower tiles (incl. the diagonal): t < 10 of dA = -dR Delta^T, t >= 10 of
-        // dP = scale dO Delta^T; k = the 32 slice columns
-        for (int t = wave; t < 20; t += 8) {
-            const int u = t % 10;
-            const int ri = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
-            const int ci = u - ri * (ri + 1) / 2;
-            const bool isa = t < 10;
-            f32x4 d = mma16(frag_r(isa ? &sm.dR[0][0] : &sm.dO[0][0], P32, 16 * ri, 0, l16, q16),
-                            frag_r(&sm.Dl[0][0], P32, 16 * ci, 0, l16, q16), f32x4{0.f, 0.f, 0.f, 0.f});
-            __bf16* S = isa ? &sm.G[0][0] : &sm.P[0][0];
-            const int col = 16 * ci + l16;
-            const float gc = sm.gam[col];
-            f32x4 rs, cs4, bsum;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * ri + 4 * q16 + e;
-                const bool keep = isa ? col < row : col <= row;
-                const float dv = keep ? (isa ? -d[e] : sc * d[e]) : 0.f;
-                const float s = (float)S[row * P64 + col];   // D o K K^T, or P
-                const float dec = GATED ? __expf(fminf(sm.gam[row] - gc, 0.f)) : 1.f;
-                const float f = isa ? sm.beta[row] : 1.f;
-                rs[e] = dv * f * s;          // dA o A (A = beta G) or dP o P
-                cs4[e] = rs[e];
-                bsum[e] = dv * s;            // dA o G (the dbeta term)
-                S[row * P64 + col] = (__bf16)(keep ? dv * f * dec : 0.f);   // W or Z
-            }
-            const f32x4 r16 = row_sum16(rs);
-            const float c4 = cs4[0] + cs4[1] + cs4[2] + cs4[3];   // this lane's 4 rows of the column
-            if (isa) {
-                const f32x4 b16 = row_sum16(bsum);
-                if (l16 == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sm.pb[16 * ri + 4 * q16 + e][2 + ci] = b16[e];
-                }
-            }
-            if (GATED) {
-                if (l16 == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sm.pg[16 * ri + 4 * q16 + e][(isa ? 4 : 24) + ci] = r16[e];
-                }
-                sm.pg[col][(isa ? 8 : 28) + 4 * ri + q16] = -c4;
-            }
-        }
-        if (GATED) {   // <M, dM'> over this wave's two dM' tiles
-            float s = 0.f;
+        const int b = c & 1;
+        {   // dM' of chunk c to the workspace (the gradient kernel's input)
+            const auto ds_rs = rsrc(a.dstates + ((cid0 + c) * a.Hv + h) * (long)BD * BD, BD * BD * 4);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int ki = 2 * (wave >> 1) + u;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s += (float)sm.M[16 * ki + 4 * q16 + e][16 * dmj + l16] * dm[u][e];
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dm[u][e]), ds_rs,
+                                                          ((16 * ki + 4 * q16 + e) * BD + j0 + 16 * dmj + l16) * 4, 0, 0);
             }
+        }
+        // ---------------------------- dDelta = scale P^T dO + diag(tail) K dM', stored transposed
+        {
+            f32x4 pd = {0.f, 0.f, 0.f, 0.f}, kd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
-            if (lane == 0) sm.mdm[wave] = s;
+            for (int k0 = 0; k0 < BC; k0 += 32)
+                if (k0 + 32 > 16 * ti) pd = mma16(frag_c(&sm.P[b][0][0], P64, 16 * ti, k0, l16, q16),
+                                                  frag_c(&sm.dO[b][0][0], P32, 16 * tj, k0, l16, q16), pd);
+#pragma unroll
+            for (int k0 = 0; k0 < BD; k0 += 32)
+                kd = mma16(frag_r(&sm.K[b][0][0], P128, 16 * ti, k0, l16, q16), frag_c(&sm.dM[0][0], P32, 16 * tj, k0, l16, q16), kd);
+            f32x4 dd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dd[e] = sc * pd[e] + sm.tail[b][16 * ti + 4 * q16 + e] * kd[e];
+            put_tile_t(&sm.dDt[0][0], P64, ti, tj, dd, l16, q16);
         }
         __syncthreads();
-
-        // --------------------------------------------------- B7: dQ and dK shares
+        // ------------------------------ dX = -diag(beta e^gamma) T^T dDelta, stored transposed
         {
-            const long ws_row = ((long)(slice * a.ncid + cid0 + c) * a.Hv + h) * BC;
-            float* wq = a.ws_dq + ws_row * BD;
-            float* wk = a.ws_dk + ws_row * BD;
-#pragma unroll 1
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const int t = wave + 8 * t4;   // tile (i, j) of the 64 x 128 output
-                const int i = t >> 3, j = t & 7;
-                // dQ = scale diag(e^gamma) dO M^T + Z K
-                f32x4 qa = mma16(frag_r(&sm.dO[0][0], P32, 16 * i, 0, l16, q16), frag_r(&sm.M[0][0], P32, 16 * j, 0, l16, q16),
-                                 f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qa[e] *= sc * sm.eg[16 * i + 4 * q16 + e];
+            for (int k0 = 0; k0 < BC; k0 += 32)
+                if (k0 + 32 > 16 * ti) acc = mma16(frag_r(&sm.Tt[b][0][0], P64, 16 * ti, k0, l16, q16),
+                                                   frag_r(&sm.dDt[0][0], P64, 16 * tj, k0, l16, q16), acc);
 #pragma unroll
-                for (int k0 = 0; k0 < BC; k0 += 32)
-                    if (k0 <= 16 * i) qa = mma16(frag_r(&sm.P[0][0], P64, 16 * i, k0, l16, q16),
-                                                 frag_c(&sm.K[0][0], P128, 16 * j, k0, l16, q16), qa);
-                // dK = -diag(beta e^gamma) dR M^T + diag(tail) Delta dM'^T + (W + W^T) K + Z^T Q
-                f32x4 k1 = mma16(frag_r(&sm.dR[0][0], P32, 16 * i, 0, l16, q16), frag_r(&sm.M[0][0], P32, 16 * j, 0, l16, q16),
-                                 f32x4{0.f, 0.f, 0.f, 0.f});
-                f32x4 k2 = mma16(frag_r(&sm.Dl[0][0], P32, 16 * i, 0, l16, q16), frag_r(&sm.dM[0][0], P32, 16 * j, 0, l16, q16),
-                                 f32x4{0.f, 0.f, 0.f, 0.f});
-                f32x4 ka;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * i + 4 * q16 + e;
-                    ka[e] = -sm.beta[row] * sm.eg[row] * k1[e] + sm.tail[row] * k2[e];
-                }
-#pragma unroll
-                for (int k0 = 0; k0 < BC; k0 += 32) {
-                    if (k0 <= 16 * i)   // W K (W strictly lower)
-                        ka = mma16(frag_r(&sm.G[0][0], P64, 16 * i, k0, l16, q16), frag_c(&sm.K[0][0], P128, 16 * j, k0, l16, q16), ka);
-                    if (k0 + 32 > 16 * i) {   // W^T K and Z^T Q (upper triangular factors)
-                        ka = mma16(frag_c(&sm.G[0][0], P64, 16 * i, k0, l16, q16), frag_c(&sm.K[0][0], P128, 16 * j, k0, l16, q16), ka);
-                        ka = mma16(frag_c(&sm.P[0][0], P64, 16 * i, k0, l16, q16), frag_c(&sm.Q[0][0], P128, 16 * j, k0, l16, q16), ka);
-                    }
-                }
-                // in the accumulator layout: tile t's 64 lanes x 4 entries, 1 KiB per tile
-                *reinterpret_cast<f32x4*>(wq + 256 * t + 4 * lane) = qa;
-                *reinterpret_cast<f32x4*>(wk + 256 * t + 4 * lane) = ka;
-            }
+            for (int e = 0; e < 4; ++e) acc[e] *= sm.bx[b][16 * ti + 4 * q16 + e];
+            put_tile_t(&sm.dXt[0][0], P64, ti, tj, acc, l16, q16);
         }
-        __syncthreads();   // the dM', M and Delta tiles are read above; dM' is replaced below
-
-        // ------------------- B8: dM' <- e^gamma_L dM' + scale Q^T diag(e^gamma) dO + K^T dX
+        __syncthreads();
+        // ------------------------- dM' <- e^gamma_L dM' + scale Q^T diag(e^gamma) dO + K^T dX
         {
-            const float gl = sm.eg[BC - 1];   // dX is not stored: dR's tokens are scaled as read
+            const float gl = sm.egl[b][0];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int ki = 2 * (wave >> 1) + u;
                 f32x4 acc = dm[u] * gl;
 #pragma unroll
                 for (int k0 = 0; k0 < BC; k0 += 32) {
-                    bf16x8 od = frag_c(&sm.dO[0][0], P32, 16 * dmj, k0, l16, q16);
-                    bf16x8 rd = frag_c(&sm.dR[0][0], P32, 16 * dmj, k0, l16, q16);
+                    bf16x8 od = frag_c(&sm.dO[b][0][0], P32, 16 * dmj, k0, l16, q16);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int tok = k0 + 8 * q16 + e;
-                        od[e] = (__bf16)((float)od[e] * sc * sm.eg[tok]);
-                        rd[e] = (__bf16)(-(float)rd[e] * sm.beta[tok] * sm.eg[tok]);
-                    }
-                    acc = mma16(frag_c(&sm.Q[0][0], P128, 16 * ki, k0, l16, q16), od, acc);
-                    acc = mma16(frag_c(&sm.K[0][0], P128, 16 * ki, k0, l16, q16), rd, acc);
+                    for (int e = 0; e < 8; ++e) od[e] = (__bf16)((float)od[e] * sm.sod[b][k0 + 8 * q16 + e]);
+                    acc = mma16(frag_c(&sm.Q[b][0][0], P128, 16 * ki, k0, l16, q16), od, acc);
+                    acc = mma16(frag_c(&sm.K[b][0][0], P128, 16 * ki, k0, l16, q16),
+                                frag_r(&sm.dXt[0][0], P64, 16 * dmj, k0, l16, q16), acc);
                 }
                 dm[u] = acc;
             }
-            put_dm();
         }
-        // this chunk's dbeta and dgamma shares (the partial slots were written before the
-        // last two barriers), on wave 7: lane = row
-        if (wave == 7) {
-            const long ws_row = ((long)(slice * a.ncid + cid0 + c) * a.Hv + h) * BC + lane;
-            float b = 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < 6; ++s2) b += sm.pb[lane][s2];
-            a.ws_db[ws_row] = b;
-            if (GATED) {
-                float gsum = 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < 46; ++s2) gsum += sm.pg[lane][s2];
-                // gamma_L, on the last row: e^gamma_L <M, dM'> + sum_r c_r (slots 44, 45 hold -c_r)
-                float ct = -(sm.pg[lane][44] + sm.pg[lane][45]);
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) ct += __shfl_xor(ct, off);
-                if (lane == BC - 1) {
-                    float m = 0.f;
-#pragma unroll
-                    for (int w = 0; w < 8; ++w) m += sm.mdm[w];
-                    gsum += sm.eg[BC - 1] * m + ct;
-                }
-                a.ws_dg[ws_row] = gsum;
-            }
+        // the next chunk's inputs into the other buffers (read last two barriers ago), the
+        // new dM' into LDS (read before the last two barriers)
+        if (c > 0) {
+            put_in(f, b ^ 1);
+            if (c > 1) fetch(c - 2, f);
         }
+        put_dm();
         __syncthreads();
-        cur = nxt;
     }
     // the initial state's gradient: dM' after the first chunk
     if (a.dh0) {
@@ -624,72 +530,421 @@ __global__ __launch_bounds__(NTB, 1) void chunk_bwd_kernel(ChunkBwdArgs a) {
     }
 }
 
-// The slices' shares added in a fixed order, one workgroup per (chunk number, q/k head):
-// dq and dk summed over the slices and over the value heads of the q/k head (the shares sit
-// in the accumulator layout: tile t = 8 i + j of 16 x 16, lane l, entry e is row
-// 16 i + 4 (l >> 4) + e, key 16 j + (l & 15)); per value head of the group, dbeta summed over
-// the slices and dg_t = the sum of dgamma_r over the rows r >= t of the chunk (a suffix scan
-// on one wave, lane = row).
-__global__ __launch_bounds__(256) void bwd_chunk_sum_kernel(ChunkBwdArgs a) {
+// ==================================== 4. every gradient of a chunk per (chunk, q/k head)
+struct alignas(16) GradSmem {
+    __bf16 K[BC][P128], Q[BC][P128];
+    __bf16 Tt[BC][P64];            // T^T; W = dA o diag(beta) D (row-major) at a head's end
+    __bf16 P[BC][P64];             // P; Z = dP o D at a head's end
+    __bf16 V[BC][P32], dO[BC][P32];   // one 32-column slice of V and dO
+    __bf16 Dl[BC][P32], dR[BC][P32];  // Delta and dR of the slice
+    __bf16 Rt[BS][P64], dDt[BS][P64]; // R^T and dDelta^T of the slice
+    __bf16 M[BD][P32], dM[BD][P32];   // the slice of M and of dM'
+    float beta[BC], gam[BC], eg[BC], tail[BC];
+    // per-row partial sums in fixed slots (summed in order at a head's end)
+    float vdr[BC][8];              // V . dR, per (slice, column block)
+    float ku[BC][8], qy[BC][8], kc[BC][8];   // K . (dR M^T), Q . (dO M^T), K . (Delta dM'^T), per key block
+    float ag[BC][4];               // sum_i dA_ri G_ri, per column block
+    float aa_r[BC][4], pp_r[BC][4];   // row sums of dA o A and dP o P, per column block
+    float aa_c[BC][16], pp_c[BC][16]; // minus their column sums, per (row block, row group)
+    float mdm[8];                  // <M, dM'> per wave
+};
+
+// one slice's inputs in registers: piece t & 255 of V (t < 256) or dO (t >= 256) (row =
+// piece / 4), pieces t and t + 512 of M's and dM''s slices (128 rows x 8 float4)
+struct GradIn {
+    uint4 vo;
+    float4 m[2], d[2];
+};
+
+template <bool GATED>
+__global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
+    __shared__ GradSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q16 = lane >> 4;
     const int hq = (int)(blockIdx.x % a.Hqk);
     const long cid = blockIdx.x / a.Hqk;
     int n;
-    if (a.cu) {   // the last sequence whose first chunk number is <= cid (strictly increasing)
-        int lo = 0, hi = a.N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (chunk_id_base(a, mid) <= cid) lo = mid; else hi = mid - 1;
-        }
-        n = lo;
-    } else {
-        n = (int)(cid / ((a.T + BC - 1) / BC));
-    }
-    long bos, eos;
-    seq_range(a.cu, n, a.T, bos, eos);
-    const long c = cid - chunk_id_base(a, n);
-    if (c * BC >= eos - bos) return;   // a number no chunk uses
-    const int rows = (int)min((long)BC, eos - bos - c * BC);
-    const long tok0 = bos + c * BC;
+    long c, bos, L;
+    if (!chunk_of_id(a, cid, n, c, bos, L)) return;
     const int grp = a.Hv / a.Hqk;
-    const long sstride = a.ncid * a.Hv * BC;   // rows between slices
-    const int tid = threadIdx.x;
-    for (int p = tid; p < BC * BD / 4; p += 256) {
-        const int t = p >> 6, ln = p & 63;
-        const int i = t >> 3, j = t & 7, l16 = ln & 15, q16 = ln >> 4;
-        f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
-        for (int sl = 0; sl < BNS; ++sl)
-            for (int g = 0; g < grp; ++g) {
-                const long r = (sl * sstride + (cid * a.Hv + (long)hq * grp + g) * BC) * BD + 4 * p;
-                sq += *reinterpret_cast<const f32x4*>(a.ws_dq + r);
-                sk += *reinterpret_cast<const f32x4*>(a.ws_dk + r);
+    const long t0 = bos + c * BC;
+    const int rows = (int)min((long)BC, L - c * BC);
+    const float sc = a.scale;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+
+    // K and Q of the chunk (rows past the end read zeros), issued with the first slice's loads
+    const uint32_t kq_tok = (uint32_t)a.Hqk * BD * 2;
+    const uint32_t kq_bytes = (uint32_t)(rows - 1) * kq_tok + BD * 2;
+    const auto k_rs = rsrc(static_cast<const __bf16*>(a.k) + (t0 * a.Hqk + hq) * BD, kq_bytes);
+    const auto q_rs = rsrc(static_cast<const __bf16*>(a.q) + (t0 * a.Hqk + hq) * BD, kq_bytes);
+    uint4 kin[2], qin[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int pc = tid + NTB * u;
+        const uint32_t off = (uint32_t)(pc >> 4) * kq_tok + (pc & 15) * 16;
+        kin[u] = ld128(k_rs, off, 0);
+        qin[u] = ld128(q_rs, off, 0);
+    }
+
+    // buffer resources over this chunk's rows (rows past the end read zeros, stores there are
+    // dropped) and this chunk's states; per-thread 32-bit offsets, the head and slice in the
+    // scalar offset
+    const uint32_t v_tok = (uint32_t)a.Hv * BD;   // elements per token of v, dO, dv
+    const auto vo_rs = rsrc(static_cast<const __bf16*>(wave < 4 ? a.v : a.dout) + t0 * v_tok, (uint32_t)rows * v_tok * 2);
+    const auto dv_rs = rsrc(a.dv + t0 * v_tok, (uint32_t)rows * v_tok * 4);
+    const uint32_t st_bytes = (uint32_t)a.Hv * BD * BD * 4;
+    const auto m_rs = rsrc(a.states + cid * a.Hv * (long)BD * BD, st_bytes);
+    const auto d_rs = rsrc(a.dstates + cid * a.Hv * (long)BD * BD, st_bytes);
+    const int vrow = (tid & 255) >> 2;
+    const uint32_t vo_off = ((uint32_t)vrow * v_tok + (tid & 3) * 8) * 2;
+    uint32_t m_off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int pc = tid + NTB * u;
+        m_off[u] = (uint32_t)((pc >> 3) * BD + (pc & 7) * 4) * 4;
+    }
+    auto fetch = [&](int g, int sl, GradIn& f) {
+        const int h = hq * grp + g, j0 = sl * BS;
+        f.vo = ld128(vo_rs, vo_off, (uint32_t)(h * BD + j0) * 2);
+        const uint32_t so = (uint32_t)(h * BD * BD + j0) * 4;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f.m[u] = __builtin_bit_cast(float4, ld128(m_rs, m_off[u], so));
+            f.d[u] = __builtin_bit_cast(float4, ld128(d_rs, m_off[u], so));
+        }
+    };
+
+    f32x4 dqg[4], dkg[4];   // dq, dk over the group's value heads: tiles (t4, wave) of 64 x 128
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) dqg[t4] = dkg[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    GradIn f;
+    fetch(0, 0, f);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int pc = tid + NTB * u, row = pc >> 4, cg = pc & 15;
+        *reinterpret_cast<uint4*>(&sm.K[row][cg * 8]) = kin[u];
+        *reinterpret_cast<uint4*>(&sm.Q[row][cg * 8]) = qin[u];
+    }
+    for (int g = 0; g < grp; ++g) {
+        const int h = hq * grp + g;
+        // ---------------------------------------- head prologue: T^T, P, beta, gamma
+        __syncthreads();   // the previous head's last reads of W, Z and the slots are done
+        {
+            const int tf = fresh(tid);
+            const uint4* tp = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.tp)) +
+                              (cid * a.Hv + h) * (2L * BC * BC / 8) + tf;
+            *reinterpret_cast<uint4*>(&sm.Tt[tf >> 3][(tf & 7) * 8]) = tp[0];
+            *reinterpret_cast<uint4*>(&sm.P[tf >> 3][(tf & 7) * 8]) = tp[BC * BC / 8];
+            for (int i = tf; i < BC * 4; i += NTB) {   // slots not every tile writes
+                (&sm.ag[0][0])[i] = 0.f;
+                (&sm.aa_r[0][0])[i] = 0.f;
+                (&sm.pp_r[0][0])[i] = 0.f;
             }
+            for (int i = tf; i < BC * 16; i += NTB) {
+                (&sm.aa_c[0][0])[i] = 0.f;
+                (&sm.pp_c[0][0])[i] = 0.f;
+            }
+        }
+        if (wave == 0) {
+            const bool ok = lane < rows;
+            const long s = (t0 + lane) * a.Hv + h;
+            float gl = 0.f, gv = 0.f;
+            if (GATED) gv = gamma_scan(ok ? a.g[s] : 0.f, gl);
+            sm.beta[lane] = ok ? a.beta[s] : 0.f;
+            sm.gam[lane] = gv;
+            sm.eg[lane] = __expf(gv);
+            sm.tail[lane] = __expf(gl - gv);
+        }
+        f32x4 dap[3];                  // dR Delta^T (t < 10) or dO Delta^T (t >= 10), tile t = wave + 8 m
+        f32x4 qa[4], uu[4], k2[4];     // dO M^T, dR M^T, Delta dM'^T: tiles (t4, wave)
+#pragma unroll
+        for (int m = 0; m < 3; ++m) dap[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) qa[t4] = uu[t4] = k2[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float mdm_t = 0.f;
+        const int ti = wave >> 1, tj = wave & 1;   // this wave's tile of a 64 x 32 product
+
+#pragma unroll 1
+        for (int sl = 0; sl < BNS; ++sl) {
+            const int j0 = sl * BS;
+            // ------------------------------------------------------ the slice's inputs
+            if (sl > 0) __syncthreads();   // the last slice's products are read
+            {
+            const int tf = fresh(tid), vr = (tf & 255) >> 2;
+            *reinterpret_cast<uint4*>(tf < 256 ? &sm.V[vr][(tf & 3) * 8] : &sm.dO[vr][(tf & 3) * 8]) = f.vo;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int pc = tf + NTB * u, mr = pc >> 3, mc = (pc & 7) * 4;
+                *reinterpret_cast<uint2*>(&sm.M[mr][mc]) =
+                    make_uint2(pack_bf16x2(f.m[u].x, f.m[u].y), pack_bf16x2(f.m[u].z, f.m[u].w));
+                *reinterpret_cast<uint2*>(&sm.dM[mr][mc]) =
+                    make_uint2(pack_bf16x2(f.d[u].x, f.d[u].y), pack_bf16x2(f.d[u].z, f.d[u].w));
+                if (GATED)
+                    mdm_t += f.m[u].x * f.d[u].x + f.m[u].y * f.d[u].y + f.m[u].z * f.d[u].z + f.m[u].w * f.d[u].w;
+            }
+            }
+            if (sl + 1 < BNS) fetch(g, sl + 1, f);
+            else if (g + 1 < grp) fetch(g + 1, 0, f);
+            __syncthreads();
+
+            // ------------- R = diag(beta) (V - diag(e^gamma) K M); dDelta = scale P^T dO + diag(tail) K dM'
+            {
+                const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;   // lane offsets rederived here
+                f32x4 x = {0.f, 0.f, 0.f, 0.f}, kd = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < BD; k0 += 32) {
+                    const bf16x8 kf = frag_r(&sm.K[0][0], P128, 16 * ti, k0, l16, q16);
+                    x = mma16(kf, frag_c(&sm.M[0][0], P32, 16 * tj, k0, l16, q16), x);
+                    kd = mma16(kf, frag_c(&sm.dM[0][0], P32, 16 * tj, k0, l16, q16), kd);
+                }
+#pragma unroll
+                for (int k0 = 0; k0 < BC; k0 += 32)
+                    if (k0 + 32 > 16 * ti) pd = mma16(frag_c(&sm.P[0][0], P64, 16 * ti, k0, l16, q16),
+                                                      frag_c(&sm.dO[0][0], P32, 16 * tj, k0, l16, q16), pd);
+                const int col = 16 * tj + l16;
+                f32x4 r, dd;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * ti + 4 * q16 + e;
+                    r[e] = sm.beta[row] * ((float)sm.V[row][col] - sm.eg[row] * x[e]);
+                    dd[e] = sc * pd[e] + sm.tail[row] * kd[e];
+                }
+                put_tile_t(&sm.Rt[0][0], P64, ti, tj, r, l16, q16);
+                put_tile_t(&sm.dDt[0][0], P64, ti, tj, dd, l16, q16);
+            }
+            __syncthreads();
+
+            // ------------------------------ Delta = T R; dR = T^T dDelta; dV; V . dR
+            {
+                const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;   // lane offsets rederived here
+                f32x4 dl = {0.f, 0.f, 0.f, 0.f}, dr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < BC; k0 += 32) {
+                    if (k0 <= 16 * ti) dl = mma16(frag_c(&sm.Tt[0][0], P64, 16 * ti, k0, l16, q16),
+                                                  frag_r(&sm.Rt[0][0], P64, 16 * tj, k0, l16, q16), dl);
+                    if (k0 + 32 > 16 * ti) dr = mma16(frag_r(&sm.Tt[0][0], P64, 16 * ti, k0, l16, q16),
+                                                      frag_r(&sm.dDt[0][0], P64, 16 * tj, k0, l16, q16), dr);
+                }
+                put_tile(&sm.Dl[0][0], P32, ti, tj, dl, l16, q16);
+                put_tile(&sm.dR[0][0], P32, ti, tj, dr, l16, q16);
+                const int col = 16 * tj + l16;
+                f32x4 vd;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * ti + 4 * q16 + e;
+                    vd[e] = (float)sm.V[row][col] * dr[e];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sm.beta[row] * dr[e]), dv_rs,
+                                                          ((uint32_t)row * v_tok + col) * 4, (uint32_t)(h * BD + j0) * 4, 0);
+                }
+                vd = row_sum16(vd);
+                if (l16 == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sm.vdr[16 * ti + 4 * q16 + e][2 * sl + tj] = vd[e];
+                }
+            }
+            __syncthreads();
+
+            // ---------------- dR Delta^T, dO Delta^T (lower tiles); dO M^T, dR M^T, Delta dM'^T
+            {
+            const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;   // lane offsets rederived here
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int t = wave + 8 * m;
+                if (t < 20) {
+                    int ri, ci;
+                    lower_tile(t % 10, ri, ci);
+                    dap[m] = mma16(frag_r(t < 10 ? &sm.dR[0][0] : &sm.dO[0][0], P32, 16 * ri, 0, l16, q16),
+                                   frag_r(&sm.Dl[0][0], P32, 16 * ci, 0, l16, q16), dap[m]);
+                }
+            }
+            {
+                const bf16x8 mf = frag_r(&sm.M[0][0], P32, 16 * wave, 0, l16, q16);
+                const bf16x8 df = frag_r(&sm.dM[0][0], P32, 16 * wave, 0, l16, q16);
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) {
+                    qa[t4] = mma16(frag_r(&sm.dO[0][0], P32, 16 * t4, 0, l16, q16), mf, qa[t4]);
+                    uu[t4] = mma16(frag_r(&sm.dR[0][0], P32, 16 * t4, 0, l16, q16), mf, uu[t4]);
+                    k2[t4] = mma16(frag_r(&sm.Dl[0][0], P32, 16 * t4, 0, l16, q16), df, k2[t4]);
+                    sched_fence();
+                }
+            }
+            }
+        }
+
+        // ------------------------------------------------- head end: W, Z, row sums
+        // (T^T was last read before the last slice's final barrier; each P tile is read and
+        // overwritten by the wave that owns it)
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;   // lane offsets rederived here
+            const int t = wave + 8 * m;
+            if (t < 20) {
+                int ri, ci;
+                lower_tile(t % 10, ri, ci);
+                const bool isa = t < 10;
+                f32x4 gk = {0.f, 0.f, 0.f, 0.f};   // K K^T (the dA tiles)
+                if (isa) {
+#pragma unroll
+                    for (int k0 = 0; k0 < BD; k0 += 32)
+                        gk = mma16(frag_r(&sm.K[0][0], P128, 16 * ri, k0, l16, q16),
+                                   frag_r(&sm.K[0][0], P128, 16 * ci, k0, l16, q16), gk);
+                }
+                const int col = 16 * ci + l16;
+                const float gc = sm.gam[col];
+                f32x4 rs, bs, wz;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * ri + 4 * q16 + e;
+                    const bool keep = isa ? col < row : col <= row;
+                    const float dv = keep ? (isa ? -dap[m][e] : sc * dap[m][e]) : 0.f;
+                    const float dec = GATED ? __expf(fminf(sm.gam[row] - gc, 0.f)) : 1.f;
+                    const float s = isa ? dec * gk[e] : (float)sm.P[row][col];   // D o K K^T, or P
+                    const float fb = isa ? sm.beta[row] : 1.f;
+                    rs[e] = dv * fb * s;     // dA o A (A = beta G) or dP o P
+                    bs[e] = dv * s;          // dA o G (the dbeta term)
+                    wz[e] = keep ? dv * fb * dec : 0.f;   // W or Z
+                }
+                put_tile(isa ? &sm.Tt[0][0] : &sm.P[0][0], P64, ri, ci, wz, l16, q16);
+                if (isa) {
+                    const f32x4 b16 = row_sum16(bs);
+                    if (l16 == 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sm.ag[16 * ri + 4 * q16 + e][ci] = b16[e];
+                    }
+                }
+                if (GATED) {
+                    const f32x4 r16 = row_sum16(rs);
+                    if (l16 == 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) (isa ? sm.aa_r : sm.pp_r)[16 * ri + 4 * q16 + e][ci] = r16[e];
+                    }
+                    (isa ? sm.aa_c : sm.pp_c)[col][4 * ri + q16] = -(rs[0] + rs[1] + rs[2] + rs[3]);
+                }
+            }
+            sched_fence();
+        }
+        if (tid < 192) {   // W's blocks above the diagonal (T^T's entries are there)
+            const int tf = fresh(tid), u = tf >> 5, r = (tf >> 1) & 15, half = tf & 1;
+            const int ri = u < 3 ? 0 : u < 5 ? 1 : 2;
+            const int ci = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+            *reinterpret_cast<uint4*>(&sm.Tt[16 * ri + r][16 * ci + 8 * half]) = z4;
+        }
+        // the three row dot products, and the state terms of this head's dq and dk
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;   // lane offsets rederived here
+            const int key = 16 * wave + l16;
+            f32x4 pq, pu, pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * t4 + 4 * q16 + e;
+                const float kv = (float)sm.K[row][key];
+                pq[e] = (float)sm.Q[row][key] * qa[t4][e];
+                pu[e] = kv * uu[t4][e];
+                pk[e] = kv * k2[t4][e];
+                dqg[t4][e] += sc * sm.eg[row] * qa[t4][e];
+                dkg[t4][e] += -sm.beta[row] * sm.eg[row] * uu[t4][e] + sm.tail[row] * k2[t4][e];
+            }
+            pu = row_sum16(pu);
+            if (GATED) {
+                pq = row_sum16(pq);
+                pk = row_sum16(pk);
+            }
+            if (l16 == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * t4 + 4 * q16 + e;
+                    sm.ku[row][wave] = pu[e];
+                    if (GATED) {
+                        sm.qy[row][wave] = pq[e];
+                        sm.kc[row][wave] = pk[e];
+                    }
+                }
+            }
+            sched_fence();
+        }
+        if (GATED) {
+            const float s = wave_sum(mdm_t);
+            if (lane == 0) sm.mdm[wave] = s;
+        }
+        __syncthreads();
+
+        // ------------------- dq += Z K; dk += W K + W^T K + Z^T Q (W in Tt, Z in P)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;   // lane offsets rederived here
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32) {
+                if (k0 <= 16 * t4) {   // the lower factors
+                    const bf16x8 kc = frag_c(&sm.K[0][0], P128, 16 * wave, k0, l16, q16);
+                    dqg[t4] = mma16(frag_r(&sm.P[0][0], P64, 16 * t4, k0, l16, q16), kc, dqg[t4]);
+                    dkg[t4] = mma16(frag_r(&sm.Tt[0][0], P64, 16 * t4, k0, l16, q16), kc, dkg[t4]);
+                }
+                if (k0 + 32 > 16 * t4) {   // the transposed (upper) factors
+                    dkg[t4] = mma16(frag_c(&sm.Tt[0][0], P64, 16 * t4, k0, l16, q16),
+                                    frag_c(&sm.K[0][0], P128, 16 * wave, k0, l16, q16), dkg[t4]);
+                    dkg[t4] = mma16(frag_c(&sm.P[0][0], P64, 16 * t4, k0, l16, q16),
+                                    frag_c(&sm.Q[0][0], P128, 16 * wave, k0, l16, q16), dkg[t4]);
+                }
+            }
+            sched_fence();   // one tile's operands in flight at a time (register pressure)
+        }
+        // this head's dbeta and dg (wave 7, lane = row)
+        if (wave == 7) {
+            const int r = fresh(lane);
+            float xdr = 0.f, db = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) xdr += sm.ku[r][s];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) db += sm.vdr[r][s];
+            db -= sm.eg[r] * xdr;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) db += sm.ag[r][s];
+            const long o = (t0 + r) * a.Hv + h;
+            if (r < rows) a.dbeta[o] = db;
+            if (GATED) {
+                float y = 0.f, cr = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    y += sm.qy[r][s];
+                    cr += sm.kc[r][s];
+                }
+                cr *= sm.tail[r];
+                float dgam = sc * sm.eg[r] * y - sm.beta[r] * sm.eg[r] * xdr - cr;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) dgam += sm.aa_r[r][s] + sm.pp_r[r][s];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) dgam += sm.aa_c[r][s] + sm.pp_c[r][s];
+                // gamma_L, on the last row: e^gamma_L <M, dM'> + sum_r c_r
+                const float ct = wave_sum(cr);
+                if (r == BC - 1) {
+                    float mm = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) mm += sm.mdm[w];
+                    dgam += sm.eg[BC - 1] * mm + ct;
+                }
+                // dg_i = sum over the rows r >= i
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float up = __shfl_down(dgam, off);
+                    if (r + off < 64) dgam += up;
+                }
+                if (r < rows) a.dg[o] = dgam;
+            }
+        }
+    }
+    // dq and dk of the q/k head
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int row = 16 * i + 4 * q16 + e;
+            const int row = 16 * t4 + 4 * q16 + e;
             if (row < rows) {
-                const long o = ((tok0 + row) * a.Hqk + hq) * BD + 16 * j + l16;
-                a.dq[o] = sq[e];
-                a.dk[o] = sk[e];
+                const long o = ((t0 + row) * a.Hqk + hq) * BD + 16 * wave + l16;
+                a.dq[o] = dqg[t4][e];
+                a.dk[o] = dkg[t4][e];
             }
-        }
-    }
-    const int lane = tid & 63;
-    for (int g = tid >> 6; g < grp; g += 4) {
-        const int h = hq * grp + g;
-        float sb = 0.f, sg = 0.f;
-        for (int sl = 0; sl < BNS; ++sl) {
-            const long r = sl * sstride + (cid * a.Hv + h) * BC + lane;
-            sb += a.ws_db[r];
-            if (a.dg) sg += a.ws_dg[r];
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_down(sg, off);
-            if (lane + off < 64) sg += o;
-        }
-        if (lane < rows) {
-            a.dbeta[(tok0 + lane) * a.Hv + h] = sb;
-            if (a.dg) a.dg[(tok0 + lane) * a.Hv + h] = sg;
         }
     }
 }
@@ -702,39 +957,74 @@ bool chunk_bwd_supported(const PrefillArgs& a) {
 }
 
 size_t chunk_bwd_workspace_bytes(const PrefillArgs& a, long ncid_l) {
-    const size_t ncid = (size_t)ncid_l;
-    const size_t states = ncid * a.Hv * BD * BD;
-    const size_t shares = (size_t)BNS * ncid * a.Hv * BC * (2 * BD + 2);
-    return (states + shares) * sizeof(float);
+    const size_t per = (size_t)ncid_l * a.Hv;
+    return per * BD * BD * sizeof(float) * 2 + per * 2 * BC * BC * 2;
 }
+
+namespace {
+// A second stream per device for the chunk-start states: that launch needs nothing the T/P
+// and carry launches produce, so it runs beside them (with few sequences it fills only part
+// of the chip); the caller's stream waits for it before the gradient launch.  Fork and join
+// are events, so the pattern also records into a graph captured on the caller's stream.
+// The record / wait sequence is serialised per process (calls from several host threads).
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_stream(SideStream*& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideStream& ss = g_side[dev];
+    if (!ss.stream) {
+        if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    out = &ss;
+    return hipSuccess;
+}
+}  // namespace
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
     ChunkBwdArgs a = a0;
     a.ncid = chunk_id_bound(a);
-    const size_t ncid = (size_t)a.ncid;
+    const size_t per = (size_t)a.ncid * a.Hv;
     float* ws = static_cast<float*>(a.ws);
     a.states = ws;
-    a.ws_dq = ws + ncid * a.Hv * BD * BD;
-    a.ws_dk = a.ws_dq + (size_t)BNS * ncid * a.Hv * BC * BD;
-    a.ws_db = a.ws_dk + (size_t)BNS * ncid * a.Hv * BC * BD;
-    a.ws_dg = a.ws_db + (size_t)BNS * ncid * a.Hv * BC;
-    // 1. the state at every chunk start (the forward kernel, outputs skipped)
+    a.dstates = ws + per * BD * BD;
+    a.tp = a.dstates + per * BD * BD;
+    const long ids = a.ncid * a.Hv, qk_ids = a.ncid * a.Hqk, chains = (long)a.N * a.Hv * BNS;
+    if (ids > 0x7fffffffL || chains > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = nullptr;
+    hipError_t e = side_stream(ss);
+    if (e != hipSuccess) return e;
+    // 1. the state at every chunk start (the prompt kernel, outputs skipped), on the side
+    //    stream once the caller's stream has reached this call
     PrefillArgs f = a;
     f.ws = a.states;
     f.hT = nullptr;
-    hipError_t e = launch_prefill_fused_states(f, s);
-    if (e != hipSuccess) return e;
-    // 2. the reverse pass per (sequence, value head, slice)
-    const long blocks = (long)a.N * a.Hv * BNS;
-    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (blocks > 0) {
-        if (a.g) hipLaunchKernelGGL(chunk_bwd_kernel<true>, dim3((unsigned)blocks), dim3(NTB), 0, s, a);
-        else hipLaunchKernelGGL(chunk_bwd_kernel<false>, dim3((unsigned)blocks), dim3(NTB), 0, s, a);
+    if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
+    if ((e = launch_prefill_fused_states(f, ss->stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return e;
+    // 2. T^T and P per (chunk, value head)
+    if (ids > 0) hipLaunchKernelGGL(chunk_tp_kernel, dim3((unsigned)ids), dim3(NTP), 0, s, a);
+    // 3. the carry per (sequence, value head, slice)
+    if (chains > 0) hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)chains), dim3(NTB), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 4. the gradients per (chunk, q/k head), after the states
+    if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
+    if (qk_ids > 0) {
+        if (a.g) hipLaunchKernelGGL(chunk_grad_kernel<true>, dim3((unsigned)qk_ids), dim3(NTB), 0, s, a);
+        else hipLaunchKernelGGL(chunk_grad_kernel<false>, dim3((unsigned)qk_ids), dim3(NTB), 0, s, a);
     }
-    // 3. the slices' shares added
-    const long sum_blocks = a.ncid * a.Hqk;
-    if (sum_blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (sum_blocks > 0) hipLaunchKernelGGL(bwd_chunk_sum_kernel, dim3((unsigned)sum_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

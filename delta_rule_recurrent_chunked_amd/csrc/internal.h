@@ -105,17 +105,16 @@ struct RecurrentBwdArgs : PrefillArgs {
 int recurrent_bwd_slices(int Dk, int Dv);
 
 // The chunkwise reverse pass: the forward's arguments, dL/do and dL/dM_T in; gradients out
-// (fp32).  The workspace holds the state at every chunk start and each 32-column slice's
-// share of dq, dk, dbeta and dgamma per (chunk, row).
+// (fp32).  The workspace holds, per (chunk number, value head), the state at the chunk's
+// start and the gradient of the state after the chunk (fp32, key-major), and T^T and P of
+// the chunk (bf16, 64 x 64 each).
 struct ChunkBwdArgs : PrefillArgs {
     const void* dout;               // [tokens, Hv, Dv] bf16
     const float* dfinal;            // [N, Hv, Dk, Dv] or null
     long ncid;                      // chunk numbers (chunk_id_bound)
     float* states;                  // [ncid, Hv, Dk, Dv]
-    float* ws_dq;                   // [4, ncid, Hv, 64 x Dk in 16 x 16 accumulator tiles]
-    float* ws_dk;                   // [4, ncid, Hv, 64 x Dk in 16 x 16 accumulator tiles]
-    float* ws_db;                   // [4, ncid, Hv, 64]
-    float* ws_dg;                   // [4, ncid, Hv, 64]
+    float* dstates;                 // [ncid, Hv, Dk, Dv]
+    void* tp;                       // [ncid, Hv, 2, 64, 64] bf16: T^T, then P
     float* dq;                      // [tokens, Hqk, Dk]
     float* dk;                      // [tokens, Hqk, Dk]
     float* dv;                      // [tokens, Hv, Dv]

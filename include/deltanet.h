@@ -268,11 +268,11 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
  * training; the learned gate and write strengths of the nnterp "linear_attention" page,
  * LinearAttention class text): given dL/do and dL/d final_state, the gradients for q, k,
  * v, beta, g and the initial state, without a per-token state trace.  It reruns the forward
- * chunk chain to keep the state at every chunk start (Dk * Dv * 4 bytes per chunk and value
- * head), then walks each sequence's chunks backwards, carrying dL/dM from chunk to chunk
- * and recomputing each chunk's matrices (A, T, P, X, Delta) from its start state; value
- * columns are split over 32-column slices whose shares of dq, dk, dbeta, dg are added in a
- * fixed order (the result is bitwise reproducible).
+ * chunk chain to keep the state at every chunk start, forms T = (I + A)^-1 and P of every
+ * chunk in parallel, walks each sequence's chunks backwards carrying only dL/dM (written
+ * out at every chunk), and then forms every gradient of every chunk in parallel from the
+ * chunk's start state and dL/dM after it.  dq and dk sum the value heads of a q/k head in a
+ * fixed order and no step uses atomics (the result is bitwise reproducible).
  *
  * Supported: bf16 q/k/v/d_o, Dk = Dv = 128, 64-token chunks, one log decay per head or
  * none, no flags; other shapes return DN_ERR_UNSUPPORTED (dn_recurrent_bwd computes them
@@ -284,9 +284,10 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
  *   dv              [B, T, Hv, Dv] fp32;  dbeta [B, T, Hv] fp32
  *   dg              [B, T, Hv] fp32, required when g is given, else ignored
  *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
- *   workspace       dn_chunk_bwd_workspace_bytes(shape) bytes: the chunk-start states and
- *                   the slices' shares ((Dk * Dv + 4 * 64 * (2 Dk + 2)) * 4 bytes per chunk
- *                   and value head); contents on entry ignored, on exit undefined
+ *   workspace       dn_chunk_bwd_workspace_bytes(shape) bytes: per chunk and value head the
+ *                   state at the chunk start and dL/dM after the chunk (fp32) and T and P
+ *                   (bf16): (2 Dk Dv * 4 + 2 * 64 * 64 * 2) bytes; contents on entry
+ *                   ignored, on exit undefined
  *
  * Errors: as dn_chunk_fwd, DN_ERR_UNSUPPORTED as above, DN_ERR_WORKSPACE.
  */

@@ -134,3 +134,42 @@ def test_chunk_bwd_rejects_unsupported():
     do = torch.zeros((1, 64, 1, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(NotImplementedError):
         dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], None, None, do)
+
+
+def test_chunk_bwd_graph_replay():
+    """dn_chunk_bwd captured in a HIP graph (its chunk-start states run on a second stream,
+    forked from and joined back to the captured one by events): three replays, each after an
+    eager call on other inputs that rewrites the workspace, match the eager result bit for
+    bit."""
+    _say("chunk bwd graph capture + replays")
+    x = make_case(B=2, T=200, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
+                  seed=85, name="chunk_bwd_graph")
+    y = make_case(B=2, T=200, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.2, init_std=0.02,
+                  seed=86, name="chunk_bwd_graph_other")
+    rng = np.random.default_rng(87)
+    do = dev_tensor(f32_to_bf16_bits(rng.standard_normal((2, 200, 2, 128)).astype(np.float32)))
+    d, e = to_inputs(x), to_inputs(y)
+    ws = torch.empty(dn.chunk_bwd_workspace_bytes(2, 200, 2, 2, 128, 128, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], do)
+    other = (e["q"], e["k"], e["v"], e["beta"], e["g"], e["init"], do)
+    eager = dn.chunk_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dn.chunk_bwd(*args, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = dn.chunk_bwd(*args, workspace=ws)
+    for rep in range(3):
+        dn.chunk_bwd(*other, workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in eager.items():
+            if v is not None:
+                assert torch.equal(out[k], v), (rep, k)
+    _say("  three replays match the eager call")
