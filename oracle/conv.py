@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-__all__ = ["causal_conv"]
+__all__ = ["causal_conv", "conv_qkv"]
 
 
 def causal_conv(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = None,
@@ -54,3 +54,25 @@ def causal_conv(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = 
             y[cu[n] + t] = acc / (1.0 + np.exp(-acc)) if activation else acc
         final[n] = seq[len(seq) - (W - 1):].T
     return y.reshape(B, T, C), final
+
+
+def conv_qkv(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray], Hqk: int, Hv: int,
+             Dk: int, Dv: int, cu_seqlens: Optional[np.ndarray] = None,
+             init_state: Optional[np.ndarray] = None, activation: bool = True,
+             qk_l2norm: bool = True, eps: float = 1e-6):
+    """The prologue of the same flowchart in one function: the convolution above over
+    x = [q | k | v] channels ``[B, T, 2 Hqk Dk + Hv Dv]``, its output split into q, k
+    ``[B, T, Hqk, Dk]`` and v ``[B, T, Hv, Dv]``, then (the flowchart's "L2 Norm" box on the
+    q and k branches) every q and k head replaced by u / sqrt(|u|^2 + eps).  Returns
+    (q, k, v, final state), fp64."""
+    y, final = causal_conv(x, weight, bias, cu_seqlens, init_state, activation)
+    B, T, C = y.shape
+    if C != 2 * Hqk * Dk + Hv * Dv:
+        raise ValueError("x must hold 2 Hqk Dk + Hv Dv channels")
+    q = y[..., :Hqk * Dk].reshape(B, T, Hqk, Dk)
+    k = y[..., Hqk * Dk:2 * Hqk * Dk].reshape(B, T, Hqk, Dk)
+    v = y[..., 2 * Hqk * Dk:].reshape(B, T, Hv, Dv)
+    if qk_l2norm:
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    return q, k, v, final

@@ -73,3 +73,58 @@ def test_split_continues_through_the_state_and_packing_equals_separate_calls():
 def test_bad_offsets():
     with pytest.raises(ValueError):
         causal_conv(np.zeros((1, 5, 2)), np.zeros((2, 4)), cu_seqlens=np.array([0, 3]))
+
+
+# ------------------------------------------------ the fused prologue (conv_qkv)
+
+def test_conv_qkv_worked_example():
+    """One q head (3, 4), one k head (0, 2), one v channel, identity filters, no activation:
+    with eps = 0 the heads become (0.6, 0.8) and (0, 1); with eps = 11 the q head is
+    (3, 4) / 6 (|u|^2 + eps = 36); v passes through."""
+    from oracle.conv import conv_qkv
+    x = np.array([[[3.0, 4.0, 0.0, 2.0, -7.0]]])          # [B=1, T=1, C=5]
+    w = np.zeros((5, 2)); w[:, -1] = 1.0                    # y_t = x_t
+    q, k, v, fin = conv_qkv(x, w, None, 1, 1, 2, 1, activation=False, eps=0.0)
+    np.testing.assert_allclose(q[0, 0, 0], [0.6, 0.8], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(k[0, 0, 0], [0.0, 1.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(v[0, 0, 0], [-7.0], rtol=0, atol=0)
+    np.testing.assert_allclose(fin[0, :, 0], [3.0, 4.0, 0.0, 2.0, -7.0])
+    q, _, _, _ = conv_qkv(x, w, None, 1, 1, 2, 1, activation=False, eps=11.0)
+    np.testing.assert_allclose(q[0, 0, 0], [0.5, 4.0 / 6.0], rtol=0, atol=1e-15)
+
+
+def test_conv_qkv_heads_are_unit_vectors_along_the_conv_output():
+    """Against causal_conv on packed sequences with states, bias and silu, GQA heads: every
+    q and k head is parallel to the convolution's head (cosine 1) with norm
+    |u| / sqrt(|u|^2 + eps); v and the final state are the convolution's, exactly; without
+    the norm all three are the convolution's channels in order."""
+    from oracle.conv import conv_qkv
+    rng = np.random.default_rng(5)
+    Hqk, Hv, Dk, Dv, W = 2, 4, 8, 4, 4
+    C = 2 * Hqk * Dk + Hv * Dv
+    lens = [7, 0, 1, 12]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x, w, b = _x(rng, T, C), rng.standard_normal((C, W)), rng.standard_normal(C)
+    init = rng.standard_normal((len(lens), C, W - 1))
+    eps = 0.3
+    u, fin_ref = causal_conv(x, w, b, cu, init)
+    q, k, v, fin = conv_qkv(x, w, b, Hqk, Hv, Dk, Dv, cu, init, eps=eps)
+    np.testing.assert_array_equal(fin, fin_ref)
+    np.testing.assert_array_equal(v.reshape(1, T, Hv * Dv), u[..., 2 * Hqk * Dk:])
+    for got, lo in ((q, 0), (k, Hqk * Dk)):
+        uh = u[..., lo:lo + Hqk * Dk].reshape(1, T, Hqk, Dk)
+        nu = np.linalg.norm(uh, axis=-1)
+        np.testing.assert_allclose(np.linalg.norm(got, axis=-1), nu / np.sqrt(nu ** 2 + eps), rtol=1e-13)
+        cos = np.sum(got * uh, axis=-1) / (np.linalg.norm(got, axis=-1) * nu)
+        np.testing.assert_allclose(cos, 1.0, rtol=1e-13)
+    q0, k0, v0, _ = conv_qkv(x, w, b, Hqk, Hv, Dk, Dv, cu, init, qk_l2norm=False)
+    np.testing.assert_array_equal(np.concatenate([q0.reshape(1, T, -1), k0.reshape(1, T, -1),
+                                                  v0.reshape(1, T, -1)], axis=-1), u)
+
+
+def test_conv_qkv_rejects_a_split_that_does_not_add_up():
+    from oracle.conv import conv_qkv
+    x = np.zeros((1, 3, 10))
+    with pytest.raises(ValueError):
+        conv_qkv(x, np.ones((10, 2)), None, 1, 1, 4, 4)
