@@ -594,6 +594,16 @@ def main():
     torch.cuda.synchronize()
     conv_us = ev0.elapsed_time(ev1) * 1e3 / 20
     conv_b = 2 * B * T * Cc * 2 + Cc * 4 * 5 + B * Cc * 3 * 2
+    # the fused prologue: the same convolution, split into q, k, v with q and k L2-normalised
+    for _ in range(3):
+        dn.conv_qkv(cx, cw, cb, Hqk, Hv, D, D)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(20):
+        dn.conv_qkv(cx, cw, cb, Hqk, Hv, D, D)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    qkv_us = ev0.elapsed_time(ev1) * 1e3 / 20
     Cd = 3 * y.Hv * y.Dk
     dx = torch.from_numpy(crng.standard_normal((y.B, Cd)).astype(np.float32)).to(dev).to(torch.bfloat16)
     dwt = torch.from_numpy((crng.standard_normal((Cd, 4)) / 2).astype(np.float32)).to(dev)
@@ -618,6 +628,16 @@ def main():
                                 "frac": conv_b / (conv_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                 "algorithmic_bytes": conv_b,
                                 "traffic": load_traffic("conv_bytes_per_call")}},
+        "prologue_conv_qkv": {
+            "what": "dn_conv_qkv: the convolution + silu, split into q, k, v tensors, q and k "
+                    "L2-normalised per head, in one pass (the rule then runs without in-call norm)",
+            "workload": f"B{B} T{T}, {Cc} channels -> q, k [B, T, {Hqk}, {D}], v [B, T, {Hv}, {D}]",
+            "kernel": "conv_kernel (split outputs, head norm)", "us_per_call": qkv_us,
+            "roofline": {"bound": "hbm", "achieved": conv_b / (qkv_us * 1e-6) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": conv_b / (qkv_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes": conv_b,
+                         "traffic": load_traffic("conv_qkv_bytes_per_call")}},
         "decode_step": {"workload": f"{y.B} sequences, {Cd} channels, conv state in place",
                         "kernel": "conv_step_kernel", "us_per_step": cstep_us,
                         "hbm_frac": cstep_b / (cstep_us * 1e-6) / 1e9 / HBM_PEAK_GBS,

@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_path", "chunk_bwd", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv",
+__all__ = ["chunk_fwd", "chunk_fwd_path", "chunk_bwd", "recurrent_fwd", "recurrent_bwd", "decode_step", "norm_gate", "causal_conv", "conv_qkv",
            "causal_conv_step", "workspace_bytes", "chunk_bwd_workspace_bytes", "lib_path", "load_library",
            "DeltaNetError", "DN_OK", "DN_ERR_INVALID_ARG", "DN_ERR_UNSUPPORTED",
            "DN_ERR_HIP", "DN_ERR_WORKSPACE", "EXPORTED"]
@@ -34,7 +34,7 @@ DN_F32, DN_BF16 = 0, 1
 EXPORTED = ("dn_chunk_fwd", "dn_chunk_fwd_workspace_bytes", "dn_decode_step", "dn_decode_step_ex",
             "dn_norm_gate", "dn_recurrent_fwd", "dn_causal_conv", "dn_causal_conv_step",
             "dn_recurrent_bwd", "dn_recurrent_bwd_workspace_bytes", "dn_chunk_fwd_path",
-            "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_chunk_bwd_workspace_bytes",
+            "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_chunk_bwd_workspace_bytes", "dn_conv_qkv",
             "dn_status_str", "dn_version")
 
 
@@ -54,6 +54,11 @@ class _ConvShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("C", ctypes.c_int32), ("width", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("activation", ctypes.c_int32)]
+
+
+class _QkvSplit(ctypes.Structure):
+    _fields_ = [("Hqk", ctypes.c_int32), ("Hv", ctypes.c_int32), ("Dk", ctypes.c_int32),
+                ("Dv", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32), ("eps", ctypes.c_float)]
 
 
 class _Epilogue(ctypes.Structure):
@@ -115,6 +120,9 @@ def load_library():
         cs = ctypes.POINTER(_ConvShape)
         lib.dn_causal_conv.argtypes = [cs, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.dn_causal_conv.restype = ctypes.c_int
+        lib.dn_conv_qkv.argtypes = [cs, ctypes.POINTER(_QkvSplit), vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, vp]
+        lib.dn_conv_qkv.restype = ctypes.c_int
         lib.dn_causal_conv_step.argtypes = [cs, vp, vp, vp, vp, vp, vp]
         lib.dn_causal_conv_step.restype = ctypes.c_int
         lib.dn_recurrent_fwd.restype = ctypes.c_int
@@ -550,6 +558,51 @@ def causal_conv(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
     if rc != DN_OK:
         _raise(rc, "dn_causal_conv")
     return out, final_state
+
+
+def conv_qkv(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], Hqk: int, Hv: int,
+             Dk: int, Dv: int, initial_state: Optional[torch.Tensor] = None,
+             output_final_state: bool = True, cu_seqlens: Optional[torch.Tensor] = None,
+             activation: Optional[str] = "silu", qk_l2norm: bool = True, eps: float = 1e-6
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """The prologue in front of the rule in one pass: :func:`causal_conv` over
+    x = [q | k | v] projections ``[B, T, 2 Hqk Dk + Hv Dv]``, split into q, k
+    ``[B, T, Hqk, Dk]`` and v ``[B, T, Hv, Dv]`` with q and k L2-normalised per head
+    (``qk_l2norm``, x / sqrt(|x|^2 + eps)).  Returns ``(q, k, v, final_state)``; hand q, k, v
+    to :func:`chunk_fwd` without ``qk_l2norm``."""
+    lib = load_library()
+    _dev(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
+    B, T, C = x.shape
+    _dev(weight, "weight", torch.float32)
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [C, W]")
+    W = weight.shape[1]
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (C,))
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", x.dtype, (N, C, W - 1))
+    final_state = torch.empty((N, C, W - 1), dtype=x.dtype, device=x.device) if output_final_state else None
+    if activation not in _ACTIVATIONS:
+        raise ValueError("activation must be 'silu' or None")
+    q = torch.empty((B, T, Hqk, Dk), dtype=x.dtype, device=x.device)
+    k = torch.empty((B, T, Hqk, Dk), dtype=x.dtype, device=x.device)
+    v = torch.empty((B, T, Hv, Dv), dtype=x.dtype, device=x.device)
+    shape = _ConvShape(B, T, N, C, W, _dtype_code(x), _ACTIVATIONS[activation])
+    split = _QkvSplit(Hqk, Hv, Dk, Dv, int(bool(qk_l2norm)), float(eps))
+    with torch.cuda.device(x.device):
+        rc = lib.dn_conv_qkv(ctypes.byref(shape), ctypes.byref(split), _ptr(x), _ptr(weight),
+                             _ptr(bias), _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens),
+                             _ptr(q), _ptr(k), _ptr(v), _stream(x.device))
+    if rc != DN_OK:
+        _raise(rc, "dn_conv_qkv")
+    return q, k, v, final_state
 
 
 def causal_conv_step(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],

@@ -1,6 +1,7 @@
 // api.cpp -- the exported C ABI (include/deltanet.h): host-side argument checks,
 // then the launch of the right kernels on the caller's stream.  No allocation, no
 // global state.
+#include <cmath>
 #include "../../include/deltanet.h"
 #include "internal.h"
 
@@ -178,6 +179,7 @@ static dn_status conv_shape(const dn_conv_shape* s, dn::ConvArgs& a) {
     a = dn::ConvArgs{};
     a.B = s->B; a.T = s->T; a.N = s->num_seqs; a.C = s->C; a.W = s->width;
     a.bf16 = s->dtype == DN_BF16; a.silu = s->activation;
+    a.y_stride = s->C;
     return DN_OK;
 }
 
@@ -200,6 +202,44 @@ dn_status dn_causal_conv(const dn_conv_shape* s, const void* x, const float* w, 
     if ((s0 && ((uintptr_t)s0 % es)) || (sT && ((uintptr_t)sT % es))) return DN_ERR_INVALID_ARG;
     if ((x && x == y) || (s0 && s0 == sT)) return DN_ERR_INVALID_ARG;
     a.x = x; a.w = w; a.b = b; a.s0 = s0; a.sT = sT; a.cu = cu; a.y = y;
+    return dn::launch_causal_conv(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+dn_status dn_conv_qkv(const dn_conv_shape* s, const dn_qkv_split* sp, const void* x,
+                      const float* w, const float* b, const void* s0, void* sT, const int32_t* cu,
+                      void* q, void* k, void* v, hipStream_t stream) {
+    dn::ConvArgs a;
+    dn_status st = conv_shape(s, a);
+    if (st != DN_OK) return st;
+    if (!sp) return DN_ERR_INVALID_ARG;
+    if (sp->Hqk < 1 || sp->Hv < 1 || sp->Dv < 8 || sp->Dv % 8) return DN_ERR_INVALID_ARG;
+    if (sp->Dk != 16 && sp->Dk != 32 && sp->Dk != 64 && sp->Dk != 128) return DN_ERR_UNSUPPORTED;
+    if ((long)s->C != 2L * sp->Hqk * sp->Dk + (long)sp->Hv * sp->Dv) return DN_ERR_INVALID_ARG;
+    if (sp->qk_l2norm != 0 && sp->qk_l2norm != 1) return DN_ERR_INVALID_ARG;
+    if (!(sp->eps >= 0.f) || !std::isfinite(sp->eps)) return DN_ERR_INVALID_ARG;
+    if (cu) {
+        if (s->B != 1 || s->num_seqs < 1) return DN_ERR_INVALID_ARG;
+    } else if (s->num_seqs != s->B) {
+        return DN_ERR_INVALID_ARG;
+    }
+    const long tokens = (long)s->B * s->T;
+    if (!w || (tokens > 0 && (!x || !q || !k || !v))) return DN_ERR_INVALID_ARG;
+    const void* p16[] = {x, q, k, v};
+    for (const void* p : p16)
+        if (p && !aligned16(p)) return DN_ERR_INVALID_ARG;
+    if (!aligned4(w) || (b && !aligned4(b)) || (cu && !aligned4(cu))) return DN_ERR_INVALID_ARG;
+    const int es = s->dtype == DN_BF16 ? 2 : 4;
+    if ((s0 && ((uintptr_t)s0 % es)) || (sT && ((uintptr_t)sT % es))) return DN_ERR_INVALID_ARG;
+    if (x && (x == q || x == k || x == v)) return DN_ERR_INVALID_ARG;
+    if (tokens > 0 && (q == k || q == v || k == v)) return DN_ERR_INVALID_ARG;
+    if (s0 && s0 == sT) return DN_ERR_INVALID_ARG;
+    a.x = x; a.w = w; a.b = b; a.s0 = s0; a.sT = sT; a.cu = cu;
+    a.qk = sp->Hqk * sp->Dk;
+    a.q = q; a.k = k; a.y = v;
+    a.y_stride = (long)sp->Hv * sp->Dv;
+    a.Dk = sp->Dk;
+    a.qk_norm = sp->qk_l2norm;
+    a.eps = sp->eps;
     return dn::launch_causal_conv(a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 

@@ -13,6 +13,9 @@
 // through them in registers: each input is read once (plus W - 1 at the block start) and
 // each output written once; the lanes of a wave read one token's consecutive channels.
 // A block that crosses sequence starts refills the window from the next sequence's state.
+// The same kernel serves the fused prologue (dn_conv_qkv): the q, k and v channel ranges go
+// to their own tensors, and q and k are L2-normalised per head, the head's Dk / 8 lanes
+// adding their squares by DPP lane moves, so the rule's inputs are ready in one pass.
 // Decode step: a thread owns 8 channels of one sequence and shifts their state in place.
 #include "internal.h"
 
@@ -74,13 +77,27 @@ __device__ __forceinline__ float state_at(const ConvArgs& a, int n, int c, int k
     return a.s0 ? ld_f32(static_cast<const T*>(a.s0), ((long)n * a.C + c) * (W - 1) + k) : 0.f;
 }
 
+// DPP lane moves within rows of 16 lanes (every lane has a source)
+template <int CTRL>
+__device__ __forceinline__ float dpp16(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// sum over each group of G consecutive lanes (G = 2, 4, 8 or 16, aligned), in every lane:
+// lane ^ 1, lane ^ 2, then the 8- and 16-lane mirrors
+__device__ __forceinline__ float group_sum(float x, int G) {
+    x += dpp16<0xB1>(x);
+    if (G >= 4) x += dpp16<0x4E>(x);
+    if (G >= 8) x += dpp16<0x141>(x);
+    if (G >= 16) x += dpp16<0x140>(x);
+    return x;
+}
+
 template <typename T, int W>
 __global__ __launch_bounds__(NTH) void conv_kernel(ConvArgs a) {
     const int g = blockIdx.y * NTH + threadIdx.x;   // channel group; blockIdx.x: token block
-    if (g * CG >= a.C) return;
-    const int c0 = g * CG;
+    const bool act = g * CG < a.C;                  // lanes past C compute lane 0's channels
+    const int c0 = act ? g * CG : 0;                // and store nothing
     const T* x = static_cast<const T*>(a.x);
-    T* y = static_cast<T*>(a.y);
     T* sT = static_cast<T*>(a.sT);
     float w[W][CG], bb[CG];
 #pragma unroll
@@ -89,7 +106,24 @@ __global__ __launch_bounds__(NTH) void conv_kernel(ConvArgs a) {
 #pragma unroll
         for (int j = 0; j < W; ++j) w[j][e] = a.w[(long)(c0 + e) * W + j];
     }
-    if (blockIdx.x == 0 && sT) {   // empty sequences keep their state
+    // this lane's output: q, k (normalised per head when asked) or the rest
+    T* ob;
+    long ostr;
+    bool nrm = false;
+    if (c0 < a.qk) {
+        ob = static_cast<T*>(a.q) + c0;
+        ostr = a.qk;
+        nrm = a.qk_norm;
+    } else if (c0 < 2 * a.qk) {
+        ob = static_cast<T*>(a.k) + (c0 - a.qk);
+        ostr = a.qk;
+        nrm = a.qk_norm;
+    } else {
+        ob = static_cast<T*>(a.y) + (c0 - 2 * a.qk);
+        ostr = a.y_stride;
+    }
+    const int G = a.Dk / CG;   // lanes per q/k head
+    if (blockIdx.x == 0 && sT && act) {   // empty sequences keep their state
         for (int n = 0; n < a.N; ++n) {
             long bos, eos;
             seq_range(a.cu, n, a.T, bos, eos);
@@ -130,7 +164,7 @@ __global__ __launch_bounds__(NTH) void conv_kernel(ConvArgs a) {
 #pragma unroll
                 for (int e = 0; e < CG; ++e) win[k][e] = state_at<T, W>(a, n, c0 + e, k);
         }
-        float xv[CG], out[CG];
+        float xv[CG], out[CG], ss = 0.f;
         ld8(x + t * a.C + c0, xv);
 #pragma unroll
         for (int e = 0; e < CG; ++e) {
@@ -138,15 +172,24 @@ __global__ __launch_bounds__(NTH) void conv_kernel(ConvArgs a) {
 #pragma unroll
             for (int k = 0; k < W - 1; ++k) acc += w[k][e] * win[k][e];
             out[e] = a.silu ? silu(acc) : acc;
+            ss += out[e] * out[e];
         }
-        st8(y + t * a.C + c0, out);
+        if (a.qk_norm) {   // |head|^2 over its G lanes (every lane of the wave takes part)
+            ss = group_sum(ss, G);
+            if (nrm) {
+                const float r = 1.f / __builtin_sqrtf(ss + a.eps);
+#pragma unroll
+                for (int e = 0; e < CG; ++e) out[e] *= r;
+            }
+        }
+        if (act) st8(ob + t * ostr, out);
 #pragma unroll
         for (int k = 0; k < W - 2; ++k)
 #pragma unroll
             for (int e = 0; e < CG; ++e) win[k][e] = win[k + 1][e];
 #pragma unroll
         for (int e = 0; e < CG; ++e) win[W - 2][e] = xv[e];
-        if (t == eos - 1 && sT) {
+        if (t == eos - 1 && sT && act) {
 #pragma unroll
             for (int e = 0; e < CG; ++e)
 #pragma unroll

@@ -69,7 +69,10 @@ struct RecurrentArgs : PrefillArgs {
     float* trace;                   // may be null
 };
 
-// Short causal depthwise convolution (+ silu), validated on the host.
+// Short causal depthwise convolution (+ silu), validated on the host.  The prompt kernel
+// can also split its output into q, k and v (the first qk channels to q, the next qk to k,
+// the rest to y with a token stride of y_stride) and L2-normalise q and k per head of Dk
+// channels; the plain convolution is qk = 0, y_stride = C.
 struct ConvArgs {
     int B, T, N, C, W;
     int bf16;
@@ -81,6 +84,13 @@ struct ConvArgs {
     void* sT;                       // [N, C, W - 1], may be null; in place for a step
     const int32_t* cu;              // may be null
     void* y;
+    int qk;                         // q (and k) channels split off; 0: none
+    long y_stride;                  // y elements per token
+    int Dk;                         // channels per q/k head (the L2 norm's group)
+    int qk_norm;                    // 1: q, k -> x / sqrt(|x|^2 + eps) per head
+    float eps;
+    void* q;                        // [tokens, qk] when qk > 0
+    void* k;                        // [tokens, qk] when qk > 0
 };
 
 // The reverse pass of the token-by-token route: the forward's arguments, its state

@@ -395,6 +395,36 @@ dn_status dn_causal_conv(const dn_conv_shape* shape, const void* x, const float*
                          const int32_t* cu_seqlens, void* y, hipStream_t stream);
 
 /*
+ * dn_conv_qkv -- the whole prologue in front of the rule in one pass (the mutichung
+ * "DeltaNet" page, "DeltaNet Transformer" flowchart: Conv, then SiLU, then the L2 norm on
+ * the q and k branches, then the delta rule): the convolution of dn_causal_conv over
+ * x = [q | k | v] projections, [.., Hqk*Dk + Hqk*Dk + Hv*Dv] channels, its output split
+ * into q, k and v tensors in the layout dn_chunk_fwd reads, with q and k L2-normalised per
+ * head (x / sqrt(|x|^2 + eps), the normalisation of DN_QK_L2NORM) inside the same pass.
+ * x is read once and q, k, v written once; hand the results to dn_chunk_fwd without
+ * DN_QK_L2NORM.
+ *
+ *   shape          as dn_causal_conv, C == 2 Hqk Dk + Hv Dv (activation 1 for the flowchart)
+ *   split          heads and head sizes (below); Dk in {16, 32, 64, 128}, Dv a multiple of 8
+ *   x, weight, bias, initial_state, final_state, cu_seqlens   as dn_causal_conv
+ *   q, k           [B, T, Hqk, Dk] dtype, 16-byte aligned
+ *   v              [B, T, Hv, Dv] dtype, 16-byte aligned; none of q, k, v aliases x or another
+ * Errors: as dn_causal_conv; DN_ERR_INVALID_ARG also for a split that does not add up to C,
+ * eps negative or not finite; DN_ERR_UNSUPPORTED for Dk outside {16, 32, 64, 128}.
+ */
+typedef struct {
+    int32_t Hqk, Hv;       /* q/k heads and value heads                                      */
+    int32_t Dk, Dv;        /* head sizes                                                     */
+    int32_t qk_l2norm;     /* 1: q and k L2-normalised per head after the conv; 0: not       */
+    float eps;             /* the normalisation's epsilon (>= 0, finite)                     */
+} dn_qkv_split;
+
+dn_status dn_conv_qkv(const dn_conv_shape* shape, const dn_qkv_split* split, const void* x,
+                      const float* weight, const float* bias, const void* initial_state,
+                      void* final_state, const int32_t* cu_seqlens, void* q, void* k, void* v,
+                      hipStream_t stream);
+
+/*
  * dn_causal_conv_step -- one token per sequence (decode): shape->B = N sequences, T == 1;
  * x, y [N, C]; conv_state [N, C, W - 1] read and overwritten (shifted by one, x appended).
  * Errors: as dn_causal_conv.

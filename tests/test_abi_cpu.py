@@ -174,6 +174,38 @@ def test_causal_conv_rejects_aliasing_and_misalignment():
 
 
 
+@pytest.mark.parametrize("split,code", [
+    ((2, 2, 64, 64), dn.DN_ERR_INVALID_ARG),            # 2*2*64 + 2*64 = 384 != C
+    ((1, 1, 24, 16), dn.DN_ERR_UNSUPPORTED),            # Dk outside {16, 32, 64, 128}
+    ((1, 1, 16, 12), dn.DN_ERR_INVALID_ARG),            # Dv not a multiple of 8
+    ((0, 2, 16, 16), dn.DN_ERR_INVALID_ARG),            # no q/k heads
+])
+def test_conv_qkv_rejects_bad_splits(split, code):
+    """dn_conv_qkv's host checks: the split must add up to C, with supported head sizes."""
+    lib = dn.load_library()
+    p = ctypes.c_void_p(16)
+    s = _cshape(C=64)
+    sp = dn._QkvSplit(*split, 1, 1e-6)
+    assert lib.dn_conv_qkv(ctypes.byref(s), ctypes.byref(sp), p, p, None, None, None, None,
+                           ctypes.c_void_p(32), ctypes.c_void_p(48), ctypes.c_void_p(64), None) == code
+
+
+def test_conv_qkv_rejects_aliasing_eps_and_misalignment():
+    lib = dn.load_library()
+    p, a, b, c = (ctypes.c_void_p(v) for v in (16, 32, 48, 64))
+    s = _cshape(C=64)                                    # 2 * 1 * 16 + 2 * 16
+    ok = dn._QkvSplit(1, 2, 16, 16, 1, 1e-6)
+    args = lambda q, k, v: (ctypes.byref(s), ctypes.byref(ok), p, p, None, None, None, None, q, k, v, None)
+    assert lib.dn_conv_qkv(*args(p, b, c)) == dn.DN_ERR_INVALID_ARG          # q aliases x
+    assert lib.dn_conv_qkv(*args(a, a, c)) == dn.DN_ERR_INVALID_ARG          # q aliases k
+    assert lib.dn_conv_qkv(*args(ctypes.c_void_p(40), b, c)) == dn.DN_ERR_INVALID_ARG   # misaligned
+    for eps in (-1.0, float("inf"), float("nan")):
+        bad = dn._QkvSplit(1, 2, 16, 16, 1, eps)
+        assert lib.dn_conv_qkv(ctypes.byref(s), ctypes.byref(bad), p, p, None, None, None, None,
+                               a, b, c, None) == dn.DN_ERR_INVALID_ARG
+    assert lib.dn_conv_qkv(ctypes.byref(s), None, p, p, None, None, None, None, a, b, c, None) == dn.DN_ERR_INVALID_ARG
+
+
 def test_reverse_pass_host_checks():
     """dn_recurrent_bwd: a decay per key channel needs g, and the workspace query counts Dk
     floats of dg per token and head with that flag."""
