@@ -1,7 +1,7 @@
 """Benchmark of the delta-rule mixer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--decode-reps R] [--graph]
-    python bench.py --only prefill2|prefill3|prefill5 [--steps K] [--warmup W]
+    python bench.py --only prefill2|prefill3|prefill5|decode|conv|chunk_bwd1|chunk_bwd4 [--steps K]
 
 One step is one prefill call (dn_chunk_fwd) over the DeltaNet layer-prefill workload
 (B=4, H=16, T=2048, d_k=d_v=128, bf16 q/k/v, fp32 beta, no decay, zero initial state,
@@ -17,8 +17,9 @@ The two other full-size prefill workloads (gated GQA B2 T8192 16 -> 32 heads; 8 
 sequences of 32,768 tokens in all) are timed right after it, each warmed for about 20 ms
 of back-to-back calls and then timed with events around 10 calls, and each gets its own
 roofline block (algorithmic bytes and flops,
-rocprofv3 counters) under ``prefill_workloads``.  ``--only`` runs one of the three alone
-(for a rocprofv3 counter pass per workload).  The decode step (256 sequences x 32 heads,
+rocprofv3 counters) under ``prefill_workloads``.  ``--only`` runs one workload alone (a
+prefill workload, the gated decode step, the conv and the fused prologue, or the reverse
+pass at B1 or B4) for a rocprofv3 counter pass per workload.  The decode step (256 sequences x 32 heads,
 state updated in place) is timed with events around a loop of back-to-back steps and
 reported in the same line, and so is the chunkwise reverse pass (dn_chunk_bwd) on the gated
 H16 T2048 shape at B1 and B4 (20 calls between events, own roofline block under
@@ -181,6 +182,62 @@ def cpu_baseline(x, budget_s=12.0):
                       f"{el:.1f} s, fp64 token-by-token recurrence, OpenMP over (sequence, head)"}
 
 
+def only_part(what, dn, dev, reps, warmup):
+    """One workload of the line alone (for a rocprofv3 counter pass): the gated decode step,
+    the conv and the fused prologue on the layer shape, or the reverse pass at B1 / B4.
+    Returns the average time per call from HIP events on the launching stream."""
+    import numpy as np
+    import torch
+    from synth import make_case
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    calls = []
+    if what == "decode":
+        y = make_case(B=DECODE["N"], T=1, Hqk=DECODE["H"], Dk=DECODE["D"], dtype="bf16", g_scale=0.1,
+                      init_std=0.02, seed=0, decode=True)
+        q, k, v = to_dev(y.q)[:, 0], to_dev(y.k)[:, 0], to_dev(y.v)[:, 0]
+        b, g = to_dev(y.beta)[:, 0], to_dev(y.g)[:, 0]
+        st = [to_dev(y.init) for _ in range(2)]
+        out = torch.empty((y.B, y.Hv, y.Dv), dtype=torch.bfloat16, device=dev)
+        calls.append(("decode_kernel", lambda i: dn.decode_step(q, k, v, b, g, st[i % 2], out=out)))
+    elif what == "conv":
+        H, D, B, T = PREFILL["H"], PREFILL["D"], PREFILL["B"], PREFILL["T"]
+        rng = np.random.default_rng(3)
+        C = 3 * H * D
+        x = torch.from_numpy(rng.standard_normal((B, T, C)).astype(np.float32)).to(dev).to(torch.bfloat16)
+        w = torch.from_numpy((rng.standard_normal((C, 4)) / 2).astype(np.float32)).to(dev)
+        b = torch.zeros(C, dtype=torch.float32, device=dev)
+        calls.append(("conv_kernel (plain)", lambda i: dn.causal_conv(x, w, b)))
+        calls.append(("conv_kernel (split, head norm)", lambda i: dn.conv_qkv(x, w, b, H, H, D, D)))
+    else:
+        bb = 1 if what == "chunk_bwd1" else 4
+        T, H, D = PREFILL["T"], PREFILL["H"], PREFILL["D"]
+        xg = make_case(B=bb, T=T, Hqk=H, Dk=D, dtype="bf16", g_scale=0.1, seed=0)
+        gq, gk, gv, gb, gg = (to_dev(a_) for a_ in (xg.q, xg.k, xg.v, xg.beta, xg.g))
+        gdo = torch.randn((bb, T, H, D), device=dev).to(torch.bfloat16)
+        gws = torch.empty(dn.chunk_bwd_workspace_bytes(bb, T, H, H, D, D, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        calls.append((f"chunk_bwd B{bb}", lambda i: dn.chunk_bwd(gq, gk, gv, gb, gg, None, gdo, workspace=gws)))
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    for name, fn in calls:
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"us_per_call": e0.elapsed_time(e1) * 1e3 / reps, "calls": reps}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,7 +248,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time a HIP-graph replay of the K steps instead of the eager launch loop")
-    ap.add_argument("--only", choices=["prefill2", "prefill3", "prefill5"], default=None,
+    ap.add_argument("--only", choices=["prefill2", "prefill3", "prefill5", "decode", "conv",
+                                       "chunk_bwd1", "chunk_bwd4"], default=None,
                     help="run only this prefill workload (a rocprofv3 counter pass per workload) "
                          "and print its timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -266,6 +324,10 @@ def main():
         del zsets, zcu
         return dict(workload=PREFILL_WHAT[cfg], **blk)
 
+    if args.only in ("decode", "conv", "chunk_bwd1", "chunk_bwd4"):
+        print(json.dumps({"only": args.only, **only_part(args.only, dn, dev, args.steps, args.warmup)}),
+              flush=True)
+        return
     if args.only:
         cfg = int(args.only[-1])
         r = time_prefill_workload(cfg, args.steps, warmup=args.warmup)
@@ -573,7 +635,8 @@ def main():
                          "algorithmic_bytes": gbytes,
                          "traffic": load_traffic(f"chunk_bwd_B{bb}_bytes_per_call")},
             "mfma": {"algorithmic_flops": gflops, "tflops": gflops / (gb_us * 1e-6) / 1e12,
-                     "frac_of_bf16_peak": gflops / (gb_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+                     "frac_of_bf16_peak": gflops / (gb_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                     "counters": load_traffic(f"chunk_bwd_B{bb}_mfma")},
         }
         del gq, gk, gv, gb, gg, gdo, gws
 
