@@ -339,7 +339,7 @@ struct alignas(16) CarrySmem {
     __bf16 Tt[2][BC][P64], P[2][BC][P64];
     __bf16 dDt[BS][P64];           // dDelta^T
     __bf16 dXt[BS][P64];           // dX^T
-    __bf16 dM[BD][P32];            // the slice of dM' (the gradient of the state after the chunk)
+    __bf16 dMt[BS][P128];          // the slice of dM' (the gradient of the state after the chunk), transposed
     float tail[2][BC], sod[2][BC], bx[2][BC], egl[2][4];
 };
 
@@ -400,8 +400,10 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
         const uint4* tp = tp_head + ((cid0 + c) * a.Hv + h) * (2L * BC * BC / 8);
         f.t = tp[0];
         f.p = tp[BC * BC / 8];
-        f.beta = ld32(b_rs, sc_off, cs);
-        f.g = ld32(g_rs, sc_off, cs);
+        if (wave == 0) {
+            f.beta = ld32(b_rs, sc_off, cs);
+            f.g = ld32(g_rs, sc_off, cs);
+        }
     };
     auto put_in = [&](const CarryIn& f, int b) {
 #pragma unroll
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
     }
     auto put_dm = [&]() {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) put_tile(&sm.dM[0][0], P32, 2 * (wave >> 1) + u, dmj, dm[u], l16, q16);
+        for (int u = 0; u < 2; ++u) put_tile_t(&sm.dMt[0][0], P128, 2 * (wave >> 1) + u, dmj, dm[u], l16, q16);
     };
 
     CarryIn f;
@@ -451,16 +453,11 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
     const int ti = wave >> 1, tj = wave & 1;   // this wave's 16 x 16 tile of a 64 x 32 product
     for (int c = nc - 1; c >= 0; --c) {
         const int b = c & 1;
-        {   // dM' of chunk c to the workspace (the gradient kernel's input)
-            const auto ds_rs = rsrc(a.dstates + ((cid0 + c) * a.Hv + h) * (long)BD * BD, BD * BD * 4);
+        {   // dM' of chunk c to the workspace (the gradient kernel's input), in 16 x 16 tiles of
+            // the accumulator layout like the chunk-start states: one 16-byte store per tile
+            float* dst = a.dstates + ((cid0 + c) * a.Hv + h) * (long)BD * BD + (2 * slice + dmj) * 256 + 4 * lane;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int ki = 2 * (wave >> 1) + u;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dm[u][e]), ds_rs,
-                                                          ((16 * ki + 4 * q16 + e) * BD + j0 + 16 * dmj + l16) * 4, 0, 0);
-            }
+            for (int u = 0; u < 2; ++u) *reinterpret_cast<f32x4*>(dst + (2 * (wave >> 1) + u) * 8 * 256) = dm[u];
         }
         // ---------------------------- dDelta = scale P^T dO + diag(tail) K dM', stored transposed
         {
@@ -471,14 +468,28 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
                                                   frag_c(&sm.dO[b][0][0], P32, 16 * tj, k0, l16, q16), pd);
 #pragma unroll
             for (int k0 = 0; k0 < BD; k0 += 32)
-                kd = mma16(frag_r(&sm.K[b][0][0], P128, 16 * ti, k0, l16, q16), frag_c(&sm.dM[0][0], P32, 16 * tj, k0, l16, q16), kd);
+                kd = mma16(frag_r(&sm.K[b][0][0], P128, 16 * ti, k0, l16, q16), frag_r(&sm.dMt[0][0], P128, 16 * tj, k0, l16, q16), kd);
             f32x4 dd;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dd[e] = sc * pd[e] + sm.tail[b][16 * ti + 4 * q16 + e] * kd[e];
             put_tile_t(&sm.dDt[0][0], P64, ti, tj, dd, l16, q16);
         }
         __syncthreads();
-        // ------------------------------ dX = -diag(beta e^gamma) T^T dDelta, stored transposed
+        // ------------------------------ dX = -diag(beta e^gamma) T^T dDelta, stored transposed;
+        // scale Q^T diag(e^gamma) dO of this wave's dM tiles (no carry in it) alongside
+        f32x4 qd[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ki = 2 * (wave >> 1) + u;
+            qd[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32) {
+                bf16x8 od = frag_c(&sm.dO[b][0][0], P32, 16 * dmj, k0, l16, q16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) od[e] = (__bf16)((float)od[e] * sm.sod[b][k0 + 8 * q16 + e]);
+                qd[u] = mma16(frag_c(&sm.Q[b][0][0], P128, 16 * ki, k0, l16, q16), od, qd[u]);
+            }
+        }
         {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -496,16 +507,11 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int ki = 2 * (wave >> 1) + u;
-                f32x4 acc = dm[u] * gl;
+                f32x4 acc = dm[u] * gl + qd[u];
 #pragma unroll
-                for (int k0 = 0; k0 < BC; k0 += 32) {
-                    bf16x8 od = frag_c(&sm.dO[b][0][0], P32, 16 * dmj, k0, l16, q16);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) od[e] = (__bf16)((float)od[e] * sm.sod[b][k0 + 8 * q16 + e]);
-                    acc = mma16(frag_c(&sm.Q[b][0][0], P128, 16 * ki, k0, l16, q16), od, acc);
+                for (int k0 = 0; k0 < BC; k0 += 32)
                     acc = mma16(frag_c(&sm.K[b][0][0], P128, 16 * ki, k0, l16, q16),
                                 frag_r(&sm.dXt[0][0], P64, 16 * dmj, k0, l16, q16), acc);
-                }
                 dm[u] = acc;
             }
         }
@@ -538,7 +544,7 @@ struct alignas(16) GradSmem {
     __bf16 V[BC][P32], dO[BC][P32];   // one 32-column slice of V and dO
     __bf16 Dl[BC][P32], dR[BC][P32];  // Delta and dR of the slice
     __bf16 Rt[BS][P64], dDt[BS][P64]; // R^T and dDelta^T of the slice
-    __bf16 M[BD][P32], dM[BD][P32];   // the slice of M and of dM'
+    __bf16 Mt[BS][P128], dMt[BS][P128];   // the slice of M and of dM', transposed
     float beta[BC], gam[BC], eg[BC], tail[BC];
     // per-row partial sums in fixed slots (summed in order at a head's end)
     float vdr[BC][8];              // V . dR, per (slice, column block)
@@ -550,7 +556,8 @@ struct alignas(16) GradSmem {
 };
 
 // one slice's inputs in registers: piece t & 255 of V (t < 256) or dO (t >= 256) (row =
-// piece / 4), pieces t and t + 512 of M's and dM''s slices (128 rows x 8 float4)
+// piece / 4), pieces t and t + 512 of M's and dM''s slices: the slice's 16 tiles (8 key
+// blocks x 2 column blocks) of 64 lanes x float4, piece p = tile (p >> 6), lane p & 63
 struct GradIn {
     uint4 vo;
     float4 m[2], d[2];
@@ -599,14 +606,14 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
     const uint32_t vo_off = ((uint32_t)vrow * v_tok + (tid & 3) * 8) * 2;
     uint32_t m_off[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int pc = tid + NTB * u;
-        m_off[u] = (uint32_t)((pc >> 3) * BD + (pc & 7) * 4) * 4;
+    for (int u = 0; u < 2; ++u) {   // tile (key block kb, column block 2 sl + cb) at (8 kb + 2 sl + cb) 256 floats
+        const int pc = tid + NTB * u, tt = pc >> 6;
+        m_off[u] = (uint32_t)(((tt >> 1) * 8 + (tt & 1)) * 256 + 4 * (pc & 63)) * 4;
     }
     auto fetch = [&](int g, int sl, GradIn& f) {
         const int h = hq * grp + g, j0 = sl * BS;
         f.vo = ld128(vo_rs, vo_off, (uint32_t)(h * BD + j0) * 2);
-        const uint32_t so = (uint32_t)(h * BD * BD + j0) * 4;
+        const uint32_t so = (uint32_t)(h * BD * BD + 2 * sl * 256) * 4;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f.m[u] = __builtin_bit_cast(float4, ld128(m_rs, m_off[u], so));
@@ -674,11 +681,12 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
             const int tf = fresh(tid), vr = (tf & 255) >> 2;
             *reinterpret_cast<uint4*>(tf < 256 ? &sm.V[vr][(tf & 3) * 8] : &sm.dO[vr][(tf & 3) * 8]) = f.vo;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int pc = tf + NTB * u, mr = pc >> 3, mc = (pc & 7) * 4;
-                *reinterpret_cast<uint2*>(&sm.M[mr][mc]) =
+            for (int u = 0; u < 2; ++u) {   // four keys of one column: 8 bytes of the transposed tile
+                const int pc = tf + NTB * u, tt = pc >> 6, ln = pc & 63;
+                const int col = 16 * (tt & 1) + (ln & 15), key = 16 * (tt >> 1) + 4 * (ln >> 4);
+                *reinterpret_cast<uint2*>(&sm.Mt[col][key]) =
                     make_uint2(pack_bf16x2(f.m[u].x, f.m[u].y), pack_bf16x2(f.m[u].z, f.m[u].w));
-                *reinterpret_cast<uint2*>(&sm.dM[mr][mc]) =
+                *reinterpret_cast<uint2*>(&sm.dMt[col][key]) =
                     make_uint2(pack_bf16x2(f.d[u].x, f.d[u].y), pack_bf16x2(f.d[u].z, f.d[u].w));
                 if (GATED)
                     mdm_t += f.m[u].x * f.d[u].x + f.m[u].y * f.d[u].y + f.m[u].z * f.d[u].z + f.m[u].w * f.d[u].w;
@@ -695,8 +703,8 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
 #pragma unroll
                 for (int k0 = 0; k0 < BD; k0 += 32) {
                     const bf16x8 kf = frag_r(&sm.K[0][0], P128, 16 * ti, k0, l16, q16);
-                    x = mma16(kf, frag_c(&sm.M[0][0], P32, 16 * tj, k0, l16, q16), x);
-                    kd = mma16(kf, frag_c(&sm.dM[0][0], P32, 16 * tj, k0, l16, q16), kd);
+                    x = mma16(kf, frag_r(&sm.Mt[0][0], P128, 16 * tj, k0, l16, q16), x);
+                    kd = mma16(kf, frag_r(&sm.dMt[0][0], P128, 16 * tj, k0, l16, q16), kd);
                 }
 #pragma unroll
                 for (int k0 = 0; k0 < BC; k0 += 32)
@@ -759,8 +767,8 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
                 }
             }
             {
-                const bf16x8 mf = frag_r(&sm.M[0][0], P32, 16 * wave, 0, l16, q16);
-                const bf16x8 df = frag_r(&sm.dM[0][0], P32, 16 * wave, 0, l16, q16);
+                const bf16x8 mf = frag_c(&sm.Mt[0][0], P128, 16 * wave, 0, l16, q16);
+                const bf16x8 df = frag_c(&sm.dMt[0][0], P128, 16 * wave, 0, l16, q16);
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4) {
                     qa[t4] = mma16(frag_r(&sm.dO[0][0], P32, 16 * t4, 0, l16, q16), mf, qa[t4]);

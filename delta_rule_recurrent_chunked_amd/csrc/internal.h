@@ -122,8 +122,8 @@ struct ChunkBwdArgs : PrefillArgs {
     const void* dout;               // [tokens, Hv, Dv] bf16
     const float* dfinal;            // [N, Hv, Dk, Dv] or null
     long ncid;                      // chunk numbers (chunk_id_bound)
-    float* states;                  // [ncid, Hv, Dk, Dv]
-    float* dstates;                 // [ncid, Hv, Dk, Dv]
+    float* states;                  // [ncid, Hv, 8 x 8 tiles of 16 x 16 in the accumulator layout]
+    float* dstates;                 // the same layout
     void* tp;                       // [ncid, Hv, 2, 64, 64] bf16: T^T, then P
     float* dq;                      // [tokens, Hqk, Dk]
     float* dk;                      // [tokens, Hqk, Dk]

@@ -494,9 +494,12 @@ __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f1
 }
 
 // -------------------------------------------------------------------------- kernel
-// STATES: the chain waves also write the state at every chunk start (fp32, key-major, at
-// a.ws + chunk_id_base(n) + chunk), the input of the chunkwise reverse pass, and the
-// output waves skip O (that launch needs only the states).
+// STATES: the chain waves also write the state at every chunk start (fp32, for chunk number
+// chunk_id_base(n) + chunk and value head h at a.ws + (number Hv + h) Dk Dv, as 8 x 8 tiles of
+// 16 keys x 16 columns in the accumulator layout: tile (key block kb, column block cb) at
+// (8 kb + cb) 256 floats, lane l's four entries (keys 16 kb + 4 (l >> 4) + e, column
+// 16 cb + (l & 15)) at 4 l, one 16-byte store each), the input of the chunkwise reverse pass;
+// the output waves skip O (that launch needs only the states).
 template <bool GATED, bool NORM, bool STATES = false>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void fused_kernel(PrefillArgs a) {
     __shared__ FusedSmem sm;
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         __syncthreads();
         float* st_out = nullptr;   // STATES: this chain wave's columns of chunk 0's start state
         if (STATES) st_out = static_cast<float*>(a.ws) + ((long)chunk_id_base(a, w.n) * a.Hv + w.h) * FD * FD +
-                             w.j0 + jc + l16;
+                             ((w.j0 + jc) / 16) * 256 + 4 * lane;
         for (int j = 0; j < nph; ++j) {
             const bool live = j < nc;
             const float* s = &sm.sc[j % 3][0][0];
@@ -579,9 +582,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             if (STATES && live) {
                 float* dst = st_out + (long)j * a.Hv * FD * FD;
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q16 + e) * FD] = M[mt][e];
+                for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 8 * 256) = M[mt];
             }
             if (live) {
                 // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
