@@ -566,8 +566,8 @@ struct GradIn {
 template <bool GATED>
 __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
     __shared__ GradSmem sm;
+    // (every phase re-derives its lane offsets l16 = lane & 15, q16 = lane >> 4 with fresh())
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, q16 = lane >> 4;
     const int hq = (int)(blockIdx.x % a.Hqk);
     const long cid = blockIdx.x / a.Hqk;
     int n;
@@ -942,17 +942,34 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
             }
         }
     }
-    // dq and dk of the q/k head
+    // dq and dk of the q/k head, staged through LDS (the slice buffers, free after the last
+    // head) so that each lane stores 16 bytes of a row; rows past the end are dropped by the
+    // range check
+    float (*stage)[BD + 4] = reinterpret_cast<float (*)[BD + 4]>(&sm.V[0][0]);
+    static_assert(sizeof(float) * BC * (BD + 4) <= sizeof(sm.V) + sizeof(sm.dO) + sizeof(sm.Dl) + sizeof(sm.dR) +
+                  sizeof(sm.Rt) + sizeof(sm.dDt) + sizeof(sm.Mt) + sizeof(sm.dMt), "dq/dk stage");
+    const uint32_t kq_tokf = (uint32_t)a.Hqk * BD;
+    const uint32_t kq_rec = ((uint32_t)(rows - 1) * kq_tokf + BD) * 4;
+    const auto dq_rs = rsrc(a.dq + (t0 * a.Hqk + hq) * BD, kq_rec);
+    const auto dk_rs = rsrc(a.dk + (t0 * a.Hqk + hq) * BD, kq_rec);
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int m = 0; m < 2; ++m) {
+        if (m) __syncthreads();   // dq's stage is read
+        {
+            const int ln = fresh(lane), l16 = ln & 15, q16 = ln >> 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * t4 + 4 * q16 + e;
-            if (row < rows) {
-                const long o = ((t0 + row) * a.Hqk + hq) * BD + 16 * wave + l16;
-                a.dq[o] = dqg[t4][e];
-                a.dk[o] = dkg[t4][e];
-            }
+            for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) stage[16 * t4 + 4 * q16 + e][16 * wave + l16] = (m ? dkg : dqg)[t4][e];
+        }
+        __syncthreads();
+        const int tf = fresh(tid);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int pc = tf + NTB * u, row = pc >> 5, c4 = (pc & 31) * 4;
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row][c4]);
+            __builtin_amdgcn_raw_buffer_store_b128(v, m ? dk_rs : dq_rs, ((uint32_t)row * kq_tokf + c4) * 4, 0, 0);
         }
     }
 }
