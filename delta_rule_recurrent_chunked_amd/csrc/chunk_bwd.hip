@@ -355,10 +355,23 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
     __shared__ CarrySmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q16 = lane >> 4;
-    const int slice = blockIdx.x % BNS;
-    const int nh = blockIdx.x / BNS;
+    // workgroup -> (sequence, value head, slice): when the count of (sequence, q/k head)
+    // pairs is a multiple of 8, the slices of the value heads of one q/k head run one after
+    // another on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share that
+    // head's K and Q through the XCD's L2
+    const int grp = a.Hv / a.Hqk, qchains = a.N * a.Hqk;
+    int slice, nh;
+    if ((qchains & 7) == 0) {
+        const int y = blockIdx.x >> 3, t = y / BNS;
+        const int qc = (blockIdx.x & 7) + 8 * (t / grp);
+        slice = y % BNS;
+        nh = (qc / a.Hqk) * a.Hv + (qc % a.Hqk) * grp + t % grp;
+    } else {
+        slice = blockIdx.x % BNS;
+        nh = blockIdx.x / BNS;
+    }
     const int h = nh % a.Hv, n = nh / a.Hv;
-    const int hq = h / (a.Hv / a.Hqk);
+    const int hq = h / grp;
     const int j0 = slice * BS;
     long bos, eos;
     seq_range(a.cu, n, a.T, bos, eos);

@@ -506,16 +506,20 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q16 = lane >> 4;
 
-    // Workgroup -> (chain = sequence * Hv + head, slice).  When the chain count is a
-    // multiple of 8, the slices of one chain land on one XCD (workgroups are dealt to
-    // the 8 XCDs round-robin), so they share the chain's K and Q through that XCD's L2.
-    const int chains = a.N * a.Hv;
+    // Workgroup -> (chain = sequence * Hv + head, slice).  When the count of (sequence, q/k
+    // head) pairs is a multiple of 8, all the slices of all the value heads of one q/k head
+    // land on one XCD (workgroups are dealt to the 8 XCDs round-robin), one after another,
+    // so they share that q/k head's K and Q through the XCD's L2.
+    const int grp = a.Hv / a.Hqk;
+    const int qchains = a.N * a.Hqk;
     const int b = blockIdx.x;
     int chain, slice;
-    if ((chains & 7) == 0) {
-        const int y = b >> 3;
+    if ((qchains & 7) == 0) {
+        const int y = b >> 3;                      // the workgroup's turn on its XCD
         slice = y % NSL;
-        chain = (b & 7) + 8 * (y / NSL);
+        const int t = y / NSL;
+        const int qc = (b & 7) + 8 * (t / grp);    // sequence * Hqk + q/k head
+        chain = (qc / a.Hqk) * a.Hv + (qc % a.Hqk) * grp + t % grp;
     } else {
         slice = b % NSL;
         chain = b / NSL;
