@@ -175,12 +175,12 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
 
 def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: torch.dtype,
                     num_seqs: Optional[int] = None, chunk_size: int = 64,
-                    g_per_key: bool = False) -> int:
-    """Device workspace (bytes) ``dn_chunk_fwd`` needs for these sizes (only the matrix-core
-    path for a log decay per key channel uses one)."""
+                    g_per_key: bool = False, qk_l2norm: bool = False) -> int:
+    """Device workspace (bytes) ``dn_chunk_fwd`` needs for these sizes (only the two-kernel
+    matrix-core paths use one: a log decay per key channel at d_k = 128, and d = 64)."""
     s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
-               DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0)
-    s.flags = DN_GATE_PER_KEY if g_per_key else 0
+               DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0,
+               *_flags(qk_l2norm, 1e-6, g_per_key))
     return int(load_library().dn_chunk_fwd_workspace_bytes(ctypes.byref(s)))
 
 
@@ -194,7 +194,7 @@ def chunk_bwd_workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: in
 
 
 _PATHS = {-1: "invalid", 0: "fused", 1: "channel_gate_two_kernels", 2: "channel_gate_one_kernel",
-          3: "vector"}
+          3: "vector", 4: "two_kernels"}
 
 
 def chunk_fwd_path(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: torch.dtype,
@@ -202,8 +202,9 @@ def chunk_fwd_path(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: t
                    qk_l2norm: bool = False, workspace_bytes: Optional[int] = None) -> str:
     """Which kernels ``chunk_fwd`` runs for these sizes: "fused" (one matrix-core kernel),
     "channel_gate_two_kernels" / "channel_gate_one_kernel" (per-key-channel gates on the
-    matrix cores, with / without enough workspace), "vector" (the vector-ALU chunked
-    kernel, about 100x slower), or "invalid".  ``workspace_bytes`` defaults to what
+    matrix cores, with / without enough workspace), "two_kernels" (d = 64 on the matrix
+    cores: T and P per chunk, then the chunk chain; needs the workspace), "vector" (the
+    vector-ALU chunked kernel, about 100x slower), or "invalid".  ``workspace_bytes`` defaults to what
     :func:`chunk_fwd` allocates itself."""
     s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
                DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0,

@@ -48,287 +48,15 @@
 // stored transposed, four values of a lane in one 8-byte write.
 #include <mutex>
 
-#include "internal.h"
-#include "mfma_ops.h"
+#include "chunk_ops.h"
 
 namespace dn {
 namespace {
+using namespace ck;
 
-constexpr int BC = 64;             // chunk
 constexpr int BD = 128;            // Dk = Dv
-constexpr int BS = 32;             // state columns per slice
 constexpr int BNS = BD / BS;       // slices
-constexpr int P128 = BD + 16;      // bf16 pitches (16-byte reads of 16 rows conflict-free)
-constexpr int P64 = BC + 16;
-constexpr int P32 = BS + 16;
-constexpr int ADP = 136;           // A's diagonal 16x16 blocks, 120 packed fp16 entries + spare
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-// --------------------------------------------------------------------- fragments
-__device__ __forceinline__ bf16x8 frag_r(const __bf16* S, int pitch, int r0, int k0, int l16, int q16) {
-    return ld8(S + (r0 + l16) * pitch + k0 + 8 * q16);
-}
-__device__ __forceinline__ bf16x8 frag_c(const __bf16* S, int pitch, int c0, int k0, int l16, int q16) {
-    const __bf16* p = S + (k0 + 8 * q16 + (l16 >> 2)) * pitch + c0 + 4 * (l16 & 3);
-    return cat(trld(p), trld(p + 4 * pitch));
-}
-__device__ __forceinline__ bf16x8 scale_r(bf16x8 x, float f) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * f);
-    return x;
-}
-// an accumulator tile C[16 i + 4 q16 + e][16 j + l16] to a bf16 row-major matrix
-__device__ __forceinline__ void put_tile(__bf16* S, int pitch, int i, int j, const f32x4& c, int l16, int q16) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) S[(16 * i + 4 * q16 + e) * pitch + 16 * j + l16] = (__bf16)c[e];
-}
-// the same tile transposed (S[16 j + l16][16 i + 4 q16 + e]): one 8-byte write per lane
-__device__ __forceinline__ void put_tile_t(__bf16* S, int pitch, int i, int j, const f32x4& c, int l16, int q16) {
-    st4(S + (16 * j + l16) * pitch + 16 * i + 4 * q16, c[0], c[1], c[2], c[3]);
-}
-// DPP lane moves within rows of 16 lanes (every lane has a source)
-template <int CTRL>
-__device__ __forceinline__ float dpp16(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-// sum over the 16 lanes of one q16 group (the tile's columns) of each of the lane's 4 rows:
-// lane ^ 1, lane ^ 2 (quad permutes), then the 8- and 16-lane mirrors, in every lane
-__device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float x = v[e];
-        x += dpp16<0xB1>(x);
-        x += dpp16<0x4E>(x);
-        x += dpp16<0x141>(x);
-        x += dpp16<0x140>(x);
-        v[e] = x;
-    }
-    return v;
-}
-// x as a value the compiler cannot see through: addresses derived from it are computed where
-// they are used instead of being hoisted out of loops and held in registers
-__device__ __forceinline__ int fresh(int x) {
-    __asm__ volatile("" : "+v"(x));
-    return x;
-}
-// sum over the wave, the same value in every lane: the four 16-lane row sums, read out and
-// added in row order
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp16<0xB1>(x);
-    x += dpp16<0x4E>(x);
-    x += dpp16<0x141>(x);
-    x += dpp16<0x140>(x);
-    const int b = __builtin_bit_cast(int, x);
-    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
-           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
-}
-// x moved by a DPP control; lanes with no source (or rows outside row_mask) get 0
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_or0(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
-}
-// gamma: inclusive scan of g over a chunk on one wave (lane = row), by DPP: shifts right by
-// 1, 2, 4, 8 lanes within each 16-lane row, then lane 15 of each row added into the next row
-// and lane 31 into the upper two rows; gl = gamma of row 63
-__device__ __forceinline__ float gamma_scan(float g, float& gl) {
-    g += dpp_or0<0x111, 0xf>(g);   // row_shr:1
-    g += dpp_or0<0x112, 0xf>(g);   // row_shr:2
-    g += dpp_or0<0x114, 0xf>(g);   // row_shr:4
-    g += dpp_or0<0x118, 0xf>(g);   // row_shr:8
-    g += dpp_or0<0x142, 0xa>(g);   // row_bcast:15 into rows 1 and 3
-    g += dpp_or0<0x143, 0xc>(g);   // row_bcast:31 into rows 2 and 3
-    gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 63));
-    return g;
-}
-// lower tile u < 10 of a 64 x 64 matrix in 16 x 16 blocks: (ri, ci), ci <= ri
-__device__ __forceinline__ void lower_tile(int u, int& ri, int& ci) {
-    ri = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
-    ci = u - ri * (ri + 1) / 2;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4(x[0], x[1], x[2], x[3]);
-}
-__device__ __forceinline__ float ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-
-// chunk number cid -> sequence n, chunk c of it, the sequence's first token and length;
-// false for a number no chunk uses
-__device__ __forceinline__ bool chunk_of_id(const ChunkBwdArgs& a, long cid, int& n, long& c, long& bos, long& L) {
-    if (a.cu) {   // the last sequence whose first chunk number is <= cid (strictly increasing)
-        int lo = 0, hi = a.N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (chunk_id_base(a, mid) <= cid) lo = mid; else hi = mid - 1;
-        }
-        n = lo;
-    } else {
-        n = (int)(cid / ((a.T + BC - 1) / BC));
-    }
-    long eos;
-    seq_range(a.cu, n, a.T, bos, eos);
-    L = eos - bos;
-    c = cid - chunk_id_base(a, n);
-    return c * BC < L;
-}
-
-// ======================================================= 2. T^T and P per (chunk, head)
-constexpr int NTP = 256;
-
-struct alignas(16) PrepSmem {
-    __bf16 K[BC][P128], Q[BC][P128];
-    __bf16 Tt[BC][P64];            // T^T, T = (I + A)^-1 lower triangular
-    __bf16 P[BC][P64];             // P = lower(D o Q K^T)
-    __bf16 G[BC][P64];             // D o K K^T, strictly lower
-    _Float16 Ad[4][ADP];           // A's diagonal blocks (strictly lower, packed by rows)
-    float beta[BC], gam[BC];
-};
-
-__global__ __launch_bounds__(NTP, 2) void chunk_tp_kernel(ChunkBwdArgs a) {
-    __shared__ PrepSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, q16 = lane >> 4;
-    const int h = (int)(blockIdx.x % a.Hv);
-    const long cid = blockIdx.x / a.Hv;
-    int n;
-    long c, bos, L;
-    if (!chunk_of_id(a, cid, n, c, bos, L)) return;
-    const int hq = h / (a.Hv / a.Hqk);
-    const long t0 = bos + c * BC;
-    const int rows = (int)min((long)BC, L - c * BC);
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-
-    for (int pc = tid; pc < BC * 16; pc += NTP) {   // K and Q, rows past the end zero
-        const int row = pc >> 4, cg = pc & 15;
-        uint4 kv = z4, qv = z4;
-        if (row < rows) {
-            const long off = ((t0 + row) * a.Hqk + hq) * BD + cg * 8;
-            kv = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.k) + off);
-            qv = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.q) + off);
-        }
-        *reinterpret_cast<uint4*>(&sm.K[row][cg * 8]) = kv;
-        *reinterpret_cast<uint4*>(&sm.Q[row][cg * 8]) = qv;
-    }
-    // the blocks above the diagonal of P and G, and below it of T^T, stay zero
-    for (int i = tid; i < BC * P64 / 8; i += NTP) {
-        reinterpret_cast<uint4*>(&sm.Tt[0][0])[i] = z4;
-        reinterpret_cast<uint4*>(&sm.P[0][0])[i] = z4;
-        reinterpret_cast<uint4*>(&sm.G[0][0])[i] = z4;
-    }
-    if (wave == 0) {
-        const bool ok = lane < rows;
-        const long s = (t0 + lane) * a.Hv + h;
-        float gl;
-        sm.gam[lane] = gamma_scan(ok && a.g ? a.g[s] : 0.f, gl);
-        sm.beta[lane] = ok ? a.beta[s] : 0.f;
-    }
-    __syncthreads();
-
-    // 20 lower tiles (incl. the diagonal): t < 10 of D o K K^T (strictly lower), t >= 10 of P
-    for (int t = wave; t < 20; t += NTP / 64) {
-        int ri, ci;
-        lower_tile(t % 10, ri, ci);
-        const __bf16* A = t < 10 ? &sm.K[0][0] : &sm.Q[0][0];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k0 = 0; k0 < BD; k0 += 32)
-            acc = mma16(frag_r(A, P128, 16 * ri, k0, l16, q16), frag_r(&sm.K[0][0], P128, 16 * ci, k0, l16, q16), acc);
-        const int col = 16 * ci + l16;
-        const float gc = sm.gam[col];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * ri + 4 * q16 + e;
-            const bool keep = t < 10 ? col < row : col <= row;
-            acc[e] = keep ? __expf(fminf(sm.gam[row] - gc, 0.f)) * acc[e] : 0.f;
-        }
-        put_tile(t < 10 ? &sm.G[0][0] : &sm.P[0][0], P64, ri, ci, acc, l16, q16);
-        if (t < 10 && ri == ci) {   // A's diagonal block ri in fp16, strictly lower, packed
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int lr = 4 * q16 + e, lc = l16;
-                if (lc < lr) sm.Ad[ri][lr * (lr - 1) / 2 + lc] = (_Float16)(sm.beta[16 * ri + lr] * acc[e]);
-            }
-        }
-    }
-    __syncthreads();
-
-    // T = (I + A)^-1 on wave 0, stored transposed
-    if (wave == 0) {
-        __bf16 (*Tt)[P64] = sm.Tt;
-        {   // the four 16x16 diagonal blocks by forward substitution (lane = block, column):
-            // column cc of T_bb is row cc of T^T_bb, written as two 16-byte pieces
-            const int b = q16, cc = l16;
-            f16x8 ap[15];
-#pragma unroll
-            for (int g = 0; g < 15; ++g) ap[g] = *reinterpret_cast<const f16x8*>(&sm.Ad[b][8 * g]);
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = r == cc ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < 15; ++m)
-#pragma unroll
-                for (int r = m + 1; r < 16; ++r) {
-                    const int idx = r * (r - 1) / 2 + m;
-                    x[r] = __builtin_fmaf(-(float)ap[idx >> 3][idx & 7], x[m], x[r]);
-                }
-            bf16x8 lo8, hi8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lo8[e] = (__bf16)x[e];
-                hi8[e] = (__bf16)x[8 + e];
-            }
-            *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b]) = lo8;
-            *reinterpret_cast<bf16x8*>(&Tt[16 * b + cc][16 * b + 8]) = hi8;
-        }
-        wave_lds_order();
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const bool lo = q16 < 2;   // k = 16 padded to the instruction's 32
-        // level 1: T21 = -T22 (A21 T11) within each 32x32 diagonal block (base 0, 32);
-        // T's block (b + 1, b) is T^T's block (b, b + 1)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const int base = 32 * hb;
-            const bf16x8 af = lo ? scale_r(frag_r(&sm.G[0][0], P64, base + 16, base, l16, q16),
-                                           sm.beta[base + 16 + l16]) : zero8();
-            const bf16x8 bf = lo ? frag_r(&Tt[0][0], P64, base, base, l16, q16) : zero8();
-            const f32x4 X1 = mma16(af, bf, z);
-            const bf16x8 tf = lo ? frag_c(&Tt[0][0], P64, base + 16, base + 16, l16, q16) : zero8();
-            const f32x4 Y1 = mma16(tf, acc_to_b(X1, z), z);
-            st4(&Tt[base + l16][base + 16 + 4 * q16], -Y1[0], -Y1[1], -Y1[2], -Y1[3]);
-        }
-        wave_lds_order();
-        // level 2: T_BL = -T_BR (A_BL T_TL), 32 x 32 blocks
-        f32x4 X2[2][2];
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int tj = 0; tj < 2; ++tj)
-                X2[ti][tj] = mma16(scale_r(frag_r(&sm.G[0][0], P64, 32 + 16 * ti, 0, l16, q16), sm.beta[32 + 16 * ti + l16]),
-                                   frag_r(&Tt[0][0], P64, 16 * tj, 0, l16, q16), z);
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int tj = 0; tj < 2; ++tj) {
-                const f32x4 Y2 = mma16(frag_c(&Tt[0][0], P64, 32 + 16 * ti, 32, l16, q16),
-                                       acc_to_b(X2[0][tj], X2[1][tj]), z);
-                st4(&Tt[16 * tj + l16][32 + 16 * ti + 4 * q16], -Y2[0], -Y2[1], -Y2[2], -Y2[3]);
-            }
-    }
-    __syncthreads();
-
-    __bf16* out = static_cast<__bf16*>(a.tp) + (cid * a.Hv + h) * (2L * BC * BC);
-    for (int pc = tid; pc < 2 * BC * 8; pc += NTP) {
-        const int m = pc >> 9, r = (pc >> 3) & 63, cg = pc & 7;
-        const __bf16* src = m ? &sm.P[r][cg * 8] : &sm.Tt[r][cg * 8];
-        *reinterpret_cast<uint4*>(out + m * BC * BC + r * BC + cg * 8) = *reinterpret_cast<const uint4*>(src);
-    }
-}
+constexpr int P128 = BD + 16;      // bf16 pitch of [token][key] tiles
 
 // ============================================ 3. the carry dM per (sequence, head, slice)
 constexpr int NTB = 512;           // 8 waves
@@ -1053,7 +781,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
     if ((e = launch_prefill_fused_states(f, ss->stream)) != hipSuccess) return e;
     if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return e;
     // 2. T^T and P per (chunk, value head)
-    if (ids > 0) hipLaunchKernelGGL(chunk_tp_kernel, dim3((unsigned)ids), dim3(NTP), 0, s, a);
+    if ((e = launch_chunk_tp(a, a.ncid, a.tp, false, s)) != hipSuccess) return e;
     // 3. the carry per (sequence, value head, slice)
     if (chains > 0) hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)chains), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
