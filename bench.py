@@ -23,7 +23,8 @@ pass at B1 or B4) for a rocprofv3 counter pass per workload.  The decode step (2
 state updated in place) is timed with events around a loop of back-to-back steps and
 reported in the same line, and so is the chunkwise reverse pass (dn_chunk_bwd) on the gated
 H16 T2048 shape at B1 and B4 (20 calls between events, own roofline block under
-``chunk_backward``).  The fp64 oracle is timed on the host cores on a bounded
+``chunk_backward``), and the gated d_k = d_v = 64 prompt of the layer's shape on its
+two-launch path (``prompt_d64``).  The fp64 oracle is timed on the host cores on a bounded
 sample of the prefill workload.
 
 Prints ONE JSON line.
@@ -601,6 +602,32 @@ def main():
                  "us_per_call": rec_us, "tokens_per_s": tokens / (rec_us * 1e-6),
                  "vs_chunked_call": rec_us / call_us}
 
+    # ------------- the d = 64 prompt (two launches: T and P of every chunk, then the chain)
+    x64 = make_case(B=B, T=T, Hqk=Hqk, Dk=64, dtype="bf16", g_scale=0.1, seed=0)
+    q64, k64, v64, b64, g64 = (to_dev(a_) for a_ in (x64.q, x64.k, x64.v, x64.beta, x64.g))
+    ws64 = torch.empty(dn.workspace_bytes(B, T, Hqk, Hv, 64, 64, torch.bfloat16), dtype=torch.uint8, device=dev)
+    o64 = torch.empty((B, T, Hv, 64), dtype=torch.bfloat16, device=dev)
+    s64 = torch.empty((B, Hv, 64, 64), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        dn.chunk_fwd(q64, k64, v64, b64, g64, None, out=o64, final_state=s64, workspace=ws64)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(10):
+        dn.chunk_fwd(q64, k64, v64, b64, g64, None, out=o64, final_state=s64, workspace=ws64)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    d64_us = ev0.elapsed_time(ev1) * 1e3 / 10
+    d64_b = prefill_bytes(B, T, Hqk, Hv, 64, True, B, False)
+    prompt_d64 = {"workload": f"gated prefill B{B} H{Hv} T{T} d_k=d_v=64 bf16, chunk 64",
+                  "path": dn.chunk_fwd_path(B, T, Hqk, Hv, 64, 64, torch.bfloat16),
+                  "kernels": "chunk_tp_kernel<64> + split_chain_kernel", "us_per_call": d64_us,
+                  "tokens_per_s": tokens / (d64_us * 1e-6), "workspace_bytes": ws64.numel(),
+                  "roofline": {"bound": "hbm", "achieved": d64_b / (d64_us * 1e-6) / 1e9,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": d64_b / (d64_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                               "algorithmic_bytes": d64_b}}
+    del ws64
+
     # ------------- the chunkwise reverse pass (dn_chunk_bwd), gated, H16 T2048, B1 and B4
     chunk_backward = {"what": "dL/dq, dk, dv, dbeta, dg and the initial state's gradient from "
                               "dL/do, through the chunked form (chunk-start states recomputed by "
@@ -745,6 +772,7 @@ def main():
         "readout_epilogue": epilogue,
         "recurrent_route": recurrent,
         "chunk_backward": chunk_backward,
+        "prompt_d64": prompt_d64,
         "causal_conv": conv,
         "cpu_baseline": None,
     }
