@@ -122,3 +122,25 @@ def test_two_kernel_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(fs, ref[1]), f"replay {rep} differs"
         _ = (o.float().sum() + 1).item()
+
+
+def test_two_kernel_final_state_may_alias_initial_state():
+    """The chain reads its columns of the initial state before it writes the final state, so
+    one tensor can serve as both (the state updated in place)."""
+    x = make_case(B=2, T=200, Hqk=2, Dk=64, dtype="bf16", g_scale=0.1, init_std=0.1, seed=11,
+                  name="d64_alias")
+    d = to_inputs(x)
+    o1, s1 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"])
+    st = d["init"].clone()
+    o2, s2 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], st, final_state=st)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+
+
+def test_two_kernel_zero_length_prompt_returns_initial_state():
+    x = make_case(B=2, T=0, Hqk=2, Dk=64, dtype="bf16", init_std=1.0, seed=12, name="d64_T0")
+    d = to_inputs(x)
+    o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, d["init"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(s, d["init"])
