@@ -1,7 +1,7 @@
 """Benchmark of the delta-rule mixer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--decode-reps R] [--graph]
-    python bench.py --only prefill2|prefill3|prefill5|decode|conv|chunk_bwd1|chunk_bwd4 [--steps K]
+    python bench.py --only prefill2|prefill3|prefill5|decode|conv|chunk_bwd1|chunk_bwd4|prompt_d64 [--steps K]
 
 One step is one prefill call (dn_chunk_fwd) over the DeltaNet layer-prefill workload
 (B=4, H=16, T=2048, d_k=d_v=128, bf16 q/k/v, fp32 beta, no decay, zero initial state,
@@ -185,7 +185,8 @@ def cpu_baseline(x, budget_s=12.0):
 
 def only_part(what, dn, dev, reps, warmup):
     """One workload of the line alone (for a rocprofv3 counter pass): the gated decode step,
-    the conv and the fused prologue on the layer shape, or the reverse pass at B1 / B4.
+    the conv and the fused prologue on the layer shape, the reverse pass at B1 / B4, or the
+    gated d = 64 prompt of the layer's shape.
     Returns the average time per call from HIP events on the launching stream."""
     import numpy as np
     import torch
@@ -214,6 +215,16 @@ def only_part(what, dn, dev, reps, warmup):
         b = torch.zeros(C, dtype=torch.float32, device=dev)
         calls.append(("conv_kernel (plain)", lambda i: dn.causal_conv(x, w, b)))
         calls.append(("conv_kernel (split, head norm)", lambda i: dn.conv_qkv(x, w, b, H, H, D, D)))
+    elif what == "prompt_d64":
+        T, H = PREFILL["T"], PREFILL["H"]
+        B = PREFILL["B"]
+        x64 = make_case(B=B, T=T, Hqk=H, Dk=64, dtype="bf16", g_scale=0.1, seed=0)
+        q, k, v, b, g = (to_dev(a_) for a_ in (x64.q, x64.k, x64.v, x64.beta, x64.g))
+        ws = torch.empty(dn.workspace_bytes(B, T, H, H, 64, 64, torch.bfloat16), dtype=torch.uint8, device=dev)
+        o = torch.empty((B, T, H, 64), dtype=torch.bfloat16, device=dev)
+        s = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev)
+        calls.append(("d64 prompt (two launches)",
+                      lambda i: dn.chunk_fwd(q, k, v, b, g, None, out=o, final_state=s, workspace=ws)))
     else:
         bb = 1 if what == "chunk_bwd1" else 4
         T, H, D = PREFILL["T"], PREFILL["H"], PREFILL["D"]
@@ -250,7 +261,7 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time a HIP-graph replay of the K steps instead of the eager launch loop")
     ap.add_argument("--only", choices=["prefill2", "prefill3", "prefill5", "decode", "conv",
-                                       "chunk_bwd1", "chunk_bwd4"], default=None,
+                                       "chunk_bwd1", "chunk_bwd4", "prompt_d64"], default=None,
                     help="run only this prefill workload (a rocprofv3 counter pass per workload) "
                          "and print its timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -325,7 +336,7 @@ def main():
         del zsets, zcu
         return dict(workload=PREFILL_WHAT[cfg], **blk)
 
-    if args.only in ("decode", "conv", "chunk_bwd1", "chunk_bwd4"):
+    if args.only in ("decode", "conv", "chunk_bwd1", "chunk_bwd4", "prompt_d64"):
         print(json.dumps({"only": args.only, **only_part(args.only, dn, dev, args.steps, args.warmup)}),
               flush=True)
         return
@@ -625,7 +636,8 @@ def main():
                   "roofline": {"bound": "hbm", "achieved": d64_b / (d64_us * 1e-6) / 1e9,
                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": d64_b / (d64_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                               "algorithmic_bytes": d64_b}}
+                               "algorithmic_bytes": d64_b,
+                               "traffic": load_traffic("prompt_d64_bytes_per_call")}}
     del ws64
 
     # ------------- the chunkwise reverse pass (dn_chunk_bwd), gated, H16 T2048, B1 and B4
