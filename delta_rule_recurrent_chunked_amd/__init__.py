@@ -185,11 +185,12 @@ def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: 
 
 
 def chunk_bwd_workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int,
-                              dtype: torch.dtype, num_seqs: Optional[int] = None) -> int:
+                              dtype: torch.dtype, num_seqs: Optional[int] = None,
+                              qk_l2norm: bool = False) -> int:
     """Device workspace (bytes) ``dn_chunk_bwd`` needs for these sizes (0 where the reverse
     pass does not support them)."""
     s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
-               DN_BF16 if dtype == torch.bfloat16 else DN_F32, 64, 1.0)
+               DN_BF16 if dtype == torch.bfloat16 else DN_F32, 64, 1.0, *_flags(qk_l2norm, 1e-6, False))
     return int(load_library().dn_chunk_bwd_workspace_bytes(ctypes.byref(s)))
 
 
@@ -382,16 +383,19 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               g: Optional[torch.Tensor], initial_state: Optional[torch.Tensor], d_o: torch.Tensor,
               d_final_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, scale: float = 1.0,
-              workspace: Optional[torch.Tensor] = None) -> dict:
+              workspace: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+              l2norm_eps: float = 1e-6) -> dict:
     """Reverse pass of the chunked form (no state trace): gradients of a loss with dL/do =
     ``d_o`` and dL/d final state = ``d_final_state`` for q, k, v, beta, g and the initial
-    state.  bf16, Dk = Dv = 128, one gate per head or none.  Returns a dict of float32
-    tensors dq, dk (``[B, T, Hqk, Dk]``), dv, dbeta, dg (None without g) and
-    d_initial_state.  ``workspace`` (uint8, at least the size the library asks for) may be
-    passed to avoid its allocation."""
+    state.  bf16, Dk = Dv = 128, one gate per head or none; with ``qk_l2norm`` the rule
+    reads q and k normalised inside the call (as ``chunk_fwd(..., qk_l2norm=True)``) and
+    dq, dk are the gradients for the raw q and k.  Returns a dict of float32 tensors dq, dk
+    (``[B, T, Hqk, Dk]``), dv, dbeta, dg (None without g) and d_initial_state.
+    ``workspace`` (uint8, at least the size the library asks for) may be passed to avoid
+    its allocation."""
     lib = load_library()
     shape, _, _, N = _prompt_args(q, k, v, beta, g, initial_state, False, cu_seqlens, scale, 64,
-                                  None, None, False, False, 1e-6)
+                                  None, None, False, qk_l2norm, l2norm_eps)
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     _dev(d_o, "d_o", q.dtype, (B, T, Hv, Dv))

@@ -709,7 +709,27 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
         for (int u = 0; u < 4; ++u) {
             const int pc = tf + NTB * u, row = pc >> 5, c4 = (pc & 31) * 4;
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row][c4]);
+            u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row][c4]);
+            if (a.rnorm) {
+                // the rows are normalised ones, x_hat = x r (r = 1 / sqrt(|x|^2 + eps)):
+                // dx = r (dx_hat - x_hat (x_hat . dx_hat)), the dot over the row's 32 lanes
+                const bf16x4 xh = *reinterpret_cast<const bf16x4*>(m ? &sm.K[row][c4] : &sm.Q[row][c4]);
+                float g4[4], x4[4], dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    g4[e] = __uint_as_float(v[e]);
+                    x4[e] = (float)xh[e];
+                    dot += x4[e] * g4[e];
+                }
+                dot += dpp16<0xB1>(dot);
+                dot += dpp16<0x4E>(dot);
+                dot += dpp16<0x141>(dot);
+                dot += dpp16<0x140>(dot);
+                dot += __shfl_xor(dot, 16);   // the row's other 16 lanes
+                const float r = row < rows ? a.rnorm[(m ? (long)a.B * a.T * a.Hqk : 0) + (t0 + row) * a.Hqk + hq] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(r * (g4[e] - x4[e] * dot));
+            }
             __builtin_amdgcn_raw_buffer_store_b128(v, m ? dk_rs : dq_rs, ((uint32_t)row * kq_tokf + c4) * 4, 0, 0);
         }
     }
@@ -719,12 +739,16 @@ __global__ __launch_bounds__(NTB, 1) void chunk_grad_kernel(ChunkBwdArgs a) {
 
 bool chunk_bwd_supported(const PrefillArgs& a) {
     const long span = ((long)a.T + 2 * BC) * (a.Hqk > a.Hv ? a.Hqk : a.Hv) * BD * 2;
-    return a.bf16 && a.Dk == BD && a.Dv == BD && a.C == BC && !a.g_per_key && !a.qk_norm && span < (1L << 31);
+    return a.bf16 && a.Dk == BD && a.Dv == BD && a.C == BC && !a.g_per_key && span < (1L << 31);
 }
 
 size_t chunk_bwd_workspace_bytes(const PrefillArgs& a, long ncid_l) {
     const size_t per = (size_t)ncid_l * a.Hv;
-    return per * BD * BD * sizeof(float) * 2 + per * 2 * BC * BC * 2;
+    // with the in-call normalisation, the normalised q and k (bf16) and the inverse norms of
+    // their rows (fp32) come first
+    const size_t nrows = (size_t)a.B * a.T * a.Hqk;
+    const size_t qk = a.qk_norm ? nrows * BD * 2 * 2 + ((nrows * 2 * sizeof(float) + 255) & ~(size_t)255) : 0;
+    return qk + per * BD * BD * sizeof(float) * 2 + per * 2 * BC * BC * 2;
 }
 
 namespace {
@@ -761,7 +785,22 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
     ChunkBwdArgs a = a0;
     a.ncid = chunk_id_bound(a);
     const size_t per = (size_t)a.ncid * a.Hv;
-    float* ws = static_cast<float*>(a.ws);
+    char* base = static_cast<char*>(a.ws);
+    hipError_t e;
+    if (a0.qk_norm) {
+        // the in-call normalisation as a pass of its own: the whole reverse pass then runs on
+        // the normalised rows (and the inverse norms of q's and k's rows), and the gradient
+        // kernel takes dq, dk back through the normalisation before it stores them
+        const size_t nrows = (size_t)a.B * a.T * a.Hqk, nb = nrows * BD * 2;
+        float* rn = reinterpret_cast<float*>(base + 2 * nb);
+        if ((e = launch_qk_norm_rows(a0, base, base + nb, rn, s)) != hipSuccess) return e;
+        a.q = base;
+        a.k = base + nb;
+        a.qk_norm = 0;
+        a.rnorm = rn;
+        base += 2 * nb + ((nrows * 2 * sizeof(float) + 255) & ~(size_t)255);
+    }
+    float* ws = reinterpret_cast<float*>(base);
     a.states = ws;
     a.dstates = ws + per * BD * BD;
     a.tp = a.dstates + per * BD * BD;
@@ -769,7 +808,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
     if (ids > 0x7fffffffL || chains > 0x7fffffffL) return hipErrorInvalidConfiguration;
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* ss = nullptr;
-    hipError_t e = side_stream(ss);
+    e = side_stream(ss);
     if (e != hipSuccess) return e;
     // 1. the state at every chunk start (the prompt kernel, outputs skipped), on the side
     //    stream once the caller's stream has reached this call

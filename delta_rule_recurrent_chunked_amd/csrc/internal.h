@@ -131,6 +131,8 @@ struct ChunkBwdArgs : PrefillArgs {
     float* dbeta;                   // [tokens, Hv]
     float* dg;                      // [tokens, Hv] or null (no gate)
     float* dh0;                     // [N, Hv, Dk, Dv] or null
+    const float* rnorm;             // null, or with q, k normalised rows: 1 / sqrt(|x|^2 + eps)
+                                    //   of the raw q rows [tokens, Hqk], then of the k rows
 };
 bool chunk_bwd_supported(const PrefillArgs& a);
 size_t chunk_bwd_workspace_bytes(const PrefillArgs& a, long ncid);
@@ -138,6 +140,10 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
 
 // Launchers (host functions); each returns hipGetLastError() after its launches.
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s);
+// the in-call normalisation as a pass of its own: bf16 q, k rows -> x / sqrt(|x|^2 + eps)
+// into qn, kn ([tokens, Hqk, Dk] bf16), and 1 / sqrt(|x|^2 + eps) of every q row, then of
+// every k row, into rnorm (may be null)
+hipError_t launch_qk_norm_rows(const PrefillArgs& a, void* qn, void* kn, float* rnorm, hipStream_t s);
 hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_causal_conv_step(const ConvArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s);

@@ -15,7 +15,7 @@
 // float4 of columns in RPT consecutive rows for the whole sequence.  Two workgroup barriers
 // per token (the column sums, then delta).  The trace, when asked for, streams out with
 // nontemporal stores.
-#include "internal.h"
+#include "chunk_ops.h"
 
 namespace dn {
 namespace {
@@ -467,50 +467,96 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(RecurrentBwdArgs a, int ns
     }
 }
 
-// dq, dk through the in-call normalisation, in place: with x_hat = x / n, n = sqrt(|x|^2 +
-// eps), dx = (dx_hat - x (x . dx_hat) / n^2) / n (zero where n = 0).  One wave per (token,
-// query/key head) row, two key channels per lane.
+// The in-call normalisation as passes of their own: NRW rows (token, query/key head) per
+// wave, two consecutive key channels per lane, every row's loads issued before the first
+// row's sums (DPP wave sums).
+constexpr int NRW = 8;
+
+// dq, dk through the normalisation, in place: with x_hat = x / n, n = sqrt(|x|^2 + eps),
+// dx = (dx_hat - x (x . dx_hat) / n^2) / n (zero where n = 0).
 template <typename T>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(RecurrentBwdArgs a) {
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);   // t * Hqk + hq
+    const long rows = (long)a.B * a.T * a.Hqk;
+    const long r0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * NRW;
     const int lane = threadIdx.x & 63;
-    if (row >= (long)a.B * a.T * a.Hqk) return;
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);
-    float xq[2], xk[2], gq[2], gk[2];
-    float nq = 0.f, nk = 0.f, sq = 0.f, sk = 0.f;
+    const bool in = 2 * lane < a.Dk;   // Dk is even
+    // dq and dk need only 4-byte alignment: 8-byte accesses where both allow them
+    const bool v2 = (((uintptr_t)a.dq | (uintptr_t)a.dk) & 7) == 0;
+    float xq[NRW][2], xk[NRW][2], gq[NRW][2], gk[NRW][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int x = lane + 64 * c;
-        const long i = row * a.Dk + x;
-        const bool in = x < a.Dk;
-        xq[c] = in ? ld_f32(q, i) : 0.f;
-        xk[c] = in ? ld_f32(k, i) : 0.f;
-        gq[c] = in ? a.dq[i] : 0.f;
-        gk[c] = in ? a.dk[i] : 0.f;
-        nq += xq[c] * xq[c];
-        nk += xk[c] * xk[c];
-        sq += xq[c] * gq[c];
-        sk += xk[c] * gk[c];
-    }
+    for (int r = 0; r < NRW; ++r) {
+        const bool ok = in && r0 + r < rows;
+        const long i0 = (r0 + r) * a.Dk + 2 * lane;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        nq += __shfl_xor(nq, off);
-        nk += __shfl_xor(nk, off);
-        sq += __shfl_xor(sq, off);
-        sk += __shfl_xor(sk, off);
-    }
-    nq += a.eps;
-    nk += a.eps;
-    const float rq = nq > 0.f ? rsqrtf(nq) : 0.f, rk = nk > 0.f ? rsqrtf(nk) : 0.f;
-    const float cq = nq > 0.f ? sq / nq : 0.f, ck = nk > 0.f ? sk / nk : 0.f;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int x = lane + 64 * c;
-        if (x < a.Dk) {
-            a.dq[row * a.Dk + x] = (gq[c] - xq[c] * cq) * rq;
-            a.dk[row * a.Dk + x] = (gk[c] - xk[c] * ck) * rk;
+        for (int c = 0; c < 2; ++c) {
+            xq[r][c] = ok ? ld_f32(q, i0 + c) : 0.f;
+            xk[r][c] = ok ? ld_f32(k, i0 + c) : 0.f;
         }
+        if (ok && v2) {
+            const float2 a2 = *reinterpret_cast<const float2*>(a.dq + i0), b2 = *reinterpret_cast<const float2*>(a.dk + i0);
+            gq[r][0] = a2.x; gq[r][1] = a2.y; gk[r][0] = b2.x; gk[r][1] = b2.y;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                gq[r][c] = ok ? a.dq[i0 + c] : 0.f;
+                gk[r][c] = ok ? a.dk[i0 + c] : 0.f;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+        const float nq = ck::wave_sum(xq[r][0] * xq[r][0] + xq[r][1] * xq[r][1]) + a.eps;
+        const float nk = ck::wave_sum(xk[r][0] * xk[r][0] + xk[r][1] * xk[r][1]) + a.eps;
+        const float sq = ck::wave_sum(xq[r][0] * gq[r][0] + xq[r][1] * gq[r][1]);
+        const float sk = ck::wave_sum(xk[r][0] * gk[r][0] + xk[r][1] * gk[r][1]);
+        const float rq = nq > 0.f ? rsqrtf(nq) : 0.f, rk = nk > 0.f ? rsqrtf(nk) : 0.f;
+        const float cq = nq > 0.f ? sq / nq : 0.f, ck_ = nk > 0.f ? sk / nk : 0.f;
+        if (!(in && r0 + r < rows)) continue;
+        const long i0 = (r0 + r) * a.Dk + 2 * lane;
+        const float q0 = (gq[r][0] - xq[r][0] * cq) * rq, q1 = (gq[r][1] - xq[r][1] * cq) * rq;
+        const float k0 = (gk[r][0] - xk[r][0] * ck_) * rk, k1 = (gk[r][1] - xk[r][1] * ck_) * rk;
+        if (v2) {
+            *reinterpret_cast<float2*>(a.dq + i0) = make_float2(q0, q1);
+            *reinterpret_cast<float2*>(a.dk + i0) = make_float2(k0, k1);
+        } else {
+            a.dq[i0] = q0; a.dq[i0 + 1] = q1;
+            a.dk[i0] = k0; a.dk[i0 + 1] = k1;
+        }
+    }
+}
+
+// q, k -> x / sqrt(|x|^2 + eps) as bf16 (zero where the sum is 0)
+__global__ __launch_bounds__(256) void norm_rows_kernel(PrefillArgs a, __bf16* qn, __bf16* kn, float* rnorm) {
+    const long rows = (long)a.B * a.T * a.Hqk;
+    const long r0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * NRW;
+    const int lane = threadIdx.x & 63;
+    const __bf16* q = static_cast<const __bf16*>(a.q);
+    const __bf16* k = static_cast<const __bf16*>(a.k);
+    const bool in = 2 * lane < a.Dk;   // Dk is even
+    uint32_t uq[NRW], uk[NRW];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+        const bool ok = in && r0 + r < rows;
+        const long i0 = (r0 + r) * a.Dk + 2 * lane;
+        uq[r] = ok ? *reinterpret_cast<const uint32_t*>(q + i0) : 0u;
+        uk[r] = ok ? *reinterpret_cast<const uint32_t*>(k + i0) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+        const float q0 = __uint_as_float(uq[r] << 16), q1 = __uint_as_float(uq[r] & 0xffff0000u);
+        const float k0 = __uint_as_float(uk[r] << 16), k1 = __uint_as_float(uk[r] & 0xffff0000u);
+        const float rq = inv_norm(ck::wave_sum(q0 * q0 + q1 * q1), a.eps);
+        const float rk = inv_norm(ck::wave_sum(k0 * k0 + k1 * k1), a.eps);
+        if (rnorm && lane == 0 && r0 + r < rows) {
+            rnorm[r0 + r] = rq;
+            rnorm[rows + r0 + r] = rk;
+        }
+        if (!(in && r0 + r < rows)) continue;
+        const long i0 = (r0 + r) * a.Dk + 2 * lane;
+        *reinterpret_cast<uint32_t*>(qn + i0) = pack_bf16x2(q0 * rq, q1 * rq);
+        *reinterpret_cast<uint32_t*>(kn + i0) = pack_bf16x2(k0 * rk, k1 * rk);
     }
 }
 
@@ -569,6 +615,17 @@ hipError_t launch_bwd_dk(const RecurrentBwdArgs& a, hipStream_t s) {
 
 int recurrent_bwd_slices(int Dk, int Dv) { return Dv / bwd_cols(Dk); }
 
+hipError_t launch_qk_norm_rows(const PrefillArgs& a, void* qn, void* kn, float* rnorm, hipStream_t s) {
+    const long rows = (long)a.B * a.T * a.Hqk;
+    if (rows == 0) return hipSuccess;
+    if (!a.bf16 || a.Dk > 128) return hipErrorInvalidValue;
+    const long blocks = (rows + 4 * NRW - 1) / (4 * NRW);
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(norm_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, static_cast<__bf16*>(qn),
+                       static_cast<__bf16*>(kn), rnorm);
+    return hipGetLastError();
+}
+
 hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
     if ((long)a.N * a.Hv == 0) return hipSuccess;
     if ((long)a.N * a.Hv * recurrent_bwd_slices(a.Dk, a.Dv) > 0x7fffffffL) return hipErrorInvalidConfiguration;
@@ -583,7 +640,7 @@ hipError_t launch_recurrent_bwd(const RecurrentBwdArgs& a, hipStream_t s) {
     }
     const long rows = tokens * a.Hqk;
     if (a.qk_norm && rows > 0) {
-        const long blocks = (rows + 3) / 4;
+        const long blocks = (rows + 4 * NRW - 1) / (4 * NRW);
         if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
         if (a.bf16) hipLaunchKernelGGL(norm_bwd_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
         else hipLaunchKernelGGL(norm_bwd_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, a);

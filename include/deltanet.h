@@ -280,8 +280,12 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
  * fixed order and no step uses atomics (the result is bitwise reproducible).
  *
  * Supported: bf16 q/k/v/d_o, Dk = Dv = 128, 64-token chunks, one log decay per head or
- * none, no flags; other shapes return DN_ERR_UNSUPPORTED (dn_recurrent_bwd computes them
- * token by token from a state trace).  Arguments as dn_recurrent_bwd without the trace:
+ * none, with or without DN_QK_L2NORM (then a first pass writes the normalised q and k,
+ * in bf16, and the inverse norms of their rows to the workspace, the reverse pass runs on
+ * them, and its last kernel takes dq, dk back through the normalisation to the raw rows
+ * as it stores them); DN_GATE_PER_KEY and other shapes
+ * return DN_ERR_UNSUPPORTED (dn_recurrent_bwd computes them token by token from a state
+ * trace).  Arguments as dn_recurrent_bwd without the trace:
  *
  *   d_o             [B, T, Hv, Dv] bf16 (required)
  *   d_final_state   [N, Hv, Dk, Dv] fp32 or NULL (zero)
@@ -291,8 +295,10 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
  *   d_initial_state [N, Hv, Dk, Dv] fp32 or NULL
  *   workspace       dn_chunk_bwd_workspace_bytes(shape) bytes: per chunk and value head the
  *                   state at the chunk start and dL/dM after the chunk (fp32) and T and P
- *                   (bf16): (2 Dk Dv * 4 + 2 * 64 * 64 * 2) bytes; contents on entry
- *                   ignored, on exit undefined
+ *                   (bf16): (2 Dk Dv * 4 + 2 * 64 * 64 * 2) bytes; with DN_QK_L2NORM
+ *                   also 2 * B * T * Hqk * Dk * 2 bytes of normalised q and k and
+ *                   2 * B * T * Hqk * 4 bytes of inverse norms (rounded up to 256);
+ *                   contents on entry ignored, on exit undefined
  *
  * Errors: as dn_chunk_fwd, DN_ERR_UNSUPPORTED as above, DN_ERR_WORKSPACE.
  */

@@ -294,3 +294,22 @@ def test_chunk_fwd_noalloc_rejects_oversized_scratch_on_the_host():
                                     None, p, None) == dn.DN_ERR_UNSUPPORTED
     assert lib.dn_chunk_fwd_noalloc(None, p, p, p, p, None, None, None, None, p,
                                     None) == dn.DN_ERR_INVALID_ARG
+
+
+def test_chunk_bwd_workspace_query():
+    """dn_chunk_bwd_workspace_bytes: per (chunk, value head) the chunk-start state and dL/dM
+    (fp32, 2 x 128 x 128 x 4 B) and T, P (bf16, 2 x 64 x 64 x 2 B), over the chunk bound;
+    with DN_QK_L2NORM also the normalised q and k (bf16, 2 x tokens x Hqk x 128 x 2 B) and the
+    inverse norms of their rows (fp32, 2 x tokens x Hqk x 4 B, rounded up to 256 B); zero for
+    shapes the reverse pass does not take."""
+    import torch
+    bf = torch.bfloat16
+    rec = 2 * 128 * 128 * 4 + 2 * 64 * 64 * 2
+    assert dn.chunk_bwd_workspace_bytes(4, 2048, 16, 16, 128, 128, bf) == 4 * 32 * 16 * rec
+    assert dn.chunk_bwd_workspace_bytes(4, 2048, 16, 16, 128, 128, bf, qk_l2norm=True) == \
+        4 * 32 * 16 * rec + 2 * 4 * 2048 * 16 * 128 * 2 + 2 * 4 * 2048 * 16 * 4
+    # 3 x 100 x 2 rows of norms = 2400 B -> 2560 B
+    assert dn.chunk_bwd_workspace_bytes(1, 100, 3, 3, 128, 128, bf, qk_l2norm=True) == \
+        dn.chunk_bwd_workspace_bytes(1, 100, 3, 3, 128, 128, bf) + 2 * 100 * 3 * 128 * 2 + 2560
+    assert dn.chunk_bwd_workspace_bytes(4, 2048, 16, 16, 64, 64, bf) == 0
+    assert dn.chunk_bwd_workspace_bytes(4, 2048, 16, 16, 128, 128, torch.float32) == 0

@@ -26,22 +26,22 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _run(x, scale=1.0, seed=81):
+def _run(x, scale=1.0, seed=81, qk_l2norm=False):
     rng = np.random.default_rng(seed)
     N = x.num_seqs
     do_dev = dev_tensor(f32_to_bf16_bits(rng.standard_normal((x.B, x.T, x.Hv, x.Dv)).astype(np.float32)))
     dfin = (0.1 * rng.standard_normal((N, x.Hv, x.Dk, x.Dv))).astype(np.float32)
     d = to_inputs(x)
     grads = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], do_dev,
-                         dev_tensor(dfin), cu_seqlens=d["cu"], scale=scale)
+                         dev_tensor(dfin), cu_seqlens=d["cu"], scale=scale, qk_l2norm=qk_l2norm)
     torch.cuda.synchronize()
     return grads, host(do_dev), dfin.astype(np.float64), d, do_dev
 
 
-def _check(x, grads, do, dfin, scale=1.0):
+def _check(x, grads, do, dfin, scale=1.0, qk_l2norm=False):
     f = x.f64()
     ref = ref_backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["init"], do, dfin,
-                       x.cu_seqlens, scale)
+                       x.cu_seqlens, scale, qk_l2norm=qk_l2norm)
     bounds = x.seq_bounds()
     errs = {}
     pairs = [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dbeta", "dbeta"),
@@ -91,6 +91,24 @@ def test_chunk_bwd(name):
     x = make_case(dtype="bf16", seed=80, name=f"chunk_bwd_{name}", **CASES[name])
     grads, do, dfin, _, _ = _run(x, scale=0.8)
     _check(x, grads, do, dfin, scale=0.8)
+
+
+NORM_CASES = {
+    "norm_gated_ragged": dict(B=2, T=200, Hqk=2, Hv=2, Dk=128, g_scale=0.1, init_std=0.02),
+    "norm_packed_gqa": dict(B=1, Hqk=1, Hv=2, Dk=128, seqlens=[70, 0, 1, 129, 64], g_scale=0.3,
+                            init_std=0.02, beta_scale=2.0),
+    "norm_plain": dict(B=1, T=130, Hqk=2, Hv=2, Dk=128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NORM_CASES))
+def test_chunk_bwd_in_call_normalisation(name):
+    """Raw N(0, 1) q and k (norms about sqrt(128)), normalised inside the call: the gradients
+    for the raw rows against the fp64 reverse pass through the same normalisation."""
+    _say(f"chunk bwd, in-call normalisation, {name}")
+    x = make_case(dtype="bf16", seed=88, name=f"chunk_bwd_{name}", qk_raw=True, **NORM_CASES[name])
+    grads, do, dfin, _, _ = _run(x, scale=0.9, qk_l2norm=True)
+    _check(x, grads, do, dfin, scale=0.9, qk_l2norm=True)
 
 
 def test_chunk_bwd_layer_workload():
