@@ -187,18 +187,25 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
     for (long c0 = bos; c0 < eos; c0 += CC) {
         const int len = (int)min((long)CC, eos - c0);
 
-        // ---- 1: block sums of g, k and q as floats (normalised if asked), V and beta
+        // ---- 1: block sums of g (each 8-token half summed on its own, then the two added,
+        // the order the two-kernel form takes), k and q as floats (normalised if asked), V
+        // and beta
         float2 L[16], kf[16], qf[16];
         {
-            float2 s = make_float2(0.f, 0.f);
+            float2 s = make_float2(0.f, 0.f), h0 = make_float2(0.f, 0.f);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                if (i == 8) {
+                    h0 = s;
+                    s = make_float2(0.f, 0.f);
+                }
                 s.x += rg[i].x;
                 s.y += rg[i].y;
-                L[i] = s;
+                L[i] = i < 8 ? s : make_float2(h0.x + s.x, h0.y + s.y);
                 kf[i] = bf2_to_f2(rk[i]);
                 qf[i] = bf2_to_f2(rq[i]);
             }
+            s = L[15];
             if (a.qk_norm) {
                 float nk[16], nq[16];
 #pragma unroll
@@ -539,26 +546,44 @@ __device__ bool chunk_of(const PrefillArgs& a, long gid, int& n, long& c) {
     return c < ((long)a.cu[lo + 1] - a.cu[lo] + CC - 1) / CC;
 }
 
+// LDS of the prep kernel: the operand tiles of one (chunk, value head) item.
+struct PrepSmemChg {
+    __bf16 Kr[CC][OP];      // k_r o exp(G_r - Z_b(r))
+    __bf16 Qr[CC][OP];      // q_r o exp(G_r - Z_b(r))
+    __bf16 Kd[CC][OP];      // k_r o exp(G_last - G_r)
+    __bf16 Kc[160][OP];     // column operands of A and P; then K o e^G (0..63), Q o e^G (64..127)
+    __bf16 A[CC][AP];
+    __bf16 P[CC][AP];
+    float Ad[NB][16][20];   // A's diagonal tiles in fp32, transposed ([column][row]), for the inverses
+    __bf16 Tb[NB][16][TP];  // (I + A_bb)^-1
+    float beta[CC];
+    float toth[2 * NB][HK]; // sums of g over each 8-token half of a block
+    float eg[HK];           // exp(G_last)
+};
+
+constexpr int NPP = 512;    // threads of the prep kernel: two waves per 16-token block
+
 // One workgroup per CU walks the (chunk, value head) items, item = chunk * Hv + head; the
-// next item's inputs are requested as soon as the current one's are consumed.
-__global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitems) {
-    __shared__ __align__(16) ChgSmem sm;
+// next item's inputs are requested as soon as the current one's are consumed.  Wave w
+// takes the 8 tokens 8 w .. 8 w + 7 (half of block w / 2), two key channels per lane, for
+// the block sums and the operands; then waves 0-3 form block w's diagonal tiles of A and
+// P and invert (I + A_ww) while waves 4-7 form the tiles below the diagonal.
+__global__ __launch_bounds__(NPP) void chg_prep_kernel(PrefillArgs a, long nitems) {
+    __shared__ __align__(16) PrepSmemChg sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int blk = w >> 1, hf = w & 1;   // this wave's rows: 16 blk + 8 hf + i, i < 8
     const int Hv = a.Hv;
-    const int u = w & 1;
     const __bf16* qp = static_cast<const __bf16*>(a.q);
     const __bf16* kp = static_cast<const __bf16*>(a.k);
+    const uint32_t g_tok = (uint32_t)Hv * HK * 4, kq_tok = (uint32_t)a.Hqk * HK * 2, b_tok = (uint32_t)Hv * 4;
 
     // A's and P's tiles above the diagonal stay zero (only the tiles on and below it are written)
-    for (int e = tid; e < CC * AP; e += NTH) {
+    for (int e = tid; e < CC * AP; e += NPP) {
         (&sm.P[0][0])[e] = (__bf16)0.f;
         (&sm.A[0][0])[e] = (__bf16)0.f;
     }
 
-    float2 rg[16];
-    uint32_t rk[16], rq[16];
-    float rb;
     // the first item from `item` on (in steps of the grid) that a chunk takes; nitems if none
     auto next_item = [&](long item) -> long {
         int n;
@@ -566,9 +591,13 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
         while (item < nitems && !chunk_of(a, item / Hv, n, cix)) item += gridDim.x;
         return item;
     };
-    // requests item `item`'s inputs (a chunk takes it): block w's tokens, key channels
-    // 2 lane and 2 lane + 1
-    auto fetch = [&](long item) {
+    // range-checked streams of an item's sequence (rows past its end read zeros) and the
+    // item's first token within it
+    struct Streams {
+        __amdgpu_buffer_rsrc_t gs, ks, qs, bs;
+        uint32_t c;
+    };
+    auto streams = [&](long item) -> Streams {
         int n;
         long cix;
         chunk_of(a, item / Hv, n, cix);
@@ -577,32 +606,59 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
         long bos, eos;
         seq_range(a.cu, n, a.T, bos, eos);
         const long L = eos - bos;
-        const uint32_t g_tok = (uint32_t)Hv * HK * 4, kq_tok = (uint32_t)a.Hqk * HK * 2, b_tok = (uint32_t)Hv * 4;
-        const __amdgpu_buffer_rsrc_t gs = rsrc(a.g + (bos * Hv + h) * HK, L > 0 ? (L - 1) * g_tok + HK * 4 : 0);
-        const __amdgpu_buffer_rsrc_t ks = rsrc(kp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
-        const __amdgpu_buffer_rsrc_t qs = rsrc(qp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
-        const __amdgpu_buffer_rsrc_t bs = rsrc(a.beta + bos * Hv + h, L > 0 ? (L - 1) * b_tok + 4 : 0);
-        const uint32_t c = (uint32_t)(cix * CC);
+        Streams s;
+        s.gs = rsrc(a.g + (bos * Hv + h) * HK, L > 0 ? (L - 1) * g_tok + HK * 4 : 0);
+        s.ks = rsrc(kp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+        s.qs = rsrc(qp + (bos * a.Hqk + hq) * HK, L > 0 ? (L - 1) * kq_tok + HK * 2 : 0);
+        s.bs = rsrc(a.beta + bos * Hv + h, L > 0 ? (L - 1) * b_tok + 4 : 0);
+        s.c = (uint32_t)(cix * CC);
+        return s;
+    };
+    float2 rg[8];
+    uint32_t rk[8], rq[8];
+    float rb = 0.f;
+    // requests item `item`'s inputs (a chunk takes it): this wave's 8 tokens, key channels
+    // 2 lane and 2 lane + 1; wave 0 also the 64 betas
+    auto fetch = [&](long item) {
+        const Streams s = streams(item);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t r = c + 16 * w + i;
-            const u32x2 gv = __builtin_amdgcn_raw_buffer_load_b64(gs, r * g_tok + 8 * lane, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = s.c + 8 * w + i;
+            const u32x2 gv = __builtin_amdgcn_raw_buffer_load_b64(s.gs, r * g_tok + 8 * lane, 0, 0);
             rg[i] = make_float2(__uint_as_float(gv[0]), __uint_as_float(gv[1]));
-            rk[i] = __builtin_amdgcn_raw_buffer_load_b32(ks, r * kq_tok + 4 * lane, 0, 0);
-            rq[i] = __builtin_amdgcn_raw_buffer_load_b32(qs, r * kq_tok + 4 * lane, 0, 0);
+            rk[i] = __builtin_amdgcn_raw_buffer_load_b32(s.ks, r * kq_tok + 4 * lane, 0, 0);
+            rq[i] = __builtin_amdgcn_raw_buffer_load_b32(s.qs, r * kq_tok + 4 * lane, 0, 0);
         }
-        rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (c + (tid & 63)) * b_tok, 0, 0));
+        if (w == 0) rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.bs, (s.c + lane) * b_tok, 0, 0));
+    };
+    // k, q rows (float pairs) normalised in place if asked: one wave reduction per row
+    auto normalise = [&](float2* kf, float2* qf, int rows) {
+        if (!a.qk_norm) return;
+#pragma unroll 1
+        for (int i = 0; i < rows; ++i) {
+            float nk = kf[i].x * kf[i].x + kf[i].y * kf[i].y, nq = qf[i].x * qf[i].x + qf[i].y * qf[i].y;
+#pragma unroll
+            for (int mm = 1; mm < 64; mm <<= 1) {
+                nk += __shfl_xor(nk, mm);
+                nq += __shfl_xor(nq, mm);
+            }
+            const float ik = inv_norm(nk, a.eps), iq = inv_norm(nq, a.eps);
+            kf[i].x *= ik;
+            kf[i].y *= ik;
+            qf[i].x *= iq;
+            qf[i].y *= iq;
+        }
     };
 
     long item = next_item(blockIdx.x);
     if (item < nitems) fetch(item);
     while (item < nitems) {
-        // ---- 1: block sums of g, k and q as floats (normalised if asked), V and beta
-        float2 L[16], kf[16], qf[16];
+        // ---- 1: sums of g over this wave's 8 tokens; k and q as floats (normalised if asked)
+        float2 L[8], kf[8], qf[8];
         {
             float2 s = make_float2(0.f, 0.f);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 s.x += rg[i].x;
                 s.y += rg[i].y;
                 L[i] = s;
@@ -610,22 +666,22 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
                 qf[i] = bf2_to_f2(rq[i]);
             }
             if (a.qk_norm) {
-                float nk[16], nq[16];
+                float nk[8], nq[8];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < 8; ++i) {
                     nk[i] = kf[i].x * kf[i].x + kf[i].y * kf[i].y;
                     nq[i] = qf[i].x * qf[i].x + qf[i].y * qf[i].y;
                 }
 #pragma unroll
                 for (int mm = 1; mm < 64; mm <<= 1) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
+                    for (int i = 0; i < 8; ++i) {
                         nk[i] += __shfl_xor(nk[i], mm);
                         nq[i] += __shfl_xor(nq[i], mm);
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < 8; ++i) {
                     const float ik = inv_norm(nk[i], a.eps), iq = inv_norm(nq[i], a.eps);
                     kf[i].x *= ik;
                     kf[i].y *= ik;
@@ -633,28 +689,39 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
                     qf[i].y *= iq;
                 }
             }
-            if (tid < CC) sm.beta[tid] = rb;
-            *reinterpret_cast<float2*>(&sm.tot[w][2 * lane]) = s;
-            const bool hb = __ballot(fminf(s.x, s.y) < -HARD) != 0;
-            if (lane == 0) sm.hard[w] = hb ? 1 : 0;
+            if (w == 0) sm.beta[lane] = rb;
+            *reinterpret_cast<float2*>(&sm.toth[w][2 * lane]) = s;
         }
         __syncthreads();
 
         const long next = next_item(item + gridDim.x);
+        const Streams cur = streams(item);   // kept for a block that decays too fast
         if (next < nitems) fetch(next);   // lands while this item is worked
-        // ---- 2: operands
-        float2 Z[NB], Zw = make_float2(0.f, 0.f), Gl = make_float2(0.f, 0.f);
+        // ---- 2: operands.  Z_b = sum of g over the blocks before b; G_r - Z_b for this
+        // wave's rows is the first half's sum (second half only) plus the running sum
+        float2 Z[NB], Zw = make_float2(0.f, 0.f), Gl = make_float2(0.f, 0.f), off = make_float2(0.f, 0.f);
+        int hardm = 0;   // blocks in which some channel decays by more than e^HARD
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             Z[b] = Gl;
-            if (b == w) Zw = Gl;
-            const float2 tb = *reinterpret_cast<const float2*>(&sm.tot[b][2 * lane]);
+            const float2 t0 = *reinterpret_cast<const float2*>(&sm.toth[2 * b][2 * lane]);
+            const float2 t1 = *reinterpret_cast<const float2*>(&sm.toth[2 * b + 1][2 * lane]);
+            const float2 tb = make_float2(t0.x + t1.x, t0.y + t1.y);
+            if (b == blk) {
+                Zw = Gl;
+                if (hf) off = t0;
+            }
+            if (__ballot(fminf(tb.x, tb.y) < -HARD) != 0) hardm |= 1 << b;
             Gl.x += tb.x;
             Gl.y += tb.y;
         }
-        uint32_t pke[16], pqe[16];  // K o e^G and Q o e^G, stored once the column operands are read
-        const bool hard = sm.hard[w] != 0;
-        if (!hard) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            L[i].x += off.x;
+            L[i].y += off.y;
+        }
+        uint32_t pke[8], pqe[8];  // K o e^G and Q o e^G, stored once the column operands are read
+        if (!((hardm >> blk) & 1)) {
             // every factor from two exponentials per entry, e^{L} and e^{-L} (L the in-block
             // sum, -L at most 60 here), and per-channel factors of at most 1
             const float2 eZ = make_float2(__expf(Zw.x), __expf(Zw.y));
@@ -663,8 +730,8 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
 #pragma unroll
             for (int b = 0; b < NB; ++b) eF[b] = make_float2(__expf(Z[b].x - Zw.x), __expf(Z[b].y - Zw.y));
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 16 * w + i;
+            for (int i = 0; i < 8; ++i) {
+                const int r = 16 * blk + 8 * hf + i;
                 const float e1x = __expf(L[i].x), e1y = __expf(L[i].y);
                 const float e2x = __expf(-L[i].x), e2y = __expf(-L[i].y);
                 const float kx = kf[i].x * e1x, ky = kf[i].y * e1y, qx = qf[i].x * e1x, qy = qf[i].y * e1y;
@@ -674,17 +741,17 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
                 pqe[i] = pack_bf16x2(qx * eZ.x, qy * eZ.y);
                 const float cx = kf[i].x * e2x, cy = kf[i].y * e2y;
                 st2(&sm.Kd[r][2 * lane], cx * eD.x, cy * eD.y);
-                st2(&sm.Kc[kc_off(w) + r][2 * lane], cx, cy);
+                st2(&sm.Kc[kc_off(blk) + r][2 * lane], cx, cy);
 #pragma unroll
                 for (int b = 1; b < NB; ++b)
-                    if (b > w) st2(&sm.Kc[kc_off(b) + r][2 * lane], cx * eF[b].x, cy * eF[b].y);
+                    if (b > blk) st2(&sm.Kc[kc_off(b) + r][2 * lane], cx * eF[b].x, cy * eF[b].y);
             }
         } else {
             // one exponential per factor, each of a difference that is at most 0 (the
             // diagonal column factor, replaced below, is capped)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 16 * w + i;
+            for (int i = 0; i < 8; ++i) {
+                const int r = 16 * blk + 8 * hf + i;
                 const float ax = __expf(Zw.x + L[i].x), ay = __expf(Zw.y + L[i].y);
                 pke[i] = pack_bf16x2(kf[i].x * ax, kf[i].y * ay);
                 pqe[i] = pack_bf16x2(qf[i].x * ax, qf[i].y * ay);
@@ -695,9 +762,9 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
                     kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    if (b < w) continue;
+                    if (b < blk) continue;
                     float cx = Z[b].x - Zw.x - L[i].x, cy = Z[b].y - Zw.y - L[i].y;
-                    if (b == w) {
+                    if (b == blk) {
                         cx = fminf(cx, CLAMP);
                         cy = fminf(cy, CLAMP);
                     }
@@ -706,84 +773,97 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
             }
         }
         if (w == 0) *reinterpret_cast<float2*>(&sm.eg[2 * lane]) = make_float2(__expf(Gl.x), __expf(Gl.y));
-        if (!hard) {
-            // block w's diagonal tiles of A and P from the rows this wave has just written
-            wave_lds_order();
-            f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+        __syncthreads();   // every operand row is in LDS
+
+        if (w < NB) {
+            // ---- 3a: block w's diagonal tiles of A and P, then (I + A_ww)^-1
+            if (!((hardm >> w) & 1)) {
+                f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 kc = ld8(&sm.Kc[kc_off(w) + 16 * w + l16][32 * s + 8 * g4]);
-                aa = mma16(ld8(&sm.Kr[16 * w + l16][32 * s + 8 * g4]), kc, aa);
-                pa = mma16(ld8(&sm.Qr[16 * w + l16][32 * s + 8 * g4]), kc, pa);
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 kc = ld8(&sm.Kc[kc_off(w) + 16 * w + l16][32 * s + 8 * g4]);
+                    aa = mma16(ld8(&sm.Kr[16 * w + l16][32 * s + 8 * g4]), kc, aa);
+                    pa = mma16(ld8(&sm.Qr[16 * w + l16][32 * s + 8 * g4]), kc, pa);
+                }
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * g4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    const float av = l16 < r ? bt[e] * aa[e] : 0.f;
+                    sm.A[16 * w + r][16 * w + l16] = (__bf16)av;
+                    sm.Ad[w][l16][r] = av;
+                    sm.P[16 * w + r][16 * w + l16] = (__bf16)(l16 <= r ? pa[e] : 0.f);
+                }
+            } else {
+                // block w decays too fast for the factored diagonal tile: one exponential per
+                // (row, column, channel), the wave summing over its 128 channels, from the
+                // block's g, k and q read again (rare, so it holds no registers elsewhere)
+                float2 hl[16], hk[16], hq[16];
+                {
+                    // the in-block sums as the operands took them: each half on its own
+                    float2 s = make_float2(0.f, 0.f), h0 = make_float2(0.f, 0.f);
+#pragma unroll 1
+                    for (int i = 0; i < 16; ++i) {
+                        const uint32_t r = cur.c + 16 * w + i;
+                        const u32x2 gv = __builtin_amdgcn_raw_buffer_load_b64(cur.gs, r * g_tok + 8 * lane, 0, 0);
+                        if (i == 8) {
+                            h0 = s;
+                            s = make_float2(0.f, 0.f);
+                        }
+                        s.x += __uint_as_float(gv[0]);
+                        s.y += __uint_as_float(gv[1]);
+                        hl[i] = i < 8 ? s : make_float2(h0.x + s.x, h0.y + s.y);
+                        hk[i] = bf2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(cur.ks, r * kq_tok + 4 * lane, 0, 0));
+                        hq[i] = bf2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(cur.qs, r * kq_tok + 4 * lane, 0, 0));
+                    }
+                }
+                normalise(hk, hq, 16);
+#pragma unroll 1
+                for (int r = 0; r < 16; ++r) {
+#pragma unroll 1
+                    for (int i = 0; i < 16; ++i) {
+                        float pa = 0.f, pp = 0.f;
+                        if (i <= r) {
+                            const float dx = __expf(hl[r].x - hl[i].x), dy = __expf(hl[r].y - hl[i].y);
+                            pa = wave_sum(hk[r].x * hk[i].x * dx + hk[r].y * hk[i].y * dy);
+                            pp = wave_sum(hq[r].x * hk[i].x * dx + hq[r].y * hk[i].y * dy);
+                        }
+                        if (lane == 0) {
+                            const float av = i < r ? sm.beta[16 * w + r] * pa : 0.f;
+                            sm.A[16 * w + r][16 * w + i] = (__bf16)av;
+                            sm.Ad[w][i][r] = av;
+                            sm.P[16 * w + r][16 * w + i] = (__bf16)pp;
+                        }
+                    }
+                }
             }
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * g4]);
+            // (I + A_ww)^-1 by forward substitution, lane c < 16 solving column c in fp32; once
+            // row i is final it is taken out of every later row at once (independent updates)
+            wave_lds_order();
+            if (lane < 16) {
+                float t[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g4 + e;
-                const float av = l16 < r ? bt[e] * aa[e] : 0.f;
-                sm.A[16 * w + r][16 * w + l16] = (__bf16)av;
-                sm.Ad[w][l16][r] = av;
-                sm.P[16 * w + r][16 * w + l16] = (__bf16)(l16 <= r ? pa[e] : 0.f);
+                for (int r = 0; r < 16; ++r) t[r] = r == lane ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                    for (int r4 = (i + 1) & ~3; r4 < 16; r4 += 4) {
+                        const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.Ad[w][i][r4]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (r4 + j > i) t[r4 + j] -= av[j] * t[i];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
             }
         } else {
-            // block w decays too fast for the factored diagonal tile: one exponential per
-            // (row, column, channel); the wave sums over its 128 channels.  Rare, so it
-            // runs over private copies rather than holding registers for the common path.
-            float2 hl[16], hk[16], hq[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                hl[i] = L[i];
-                hk[i] = kf[i];
-                hq[i] = qf[i];
-            }
-#pragma unroll 1
-            for (int r = 0; r < 16; ++r) {
-#pragma unroll 1
-                for (int i = 0; i < 16; ++i) {
-                    float pa = 0.f, pp = 0.f;
-                    if (i <= r) {
-                        const float dx = __expf(hl[r].x - hl[i].x), dy = __expf(hl[r].y - hl[i].y);
-                        pa = wave_sum(hk[r].x * hk[i].x * dx + hk[r].y * hk[i].y * dy);
-                        pp = wave_sum(hq[r].x * hk[i].x * dx + hq[r].y * hk[i].y * dy);
-                    }
-                    if (lane == 0) {
-                        const float av = i < r ? sm.beta[16 * w + r] * pa : 0.f;
-                        sm.A[16 * w + r][16 * w + i] = (__bf16)av;
-                        sm.Ad[w][i][r] = av;
-                        sm.P[16 * w + r][16 * w + i] = (__bf16)pp;
-                    }
-                }
-            }
-        }
-        // (I + A_ww)^-1 by forward substitution, lane c < 16 solving column c in fp32; once
-        // row i is final it is taken out of every later row at once (independent updates)
-        wave_lds_order();
-        if (lane < 16) {
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = r == lane ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < 15; ++i) {
-#pragma unroll
-                for (int r4 = (i + 1) & ~3; r4 < 16; r4 += 4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.Ad[w][i][r4]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (r4 + j > i) t[r4 + j] -= av[j] * t[i];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Tb[w][r][lane] = (__bf16)t[r];
-        }
-        __syncthreads();
-
-        // ---- 3: A (waves 0, 1) and P (waves 2, 3) below the diagonal, three tiles per wave
-        {
-            const bool isP = w >= 2;
+            // ---- 3b: A (waves 4, 5) and P (waves 6, 7) below the diagonal, three tiles a wave
+            const bool isP = w >= 6;
 #pragma unroll
             for (int tt = 0; tt < 3; ++tt) {
                 int b, bp;
-                offdiag_tile(2 * tt + u, b, bp);
+                offdiag_tile(2 * tt + hf, b, bp);
                 const __bf16* rowp = isP ? &sm.Qr[16 * b + l16][8 * g4] : &sm.Kr[16 * b + l16][8 * g4];
                 const __bf16* colp = &sm.Kc[kc_off(b) + 16 * bp + l16][8 * g4];
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -803,22 +883,24 @@ __global__ __launch_bounds__(NTH) void chg_prep_kernel(PrefillArgs a, long nitem
 
         // ---- 4: K o e^G and Q o e^G over the column operands
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            *reinterpret_cast<uint32_t*>(&sm.Kc[16 * w + i][2 * lane]) = pke[i];
-            *reinterpret_cast<uint32_t*>(&sm.Kc[CC + 16 * w + i][2 * lane]) = pqe[i];
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * blk + 8 * hf + i;
+            *reinterpret_cast<uint32_t*>(&sm.Kc[r][2 * lane]) = pke[i];
+            *reinterpret_cast<uint32_t*>(&sm.Kc[CC + r][2 * lane]) = pqe[i];
         }
         __syncthreads();
 
         // ---- out: this item's operands to its workspace record
         char* rec = static_cast<char*>(a.ws) + item * OP_BYTES;
-        for (int e = tid; e < 1024; e += NTH) {
+#pragma unroll
+        for (int e = tid; e < 1024; e += NPP) {
             const int r = e >> 4, p = e & 15;
             *reinterpret_cast<u32x4v*>(rec + OP_KE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[r][8 * p]);
             *reinterpret_cast<u32x4v*>(rec + OP_QE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[CC + r][8 * p]);
             *reinterpret_cast<u32x4v*>(rec + OP_KD + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kd[r][8 * p]);
         }
-        for (int e = tid; e < 512; e += NTH) {
-            const int r = e >> 3, p = e & 7;
+        {
+            const int r = tid >> 3, p = tid & 7;
             *reinterpret_cast<u32x4v*>(rec + OP_A + r * 128 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.A[r][8 * p]);
             *reinterpret_cast<u32x4v*>(rec + OP_P + r * 128 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.P[r][8 * p]);
         }
@@ -1119,7 +1201,7 @@ hipError_t launch_prefill_chg(const PrefillArgs& a, hipStream_t s) {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 256;
         const long prep = items < cus ? items : cus;   // one workgroup per CU (its LDS allows no more)
-        hipLaunchKernelGGL(chg_prep_kernel, dim3((unsigned)prep), dim3(NTH), 0, s, a, items);
+        hipLaunchKernelGGL(chg_prep_kernel, dim3((unsigned)prep), dim3(NPP), 0, s, a, items);
         hipLaunchKernelGGL(chg_chain_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
     } else {
         hipLaunchKernelGGL(prefill_chg_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
