@@ -23,8 +23,8 @@ pass at B1 or B4) for a rocprofv3 counter pass per workload.  The decode step (2
 state updated in place) is timed with events around a loop of back-to-back steps and
 reported in the same line, and so is the chunkwise reverse pass (dn_chunk_bwd) on the gated
 H16 T2048 shape at B1 and B4 (20 calls between events, own roofline block under
-``chunk_backward``), and the gated d_k = d_v = 64 prompt of the layer's shape on its
-two-launch path (``prompt_d64``).  The fp64 oracle is timed on the host cores on a bounded
+``chunk_backward``), and the gated d_k = d_v = 64 prompt of the layer's shape on the same
+one-launch kernel at d = 64 (``prompt_d64``).  The fp64 oracle is timed on the host cores on a bounded
 sample of the prefill workload.
 
 Prints ONE JSON line.
@@ -220,11 +220,10 @@ def only_part(what, dn, dev, reps, warmup):
         B = PREFILL["B"]
         x64 = make_case(B=B, T=T, Hqk=H, Dk=64, dtype="bf16", g_scale=0.1, seed=0)
         q, k, v, b, g = (to_dev(a_) for a_ in (x64.q, x64.k, x64.v, x64.beta, x64.g))
-        ws = torch.empty(dn.workspace_bytes(B, T, H, H, 64, 64, torch.bfloat16), dtype=torch.uint8, device=dev)
         o = torch.empty((B, T, H, 64), dtype=torch.bfloat16, device=dev)
         s = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev)
-        calls.append(("d64 prompt (two launches)",
-                      lambda i: dn.chunk_fwd(q, k, v, b, g, None, out=o, final_state=s, workspace=ws)))
+        calls.append(("d64 prompt (one launch)",
+                      lambda i: dn.chunk_fwd(q, k, v, b, g, None, out=o, final_state=s)))
     else:
         bb = 1 if what == "chunk_bwd1" else 4
         T, H, D = PREFILL["T"], PREFILL["H"], PREFILL["D"]
@@ -331,7 +330,7 @@ def main():
         z_us = e0.elapsed_time(e1) * 1e3 / reps
         init = z.init is not None
         zb = prefill_bytes(z.B, z.T, z.Hqk, z.Hv, z.Dk, gated=z.g is not None, N=z.num_seqs, init=init)
-        kern = "fused_kernel<%s, false>" % ("true" if z.g is not None else "false")
+        kern = "fused_kernel<128, %s, false>" % ("true" if z.g is not None else "false")
         blk = prefill_roofline(f"prefill_config{cfg}", kern, z_us, zb, z.B * z.T, z.Hqk, z.Hv, z.Dk)
         del zsets, zcu
         return dict(workload=PREFILL_WHAT[cfg], **blk)
@@ -405,7 +404,7 @@ def main():
     tokens = B * T
     alg_b = prefill_bytes(B, T, Hqk, Hv, D, gated=False, N=B, init=False)
     traffic_d = load_traffic("decode_bytes_per_call")
-    head_block = prefill_roofline("prefill_config2", "fused_kernel<false, false>", call_us, alg_b,
+    head_block = prefill_roofline("prefill_config2", "fused_kernel<128, false, false>", call_us, alg_b,
                                   tokens, Hqk, Hv, D)
 
     # ------------------------------------ the other two full-size prefill workloads, right
@@ -476,7 +475,7 @@ def main():
     in_rule_norm = {
         "what": "q and k handed raw (N(0,1) draws) and L2-normalised inside the call "
                 "(DN_QK_L2NORM, eps 1e-6); same workloads, same timing as above",
-        "prefill": {"kernel": "fused_kernel<false, true>", "us_per_call": norm_us,
+        "prefill": {"kernel": "fused_kernel<128, false, true>", "us_per_call": norm_us,
                     "tokens_per_s": tokens / (norm_us * 1e-6),
                     "hbm_frac": alg_b / (norm_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                     "traffic": load_traffic("prefill_qk_l2norm_bytes_per_call"),
@@ -616,32 +615,30 @@ def main():
                  "us_per_call": rec_us, "tokens_per_s": tokens / (rec_us * 1e-6),
                  "vs_chunked_call": rec_us / call_us}
 
-    # ------------- the d = 64 prompt (two launches: T and P of every chunk, then the chain)
+    # ------------- the d = 64 prompt (the one-launch kernel at d_k = d_v = 64)
     x64 = make_case(B=B, T=T, Hqk=Hqk, Dk=64, dtype="bf16", g_scale=0.1, seed=0)
     q64, k64, v64, b64, g64 = (to_dev(a_) for a_ in (x64.q, x64.k, x64.v, x64.beta, x64.g))
-    ws64 = torch.empty(dn.workspace_bytes(B, T, Hqk, Hv, 64, 64, torch.bfloat16), dtype=torch.uint8, device=dev)
     o64 = torch.empty((B, T, Hv, 64), dtype=torch.bfloat16, device=dev)
     s64 = torch.empty((B, Hv, 64, 64), dtype=torch.float32, device=dev)
     for _ in range(3):
-        dn.chunk_fwd(q64, k64, v64, b64, g64, None, out=o64, final_state=s64, workspace=ws64)
+        dn.chunk_fwd(q64, k64, v64, b64, g64, None, out=o64, final_state=s64)
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(10):
-        dn.chunk_fwd(q64, k64, v64, b64, g64, None, out=o64, final_state=s64, workspace=ws64)
+    for _ in range(20):
+        dn.chunk_fwd(q64, k64, v64, b64, g64, None, out=o64, final_state=s64)
     ev1.record(stream)
     torch.cuda.synchronize()
-    d64_us = ev0.elapsed_time(ev1) * 1e3 / 10
+    d64_us = ev0.elapsed_time(ev1) * 1e3 / 20
     d64_b = prefill_bytes(B, T, Hqk, Hv, 64, True, B, False)
     prompt_d64 = {"workload": f"gated prefill B{B} H{Hv} T{T} d_k=d_v=64 bf16, chunk 64",
                   "path": dn.chunk_fwd_path(B, T, Hqk, Hv, 64, 64, torch.bfloat16),
-                  "kernels": "chunk_tp_kernel<64> + split_chain_kernel", "us_per_call": d64_us,
-                  "tokens_per_s": tokens / (d64_us * 1e-6), "workspace_bytes": ws64.numel(),
+                  "kernels": "fused_kernel<64, true, false>", "us_per_call": d64_us,
+                  "tokens_per_s": tokens / (d64_us * 1e-6),
                   "roofline": {"bound": "hbm", "achieved": d64_b / (d64_us * 1e-6) / 1e9,
                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": d64_b / (d64_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                "algorithmic_bytes": d64_b,
                                "traffic": load_traffic("prompt_d64_bytes_per_call")}}
-    del ws64
 
     # ------------- the chunkwise reverse pass (dn_chunk_bwd), gated, H16 T2048, B1 and B4
     chunk_backward = {"what": "dL/dq, dk, dv, dbeta, dg and the initial state's gradient from "
@@ -667,7 +664,7 @@ def main():
         gflops = chunk_bwd_flops(bb * T, Hv, D, 64)
         chunk_backward[f"B{bb}"] = {
             "workload": f"B{bb} H{Hv} T{T} d{D} bf16, g = -0.1 softplus(z), zero initial state",
-            "kernels": "fused_kernel<true, false, true> (chunk-start states, second stream) + "
+            "kernels": "fused_kernel<128, true, false, true> (chunk-start states, second stream) + "
                        "chunk_tp_kernel (T, P) + chunk_carry_kernel (dL/dM per chunk) + "
                        "chunk_grad_kernel<true> (gradients per chunk)",
             "us_per_call": gb_us, "tokens_per_s": bb * T / (gb_us * 1e-6),

@@ -177,7 +177,7 @@ def workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: 
                     num_seqs: Optional[int] = None, chunk_size: int = 64,
                     g_per_key: bool = False, qk_l2norm: bool = False) -> int:
     """Device workspace (bytes) ``dn_chunk_fwd`` needs for these sizes (only the two-kernel
-    matrix-core paths use one: a log decay per key channel at d_k = 128, and d = 64)."""
+    matrix-core path of a log decay per key channel at d_k = 128 uses one)."""
     s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
                DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0,
                *_flags(qk_l2norm, 1e-6, g_per_key))
@@ -195,17 +195,16 @@ def chunk_bwd_workspace_bytes(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: in
 
 
 _PATHS = {-1: "invalid", 0: "fused", 1: "channel_gate_two_kernels", 2: "channel_gate_one_kernel",
-          3: "vector", 4: "two_kernels"}
+          3: "vector"}
 
 
 def chunk_fwd_path(B: int, T: int, Hqk: int, Hv: int, Dk: int, Dv: int, dtype: torch.dtype,
                    num_seqs: Optional[int] = None, chunk_size: int = 64, g_per_key: bool = False,
                    qk_l2norm: bool = False, workspace_bytes: Optional[int] = None) -> str:
-    """Which kernels ``chunk_fwd`` runs for these sizes: "fused" (one matrix-core kernel),
-    "channel_gate_two_kernels" / "channel_gate_one_kernel" (per-key-channel gates on the
-    matrix cores, with / without enough workspace), "two_kernels" (d = 64 on the matrix
-    cores: T and P per chunk, then the chunk chain; needs the workspace), "vector" (the
-    vector-ALU chunked kernel, about 100x slower), or "invalid".  ``workspace_bytes`` defaults to what
+    """Which kernels ``chunk_fwd`` runs for these sizes: "fused" (one matrix-core kernel, bf16
+    d = 128 or 64), "channel_gate_two_kernels" / "channel_gate_one_kernel" (per-key-channel
+    gates on the matrix cores, with / without enough workspace), "vector" (the vector-ALU
+    chunked kernel, about 100x slower), or "invalid".  ``workspace_bytes`` defaults to what
     :func:`chunk_fwd` allocates itself."""
     s = _Shape(B, T, B if num_seqs is None else num_seqs, Hqk, Hv, Dk, Dv,
                DN_BF16 if dtype == torch.bfloat16 else DN_F32, chunk_size, 1.0,

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libdeltanet.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = ["api.cpp", "decode.hip", "prefill_generic.hip", "prefill_fused.hip", "prefill_chg.hip",
            "epilogue.hip",
-           "recurrent.hip", "conv.hip", "chunk_bwd.hip", "prefill_split.hip"]
+           "recurrent.hip", "conv.hip", "chunk_bwd.hip", "chunk_tp.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -87,8 +87,8 @@ size_t dn_chunk_fwd_workspace_bytes(const dn_shape* s) {
     dn::PrefillArgs a;
     const bool packed = s && s->B == 1 && s->num_seqs != 1;
     if (prefill_shape(s, packed, a) != DN_OK) return 0;
-    // the two-kernel paths keep per-chunk operands in HBM (at most one of the two applies)
-    return dn::prefill_chg_workspace_bytes(a) + dn::prefill_split_workspace_bytes(a);
+    // the two-kernel channel-gate path keeps per-chunk operands in HBM
+    return dn::prefill_chg_workspace_bytes(a);
 }
 
 int32_t dn_chunk_fwd_path(const dn_shape* s, size_t ws_bytes) {
@@ -100,22 +100,20 @@ int32_t dn_chunk_fwd_path(const dn_shape* s, size_t ws_bytes) {
         const size_t need = dn::prefill_chg_workspace_bytes(a);
         return ws_bytes >= need ? DN_PATH_CHANNEL_GATE_TWO_KERNELS : DN_PATH_CHANNEL_GATE_ONE_KERNEL;
     }
-    if (dn::prefill_split_supported(a))
-        return ws_bytes >= dn::prefill_split_workspace_bytes(a) ? DN_PATH_TWO_KERNELS : DN_PATH_VECTOR;
     return dn::prefill_fused_supported(a) ? DN_PATH_FUSED : DN_PATH_VECTOR;
 }
 
 dn_status dn_chunk_fwd_noalloc(const dn_shape* s, const void* q, const void* k, const void* v,
                                const float* beta, const float* g, const float* h0, float* hT,
                                const int32_t* cu, void* o, hipStream_t stream) {
-    // Only the two-kernel paths need scratch; they get the static array (the checks that
-    // follow in dn_chunk_fwd see a workspace of exactly the array's size).
+    // Only the two-kernel channel-gate path needs scratch; it gets the static array (the
+    // checks that follow in dn_chunk_fwd see a workspace of exactly the array's size).
     dn::PrefillArgs a;
     dn_status st = prefill_shape(s, cu != nullptr, a);
     if (st != DN_OK) return st;
     void* ws = nullptr;
     size_t ws_bytes = 0;
-    const size_t need = dn::prefill_chg_workspace_bytes(a) + dn::prefill_split_workspace_bytes(a);
+    const size_t need = dn::prefill_chg_workspace_bytes(a);
     if (need > 0) {
         if (need > dn::noalloc_scratch_bytes()) return DN_ERR_WORKSPACE;
         if (dn::noalloc_scratch(&ws) != hipSuccess) return DN_ERR_HIP;
@@ -146,8 +144,6 @@ dn_status dn_chunk_fwd(const dn_shape* s, const void* q, const void* k, const vo
     hipError_t e;
     if (dn::prefill_fused_supported(a)) {
         e = dn::launch_prefill_fused(a, stream);
-    } else if (dn::prefill_split_supported(a) && ws && ws_bytes >= dn::prefill_split_workspace_bytes(a)) {
-        e = dn::launch_prefill_split(a, stream);
     } else {
         e = dn::launch_prefill_generic(a, stream);
     }

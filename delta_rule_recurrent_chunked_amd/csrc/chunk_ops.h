@@ -1,5 +1,5 @@
-// chunk_ops.h -- device helpers shared by the two-launch prompt (prefill_split.hip) and the
-// chunkwise reverse pass (chunk_bwd.hip): MFMA operand fragments out of LDS, tile stores,
+// chunk_ops.h -- device helpers shared by the T/P kernel (chunk_tp.hip) and the chunkwise
+// reverse pass (chunk_bwd.hip): MFMA operand fragments out of LDS, tile stores,
 // DPP lane sums, the in-chunk decay scan, buffer loads, and the chunk numbering of the
 // workspace records.
 #pragma once

@@ -165,10 +165,6 @@ hipError_t launch_prefill_fused_states(const PrefillArgs& a, hipStream_t s);
 // T^T and P (bf16, 64 x 64 each) of every (chunk number < ncid, value head) to tp, one
 // 16 KiB record each: record cid * Hv + h, or h * ncid + cid when head_major
 hipError_t launch_chunk_tp(const PrefillArgs& a, long ncid, void* tp, bool head_major, hipStream_t s);
-// the two-launch prompt (bf16 d = 64): T and P to a.ws, then the chunk chain
-bool prefill_split_supported(const PrefillArgs& a);
-size_t prefill_split_workspace_bytes(const PrefillArgs& a);
-hipError_t launch_prefill_split(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace dn
 

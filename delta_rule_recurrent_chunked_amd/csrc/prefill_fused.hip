@@ -65,9 +65,7 @@ namespace dn {
 namespace {
 
 constexpr int FC = 64;             // chunk
-constexpr int FD = 128;            // Dk = Dv
 constexpr int DVS = 32;            // state columns per workgroup
-constexpr int NSL = FD / DVS;      // slices per (sequence, value head)
 constexpr int CW = 16;             // state columns per chain wave
 constexpr int NCW = DVS / CW;      // chain waves
 // bf16 row pitches.  gfx950's LDS serves a 16-byte-per-lane read 32 lanes at a time
@@ -76,7 +74,6 @@ constexpr int NCW = DVS / CW;      // chain waves
 // offsets (pitch in dwords x row, mod 128) must be distinct multiples of 8: 72 dwords for
 // the 128-wide K and Q rows, 40 for the 64-wide T and A rows.  V (read only transposed,
 // 16 rows x 8 dwords) takes 24.
-constexpr int KPITCH = FD + 16;
 constexpr int CPITCH = FC + 16;
 constexpr int VPITCH = DVS + 16;
 // A's diagonal blocks, 120 packed fp16 entries each (+ a spare slot), 68 dwords apart: the
@@ -85,6 +82,21 @@ constexpr int ADPITCH = 136;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int NT = 512;            // threads (8 waves)
 constexpr int NLD = 128;           // loader threads (waves 4, 5)
+
+// What depends on the head size D = Dk = Dv (64 or 128): the K and Q rows, the 32-key steps
+// of a product over keys, the 16-key tiles of a state slice, the slices of a head, and the
+// 16-byte pieces of K (and Q) each loader lane moves per chunk.
+template <int D>
+struct Dims {
+    static_assert(D == 64 || D == 128, "head size");
+    static constexpr int KPITCH = D + 16;          // bf16 pitch of K and Q rows (72 or 40 dwords)
+    static constexpr int NKS = D / 32;             // 32-key steps
+    static constexpr int NKT = D / 16;             // 16-key tiles of the state
+    static constexpr int NSL = D / DVS;            // slices per (sequence, value head)
+    static constexpr int PPR = D / 8;              // 16-byte pieces per K row (a power of 2)
+    static constexpr int PPR_LOG = D == 128 ? 4 : 3;
+    static constexpr int NKP = FC * PPR / NLD;     // K pieces per loader lane
+};
 
 // Per-token scalars of a chunk.  With e(I) = 16 I + 15 the last token of 16-token block I,
 // exp(gamma_r - gamma_i) for i in block I < block of r factors as
@@ -95,23 +107,25 @@ constexpr int NLD = 128;           // loader threads (waves 4, 5)
 enum Sc { SC_BETA = 0, SC_GAM = 1, SC_EG = 2, SC_TAIL = 3, SC_F2 = 4, SC_F1 = 5,
           SC_B1 = 8, SC_B2 = 9, SC_S2 = 10, SC_N = 11 };
 
+template <int D>
 struct alignas(16) FusedSmem {
-    __bf16 K[2][FC][KPITCH];       // chunk keys, token-major (chunk j in K[j & 1])
-    __bf16 Q[2][FC][KPITCH];       // chunk queries, token-major
+    __bf16 K[2][FC][Dims<D>::KPITCH];   // chunk keys, token-major (chunk j in K[j & 1])
+    __bf16 Q[2][FC][Dims<D>::KPITCH];   // chunk queries, token-major
     __bf16 V[FC][VPITCH];          // value slice of the next chunk the chain reads
     __bf16 Tt[FC][CPITCH];         // T^T of the chunk being processed
     __bf16 Ab[FC][CPITCH];         // A in bf16 (blocks below the 16x16 block diagonal)
     _Float16 Ad[4][ADPITCH];       // A's diagonal 16x16 blocks, fp16, strictly lower part
                                    //   packed by rows: (r, m), m < r, at r (r - 1) / 2 + m
-    bf16x8 mb[2][NCW][4][64];      // chain -> output: bf16 state as B operands (k = key)
+    bf16x8 mb[2][NCW][Dims<D>::NKS][64];   // chain -> output: bf16 state as B operands (k = key)
     bf16x8 dd[NCW][2][64];         // chain -> output: Delta as B operands (k = token)
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
     int seq_len[NT];               // packed batches of up to 512 sequences: their lengths,
     int rank_seq[NT];              //   and the sequence of each length rank
 };
 
+template <int D>
 struct LoadSet {
-    uint4 k[8], q[8], v[2];
+    uint4 k[Dims<D>::NKP], q[Dims<D>::NKP], v[2];
     float beta, g;
 };
 
@@ -128,23 +142,25 @@ struct Geo {  // where this workgroup works
 // unconditional, and each lane keeps one 32-bit offset per 16-byte piece.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+template <int D>
 struct Streams {
     __amdgpu_buffer_rsrc_t k, q, v, beta, g;
     uint32_t kq_chunk, v_chunk, s_chunk;   // bytes per chunk of 64 tokens
-    uint32_t off_kq[8], off_v[2], off_s;   // this lane's piece offsets within a chunk
+    uint32_t off_kq[Dims<D>::NKP], off_v[2], off_s;   // this lane's piece offsets within a chunk
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w, int lt, Streams& st) {
+template <int D>
+__device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w, int lt, Streams<D>& st) {
     const long L = w.eos - w.bos;           // tokens of this sequence
-    const uint32_t kq_tok = (uint32_t)a.Hqk * FD * 2, v_tok = (uint32_t)a.Hv * FD * 2, s_tok = (uint32_t)a.Hv * 4;
-    const uint32_t kq_end = L > 0 ? (uint32_t)((L - 1) * kq_tok + FD * 2) : 0;
+    const uint32_t kq_tok = (uint32_t)a.Hqk * D * 2, v_tok = (uint32_t)a.Hv * D * 2, s_tok = (uint32_t)a.Hv * 4;
+    const uint32_t kq_end = L > 0 ? (uint32_t)((L - 1) * kq_tok + D * 2) : 0;
     const uint32_t v_end = L > 0 ? (uint32_t)((L - 1) * v_tok + DVS * 2) : 0;
     const uint32_t s_end = L > 0 ? (uint32_t)((L - 1) * s_tok + 4) : 0;
-    const long kq0 = (w.bos * a.Hqk + w.hq) * FD, v0 = (w.bos * a.Hv + w.h) * FD + w.j0, s0 = w.bos * a.Hv + w.h;
+    const long kq0 = (w.bos * a.Hqk + w.hq) * D, v0 = (w.bos * a.Hv + w.h) * D + w.j0, s0 = w.bos * a.Hv + w.h;
     st.k = rsrc(static_cast<const __bf16*>(a.k) + kq0, kq_end);
     st.q = rsrc(static_cast<const __bf16*>(a.q) + kq0, kq_end);
     st.v = rsrc(static_cast<const __bf16*>(a.v) + v0, v_end);
@@ -154,9 +170,9 @@ __device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w,
     st.v_chunk = FC * v_tok;
     st.s_chunk = FC * s_tok;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < Dims<D>::NKP; ++p) {
         const int v = lt + NLD * p;
-        st.off_kq[p] = (uint32_t)(v >> 4) * kq_tok + (v & 15) * 16;
+        st.off_kq[p] = (uint32_t)(v >> Dims<D>::PPR_LOG) * kq_tok + (v & (Dims<D>::PPR - 1)) * 16;
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -168,7 +184,8 @@ __device__ __forceinline__ void make_streams(const PrefillArgs& a, const Geo& w,
 
 __device__ __forceinline__ uint4 u4(u32x4 x) { return make_uint4(x[0], x[1], x[2], x[3]); }
 
-__device__ __forceinline__ void fetch(const Streams& st, int j, LoadSet& f) {
+template <int D>
+__device__ __forceinline__ void fetch(const Streams<D>& st, int j, LoadSet<D>& f) {
     // the chunk offset goes into the per-lane offset, which the range check covers
     // issued in the order of use (loads complete in order): the scalars and K, which the
     // first half takes, before Q and V
@@ -176,10 +193,10 @@ __device__ __forceinline__ void fetch(const Streams& st, int j, LoadSet& f) {
     f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.beta, st.off_s + cs, 0, 0));
     f.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.g, st.off_s + cs, 0, 0));
 #pragma unroll
-    for (int p = 0; p < 8; ++p) f.k[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.k, st.off_kq[p] + ckq, 0, 0));
+    for (int p = 0; p < Dims<D>::NKP; ++p) f.k[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.k, st.off_kq[p] + ckq, 0, 0));
     sched_fence();
 #pragma unroll
-    for (int p = 0; p < 8; ++p) f.q[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.q, st.off_kq[p] + ckq, 0, 0));
+    for (int p = 0; p < Dims<D>::NKP; ++p) f.q[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.q, st.off_kq[p] + ckq, 0, 0));
 #pragma unroll
     for (int p = 0; p < 2; ++p) f.v[p] = u4(__builtin_amdgcn_raw_buffer_load_b128(st.v, st.off_v[p] + cv, 0, 0));
 }
@@ -194,10 +211,11 @@ __device__ __forceinline__ float lane_f32(float x, int l) {
 }
 
 // K and the per-token scalars of chunk j (rows past the sequence end hold zeros)
-__device__ __forceinline__ void put_k(FusedSmem& sm, int j, int lt, const LoadSet& f) {
+template <int D>
+__device__ __forceinline__ void put_k(FusedSmem<D>& sm, int j, int lt, const LoadSet<D>& f) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int v = lt + NLD * p, row = v >> 4, cg = v & 15;
+    for (int p = 0; p < Dims<D>::NKP; ++p) {
+        const int v = lt + NLD * p, row = v >> Dims<D>::PPR_LOG, cg = v & (Dims<D>::PPR - 1);
         *reinterpret_cast<uint4*>(&sm.K[j & 1][row][cg * 8]) = f.k[p];
     }
     if (lt < FC) {  // one wave: inclusive scan of the log decays over the chunk (DPP)
@@ -222,15 +240,17 @@ __device__ __forceinline__ void put_k(FusedSmem& sm, int j, int lt, const LoadSe
 }
 
 // Q of chunk j
-__device__ __forceinline__ void put_q(FusedSmem& sm, int j, int lt, const LoadSet& f) {
+template <int D>
+__device__ __forceinline__ void put_q(FusedSmem<D>& sm, int j, int lt, const LoadSet<D>& f) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int v = lt + NLD * p, row = v >> 4, cg = v & 15;
+    for (int p = 0; p < Dims<D>::NKP; ++p) {
+        const int v = lt + NLD * p, row = v >> Dims<D>::PPR_LOG, cg = v & (Dims<D>::PPR - 1);
         *reinterpret_cast<uint4*>(&sm.Q[j & 1][row][cg * 8]) = f.q[p];
     }
 }
 
-__device__ __forceinline__ void put_v(FusedSmem& sm, int lt, const LoadSet& f) {
+template <int D>
+__device__ __forceinline__ void put_v(FusedSmem<D>& sm, int lt, const LoadSet<D>& f) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int v = lt + NLD * p;
@@ -242,11 +262,13 @@ __device__ __forceinline__ void put_v(FusedSmem& sm, int lt, const LoadSet& f) {
 // Key fragments of one chunk as 16x16x32 operands: kf[X][s] = rows 16 X + l16, keys
 // 32 s + 8 q16 .. +7.  The same fragment serves as A operand (rows of the tile) and as
 // B operand (columns of the tile) of a product contracting over keys.
-__device__ __forceinline__ void load_rows(const __bf16 (*src)[KPITCH], int l16, int q16, bf16x8 (&f)[4][4]) {
+template <int D>
+__device__ __forceinline__ void load_rows(const __bf16 (*src)[Dims<D>::KPITCH], int l16, int q16,
+                                          bf16x8 (&f)[4][Dims<D>::NKS]) {
 #pragma unroll
     for (int X = 0; X < 4; ++X)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) f[X][s] = ld8(&src[16 * X + l16][32 * s + 8 * q16]);
+        for (int s = 0; s < Dims<D>::NKS; ++s) f[X][s] = ld8(&src[16 * X + l16][32 * s + 8 * q16]);
 }
 
 // A and P come from 16x16 tiles (I, R), I <= R, of K K^T and K Q^T: tile (I, R) holds
@@ -292,8 +314,8 @@ constexpr int a_tile_r(int part, int n) { return part == 0 ? n : part == 1 ? 2 *
 // tiles, scales A's rows by s_r^2 and publishes the chain's factors (SC_B1, SC_B2, SC_S2)
 // for row 16 q16 + l16.  Parts 1 and 2 write their tiles with beta alone; their consumers
 // apply s_r^2 to the rows of the products they form from them.
-template <bool GATED, bool NORM, int PART>
-__device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16, float eps) {
+template <int D, bool GATED, bool NORM, int PART>
+__device__ __forceinline__ void make_a(FusedSmem<D>& sm, int j, int l16, int q16, float eps) {
     constexpr bool NRM = NORM && PART == 0;
     constexpr int NTL = a_tiles(PART);
     // every LDS read before the first store (a read after a store waits a round trip)
@@ -308,14 +330,14 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16, f
     }
     float egq = 1.f;
     if (NRM) egq = s[SC_EG * FC + 16 * q16 + l16];
-    bf16x8 kf[4][4];
-    load_rows(sm.K[j & 1], l16, q16, kf);
+    bf16x8 kf[4][Dims<D>::NKS];
+    load_rows<D>(sm.K[j & 1], l16, q16, kf);
     sched_fence();  // all fragments in one round trip (the compiler would stage them)
     f32x4 G[NTL];
 #pragma unroll
     for (int n = 0; n < NTL; ++n) G[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < Dims<D>::NKS; ++ks)
 #pragma unroll
         for (int n = 0; n < NTL; ++n)
             G[n] = mma16(kf[a_tile_i(PART, n)][ks], kf[a_tile_r(PART, n)][ks], G[n]);
@@ -356,7 +378,8 @@ __device__ __forceinline__ void make_a(FusedSmem& sm, int j, int l16, int q16, f
 
 // Diagonal block q16 of A (packed, as part 0 of make_a wrote it) into registers, by the
 // wave that wrote it: the UT inverse of the next half starts without an LDS round trip.
-__device__ __forceinline__ void load_ad(const FusedSmem& sm, int q16, f16x8 (&ap)[15]) {
+template <int D>
+__device__ __forceinline__ void load_ad(const FusedSmem<D>& sm, int q16, f16x8 (&ap)[15]) {
     wave_lds_order();
 #pragma unroll
     for (int g = 0; g < 15; ++g) ap[g] = *reinterpret_cast<const f16x8*>(&sm.Ad[q16][8 * g]);
@@ -373,9 +396,9 @@ constexpr int p_block(int half, int u) { return half == 0 ? (u == 0 ? 0 : 3) : (
 //
 // With the in-rule normalisation it also returns |q_r|^2 of its query rows (qn[u], row
 // 16 R_u + l16), the diagonal of Q Q^T tiles formed from the same fragments.
-template <bool GATED, bool NORM, int HALF>
-__device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 (&qf)[2][4], int l16, int q16,
-                                       bf16x8 (&pt)[2][2], float (&qn)[2]) {
+template <int D, bool GATED, bool NORM, int HALF>
+__device__ __forceinline__ void make_p(const FusedSmem<D>& sm, int j, const bf16x8 (&qf)[2][Dims<D>::NKS], int l16,
+                                       int q16, bf16x8 (&pt)[2][2], float (&qn)[2]) {
     const float* s = &sm.sc[j % 3][0][0];
     DecayIn din[2][4];
     if (GATED) {
@@ -386,15 +409,15 @@ __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 
             for (int I = 0; I <= R; ++I) din[u][I] = decay_load(s, R, I, r, 16 * I + 4 * q16);
         }
     }
-    bf16x8 kf[4][4];
-    load_rows(sm.K[j & 1], l16, q16, kf);
+    bf16x8 kf[4][Dims<D>::NKS];
+    load_rows<D>(sm.K[j & 1], l16, q16, kf);
     f32x4 G[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int I = 0; I < 4; ++I) G[u][I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < Dims<D>::NKS; ++ks)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int R = p_block(HALF, u);
@@ -406,7 +429,7 @@ __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 
         for (int u = 0; u < 2; ++u) {
             f32x4 gq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) gq = mma16(qf[u][ks], qf[u][ks], gq);
+            for (int ks = 0; ks < Dims<D>::NKS; ++ks) gq = mma16(qf[u][ks], qf[u][ks], gq);
             qn[u] = gram_diag(gq, l16);
         }
     }
@@ -440,8 +463,8 @@ __device__ __forceinline__ void make_p(const FusedSmem& sm, int j, const bf16x8 
 // With the in-rule normalisation the stored A21 rows lack s_r^2 (the tiles below the
 // block diagonal are written with beta alone): the product A21 T11 takes it per row, from
 // s2 = the chunk's SC_S2 scalars.
-template <bool NORM>
-__device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f16x8 (&ap)[15], const float* s2) {
+template <int D, bool NORM>
+__device__ __forceinline__ void make_t(FusedSmem<D>& sm, int l16, int q16, const f16x8 (&ap)[15], const float* s2) {
     {
         // lane = 16 * block + column c: solve (I + A_bb) x = e_c in the column order: once
         // x[m] is final, subtract its share from every later row.  ap holds the block's
@@ -500,9 +523,10 @@ __device__ __forceinline__ void make_t(FusedSmem& sm, int l16, int q16, const f1
 // (8 kb + cb) 256 floats, lane l's four entries (keys 16 kb + 4 (l >> 4) + e, column
 // 16 cb + (l & 15)) at 4 l, one 16-byte store each), the input of the chunkwise reverse pass;
 // the output waves skip O (that launch needs only the states).
-template <bool GATED, bool NORM, bool STATES = false>
+template <int D, bool GATED, bool NORM, bool STATES = false>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void fused_kernel(PrefillArgs a) {
-    __shared__ FusedSmem sm;
+    constexpr int NKS = Dims<D>::NKS, NKT = Dims<D>::NKT, NSL = Dims<D>::NSL, KPITCH = Dims<D>::KPITCH;
+    __shared__ FusedSmem<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q16 = lane >> 4;
 
@@ -557,26 +581,26 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         // ------------------------------------------------------------ chain waves
         const int jc = CW * wave;
         __builtin_amdgcn_s_setprio(2);  // the sequential chain goes first on its SIMD
-        f32x4 M[8];  // tile mt: keys 16 mt + 4 q16 + e, column jc + l16 of the slice
+        f32x4 M[NKT];  // tile mt: keys 16 mt + 4 q16 + e, column jc + l16 of the slice
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < NKT; ++mt) M[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (a.h0) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < NKT; ++mt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    M[mt][e] = a.h0[((long)w.nh * FD + 16 * mt + 4 * q16 + e) * FD + w.j0 + jc + l16];
+                    M[mt][e] = a.h0[((long)w.nh * D + 16 * mt + 4 * q16 + e) * D + w.j0 + jc + l16];
         }
-        bf16x8 mb[4];  // the state at the chunk start as B operands: k = key 32 s + 8 q16 + e
+        bf16x8 mb[NKS];  // the state at the chunk start as B operands: k = key 32 s + 8 q16 + e
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NKS; ++s) {
             mb[s] = acc_to_b(M[2 * s], M[2 * s + 1]);
             sm.mb[0][wave][s][lane] = mb[s];
         }
         __syncthreads();
         __syncthreads();
         float* st_out = nullptr;   // STATES: this chain wave's columns of chunk 0's start state
-        if (STATES) st_out = static_cast<float*>(a.ws) + ((long)chunk_id_base(a, w.n) * a.Hv + w.h) * FD * FD +
+        if (STATES) st_out = static_cast<float*>(a.ws) + ((long)chunk_id_base(a, w.n) * a.Hv + w.h) * D * D +
                              ((w.j0 + jc) / 16) * 256 + 4 * lane;
         for (int j = 0; j < nph; ++j) {
             const bool live = j < nc;
@@ -584,9 +608,9 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             bf16x8 rb0;   // R rows 0..31 as B operand (k = token)
             f32x4 R[4];   // R, token tile t: tokens 16 t + 4 q16 + e, column jc + l16
             if (STATES && live) {
-                float* dst = st_out + (long)j * a.Hv * FD * FD;
+                float* dst = st_out + (long)j * a.Hv * D * D;
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 8 * 256) = M[mt];
+                for (int mt = 0; mt < NKT; ++mt) *reinterpret_cast<f32x4*>(dst + mt * NKT * 256) = M[mt];
             }
             if (live) {
                 // X = K M: token tile t holds tokens 16 t + 4 q16 + e, column jc + l16
@@ -594,7 +618,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                 for (int t = 0; t < 4; ++t) X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         X[t] = mma16(ld8(&sm.K[j & 1][16 * t + l16][32 * ks + 8 * q16]), mb[ks], X[t]);
@@ -641,13 +665,13 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
                     for (int t = 0; t < 4; ++t) tl[t] = *reinterpret_cast<const f32x4*>(&s[SC_TAIL * FC + 16 * t + 4 * q16]);
                     Gl = s[SC_EG * FC + FC - 1];
                 }
-                f32x4 D[4];
+                f32x4 Dl[4];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const __bf16* src = &sm.Tt[8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
-                    D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
+                    Dl[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
                 }
-                const bf16x8 dtop = acc_to_b(-D[0], -D[1]);
+                const bf16x8 dtop = acc_to_b(-Dl[0], -Dl[1]);
 #pragma unroll
                 for (int t = 2; t < 4; ++t) {
                     if (NORM) R[t] += s2bl[t - 2] * mma16(abl[t - 2], dtop, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -657,33 +681,33 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                 for (int t = 2; t < 4; ++t) {
                     const __bf16* src = &sm.Tt[32 + 8 * q16 + (l16 >> 2)][16 * t + 4 * (l16 & 3)];
-                    D[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), zb, f32x4{0.f, 0.f, 0.f, 0.f});
+                    Dl[t] = mma16(cat(trld(src), trld(src + 4 * CPITCH)), zb, f32x4{0.f, 0.f, 0.f, 0.f});
                 }
                 bf16x8 db[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    db[u] = acc_to_b(D[2 * u], D[2 * u + 1]);
+                    db[u] = acc_to_b(Dl[2 * u], Dl[2 * u + 1]);
                     sm.dd[wave][u][lane] = db[u];
                 }
                 if (GATED) {  // Delta~ = diag(exp(gamma_last - gamma)) Delta for the state update
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) D[t] *= tl[t];
-                    db[0] = acc_to_b(D[0], D[1]);
-                    db[1] = acc_to_b(D[2], D[3]);
+                    for (int t = 0; t < 4; ++t) Dl[t] *= tl[t];
+                    db[0] = acc_to_b(Dl[0], Dl[1]);
+                    db[1] = acc_to_b(Dl[2], Dl[3]);
 #pragma unroll
-                    for (int mt = 0; mt < 8; ++mt) M[mt] *= Gl;
+                    for (int mt = 0; mt < NKT; ++mt) M[mt] *= Gl;
                 }
                 // M <- exp(gamma_last) M + K^T Delta~  (rows past the chunk end add g = 0)
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int mt = 0; mt < 8; ++mt) {
+                    for (int mt = 0; mt < NKT; ++mt) {
                         // A operand K^T[16 mt + m][k] = K[k][16 mt + m], k = 32 u + 8 q16 + e
                         const __bf16* src = &sm.K[j & 1][32 * u + 8 * q16 + (l16 >> 2)][16 * mt + 4 * (l16 & 3)];
                         M[mt] = mma16(cat(trld(src), trld(src + 4 * KPITCH)), db[u], M[mt]);
                     }
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
+                for (int s4 = 0; s4 < NKS; ++s4) {
                     mb[s4] = acc_to_b(M[2 * s4], M[2 * s4 + 1]);
                     sm.mb[(j + 1) & 1][wave][s4][lane] = mb[s4];
                 }
@@ -692,10 +716,10 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         }
         if (a.hT) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < NKT; ++mt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    a.hT[((long)w.nh * FD + 16 * mt + 4 * q16 + e) * FD + w.j0 + jc + l16] = M[mt][e];
+                    a.hT[((long)w.nh * D + 16 * mt + 4 * q16 + e) * D + w.j0 + jc + l16] = M[mt][e];
         }
     } else if (wave == 3 || wave == 7) {
         // ----------------------------------------------------------- output waves
@@ -710,13 +734,13 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         // of the slice, so rows past the sequence end are dropped by the range check.  The
         // other slices of the row, on the same XCD, fill the rest of its cache lines.
         const long L = w.eos - w.bos;
-        const uint32_t o_tok = (uint32_t)a.Hv * FD * 2;
+        const uint32_t o_tok = (uint32_t)a.Hv * D * 2;
         const __amdgpu_buffer_rsrc_t o_rs =
-            rsrc(static_cast<__bf16*>(a.o) + (w.bos * a.Hv + w.h) * FD + w.j0,
+            rsrc(static_cast<__bf16*>(a.o) + (w.bos * a.Hv + w.h) * D + w.j0,
                  L > 0 ? (uint32_t)((L - 1) * o_tok + DVS * 2) : 0);
         f32x4 yt[2][2];      // Y^T tile (u, c): columns 16 c + 4 q16 + e, query 16 R_u + l16
         bf16x8 pt[2][2];     // P^T of the chunk as B operands (make_p)
-        bf16x8 qf[2][4];     // query rows of R_u: qf[u][ks] = keys 32 ks + 8 q16 ..
+        bf16x8 qf[2][NKS];   // query rows of R_u: qf[u][ks] = keys 32 ks + 8 q16 ..
         float qn[2] = {0.f, 0.f};   // in-rule normalisation: |q_r|^2 of the rows of P^T
         __syncthreads();
         __syncthreads();
@@ -760,23 +784,23 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             if (y_live) {
                 // Y^T = M^T Q^T with the chain's bf16 state at the start of chunk j (written at
                 // the end of the previous phase)
-                bf16x8 m4[2][4];
+                bf16x8 m4[2][NKS];
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) m4[c][ks] = sm.mb[j & 1][c][ks][lane];
+                    for (int ks = 0; ks < NKS; ++ks) m4[c][ks] = sm.mb[j & 1][c][ks][lane];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int R = ow == 0 ? 3 * u : 1 + u;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) qf[u][ks] = ld8(&sm.Q[j & 1][16 * R + l16][32 * ks + 8 * q16]);
+                    for (int ks = 0; ks < NKS; ++ks) qf[u][ks] = ld8(&sm.Q[j & 1][16 * R + l16][32 * ks + 8 * q16]);
                 }
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int c = 0; c < 2; ++c) yt[u][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -784,17 +808,17 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
             }
             __syncthreads();
             if (y_live) {  // P of chunk j for the same query rows
-                if (ow == 0) make_p<GATED, NORM, 0>(sm, j, qf, l16, q16, pt, qn);
-                else make_p<GATED, NORM, 1>(sm, j, qf, l16, q16, pt, qn);
+                if (ow == 0) make_p<D, GATED, NORM, 0>(sm, j, qf, l16, q16, pt, qn);
+                else make_p<D, GATED, NORM, 1>(sm, j, qf, l16, q16, pt, qn);
             }
             __syncthreads();
         }
     } else if (wave == 4 || wave == 5) {
         // ---------------------------------------------------------------- loaders
         const int lt = tid - 256;
-        Streams st;
-        make_streams(a, w, lt, st);
-        LoadSet f0, f1;   // even chunks in f0, odd chunks in f1
+        Streams<D> st;
+        make_streams<D>(a, w, lt, st);
+        LoadSet<D> f0, f1;   // even chunks in f0, odd chunks in f1
         fetch(st, 0, f0);
         fetch(st, 1, f1);
         // phase -1: chunk 0
@@ -835,27 +859,27 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         // the longer steps of both halves; the other A wave has slack
         __builtin_amdgcn_s_setprio(2);
         __syncthreads();
-        make_a<GATED, NORM, 0>(sm, 0, l16, q16, a.eps);
-        load_ad(sm, q16, ap);
+        make_a<D, GATED, NORM, 0>(sm, 0, l16, q16, a.eps);
+        load_ad<D>(sm, q16, ap);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            if (j < nc) make_t<NORM>(sm, l16, q16, ap, &sm.sc[j % 3][SC_S2][0]);
+            if (j < nc) make_t<D, NORM>(sm, l16, q16, ap, &sm.sc[j % 3][SC_S2][0]);
             __syncthreads();
             if (j + 1 < nc) {
-                make_a<GATED, NORM, 0>(sm, j + 1, l16, q16, a.eps);
-                load_ad(sm, q16, ap);
+                make_a<D, GATED, NORM, 0>(sm, j + 1, l16, q16, a.eps);
+                load_ad<D>(sm, q16, ap);
             }
             __syncthreads();
         }
     } else {
         // ------------------ wave 2: A_BL of j in the first half, A21 of j + 1 in the second
         __syncthreads();
-        make_a<GATED, NORM, 1>(sm, 0, l16, q16, a.eps);
+        make_a<D, GATED, NORM, 1>(sm, 0, l16, q16, a.eps);
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
-            if (j < nc) make_a<GATED, NORM, 2>(sm, j, l16, q16, a.eps);
+            if (j < nc) make_a<D, GATED, NORM, 2>(sm, j, l16, q16, a.eps);
             __syncthreads();
-            if (j + 1 < nc) make_a<GATED, NORM, 1>(sm, j + 1, l16, q16, a.eps);
+            if (j + 1 < nc) make_a<D, GATED, NORM, 1>(sm, j + 1, l16, q16, a.eps);
             __syncthreads();
         }
     }
@@ -866,35 +890,43 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 bool prefill_fused_supported(const PrefillArgs& a) {
     // buffer offsets are 32-bit: a sequence (plus the two chunks fetched past its end) must
     // span less than 2 GiB of q / k / v / o
-    const long span = ((long)a.T + 2 * FC) * (a.Hqk > a.Hv ? a.Hqk : a.Hv) * FD * 2;
-    return a.bf16 && a.Dk == FD && a.Dv == FD && a.C == FC && !a.g_per_key && span < (1L << 31);
+    const long span = ((long)a.T + 2 * FC) * (a.Hqk > a.Hv ? a.Hqk : a.Hv) * a.Dk * 2;
+    return a.bf16 && a.Dk == a.Dv && (a.Dk == 128 || a.Dk == 64) && a.C == FC && !a.g_per_key &&
+           span < (1L << 31);
 }
 
 hipError_t launch_prefill_fused_states(const PrefillArgs& a, hipStream_t s) {
-    const long blocks = (long)a.N * a.Hv * NSL;
+    // the chunk-start states of the reverse pass (d = 128 only)
+    if (a.Dk != 128 || a.Dv != 128) return hipErrorInvalidValue;
+    const long blocks = (long)a.N * a.Hv * Dims<128>::NSL;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (blocks > 0) {
         const dim3 grid((unsigned)blocks), block(NT);
-        if (a.g) hipLaunchKernelGGL((fused_kernel<true, false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((fused_kernel<false, false, true>), grid, block, 0, s, a);
+        if (a.g) hipLaunchKernelGGL((fused_kernel<128, true, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((fused_kernel<128, false, false, true>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fused_d(const PrefillArgs& a, hipStream_t s) {
+    const long blocks = (long)a.N * a.Hv * Dims<D>::NSL;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (blocks > 0) {
+        const dim3 grid((unsigned)blocks), block(NT);
+        if (a.qk_norm) {
+            if (a.g) hipLaunchKernelGGL((fused_kernel<D, true, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((fused_kernel<D, false, true>), grid, block, 0, s, a);
+        } else {
+            if (a.g) hipLaunchKernelGGL((fused_kernel<D, true, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((fused_kernel<D, false, false>), grid, block, 0, s, a);
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t s) {
-    const long blocks = (long)a.N * a.Hv * NSL;
-    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (blocks > 0) {
-        const dim3 grid((unsigned)blocks), block(NT);
-        if (a.qk_norm) {
-            if (a.g) hipLaunchKernelGGL((fused_kernel<true, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((fused_kernel<false, true>), grid, block, 0, s, a);
-        } else {
-            if (a.g) hipLaunchKernelGGL((fused_kernel<true, false>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((fused_kernel<false, false>), grid, block, 0, s, a);
-        }
-    }
-    return hipGetLastError();
+    return a.Dk == 64 ? launch_fused_d<64>(a, s) : launch_fused_d<128>(a, s);
 }
 
 }  // namespace dn

@@ -130,17 +130,15 @@ typedef struct {
  *   o              [B, T, Hv, Dv]   dtype, written for every token
  *   workspace      device scratch of dn_chunk_fwd_workspace_bytes(shape) bytes, or
  *                                   NULL (with less, the per-key-channel path runs as
- *                                   one slower kernel, and the bf16 Dk = Dv = 64 path on
- *                                   the vector ALUs); contents on entry are ignored,
+ *                                   one slower kernel); contents on entry are ignored,
  *                                   on exit undefined (two calls in flight on one workspace race)
  *
  * Errors: DN_ERR_INVALID_ARG (null required pointer, non-positive sizes, Hv % Hqk,
  * B != 1 or num_seqs < 1 with cu_seqlens, num_seqs != B without, misaligned
  * pointer, unknown flags, negative or non-finite l2norm_eps), DN_ERR_UNSUPPORTED
  * (Dk, Dv, chunk_size or dtype not supported), DN_ERR_HIP.  A missing or short
- * workspace is not an error: the per-key-channel path then runs as one kernel, the
- * Dk = Dv = 64 path as the vector kernel (dn_chunk_fwd_path tells which kernels a call
- * runs).  T == 0 is valid:
+ * workspace is not an error: the per-key-channel path then runs as one kernel
+ * (dn_chunk_fwd_path tells which kernels a call runs).  T == 0 is valid:
  * final_state = initial_state.
  */
 dn_status dn_chunk_fwd(const dn_shape* shape,
@@ -151,23 +149,22 @@ dn_status dn_chunk_fwd(const dn_shape* shape,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
-/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none).  Two bf16
- * paths with 64-token chunks use one, keeping the state-independent operands of each
+/* Bytes of device workspace dn_chunk_fwd needs for this shape (0 when none).  One bf16
+ * path with 64-token chunks uses one, keeping the state-independent operands of each
  * (chunk, value head) there for the sequential pass: DN_GATE_PER_KEY at Dk = 128, Dv a
  * multiple of 32 (68,352 B each; given less, one slower kernel forms them inside its
- * chunk loop), and the scalar or no gate at Dk = Dv = 64 without DN_QK_L2NORM (T and P of
- * the chunk, 16,384 B each; given less, the vector-ALU kernel runs). */
+ * chunk loop). */
 size_t dn_chunk_fwd_workspace_bytes(const dn_shape* shape);
 
 /*
  * dn_chunk_fwd_noalloc -- dn_chunk_fwd for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
- * Same arguments and results as dn_chunk_fwd, without the workspace.  The two paths that
- * need scratch (gates per key channel on the matrix cores: 68,352 B per chunk and value
- * head; bf16 Dk = Dv = 64: 16,384 B) take it from a static device array of
- * DN_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the process ends;
- * the call allocates nothing.  A call whose records exceed the array (more than 981, or
- * 4,096, (chunk, value head) pairs) returns DN_ERR_WORKSPACE, before any launch.  Every call on one GPU shares that GPU's array:
+ * Same arguments and results as dn_chunk_fwd, without the workspace.  The path that
+ * needs scratch (gates per key channel on the matrix cores: 68,352 B per chunk and value
+ * head) takes it from a static device array of DN_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing.  A call whose
+ * records exceed the array (more than 981 (chunk, value head) pairs) returns
+ * DN_ERR_WORKSPACE, before any launch.  Every call on one GPU shares that GPU's array:
  * calls that overlap in time on one GPU (different streams, or host threads) race and
  * must be serialised by the caller.  Nothing in the array needs clearing between calls.
  *
@@ -183,17 +180,16 @@ dn_status dn_chunk_fwd_noalloc(const dn_shape* shape,
 
 /* Which kernels dn_chunk_fwd runs for this shape and workspace size (no launch, no
  * device access).  Only bf16 prompts with 64-token chunks run on the matrix cores: at
- * Dk = Dv = 128 in one kernel, at Dk = Dv = 64 without DN_QK_L2NORM in two given the
- * workspace, and with DN_GATE_PER_KEY at Dk = 128, Dv a multiple of 32; every other
- * supported shape runs the vector-ALU chunked kernel, which is about 100x slower on the
- * same work.  Returns DN_PATH_INVALID for a shape dn_chunk_fwd would reject. */
+ * Dk = Dv = 128 or Dk = Dv = 64 in one kernel (with or without DN_QK_L2NORM), and with
+ * DN_GATE_PER_KEY at Dk = 128, Dv a multiple of 32; every other supported shape runs the
+ * vector-ALU chunked kernel, which is about 100x slower on the same work.  Returns
+ * DN_PATH_INVALID for a shape dn_chunk_fwd would reject. */
 typedef enum {
     DN_PATH_INVALID = -1,
     DN_PATH_FUSED = 0,                         /* one matrix-core kernel                     */
     DN_PATH_CHANNEL_GATE_TWO_KERNELS = 1,      /* per-key-channel gates, with the workspace  */
     DN_PATH_CHANNEL_GATE_ONE_KERNEL = 2,       /* per-key-channel gates, workspace too small */
-    DN_PATH_VECTOR = 3,                        /* vector-ALU chunked kernel                  */
-    DN_PATH_TWO_KERNELS = 4                    /* d = 64: T and P per chunk, then the chain  */
+    DN_PATH_VECTOR = 3                         /* vector-ALU chunked kernel                  */
 } dn_path;
 int32_t dn_chunk_fwd_path(const dn_shape* shape, size_t workspace_bytes);
 

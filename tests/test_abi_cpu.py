@@ -247,9 +247,9 @@ def test_chunk_fwd_path_reports_the_kernels():
     assert path(4, 2048, 16, 16, 128, 128, bf) == "fused"
     assert path(1, 32768, 32, 32, 128, 128, bf, num_seqs=8) == "fused"
     assert path(4, 2048, 16, 16, 128, 128, bf, qk_l2norm=True) == "fused"
-    assert path(4, 2048, 16, 16, 64, 64, bf) == "two_kernels"
-    assert path(4, 2048, 16, 16, 64, 64, bf, workspace_bytes=0) == "vector"
-    assert path(4, 2048, 16, 16, 64, 64, bf, qk_l2norm=True) == "vector"
+    assert path(4, 2048, 16, 16, 64, 64, bf) == "fused"
+    assert path(4, 2048, 16, 16, 64, 64, bf, workspace_bytes=0) == "fused"
+    assert path(4, 2048, 16, 16, 64, 64, bf, qk_l2norm=True) == "fused"
     assert path(4, 2048, 16, 16, 64, 64, f32) == "vector"
     assert path(4, 2048, 16, 16, 64, 128, bf) == "vector"
     assert path(4, 2048, 16, 16, 128, 128, f32) == "vector"
@@ -262,14 +262,14 @@ def test_chunk_fwd_path_reports_the_kernels():
     assert path(4, 2048, 16, 16, 48, 128, bf) == "invalid"
 
 
-def test_two_kernel_prompt_workspace_query():
-    """dn_chunk_fwd_workspace_bytes for the bf16 d = 64 prompt: T and P of every (chunk,
-    value head), 2 x 64 x 64 bf16 = 16,384 B, over the same chunk bound; zero with the
-    in-rule normalisation, in fp32, with other chunk sizes or unequal key and value sizes."""
+def test_d64_prompt_workspace_query():
+    """dn_chunk_fwd_workspace_bytes is zero for the bf16 d = 64 prompt (one kernel, every
+    intermediate on chip), with or without the in-rule normalisation, and for the shapes that
+    run on the vector ALUs."""
     import torch
     bf = torch.bfloat16
-    assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, bf) == 4 * 32 * 16 * 16384
-    assert dn.workspace_bytes(1, 300, 2, 4, 64, 64, bf, num_seqs=5) == 10 * 4 * 16384
+    assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, bf) == 0
+    assert dn.workspace_bytes(1, 300, 2, 4, 64, 64, bf, num_seqs=5) == 0
     assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, bf, qk_l2norm=True) == 0
     assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, torch.float32) == 0
     assert dn.workspace_bytes(4, 2048, 16, 16, 64, 64, bf, chunk_size=32) == 0

@@ -46,6 +46,11 @@ CASES = {
                                    init_std=0.02, beta_scale=2.0),
     "fused_gated_long": dict(B=1, T=1000, Hqk=1, Hv=2, Dk=128, dtype="bf16", g_scale=0.05,
                              init_std=0.02, beta_scale=2.0),
+    # the same kernel at d = 64
+    "fused_d64_plain_ragged": dict(B=2, T=333, Hqk=2, Dk=64, dtype="bf16"),
+    "fused_d64_gated_packed_gqa": dict(B=1, Hqk=2, Hv=4, Dk=64, dtype="bf16",
+                                       seqlens=[70, 0, 1, 64, 129, 0], g_scale=0.05,
+                                       init_std=0.02, beta_scale=2.0),
     # the vector-ALU path: fp32 (1e-4 bar) and bf16 at other head sizes
     "generic_f32_d64": dict(B=1, T=150, Hqk=2, Dk=64, dtype="f32", g_scale=0.1, init_std=0.3),
     "generic_f32_d128_packed": dict(B=1, Hqk=1, Hv=2, Dk=128, dtype="f32",

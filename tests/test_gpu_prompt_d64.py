@@ -1,11 +1,11 @@
-"""The bf16 d = 64 prompt on the matrix cores (T and P of every chunk, then the chunk
-chain) against the fp64 oracle, through the C ABI (needs an MI355X).
+"""The bf16 d = 64 prompt on the matrix cores (the one-launch kernel at d_k = d_v = 64)
+against the fp64 oracle, through the C ABI (needs an MI355X).
 
 Bar: relative L2 1e-2 (bf16 inputs) over whole tensors and per (sequence, value head).
 The cases cover ragged tails, packed batches with empty and one-token sequences, initial
 states, GQA with the (sequence, q/k head) count a multiple of 8 (the XCD-grouped workgroup
-order) and not, no gate, strong decay, write strengths up to 2, a long sequence, the
-workspace fallback to the vector kernel, and graph replay.
+order) and not, no gate, strong decay, write strengths up to 2, a long sequence, graph
+replay, and a final state that aliases the initial one.
 """
 import sys
 
@@ -60,48 +60,34 @@ def _check(x, o, s, scale):
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_two_kernel_prompt(name):
+def test_d64_prompt(name):
     x = make_case(Dk=64, dtype="bf16", seed=17, name=name, **CASES[name])
-    _say(f"two-kernel prompt {name}: B{x.B} T{x.T} {x.Hqk}->{x.Hv} heads, {x.num_seqs} sequences")
+    _say(f"d64 prompt {name}: B{x.B} T{x.T} {x.Hqk}->{x.Hv} heads, {x.num_seqs} sequences")
     assert dn.chunk_fwd_path(x.B, x.T, x.Hqk, x.Hv, 64, 64, torch.bfloat16,
-                             num_seqs=x.num_seqs) == "two_kernels"
+                             num_seqs=x.num_seqs) == "fused"
     o, s = _run(x, 0.8)
     _check(x, o, s, 0.8)
 
 
-def test_short_workspace_runs_the_vector_kernel():
-    """Given less workspace than asked for, the same call runs the vector kernel, within the
-    same bar."""
-    x = make_case(B=1, T=150, Hqk=2, Dk=64, dtype="bf16", g_scale=0.1, init_std=0.1, seed=5,
-                  name="d64_short_workspace")
-    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
-    assert dn.chunk_fwd_path(1, 150, 2, 2, 64, 64, torch.bfloat16, workspace_bytes=16) == "vector"
-    o1, s1 = _run(x, 1.0, workspace=ws)
-    _check(x, o1, s1, 1.0)
-    o2, s2 = _run(x, 1.0)
-    assert rel_l2(o1, o2) < 1e-2 and rel_l2(s1, s2) < 1e-2
-
-
-def test_in_rule_norm_and_fp32_stay_on_the_vector_kernel():
-    assert dn.chunk_fwd_path(1, 128, 2, 2, 64, 64, torch.bfloat16, qk_l2norm=True) == "vector"
+def test_d64_needs_no_workspace_and_other_forms_stay_on_the_vector_kernel():
+    assert dn.workspace_bytes(1, 128, 2, 2, 64, 64, torch.bfloat16) == 0
+    assert dn.chunk_fwd_path(1, 128, 2, 2, 64, 64, torch.bfloat16, workspace_bytes=0) == "fused"
+    assert dn.chunk_fwd_path(1, 128, 2, 2, 64, 64, torch.bfloat16, qk_l2norm=True) == "fused"
     assert dn.chunk_fwd_path(1, 128, 2, 2, 64, 64, torch.float32) == "vector"
     assert dn.chunk_fwd_path(1, 128, 2, 2, 64, 64, torch.bfloat16, chunk_size=32) == "vector"
-    assert dn.workspace_bytes(1, 128, 2, 2, 64, 64, torch.bfloat16, qk_l2norm=True) == 0
+    assert dn.chunk_fwd_path(1, 128, 2, 2, 64, 32, torch.bfloat16) == "vector"
 
 
-def test_two_kernel_graph_replay():
-    """A HIP graph of the two launches replays to the eager result, every replay."""
+def test_d64_graph_replay():
+    """A HIP graph of the launch replays to the eager result, every replay."""
     x = make_case(B=2, T=500, Hqk=2, Hv=4, Dk=64, dtype="bf16", g_scale=0.1, init_std=0.02,
                   seed=9, name="d64_graph")
     d = to_inputs(x)
     o = torch.empty((x.B, x.T, x.Hv, 64), dtype=torch.bfloat16, device="cuda")
     fs = torch.empty((x.B, x.Hv, 64, 64), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dn.workspace_bytes(x.B, x.T, x.Hqk, x.Hv, 64, 64, torch.bfloat16),
-                     dtype=torch.uint8, device="cuda")
 
     def call():
-        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], out=o, final_state=fs,
-                     workspace=ws)
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], out=o, final_state=fs)
 
     call()
     torch.cuda.synchronize()
@@ -116,7 +102,7 @@ def test_two_kernel_graph_replay():
     with torch.cuda.graph(g):
         call()
     for rep in range(3):
-        o.zero_(), fs.zero_(), ws.zero_()
+        o.zero_(), fs.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -124,9 +110,9 @@ def test_two_kernel_graph_replay():
         _ = (o.float().sum() + 1).item()
 
 
-def test_two_kernel_final_state_may_alias_initial_state():
-    """The chain reads its columns of the initial state before it writes the final state, so
-    one tensor can serve as both (the state updated in place)."""
+def test_d64_final_state_may_alias_initial_state():
+    """Each chain wave reads its columns of the initial state before it writes the final
+    state, so one tensor can serve as both (the state updated in place)."""
     x = make_case(B=2, T=200, Hqk=2, Dk=64, dtype="bf16", g_scale=0.1, init_std=0.1, seed=11,
                   name="d64_alias")
     d = to_inputs(x)
@@ -138,7 +124,7 @@ def test_two_kernel_final_state_may_alias_initial_state():
     assert torch.equal(o1, o2) and torch.equal(s1, st)
 
 
-def test_two_kernel_zero_length_prompt_returns_initial_state():
+def test_d64_zero_length_prompt_returns_initial_state():
     x = make_case(B=2, T=0, Hqk=2, Dk=64, dtype="bf16", init_std=1.0, seed=12, name="d64_T0")
     d = to_inputs(x)
     o, s = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, d["init"])

@@ -66,38 +66,13 @@ def test_noalloc_matches_workspace_call_twice():
 
 
 def test_noalloc_without_scratch_need():
-    """A prompt that needs no scratch (one gate per head, the fused kernel) runs through the
-    allocation-free call unchanged."""
-    x = make_case(B=2, T=200, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
-                  seed=73, name="noalloc_fused")
-    d = to_inputs(x)
-    o1, s1 = _noalloc(x, d)
-    o2, s2 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"])
-    torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(s1, s2)
-
-
-def test_noalloc_d64_two_kernels_twice():
-    """The d = 64 two-kernel prompt takes T and P of every chunk from the static array: two
-    calls in a row, the second smaller, each bit for bit equal to the workspace call."""
-    cases = [
-        make_case(B=1, Hqk=2, Hv=4, Dk=64, dtype="bf16", seqlens=[900, 0, 257], g_scale=0.1,
-                  init_std=0.02, beta_scale=2.0, seed=74, name="noalloc_d64_first"),
-        make_case(B=1, T=100, Hqk=1, Hv=2, Dk=64, dtype="bf16", g_scale=0.3, seed=75,
-                  name="noalloc_d64_second"),
-    ]
-    for x in cases:
-        _say(f"noalloc {x.name}: B{x.B} T{x.T} Hv{x.Hv} sequences {x.num_seqs}")
-        assert dn.chunk_fwd_path(x.B, x.T, x.Hqk, x.Hv, 64, 64, torch.bfloat16,
-                                 num_seqs=x.num_seqs) == "two_kernels"
+    """Prompts that need no scratch (one gate per head, the fused kernel at d = 128 and 64)
+    run through the allocation-free call unchanged."""
+    for D, seed in ((128, 73), (64, 74)):
+        x = make_case(B=2, T=200, Hqk=2, Hv=2, Dk=D, dtype="bf16", g_scale=0.1, init_std=0.02,
+                      seed=seed, name=f"noalloc_fused_d{D}")
         d = to_inputs(x)
         o1, s1 = _noalloc(x, d)
-        o2, s2 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"],
-                              cu_seqlens=d["cu"])
+        o2, s2 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"])
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2) and torch.equal(s1, s2), "differs from the workspace call"
-        o_ref, s_ref = run_oracle(x)
-        eo, es = rel_l2(host(o1), o_ref), rel_l2(host(s1), s_ref)
-        uo, us, where = per_unit_rel(host(o1), o_ref, host(s1), s_ref, x)
-        _say(f"  rel_l2 o={eo:.2e} state={es:.2e}; worst (sequence, head) {uo:.2e} {us:.2e}")
-        assert max(eo, es, uo, us) <= tol(x)
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
