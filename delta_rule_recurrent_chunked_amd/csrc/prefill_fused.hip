@@ -1,6 +1,6 @@
 // prefill_fused.hip -- one-kernel chunked prefill of the gated delta rule on the gfx950
-// matrix cores (bf16 operands, fp32 accumulation), for bf16 inputs with Dk = Dv = 128 and
-// 64-token chunks.
+// matrix cores (bf16 operands, fp32 accumulation), for bf16 inputs with Dk = Dv = 128 or
+// Dk = Dv = 64 (the head size D is a template parameter) and 64-token chunks.
 //
 // The algebra is the chunked form of the update on the frankenstein "DeltaNet
 // Attention" page (module docstring), with the gate order of the nnterp
@@ -50,8 +50,8 @@
 // wave that runs it builds A's diagonal tiles itself and keeps them in registers.  The
 // chain waves and that wave raise their wave priority: their instructions issue first.
 //
-// Chain wave w owns state columns 16w .. 16w+15 of the slice as eight 16x16 fp32
-// accumulator tiles; products that consume its results take them as B operands through
+// Chain wave w owns state columns 16w .. 16w+15 of the slice as D / 16 16x16 fp32
+// accumulator tiles (one per 16 keys); products that consume its results take them as B operands through
 // register lane swaps (acc_to_b).  The output waves get the chain's bf16 state and Delta
 // fragments through LDS and use them as the A operands of the transposed products; P stays
 // in their registers, and store O to HBM from their registers.  LDS holds K and Q
