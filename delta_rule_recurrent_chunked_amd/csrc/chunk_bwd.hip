@@ -59,7 +59,9 @@ constexpr int BNS = BD / BS;       // slices
 constexpr int P128 = BD + 16;      // bf16 pitch of [token][key] tiles
 
 // ============================================ 3. the carry dM per (sequence, head, slice)
-constexpr int NTB = 512;           // 8 waves
+constexpr int NTB = 512;           // 8 waves (the gradient kernel; the carry's compute waves)
+constexpr int NTC = 768;           // the carry: 8 compute waves and 4 loader waves
+constexpr int NLC = NTC - NTB;     // loader threads
 
 struct alignas(16) CarrySmem {
     __bf16 K[2][BC][P128], Q[2][BC][P128];    // two chunks: the current one and the next
@@ -71,15 +73,18 @@ struct alignas(16) CarrySmem {
     float tail[2][BC], sod[2][BC], bx[2][BC], egl[2][4];
 };
 
-// one chunk's inputs in registers: thread t holds 16-byte pieces t and t + 512 of K and Q
-// (row = piece / 16), piece t of dO's slice (t < 256, row = piece / 4), piece t of T^T and
-// of P (row = piece / 8), beta and g of token t (t < 64)
+// one chunk's inputs in a loader thread's registers: loader thread t holds 16-byte pieces
+// t + 256 u of K and Q (u < 4, row = piece / 16), piece t of dO's slice (row = piece / 4),
+// pieces t + 256 u of T^T and of P (u < 2, row = piece / 8), beta and g of token t (t < 64)
 struct CarryIn {
-    uint4 k[2], q[2], o, t, p;
+    uint4 k[4], q[4], o, t[2], p[2];
     float beta, g;
 };
 
-__global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
+// Waves 0-7 run the three product steps of each chunk; waves 8-11 move the next chunk's
+// inputs into the other half of the double-buffered LDS and request the chunk after it, so
+// that neither sits between the products.  Every wave takes the three barriers of a chunk.
+__global__ __launch_bounds__(NTC, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
     __shared__ CarrySmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q16 = lane >> 4;
@@ -119,44 +124,52 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
     const auto o_rs = rsrc(static_cast<const __bf16*>(a.dout) + v0, v_end);
     const auto b_rs = rsrc(a.beta + s0, s_end);
     const auto g_rs = rsrc(a.g ? a.g + s0 : a.beta + s0, a.g ? s_end : 0);
-    uint32_t kq_off[2];
+    const bool loader = wave >= NTB / 64;
+    const int lt = tid - NTB;   // loader thread 0 .. 255 (negative on the compute waves)
+    uint32_t kq_off[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int pc = tid + NTB * u;
+    for (int u = 0; u < 4; ++u) {
+        const int pc = lt + NLC * u;
         kq_off[u] = (uint32_t)(pc >> 4) * kq_tok + (pc & 15) * 16;
     }
-    const int op = tid & 255;
-    const uint32_t o_off = (uint32_t)(op >> 2) * v_tok + (op & 3) * 16;
+    const uint32_t o_off = (uint32_t)(lt >> 2) * v_tok + (lt & 3) * 16;
     const uint32_t sc_off = (uint32_t)lane * s_tok;
-    const uint4* tp_head = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.tp)) + tid;
+    const uint4* tp_head = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.tp)) + lt;
 
-    auto fetch = [&](int c, CarryIn& f) {
+    auto fetch = [&](int c, CarryIn& f) {   // loader waves only
         const uint32_t ck = (uint32_t)c * BC * kq_tok, cv = (uint32_t)c * BC * v_tok, cs = (uint32_t)c * BC * s_tok;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 4; ++u) {
             f.k[u] = ld128(k_rs, kq_off[u], ck);
             f.q[u] = ld128(q_rs, kq_off[u], ck);
         }
         f.o = ld128(o_rs, o_off, cv);
         const uint4* tp = tp_head + ((cid0 + c) * a.Hv + h) * (2L * BC * BC / 8);
-        f.t = tp[0];
-        f.p = tp[BC * BC / 8];
-        if (wave == 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f.t[u] = tp[NLC * u];
+            f.p[u] = tp[BC * BC / 8 + NLC * u];
+        }
+        if (lt < 64) {
             f.beta = ld32(b_rs, sc_off, cs);
             f.g = ld32(g_rs, sc_off, cs);
         }
     };
-    auto put_in = [&](const CarryIn& f, int b) {
+    auto put_in = [&](const CarryIn& f, int b) {   // loader waves only
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int pc = tid + NTB * u, row = pc >> 4, cg = pc & 15;
+        for (int u = 0; u < 4; ++u) {
+            const int pc = lt + NLC * u, row = pc >> 4, cg = pc & 15;
             *reinterpret_cast<uint4*>(&sm.K[b][row][cg * 8]) = f.k[u];
             *reinterpret_cast<uint4*>(&sm.Q[b][row][cg * 8]) = f.q[u];
         }
-        if (tid < 256) *reinterpret_cast<uint4*>(&sm.dO[b][op >> 2][(op & 3) * 8]) = f.o;
-        *reinterpret_cast<uint4*>(&sm.Tt[b][tid >> 3][(tid & 7) * 8]) = f.t;
-        *reinterpret_cast<uint4*>(&sm.P[b][tid >> 3][(tid & 7) * 8]) = f.p;
-        if (wave == 0) {
+        *reinterpret_cast<uint4*>(&sm.dO[b][lt >> 2][(lt & 3) * 8]) = f.o;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pc = lt + NLC * u;
+            *reinterpret_cast<uint4*>(&sm.Tt[b][pc >> 3][(pc & 7) * 8]) = f.t[u];
+            *reinterpret_cast<uint4*>(&sm.P[b][pc >> 3][(pc & 7) * 8]) = f.p[u];
+        }
+        if (lt < 64) {
             float gl;
             const float gv = gamma_scan(a.g ? f.g : 0.f, gl);
             const float eg = __expf(gv);
@@ -169,6 +182,30 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
 
     // dM' of this slice in MFMA accumulators: wave w holds tiles (key block 2 (w >> 1) + u,
     // column block w & 1), u = 0, 1: keys 16 (2 (w >> 1) + u) + 4 q16 + e, column 16 (w & 1) + l16
+    if (loader) {
+        // ------------------------------------------------------------ loader waves
+        // at the start of chunk c's turn: chunk c - 1's inputs (requested a turn ago) into the
+        // buffer chunk c + 1 used, then the request for chunk c - 2
+        CarryIn f;
+        if (nc > 0) {
+            fetch(nc - 1, f);
+            put_in(f, (nc - 1) & 1);
+            if (nc > 1) fetch(nc - 2, f);
+        }
+        __syncthreads();
+        for (int c = nc - 1; c >= 0; --c) {
+            if (c > 0) {
+                put_in(f, (c & 1) ^ 1);
+                if (c > 1) fetch(c - 2, f);
+            }
+            __syncthreads();
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- compute waves
     f32x4 dm[2];
     const int dmj = wave & 1;
 #pragma unroll
@@ -183,13 +220,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
         for (int u = 0; u < 2; ++u) put_tile_t(&sm.dMt[0][0], P128, 2 * (wave >> 1) + u, dmj, dm[u], l16, q16);
     };
 
-    CarryIn f;
     put_dm();
-    if (nc > 0) {
-        fetch(nc - 1, f);
-        put_in(f, (nc - 1) & 1);
-        if (nc > 1) fetch(nc - 2, f);
-    }
     __syncthreads();
     const int ti = wave >> 1, tj = wave & 1;   // this wave's 16 x 16 tile of a 64 x 32 product
     for (int c = nc - 1; c >= 0; --c) {
@@ -256,12 +287,7 @@ __global__ __launch_bounds__(NTB, 1) void chunk_carry_kernel(ChunkBwdArgs a) {
                 dm[u] = acc;
             }
         }
-        // the next chunk's inputs into the other buffers (read last two barriers ago), the
-        // new dM' into LDS (read before the last two barriers)
-        if (c > 0) {
-            put_in(f, b ^ 1);
-            if (c > 1) fetch(c - 2, f);
-        }
+        // the new dM' into LDS (read before the last two barriers)
         put_dm();
         __syncthreads();
     }
@@ -822,7 +848,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
     // 2. T^T and P per (chunk, value head)
     if ((e = launch_chunk_tp(a, a.ncid, a.tp, false, s)) != hipSuccess) return e;
     // 3. the carry per (sequence, value head, slice)
-    if (chains > 0) hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)chains), dim3(NTB), 0, s, a);
+    if (chains > 0) hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)chains), dim3(NTC), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 4. the gradients per (chunk, q/k head), after the states
     if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
