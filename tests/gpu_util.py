@@ -67,12 +67,12 @@ def per_unit_rel(o, o_ref, s, s_ref, x: DeltaInputs):
 
 
 def log_errors(case: str, **errors):
-    """Append one case's measured errors to gpurun_out/parity_errors.jsonl (kept with the
-    run's other outputs)."""
+    """Append one case's measured errors to parity_errors.jsonl in the output folder of the
+    run (DN_OUTPUT_DIR, by default the repository's untracked output folder)."""
     import json
     import os
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    out = os.path.join(root, "gpurun_out")
+    out = os.environ.get("DN_OUTPUT_DIR", os.path.join(root, "gpurun_out"))
     os.makedirs(out, exist_ok=True)
     with open(os.path.join(out, "parity_errors.jsonl"), "a") as f:
         f.write(json.dumps({"case": case, **{k: (float(v) if isinstance(v, (float, np.floating))
