@@ -121,6 +121,9 @@ struct alignas(16) FusedSmem {
     float sc[3][SC_N][FC];         // per chunk (slot j % 3): the Sc scalars
     int seq_len[NT];               // packed batches of up to 512 sequences: their lengths,
     int rank_seq[NT];              //   and the sequence of each length rank
+    f32x4 pdec[2][4][64];          // with decay, chunk j's (slot j & 1) factors exp(gamma_r -
+                                   //   gamma_i) of the four diagonal 16x16 tiles, lane layout
+                                   //   of the Gram tiles: A's wave forms them, P's waves reuse them
 };
 
 template <int D>
@@ -359,7 +362,10 @@ __device__ __forceinline__ void make_a(FusedSmem<D>& sm, int j, int l16, int q16
         const int I = a_tile_i(PART, n), R = a_tile_r(PART, n);
         const int r = 16 * R + l16, i0 = 16 * I + 4 * q16;
         f32x4 d = {1.f, 1.f, 1.f, 1.f};
-        if (GATED) d = decay_eval(din[n], I == R);
+        if (GATED) {
+            d = decay_eval(din[n], I == R);
+            if (PART == 0) sm.pdec[j & 1][n][16 * q16 + l16] = d;   // the same factors for P
+        }
         f32x4 av;
 #pragma unroll
         for (int e = 0; e < 4; ++e) av[e] = br[n] * d[e] * G[n][e];
@@ -401,12 +407,14 @@ __device__ __forceinline__ void make_p(const FusedSmem<D>& sm, int j, const bf16
                                        int q16, bf16x8 (&pt)[2][2], float (&qn)[2]) {
     const float* s = &sm.sc[j % 3][0][0];
     DecayIn din[2][4];
+    f32x4 pd[2];   // the diagonal tiles' factors, as A's wave formed them for this chunk
     if (GATED) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int R = p_block(HALF, u), r = 16 * R + l16;
+            pd[u] = sm.pdec[j & 1][R][16 * q16 + l16];
 #pragma unroll
-            for (int I = 0; I <= R; ++I) din[u][I] = decay_load(s, R, I, r, 16 * I + 4 * q16);
+            for (int I = 0; I < R; ++I) din[u][I] = decay_load(s, R, I, r, 16 * I + 4 * q16);
         }
     }
     bf16x8 kf[4][Dims<D>::NKS];
@@ -442,7 +450,7 @@ __device__ __forceinline__ void make_p(const FusedSmem<D>& sm, int j, const bf16
             // tile (I, R): lane holds P[r][i] for i = 16 I + 4 q16 + e; zero above the diagonal
             const int i0 = 16 * I + 4 * q16;
             f32x4 d = {1.f, 1.f, 1.f, 1.f};
-            if (GATED) d = decay_eval(din[u][I], I == R);
+            if (GATED) d = I == R ? pd[u] : decay_eval(din[u][I], false);
 #pragma unroll
             for (int e = 0; e < 4; ++e) G[u][I][e] = (I < R || i0 + e <= r) ? d[e] * G[u][I][e] : 0.f;
         }
