@@ -91,6 +91,11 @@ EDGE = {
     "packed_300_seqs": dict(B=1, Hqk=1, Hv=2, Dk=128, dtype="bf16",
                             seqlens=[(29 * i + 3) % 41 for i in range(300)], g_scale=0.1,
                             init_std=0.02, beta_scale=2.0),
+    # 600 short packed sequences: more than the kernel ranks longest first (512), so they
+    # run in their own order
+    "packed_600_seqs_unranked": dict(B=1, Hqk=1, Hv=1, Dk=128, dtype="bf16",
+                                     seqlens=[(31 * i + 5) % 37 for i in range(600)], g_scale=0.1,
+                                     init_std=0.02),
     # 64 packed sequences, lengths 0..127
     "packed_64_seqs": dict(B=1, Hqk=1, Hv=2, Dk=128, dtype="bf16",
                            seqlens=[(53 * i + 11) % 128 for i in range(64)], g_scale=0.1,

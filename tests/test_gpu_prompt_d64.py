@@ -36,6 +36,9 @@ CASES = {
     "d64_short": dict(B=3, T=7, Hqk=2, g_scale=0.1),
     "d64_many_packed": dict(B=1, Hqk=2, Hv=2, seqlens=[(37 * i) % 150 for i in range(40)],
                             g_scale=0.1, init_std=0.02),
+    # more packed sequences than the kernel ranks longest first (512)
+    "d64_packed_600_unranked": dict(B=1, Hqk=1, Hv=1, seqlens=[(31 * i + 5) % 37 for i in range(600)],
+                                    g_scale=0.1, init_std=0.02),
 }
 
 
