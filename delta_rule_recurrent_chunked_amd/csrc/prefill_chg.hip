@@ -550,7 +550,6 @@ __device__ bool chunk_of(const PrefillArgs& a, long gid, int& n, long& c) {
 struct PrepSmemChg {
     __bf16 Kr[CC][OP];      // k_r o exp(G_r - Z_b(r))
     __bf16 Qr[CC][OP];      // q_r o exp(G_r - Z_b(r))
-    __bf16 Kd[CC][OP];      // k_r o exp(G_last - G_r)
     __bf16 Kc[160][OP];     // column operands of A and P; then K o e^G (0..63), Q o e^G (64..127)
     __bf16 A[CC][AP];
     __bf16 P[CC][AP];
@@ -720,7 +719,13 @@ __global__ __launch_bounds__(NPP) void chg_prep_kernel(PrefillArgs a, long nitem
             L[i].x += off.x;
             L[i].y += off.y;
         }
-        uint32_t pke[8], pqe[8];  // K o e^G and Q o e^G, stored once the column operands are read
+        // this wave's rows of K o e^G, Q o e^G and K o e^{G_last - G} go to the record from
+        // registers as they are formed (a row of 128 channels is one 256-byte store a wave),
+        // so that only A, P, the inverses, e^{G_last} and beta leave at the item's end
+        char* rec = static_cast<char*>(a.ws) + item * OP_BYTES;
+        auto put_row = [&](long off, int r, float x, float y) {
+            *reinterpret_cast<uint32_t*>(rec + off + r * 256 + 4 * lane) = pack_bf16x2(x, y);
+        };
         if (!((hardm >> blk) & 1)) {
             // every factor from two exponentials per entry, e^{L} and e^{-L} (L the in-block
             // sum, -L at most 60 here), and per-channel factors of at most 1
@@ -737,10 +742,10 @@ __global__ __launch_bounds__(NPP) void chg_prep_kernel(PrefillArgs a, long nitem
                 const float kx = kf[i].x * e1x, ky = kf[i].y * e1y, qx = qf[i].x * e1x, qy = qf[i].y * e1y;
                 st2(&sm.Kr[r][2 * lane], kx, ky);
                 st2(&sm.Qr[r][2 * lane], qx, qy);
-                pke[i] = pack_bf16x2(kx * eZ.x, ky * eZ.y);
-                pqe[i] = pack_bf16x2(qx * eZ.x, qy * eZ.y);
+                put_row(OP_KE, r, kx * eZ.x, ky * eZ.y);
+                put_row(OP_QE, r, qx * eZ.x, qy * eZ.y);
                 const float cx = kf[i].x * e2x, cy = kf[i].y * e2y;
-                st2(&sm.Kd[r][2 * lane], cx * eD.x, cy * eD.y);
+                put_row(OP_KD, r, cx * eD.x, cy * eD.y);
                 st2(&sm.Kc[kc_off(blk) + r][2 * lane], cx, cy);
 #pragma unroll
                 for (int b = 1; b < NB; ++b)
@@ -753,13 +758,12 @@ __global__ __launch_bounds__(NPP) void chg_prep_kernel(PrefillArgs a, long nitem
             for (int i = 0; i < 8; ++i) {
                 const int r = 16 * blk + 8 * hf + i;
                 const float ax = __expf(Zw.x + L[i].x), ay = __expf(Zw.y + L[i].y);
-                pke[i] = pack_bf16x2(kf[i].x * ax, kf[i].y * ay);
-                pqe[i] = pack_bf16x2(qf[i].x * ax, qf[i].y * ay);
+                put_row(OP_KE, r, kf[i].x * ax, kf[i].y * ay);
+                put_row(OP_QE, r, qf[i].x * ax, qf[i].y * ay);
                 const float ex = __expf(L[i].x), ey = __expf(L[i].y);
                 st2(&sm.Kr[r][2 * lane], kf[i].x * ex, kf[i].y * ey);
                 st2(&sm.Qr[r][2 * lane], qf[i].x * ex, qf[i].y * ey);
-                st2(&sm.Kd[r][2 * lane], kf[i].x * __expf(Gl.x - Zw.x - L[i].x),
-                    kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
+                put_row(OP_KD, r, kf[i].x * __expf(Gl.x - Zw.x - L[i].x), kf[i].y * __expf(Gl.y - Zw.y - L[i].y));
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     if (b < blk) continue;
@@ -881,24 +885,7 @@ __global__ __launch_bounds__(NPP) void chg_prep_kernel(PrefillArgs a, long nitem
         }
         __syncthreads();
 
-        // ---- 4: K o e^G and Q o e^G over the column operands
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 16 * blk + 8 * hf + i;
-            *reinterpret_cast<uint32_t*>(&sm.Kc[r][2 * lane]) = pke[i];
-            *reinterpret_cast<uint32_t*>(&sm.Kc[CC + r][2 * lane]) = pqe[i];
-        }
-        __syncthreads();
-
-        // ---- out: this item's operands to its workspace record
-        char* rec = static_cast<char*>(a.ws) + item * OP_BYTES;
-#pragma unroll
-        for (int e = tid; e < 1024; e += NPP) {
-            const int r = e >> 4, p = e & 15;
-            *reinterpret_cast<u32x4v*>(rec + OP_KE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[r][8 * p]);
-            *reinterpret_cast<u32x4v*>(rec + OP_QE + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kc[CC + r][8 * p]);
-            *reinterpret_cast<u32x4v*>(rec + OP_KD + r * 256 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.Kd[r][8 * p]);
-        }
+        // ---- out: the rest of this item's record
         {
             const int r = tid >> 3, p = tid & 7;
             *reinterpret_cast<u32x4v*>(rec + OP_A + r * 128 + p * 16) = *reinterpret_cast<const u32x4v*>(&sm.A[r][8 * p]);
