@@ -420,11 +420,12 @@ __global__ __launch_bounds__(NTH) void prefill_chg_kernel(PrefillArgs a) {
                 f32x4 x = z4;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) x = mma16(ld8(&sm.Kc[16 * b + l16][32 * s + 8 * g4]), mb[s], x);
+                // V read transposed: the lane's four tokens of its column in one read
+                const int r0 = 16 * b + 4 * g4;
+                const bf16x4 vv = trld(&sm.V[r0 + (l16 >> 2)][16 * u + 4 * (l16 & 3)]);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[r0]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * b + 4 * g4 + e;
-                    R[b][e] = sm.beta[r] * ((float)sm.V[r][16 * u + l16] - x[e]);
-                }
+                for (int e = 0; e < 4; ++e) R[b][e] = bt[e] * ((float)vv[e] - x[e]);
             }
             bf16x8 ta[NB];
 #pragma unroll
@@ -978,11 +979,12 @@ __global__ __launch_bounds__(NTH) void chg_chain_kernel(PrefillArgs a) {
                 f32x4 x = z4;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) x = mma16(ld8(&sm.Ke[cb][16 * b + l16][32 * s + 8 * g4]), mb[s], x);
+                // V read transposed: the lane's four tokens of its column in one read
+                const int r0 = 16 * b + 4 * g4;
+                const bf16x4 vv = trld(&sm.V[cb][r0 + (l16 >> 2)][16 * u + 4 * (l16 & 3)]);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[cb][r0]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * b + 4 * g4 + e;
-                    R[b][e] = sm.beta[cb][r] * ((float)sm.V[cb][r][16 * u + l16] - x[e]);
-                }
+                for (int e = 0; e < 4; ++e) R[b][e] = bt[e] * ((float)vv[e] - x[e]);
             }
             bf16x8 ta[NB];
 #pragma unroll
