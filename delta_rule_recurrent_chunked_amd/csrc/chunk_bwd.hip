@@ -791,6 +791,24 @@ constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
 std::mutex g_side_mu;
 
+// compute units of the current device (queried once per device)
+int g_cus[kMaxDevices];
+
+hipError_t cu_count(int& n) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (!g_cus[dev]) {
+        int v = 0;
+        if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        g_cus[dev] = v > 0 ? v : 1;
+    }
+    n = g_cus[dev];
+    return hipSuccess;
+}
+
 hipError_t side_stream(SideStream*& out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -832,15 +850,31 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a0, hipStream_t s) {
     a.tp = a.dstates + per * BD * BD;
     const long ids = a.ncid * a.Hv, qk_ids = a.ncid * a.Hqk, chains = (long)a.N * a.Hv * BNS;
     if (ids > 0x7fffffffL || chains > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    PrefillArgs f = a;
+    f.ws = a.states;
+    f.hT = nullptr;
+    int cus = 0;
+    if ((e = cu_count(cus)) != hipSuccess) return e;
+    if (chains >= cus) {
+        // The states launch alone fills the chip (one workgroup per CU), so no launch could
+        // run beside it: it writes the T^T and P records itself, and the four steps run in
+        // order on the caller's stream, without the T/P launch.
+        f.tp_rec = a.tp;
+        if ((e = launch_prefill_fused_states(f, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)chains), dim3(NTC), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (qk_ids > 0) {
+            if (a.g) hipLaunchKernelGGL(chunk_grad_kernel<true>, dim3((unsigned)qk_ids), dim3(NTB), 0, s, a);
+            else hipLaunchKernelGGL(chunk_grad_kernel<false>, dim3((unsigned)qk_ids), dim3(NTB), 0, s, a);
+        }
+        return hipGetLastError();
+    }
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* ss = nullptr;
     e = side_stream(ss);
     if (e != hipSuccess) return e;
     // 1. the state at every chunk start (the prompt kernel, outputs skipped), on the side
     //    stream once the caller's stream has reached this call
-    PrefillArgs f = a;
-    f.ws = a.states;
-    f.hT = nullptr;
     if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
     if ((e = launch_prefill_fused_states(f, ss->stream)) != hipSuccess) return e;

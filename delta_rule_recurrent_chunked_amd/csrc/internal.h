@@ -26,6 +26,8 @@ struct PrefillArgs {
     void* o;
     void* ws;                       // caller's workspace (the two-kernel channel-gate path)
     size_t ws_bytes;
+    void* tp_rec;                   // the chunk-start states launch only: may be null, else
+                                    //   T^T and P of every chunk (the reverse pass's records)
 };
 
 // Readout epilogue, validated on the host (kind < 0: none).

@@ -524,13 +524,62 @@ __device__ __forceinline__ void make_t(FusedSmem<D>& sm, int l16, int q16, const
     }
 }
 
+// The reverse pass's record of chunk j (T^T, then P, bf16 64 x 64 each, row-major), written
+// in the second half of phase j by the two output waves of a (sequence, head)'s first slice.
+// P: each wave's rows, from the P^T fragments make_p formed (lane l16 of q16 holds row
+// 16 R + l16, keys 32 s + 8 q16 ..; the tiles above R are zero).  T^T: wave 0 forms the
+// block of T below its two 32x32 diagonal blocks, T_BL = -T_BR (A_BL T_TL) (A_BL is the
+// chain's block of A, still in Ab), and copies the diagonal blocks from Tt, which the
+// UT-inverse wave wrote in the first half and rewrites only in the next phase.
+template <int D>
+__device__ __forceinline__ void put_tp_record(const FusedSmem<D>& sm, __bf16* rec, int ow, const bf16x8 (&pt)[2][2],
+                                              int lane) {
+    const int l16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int R = p_block(ow, u);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+            *reinterpret_cast<bf16x8*>(rec + FC * FC + (16 * R + l16) * FC + 32 * sb + 8 * q16) =
+                2 * sb <= R ? pt[u][sb] : zero8();
+    }
+    if (ow != 0) return;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 X[2][2];   // A_BL T_TL: tile (ti, tj) rows 32 + 16 ti, columns 16 tj
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+            X[ti][tj] = mma16(ld8(&sm.Ab[32 + 16 * ti + l16][8 * q16]), ld8(&sm.Tt[16 * tj + l16][8 * q16]), z4);
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+        // A operand T_BR[16 ti + m][k] = Tt[32 + k][32 + 16 ti + m] (transposed read)
+        const __bf16* src = &sm.Tt[32 + 8 * q16 + (l16 >> 2)][32 + 16 * ti + 4 * (l16 & 3)];
+        const bf16x8 ta = cat(trld(src), trld(src + 4 * CPITCH));
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+            // T[32 + 16 ti + 4 q16 + e][16 tj + l16] = -Y[e]: row 16 tj + l16 of T^T
+            const f32x4 Y = mma16(ta, acc_to_b(X[0][tj], X[1][tj]), z4);
+            st4(rec + (16 * tj + l16) * FC + 32 + 16 * ti + 4 * q16, -Y[0], -Y[1], -Y[2], -Y[3]);
+        }
+    }
+    // the diagonal blocks (lane = row of T^T) and the zero block left of the lower one
+    const int c0 = lane < 32 ? 0 : 32;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<bf16x8*>(rec + lane * FC + c0 + 8 * p) = ld8(&sm.Tt[lane][c0 + 8 * p]);
+        if (lane >= 32) *reinterpret_cast<bf16x8*>(rec + lane * FC + 8 * p) = zero8();
+    }
+}
+
 // -------------------------------------------------------------------------- kernel
 // STATES: the chain waves also write the state at every chunk start (fp32, for chunk number
 // chunk_id_base(n) + chunk and value head h at a.ws + (number Hv + h) Dk Dv, as 8 x 8 tiles of
 // 16 keys x 16 columns in the accumulator layout: tile (key block kb, column block cb) at
 // (8 kb + cb) 256 floats, lane l's four entries (keys 16 kb + 4 (l >> 4) + e, column
 // 16 cb + (l & 15)) at 4 l, one 16-byte store each), the input of the chunkwise reverse pass;
-// the output waves skip O (that launch needs only the states).
+// the output waves skip O, and with a.tp_rec those of the first slice write each chunk's
+// T^T and P record of the reverse pass instead (put_tp_record).
 template <int D, bool GATED, bool NORM, bool STATES = false>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void fused_kernel(PrefillArgs a) {
     constexpr int NKS = Dims<D>::NKS, NKT = Dims<D>::NKT, NSL = Dims<D>::NSL, KPITCH = Dims<D>::KPITCH;
@@ -750,10 +799,17 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         bf16x8 pt[2][2];     // P^T of the chunk as B operands (make_p)
         bf16x8 qf[2][NKS];   // query rows of R_u: qf[u][ks] = keys 32 ks + 8 q16 ..
         float qn[2] = {0.f, 0.f};   // in-rule normalisation: |q_r|^2 of the rows of P^T
+        // STATES with a.tp_rec: the first slice's output waves, which store no O, write every
+        // chunk's T^T and P record instead
+        __bf16* rec = nullptr;
+        if (STATES && !NORM && a.tp_rec && slice == 0)
+            rec = static_cast<__bf16*>(a.tp_rec) + (chunk_id_base(a, w.n) * a.Hv + w.h) * (2L * FC * FC);
+        const long rec_step = (long)a.Hv * 2 * FC * FC;   // to the next chunk's record
         __syncthreads();
         __syncthreads();
         for (int j = 0; j < nph; ++j) {
             const bool o_live = !STATES && j >= 1 && j <= nc, y_live = !STATES && j < nc;
+            const bool r_live = rec && j < nc;
             if (o_live) {
                 // O of chunk j - 1 = scale (exp(gamma) Y + P Delta), P lower triangular
                 const int jp = j - 1;
@@ -814,11 +870,20 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
                         for (int c = 0; c < 2; ++c) yt[u][c] = mma16(m4[c][ks], qf[u][ks], yt[u][c]);
             }
+            if (r_live) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int R = ow == 0 ? 3 * u : 1 + u;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) qf[u][ks] = ld8(&sm.Q[j & 1][16 * R + l16][32 * ks + 8 * q16]);
+                }
+            }
             __syncthreads();
-            if (y_live) {  // P of chunk j for the same query rows
+            if (y_live || r_live) {  // P of chunk j for the same query rows
                 if (ow == 0) make_p<D, GATED, NORM, 0>(sm, j, qf, l16, q16, pt, qn);
                 else make_p<D, GATED, NORM, 1>(sm, j, qf, l16, q16, pt, qn);
             }
+            if (r_live) put_tp_record<D>(sm, rec + j * rec_step, ow, pt, lane);
             __syncthreads();
         }
     } else if (wave == 4 || wave == 5) {

@@ -273,7 +273,11 @@ dn_status dn_recurrent_bwd(const dn_shape* shape,
  * chunk in parallel, walks each sequence's chunks backwards carrying only dL/dM (written
  * out at every chunk), and then forms every gradient of every chunk in parallel from the
  * chunk's start state and dL/dM after it.  dq and dk sum the value heads of a q/k head in a
- * fixed order and no step uses atomics (the result is bitwise reproducible).
+ * fixed order and no step uses atomics (the result is bitwise reproducible).  With fewer
+ * (sequence, value head) pairs than a quarter of the GPU's compute units, the rerun of the
+ * forward runs on a second stream of the library's own, forked from and joined to `stream`
+ * by events (so the call can be captured into a graph on `stream`); otherwise every step
+ * runs on `stream`.
  *
  * Supported: bf16 q/k/v/d_o, Dk = Dv = 128, 64-token chunks, one log decay per head or
  * none, with or without DN_QK_L2NORM (then a first pass writes the normalised q and k,

@@ -82,6 +82,13 @@ CASES = {
     "gated_packed_gqa": dict(B=1, Hqk=1, Hv=2, Dk=128, seqlens=[70, 0, 1, 129, 64], g_scale=0.3,
                              init_std=0.02, beta_scale=2.0),
     "strong_decay": dict(B=1, T=300, Hqk=2, Hv=4, Dk=128, g_scale=3.0, init_std=0.02),
+    # at least one states workgroup per CU (sequences x value heads x 4 slices >= 256): the
+    # states launch writes the T^T and P records itself and nothing runs beside it
+    "full_chip_gated_ragged": dict(B=2, T=200, Hqk=8, Hv=32, Dk=128, g_scale=0.1, init_std=0.02,
+                                   beta_scale=2.0),
+    "full_chip_plain_rows": dict(B=4, T=130, Hqk=16, Hv=16, Dk=128),
+    "full_chip_packed_strong_decay": dict(B=1, Hqk=8, Hv=16, Dk=128, seqlens=[70, 0, 1, 129, 64, 300],
+                                          g_scale=3.0, init_std=0.02),
 }
 
 
@@ -98,6 +105,7 @@ NORM_CASES = {
     "norm_packed_gqa": dict(B=1, Hqk=1, Hv=2, Dk=128, seqlens=[70, 0, 1, 129, 64], g_scale=0.3,
                             init_std=0.02, beta_scale=2.0),
     "norm_plain": dict(B=1, T=130, Hqk=2, Hv=2, Dk=128),
+    "norm_full_chip_gated": dict(B=2, T=150, Hqk=16, Hv=32, Dk=128, g_scale=0.1, init_std=0.02),
 }
 
 
@@ -154,20 +162,21 @@ def test_chunk_bwd_rejects_unsupported():
         dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], None, None, do)
 
 
-def test_chunk_bwd_graph_replay():
-    """dn_chunk_bwd captured in a HIP graph (its chunk-start states run on a second stream,
-    forked from and joined back to the captured one by events): three replays, each after an
-    eager call on other inputs that rewrites the workspace, match the eager result bit for
-    bit."""
-    _say("chunk bwd graph capture + replays")
-    x = make_case(B=2, T=200, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
+@pytest.mark.parametrize("Hqk,Hv", [(2, 2), (16, 32)])
+def test_chunk_bwd_graph_replay(Hqk, Hv):
+    """dn_chunk_bwd captured in a HIP graph (with few heads its chunk-start states run on a
+    second stream, forked from and joined back to the captured one by events; with 32 heads
+    at B2 every launch runs on the captured stream): three replays, each after an eager call
+    on other inputs that rewrites the workspace, match the eager result bit for bit."""
+    _say(f"chunk bwd graph capture + replays, {Hqk} -> {Hv} heads")
+    x = make_case(B=2, T=200, Hqk=Hqk, Hv=Hv, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
                   seed=85, name="chunk_bwd_graph")
-    y = make_case(B=2, T=200, Hqk=2, Hv=2, Dk=128, dtype="bf16", g_scale=0.2, init_std=0.02,
+    y = make_case(B=2, T=200, Hqk=Hqk, Hv=Hv, Dk=128, dtype="bf16", g_scale=0.2, init_std=0.02,
                   seed=86, name="chunk_bwd_graph_other")
     rng = np.random.default_rng(87)
-    do = dev_tensor(f32_to_bf16_bits(rng.standard_normal((2, 200, 2, 128)).astype(np.float32)))
+    do = dev_tensor(f32_to_bf16_bits(rng.standard_normal((2, 200, Hv, 128)).astype(np.float32)))
     d, e = to_inputs(x), to_inputs(y)
-    ws = torch.empty(dn.chunk_bwd_workspace_bytes(2, 200, 2, 2, 128, 128, torch.bfloat16),
+    ws = torch.empty(dn.chunk_bwd_workspace_bytes(2, 200, Hqk, Hv, 128, 128, torch.bfloat16),
                      dtype=torch.uint8, device="cuda")
     args = (d["q"], d["k"], d["v"], d["beta"], d["g"], d["init"], do)
     other = (e["q"], e["k"], e["v"], e["beta"], e["g"], e["init"], do)
