@@ -129,6 +129,17 @@ def test_chunk_bwd_layer_workload():
     _check(x, grads, do, dfin)
 
 
+def test_chunk_bwd_layer_workload_b4():
+    """B4 H16 T2048 d128 bf16 gated, the reverse-pass shape the benchmark times at B4: 256
+    states workgroups, so the states launch writes the T^T and P records and every launch
+    runs on the caller's stream."""
+    _say("chunk bwd B4 H16 T2048 gated")
+    x = make_case(B=4, T=2048, Hqk=16, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02, seed=89,
+                  name="chunk_bwd_B4_H16_T2048")
+    grads, do, dfin, _, _ = _run(x)
+    _check(x, grads, do, dfin)
+
+
 def test_chunk_bwd_bitwise_repeatable_and_agrees_with_recurrent():
     """Two calls agree bit for bit; the token-by-token reverse pass (dn_recurrent_bwd, a
     different algorithm on the GPU) agrees with it to the bf16 bar."""
