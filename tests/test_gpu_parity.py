@@ -162,7 +162,8 @@ def test_final_state_may_alias_initial_state():
 def test_split_continuation():
     """prefill(0..T) == prefill(t0..T) started from prefill(0..t0)'s final state."""
     _say("split continuation")
-    x = make_case(B=1, T=300, Hqk=2, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02, seed=6)
+    x = make_case(B=1, T=300, Hqk=2, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02, seed=6,
+                  name="split_continuation")
     d = to_inputs(x)
     t0 = 137
     oa, sa = dn.chunk_fwd(d["q"][:, :t0].contiguous(), d["k"][:, :t0].contiguous(),
@@ -181,7 +182,7 @@ def test_prefill_equals_decode_steps():
     """T decode steps from the same start reach the oracle's result as well."""
     _say("decode steps vs oracle")
     x = make_case(B=3, T=40, Hqk=2, Hv=4, Dk=128, dtype="bf16", g_scale=0.1, init_std=0.02,
-                  beta_scale=2.0, seed=8)
+                  beta_scale=2.0, seed=8, name="prefill_vs_decode_steps")
     d = to_inputs(x)
     state = d["init"].clone()
     outs = []
