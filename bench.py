@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -112,15 +113,23 @@ def decode_bytes(N, Hqk, Hv, D):
     return N * Hv * D * D * 4 * 2 + N * (2 * Hqk * D * 2 + 2 * Hv * D * 2 + 2 * Hv * 4)
 
 
+def code_text(src):
+    """A source file's code without its comments and blank lines (a comment edit leaves the
+    built kernels, and so their counters, unchanged)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in src.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest():
-    """Digest of every kernel source: counters in profiles/traffic.json are used only while
-    the sources are the ones they were taken on."""
+    """Digest of the code of every kernel source: counters in profiles/traffic.json are used
+    only while the code is the one they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "delta_rule_recurrent_chunked_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                h.update(f.encode() + b"\0" + code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

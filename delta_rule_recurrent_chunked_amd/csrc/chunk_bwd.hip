@@ -31,7 +31,9 @@
 // Only the carry dM runs across chunks, and it needs just T, P and the chunk's inputs; the
 // rest is independent per chunk once M and dM' are known.  Four launches:
 //   1. the prompt kernel writes the state at every chunk start (outputs skipped);
-//   2. chunk_tp_kernel, one workgroup per (chunk, value head): T^T and P to the workspace;
+//   2. chunk_tp_kernel, one workgroup per (chunk, value head): T^T and P to the workspace
+//      (when launch 1 has a workgroup for every CU, nothing could run beside it, and it
+//      writes T^T and P itself instead);
 //   3. chunk_carry_kernel, one workgroup per (sequence, value head, 32-column slice): the
 //      chunks backwards, dM' kept in MFMA accumulators and written out at every chunk (the
 //      last one is the initial state's gradient);
