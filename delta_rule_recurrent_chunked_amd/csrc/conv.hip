@@ -44,16 +44,19 @@ __device__ __forceinline__ void ld8(const T* p, float (&v)[CG]) {
     }
 }
 
+// 8 outputs, in nontemporal stores (nothing reads them again in this kernel)
 template <typename T>
 __device__ __forceinline__ void st8(T* p, const float (&v)[CG]) {
     if constexpr (sizeof(T) == 2) {
         __bf16 h[CG];
 #pragma unroll
         for (int e = 0; e < CG; ++e) h[e] = (__bf16)v[e];
-        *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, h);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(p));
     } else {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f32x4v{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4v*>(p));
+        __builtin_nontemporal_store(f32x4v{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4v*>(p + 4));
     }
 }
 

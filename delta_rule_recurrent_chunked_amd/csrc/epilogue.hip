@@ -11,8 +11,9 @@
 // A row of d_v entries is spread over d_v * sizeof(T) / 16 lanes, one 16-byte piece each;
 // the mean and the sum of squares reduce over those lanes with DPP butterflies (two
 // passes: the mean first, then squares around it).  The weight, bias and gate of a lane's
-// entries are requested with its piece of o, before the first wait.  Each byte of o, z and y moves once, in 16-byte
-// loads and stores: the kernel is bound by HBM bandwidth.
+// entries are requested with its piece of o, before the first wait.  Each byte of o, z and
+// y moves once, in 16-byte nontemporal loads and stores (nothing is read again, so they
+// bypass the caches' retention): the kernel is bound by HBM bandwidth.
 #include "internal.h"
 
 namespace dn {
@@ -20,7 +21,9 @@ namespace {
 
 template <typename T>
 __device__ __forceinline__ void ld16(const void* base, long off, float (&x)[16 / sizeof(T)]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(base) + off);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 uv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(base) + off));
+    const uint4 u = make_uint4(uv[0], uv[1], uv[2], uv[3]);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -40,9 +43,11 @@ __device__ __forceinline__ void st16(void* base, long off, const float (&y)[16 /
         __bf16 h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = (__bf16)y[e];
-        *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, h);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(p));
     } else {
-        *reinterpret_cast<float4*>(p) = make_float4(y[0], y[1], y[2], y[3]);
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f32x4v{y[0], y[1], y[2], y[3]}, reinterpret_cast<f32x4v*>(p));
     }
 }
 
