@@ -90,6 +90,17 @@ def test_traffic_is_used_only_for_the_sources_it_was_measured_on(tmp_path, monke
     assert blk["mfma"]["algorithmic_flops"] == 18_253_611_008
 
 
+def test_counter_digest_ignores_comments_only():
+    """The digest that keys the counters covers the code: comments and blank lines may change,
+    a changed token may not."""
+    src = "// a kernel\n__global__ void k(int* p) {  // one store\n\n    p[0] = 1; /* the\n  value */\n}\n"
+    same = "/* reworded\n   header */\n__global__ void k(int* p) {\n    p[0] = 1;   // stores one\n}\n"
+    other = "__global__ void k(int* p) {\n    p[0] = 2;\n}\n"
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(other)
+    assert "one store" not in bench.code_text(src) and "p[0] = 1;" in bench.code_text(src)
+
+
 def test_chunk_bwd_bytes_and_flops():
     """The reverse pass's algorithmic bytes and flops, written out per term for the gated
     B1 H16 T2048 d128 shape: bf16 q, k, v, dL/do in; fp32 beta, g in; fp32 dq, dk, dv,
